@@ -1,0 +1,141 @@
+"""CPU float64 oracle for the HGRN2 recurrence.
+
+TEST INFRASTRUCTURE: only the tests, ``__graft_entry__.smoke()`` and the
+benchmark's CPU-baseline leg import this package.  The product path
+(``linear_attention_hgrn2_amd``) never imports it.
+
+The arithmetic lives in ``hgrn2_oracle.c`` (step-by-step recurrence, hand
+backpropagation through time, one decode step), compiled with gcc into
+``liboracle_hgrn2.so`` next to it.  This module only converts arrays to
+contiguous float64 and calls it.  ``exact`` holds an exact rational-arithmetic
+version of the same loops for tiny inputs.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "hgrn2_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle_hgrn2.so")
+_lib = None
+
+__all__ = ["build", "forward", "backward", "decode_step", "threads", "Oracle", "default"]
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle (gcc, -O2, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+                               "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _f64(x):
+    if x is None:
+        return None
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _p(x):
+    return None if x is None else x.ctypes.data_as(ctypes.c_void_p)
+
+
+class Oracle:
+    """ctypes handle on one build of the C oracle (the default build, or a
+    differently compiled copy that a test supplies)."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        I = ctypes.c_int
+        lib.oracle_fwd.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P]
+        lib.oracle_bwd.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P]
+        lib.oracle_decode.argtypes = [I, I, I, I, P, P, P, P, P, P]
+        lib.oracle_threads.restype = I
+        self.lib = lib
+        self.path = path
+
+    def threads(self) -> int:
+        return int(self.lib.oracle_threads())
+
+    def forward(self, q, k, v, log_f, h0=None):
+        q, k, v, log_f, h0 = map(_f64, (q, k, v, log_f, h0))
+        B, T, H, DK = q.shape
+        DV = v.shape[-1]
+        assert k.shape == q.shape and log_f.shape == q.shape and v.shape == (B, T, H, DV)
+        if h0 is not None:
+            assert h0.shape == (B, H, DK, DV)
+        y = np.zeros((B, T, H, DV))
+        ht = np.zeros((B, H, DK, DV))
+        self.lib.oracle_fwd(B, T, H, DK, DV, _p(q), _p(k), _p(v), _p(log_f), _p(h0),
+                            _p(y), _p(ht))
+        return y, ht
+
+    def backward(self, q, k, v, log_f, dy, h0=None, dht=None):
+        q, k, v, log_f, dy, h0, dht = map(_f64, (q, k, v, log_f, dy, h0, dht))
+        B, T, H, DK = q.shape
+        DV = v.shape[-1]
+        assert dy.shape == v.shape
+        dq = np.zeros_like(q)
+        dk = np.zeros_like(k)
+        dv = np.zeros_like(v)
+        dl = np.zeros_like(log_f)
+        dh0 = np.zeros((B, H, DK, DV))
+        self.lib.oracle_bwd(B, T, H, DK, DV, _p(q), _p(k), _p(v), _p(log_f), _p(h0), _p(dy),
+                            _p(dht), _p(dq), _p(dk), _p(dv), _p(dl), _p(dh0))
+        return dq, dk, dv, dl, dh0
+
+    def decode_step(self, q, k, v, log_f, state):
+        q, k, v, log_f = map(_f64, (q, k, v, log_f))
+        S = np.array(state, dtype=np.float64, copy=True, order="C")
+        B, H, DK = q.shape
+        DV = v.shape[-1]
+        y = np.zeros((B, H, DV))
+        self.lib.oracle_decode(B, H, DK, DV, _p(q), _p(k), _p(v), _p(log_f), _p(S), _p(y))
+        return y, S
+
+
+def _load() -> Oracle:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        _lib = Oracle(_LIB)
+    return _lib
+
+
+def default() -> Oracle:
+    """The oracle built from ``hgrn2_oracle.c``."""
+    return _load()
+
+
+def threads() -> int:
+    """OpenMP threads the oracle uses."""
+    return _load().threads()
+
+
+def forward(q, k, v, log_f, h0=None):
+    """y [B,T,H,DV], ht [B,H,DK,DV] of the step recurrence, float64.
+
+    q, k, log_f: [B,T,H,DK]; v: [B,T,H,DV]; h0: [B,H,DK,DV] or None (zero)."""
+    return _load().forward(q, k, v, log_f, h0)
+
+
+def backward(q, k, v, log_f, dy, h0=None, dht=None):
+    """(dq, dk, dv, dlog_f, dh0) of L = sum(y*dy) + sum(ht*dht), float64.
+
+    k and log_f are independent inputs (no tying)."""
+    return _load().backward(q, k, v, log_f, dy, h0, dht)
+
+
+def decode_step(q, k, v, log_f, state):
+    """One recurrent step: returns (y [B,H,DV], new state [B,H,DK,DV]); the
+    input state array is not modified."""
+    return _load().decode_step(q, k, v, log_f, state)
