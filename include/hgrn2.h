@@ -1,0 +1,141 @@
+/*
+ * hgrn2.h -- C ABI of the MI355X (gfx950) HGRN2 recurrence library.
+ *
+ * The operation (HGRN2: Gated Linear RNNs with State Expansion, paperlayer.ai
+ * summary, §3.2 "HGRN2"): for every batch element b and head h, a d_k x d_v
+ * matrix state S whose rows (decay channels) are scaled by the forget gate
+ * f_t = exp(log_f_t) and which receives the outer product of the input-gate
+ * vector k_t with the input v_t; the output is the matrix-vector product of
+ * the output gate q_t with the state, taken after the update:
+ *
+ *     S_t = Diag(f_t) S_{t-1} + k_t^T v_t,        y_t = q_t S_t,
+ *
+ * (HGRN2 ties k = 1 - f, §2.1 and §3.2 p.5; here k is an input of its own so
+ * the caller can tie it or not).  Training uses the chunkwise linear-attention
+ * form of this recurrence (§3.2 p.5: identical to GLA's, so chunkwise
+ * algorithms apply); inference uses the recurrent form one token at a time
+ * (§1: linear inference complexity).
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers owned by the caller.  The library never
+ *     allocates or frees memory, keeps no global state and never synchronises:
+ *     every call only enqueues kernels on `stream` (a hipStream_t, or NULL for
+ *     the default stream) and returns.
+ *   - Token tensors q, k, log_f, v, y and their gradients are contiguous
+ *     row-major [B, T, H, D] (D fastest), 16-byte aligned.  States
+ *     (h0, ht, dht, dh0, the decode state) are float32 [B, H, DK, DV], DV
+ *     fastest, 16-byte aligned.
+ *   - dtype: HGRN2_F32 (float) or HGRN2_BF16 (bfloat16 bits).  y and all
+ *     token gradients have the input dtype.  Accumulation is float32.
+ *   - Supported sizes: DK == DV == D in {16, 32, 64, 128}; chunk in
+ *     {16, 32, 64}; any B, H >= 1 and T >= 1 (a partial last chunk is masked).
+ *     hgrn2_supported() tells which (D, chunk, dtype) combinations have a
+ *     kernel; others return HGRN2_ERR_UNSUPPORTED.
+ *   - Gate precondition: log_f <= 0 and not NaN.  -inf (f = 0) is allowed;
+ *     kernels floor log_f at -200, where exp() is already 0 in float32.
+ *   - Errors: arguments are checked before anything is launched; on an
+ *     argument error nothing is enqueued.  A launch failure returns
+ *     HGRN2_ERR_HIP.  hgrn2_last_error() gives a message for the last failing
+ *     call on the calling thread.  No C++ exception crosses this boundary.
+ *   - Outputs must not alias inputs, except where stated.
+ */
+#ifndef HGRN2_H
+#define HGRN2_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HGRN2_ABI_VERSION 1
+
+typedef enum {
+  HGRN2_OK = 0,
+  HGRN2_ERR_INVALID_ARG = 1, /* null required pointer, size <= 0, misalignment, aliasing */
+  HGRN2_ERR_UNSUPPORTED = 2, /* valid arguments with no kernel (D, chunk, dtype)          */
+  HGRN2_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required               */
+  HGRN2_ERR_HIP = 4          /* the HIP runtime reported an error at launch              */
+} hgrn2_status;
+
+typedef enum { HGRN2_F32 = 0, HGRN2_BF16 = 1 } hgrn2_dtype;
+
+/* HGRN2_ABI_VERSION of the built library. */
+int hgrn2_abi_version(void);
+
+/* Static English name of a status code. */
+const char *hgrn2_status_string(int status);
+
+/* Message describing the last non-OK return on the calling thread ("" if none). */
+const char *hgrn2_last_error(void);
+
+/* 1 if a kernel exists for DK = DV = D, this chunk size and this dtype, else 0. */
+int hgrn2_supported(int D, int chunk, int dtype);
+
+/* Number of chunks, ceil(T / chunk). */
+int hgrn2_num_chunks(int T, int chunk);
+
+/* Bytes of the chunk-boundary state buffer: B*H*(N+1)*DK*DV*4, N = ceil(T/chunk).
+ * Entry n (n = 0..N) is the float32 state after the first n chunks, entry 0
+ * being h0 (or zero) and entry N the final state.  Layout [B, H, N+1, DK, DV]. */
+size_t hgrn2_states_bytes(int B, int T, int H, int DK, int DV, int chunk);
+
+/* Workspace bytes hgrn2_bwd needs: 0 when the caller passes states_in,
+ * hgrn2_states_bytes(...) when it passes states_in = NULL (the states are
+ * then recomputed into the workspace). */
+size_t hgrn2_bwd_workspace_bytes(int B, int T, int H, int DK, int DV, int chunk,
+                                 int have_states);
+
+/*
+ * Chunked forward (HGRN2 summary §3.2 p.5, chunkwise form of the recurrence).
+ *   q, k, log_f : [B,T,H,DK] dtype      v : [B,T,H,DV] dtype
+ *   h0          : [B,H,DK,DV] float32, or NULL for a zero initial state
+ *   y           : [B,T,H,DV] dtype (written)
+ *   ht          : [B,H,DK,DV] float32 final state, or NULL (not wanted).
+ *                 ht may alias h0.
+ *   states_out  : hgrn2_states_bytes() float32 chunk-boundary states for the
+ *                 backward, or NULL (inference).
+ */
+hgrn2_status hgrn2_fwd(int B, int T, int H, int DK, int DV, int chunk, int dtype,
+                       const void *q, const void *k, const void *v, const void *log_f,
+                       const float *h0, void *y, float *ht, float *states_out,
+                       void *stream);
+
+/*
+ * Chunked backward by reverse chunk scan of the state adjoint, for the loss
+ * L = sum(y * dy) + sum(ht * dht).  Gradients are partial derivatives with k
+ * and log_f independent; a caller that ties k = 1 - exp(log_f) adds
+ * -exp(log_f) * dk to dlog_f itself.
+ *   q, k, v, log_f, h0 : as passed to hgrn2_fwd (same chunk size)
+ *   states_in   : the states_out of that hgrn2_fwd call, or NULL (recompute;
+ *                 needs a workspace of hgrn2_states_bytes())
+ *   dy          : [B,T,H,DV] dtype
+ *   dht         : [B,H,DK,DV] float32, or NULL (zero)
+ *   dq, dk, dlog_f : [B,T,H,DK] dtype (written)   dv : [B,T,H,DV] dtype (written)
+ *   dh0         : [B,H,DK,DV] float32 (written), or NULL (not wanted)
+ *   ws, ws_bytes: workspace (see hgrn2_bwd_workspace_bytes); may be NULL/0
+ *                 when states_in is given.
+ */
+hgrn2_status hgrn2_bwd(int B, int T, int H, int DK, int DV, int chunk, int dtype,
+                       const void *q, const void *k, const void *v, const void *log_f,
+                       const float *h0, const float *states_in, const void *dy,
+                       const float *dht, void *dq, void *dk, void *dv, void *dlog_f,
+                       float *dh0, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * One recurrent decode step (HGRN2 summary §1, recurrent inference): for every
+ * (b, h), S <- Diag(exp(log_f)) S + k^T v in place, then y = q S.
+ *   q, k, log_f : [B,H,DK] dtype      v : [B,H,DV] dtype
+ *   state       : [B,H,DK,DV] float32, read and overwritten
+ *   y           : [B,H,DV] dtype (written)
+ * Any D in {16, 32, 64, 128} with DK == DV; dtype F32 or BF16.
+ */
+hgrn2_status hgrn2_decode_step(int B, int H, int DK, int DV, int dtype, const void *q,
+                               const void *k, const void *v, const void *log_f,
+                               float *state, void *y, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HGRN2_H */

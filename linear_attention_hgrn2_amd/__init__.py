@@ -1,0 +1,16 @@
+"""HGRN2 gated linear recurrence with outer-product state expansion, on AMD
+MI355X (gfx950).
+
+The computation lives in ``libhgrn2.so`` (C ABI in ``include/hgrn2.h``, HIP
+kernels in ``csrc/``); this package is its thin Python binding:
+
+  fwd(q, k, v, log_f, h0=None, chunk=64)        chunked forward
+  bwd(q, k, v, log_f, dy, h0, dht, states)      chunked backward
+  decode_step(q, k, v, log_f, state)            one recurrent step, in place
+  hgrn2_chunk(q, k, v, log_f, h0, chunk)        autograd wrapper
+"""
+from ._binding import (BF16, F32, HGRN2Chunk, HGRN2Error, LIB_PATH, bwd, decode_step, fwd,
+                       hgrn2_chunk, lib, num_chunks, states_shape, supported)
+
+__all__ = ["fwd", "bwd", "decode_step", "hgrn2_chunk", "HGRN2Chunk", "HGRN2Error", "supported",
+           "num_chunks", "states_shape", "lib", "LIB_PATH", "F32", "BF16"]

@@ -1,0 +1,208 @@
+"""ctypes binding of libhgrn2.so (see include/hgrn2.h).
+
+Argument marshalling only: shapes and dtypes are checked, outputs are
+allocated with torch when the caller does not pass them, and every step of the
+computation runs in the library's HIP kernels on torch's current stream.
+There is no fallback: if the library is missing or a call fails, an exception
+is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhgrn2.so")
+
+F32, BF16 = 0, 1
+_DT = {torch.float32: F32, torch.bfloat16: BF16}
+
+
+class HGRN2Error(RuntimeError):
+    """A non-OK status from the library."""
+
+    def __init__(self, status: int, where: str, msg: str):
+        super().__init__("%s: %s (%s)" % (where, _lib().hgrn2_status_string(status).decode(), msg))
+        self.status = status
+
+
+_handle = None
+
+
+def _lib():
+    global _handle
+    if _handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libhgrn2.so is not built: run `python -m linear_attention_hgrn2_amd.build` "
+                              "(or __graft_entry__.build())")
+        lib = ctypes.CDLL(LIB_PATH)
+        I, P, Z = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+        lib.hgrn2_abi_version.restype = I
+        lib.hgrn2_status_string.restype = ctypes.c_char_p
+        lib.hgrn2_status_string.argtypes = [I]
+        lib.hgrn2_last_error.restype = ctypes.c_char_p
+        lib.hgrn2_supported.argtypes = [I, I, I]
+        lib.hgrn2_supported.restype = I
+        lib.hgrn2_num_chunks.argtypes = [I, I]
+        lib.hgrn2_num_chunks.restype = I
+        lib.hgrn2_states_bytes.argtypes = [I, I, I, I, I, I]
+        lib.hgrn2_states_bytes.restype = Z
+        lib.hgrn2_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+        lib.hgrn2_bwd_workspace_bytes.restype = Z
+        lib.hgrn2_fwd.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P]
+        lib.hgrn2_fwd.restype = I
+        lib.hgrn2_bwd.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
+        lib.hgrn2_bwd.restype = I
+        lib.hgrn2_decode_step.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P]
+        lib.hgrn2_decode_step.restype = I
+        _handle = lib
+    return _handle
+
+
+def lib():
+    """The loaded ctypes library (raises ImportError if it is not built)."""
+    return _lib()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise HGRN2Error(status, where, _lib().hgrn2_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _tok(name, t, B, T, H, D, dtype):
+    if t.shape != (B, T, H, D):
+        raise ValueError("%s: expected shape %s, got %s" % (name, (B, T, H, D), tuple(t.shape)))
+    if t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+        raise ValueError("%s: expected a contiguous %s CUDA tensor" % (name, dtype))
+
+
+def _st(name, t, B, H, D):
+    if t is None:
+        return
+    if t.shape != (B, H, D, D) or t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError("%s: expected a contiguous float32 CUDA tensor of shape %s" % (name, (B, H, D, D)))
+
+
+def supported(D: int, chunk: int, dtype: torch.dtype) -> bool:
+    return bool(_lib().hgrn2_supported(D, chunk, _DT[dtype]))
+
+
+def num_chunks(T: int, chunk: int) -> int:
+    return int(_lib().hgrn2_num_chunks(T, chunk))
+
+
+def states_shape(B, T, H, D, chunk):
+    return (B, H, num_chunks(T, chunk) + 1, D, D)
+
+
+def fwd(q, k, v, log_f, h0=None, *, chunk=64, want_ht=True, want_states=False,
+        y=None, ht=None, states=None):
+    """Chunked forward.  Returns (y, ht or None, states or None)."""
+    B, T, H, D = q.shape
+    dt = q.dtype
+    if dt not in _DT:
+        raise ValueError("dtype must be float32 or bfloat16")
+    for n, t in (("q", q), ("k", k), ("v", v), ("log_f", log_f)):
+        _tok(n, t, B, T, H, D, dt)
+    _st("h0", h0, B, H, D)
+    if y is None:
+        y = torch.empty_like(q)
+    _tok("y", y, B, T, H, D, dt)
+    if want_ht and ht is None:
+        ht = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+    _st("ht", ht, B, H, D)
+    if want_states and states is None:
+        states = torch.empty(states_shape(B, T, H, D, chunk), dtype=torch.float32, device=q.device)
+    if states is not None and (tuple(states.shape) != states_shape(B, T, H, D, chunk)
+                               or states.dtype != torch.float32 or not states.is_contiguous()):
+        raise ValueError("states: expected float32 %s" % (states_shape(B, T, H, D, chunk),))
+    st = _lib().hgrn2_fwd(B, T, H, D, D, chunk, _DT[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(log_f),
+                          _ptr(h0), _ptr(y), _ptr(ht), _ptr(states), _stream())
+    _check(st, "hgrn2_fwd")
+    return y, ht, states
+
+
+def bwd(q, k, v, log_f, dy, h0=None, dht=None, states=None, *, chunk=64, want_dh0=True,
+        dq=None, dk=None, dv=None, dlog_f=None, dh0=None, ws=None):
+    """Chunked backward.  Returns (dq, dk, dv, dlog_f, dh0 or None)."""
+    B, T, H, D = q.shape
+    dt = q.dtype
+    for n, t in (("q", q), ("k", k), ("v", v), ("log_f", log_f), ("dy", dy)):
+        _tok(n, t, B, T, H, D, dt)
+    _st("h0", h0, B, H, D)
+    _st("dht", dht, B, H, D)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    dlog_f = torch.empty_like(log_f) if dlog_f is None else dlog_f
+    for n, t in (("dq", dq), ("dk", dk), ("dv", dv), ("dlog_f", dlog_f)):
+        _tok(n, t, B, T, H, D, dt)
+    if want_dh0 and dh0 is None:
+        dh0 = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+    _st("dh0", dh0, B, H, D)
+    ws_bytes = 0
+    if states is None:
+        need = int(_lib().hgrn2_bwd_workspace_bytes(B, T, H, D, D, chunk, 0))
+        if ws is None:
+            ws = torch.empty(need // 4, dtype=torch.float32, device=q.device)
+        ws_bytes = ws.numel() * ws.element_size()
+    st = _lib().hgrn2_bwd(B, T, H, D, D, chunk, _DT[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(log_f),
+                          _ptr(h0), _ptr(states), _ptr(dy), _ptr(dht), _ptr(dq), _ptr(dk),
+                          _ptr(dv), _ptr(dlog_f), _ptr(dh0), _ptr(ws), ws_bytes, _stream())
+    _check(st, "hgrn2_bwd")
+    return dq, dk, dv, dlog_f, dh0
+
+
+def decode_step(q, k, v, log_f, state, *, y=None):
+    """One recurrent step; `state` [B,H,D,D] float32 is updated in place.  Returns y [B,H,D]."""
+    B, H, D = q.shape
+    dt = q.dtype
+    for n, t in (("q", q), ("k", k), ("v", v), ("log_f", log_f)):
+        if t.shape != (B, H, D) or t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s: expected a contiguous %s CUDA tensor of shape %s" % (n, dt, (B, H, D)))
+    _st("state", state, B, H, D)
+    if y is None:
+        y = torch.empty_like(q)
+    st = _lib().hgrn2_decode_step(B, H, D, D, _DT[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(log_f),
+                                  _ptr(state), _ptr(y), _stream())
+    _check(st, "hgrn2_decode_step")
+    return y
+
+
+class HGRN2Chunk(torch.autograd.Function):
+    """Autograd wrapper: y, ht = HGRN2Chunk.apply(q, k, v, log_f, h0, chunk).
+
+    k and log_f are independent inputs (a caller tying k = 1 - exp(log_f) in
+    torch gets the tied gradient from autograd through that expression)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, log_f, h0, chunk):
+        y, ht, states = fwd(q, k, v, log_f, h0, chunk=chunk, want_ht=True, want_states=True)
+        ctx.save_for_backward(q, k, v, log_f, h0, states)
+        ctx.chunk = chunk
+        return y, ht
+
+    @staticmethod
+    def backward(ctx, dy, dht):
+        q, k, v, log_f, h0, states = ctx.saved_tensors
+        dy = dy.contiguous() if dy is not None else torch.zeros_like(q)
+        dht = dht.contiguous() if dht is not None else None
+        dq, dk, dv, dl, dh0 = bwd(q, k, v, log_f, dy, h0, dht, states, chunk=ctx.chunk,
+                                  want_dh0=h0 is not None)
+        return dq, dk, dv, dl, dh0, None
+
+
+def hgrn2_chunk(q, k, v, log_f, h0=None, chunk=64):
+    """Differentiable chunked HGRN2 recurrence: returns (y, ht)."""
+    return HGRN2Chunk.apply(q, k, v, log_f, h0, chunk)

@@ -1,0 +1,265 @@
+// C ABI of the HGRN2 recurrence library: argument checks, dispatch, errors.
+// Every check runs before the first HIP call, so a rejected call enqueues
+// nothing.  The declarations and their contracts are in include/hgrn2.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cstdio>
+#include <string>
+
+#include "../../include/hgrn2.h"
+#include "dispatch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+hgrn2_status fail(hgrn2_status s, const std::string &msg) {
+  g_last_error = msg;
+  return s;
+}
+
+bool valid_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool valid_chunk(int c) { return c == 16 || c == 32 || c == 64; }
+bool valid_dtype(int t) { return t == HGRN2_F32 || t == HGRN2_BF16; }
+size_t dsize(int t) { return t == HGRN2_BF16 ? 2 : 4; }
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Range {
+  const char *name;
+  const void *p;
+  size_t bytes;
+};
+
+bool overlap(const Range &a, const Range &b) {
+  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, a1 = a0 + a.bytes;
+  const uintptr_t b0 = (uintptr_t)b.p, b1 = b0 + b.bytes;
+  return a0 < b1 && b0 < a1;
+}
+
+// Fails when any output range overlaps any input range or another output.
+bool check_aliasing(const Range *ins, int nin, const Range *outs, int nout, std::string &msg) {
+  for (int o = 0; o < nout; ++o) {
+    for (int i = 0; i < nin; ++i)
+      if (overlap(outs[o], ins[i])) {
+        msg = std::string(outs[o].name) + " overlaps input " + ins[i].name;
+        return false;
+      }
+    for (int p = o + 1; p < nout; ++p)
+      if (overlap(outs[o], outs[p])) {
+        msg = std::string(outs[o].name) + " overlaps output " + outs[p].name;
+        return false;
+      }
+  }
+  return true;
+}
+
+hgrn2_status check_common(int B, int T, int H, int DK, int DV, int chunk, int dtype) {
+  if (B <= 0 || T <= 0 || H <= 0)
+    return fail(HGRN2_ERR_INVALID_ARG, "B, T and H must be >= 1");
+  if (DK <= 0 || DV <= 0 || chunk <= 0) return fail(HGRN2_ERR_INVALID_ARG, "DK, DV and chunk must be >= 1");
+  if ((long long)B * H > (1LL << 30) || (long long)B * T * H > (1LL << 40))
+    return fail(HGRN2_ERR_INVALID_ARG, "problem too large");
+  if (!valid_dtype(dtype)) return fail(HGRN2_ERR_INVALID_ARG, "dtype must be HGRN2_F32 or HGRN2_BF16");
+  if (DK != DV || !valid_d(DK))
+    return fail(HGRN2_ERR_UNSUPPORTED, "need DK == DV in {16, 32, 64, 128}");
+  if (!valid_chunk(chunk)) return fail(HGRN2_ERR_UNSUPPORTED, "chunk must be 16, 32 or 64");
+  return HGRN2_OK;
+}
+
+hgrn2_status check_ptrs(std::initializer_list<std::pair<const char *, const void *>> req,
+                        std::initializer_list<std::pair<const char *, const void *>> opt) {
+  for (auto &p : req) {
+    if (!p.second) return fail(HGRN2_ERR_INVALID_ARG, std::string(p.first) + " is NULL");
+    if (!aligned16(p.second)) return fail(HGRN2_ERR_INVALID_ARG, std::string(p.first) + " is not 16-byte aligned");
+  }
+  for (auto &p : opt)
+    if (p.second && !aligned16(p.second))
+      return fail(HGRN2_ERR_INVALID_ARG, std::string(p.first) + " is not 16-byte aligned");
+  return HGRN2_OK;
+}
+
+hgrn2_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) {
+    g_last_error.clear();
+    return HGRN2_OK;
+  }
+  if (e == hipErrorNotSupported) return fail(HGRN2_ERR_UNSUPPORTED, std::string(what) + ": no kernel for these sizes");
+  return fail(HGRN2_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int hgrn2_abi_version(void) { return HGRN2_ABI_VERSION; }
+
+const char *hgrn2_status_string(int s) {
+  switch (s) {
+    case HGRN2_OK: return "HGRN2_OK";
+    case HGRN2_ERR_INVALID_ARG: return "HGRN2_ERR_INVALID_ARG";
+    case HGRN2_ERR_UNSUPPORTED: return "HGRN2_ERR_UNSUPPORTED";
+    case HGRN2_ERR_WORKSPACE: return "HGRN2_ERR_WORKSPACE";
+    case HGRN2_ERR_HIP: return "HGRN2_ERR_HIP";
+  }
+  return "HGRN2_UNKNOWN_STATUS";
+}
+
+const char *hgrn2_last_error(void) { return g_last_error.c_str(); }
+
+int hgrn2_supported(int D, int chunk, int dtype) {
+  if (!valid_d(D) || !valid_chunk(chunk) || !valid_dtype(dtype)) return 0;
+  return hgrn2::fwd_exists(dtype, D, chunk) && hgrn2::bwd_exists(dtype, D, chunk) ? 1 : 0;
+}
+
+int hgrn2_num_chunks(int T, int chunk) {
+  if (T <= 0 || chunk <= 0) return 0;
+  return (T + chunk - 1) / chunk;
+}
+
+size_t hgrn2_states_bytes(int B, int T, int H, int DK, int DV, int chunk) {
+  if (B <= 0 || T <= 0 || H <= 0 || DK <= 0 || DV <= 0 || chunk <= 0) return 0;
+  const size_t N = (size_t)hgrn2_num_chunks(T, chunk);
+  return (size_t)B * H * (N + 1) * DK * DV * sizeof(float);
+}
+
+size_t hgrn2_bwd_workspace_bytes(int B, int T, int H, int DK, int DV, int chunk, int have_states) {
+  return have_states ? 0 : hgrn2_states_bytes(B, T, H, DK, DV, chunk);
+}
+
+hgrn2_status hgrn2_fwd(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
+                       const void *k, const void *v, const void *log_f, const float *h0, void *y,
+                       float *ht, float *states_out, void *stream) {
+  hgrn2_status st = check_common(B, T, H, DK, DV, chunk, dtype);
+  if (st != HGRN2_OK) return st;
+  st = check_ptrs({{"q", q}, {"k", k}, {"v", v}, {"log_f", log_f}, {"y", y}},
+                  {{"h0", h0}, {"ht", ht}, {"states_out", states_out}});
+  if (st != HGRN2_OK) return st;
+  if (!hgrn2::fwd_exists(dtype, DK, chunk))
+    return fail(HGRN2_ERR_UNSUPPORTED, "no forward kernel for this D, chunk and dtype");
+  const size_t tok = (size_t)B * T * H * DK * dsize(dtype);
+  const size_t sb = (size_t)B * H * DK * DV * sizeof(float);
+  const size_t stb = hgrn2_states_bytes(B, T, H, DK, DV, chunk);
+  // ht may be exactly h0 (each workgroup reads its slice of h0 before it
+  // writes the same slice of ht); any other overlap is an error.
+  const Range ins[] = {{"q", q, tok}, {"k", k, tok}, {"v", v, tok}, {"log_f", log_f, tok},
+                       {"h0", (ht == h0) ? nullptr : h0, sb}};
+  const Range outs[] = {{"y", y, tok}, {"ht", ht, sb}, {"states_out", states_out, stb}};
+  std::string msg;
+  if (!check_aliasing(ins, 5, outs, 3, msg)) return fail(HGRN2_ERR_INVALID_ARG, msg);
+  if (ht == h0 && ht && overlap(Range{"y", y, tok}, Range{"h0", h0, sb}))
+    return fail(HGRN2_ERR_INVALID_ARG, "y overlaps h0");
+
+  hgrn2::FwdArgs a;
+  a.B = B;
+  a.T = T;
+  a.H = H;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.log_f = log_f;
+  a.h0 = h0;
+  a.y = y;
+  a.ht = ht;
+  a.states = states_out;
+  a.N = hgrn2_num_chunks(T, chunk);
+  return hip_status(hgrn2::dispatch_fwd(dtype, DK, chunk, a, (hipStream_t)stream), "hgrn2_fwd");
+}
+
+hgrn2_status hgrn2_bwd(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
+                       const void *k, const void *v, const void *log_f, const float *h0,
+                       const float *states_in, const void *dy, const float *dht, void *dq,
+                       void *dk, void *dv, void *dlog_f, float *dh0, void *ws, size_t ws_bytes,
+                       void *stream) {
+  hgrn2_status st = check_common(B, T, H, DK, DV, chunk, dtype);
+  if (st != HGRN2_OK) return st;
+  st = check_ptrs({{"q", q}, {"k", k}, {"v", v}, {"log_f", log_f}, {"dy", dy}, {"dq", dq},
+                   {"dk", dk}, {"dv", dv}, {"dlog_f", dlog_f}},
+                  {{"h0", h0}, {"states_in", states_in}, {"dht", dht}, {"dh0", dh0}, {"ws", ws}});
+  if (st != HGRN2_OK) return st;
+  if (!hgrn2::bwd_exists(dtype, DK, chunk) || !hgrn2::fwd_exists(dtype, DK, chunk))
+    return fail(HGRN2_ERR_UNSUPPORTED, "no backward kernel for this D, chunk and dtype");
+  const size_t tok = (size_t)B * T * H * DK * dsize(dtype);
+  const size_t sb = (size_t)B * H * DK * DV * sizeof(float);
+  const size_t stb = hgrn2_states_bytes(B, T, H, DK, DV, chunk);
+  const float *states = states_in;
+  if (!states) {
+    if (!ws || ws_bytes < stb)
+      return fail(HGRN2_ERR_WORKSPACE, "states_in is NULL: need a workspace of hgrn2_states_bytes()");
+  }
+  const Range ins[] = {{"q", q, tok},   {"k", k, tok},   {"v", v, tok},          {"log_f", log_f, tok},
+                       {"h0", h0, sb},  {"dy", dy, tok}, {"dht", dht, sb},       {"states_in", states_in, stb}};
+  const Range outs[] = {{"dq", dq, tok},         {"dk", dk, tok},  {"dv", dv, tok},
+                        {"dlog_f", dlog_f, tok}, {"dh0", dh0, sb}, {"ws", states ? nullptr : ws, stb}};
+  std::string msg;
+  if (!check_aliasing(ins, 8, outs, 6, msg)) return fail(HGRN2_ERR_INVALID_ARG, msg);
+
+  const int N = hgrn2_num_chunks(T, chunk);
+  if (!states) {
+    // recompute the chunk-boundary states with the forward kernel (no outputs)
+    hgrn2::FwdArgs f;
+    f.B = B;
+    f.T = T;
+    f.H = H;
+    f.q = q;
+    f.k = k;
+    f.v = v;
+    f.log_f = log_f;
+    f.h0 = h0;
+    f.y = nullptr;
+    f.ht = nullptr;
+    f.states = (float *)ws;
+    f.N = N;
+    hgrn2_status s1 = hip_status(hgrn2::dispatch_fwd(dtype, DK, chunk, f, (hipStream_t)stream),
+                                 "hgrn2_bwd (state recompute)");
+    if (s1 != HGRN2_OK) return s1;
+    states = (const float *)ws;
+  }
+  hgrn2::BwdArgs a;
+  a.B = B;
+  a.T = T;
+  a.H = H;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.log_f = log_f;
+  a.dy = dy;
+  a.states = states;
+  a.dht = dht;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dlog_f = dlog_f;
+  a.dh0 = dh0;
+  a.N = N;
+  return hip_status(hgrn2::dispatch_bwd(dtype, DK, chunk, a, (hipStream_t)stream), "hgrn2_bwd");
+}
+
+hgrn2_status hgrn2_decode_step(int B, int H, int DK, int DV, int dtype, const void *q, const void *k,
+                               const void *v, const void *log_f, float *state, void *y, void *stream) {
+  if (B <= 0 || H <= 0) return fail(HGRN2_ERR_INVALID_ARG, "B and H must be >= 1");
+  if ((long long)B * H > (1LL << 30)) return fail(HGRN2_ERR_INVALID_ARG, "problem too large");
+  if (!valid_dtype(dtype)) return fail(HGRN2_ERR_INVALID_ARG, "dtype must be HGRN2_F32 or HGRN2_BF16");
+  if (DK != DV || !valid_d(DK)) return fail(HGRN2_ERR_UNSUPPORTED, "need DK == DV in {16, 32, 64, 128}");
+  hgrn2_status st = check_ptrs({{"q", q}, {"k", k}, {"v", v}, {"log_f", log_f}, {"state", state}, {"y", y}}, {});
+  if (st != HGRN2_OK) return st;
+  const size_t vec = (size_t)B * H * DK * dsize(dtype);
+  const size_t sb = (size_t)B * H * DK * DV * sizeof(float);
+  const Range ins[] = {{"q", q, vec}, {"k", k, vec}, {"v", v, vec}, {"log_f", log_f, vec}};
+  const Range outs[] = {{"y", y, vec}, {"state", state, sb}};
+  std::string msg;
+  if (!check_aliasing(ins, 4, outs, 2, msg)) return fail(HGRN2_ERR_INVALID_ARG, msg);
+  hgrn2::DecodeArgs a;
+  a.B = B;
+  a.H = H;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.log_f = log_f;
+  a.state = state;
+  a.y = y;
+  return hip_status(hgrn2::dispatch_decode(dtype, DK, a, (hipStream_t)stream), "hgrn2_decode_step");
+}
+
+}  // extern "C"

@@ -1,0 +1,156 @@
+// Device-side building blocks shared by the HGRN2 chunk kernels (gfx950).
+//
+// Matrix-core convention used throughout (wave64, one 16x16 output tile per
+// MFMA group):
+//   lane l = 16*g + n   (n = l & 15, g = l >> 4)
+//   operand fragment  : 8 values per lane ("slots" 0..7).  For D = A*B the
+//                       A fragment of lane l holds A[m = n][k(g, slot)] and the
+//                       B fragment holds B[k(g, slot)][col = n].  Any mapping
+//                       k(g, slot) works as long as A and B use the same one,
+//                       which lets us feed accumulators back in as operands.
+//   accumulator       : 4 floats per lane, reg r holds D[row = 4g + r][col = n].
+// bf16 operands go through one v_mfma_f32_16x16x32_bf16; float32 operands go
+// through eight v_mfma_f32_16x16x4_f32, slot i in instruction i.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hgrn2 {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+struct bf16_t {  // storage type of a bfloat16 value in memory
+  uint16_t bits;
+};
+
+// ------------------------------------------------------------ conversions
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) {
+  return __uint_as_float(((uint32_t)x.bits) << 16);
+}
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
+  __bf16 h = (__bf16)x;  // round to nearest even (v_cvt_pk_bf16_f32)
+  bf16_t r;
+  r.bits = __builtin_bit_cast(uint16_t, h);
+  return r;
+}
+
+// Unpack a 16-byte vector of storage values into floats.
+template <typename T> struct Vec;
+template <> struct Vec<float> {
+  static constexpr int N = 4;  // elements per 16 bytes
+  __device__ static __forceinline__ void unpack(const uint4 &u, float *o) {
+    o[0] = __uint_as_float(u.x);
+    o[1] = __uint_as_float(u.y);
+    o[2] = __uint_as_float(u.z);
+    o[3] = __uint_as_float(u.w);
+  }
+};
+template <> struct Vec<bf16_t> {
+  static constexpr int N = 8;
+  __device__ static __forceinline__ void unpack(const uint4 &u, float *o) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = __uint_as_float(w[i] << 16);
+      o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+
+// ------------------------------------------------------------ fragments
+struct Frag {
+  float v[8];
+};
+
+__device__ __forceinline__ void frag_zero(Frag &f) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f.v[i] = 0.f;
+}
+
+__device__ __forceinline__ void acc_zero(f32x4_t &a) { a = f32x4_t{0.f, 0.f, 0.f, 0.f}; }
+
+// D += A * B over one 32-wide k step.  Op = bf16_t: one bf16 MFMA;
+// Op = float: eight float32 MFMAs.
+template <typename Op> struct Mma;
+template <> struct Mma<bf16_t> {
+  __device__ static __forceinline__ void run(f32x4_t &acc, const Frag &a, const Frag &b) {
+    bf16x8_t x, y;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      x[i] = (__bf16)a.v[i];
+      y[i] = (__bf16)b.v[i];
+    }
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, acc, 0, 0, 0);
+  }
+};
+template <> struct Mma<float> {
+  __device__ static __forceinline__ void run(f32x4_t &acc, const Frag &a, const Frag &b) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[i], b.v[i], acc, 0, 0, 0);
+  }
+};
+
+// D += A * B with B carried as an unevaluated bf16 pair (hi + lo), i.e. to
+// about 16 significant bits, at the cost of a second MFMA.  Used where two
+// products must stay consistent enough for a later difference of them to
+// cancel (the intra-chunk parts of dq and dk feed q*dq - k*dk).
+template <typename Op> struct MmaSplitB;
+template <> struct MmaSplitB<bf16_t> {
+  __device__ static __forceinline__ void run(f32x4_t &acc, const Frag &a, const Frag &b) {
+    bf16x8_t x, yh, yl;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      x[i] = (__bf16)a.v[i];
+      yh[i] = (__bf16)b.v[i];
+      yl[i] = (__bf16)(b.v[i] - (float)yh[i]);
+    }
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, yh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, yl, acc, 0, 0, 0);
+  }
+};
+template <> struct MmaSplitB<float> : Mma<float> {};
+
+// Operand pre-converted to the MFMA input type, for fragments reused many times.
+template <typename Op> struct PFrag;
+template <> struct PFrag<bf16_t> {
+  bf16x8_t x;
+  __device__ __forceinline__ void set(const Frag &f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = (__bf16)f.v[i];
+  }
+};
+template <> struct PFrag<float> {
+  float x[8];
+  __device__ __forceinline__ void set(const Frag &f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = f.v[i];
+  }
+};
+__device__ __forceinline__ void mma(f32x4_t &acc, const PFrag<bf16_t> &a, const PFrag<bf16_t> &b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.x, b.x, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4_t &acc, const PFrag<float> &a, const PFrag<float> &b) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x[i], b.x[i], acc, 0, 0, 0);
+}
+
+// ------------------------------------------------------------ misc
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Floor for log f: exp(-200) is 0 in float32 and finite differences of
+// prefix sums stay finite even for log f = -inf.
+constexpr float kLogFloor = -200.f;
+// Widest decay range (in nats) inside one 16-token sub-block for which the
+// diagonal block is evaluated through the factorised matrix-core form.
+// Factors then stay within exp(+-64), far from float32/bf16 overflow and
+// underflow; wider blocks are evaluated directly.
+constexpr float kDiagLimit = 64.f;
+
+__device__ __forceinline__ float floor_logf(float x) { return fmaxf(x, kLogFloor); }
+
+}  // namespace hgrn2

@@ -1,0 +1,108 @@
+"""The C-ABI library loads, exports every symbol include/hgrn2.h declares, and
+rejects bad arguments before touching the GPU.  CPU only: no call here
+reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hgrn2.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import linear_attention_hgrn2_amd as m
+    return m.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(hgrn2_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("hgrn2_fwd", "hgrn2_bwd", "hgrn2_decode_step"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_strings(lib):
+    assert lib.hgrn2_abi_version() == 1
+    for s in range(5):
+        assert lib.hgrn2_status_string(s).startswith(b"HGRN2_")
+
+
+def test_sizes(lib):
+    assert lib.hgrn2_num_chunks(4096, 64) == 64
+    assert lib.hgrn2_num_chunks(250, 16) == 16
+    assert lib.hgrn2_states_bytes(8, 4096, 16, 128, 128, 64) == 8 * 16 * 65 * 128 * 128 * 4
+    assert lib.hgrn2_bwd_workspace_bytes(1, 100, 1, 16, 16, 16, 1) == 0
+    assert lib.hgrn2_bwd_workspace_bytes(1, 100, 1, 16, 16, 16, 0) == 8 * 16 * 16 * 4
+    assert lib.hgrn2_supported(128, 64, 1) == 1
+    assert lib.hgrn2_supported(48, 64, 1) == 0
+    assert lib.hgrn2_supported(128, 128, 1) == 0
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation
+
+
+def _fwd(lib, **kw):
+    a = dict(B=1, T=10, H=1, DK=16, DV=16, chunk=16, dt=0, q=FAKE, k=FAKE + 0x1000, v=FAKE + 0x2000,
+             lf=FAKE + 0x3000, h0=None, y=FAKE + 0x4000, ht=None, st=None)
+    a.update(kw)
+    return lib.hgrn2_fwd(a["B"], a["T"], a["H"], a["DK"], a["DV"], a["chunk"], a["dt"], a["q"], a["k"],
+                         a["v"], a["lf"], a["h0"], a["y"], a["ht"], a["st"], None)
+
+
+def test_fwd_rejections(lib):
+    assert _fwd(lib, B=0) == 1
+    assert _fwd(lib, T=-3) == 1
+    assert _fwd(lib, q=None) == 1
+    assert b"q is NULL" in lib.hgrn2_last_error()
+    assert _fwd(lib, q=FAKE + 4) == 1                 # misaligned
+    assert _fwd(lib, dt=7) == 1
+    assert _fwd(lib, DK=48, DV=48) == 2
+    assert _fwd(lib, DK=16, DV=32) == 2
+    assert _fwd(lib, chunk=24) == 2
+    assert _fwd(lib, y=FAKE) == 1                      # y aliases q
+    assert _fwd(lib, dt=0, DK=128, DV=128, chunk=64) == 2   # float32 d128 chunk 64 has no kernel
+
+
+def test_bwd_rejections(lib):
+    P = [FAKE + i * 0x100000 for i in range(12)]
+    # states_in NULL and no workspace
+    r = lib.hgrn2_bwd(1, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], P[3], None, None, P[4], None,
+                      P[5], P[6], P[7], P[8], None, None, 0, None)
+    assert r == 3
+    # dq aliases dy
+    r = lib.hgrn2_bwd(1, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], P[3], None, P[9], P[4], None,
+                      P[4], P[6], P[7], P[8], None, None, 0, None)
+    assert r == 1
+    r = lib.hgrn2_bwd(1, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], P[3], None, P[9], P[4], None,
+                      None, P[6], P[7], P[8], None, None, 0, None)
+    assert r == 1
+
+
+def test_decode_rejections(lib):
+    P = [FAKE + i * 0x100000 for i in range(8)]
+    assert lib.hgrn2_decode_step(0, 1, 16, 16, 0, P[0], P[1], P[2], P[3], P[4], P[5], None) == 1
+    assert lib.hgrn2_decode_step(1, 1, 24, 24, 0, P[0], P[1], P[2], P[3], P[4], P[5], None) == 2
+    assert lib.hgrn2_decode_step(1, 1, 16, 16, 0, P[0], P[1], P[2], P[3], P[4], P[4], None) == 1
+
+
+def test_product_path_does_not_import_the_oracle():
+    import linear_attention_hgrn2_amd
+    pkg = os.path.dirname(linear_attention_hgrn2_amd.__file__)
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".h", ".hip", ".cpp")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in src.replace("oracle-free", ""), f

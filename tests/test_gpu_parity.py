@@ -1,0 +1,168 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle on
+identical seeded inputs.  Tolerances: normwise relative error per (b, h)
+slice <= 2e-2 for bfloat16 inputs and <= 1e-4 for float32 inputs."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import TOL, inputs64, select_bh, slice_rel, to_dev, to_host64
+
+pytestmark = pytest.mark.gpu
+
+
+def _hip():
+    import linear_attention_hgrn2_amd as m
+    return m
+
+
+def _case(dtype, B, T, H, D, lam=0.0, seed=7, h0std=0.0, qscale=None, train=True):
+    w = synth.Workload("case", B=B, H=H, T=T, D=D, chunk=0, dtype=dtype, lam=lam,
+                       qscale=(1.0 / np.sqrt(D) if qscale is None else qscale), h0std=h0std,
+                       train=train, seed=seed)
+    return synth.generate(w)
+
+
+def _fwd_check(d, chunk, label=""):
+    m = _hip()
+    import torch
+    dt = d["dtype"]
+    q, k, v, lf = (to_dev(d[n], dt) for n in ("q", "k", "v", "log_f"))
+    h0 = to_dev(d["h0"], "f32")
+    y, ht, _ = m.fwd(q, k, v, lf, h0, chunk=chunk)
+    torch.cuda.synchronize()
+    x = inputs64(d)
+    yr, htr = oracle.forward(x["q"], x["k"], x["v"], x["log_f"], x["h0"])
+    ey = slice_rel(to_host64(y), yr)
+    eh = slice_rel(to_host64(ht), htr, token_major=False)
+    print("%s fwd D=%d C=%d %s: y %.3e ht %.3e" % (label, d["D"], chunk, dt, ey, eh), flush=True)
+    assert ey <= TOL[dt], ey
+    assert eh <= TOL[dt], eh
+    return y, ht
+
+
+def _bwd_check(d, chunk, use_states=True, with_dht=True, label=""):
+    m = _hip()
+    import torch
+    dt = d["dtype"]
+    q, k, v, lf, dy = (to_dev(d[n], dt) for n in ("q", "k", "v", "log_f", "dy"))
+    h0 = to_dev(d["h0"], "f32")
+    rng = np.random.default_rng(d["seed"] + 99)
+    dht_np = (rng.standard_normal((d["B"], d["H"], d["D"], d["D"])) * 0.5).astype(np.float32) if with_dht else None
+    dht = to_dev(dht_np, "f32")
+    states = None
+    if use_states:
+        _, _, states = m.fwd(q, k, v, lf, h0, chunk=chunk, want_ht=False, want_states=True)
+    dq, dk, dv, dl, dh0 = m.bwd(q, k, v, lf, dy, h0, dht, states, chunk=chunk)
+    torch.cuda.synchronize()
+    x = inputs64(d)
+    ref = oracle.backward(x["q"], x["k"], x["v"], x["log_f"], x["dy"], x["h0"],
+                          None if dht_np is None else dht_np.astype(np.float64))
+    errs = {}
+    for name, g, r in zip(("dq", "dk", "dv", "dlog_f"), (dq, dk, dv, dl), ref[:4]):
+        errs[name] = slice_rel(to_host64(g), r)
+    errs["dh0"] = slice_rel(to_host64(dh0), ref[4], token_major=False)
+    print("%s bwd D=%d C=%d %s: %s" % (label, d["D"], chunk, dt,
+                                       " ".join("%s %.3e" % kv for kv in errs.items())), flush=True)
+    for name, e in errs.items():
+        assert e <= TOL[dt], (name, e)
+
+
+# ------------------------------------------------------------------ forward
+
+def test_fwd_tiny_f32_workload():
+    """The tiny float32 workload: B1 H2 T256 d16, chunk 16, zero initial state."""
+    d = synth.generate("tiny_f32")
+    _fwd_check(d, 16, "tiny_f32")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D,C", [(16, 16), (16, 64), (32, 32), (64, 16), (64, 64), (128, 16),
+                                 (128, 32), (128, 64)])
+def test_fwd_shapes(dtype, D, C):
+    import linear_attention_hgrn2_amd as m
+    import torch
+    if not m.supported(D, C, torch.float32 if dtype == "f32" else torch.bfloat16):
+        pytest.skip("no kernel for this combination")
+    d = _case(dtype, B=2, T=3 * C + 5, H=3, D=D, lam=0.3, h0std=0.5, qscale=1.0)
+    _fwd_check(d, C)
+
+
+def test_fwd_extreme_gates():
+    """log f = -inf (reset), -200 (floor) and decays wide enough to force the
+    direct evaluation of diagonal sub-blocks."""
+    for dtype in ("f32", "bf16"):
+        d = _case(dtype, B=1, T=150, H=2, D=64, lam=0.0, h0std=0.3, qscale=1.0)
+        lf = synth.to_f64(d["log_f"], dtype)
+        lf[0, 3, 0, :] = -np.inf
+        lf[0, 20, 1, 2] = -200.0
+        lf[0, 40:44, 0, 1] = -30.0   # 120 nats inside one 16-token block
+        lf[0, 70:80, 1, :] = -9.0
+        d["log_f"] = lf.astype(np.float32) if dtype == "f32" else synth.f32_to_bf16_bits(lf.astype(np.float32))
+        _fwd_check(d, 64, "extreme")
+        _fwd_check(d, 16, "extreme")
+
+
+def test_fwd_ht_aliases_h0():
+    m = _hip()
+    import torch
+    d = _case("f32", B=2, T=70, H=2, D=32, h0std=1.0, qscale=1.0)
+    q, k, v, lf = (to_dev(d[n], "f32") for n in ("q", "k", "v", "log_f"))
+    h0 = to_dev(d["h0"], "f32")
+    _, ht_ref, _ = m.fwd(q, k, v, lf, h0.clone(), chunk=32)
+    s = h0.clone()
+    m.fwd(q, k, v, lf, s, chunk=32, ht=s)
+    torch.cuda.synchronize()
+    assert torch.equal(s, ht_ref)
+
+
+# ----------------------------------------------------------------- backward
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D,C", [(16, 16), (32, 32), (64, 16), (64, 64), (128, 16), (128, 64)])
+def test_bwd_shapes(dtype, D, C):
+    import linear_attention_hgrn2_amd as m
+    import torch
+    if not m.supported(D, C, torch.float32 if dtype == "f32" else torch.bfloat16):
+        pytest.skip("no kernel for this combination")
+    d = _case(dtype, B=2, T=2 * C + 7, H=2, D=D, lam=0.3, h0std=0.5, qscale=1.0)
+    _bwd_check(d, C)
+
+
+def test_bwd_recompute_states_and_no_dht():
+    d = _case("bf16", B=1, T=200, H=2, D=128, lam=0.0, h0std=0.0, qscale=1.0)
+    _bwd_check(d, 64, use_states=False, with_dht=False, label="recompute")
+
+
+def test_bwd_extreme_gates():
+    for dtype in ("f32", "bf16"):
+        d = _case(dtype, B=1, T=150, H=2, D=64, lam=0.0, h0std=0.3, qscale=1.0)
+        lf = synth.to_f64(d["log_f"], dtype)
+        lf[0, 3, 0, :] = -np.inf
+        lf[0, 20, 1, 2] = -200.0
+        lf[0, 40:44, 0, 1] = -30.0
+        lf[0, 70:80, 1, :] = -9.0
+        d["log_f"] = lf.astype(np.float32) if dtype == "f32" else synth.f32_to_bf16_bits(lf.astype(np.float32))
+        _bwd_check(d, 64, label="extreme")
+        _bwd_check(d, 16, label="extreme")
+
+
+# ------------------------------------------------------------------- decode
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [16, 32, 64, 128])
+def test_decode(dtype, D):
+    m = _hip()
+    import torch
+    d = synth.generate_decode("decode_f32", B=3, H=5, D=D, seed=11)
+    conv = (lambda a: a) if dtype == "f32" else (lambda a: synth.f32_to_bf16_bits(a))
+    q, k, v, lf = (to_dev(conv(d[n]), dtype) for n in ("q", "k", "v", "log_f"))
+    S = to_dev(d["state"], "f32")
+    y = m.decode_step(q, k, v, lf, S)
+    torch.cuda.synchronize()
+    x = {n: synth.to_f64(conv(d[n]), dtype) for n in ("q", "k", "v", "log_f")}
+    yr, Sr = oracle.decode_step(x["q"], x["k"], x["v"], x["log_f"], d["state"].astype(np.float64))
+    ey = np.linalg.norm(to_host64(y) - yr) / np.linalg.norm(yr)
+    es = np.linalg.norm(to_host64(S) - Sr) / np.linalg.norm(Sr)
+    print("decode D=%d %s: y %.3e state %.3e" % (D, dtype, ey, es), flush=True)
+    assert ey <= TOL[dtype] and es <= 1e-5
