@@ -84,7 +84,7 @@ def bench_train(torch, m, args):
     sets = make_train_sets(torch, w, synth.TRAIN_LAMBDAS)
     dev = sets[0]["q"].device
     y = torch.empty((B, T, H, D), dtype=torch.bfloat16, device=dev)
-    states = torch.empty(m.states_shape(B, T, H, D, C), dtype=torch.float32, device=dev)
+    states = torch.empty(m.states_shape(B, T, H, D, C), dtype=torch.bfloat16, device=dev)
     grads = [torch.empty((B, T, H, D), dtype=torch.bfloat16, device=dev) for _ in range(4)]
 
     def step(i, timer=None):
@@ -201,7 +201,7 @@ def main():
                          "global_batch": w.B, "seq_len": w.T, "heads": w.H, "head_dim": w.D,
                          "chunk": w.chunk, "parallelism": "none (1 GPU)"}
         tok = w.B * w.T * w.H * w.D * 2                 # one bf16 [B,T,H,D] tensor
-        st = w.B * w.H * (w.T // w.chunk + 1) * w.D * w.D * 4
+        st = w.B * w.H * (w.T // w.chunk + 1) * w.D * w.D * 2   # bf16 chunk-boundary states
         fwd_bytes = 4 * tok + tok + st                  # q,k,v,log_f in; y, states out
         bwd_bytes = 5 * tok + st + 4 * tok              # q,k,v,log_f,dy,states in; 4 grads out
         th = w.B * w.T * w.H

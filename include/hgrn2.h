@@ -75,15 +75,19 @@ int hgrn2_supported(int D, int chunk, int dtype);
 /* Number of chunks, ceil(T / chunk). */
 int hgrn2_num_chunks(int T, int chunk);
 
-/* Bytes of the chunk-boundary state buffer: B*H*(N+1)*DK*DV*4, N = ceil(T/chunk).
- * Entry n (n = 0..N) is the float32 state after the first n chunks, entry 0
- * being h0 (or zero) and entry N the final state.  Layout [B, H, N+1, DK, DV]. */
-size_t hgrn2_states_bytes(int B, int T, int H, int DK, int DV, int chunk);
+/* Bytes of the chunk-boundary state buffer: B*H*(N+1)*DK*DV*sizeof(dtype),
+ * N = ceil(T/chunk).  Entry n (n = 0..N) is the state after the first n
+ * chunks, rounded to `dtype` (the input dtype of the call), entry 0 being h0
+ * (or zero) and entry N the final state.  Layout [B, H, N+1, DK, DV].  The
+ * recurrence itself always carries its state in float32; these rounded copies
+ * only feed the backward, whose matrix-core products consume the state in the
+ * input dtype anyway.  Returns 0 for invalid arguments. */
+size_t hgrn2_states_bytes(int B, int T, int H, int DK, int DV, int chunk, int dtype);
 
 /* Workspace bytes hgrn2_bwd needs: 0 when the caller passes states_in,
  * hgrn2_states_bytes(...) when it passes states_in = NULL (the states are
  * then recomputed into the workspace). */
-size_t hgrn2_bwd_workspace_bytes(int B, int T, int H, int DK, int DV, int chunk,
+size_t hgrn2_bwd_workspace_bytes(int B, int T, int H, int DK, int DV, int chunk, int dtype,
                                  int have_states);
 
 /*
@@ -93,12 +97,12 @@ size_t hgrn2_bwd_workspace_bytes(int B, int T, int H, int DK, int DV, int chunk,
  *   y           : [B,T,H,DV] dtype (written)
  *   ht          : [B,H,DK,DV] float32 final state, or NULL (not wanted).
  *                 ht may alias h0.
- *   states_out  : hgrn2_states_bytes() float32 chunk-boundary states for the
- *                 backward, or NULL (inference).
+ *   states_out  : hgrn2_states_bytes() bytes of chunk-boundary states (input
+ *                 dtype) for the backward, or NULL (inference).
  */
 hgrn2_status hgrn2_fwd(int B, int T, int H, int DK, int DV, int chunk, int dtype,
                        const void *q, const void *k, const void *v, const void *log_f,
-                       const float *h0, void *y, float *ht, float *states_out,
+                       const float *h0, void *y, float *ht, void *states_out,
                        void *stream);
 
 /*
@@ -118,7 +122,7 @@ hgrn2_status hgrn2_fwd(int B, int T, int H, int DK, int DV, int chunk, int dtype
  */
 hgrn2_status hgrn2_bwd(int B, int T, int H, int DK, int DV, int chunk, int dtype,
                        const void *q, const void *k, const void *v, const void *log_f,
-                       const float *h0, const float *states_in, const void *dy,
+                       const float *h0, const void *states_in, const void *dy,
                        const float *dht, void *dq, void *dk, void *dv, void *dlog_f,
                        float *dh0, void *ws, size_t ws_bytes, void *stream);
 

@@ -48,9 +48,9 @@ def _lib():
         lib.hgrn2_supported.restype = I
         lib.hgrn2_num_chunks.argtypes = [I, I]
         lib.hgrn2_num_chunks.restype = I
-        lib.hgrn2_states_bytes.argtypes = [I, I, I, I, I, I]
+        lib.hgrn2_states_bytes.argtypes = [I, I, I, I, I, I, I]
         lib.hgrn2_states_bytes.restype = Z
-        lib.hgrn2_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+        lib.hgrn2_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
         lib.hgrn2_bwd_workspace_bytes.restype = Z
         lib.hgrn2_fwd.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P]
         lib.hgrn2_fwd.restype = I
@@ -123,10 +123,10 @@ def fwd(q, k, v, log_f, h0=None, *, chunk=64, want_ht=True, want_states=False,
         ht = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
     _st("ht", ht, B, H, D)
     if want_states and states is None:
-        states = torch.empty(states_shape(B, T, H, D, chunk), dtype=torch.float32, device=q.device)
+        states = torch.empty(states_shape(B, T, H, D, chunk), dtype=dt, device=q.device)
     if states is not None and (tuple(states.shape) != states_shape(B, T, H, D, chunk)
-                               or states.dtype != torch.float32 or not states.is_contiguous()):
-        raise ValueError("states: expected float32 %s" % (states_shape(B, T, H, D, chunk),))
+                               or states.dtype != dt or not states.is_contiguous()):
+        raise ValueError("states: expected %s %s" % (dt, states_shape(B, T, H, D, chunk)))
     st = _lib().hgrn2_fwd(B, T, H, D, D, chunk, _DT[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(log_f),
                           _ptr(h0), _ptr(y), _ptr(ht), _ptr(states), _stream())
     _check(st, "hgrn2_fwd")
@@ -153,10 +153,13 @@ def bwd(q, k, v, log_f, dy, h0=None, dht=None, states=None, *, chunk=64, want_dh
     _st("dh0", dh0, B, H, D)
     ws_bytes = 0
     if states is None:
-        need = int(_lib().hgrn2_bwd_workspace_bytes(B, T, H, D, D, chunk, 0))
+        need = int(_lib().hgrn2_bwd_workspace_bytes(B, T, H, D, D, chunk, _DT[dt], 0))
         if ws is None:
-            ws = torch.empty(need // 4, dtype=torch.float32, device=q.device)
+            ws = torch.empty(need, dtype=torch.uint8, device=q.device)
         ws_bytes = ws.numel() * ws.element_size()
+    elif (tuple(states.shape) != states_shape(B, T, H, D, chunk) or states.dtype != dt
+          or not states.is_contiguous()):
+        raise ValueError("states: expected %s %s" % (dt, states_shape(B, T, H, D, chunk)))
     st = _lib().hgrn2_bwd(B, T, H, D, D, chunk, _DT[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(log_f),
                           _ptr(h0), _ptr(states), _ptr(dy), _ptr(dht), _ptr(dq), _ptr(dk),
                           _ptr(dv), _ptr(dlog_f), _ptr(dh0), _ptr(ws), ws_bytes, _stream())

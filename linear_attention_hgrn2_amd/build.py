@@ -28,7 +28,7 @@ FLAGS = [
     # packed float32 vector ops are kept out of every code object
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-    "-Wno-unused-command-line-argument",
+    "-Wno-unused-command-line-argument", "-Wno-shadow",
 ]
 
 

@@ -118,19 +118,20 @@ int hgrn2_num_chunks(int T, int chunk) {
   return (T + chunk - 1) / chunk;
 }
 
-size_t hgrn2_states_bytes(int B, int T, int H, int DK, int DV, int chunk) {
-  if (B <= 0 || T <= 0 || H <= 0 || DK <= 0 || DV <= 0 || chunk <= 0) return 0;
+size_t hgrn2_states_bytes(int B, int T, int H, int DK, int DV, int chunk, int dtype) {
+  if (B <= 0 || T <= 0 || H <= 0 || DK <= 0 || DV <= 0 || chunk <= 0 || !valid_dtype(dtype)) return 0;
   const size_t N = (size_t)hgrn2_num_chunks(T, chunk);
-  return (size_t)B * H * (N + 1) * DK * DV * sizeof(float);
+  return (size_t)B * H * (N + 1) * DK * DV * dsize(dtype);
 }
 
-size_t hgrn2_bwd_workspace_bytes(int B, int T, int H, int DK, int DV, int chunk, int have_states) {
-  return have_states ? 0 : hgrn2_states_bytes(B, T, H, DK, DV, chunk);
+size_t hgrn2_bwd_workspace_bytes(int B, int T, int H, int DK, int DV, int chunk, int dtype,
+                                 int have_states) {
+  return have_states ? 0 : hgrn2_states_bytes(B, T, H, DK, DV, chunk, dtype);
 }
 
 hgrn2_status hgrn2_fwd(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
                        const void *k, const void *v, const void *log_f, const float *h0, void *y,
-                       float *ht, float *states_out, void *stream) {
+                       float *ht, void *states_out, void *stream) {
   hgrn2_status st = check_common(B, T, H, DK, DV, chunk, dtype);
   if (st != HGRN2_OK) return st;
   st = check_ptrs({{"q", q}, {"k", k}, {"v", v}, {"log_f", log_f}, {"y", y}},
@@ -140,7 +141,7 @@ hgrn2_status hgrn2_fwd(int B, int T, int H, int DK, int DV, int chunk, int dtype
     return fail(HGRN2_ERR_UNSUPPORTED, "no forward kernel for this D, chunk and dtype");
   const size_t tok = (size_t)B * T * H * DK * dsize(dtype);
   const size_t sb = (size_t)B * H * DK * DV * sizeof(float);
-  const size_t stb = hgrn2_states_bytes(B, T, H, DK, DV, chunk);
+  const size_t stb = hgrn2_states_bytes(B, T, H, DK, DV, chunk, dtype);
   // ht may be exactly h0 (each workgroup reads its slice of h0 before it
   // writes the same slice of ht); any other overlap is an error.
   const Range ins[] = {{"q", q, tok}, {"k", k, tok}, {"v", v, tok}, {"log_f", log_f, tok},
@@ -169,7 +170,7 @@ hgrn2_status hgrn2_fwd(int B, int T, int H, int DK, int DV, int chunk, int dtype
 
 hgrn2_status hgrn2_bwd(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
                        const void *k, const void *v, const void *log_f, const float *h0,
-                       const float *states_in, const void *dy, const float *dht, void *dq,
+                       const void *states_in, const void *dy, const float *dht, void *dq,
                        void *dk, void *dv, void *dlog_f, float *dh0, void *ws, size_t ws_bytes,
                        void *stream) {
   hgrn2_status st = check_common(B, T, H, DK, DV, chunk, dtype);
@@ -182,8 +183,8 @@ hgrn2_status hgrn2_bwd(int B, int T, int H, int DK, int DV, int chunk, int dtype
     return fail(HGRN2_ERR_UNSUPPORTED, "no backward kernel for this D, chunk and dtype");
   const size_t tok = (size_t)B * T * H * DK * dsize(dtype);
   const size_t sb = (size_t)B * H * DK * DV * sizeof(float);
-  const size_t stb = hgrn2_states_bytes(B, T, H, DK, DV, chunk);
-  const float *states = states_in;
+  const size_t stb = hgrn2_states_bytes(B, T, H, DK, DV, chunk, dtype);
+  const void *states = states_in;
   if (!states) {
     if (!ws || ws_bytes < stb)
       return fail(HGRN2_ERR_WORKSPACE, "states_in is NULL: need a workspace of hgrn2_states_bytes()");
@@ -209,12 +210,12 @@ hgrn2_status hgrn2_bwd(int B, int T, int H, int DK, int DV, int chunk, int dtype
     f.h0 = h0;
     f.y = nullptr;
     f.ht = nullptr;
-    f.states = (float *)ws;
+    f.states = ws;
     f.N = N;
     hgrn2_status s1 = hip_status(hgrn2::dispatch_fwd(dtype, DK, chunk, f, (hipStream_t)stream),
                                  "hgrn2_bwd (state recompute)");
     if (s1 != HGRN2_OK) return s1;
-    states = (const float *)ws;
+    states = ws;
   }
   hgrn2::BwdArgs a;
   a.B = B;

@@ -14,28 +14,42 @@
 // the part of <dL/dS, S> that flows through steps >= t, which reduces to the
 // chunk-local reverse sum plus the carry rowsum(S_end * Lam) from the right.
 //
-// One workgroup owns one (batch, head) with the full D x D adjoint in float32
-// accumulators: wave w owns channels [16w, 16w+16) of Lam^T (and of dq, dk,
-// dlog_f) and value columns [16w, 16w+16) of dv.  S_prev comes from the
-// chunk-boundary states saved by the forward (or recomputed by it).
-// Exponents are anchored as in the forward so that they are <= 0, except on
-// diagonal sub-blocks, which are evaluated directly when their decay range
-// exceeds kDiagLimit.
+// Each (batch, head) is handled by two workgroups that walk the chunks in
+// reverse side by side, each carrying the full D x D adjoint in float32
+// accumulators in the layout its products need:
+//   channel side: Lam^T, wave w owning channels [16w, 16w+16); computes dA,
+//                 dq, dk, dlog_f (everything contracted against channels);
+//   value side  : Lam, wave w owning value columns [16w, 16w+16); computes A
+//                 and dv.
+// Both update their copy of the adjoint from the same operands, so the two
+// never communicate.  S_prev comes from the chunk-boundary states saved by
+// the forward.
 //
-// Precision: dlog_f is a reverse sum of q*dq - k*dk, whose intra-chunk parts
+// Per chunk a preparation pass evaluates every decayed operand once, with
+// exponents anchored inside the span they cover (<= 0 except on diagonal
+// sub-blocks; those are evaluated directly when their decay range exceeds
+// kDiagLimit).  16-token sub-blocks carry block-local prefixes ell (totals
+// L_j, starts P_j); the operands are
+//   qo = q e^{ell}, ko = k e^{L_j - ell}, kh = k e^{Gamma - b}, qh = q e^b,
+// and the remaining per-block factors e^{P_i - P_{j+1}} (gap), e^{-L_j}
+// (diagonal) are per-channel scalars applied to whole fragments.
+//
+// Precision: dlog_f is a reverse sum of q dq - k dk, whose intra-chunk parts
 // cancel pair by pair (only token pairs straddling t survive).  Rounding the
 // decayed k and q operands of dq and dk independently to bf16 would destroy
-// that cancellation, so those two operands are carried as bf16 hi + lo pairs.
+// that cancellation, so the channel side keeps qo, ko in float32 and feeds
+// them to the MFMA as bf16 hi + lo pairs, and forms q dq, k dk in float32.
 #pragma once
 
 #include "common.h"
+#include "fwd.h"
 
 namespace hgrn2 {
 
 struct BwdArgs {
   int B, T, H;
   const void *q, *k, *v, *log_f, *dy;
-  const float *states;  // [B,H,N+1,D,D]
+  const void *states;  // [B,H,N+1,D,D], input dtype
   const float *dht;
   void *dq, *dk, *dv, *dlog_f;
   float *dh0;
@@ -47,47 +61,59 @@ struct BwdCfg {
   static constexpr int NW = D / 16;
   static constexpr int NT = NW * 64;
   static constexpr int NB = C / 16;
+  static constexpr int NPAIR = NB * (NB + 1) / 2;
   static constexpr int CB = D / 16;
   static constexpr int KSD = (D + 31) / 32;
   static constexpr int KSC = (C + 31) / 32;
   static constexpr int EPV = 16 / (int)sizeof(TIn);
-  static constexpr int LDQ = D + EPV;
-  static constexpr int LDL = D + 4;
-  static constexpr int LDLAM = D + EPV;
-  static constexpr int LDA = C + EPV;
+  static constexpr int LDN = D + EPV;   // [token][channel] rows
+  static constexpr int LDA = C + EPV;   // [token][token] rows
+  static constexpr int LDT = C + 4;     // float32 [channel][token] rows
+  static constexpr int LDL = D + 4;     // float32 [token][channel] rows
   static constexpr int VQ = C * D / EPV;
   static constexpr int NVQ = (VQ + NT - 1) / NT;
-  struct Smem {
-    TIn q[C][LDQ];
-    TIn k[C][LDQ];
-    TIn v[C][LDQ];
-    TIn dy[C][LDQ];
-    float l[C][LDL];
-    TIn lamT[D][LDLAM];   // Lam^T[j][c] of the chunk being processed
-    TIn dA[C][LDA];       // dA[t][s], causal
-    TIn At[C][LDA];       // A^T[s][t], causal
+  struct SmemC {                 // channel side
+    float lT[D][LDT];            // ell, channel-major
+    float qoT[D][LDT];           // q e^{ell}
+    float koT[D][LDT];           // k e^{L_j - ell}
+    TIn v[C][LDN];
+    TIn dy[C][LDN];
+    TIn dA[C][LDA];              // dA[t][s], causal
     float Lb[NB][D];
     float Pb[NB + 1][D];
     int flags;
   };
+  struct SmemV {                 // value side
+    float l[C][LDL];             // ell, token-major
+    TIn qo[C][LDN];              // q e^{ell}
+    TIn ko[C][LDN];              // k e^{L_j - ell}
+    TIn kh[C][LDN];              // k e^{Gamma - b}
+    TIn qhT[D][LDA];             // (q e^b)^T
+    TIn dy[C][LDN];
+    TIn At[C][LDA];              // A^T[s][t], causal
+    float Lb[NB][D];
+    float Pb[NB + 1][D];
+    float gp[NPAIR][D];          // gap factors of the score blocks
+    int flags;
+  };
+  union Smem {
+    SmemC c;
+    SmemV v;
+  };
   static constexpr bool fits = sizeof(Smem) <= 160 * 1024;  // LDS per workgroup on gfx950
 };
 
+// ---------------------------------------------------------------- channel side
 template <typename TIn, int D, int C>
-__global__ __launch_bounds__(4 * D) void hgrn2_bwd_kernel(BwdArgs args) {
+__device__ __forceinline__ void bwd_channel_side(const BwdArgs &args, typename BwdCfg<TIn, D, C>::SmemC &sm,
+                                                 int b, int h) {
   using Cfg = BwdCfg<TIn, D, C>;
-  constexpr int NW = Cfg::NW, NT = Cfg::NT, NB = Cfg::NB, CB = Cfg::CB, KSD = Cfg::KSD,
-                KSC = Cfg::KSC, EPV = Cfg::EPV;
-  __shared__ typename Cfg::Smem sm;
-
-  const int B = args.B, T = args.T, H = args.H, N = args.N;
-  const int bh = blockIdx.x;
-  if (bh >= B * H) return;
-  const int b = bh / H, h = bh % H;
+  constexpr int NT = Cfg::NT, NB = Cfg::NB, CB = Cfg::CB, KSD = Cfg::KSD, KSC = Cfg::KSC,
+                EPV = Cfg::EPV, NW = Cfg::NW, NPAIR = Cfg::NPAIR;
+  const int T = args.T, H = args.H, N = args.N;
+  const int bh = b * H + h;
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, n16 = lane & 15, g = lane >> 4;
-  const int cw = w * 16 + n16;  // this lane's channel (dq, dk, dlog_f, Lam^T column)
-  const int jw = w * 16 + n16;  // this lane's value column (dv)
+  const int w = tid >> 6;
 
   const TIn *gq = (const TIn *)args.q;
   const TIn *gk = (const TIn *)args.k;
@@ -96,50 +122,44 @@ __global__ __launch_bounds__(4 * D) void hgrn2_bwd_kernel(BwdArgs args) {
   const TIn *gdy = (const TIn *)args.dy;
   TIn *gdq = (TIn *)args.dq;
   TIn *gdk = (TIn *)args.dk;
-  TIn *gdv = (TIn *)args.dv;
   TIn *gdl = (TIn *)args.dlog_f;
   const size_t SS = (size_t)D * D;
-  const float *st_base = args.states + (size_t)bh * (N + 1) * SS;
+  const TIn *st_base = (const TIn *)args.states + (size_t)bh * (N + 1) * SS;
+  auto tok = [&](int t) { return (((size_t)b * T + t) * H + h) * D; };
 
-  // Channel-row fragment of a state, in the value-column order of the Lam^T
-  // accumulators: slot x of k step ks is column j = 16(2ks + x/4) + 4g + x%4.
-  auto load_state_frag = [&](const float *St, Frag *f) {
+  // Row cw of a state, in the value-column order of the Lam^T accumulators:
+  // slot x of k step ks is column j = 16(2ks + x/4) + 4g + x%4.
+  auto load_state_frag = [&](const TIn *St, Frag *f) {
+    const int lane = opaque(tid & 63), n16 = lane & 15, g = lane >> 4, cw = w * 16 + n16;
 #pragma unroll
-    for (int ks = 0; ks < KSD; ++ks) {
+    for (int ks = 0; ks < KSD; ++ks)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int jb = 2 * ks + half;
-        if (jb < CB) {
-          const float4 u = *(const float4 *)(St + (size_t)cw * D + jb * 16 + 4 * g);
-          f[ks].v[4 * half + 0] = u.x;
-          f[ks].v[4 * half + 1] = u.y;
-          f[ks].v[4 * half + 2] = u.z;
-          f[ks].v[4 * half + 3] = u.w;
-        } else {
 #pragma unroll
-          for (int x = 0; x < 4; ++x) f[ks].v[4 * half + x] = 0.f;
-        }
+        for (int x = 0; x < 4; ++x)
+          f[ks].v[4 * half + x] = (jb < CB) ? to_f32(St[(size_t)cw * D + jb * 16 + 4 * g + x]) : 0.f;
       }
-    }
   };
 
-  // ---- adjoint Lam^T: tile jb holds rows j = 16jb + 4g + r, column c = cw
-  f32x4_t Lam[CB];
+  // Lam^T: tile jb holds rows j = 16jb + 4g + r, column c = cw.
+  f32x4_t LamT[CB];
+  {
+    const int lane = tid & 63, n16 = lane & 15, g = lane >> 4, cw = w * 16 + n16;
 #pragma unroll
-  for (int jb = 0; jb < CB; ++jb)
+    for (int jb = 0; jb < CB; ++jb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      Lam[jb][r] = args.dht ? args.dht[(size_t)bh * SS + (size_t)cw * D + jb * 16 + 4 * g + r] : 0.f;
-
-  // carry = rowsum(S_end * Lam) for the chunk about to be processed
-  auto rowsum = [&](const Frag *Sf) {
+      for (int r = 0; r < 4; ++r)
+        LamT[jb][r] = args.dht ? args.dht[(size_t)bh * SS + (size_t)cw * D + jb * 16 + 4 * g + r] : 0.f;
+  }
+  auto rowsum = [&](const Frag *Sf) {  // sum_j S[cw][j] Lam[cw][j]
     float a = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KSD; ++ks)
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
         const int jb = 2 * ks + (x >> 2);
-        if (jb < CB) a += Sf[ks].v[x] * Lam[jb][x & 3];
+        if (jb < CB) a += Sf[ks].v[x] * LamT[jb][x & 3];
       }
     a += __shfl_xor(a, 16);
     a += __shfl_xor(a, 32);
@@ -163,7 +183,7 @@ __global__ __launch_bounds__(4 * D) void hgrn2_bwd_kernel(BwdArgs args) {
       uint4 z = make_uint4(0, 0, 0, 0);
       pq[it] = pk[it] = pv[it] = pd[it] = pl[it] = z;
       if (idx < Cfg::VQ && row < len) {
-        const size_t off = (((size_t)b * T + t0 + row) * H + h) * D + col;
+        const size_t off = tok(t0 + row) + col;
         pq[it] = *(const uint4 *)(gq + off);
         pk[it] = *(const uint4 *)(gk + off);
         pv[it] = *(const uint4 *)(gv + off);
@@ -177,380 +197,307 @@ __global__ __launch_bounds__(4 * D) void hgrn2_bwd_kernel(BwdArgs args) {
   for (int n = N - 1; n >= 0; --n) {
     const int t0 = n * C;
     const int len = min(C, T - t0);
-    __syncthreads();
-#pragma unroll
-    for (int it = 0; it < Cfg::NVQ; ++it) {
-      const int idx = tid + it * NT;
-      if (idx < Cfg::VQ) {
-        const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
-        *(uint4 *)&sm.q[row][col] = pq[it];
-        *(uint4 *)&sm.k[row][col] = pk[it];
-        *(uint4 *)&sm.v[row][col] = pv[it];
-        *(uint4 *)&sm.dy[row][col] = pd[it];
-        float f[EPV];
-        Vec<TIn>::unpack(pl[it], f);
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) sm.l[row][col + e] = floor_logf(f[e]);
-      }
-    }
-    // Lam^T (the adjoint entering this chunk from the right) -> LDS
-#pragma unroll
-    for (int jb = 0; jb < CB; ++jb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sm.lamT[jb * 16 + 4 * g + r][cw] = from_f32<TIn>(Lam[jb][r]);
-    if (tid == 0) sm.flags = 0;
-    __syncthreads();
-    if (n > 0) prefetch(n - 1);
     Frag Sprev[KSD];  // S at the start of this chunk (boundary state n)
     load_state_frag(st_base + (size_t)n * SS, Sprev);
 
-    // ---- block-local prefixes
+    // ================= preparation =================
+    __syncthreads();
     {
-      int fl = 0;
-      for (int p = tid; p < NB * D; p += NT) {
-        const int i = p / D, c = p % D;
-        float acc = 0.f;
+      const int tid = opaque(threadIdx.x);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          acc += sm.l[i * 16 + r][c];
-          sm.l[i * 16 + r][c] = acc;
+      for (int it = 0; it < Cfg::NVQ; ++it) {
+        const int idx = tid + it * NT;
+        if (idx < Cfg::VQ) {
+          const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
+          *(uint4 *)&sm.v[row][col] = pv[it];
+          *(uint4 *)&sm.dy[row][col] = pd[it];
+          float f[EPV];
+          Vec<TIn>::unpack(pl[it], f);
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) sm.lT[col + e][row] = floor_logf(f[e]);
         }
-        sm.Lb[i][c] = acc;
-        if (-acc > kDiagLimit) fl |= 1 << i;
       }
-      if (fl) atomicOr(&sm.flags, fl);
-    }
-    __syncthreads();
-    for (int c = tid; c < D; c += NT) {
-      float s = 0.f;
+      if (tid == 0) sm.flags = 0;
+      __syncthreads();
+      {  // block-local inclusive prefixes along tokens, block totals, flags
+        int fl = 0;
+        for (int p = tid; p < NB * D; p += NT) {
+          const int i = p / D, c = p % D;
+          float acc = 0.f;
 #pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        sm.Pb[i][c] = s;
-        s += sm.Lb[i][c];
+          for (int u4 = 0; u4 < 4; ++u4) {
+            float4 *pp = (float4 *)&sm.lT[c][i * 16 + 4 * u4];
+            float4 x = *pp;
+            acc += x.x;
+            x.x = acc;
+            acc += x.y;
+            x.y = acc;
+            acc += x.z;
+            x.z = acc;
+            acc += x.w;
+            x.w = acc;
+            *pp = x;
+          }
+          sm.Lb[i][c] = acc;
+          if (-acc > kDiagLimit) fl |= 1 << i;
+        }
+        if (fl) atomicOr(&sm.flags, fl);
       }
-      sm.Pb[NB][c] = s;
+      __syncthreads();
+      for (int c = tid; c < D; c += NT) {
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          sm.Pb[i][c] = s;
+          s += sm.Lb[i][c];
+        }
+        sm.Pb[NB][c] = s;
+      }
+#pragma unroll
+      for (int it = 0; it < Cfg::NVQ; ++it) {
+        const int idx = tid + it * NT;
+        if (idx < Cfg::VQ) {
+          const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
+          const int jb = row >> 4;
+          float fq[EPV], fk[EPV];
+          Vec<TIn>::unpack(pq[it], fq);
+          Vec<TIn>::unpack(pk[it], fk);
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) {
+            const int c = col + e;
+            const float l = sm.lT[c][row];
+            sm.qoT[c][row] = fq[e] * __expf(l);
+            sm.koT[c][row] = fk[e] * __expf(sm.Lb[jb][c] - l);
+          }
+        }
+      }
     }
+    const int flags = sm.flags;  // final since the barrier after the prefix pass
     __syncthreads();
-    const int flags = sm.flags;
+    if (n > 0) prefetch(n - 1);  // in flight while this chunk computes
 
-    // ---- dA (from dA^T tiles = V dY^T) and A^T (from A tiles = Q~ K~^T)
-    constexpr int NPAIR = NB * (NB + 1) / 2;
-    for (int job = w; job < 2 * NPAIR; job += NW) {
-      const int pi = job % NPAIR;
+    // ================= dA tiles (from dA^T = V dY^T) =================
+    for (int pi = w; pi < NPAIR; pi += NW) {
+      const int lane = opaque(tid & 63), n16 = lane & 15, g = lane >> 4;
       int ib = 0, jb = pi;  // t block ib >= s block jb
       while (jb > ib) {
         jb -= ib + 1;
         ++ib;
       }
+      const int s_row = jb * 16 + n16, t_col = ib * 16 + n16;
       f32x4_t acc;
       acc_zero(acc);
-      if (job < NPAIR) {
-        // dA^T tile: rows s in block jb (A-operand V[s][:]), columns t in block ib (B-operand dY[t][:])
-        const int s_row = jb * 16 + n16, t_col = ib * 16 + n16;
 #pragma unroll
-        for (int ks = 0; ks < KSD; ++ks) {
-          const int c0 = ks * 32 + 8 * g;
-          Frag fa, fb;
-          if (c0 < D) {
+      for (int ks = 0; ks < KSD; ++ks) {
+        const int c0 = ks * 32 + 8 * g;  // D = 16: lanes with c0 >= D feed zeros (the MFMA runs on the whole wave)
+        mma(acc, c0 < D ? ld8(&sm.v[s_row][c0]) : pfrag_zero<TIn>(),
+            c0 < D ? ld8(&sm.dy[t_col][c0]) : pfrag_zero<TIn>());
+      }
 #pragma unroll
-            for (int x = 0; x < 8; ++x) {
-              fa.v[x] = to_f32(sm.v[s_row][c0 + x]);
-              fb.v[x] = to_f32(sm.dy[t_col][c0 + x]);
-            }
-          } else {
-            frag_zero(fa);
-            frag_zero(fb);
-          }
-          Mma<TIn>::run(acc, fa, fb);
-        }
-        // lane holds dA^T[s = 16jb + 4g + r][t = t_col] -> dA[t][s..s+3]
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int s = jb * 16 + 4 * g + r;
-          sm.dA[t_col][s] = from_f32<TIn>((jb < ib || s <= t_col) ? acc[r] : 0.f);
-        }
-      } else {
-        // A tile: rows t in block ib (A-operand q e^{ell}), columns s in block jb
-        const int t_row = ib * 16 + n16, s_col = jb * 16 + n16;
-        const bool direct = (jb == ib) && ((flags >> ib) & 1);
-        if (!direct) {
-#pragma unroll
-          for (int ks = 0; ks < KSD; ++ks) {
-            const int c0 = ks * 32 + 8 * g;
-            Frag fa, fb;
-            if (c0 < D) {
-#pragma unroll
-              for (int x = 0; x < 8; ++x) {
-                const int c = c0 + x;
-                const float eK = (jb < ib) ? (sm.Lb[jb][c] - sm.l[s_col][c]) + (sm.Pb[ib][c] - sm.Pb[jb + 1][c])
-                                           : -sm.l[s_col][c];
-                fa.v[x] = to_f32(sm.q[t_row][c]) * __expf(sm.l[t_row][c]);
-                fb.v[x] = to_f32(sm.k[s_col][c]) * __expf(eK);
-              }
-            } else {
-              frag_zero(fa);
-              frag_zero(fb);
-            }
-            Mma<TIn>::run(acc, fa, fb);
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = ib * 16 + 4 * g + r;
-            float a = 0.f;
-            if (s_col <= t)
-              for (int c = 0; c < D; ++c)
-                a += to_f32(sm.q[t][c]) * to_f32(sm.k[s_col][c]) * __expf(sm.l[t][c] - sm.l[s_col][c]);
-            acc[r] = a;
-          }
-        }
-        // lane holds A[t = 16ib + 4g + r][s = s_col] -> A^T[s][t..t+3]
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = ib * 16 + 4 * g + r;
-          sm.At[s_col][t] = from_f32<TIn>((jb < ib || s_col <= t) ? acc[r] : 0.f);
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int s = jb * 16 + 4 * g + r;
+        sm.dA[t_col][s] = from_f32<TIn>((jb < ib || s <= t_col) ? acc[r] : 0.f);
       }
     }
     __syncthreads();
 
-    // ---- dq for channels cw (rows t in block i)
-    f32x4_t dq[NB];
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      acc_zero(dq[i]);
-      const int t = i * 16 + n16;
-      // inter: dY[t][j] S_prev[c][j], j in the Lam^T accumulator order
-#pragma unroll
-      for (int ks = 0; ks < KSD; ++ks) {
-        Frag fa;
-#pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          const int jb = 2 * ks + (x >> 2);
-          fa.v[x] = (jb < CB) ? to_f32(sm.dy[t][jb * 16 + 4 * g + (x & 3)]) : 0.f;
-        }
-        Mma<TIn>::run(dq[i], fa, Sprev[ks]);
-      }
-      const float eP = __expf(sm.Pb[i][cw]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dq[i][r] *= eP;
-      // intra: sum_s dA[t][s] k_s e^{P_i - b_s}, s < 16(i+1)
-      const bool direct = (flags >> i) & 1;
-#pragma unroll
-      for (int ks = 0; ks < KSC; ++ks) {
-        if (ks * 32 < 16 * (i + 1)) {
-          Frag fa, fb;
-#pragma unroll
-          for (int x = 0; x < 8; ++x) {
-            const int s = ks * 32 + 8 * g + x;
-            const int sb = s >> 4;
-            const bool ok = s < 16 * (i + 1) && s < C && !(direct && sb == i);
-            fa.v[x] = ok ? to_f32(sm.dA[t][s]) : 0.f;
-            float e = 0.f;
-            if (ok) {
-              const float ex = (sb < i) ? (sm.Lb[sb][cw] - sm.l[s][cw]) + (sm.Pb[i][cw] - sm.Pb[sb + 1][cw])
-                                        : -sm.l[s][cw];
-              e = to_f32(sm.k[s][cw]) * __expf(ex);
-            }
-            fb.v[x] = e;
-          }
-          MmaSplitB<TIn>::run(dq[i], fa, fb);
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tt = i * 16 + 4 * g + r;
-        dq[i][r] *= __expf(sm.l[tt][cw]);
-        if (direct) {
-          float a = 0.f;
-          for (int s = i * 16; s <= tt; ++s)
-            a += to_f32(sm.dA[tt][s]) * to_f32(sm.k[s][cw]) * __expf(sm.l[tt][cw] - sm.l[s][cw]);
-          dq[i][r] += a;
-        }
-      }
-    }
-
-    // ---- dk for channels cw (rows s in block j)
-    f32x4_t dk[NB];
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      acc_zero(dk[j]);
-      const int s = j * 16 + n16;
-      // inter: V[s][j'] Lam[c][j'] with Lam^T accumulators as the B operand
-#pragma unroll
-      for (int ks = 0; ks < KSD; ++ks) {
-        Frag fa, fb;
-#pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          const int jb = 2 * ks + (x >> 2);
-          if (jb < CB) {
-            fa.v[x] = to_f32(sm.v[s][jb * 16 + 4 * g + (x & 3)]);
-            fb.v[x] = Lam[jb][x & 3];
-          } else {
-            fa.v[x] = 0.f;
-            fb.v[x] = 0.f;
-          }
-        }
-        Mma<TIn>::run(dk[j], fa, fb);
-      }
-      const float eG = __expf(sm.Pb[NB][cw] - sm.Pb[j + 1][cw]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dk[j][r] *= eG;
-      // intra: sum_{t >= 16j} dA^T[s][t] q_t e^{b_t - E_j}
-      const bool direct = (flags >> j) & 1;
-#pragma unroll
-      for (int ks = 0; ks < KSC; ++ks) {
-        if (ks * 32 + 32 > 16 * j) {
-          Frag fa, fb;
-#pragma unroll
-          for (int x = 0; x < 8; ++x) {
-            const int t = ks * 32 + 8 * g + x;
-            const int tb = t >> 4;
-            const bool ok = t >= 16 * j && t < C && !(direct && tb == j);
-            fa.v[x] = ok ? to_f32(sm.dA[t][s]) : 0.f;
-            float e = 0.f;
-            if (ok) {
-              const float ex = (tb > j) ? sm.l[t][cw] + (sm.Pb[tb][cw] - sm.Pb[j + 1][cw])
-                                        : sm.l[t][cw] - sm.Lb[j][cw];
-              e = to_f32(sm.q[t][cw]) * __expf(ex);
-            }
-            fb.v[x] = e;
-          }
-          MmaSplitB<TIn>::run(dk[j], fa, fb);
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int ss = j * 16 + 4 * g + r;
-        dk[j][r] *= __expf(sm.Lb[j][cw] - sm.l[ss][cw]);
-        if (direct) {
-          float a = 0.f;
-          for (int t = ss; t < j * 16 + 16; ++t)
-            a += to_f32(sm.dA[t][ss]) * to_f32(sm.q[t][cw]) * __expf(sm.l[t][cw] - sm.l[ss][cw]);
-          dk[j][r] += a;
-        }
-      }
-    }
-
-    // ---- dv for value columns jw (rows s in block j)
-    Frag fdyT[KSC];  // dY^T fragments: column jw, k = token
-#pragma unroll
-    for (int ks = 0; ks < KSC; ++ks)
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        const int t = ks * 32 + 8 * g + x;
-        fdyT[ks].v[x] = (t < C) ? to_f32(sm.dy[t][jw]) : 0.f;
-      }
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      f32x4_t acc;
-      acc_zero(acc);
-      const int s = j * 16 + n16;
-      // inter: (k e^{Gamma - b})[s][c] Lam[c][jw]
-#pragma unroll
-      for (int ks = 0; ks < KSD; ++ks) {
-        const int c0 = ks * 32 + 8 * g;
-        Frag fa, fb;
-        if (c0 < D) {
-#pragma unroll
-          for (int x = 0; x < 8; ++x) {
-            const int c = c0 + x;
-            const float ex = (sm.Pb[NB][c] - sm.Pb[j + 1][c]) + (sm.Lb[j][c] - sm.l[s][c]);
-            fa.v[x] = to_f32(sm.k[s][c]) * __expf(ex);
-            fb.v[x] = to_f32(sm.lamT[jw][c]);
-          }
-        } else {
-          frag_zero(fa);
-          frag_zero(fb);
-        }
-        Mma<TIn>::run(acc, fa, fb);
-      }
-      // intra: A^T[s][t] dY[t][jw], t >= 16j
-#pragma unroll
-      for (int ks = 0; ks < KSC; ++ks) {
-        if (ks * 32 + 32 > 16 * j) {
-          Frag fa;
-#pragma unroll
-          for (int x = 0; x < 8; ++x) {
-            const int t = ks * 32 + 8 * g + x;
-            fa.v[x] = (t >= 16 * j && t < C) ? to_f32(sm.At[s][t]) : 0.f;
-          }
-          Mma<TIn>::run(acc, fa, fdyT[ks]);
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int ss = j * 16 + 4 * g + r;
-        if (ss < len) gdv[(((size_t)b * T + t0 + ss) * H + h) * D + jw] = from_f32<TIn>(acc[r]);
-      }
-    }
-
-    // ---- dlog_f: reverse cumulative sum of q dq - k dk inside the chunk, plus carry
+    // ================= dq, dk, dlog_f for channel cw =================
+    float u[NB][4];  // q dq - k dk at tokens 16i + 4g + r
     {
+      const int lane = opaque(tid & 63), n16 = lane & 15, g = lane >> 4, cw = w * 16 + n16;
+      PFrag<TIn> SP[KSD];
+#pragma unroll
+      for (int ks = 0; ks < KSD; ++ks) SP[ks] = to_pfrag<TIn>(Sprev[ks]);
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        f32x4_t dq;
+        acc_zero(dq);
+        const int t = i * 16 + n16;
+        // inter: dY[t][j] S_prev[cw][j], j in the accumulator order of S_prev's fragment
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) {
+          const int j0 = 2 * ks * 16 + 4 * g;
+          const int j1 = (2 * ks + 1 < CB) ? j0 + 16 : j0;  // D = 16: slots 4-7 meet zeros of S_prev
+          mma(dq, ld4x2(&sm.dy[t][j0], &sm.dy[t][j1]), SP[ks]);
+        }
+        const float eP = __expf(sm.Pb[i][cw]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dq[r] *= eP;
+        // intra: sum_s dA[t][s] k_s e^{P_i - b_s}, s < 16(i+1)
+        const bool direct = (flags >> i) & 1;
+#pragma unroll
+        for (int ks = 0; ks < KSC; ++ks) {
+          if (ks * 32 < 16 * (i + 1)) {
+            const int s0 = ks * 32 + 8 * g;  // 8 tokens of one 16-block
+            const int sb = s0 >> 4;
+            const bool ok = s0 < 16 * (i + 1) && s0 < C && !(direct && sb == i);
+            Frag fb;
+            PFrag<TIn> fa;
+            if (ok) {
+              const float gap = (sb < i) ? __expf(sm.Pb[i][cw] - sm.Pb[sb + 1][cw]) : __expf(-sm.Lb[i][cw]);
+              fa = ld8(&sm.dA[t][s0]);
+              const float4 k0 = *(const float4 *)&sm.koT[cw][s0];
+              const float4 k1 = *(const float4 *)&sm.koT[cw][s0 + 4];
+              fb.v[0] = k0.x * gap; fb.v[1] = k0.y * gap; fb.v[2] = k0.z * gap; fb.v[3] = k0.w * gap;
+              fb.v[4] = k1.x * gap; fb.v[5] = k1.y * gap; fb.v[6] = k1.z * gap; fb.v[7] = k1.w * gap;
+            } else {
+              fa = pfrag_zero<TIn>();
+              frag_zero(fb);
+            }
+            mma_split(dq, fa, fb);
+          }
+        }
+        const float4 l4 = *(const float4 *)&sm.lT[cw][i * 16 + 4 * g];
+        const float4 q4 = *(const float4 *)&sm.qoT[cw][i * 16 + 4 * g];
+        const float ll[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float qq[4] = {q4.x, q4.y, q4.z, q4.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tt = i * 16 + 4 * g + r;
+          u[i][r] = qq[r] * dq[r];  // q dq = (q e^{ell}) X
+          float val = dq[r] * __expf(ll[r]);
+          if (direct && tt < len) {
+            float a = 0.f;
+            for (int s = i * 16; s <= tt; ++s)
+              a += to_f32(sm.dA[tt][s]) * to_f32(gk[tok(t0 + s) + cw]) * __expf(ll[r] - sm.lT[cw][s]);
+            val += a;
+            u[i][r] += to_f32(gq[tok(t0 + tt) + cw]) * a;
+          }
+          if (tt < len) gdq[tok(t0 + tt) + cw] = from_f32<TIn>(val);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    {
+      const int lane = opaque(tid & 63), n16 = lane & 15, g = lane >> 4, cw = w * 16 + n16;
+      PFrag<TIn> LP[KSD];  // Lam^T as B operand, j in accumulator order
+#pragma unroll
+      for (int ks = 0; ks < KSD; ++ks) {
+        Frag f;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const int jb = 2 * ks + (x >> 2);
+          f.v[x] = (jb < CB) ? LamT[jb][x & 3] : 0.f;
+        }
+        LP[ks] = to_pfrag<TIn>(f);
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        f32x4_t dk;
+        acc_zero(dk);
+        const int s = j * 16 + n16;
+        // inter: V[s][j'] Lam[cw][j']
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) {
+          const int j0 = 2 * ks * 16 + 4 * g;
+          const int j1 = (2 * ks + 1 < CB) ? j0 + 16 : j0;
+          mma(dk, ld4x2(&sm.v[s][j0], &sm.v[s][j1]), LP[ks]);
+        }
+        const float eG = __expf(sm.Pb[NB][cw] - sm.Pb[j + 1][cw]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dk[r] *= eG;
+        // intra: sum_{t >= 16j} dA^T[s][t] q_t e^{b_t - E_j}
+        const bool direct = (flags >> j) & 1;
+#pragma unroll
+        for (int ks = 0; ks < KSC; ++ks) {
+          if (ks * 32 + 32 > 16 * j) {
+            const int tq0 = ks * 32 + 8 * g;
+            const int tb = tq0 >> 4;
+            const bool ok = tq0 >= 16 * j && tq0 < C && !(direct && tb == j);
+            Frag fa, fb;
+            if (ok) {
+              const float gap = (tb > j) ? __expf(sm.Pb[tb][cw] - sm.Pb[j + 1][cw]) : __expf(-sm.Lb[j][cw]);
+              const float4 q0 = *(const float4 *)&sm.qoT[cw][tq0];
+              const float4 q1 = *(const float4 *)&sm.qoT[cw][tq0 + 4];
+              fb.v[0] = q0.x * gap; fb.v[1] = q0.y * gap; fb.v[2] = q0.z * gap; fb.v[3] = q0.w * gap;
+              fb.v[4] = q1.x * gap; fb.v[5] = q1.y * gap; fb.v[6] = q1.z * gap; fb.v[7] = q1.w * gap;
+#pragma unroll
+              for (int x = 0; x < 8; ++x) fa.v[x] = to_f32(sm.dA[tq0 + x][s]);
+            } else {
+              frag_zero(fa);
+              frag_zero(fb);
+            }
+            mma_split(dk, to_pfrag<TIn>(fa), fb);
+          }
+        }
+        const float4 l4 = *(const float4 *)&sm.lT[cw][j * 16 + 4 * g];
+        const float4 k4 = *(const float4 *)&sm.koT[cw][j * 16 + 4 * g];
+        const float ll[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float kk[4] = {k4.x, k4.y, k4.z, k4.w};
+        const float Lj = sm.Lb[j][cw];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int ss = j * 16 + 4 * g + r;
+          u[j][r] -= kk[r] * dk[r];  // k dk = (k e^{L_j - ell}) Z
+          float val = dk[r] * __expf(Lj - ll[r]);
+          if (direct && ss < len) {
+            float a = 0.f;
+            for (int t = ss; t < j * 16 + 16; ++t)
+              a += to_f32(sm.dA[t][ss]) * to_f32(gq[tok(t0 + t) + cw]) * __expf(sm.lT[cw][t] - ll[r]);
+            val += a;
+            u[j][r] -= to_f32(gk[tok(t0 + ss) + cw]) * a;
+          }
+          if (ss < len) gdk[tok(t0 + ss) + cw] = from_f32<TIn>(val);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    {  // dlog_f: reverse cumulative sum of u inside the chunk, plus the carry
+      const int lane = opaque(tid & 63), n16 = lane & 15, g = lane >> 4, cw = w * 16 + n16;
       float suf[NB][4], tot[NB];
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
         float run = 0.f;
 #pragma unroll
         for (int r = 3; r >= 0; --r) {
-          const int t = i * 16 + 4 * g + r;
-          run += to_f32(sm.q[t][cw]) * dq[i][r] - to_f32(sm.k[t][cw]) * dk[i][r];
+          run += u[i][r];
           suf[i][r] = run;
         }
         tot[i] = run;
       }
-      float above[NB], blk[NB];
-#pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        float a = 0.f, s = 0.f;
-#pragma unroll
-        for (int gp = 0; gp < 4; ++gp) {
-          const float u = __shfl(tot[i], n16 + 16 * gp);
-          s += u;
-          if (gp > g) a += u;
-        }
-        above[i] = a;
-        blk[i] = s;
-      }
       float rest = carry;
 #pragma unroll
       for (int i = NB - 1; i >= 0; --i) {
+        float above = 0.f, blk = 0.f;
+#pragma unroll
+        for (int gp = 0; gp < 4; ++gp) {
+          const float x = __shfl(tot[i], n16 + 16 * gp);
+          blk += x;
+          if (gp > g) above += x;
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = i * 16 + 4 * g + r;
-          if (t < len)
-            gdl[(((size_t)b * T + t0 + t) * H + h) * D + cw] = from_f32<TIn>(suf[i][r] + above[i] + rest);
+          if (t < len) gdl[tok(t0 + t) + cw] = from_f32<TIn>(suf[i][r] + above + rest);
         }
-        rest += blk[i];
+        rest += blk;
       }
     }
-#pragma unroll
-    for (int i = 0; i < NB; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = i * 16 + 4 * g + r;
-        if (t < len) {
-          const size_t off = (((size_t)b * T + t0 + t) * H + h) * D + cw;
-          gdq[off] = from_f32<TIn>(dq[i][r]);
-          gdk[off] = from_f32<TIn>(dk[i][r]);
-        }
-      }
 
-    // ---- Lam^T <- e^Gamma Lam^T + dY^T (q e^b)
+    // ================= Lam^T <- e^{Gamma} Lam^T + dY^T (q e^b) =================
     {
+      const int lane = opaque(tid & 63), n16 = lane & 15, g = lane >> 4, cw = w * 16 + n16;
       const float eG = __expf(sm.Pb[NB][cw]);
-      Frag fqh[KSC];  // (q e^b)^T fragments: column cw, k = token
+      PFrag<TIn> fqh[KSC];  // (q e^b)^T fragments: column cw, k = token
 #pragma unroll
-      for (int ks = 0; ks < KSC; ++ks)
-#pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          const int t = ks * 32 + 8 * g + x;
-          fqh[ks].v[x] = (t < C) ? to_f32(sm.q[t][cw]) * __expf(sm.Pb[t >> 4][cw] + sm.l[t][cw]) : 0.f;
+      for (int ks = 0; ks < KSC; ++ks) {
+        const int tq0 = ks * 32 + 8 * g;
+        Frag f;
+        if (tq0 < C) {
+          const float eP = __expf(sm.Pb[tq0 >> 4][cw]);
+          const float4 q0 = *(const float4 *)&sm.qoT[cw][tq0];
+          const float4 q1 = *(const float4 *)&sm.qoT[cw][tq0 + 4];
+          f.v[0] = q0.x * eP; f.v[1] = q0.y * eP; f.v[2] = q0.z * eP; f.v[3] = q0.w * eP;
+          f.v[4] = q1.x * eP; f.v[5] = q1.y * eP; f.v[6] = q1.z * eP; f.v[7] = q1.w * eP;
+        } else {
+          frag_zero(f);
         }
+        fqh[ks] = to_pfrag<TIn>(f);
+      }
 #pragma unroll
       for (int jb = 0; jb < CB; ++jb) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Lam[jb][r] *= eG;
+        for (int r = 0; r < 4; ++r) LamT[jb][r] *= eG;
         const int jrow = jb * 16 + n16;
 #pragma unroll
         for (int ks = 0; ks < KSC; ++ks) {
@@ -560,25 +507,313 @@ __global__ __launch_bounds__(4 * D) void hgrn2_bwd_kernel(BwdArgs args) {
             const int t = ks * 32 + 8 * g + x;
             fa.v[x] = (t < C) ? to_f32(sm.dy[t][jrow]) : 0.f;
           }
-          Mma<TIn>::run(Lam[jb], fa, fqh[ks]);
+          mma(LamT[jb], to_pfrag<TIn>(fa), fqh[ks]);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    carry = rowsum(Sprev);
+    if (n > 0) carry = rowsum(Sprev);
   }
   if (args.dh0) {
+    const int lane = tid & 63, n16 = lane & 15, g = lane >> 4, cw = w * 16 + n16;
 #pragma unroll
     for (int jb = 0; jb < CB; ++jb)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        args.dh0[(size_t)bh * SS + (size_t)cw * D + jb * 16 + 4 * g + r] = Lam[jb][r];
+        args.dh0[(size_t)bh * SS + (size_t)cw * D + jb * 16 + 4 * g + r] = LamT[jb][r];
   }
+}
+
+// ------------------------------------------------------------------ value side
+template <typename TIn, int D, int C>
+__device__ __forceinline__ void bwd_value_side(const BwdArgs &args, typename BwdCfg<TIn, D, C>::SmemV &sm,
+                                               int b, int h) {
+  using Cfg = BwdCfg<TIn, D, C>;
+  constexpr int NT = Cfg::NT, NB = Cfg::NB, CB = Cfg::CB, KSD = Cfg::KSD, KSC = Cfg::KSC,
+                EPV = Cfg::EPV, NW = Cfg::NW, NPAIR = Cfg::NPAIR;
+  const int T = args.T, H = args.H, N = args.N;
+  const int bh = b * H + h;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+
+  const TIn *gq = (const TIn *)args.q;
+  const TIn *gk = (const TIn *)args.k;
+  const TIn *gl = (const TIn *)args.log_f;
+  const TIn *gdy = (const TIn *)args.dy;
+  TIn *gdv = (TIn *)args.dv;
+  const size_t SS = (size_t)D * D;
+  auto tok = [&](int t) { return (((size_t)b * T + t) * H + h) * D; };
+
+  // Lam: tile cb holds rows c = 16cb + 4g + r, column j = jw.
+  f32x4_t Lam[CB];
+  {
+    const int lane = tid & 63, n16 = lane & 15, g = lane >> 4, jw = w * 16 + n16;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        Lam[cb][r] = args.dht ? args.dht[(size_t)bh * SS + (size_t)(cb * 16 + 4 * g + r) * D + jw] : 0.f;
+  }
+
+  uint4 pq[Cfg::NVQ], pk[Cfg::NVQ], pd[Cfg::NVQ], pl[Cfg::NVQ];
+  auto prefetch = [&](int n) {
+    const int t0 = n * C;
+    const int len = min(C, T - t0);
+#pragma unroll
+    for (int it = 0; it < Cfg::NVQ; ++it) {
+      const int idx = tid + it * NT;
+      const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
+      uint4 z = make_uint4(0, 0, 0, 0);
+      pq[it] = pk[it] = pd[it] = pl[it] = z;
+      if (idx < Cfg::VQ && row < len) {
+        const size_t off = tok(t0 + row) + col;
+        pq[it] = *(const uint4 *)(gq + off);
+        pk[it] = *(const uint4 *)(gk + off);
+        pd[it] = *(const uint4 *)(gdy + off);
+        pl[it] = *(const uint4 *)(gl + off);
+      }
+    }
+  };
+  prefetch(N - 1);
+
+  for (int n = N - 1; n >= 0; --n) {
+    const int t0 = n * C;
+    const int len = min(C, T - t0);
+
+    // ================= preparation =================
+    __syncthreads();
+    {
+      const int tid = opaque(threadIdx.x);
+#pragma unroll
+      for (int it = 0; it < Cfg::NVQ; ++it) {
+        const int idx = tid + it * NT;
+        if (idx < Cfg::VQ) {
+          const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
+          *(uint4 *)&sm.dy[row][col] = pd[it];
+          float f[EPV];
+          Vec<TIn>::unpack(pl[it], f);
+#pragma unroll
+          for (int e = 0; e < EPV; e += 4)
+            *(float4 *)&sm.l[row][col + e] =
+                make_float4(floor_logf(f[e]), floor_logf(f[e + 1]), floor_logf(f[e + 2]), floor_logf(f[e + 3]));
+        }
+      }
+      if (tid == 0) sm.flags = 0;
+      __syncthreads();
+      {
+        int fl = 0;
+        for (int p = tid; p < NB * D; p += NT) {
+          const int i = p / D, c = p % D;
+          float acc = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            acc += sm.l[i * 16 + r][c];
+            sm.l[i * 16 + r][c] = acc;
+          }
+          sm.Lb[i][c] = acc;
+          if (-acc > kDiagLimit) fl |= 1 << i;
+        }
+        if (fl) atomicOr(&sm.flags, fl);
+      }
+      __syncthreads();
+      for (int c = tid; c < D; c += NT) {
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          sm.Pb[i][c] = s;
+          s += sm.Lb[i][c];
+        }
+        sm.Pb[NB][c] = s;
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+          for (int j = 0; j <= i; ++j)
+            sm.gp[pair_index(i, j)][c] = (j < i) ? __expf(sm.Pb[i][c] - sm.Pb[j + 1][c]) : __expf(-sm.Lb[i][c]);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int it = 0; it < Cfg::NVQ; ++it) {
+        const int idx = tid + it * NT;
+        if (idx < Cfg::VQ) {
+          const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
+          const int jb = row >> 4;
+          float fq[EPV], fk[EPV];
+          Vec<TIn>::unpack(pq[it], fq);
+          Vec<TIn>::unpack(pk[it], fk);
+          TIn oq[EPV], ok[EPV], oh[EPV];
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) {
+            const int c = col + e;
+            const float l = sm.l[row][c];
+            const float ko = fk[e] * __expf(sm.Lb[jb][c] - l);
+            const float qo = fq[e] * __expf(l);
+            oq[e] = from_f32<TIn>(qo);
+            ok[e] = from_f32<TIn>(ko);
+            oh[e] = from_f32<TIn>(ko * __expf(sm.Pb[NB][c] - sm.Pb[jb + 1][c]));
+            sm.qhT[c][row] = from_f32<TIn>(qo * __expf(sm.Pb[jb][c]));
+          }
+          *(uint4 *)&sm.qo[row][col] = *(const uint4 *)oq;
+          *(uint4 *)&sm.ko[row][col] = *(const uint4 *)ok;
+          *(uint4 *)&sm.kh[row][col] = *(const uint4 *)oh;
+        }
+      }
+    }
+    const int flags = sm.flags;  // final since the barrier after the prefix pass
+    __syncthreads();
+    if (n > 0) prefetch(n - 1);
+
+    // ================= A tiles -> A^T =================
+    for (int pi = w; pi < NPAIR; pi += NW) {
+      const int lane = opaque(tid & 63), n16 = lane & 15, g = lane >> 4;
+      int ib = 0, jb = pi;  // t block ib >= s block jb
+      while (jb > ib) {
+        jb -= ib + 1;
+        ++ib;
+      }
+      const int t_row = ib * 16 + n16, s_col = jb * 16 + n16;
+      f32x4_t acc;
+      acc_zero(acc);
+      const bool direct = (jb == ib) && ((flags >> ib) & 1);
+      if (!direct) {
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) {
+          const int c0 = ks * 32 + 8 * g;  // D = 16: lanes with c0 >= D feed zeros
+          Frag fb;
+          PFrag<TIn> fa;
+          if (c0 < D) {
+            float kv[8];
+            Vec<TIn>::unpack(*(const uint4 *)&sm.ko[s_col][c0], kv);
+            if constexpr (EPV == 4) Vec<TIn>::unpack(*(const uint4 *)&sm.ko[s_col][c0 + 4], kv + 4);
+            const float4 g0 = *(const float4 *)&sm.gp[pi][c0];
+            const float4 g1 = *(const float4 *)&sm.gp[pi][c0 + 4];
+            fb.v[0] = kv[0] * g0.x; fb.v[1] = kv[1] * g0.y; fb.v[2] = kv[2] * g0.z; fb.v[3] = kv[3] * g0.w;
+            fb.v[4] = kv[4] * g1.x; fb.v[5] = kv[5] * g1.y; fb.v[6] = kv[6] * g1.z; fb.v[7] = kv[7] * g1.w;
+            fa = ld8(&sm.qo[t_row][c0]);
+          } else {
+            frag_zero(fb);
+            fa = pfrag_zero<TIn>();
+          }
+          mma(acc, fa, to_pfrag<TIn>(fb));
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = ib * 16 + 4 * g + r;
+          float a = 0.f;
+          if (s_col <= t && t < len)
+            for (int c = 0; c < D; ++c)
+              a += to_f32(gq[tok(t0 + t) + c]) * to_f32(gk[tok(t0 + s_col) + c]) *
+                   __expf(sm.l[t][c] - sm.l[s_col][c]);
+          acc[r] = a;
+        }
+      }
+      // lane holds A[t = 16ib + 4g + r][s = s_col] -> A^T[s][t..t+3]
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = ib * 16 + 4 * g + r;
+        sm.At[s_col][t] = from_f32<TIn>((jb < ib || s_col <= t) ? acc[r] : 0.f);
+      }
+    }
+    __syncthreads();
+
+    // ================= dv for value column jw, then Lam update =================
+    {
+      const int lane = opaque(tid & 63), n16 = lane & 15, g = lane >> 4, jw = w * 16 + n16;
+      PFrag<TIn> fdyT[KSC];  // dY^T fragments: column jw, k = token
+#pragma unroll
+      for (int ks = 0; ks < KSC; ++ks) {
+        Frag f;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const int t = ks * 32 + 8 * g + x;
+          f.v[x] = (t < C) ? to_f32(sm.dy[t][jw]) : 0.f;
+        }
+        fdyT[ks] = to_pfrag<TIn>(f);
+      }
+      PFrag<TIn> LP[KSD];  // Lam as B operand, channels in accumulator order
+#pragma unroll
+      for (int ks = 0; ks < KSD; ++ks) {
+        Frag f;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const int cb = 2 * ks + (x >> 2);
+          f.v[x] = (cb < CB) ? Lam[cb][x & 3] : 0.f;
+        }
+        LP[ks] = to_pfrag<TIn>(f);
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        f32x4_t acc;
+        acc_zero(acc);
+        const int s = j * 16 + n16;
+        // inter: (k e^{Gamma - b})[s][c] Lam[c][jw]
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) {
+          const int c0 = 2 * ks * 16 + 4 * g;
+          const int c1 = (2 * ks + 1 < CB) ? c0 + 16 : c0;  // D = 16: slots 4-7 meet zeros of Lam
+          mma(acc, ld4x2(&sm.kh[s][c0], &sm.kh[s][c1]), LP[ks]);
+        }
+        // intra: A^T[s][t] dY[t][jw], t >= 16j
+#pragma unroll
+        for (int ks = 0; ks < KSC; ++ks) {
+          if (ks * 32 + 32 > 16 * j) {
+            const int t0f = ks * 32 + 8 * g;
+            const PFrag<TIn> fa = (t0f >= 16 * j && t0f < C) ? ld8(&sm.At[s][t0f]) : pfrag_zero<TIn>();
+            mma(acc, fa, fdyT[ks]);
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int ss = j * 16 + 4 * g + r;
+          if (ss < len) gdv[tok(t0 + ss) + jw] = from_f32<TIn>(acc[r]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // Lam[c][jw] <- e^{Gamma} Lam + sum_t (q e^b)[t][c] dY[t][jw]
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const float4 g4 = *(const float4 *)&sm.Pb[NB][cb * 16 + 4 * g];
+        Lam[cb][0] *= __expf(g4.x);
+        Lam[cb][1] *= __expf(g4.y);
+        Lam[cb][2] *= __expf(g4.z);
+        Lam[cb][3] *= __expf(g4.w);
+        const int crow = cb * 16 + n16;
+#pragma unroll
+        for (int ks = 0; ks < KSC; ++ks) {
+          const int tq0 = ks * 32 + 8 * g;
+          const PFrag<TIn> fa = (tq0 < C) ? ld8(&sm.qhT[crow][tq0]) : pfrag_zero<TIn>();
+          mma(Lam[cb], fa, fdyT[ks]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+}
+
+template <typename TIn, int D, int C>
+__global__ __launch_bounds__(4 * D) void hgrn2_bwd_kernel(BwdArgs args) {
+  using Cfg = BwdCfg<TIn, D, C>;
+  __shared__ typename Cfg::Smem sm;
+  // Work-group id -> (b, h, side).  The two sides of one (b, h) get ids that
+  // differ by 8, so they land on the same XCD (workgroups are dealt to the
+  // 8 XCDs round-robin) and share its L2 for the chunk tiles both read.
+  const int bid = blockIdx.x;
+  const int grp = bid >> 4, rem = bid & 15;
+  const int side = rem >> 3;
+  const int bh = grp * 8 + (rem & 7);
+  if (bh >= args.B * args.H) return;
+  const int b = bh / args.H, h = bh % args.H;
+  if (side == 0)
+    bwd_channel_side<TIn, D, C>(args, sm.c, b, h);
+  else
+    bwd_value_side<TIn, D, C>(args, sm.v, b, h);
 }
 
 template <typename TIn, int D, int C>
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream) {
   using Cfg = BwdCfg<TIn, D, C>;
-  hipLaunchKernelGGL((hgrn2_bwd_kernel<TIn, D, C>), dim3(a.B * a.H), dim3(Cfg::NT), 0, stream, a);
+  const int groups = (a.B * a.H + 7) / 8;
+  hipLaunchKernelGGL((hgrn2_bwd_kernel<TIn, D, C>), dim3(groups * 16), dim3(Cfg::NT), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -9,6 +9,8 @@
 //                       k(g, slot) works as long as A and B use the same one,
 //                       which lets us feed accumulators back in as operands.
 //   accumulator       : 4 floats per lane, reg r holds D[row = 4g + r][col = n].
+// An MFMA must be issued by the whole wave: lanes without data feed zeros,
+// never skip the instruction under a lane-dependent branch.
 // bf16 operands go through one v_mfma_f32_16x16x32_bf16; float32 operands go
 // through eight v_mfma_f32_16x16x4_f32, slot i in instruction i.
 #pragma once
@@ -139,8 +141,80 @@ __device__ __forceinline__ void mma(f32x4_t &acc, const PFrag<float> &a, const P
   for (int i = 0; i < 8; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x[i], b.x[i], acc, 0, 0, 0);
 }
 
+// Operand loads straight from LDS into MFMA-ready registers.
+// ld8: 8 consecutive elements (16-byte aligned for bf16, 32 for float).
+// ld4x2: slots 0-3 from p0 and 4-7 from p1 (each 4 consecutive elements).
+__device__ __forceinline__ PFrag<bf16_t> ld8(const bf16_t *p) {
+  PFrag<bf16_t> f;
+  f.x = *(const bf16x8_t *)p;
+  return f;
+}
+__device__ __forceinline__ PFrag<float> ld8(const float *p) {
+  PFrag<float> f;
+  const float4 a = ((const float4 *)p)[0], b = ((const float4 *)p)[1];
+  f.x[0] = a.x; f.x[1] = a.y; f.x[2] = a.z; f.x[3] = a.w;
+  f.x[4] = b.x; f.x[5] = b.y; f.x[6] = b.z; f.x[7] = b.w;
+  return f;
+}
+__device__ __forceinline__ PFrag<bf16_t> ld4x2(const bf16_t *p0, const bf16_t *p1) {
+  union {
+    uint2 u[2];
+    bf16x8_t v;
+  } t;
+  t.u[0] = *(const uint2 *)p0;
+  t.u[1] = *(const uint2 *)p1;
+  PFrag<bf16_t> f;
+  f.x = t.v;
+  return f;
+}
+__device__ __forceinline__ PFrag<float> ld4x2(const float *p0, const float *p1) {
+  PFrag<float> f;
+  const float4 a = *(const float4 *)p0, b = *(const float4 *)p1;
+  f.x[0] = a.x; f.x[1] = a.y; f.x[2] = a.z; f.x[3] = a.w;
+  f.x[4] = b.x; f.x[5] = b.y; f.x[6] = b.z; f.x[7] = b.w;
+  return f;
+}
+template <typename Op> __device__ __forceinline__ PFrag<Op> pfrag_zero() {
+  Frag z;
+  frag_zero(z);
+  PFrag<Op> f;
+  f.set(z);
+  return f;
+}
+template <typename Op> __device__ __forceinline__ PFrag<Op> to_pfrag(const Frag &a) {
+  PFrag<Op> f;
+  f.set(a);
+  return f;
+}
+
+// D += A * B with B given in float32 and carried as a bf16 hi + lo pair (see
+// MmaSplitB); A already in MFMA form.
+__device__ __forceinline__ void mma_split(f32x4_t &acc, const PFrag<bf16_t> &a, const Frag &b) {
+  bf16x8_t yh, yl;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    yh[i] = (__bf16)b.v[i];
+    yl[i] = (__bf16)(b.v[i] - (float)yh[i]);
+  }
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.x, yh, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.x, yl, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma_split(f32x4_t &acc, const PFrag<float> &a, const Frag &b) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x[i], b.v[i], acc, 0, 0, 0);
+}
+
 // ------------------------------------------------------------ misc
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Returns x, but hides its value from the optimiser.  Lane-derived indices
+// are passed through this at the start of each phase of a chunk loop so that
+// their LDS addresses are recomputed next to their uses instead of being
+// hoisted out of the loop and kept live (which spills registers).
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 
 // Floor for log f: exp(-200) is 0 in float32 and finite differences of
 // prefix sums stay finite even for log f = -inf.

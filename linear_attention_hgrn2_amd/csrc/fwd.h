@@ -12,11 +12,15 @@
 //   A     = tril( sum_c q_t k_s e^{b_t - b_s} )        (C x C, shared by all slices)
 //   Y     = A V + (q e^b) S                           (intra + inter chunk)
 //   S    <- e^Gamma S + (k e^{Gamma - b})^T V         (state passing, float32)
-// Every exponent is a partial sum of log f anchored inside the span it
-// covers, so it is <= 0: sub-blocks of 16 tokens carry block-local prefixes
-// ell, the off-diagonal blocks of A use anchors at sub-block boundaries, and
-// diagonal blocks whose in-block decay exceeds kDiagLimit nats are evaluated
-// directly instead of through the factorised product.
+//
+// A preparation pass evaluates each decayed operand once per chunk, with
+// exponents anchored inside the span they cover so that they are <= 0:
+// 16-token sub-blocks carry block-local prefixes ell (totals L_j, starts P_j),
+//   qo = q e^{ell}, ko = k e^{L_j - ell}, kh = ko e^{Gamma - P_{j+1}} = k e^{Gamma - b}.
+// Block (t in i, s in j) of A is qo_t . (ko_s * gap_ij) with
+// gap_ij = e^{P_i - P_{j+1}} (<= 1) off the diagonal and e^{-L_i} on it; a
+// diagonal block whose in-block decay exceeds kDiagLimit nats is evaluated
+// directly.  The inter-chunk readout uses qo against S scaled by e^{P_i}.
 #pragma once
 
 #include "common.h"
@@ -29,8 +33,8 @@ struct FwdArgs {
   const float *h0;
   void *y;
   float *ht;
-  float *states;  // [B,H,N+1,D,D] or null
-  int N;          // number of chunks
+  void *states;  // [B,H,N+1,D,D] in the input dtype, or null
+  int N;         // number of chunks
 };
 
 template <typename TIn, int D, int C, int DVT>
@@ -38,39 +42,46 @@ struct FwdCfg {
   static constexpr int NW = DVT / 16;             // waves; wave w owns state columns [16w, 16w+16)
   static constexpr int NT = NW * 64;
   static constexpr int NB = C / 16;               // 16-token sub-blocks per chunk
+  static constexpr int NPAIR = NB * (NB + 1) / 2;
   static constexpr int CB = D / 16;               // 16-channel blocks of d_k
   static constexpr int KSD = (D + 31) / 32;       // 32-wide k steps over channels
   static constexpr int KSC = (C + 31) / 32;       // 32-wide k steps over tokens
   static constexpr int EPV = 16 / (int)sizeof(TIn);
-  static constexpr int LDQ = D + EPV;             // q, k rows (16-byte pad)
-  static constexpr int LDL = D + 4;               // ell rows (float)
+  static constexpr int LDN = D + EPV;             // natural [token][channel] rows (16-byte pad)
+  static constexpr int LDL = D + 4;
   static constexpr int LDV = DVT + EPV;
-  static constexpr int LDKT = C + EPV;            // (k e^{Gamma-b})^T rows
-  static constexpr int LDA = C + EPV;             // A rows
+  static constexpr int LDKT = C + EPV;
+  static constexpr int LDA = C + EPV;
   static constexpr int VQ = C * D / EPV;          // 16-byte vectors per [C x D] tile
   static constexpr int VV = C * DVT / EPV;        // ... per [C x DVT] tile
   static constexpr int NVQ = (VQ + NT - 1) / NT;
   static constexpr int NVV = (VV + NT - 1) / NT;
   struct Smem {
-    TIn q[C][LDQ];
-    TIn k[C][LDQ];
     float l[C][LDL];          // block-local inclusive prefix of floored log f
+    TIn qo[C][LDN];           // q e^{ell}
+    TIn ko[C][LDN];           // k e^{L_j - ell}
+    TIn khT[D][LDKT];         // (k e^{Gamma - b})^T
     TIn v[C][LDV];
-    TIn khT[D][LDKT];         // (k e^{Gamma - b})^T, operand of the state update
     TIn a[C][LDA];            // causal scores A[t][s]
-    float Lb[NB][D];          // sub-block totals
-    float Pb[NB + 1][D];      // chunk-relative sub-block starts; Pb[NB] = Gamma
+    float Lb[NB][D];          // sub-block totals L_j
+    float Pb[NB + 1][D];      // sub-block starts P_j; Pb[NB] = Gamma
+    float ePb[NB][D];         // e^{P_i}
+    float eG[D];              // e^{Gamma}
+    float gp[NPAIR][D];       // gap factors of the score blocks
     int flags;                // bit i: diagonal block i evaluated directly
   };
   static constexpr bool fits = sizeof(Smem) <= 160 * 1024;  // LDS per workgroup on gfx950
   static_assert(D % DVT == 0 && DVT % 16 == 0 && C % 16 == 0, "tile shape");
 };
 
+// pair index of score block (i, j), j <= i
+__host__ __device__ constexpr int pair_index(int i, int j) { return i * (i + 1) / 2 + j; }
+
 template <typename TIn, int D, int C, int DVT>
 __global__ __launch_bounds__(4 * DVT) void hgrn2_fwd_kernel(FwdArgs args) {
   using Cfg = FwdCfg<TIn, D, C, DVT>;
   constexpr int NW = Cfg::NW, NT = Cfg::NT, NB = Cfg::NB, CB = Cfg::CB, KSD = Cfg::KSD,
-                KSC = Cfg::KSC, EPV = Cfg::EPV;
+                KSC = Cfg::KSC, EPV = Cfg::EPV, NPAIR = Cfg::NPAIR;
   __shared__ typename Cfg::Smem sm;
 
   const int B = args.B, T = args.T, H = args.H;
@@ -95,8 +106,10 @@ __global__ __launch_bounds__(4 * DVT) void hgrn2_fwd_kernel(FwdArgs args) {
   const TIn *gv = (const TIn *)args.v;
   const TIn *gl = (const TIn *)args.log_f;
   TIn *gy = (TIn *)args.y;
+  TIn *gst = (TIn *)args.states;
   const size_t SS = (size_t)D * D;
   const size_t state_base = (size_t)bh * SS;
+  auto tok = [&](int t) { return (((size_t)b * T + t) * H + h) * D; };
 
   // ---- state slice: S[cb] holds rows [16cb, 16cb+16) x columns j0 + 16w + [0,16)
   f32x4_t S[CB];
@@ -109,13 +122,14 @@ __global__ __launch_bounds__(4 * DVT) void hgrn2_fwd_kernel(FwdArgs args) {
       S[cb][r] = args.h0 ? args.h0[state_base + (size_t)c * D + jcol] : 0.f;
     }
   }
-  if (args.states) {
-    float *st = args.states + (size_t)bh * (N + 1) * SS;
+  auto store_state = [&](int n) {
+    TIn *st = gst + ((size_t)bh * (N + 1) + n) * SS;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) st[(size_t)(cb * 16 + 4 * g + r) * D + jcol] = S[cb][r];
-  }
+      for (int r = 0; r < 4; ++r) st[(size_t)(cb * 16 + 4 * g + r) * D + jcol] = from_f32<TIn>(S[cb][r]);
+  };
+  if (gst) store_state(0);
 
   // ---- register prefetch of one chunk's tiles
   uint4 pq[Cfg::NVQ], pk[Cfg::NVQ], pl[Cfg::NVQ], pv[Cfg::NVV];
@@ -128,7 +142,7 @@ __global__ __launch_bounds__(4 * DVT) void hgrn2_fwd_kernel(FwdArgs args) {
       const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
       uint4 zq = make_uint4(0, 0, 0, 0), zk = zq, zl = zq;
       if (idx < Cfg::VQ && row < len) {
-        const size_t off = (((size_t)b * T + t0 + row) * H + h) * D + col;
+        const size_t off = tok(t0 + row) + col;
         zq = *(const uint4 *)(gq + off);
         zk = *(const uint4 *)(gk + off);
         zl = *(const uint4 *)(gl + off);
@@ -142,10 +156,7 @@ __global__ __launch_bounds__(4 * DVT) void hgrn2_fwd_kernel(FwdArgs args) {
       const int idx = tid + it * NT;
       const int row = idx / (DVT / EPV), col = (idx % (DVT / EPV)) * EPV;
       uint4 zv = make_uint4(0, 0, 0, 0);
-      if (idx < Cfg::VV && row < len) {
-        const size_t off = (((size_t)b * T + t0 + row) * H + h) * D + j0 + col;
-        zv = *(const uint4 *)(gv + off);
-      }
+      if (idx < Cfg::VV && row < len) zv = *(const uint4 *)(gv + tok(t0 + row) + j0 + col);
       pv[it] = zv;
     }
   };
@@ -154,19 +165,21 @@ __global__ __launch_bounds__(4 * DVT) void hgrn2_fwd_kernel(FwdArgs args) {
   for (int n = 0; n < N; ++n) {
     const int t0 = n * C;
     const int len = min(C, T - t0);
+    // ================= preparation =================
     __syncthreads();  // previous chunk's readers of LDS are done
-    // ---- registers -> LDS
+    {
+    const int tid = opaque(threadIdx.x);
 #pragma unroll
     for (int it = 0; it < Cfg::NVQ; ++it) {
       const int idx = tid + it * NT;
       if (idx < Cfg::VQ) {
         const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
-        *(uint4 *)&sm.q[row][col] = pq[it];
-        *(uint4 *)&sm.k[row][col] = pk[it];
         float f[EPV];
         Vec<TIn>::unpack(pl[it], f);
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) sm.l[row][col + e] = floor_logf(f[e]);
+        for (int e = 0; e < EPV; e += 4)
+          *(float4 *)&sm.l[row][col + e] =
+              make_float4(floor_logf(f[e]), floor_logf(f[e + 1]), floor_logf(f[e + 2]), floor_logf(f[e + 3]));
       }
     }
 #pragma unroll
@@ -179,10 +192,7 @@ __global__ __launch_bounds__(4 * DVT) void hgrn2_fwd_kernel(FwdArgs args) {
     }
     if (tid == 0) sm.flags = 0;
     __syncthreads();
-    if (n + 1 < N) prefetch(n + 1);  // in flight while this chunk computes
-
-    // ---- block-local prefixes of log f, block totals, diagonal-range flags
-    {
+    {  // block-local prefixes of log f, block totals, diagonal-range flags
       int fl = 0;
       for (int p = tid; p < NB * D; p += NT) {
         const int i = p / D, c = p % D;
@@ -203,29 +213,56 @@ __global__ __launch_bounds__(4 * DVT) void hgrn2_fwd_kernel(FwdArgs args) {
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
         sm.Pb[i][c] = s;
+        sm.ePb[i][c] = __expf(s);
         s += sm.Lb[i][c];
       }
       sm.Pb[NB][c] = s;
+      sm.eG[c] = __expf(s);
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j <= i; ++j)
+          sm.gp[pair_index(i, j)][c] = (j < i) ? __expf(sm.Pb[i][c] - sm.Pb[j + 1][c]) : __expf(-sm.Lb[i][c]);
     }
     __syncthreads();
-    const int flags = sm.flags;
-
-    // ---- (k e^{Gamma - b})^T: exponent (Gamma - P_{j+1}) + (L_j - ell_s) <= 0
-    for (int e = tid; e < C * D; e += NT) {
-      const int s = e % C, c = e / C, jb = s / 16;
-      const float ex = (sm.Pb[NB][c] - sm.Pb[jb + 1][c]) + (sm.Lb[jb][c] - sm.l[s][c]);
-      sm.khT[c][s] = from_f32<TIn>(to_f32(sm.k[s][c]) * __expf(ex));
+#pragma unroll
+    for (int it = 0; it < Cfg::NVQ; ++it) {
+      const int idx = tid + it * NT;
+      if (idx < Cfg::VQ) {
+        const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
+        const int jb = row >> 4;
+        float fq[EPV], fk[EPV];
+        Vec<TIn>::unpack(pq[it], fq);
+        Vec<TIn>::unpack(pk[it], fk);
+        TIn oq[EPV], ok[EPV];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          const int c = col + e;
+          const float l = sm.l[row][c];
+          const float kown = fk[e] * __expf(sm.Lb[jb][c] - l);
+          oq[e] = from_f32<TIn>(fq[e] * __expf(l));
+          ok[e] = from_f32<TIn>(kown);
+          sm.khT[c][row] = from_f32<TIn>(kown * __expf(sm.Pb[NB][c] - sm.Pb[jb + 1][c]));
+        }
+        *(uint4 *)&sm.qo[row][col] = *(const uint4 *)oq;
+        *(uint4 *)&sm.ko[row][col] = *(const uint4 *)ok;
+      }
     }
+    }
+    const int flags = sm.flags;  // final since the barrier after the prefix pass
+    __syncthreads();
+    if (n + 1 < N) prefetch(n + 1);  // in flight while this chunk computes
 
-    // ---- causal scores, as transposed tiles (rows s in block jb, columns t in block ib)
-    for (int pi = w; pi < NB * (NB + 1) / 2; pi += NW) {
-      int ib = 0, jb = pi;
-      while (jb > ib) {  // pair index -> (ib, jb), jb <= ib
+    // ================= causal scores, as transposed tiles =================
+    for (int pi = w; pi < NPAIR; pi += NW) {
+      const int lane = opaque(tid & 63), n16 = lane & 15, g = lane >> 4;
+      int ib = 0, jb = pi;  // rows s in block jb, columns t in block ib, jb <= ib
+      while (jb > ib) {
         jb -= ib + 1;
         ++ib;
       }
-      const int s_row = jb * 16 + n16;   // A-operand row (token s)
-      const int t_col = ib * 16 + n16;   // B-operand column (token t)
+      const int s_row = jb * 16 + n16;
+      const int t_col = ib * 16 + n16;
       f32x4_t acc;
       acc_zero(acc);
       const bool direct = (jb == ib) && ((flags >> ib) & 1);
@@ -235,13 +272,20 @@ __global__ __launch_bounds__(4 * DVT) void hgrn2_fwd_kernel(FwdArgs args) {
           const int c0 = ks * 32 + 8 * g;
           Frag fa, fb;
           if (c0 < D) {
+            float kv[8], qv[8];
+            Vec<TIn>::unpack(*(const uint4 *)&sm.ko[s_row][c0], kv);
+            Vec<TIn>::unpack(*(const uint4 *)&sm.qo[t_col][c0], qv);
+            if constexpr (EPV == 4) {
+              Vec<TIn>::unpack(*(const uint4 *)&sm.ko[s_row][c0 + 4], kv + 4);
+              Vec<TIn>::unpack(*(const uint4 *)&sm.qo[t_col][c0 + 4], qv + 4);
+            }
+            const float4 g0 = *(const float4 *)&sm.gp[pi][c0];
+            const float4 g1 = *(const float4 *)&sm.gp[pi][c0 + 4];
+            const float gv8[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
 #pragma unroll
             for (int x = 0; x < 8; ++x) {
-              const int c = c0 + x;
-              const float eK = (jb < ib) ? (sm.Lb[jb][c] - sm.l[s_row][c]) + (sm.Pb[ib][c] - sm.Pb[jb + 1][c])
-                                         : -sm.l[s_row][c];
-              fa.v[x] = to_f32(sm.k[s_row][c]) * __expf(eK);
-              fb.v[x] = to_f32(sm.q[t_col][c]) * __expf(sm.l[t_col][c]);
+              fa.v[x] = kv[x] * gv8[x];
+              fb.v[x] = qv[x];
             }
           } else {
             frag_zero(fa);
@@ -255,9 +299,10 @@ __global__ __launch_bounds__(4 * DVT) void hgrn2_fwd_kernel(FwdArgs args) {
         for (int r = 0; r < 4; ++r) {
           const int s = jb * 16 + 4 * g + r;
           float a = 0.f;
-          if (s <= t_col)
+          if (s <= t_col && t_col < len)
             for (int c = 0; c < D; ++c)
-              a += to_f32(sm.q[t_col][c]) * to_f32(sm.k[s][c]) * __expf(sm.l[t_col][c] - sm.l[s][c]);
+              a += to_f32(gq[tok(t0 + t_col) + c]) * to_f32(gk[tok(t0 + s) + c]) *
+                   __expf(sm.l[t_col][c] - sm.l[s][c]);
           acc[r] = a;
         }
       }
@@ -269,6 +314,8 @@ __global__ __launch_bounds__(4 * DVT) void hgrn2_fwd_kernel(FwdArgs args) {
     }
     __syncthreads();
 
+    {
+    const int lane = opaque(tid & 63), n16 = lane & 15, g = lane >> 4;
     // ---- V fragments (k = token), reused by the intra product and the state update
     Frag fv[KSC];
 #pragma unroll
@@ -280,39 +327,51 @@ __global__ __launch_bounds__(4 * DVT) void hgrn2_fwd_kernel(FwdArgs args) {
       }
     }
 
-    // ---- Y = A V + (q e^b) S_prev  for this wave's 16 columns
+    // ---- Y = A V + qo (e^{P_i} S_prev)  for this wave's 16 columns
     f32x4_t Y[NB];
 #pragma unroll
     for (int tb = 0; tb < NB; ++tb) {
       acc_zero(Y[tb]);
       const int t = tb * 16 + n16;
-      // intra: s < 16 (tb + 1)
 #pragma unroll
       for (int ks = 0; ks < KSC; ++ks) {
         if (ks * 32 < 16 * (tb + 1)) {
           Frag fa;
+          const int s0 = ks * 32 + 8 * g;
+          if (s0 < 16 * (tb + 1) && s0 < C) {
+            float av[8];
+            Vec<TIn>::unpack(*(const uint4 *)&sm.a[t][s0], av);
+            if constexpr (EPV == 4) Vec<TIn>::unpack(*(const uint4 *)&sm.a[t][s0 + 4], av + 4);
 #pragma unroll
-          for (int x = 0; x < 8; ++x) {
-            const int s = ks * 32 + 8 * g + x;
-            fa.v[x] = (s < 16 * (tb + 1) && s < C) ? to_f32(sm.a[t][s]) : 0.f;
+            for (int x = 0; x < 8; ++x) fa.v[x] = av[x];
+          } else {
+            frag_zero(fa);
           }
           Mma<TIn>::run(Y[tb], fa, fv[ks]);
         }
       }
-      // inter: channels in the accumulator order of S (slots 0-3: block 2ks, 4-7: block 2ks+1)
+      // channels in the accumulator order of S (slots 0-3: block 2ks, 4-7: block 2ks+1)
 #pragma unroll
       for (int ks = 0; ks < KSD; ++ks) {
         Frag fa, fb;
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          const int cb = 2 * ks + (x >> 2);
-          const int c = cb * 16 + 4 * g + (x & 3);
+        for (int hf = 0; hf < 2; ++hf) {
+          const int cb = 2 * ks + hf;
           if (cb < CB) {
-            fa.v[x] = to_f32(sm.q[t][c]) * __expf(sm.Pb[tb][c] + sm.l[t][c]);
-            fb.v[x] = S[cb][x & 3];
+            const int c = cb * 16 + 4 * g;
+            const float4 e4 = *(const float4 *)&sm.ePb[tb][c];
+            const float ee[4] = {e4.x, e4.y, e4.z, e4.w};
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+              fa.v[4 * hf + x] = to_f32(sm.qo[t][c + x]);
+              fb.v[4 * hf + x] = S[cb][x] * ee[x];
+            }
           } else {
-            fa.v[x] = 0.f;
-            fb.v[x] = 0.f;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+              fa.v[4 * hf + x] = 0.f;
+              fb.v[4 * hf + x] = 0.f;
+            }
           }
         }
         Mma<TIn>::run(Y[tb], fa, fb);
@@ -322,16 +381,24 @@ __global__ __launch_bounds__(4 * DVT) void hgrn2_fwd_kernel(FwdArgs args) {
     // ---- S <- e^Gamma S + (k e^{Gamma-b})^T V
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) S[cb][r] *= __expf(sm.Pb[NB][cb * 16 + 4 * g + r]);
+      const float4 e4 = *(const float4 *)&sm.eG[cb * 16 + 4 * g];
+      S[cb][0] *= e4.x;
+      S[cb][1] *= e4.y;
+      S[cb][2] *= e4.z;
+      S[cb][3] *= e4.w;
+      const int c = cb * 16 + n16;
 #pragma unroll
       for (int ks = 0; ks < KSC; ++ks) {
         Frag fa;
-        const int c = cb * 16 + n16;
+        const int s0 = ks * 32 + 8 * g;
+        if (s0 < C) {
+          float kv[8];
+          Vec<TIn>::unpack(*(const uint4 *)&sm.khT[c][s0], kv);
+          if constexpr (EPV == 4) Vec<TIn>::unpack(*(const uint4 *)&sm.khT[c][s0 + 4], kv + 4);
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          const int s = ks * 32 + 8 * g + x;
-          fa.v[x] = (s < C) ? to_f32(sm.khT[c][s]) : 0.f;
+          for (int x = 0; x < 8; ++x) fa.v[x] = kv[x];
+        } else {
+          frag_zero(fa);
         }
         Mma<TIn>::run(S[cb], fa, fv[ks]);
       }
@@ -344,16 +411,11 @@ __global__ __launch_bounds__(4 * DVT) void hgrn2_fwd_kernel(FwdArgs args) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = tb * 16 + 4 * g + r;
-          if (t < len) gy[(((size_t)b * T + t0 + t) * H + h) * D + jcol] = from_f32<TIn>(Y[tb][r]);
+          if (t < len) gy[tok(t0 + t) + jcol] = from_f32<TIn>(Y[tb][r]);
         }
     }
-    if (args.states) {
-      float *st = args.states + ((size_t)bh * (N + 1) + n + 1) * SS;
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) st[(size_t)(cb * 16 + 4 * g + r) * D + jcol] = S[cb][r];
     }
+    if (gst) store_state(n + 1);
   }
   if (args.ht) {
 #pragma unroll

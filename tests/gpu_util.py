@@ -25,9 +25,12 @@ def to_host64(t: torch.Tensor) -> np.ndarray:
 
 
 def slice_rel(got: np.ndarray, ref: np.ndarray, token_major=True) -> float:
-    """Largest normwise relative error over (b, h) slices.
+    """Largest normwise relative error over (b, h) slices (inf if the GPU
+    result holds a NaN or an infinity).
 
     token tensors are [B,T,H,D]; state tensors [B,H,D,D]."""
+    if not np.all(np.isfinite(got)):
+        return float("inf")
     worst = 0.0
     if token_major:
         B, _, H, _ = ref.shape

@@ -43,9 +43,11 @@ def test_abi_version_and_strings(lib):
 def test_sizes(lib):
     assert lib.hgrn2_num_chunks(4096, 64) == 64
     assert lib.hgrn2_num_chunks(250, 16) == 16
-    assert lib.hgrn2_states_bytes(8, 4096, 16, 128, 128, 64) == 8 * 16 * 65 * 128 * 128 * 4
-    assert lib.hgrn2_bwd_workspace_bytes(1, 100, 1, 16, 16, 16, 1) == 0
-    assert lib.hgrn2_bwd_workspace_bytes(1, 100, 1, 16, 16, 16, 0) == 8 * 16 * 16 * 4
+    assert lib.hgrn2_states_bytes(8, 4096, 16, 128, 128, 64, 0) == 8 * 16 * 65 * 128 * 128 * 4
+    assert lib.hgrn2_states_bytes(8, 4096, 16, 128, 128, 64, 1) == 8 * 16 * 65 * 128 * 128 * 2
+    assert lib.hgrn2_states_bytes(8, 4096, 16, 128, 128, 64, 5) == 0
+    assert lib.hgrn2_bwd_workspace_bytes(1, 100, 1, 16, 16, 16, 0, 1) == 0
+    assert lib.hgrn2_bwd_workspace_bytes(1, 100, 1, 16, 16, 16, 0, 0) == 8 * 16 * 16 * 4
     assert lib.hgrn2_supported(128, 64, 1) == 1
     assert lib.hgrn2_supported(48, 64, 1) == 0
     assert lib.hgrn2_supported(128, 128, 1) == 0
