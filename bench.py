@@ -36,6 +36,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--decode-steps", type=int, default=50)
     p.add_argument("--only", choices=["train", "decode", "all"], default="all")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="also run a plain 1 GiB device copy (calibrates profiler byte counters)")
     return p.parse_args()
 
 
@@ -232,6 +234,13 @@ def main():
             out["unit"] = "GB/s"
             out["ms_per_step"] = dres["ms"]
             out["config"] = {"workload": "decode_f32: B256 H16 d128"}
+    if args.calib_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
     if res is not None and not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(res)
     print(json.dumps(out), flush=True)

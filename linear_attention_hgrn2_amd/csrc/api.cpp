@@ -7,7 +7,7 @@
 #include <cstdio>
 #include <string>
 
-#include "../../include/hgrn2.h"
+#include "hgrn2.h"
 #include "dispatch.h"
 
 namespace {

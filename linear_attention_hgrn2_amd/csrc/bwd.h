@@ -25,7 +25,8 @@
 // never communicate.  S_prev comes from the chunk-boundary states saved by
 // the forward.
 //
-// Per chunk a preparation pass evaluates every decayed operand once, with
+// Per chunk a preparation pass evaluates every decayed operand once (the
+// channel-major tiles use the bank-spreading TT32/TT16 layouts), with
 // exponents anchored inside the span they cover (<= 0 except on diagonal
 // sub-blocks; those are evaluated directly when their decay range exceeds
 // kDiagLimit).  16-token sub-blocks carry block-local prefixes ell (totals
@@ -68,14 +69,13 @@ struct BwdCfg {
   static constexpr int EPV = 16 / (int)sizeof(TIn);
   static constexpr int LDN = D + EPV;   // [token][channel] rows
   static constexpr int LDA = C + EPV;   // [token][token] rows
-  static constexpr int LDT = C + 4;     // float32 [channel][token] rows
   static constexpr int LDL = D + 4;     // float32 [token][channel] rows
   static constexpr int VQ = C * D / EPV;
   static constexpr int NVQ = (VQ + NT - 1) / NT;
   struct SmemC {                 // channel side
-    float lT[D][LDT];            // ell, channel-major
-    float qoT[D][LDT];           // q e^{ell}
-    float koT[D][LDT];           // k e^{L_j - ell}
+    float lT[D * TT32<C>::LD];   // ell, channel-major (TT32 layout)
+    float qoT[D * TT32<C>::LD];  // q e^{ell}
+    float koT[D * TT32<C>::LD];  // k e^{L_j - ell}
     TIn v[C][LDN];
     TIn dy[C][LDN];
     TIn dA[C][LDA];              // dA[t][s], causal
@@ -88,7 +88,7 @@ struct BwdCfg {
     TIn qo[C][LDN];              // q e^{ell}
     TIn ko[C][LDN];              // k e^{L_j - ell}
     TIn kh[C][LDN];              // k e^{Gamma - b}
-    TIn qhT[D][LDA];             // (q e^b)^T
+    TIn qhT[D * TTile<TIn, C>::LD];  // (q e^b)^T (TTile layout)
     TIn dy[C][LDN];
     TIn At[C][LDA];              // A^T[s][t], causal
     float Lb[NB][D];
@@ -214,7 +214,7 @@ __device__ __forceinline__ void bwd_channel_side(const BwdArgs &args, typename B
           float f[EPV];
           Vec<TIn>::unpack(pl[it], f);
 #pragma unroll
-          for (int e = 0; e < EPV; ++e) sm.lT[col + e][row] = floor_logf(f[e]);
+          for (int e = 0; e < EPV; ++e) sm.lT[TT32<C>::at(col + e, row)] = floor_logf(f[e]);
         }
       }
       if (tid == 0) sm.flags = 0;
@@ -226,7 +226,7 @@ __device__ __forceinline__ void bwd_channel_side(const BwdArgs &args, typename B
           float acc = 0.f;
 #pragma unroll
           for (int u4 = 0; u4 < 4; ++u4) {
-            float4 *pp = (float4 *)&sm.lT[c][i * 16 + 4 * u4];
+            float4 *pp = (float4 *)&sm.lT[TT32<C>::at(c, i * 16 + 4 * u4)];
             float4 x = *pp;
             acc += x.x;
             x.x = acc;
@@ -265,9 +265,10 @@ __device__ __forceinline__ void bwd_channel_side(const BwdArgs &args, typename B
 #pragma unroll
           for (int e = 0; e < EPV; ++e) {
             const int c = col + e;
-            const float l = sm.lT[c][row];
-            sm.qoT[c][row] = fq[e] * __expf(l);
-            sm.koT[c][row] = fk[e] * __expf(sm.Lb[jb][c] - l);
+            const int o = TT32<C>::at(c, row);
+            const float l = sm.lT[o];
+            sm.qoT[o] = fq[e] * __expf(l);
+            sm.koT[o] = fk[e] * __expf(sm.Lb[jb][c] - l);
           }
         }
       }
@@ -336,8 +337,8 @@ __device__ __forceinline__ void bwd_channel_side(const BwdArgs &args, typename B
             if (ok) {
               const float gap = (sb < i) ? __expf(sm.Pb[i][cw] - sm.Pb[sb + 1][cw]) : __expf(-sm.Lb[i][cw]);
               fa = ld8(&sm.dA[t][s0]);
-              const float4 k0 = *(const float4 *)&sm.koT[cw][s0];
-              const float4 k1 = *(const float4 *)&sm.koT[cw][s0 + 4];
+              const float4 k0 = *(const float4 *)&sm.koT[TT32<C>::at(cw, s0)];
+              const float4 k1 = *(const float4 *)&sm.koT[TT32<C>::at(cw, s0 + 4)];
               fb.v[0] = k0.x * gap; fb.v[1] = k0.y * gap; fb.v[2] = k0.z * gap; fb.v[3] = k0.w * gap;
               fb.v[4] = k1.x * gap; fb.v[5] = k1.y * gap; fb.v[6] = k1.z * gap; fb.v[7] = k1.w * gap;
             } else {
@@ -347,8 +348,8 @@ __device__ __forceinline__ void bwd_channel_side(const BwdArgs &args, typename B
             mma_split(dq, fa, fb);
           }
         }
-        const float4 l4 = *(const float4 *)&sm.lT[cw][i * 16 + 4 * g];
-        const float4 q4 = *(const float4 *)&sm.qoT[cw][i * 16 + 4 * g];
+        const float4 l4 = *(const float4 *)&sm.lT[TT32<C>::at(cw, i * 16 + 4 * g)];
+        const float4 q4 = *(const float4 *)&sm.qoT[TT32<C>::at(cw, i * 16 + 4 * g)];
         const float ll[4] = {l4.x, l4.y, l4.z, l4.w};
         const float qq[4] = {q4.x, q4.y, q4.z, q4.w};
 #pragma unroll
@@ -359,7 +360,7 @@ __device__ __forceinline__ void bwd_channel_side(const BwdArgs &args, typename B
           if (direct && tt < len) {
             float a = 0.f;
             for (int s = i * 16; s <= tt; ++s)
-              a += to_f32(sm.dA[tt][s]) * to_f32(gk[tok(t0 + s) + cw]) * __expf(ll[r] - sm.lT[cw][s]);
+              a += to_f32(sm.dA[tt][s]) * to_f32(gk[tok(t0 + s) + cw]) * __expf(ll[r] - sm.lT[TT32<C>::at(cw, s)]);
             val += a;
             u[i][r] += to_f32(gq[tok(t0 + tt) + cw]) * a;
           }
@@ -407,8 +408,8 @@ __device__ __forceinline__ void bwd_channel_side(const BwdArgs &args, typename B
             Frag fa, fb;
             if (ok) {
               const float gap = (tb > j) ? __expf(sm.Pb[tb][cw] - sm.Pb[j + 1][cw]) : __expf(-sm.Lb[j][cw]);
-              const float4 q0 = *(const float4 *)&sm.qoT[cw][tq0];
-              const float4 q1 = *(const float4 *)&sm.qoT[cw][tq0 + 4];
+              const float4 q0 = *(const float4 *)&sm.qoT[TT32<C>::at(cw, tq0)];
+              const float4 q1 = *(const float4 *)&sm.qoT[TT32<C>::at(cw, tq0 + 4)];
               fb.v[0] = q0.x * gap; fb.v[1] = q0.y * gap; fb.v[2] = q0.z * gap; fb.v[3] = q0.w * gap;
               fb.v[4] = q1.x * gap; fb.v[5] = q1.y * gap; fb.v[6] = q1.z * gap; fb.v[7] = q1.w * gap;
 #pragma unroll
@@ -420,8 +421,8 @@ __device__ __forceinline__ void bwd_channel_side(const BwdArgs &args, typename B
             mma_split(dk, to_pfrag<TIn>(fa), fb);
           }
         }
-        const float4 l4 = *(const float4 *)&sm.lT[cw][j * 16 + 4 * g];
-        const float4 k4 = *(const float4 *)&sm.koT[cw][j * 16 + 4 * g];
+        const float4 l4 = *(const float4 *)&sm.lT[TT32<C>::at(cw, j * 16 + 4 * g)];
+        const float4 k4 = *(const float4 *)&sm.koT[TT32<C>::at(cw, j * 16 + 4 * g)];
         const float ll[4] = {l4.x, l4.y, l4.z, l4.w};
         const float kk[4] = {k4.x, k4.y, k4.z, k4.w};
         const float Lj = sm.Lb[j][cw];
@@ -433,7 +434,7 @@ __device__ __forceinline__ void bwd_channel_side(const BwdArgs &args, typename B
           if (direct && ss < len) {
             float a = 0.f;
             for (int t = ss; t < j * 16 + 16; ++t)
-              a += to_f32(sm.dA[t][ss]) * to_f32(gq[tok(t0 + t) + cw]) * __expf(sm.lT[cw][t] - ll[r]);
+              a += to_f32(sm.dA[t][ss]) * to_f32(gq[tok(t0 + t) + cw]) * __expf(sm.lT[TT32<C>::at(cw, t)] - ll[r]);
             val += a;
             u[j][r] -= to_f32(gk[tok(t0 + ss) + cw]) * a;
           }
@@ -485,8 +486,8 @@ __device__ __forceinline__ void bwd_channel_side(const BwdArgs &args, typename B
         Frag f;
         if (tq0 < C) {
           const float eP = __expf(sm.Pb[tq0 >> 4][cw]);
-          const float4 q0 = *(const float4 *)&sm.qoT[cw][tq0];
-          const float4 q1 = *(const float4 *)&sm.qoT[cw][tq0 + 4];
+          const float4 q0 = *(const float4 *)&sm.qoT[TT32<C>::at(cw, tq0)];
+          const float4 q1 = *(const float4 *)&sm.qoT[TT32<C>::at(cw, tq0 + 4)];
           f.v[0] = q0.x * eP; f.v[1] = q0.y * eP; f.v[2] = q0.z * eP; f.v[3] = q0.w * eP;
           f.v[4] = q1.x * eP; f.v[5] = q1.y * eP; f.v[6] = q1.z * eP; f.v[7] = q1.w * eP;
         } else {
@@ -650,7 +651,7 @@ __device__ __forceinline__ void bwd_value_side(const BwdArgs &args, typename Bwd
             oq[e] = from_f32<TIn>(qo);
             ok[e] = from_f32<TIn>(ko);
             oh[e] = from_f32<TIn>(ko * __expf(sm.Pb[NB][c] - sm.Pb[jb + 1][c]));
-            sm.qhT[c][row] = from_f32<TIn>(qo * __expf(sm.Pb[jb][c]));
+            sm.qhT[TTile<TIn, C>::at(c, row)] = from_f32<TIn>(qo * __expf(sm.Pb[jb][c]));
           }
           *(uint4 *)&sm.qo[row][col] = *(const uint4 *)oq;
           *(uint4 *)&sm.ko[row][col] = *(const uint4 *)ok;
@@ -781,7 +782,7 @@ __device__ __forceinline__ void bwd_value_side(const BwdArgs &args, typename Bwd
 #pragma unroll
         for (int ks = 0; ks < KSC; ++ks) {
           const int tq0 = ks * 32 + 8 * g;
-          const PFrag<TIn> fa = (tq0 < C) ? ld8(&sm.qhT[crow][tq0]) : pfrag_zero<TIn>();
+          const PFrag<TIn> fa = (tq0 < C) ? ldT8<C>(sm.qhT, crow, tq0) : pfrag_zero<TIn>();
           mma(Lam[cb], fa, fdyT[ks]);
         }
         __builtin_amdgcn_sched_barrier(0);

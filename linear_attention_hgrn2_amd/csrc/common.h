@@ -204,6 +204,39 @@ __device__ __forceinline__ void mma_split(f32x4_t &acc, const PFrag<float> &a, c
   for (int i = 0; i < 8; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x[i], b.v[i], acc, 0, 0, 0);
 }
 
+// ------------------------------------------------------------ channel-major tiles
+// A [rows][C tokens] tile whose 16-byte chunks are rotated along the row by
+// (row >> 3) + (row & 7).  Both the scalar column writes of the preparation
+// pass (sixteen lanes writing rows 8m + e of one token) and the row-fragment
+// reads of the products (sixteen lanes reading rows r..r+15 at one token)
+// then touch distinct banks.  TT32: 4-byte elements (rows padded by 16 bytes
+// at C = 64); TT16: 2-byte elements.
+template <int C> struct TT32 {
+  static constexpr int LD = (C == 64) ? C + 4 : C;
+  static constexpr int NCH = C / 4;
+  __device__ static __forceinline__ int at(int r, int t) {
+    return r * LD + ((((t >> 2) + (r >> 3) + (r & 7)) & (NCH - 1)) << 2) + (t & 3);
+  }
+};
+template <int C> struct TT16 {
+  static constexpr int LD = C;
+  static constexpr int NCH = C / 8;
+  __device__ static __forceinline__ int at(int r, int t) {
+    return r * LD + ((((t >> 3) + (r >> 3) + (r & 7)) & (NCH - 1)) << 3) + (t & 7);
+  }
+};
+template <typename T, int C> struct TTile;
+template <int C> struct TTile<float, C> : TT32<C> {};
+template <int C> struct TTile<bf16_t, C> : TT16<C> {};
+
+// 8 consecutive tokens t0..t0+7 (t0 a multiple of 8) of row r of a TTile.
+template <int C> __device__ __forceinline__ PFrag<bf16_t> ldT8(const bf16_t *tile, int r, int t0) {
+  return ld8(tile + TT16<C>::at(r, t0));
+}
+template <int C> __device__ __forceinline__ PFrag<float> ldT8(const float *tile, int r, int t0) {
+  return ld4x2(tile + TT32<C>::at(r, t0), tile + TT32<C>::at(r, t0 + 4));
+}
+
 // ------------------------------------------------------------ misc
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 

@@ -60,7 +60,7 @@ struct FwdCfg {
     float l[C][LDL];          // block-local inclusive prefix of floored log f
     TIn qo[C][LDN];           // q e^{ell}
     TIn ko[C][LDN];           // k e^{L_j - ell}
-    TIn khT[D][LDKT];         // (k e^{Gamma - b})^T
+    TIn khT[D * TTile<TIn, C>::LD];  // (k e^{Gamma - b})^T (TTile layout)
     TIn v[C][LDV];
     TIn a[C][LDA];            // causal scores A[t][s]
     float Lb[NB][D];          // sub-block totals L_j
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(4 * DVT) void hgrn2_fwd_kernel(FwdArgs args) {
           const float kown = fk[e] * __expf(sm.Lb[jb][c] - l);
           oq[e] = from_f32<TIn>(fq[e] * __expf(l));
           ok[e] = from_f32<TIn>(kown);
-          sm.khT[c][row] = from_f32<TIn>(kown * __expf(sm.Pb[NB][c] - sm.Pb[jb + 1][c]));
+          sm.khT[TTile<TIn, C>::at(c, row)] = from_f32<TIn>(kown * __expf(sm.Pb[NB][c] - sm.Pb[jb + 1][c]));
         }
         *(uint4 *)&sm.qo[row][col] = *(const uint4 *)oq;
         *(uint4 *)&sm.ko[row][col] = *(const uint4 *)ok;
@@ -317,14 +317,16 @@ __global__ __launch_bounds__(4 * DVT) void hgrn2_fwd_kernel(FwdArgs args) {
     {
     const int lane = opaque(tid & 63), n16 = lane & 15, g = lane >> 4;
     // ---- V fragments (k = token), reused by the intra product and the state update
-    Frag fv[KSC];
+    PFrag<TIn> fv[KSC];
 #pragma unroll
     for (int ks = 0; ks < KSC; ++ks) {
+      Frag f;
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
         const int s = ks * 32 + 8 * g + x;
-        fv[ks].v[x] = (s < C) ? to_f32(sm.v[s][w * 16 + n16]) : 0.f;
+        f.v[x] = (s < C) ? to_f32(sm.v[s][w * 16 + n16]) : 0.f;
       }
+      fv[ks] = to_pfrag<TIn>(f);
     }
 
     // ---- Y = A V + qo (e^{P_i} S_prev)  for this wave's 16 columns
@@ -336,45 +338,31 @@ __global__ __launch_bounds__(4 * DVT) void hgrn2_fwd_kernel(FwdArgs args) {
 #pragma unroll
       for (int ks = 0; ks < KSC; ++ks) {
         if (ks * 32 < 16 * (tb + 1)) {
-          Frag fa;
           const int s0 = ks * 32 + 8 * g;
-          if (s0 < 16 * (tb + 1) && s0 < C) {
-            float av[8];
-            Vec<TIn>::unpack(*(const uint4 *)&sm.a[t][s0], av);
-            if constexpr (EPV == 4) Vec<TIn>::unpack(*(const uint4 *)&sm.a[t][s0 + 4], av + 4);
-#pragma unroll
-            for (int x = 0; x < 8; ++x) fa.v[x] = av[x];
-          } else {
-            frag_zero(fa);
-          }
-          Mma<TIn>::run(Y[tb], fa, fv[ks]);
+          mma(Y[tb], (s0 < 16 * (tb + 1) && s0 < C) ? ld8(&sm.a[t][s0]) : pfrag_zero<TIn>(), fv[ks]);
         }
       }
       // channels in the accumulator order of S (slots 0-3: block 2ks, 4-7: block 2ks+1)
 #pragma unroll
       for (int ks = 0; ks < KSD; ++ks) {
-        Frag fa, fb;
+        Frag fb;
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
           const int cb = 2 * ks + hf;
           if (cb < CB) {
-            const int c = cb * 16 + 4 * g;
-            const float4 e4 = *(const float4 *)&sm.ePb[tb][c];
-            const float ee[4] = {e4.x, e4.y, e4.z, e4.w};
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-              fa.v[4 * hf + x] = to_f32(sm.qo[t][c + x]);
-              fb.v[4 * hf + x] = S[cb][x] * ee[x];
-            }
+            const float4 e4 = *(const float4 *)&sm.ePb[tb][cb * 16 + 4 * g];
+            fb.v[4 * hf + 0] = S[cb][0] * e4.x;
+            fb.v[4 * hf + 1] = S[cb][1] * e4.y;
+            fb.v[4 * hf + 2] = S[cb][2] * e4.z;
+            fb.v[4 * hf + 3] = S[cb][3] * e4.w;
           } else {
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-              fa.v[4 * hf + x] = 0.f;
-              fb.v[4 * hf + x] = 0.f;
-            }
+            for (int x = 0; x < 4; ++x) fb.v[4 * hf + x] = 0.f;
           }
         }
-        Mma<TIn>::run(Y[tb], fa, fb);
+        const int c0 = 2 * ks * 16 + 4 * g;
+        const int c1 = (2 * ks + 1 < CB) ? c0 + 16 : c0;  // D = 16: slots 4-7 meet zeros
+        mma(Y[tb], ld4x2(&sm.qo[t][c0], &sm.qo[t][c1]), to_pfrag<TIn>(fb));
       }
     }
 
@@ -389,18 +377,8 @@ __global__ __launch_bounds__(4 * DVT) void hgrn2_fwd_kernel(FwdArgs args) {
       const int c = cb * 16 + n16;
 #pragma unroll
       for (int ks = 0; ks < KSC; ++ks) {
-        Frag fa;
         const int s0 = ks * 32 + 8 * g;
-        if (s0 < C) {
-          float kv[8];
-          Vec<TIn>::unpack(*(const uint4 *)&sm.khT[c][s0], kv);
-          if constexpr (EPV == 4) Vec<TIn>::unpack(*(const uint4 *)&sm.khT[c][s0 + 4], kv + 4);
-#pragma unroll
-          for (int x = 0; x < 8; ++x) fa.v[x] = kv[x];
-        } else {
-          frag_zero(fa);
-        }
-        Mma<TIn>::run(S[cb], fa, fv[ks]);
+        mma(S[cb], (s0 < C) ? ldT8<C>(sm.khT, c, s0) : pfrag_zero<TIn>(), fv[ks]);
       }
     }
 
