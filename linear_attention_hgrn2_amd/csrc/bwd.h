@@ -405,20 +405,17 @@ __device__ __forceinline__ void bwd_channel_side(const BwdArgs &args, typename B
             const int tq0 = ks * 32 + 8 * g;
             const int tb = tq0 >> 4;
             const bool ok = tq0 >= 16 * j && tq0 < C && !(direct && tb == j);
-            Frag fa, fb;
+            Frag fb;
             if (ok) {
               const float gap = (tb > j) ? __expf(sm.Pb[tb][cw] - sm.Pb[j + 1][cw]) : __expf(-sm.Lb[j][cw]);
               const float4 q0 = *(const float4 *)&sm.qoT[TT32<C>::at(cw, tq0)];
               const float4 q1 = *(const float4 *)&sm.qoT[TT32<C>::at(cw, tq0 + 4)];
               fb.v[0] = q0.x * gap; fb.v[1] = q0.y * gap; fb.v[2] = q0.z * gap; fb.v[3] = q0.w * gap;
               fb.v[4] = q1.x * gap; fb.v[5] = q1.y * gap; fb.v[6] = q1.z * gap; fb.v[7] = q1.w * gap;
-#pragma unroll
-              for (int x = 0; x < 8; ++x) fa.v[x] = to_f32(sm.dA[tq0 + x][s]);
             } else {
-              frag_zero(fa);
               frag_zero(fb);
             }
-            mma_split(dk, to_pfrag<TIn>(fa), fb);
+            mma_split(dk, ldcol8(&sm.dA[ok ? tq0 : 0][s], Cfg::LDA, ok), fb);
           }
         }
         const float4 l4 = *(const float4 *)&sm.lT[TT32<C>::at(cw, j * 16 + 4 * g)];
@@ -502,13 +499,8 @@ __device__ __forceinline__ void bwd_channel_side(const BwdArgs &args, typename B
         const int jrow = jb * 16 + n16;
 #pragma unroll
         for (int ks = 0; ks < KSC; ++ks) {
-          Frag fa;
-#pragma unroll
-          for (int x = 0; x < 8; ++x) {
-            const int t = ks * 32 + 8 * g + x;
-            fa.v[x] = (t < C) ? to_f32(sm.dy[t][jrow]) : 0.f;
-          }
-          mma(LamT[jb], to_pfrag<TIn>(fa), fqh[ks]);
+          const int tq0 = ks * 32 + 8 * g;
+          mma(LamT[jb], ldcol8(&sm.dy[tq0 < C ? tq0 : 0][jrow], Cfg::LDN, tq0 < C), fqh[ks]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -723,13 +715,8 @@ __device__ __forceinline__ void bwd_value_side(const BwdArgs &args, typename Bwd
       PFrag<TIn> fdyT[KSC];  // dY^T fragments: column jw, k = token
 #pragma unroll
       for (int ks = 0; ks < KSC; ++ks) {
-        Frag f;
-#pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          const int t = ks * 32 + 8 * g + x;
-          f.v[x] = (t < C) ? to_f32(sm.dy[t][jw]) : 0.f;
-        }
-        fdyT[ks] = to_pfrag<TIn>(f);
+        const int tq0 = ks * 32 + 8 * g;
+        fdyT[ks] = ldcol8(&sm.dy[tq0 < C ? tq0 : 0][jw], Cfg::LDN, tq0 < C);
       }
       PFrag<TIn> LP[KSD];  // Lam as B operand, channels in accumulator order
 #pragma unroll

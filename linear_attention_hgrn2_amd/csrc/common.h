@@ -174,6 +174,23 @@ __device__ __forceinline__ PFrag<float> ld4x2(const float *p0, const float *p1) 
   f.x[4] = b.x; f.x[5] = b.y; f.x[6] = b.z; f.x[7] = b.w;
   return f;
 }
+// Gather 8 elements p[0], p[stride], ..., p[7 * stride] (a column of a
+// row-major LDS tile) straight into MFMA form; lanes with `valid` false get
+// zeros.  bf16 elements are loaded as 16-bit halves without a float round trip.
+__device__ __forceinline__ PFrag<bf16_t> ldcol8(const bf16_t *p, int stride, bool valid) {
+  PFrag<bf16_t> f;
+  const __bf16 z = (__bf16)0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f.x[i] = valid ? __builtin_bit_cast(__bf16, p[i * stride].bits) : z;
+  return f;
+}
+__device__ __forceinline__ PFrag<float> ldcol8(const float *p, int stride, bool valid) {
+  PFrag<float> f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f.x[i] = valid ? p[i * stride] : 0.f;
+  return f;
+}
+
 template <typename Op> __device__ __forceinline__ PFrag<Op> pfrag_zero() {
   Frag z;
   frag_zero(z);

@@ -320,13 +320,8 @@ __global__ __launch_bounds__(4 * DVT) void hgrn2_fwd_kernel(FwdArgs args) {
     PFrag<TIn> fv[KSC];
 #pragma unroll
     for (int ks = 0; ks < KSC; ++ks) {
-      Frag f;
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        const int s = ks * 32 + 8 * g + x;
-        f.v[x] = (s < C) ? to_f32(sm.v[s][w * 16 + n16]) : 0.f;
-      }
-      fv[ks] = to_pfrag<TIn>(f);
+      const int s0 = ks * 32 + 8 * g;
+      fv[ks] = ldcol8(&sm.v[s0 < C ? s0 : 0][w * 16 + n16], Cfg::LDV, s0 < C);
     }
 
     // ---- Y = A V + qo (e^{P_i} S_prev)  for this wave's 16 columns
