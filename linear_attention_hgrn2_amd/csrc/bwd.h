@@ -73,10 +73,18 @@ struct BwdCfg {
   static constexpr int VQ = C * D / EPV;
   static constexpr int NVQ = (VQ + NT - 1) / NT;
   struct SmemC {                 // channel side
-    float lT[D * TT32<C>::LD];   // ell, channel-major (TT32 layout)
+    union {
+      struct {
+        float lT[D * TT32<C>::LD];   // ell, channel-major (TT32 layout)
+        float koT[D * TT32<C>::LD];  // k e^{L_j - ell}
+      };
+      struct {                       // once dq and dk are done: output staging
+        TIn sq[C][LDN];              // dq
+        TIn sl[C][LDN];              // dlog_f
+      };
+    };
     float qoT[D * TT32<C>::LD];  // q e^{ell}
-    float koT[D * TT32<C>::LD];  // k e^{L_j - ell}
-    TIn v[C][LDN];
+    TIn v[C][LDN];               // V; once dk is done: dk staging
     TIn dy[C][LDN];
     TIn dA[C][LDA];              // dA[t][s], causal
     float Lb[NB][D];
@@ -86,7 +94,7 @@ struct BwdCfg {
   struct SmemV {                 // value side
     float l[C][LDL];             // ell, token-major
     TIn qo[C][LDN];              // q e^{ell}
-    TIn ko[C][LDN];              // k e^{L_j - ell}
+    TIn ko[C][LDN];              // k e^{L_j - ell}; once the score tiles are done: dv staging
     TIn kh[C][LDN];              // k e^{Gamma - b}
     TIn qhT[D * TTile<TIn, C>::LD];  // (q e^b)^T (TTile layout)
     TIn dy[C][LDN];
@@ -291,8 +299,8 @@ __device__ __forceinline__ void bwd_channel_side(const BwdArgs &args, typename B
 #pragma unroll
       for (int ks = 0; ks < KSD; ++ks) {
         const int c0 = ks * 32 + 8 * g;  // D = 16: lanes with c0 >= D feed zeros (the MFMA runs on the whole wave)
-        mma(acc, c0 < D ? ld8(&sm.v[s_row][c0]) : pfrag_zero<TIn>(),
-            c0 < D ? ld8(&sm.dy[t_col][c0]) : pfrag_zero<TIn>());
+        const bool ok = c0 < D;
+        mma(acc, masked(ld8(&sm.v[s_row][ok ? c0 : 0]), ok), ld8(&sm.dy[t_col][ok ? c0 : 0]));
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -302,73 +310,13 @@ __device__ __forceinline__ void bwd_channel_side(const BwdArgs &args, typename B
     }
     __syncthreads();
 
-    // ================= dq, dk, dlog_f for channel cw =================
-    float u[NB][4];  // q dq - k dk at tokens 16i + 4g + r
-    {
-      const int lane = opaque(tid & 63), n16 = lane & 15, g = lane >> 4, cw = w * 16 + n16;
-      PFrag<TIn> SP[KSD];
-#pragma unroll
-      for (int ks = 0; ks < KSD; ++ks) SP[ks] = to_pfrag<TIn>(Sprev[ks]);
-#pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        f32x4_t dq;
-        acc_zero(dq);
-        const int t = i * 16 + n16;
-        // inter: dY[t][j] S_prev[cw][j], j in the accumulator order of S_prev's fragment
-#pragma unroll
-        for (int ks = 0; ks < KSD; ++ks) {
-          const int j0 = 2 * ks * 16 + 4 * g;
-          const int j1 = (2 * ks + 1 < CB) ? j0 + 16 : j0;  // D = 16: slots 4-7 meet zeros of S_prev
-          mma(dq, ld4x2(&sm.dy[t][j0], &sm.dy[t][j1]), SP[ks]);
-        }
-        const float eP = __expf(sm.Pb[i][cw]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dq[r] *= eP;
-        // intra: sum_s dA[t][s] k_s e^{P_i - b_s}, s < 16(i+1)
-        const bool direct = (flags >> i) & 1;
-#pragma unroll
-        for (int ks = 0; ks < KSC; ++ks) {
-          if (ks * 32 < 16 * (i + 1)) {
-            const int s0 = ks * 32 + 8 * g;  // 8 tokens of one 16-block
-            const int sb = s0 >> 4;
-            const bool ok = s0 < 16 * (i + 1) && s0 < C && !(direct && sb == i);
-            Frag fb;
-            PFrag<TIn> fa;
-            if (ok) {
-              const float gap = (sb < i) ? __expf(sm.Pb[i][cw] - sm.Pb[sb + 1][cw]) : __expf(-sm.Lb[i][cw]);
-              fa = ld8(&sm.dA[t][s0]);
-              const float4 k0 = *(const float4 *)&sm.koT[TT32<C>::at(cw, s0)];
-              const float4 k1 = *(const float4 *)&sm.koT[TT32<C>::at(cw, s0 + 4)];
-              fb.v[0] = k0.x * gap; fb.v[1] = k0.y * gap; fb.v[2] = k0.z * gap; fb.v[3] = k0.w * gap;
-              fb.v[4] = k1.x * gap; fb.v[5] = k1.y * gap; fb.v[6] = k1.z * gap; fb.v[7] = k1.w * gap;
-            } else {
-              fa = pfrag_zero<TIn>();
-              frag_zero(fb);
-            }
-            mma_split(dq, fa, fb);
-          }
-        }
-        const float4 l4 = *(const float4 *)&sm.lT[TT32<C>::at(cw, i * 16 + 4 * g)];
-        const float4 q4 = *(const float4 *)&sm.qoT[TT32<C>::at(cw, i * 16 + 4 * g)];
-        const float ll[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float qq[4] = {q4.x, q4.y, q4.z, q4.w};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int tt = i * 16 + 4 * g + r;
-          u[i][r] = qq[r] * dq[r];  // q dq = (q e^{ell}) X
-          float val = dq[r] * __expf(ll[r]);
-          if (direct && tt < len) {
-            float a = 0.f;
-            for (int s = i * 16; s <= tt; ++s)
-              a += to_f32(sm.dA[tt][s]) * to_f32(gk[tok(t0 + s) + cw]) * __expf(ll[r] - sm.lT[TT32<C>::at(cw, s)]);
-            val += a;
-            u[i][r] += to_f32(gq[tok(t0 + tt) + cw]) * a;
-          }
-          if (tt < len) gdq[tok(t0 + tt) + cw] = from_f32<TIn>(val);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
+    // ================= dk, dq, dlog_f for channel cw =================
+    // Results are staged in LDS regions whose contents are dead by then and
+    // written out as whole rows (16-byte stores): the accumulator layout puts
+    // one channel per lane, so direct stores would be scattered 2-byte writes.
+    float u[NB][4];   // q dq - k dk at tokens 16i + 4g + r
+    float vk[NB][4];  // dk
+    float vq[NB][4];  // dq, then dlog_f
     {
       const int lane = opaque(tid & 63), n16 = lane & 15, g = lane >> 4, cw = w * 16 + n16;
       PFrag<TIn> LP[KSD];  // Lam^T as B operand, j in accumulator order
@@ -397,36 +345,37 @@ __device__ __forceinline__ void bwd_channel_side(const BwdArgs &args, typename B
         const float eG = __expf(sm.Pb[NB][cw] - sm.Pb[j + 1][cw]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) dk[r] *= eG;
-        // intra: sum_{t >= 16j} dA^T[s][t] q_t e^{b_t - E_j}
+        // intra: sum_{t >= 16j} dA^T[s][t] q_t e^{b_t - E_j}; the lane's 8 tokens lie
+        // in block tb with factor e^{P_tb - P_{j+1}} (tb > j) or e^{-L_j} (tb == j)
         const bool direct = (flags >> j) & 1;
 #pragma unroll
         for (int ks = 0; ks < KSC; ++ks) {
           if (ks * 32 + 32 > 16 * j) {
             const int tq0 = ks * 32 + 8 * g;
             const int tb = tq0 >> 4;
-            const bool ok = tq0 >= 16 * j && tq0 < C && !(direct && tb == j);
+            const bool ok = tb >= j && tq0 < C && !(direct && tb == j);
+            const int tbc = tb < NB ? tb : NB - 1;
+            const float ex = (tb > j) ? sm.Pb[tbc][cw] - sm.Pb[j + 1][cw] : -sm.Lb[j][cw];
+            const float gap = __expf(ok ? ex : 0.f);
+            const int tqc = tbc * 16 + (tq0 & 15);
+            const float4 q0 = ldf4(&sm.qoT[TT32<C>::at(cw, tqc)]);
+            const float4 q1 = ldf4(&sm.qoT[TT32<C>::at(cw, tqc + 4)]);
             Frag fb;
-            if (ok) {
-              const float gap = (tb > j) ? __expf(sm.Pb[tb][cw] - sm.Pb[j + 1][cw]) : __expf(-sm.Lb[j][cw]);
-              const float4 q0 = *(const float4 *)&sm.qoT[TT32<C>::at(cw, tq0)];
-              const float4 q1 = *(const float4 *)&sm.qoT[TT32<C>::at(cw, tq0 + 4)];
-              fb.v[0] = q0.x * gap; fb.v[1] = q0.y * gap; fb.v[2] = q0.z * gap; fb.v[3] = q0.w * gap;
-              fb.v[4] = q1.x * gap; fb.v[5] = q1.y * gap; fb.v[6] = q1.z * gap; fb.v[7] = q1.w * gap;
-            } else {
-              frag_zero(fb);
-            }
-            mma_split(dk, ldcol8(&sm.dA[ok ? tq0 : 0][s], Cfg::LDA, ok), fb);
+            fb.v[0] = q0.x * gap; fb.v[1] = q0.y * gap; fb.v[2] = q0.z * gap; fb.v[3] = q0.w * gap;
+            fb.v[4] = q1.x * gap; fb.v[5] = q1.y * gap; fb.v[6] = q1.z * gap; fb.v[7] = q1.w * gap;
+            masked(fb, ok);
+            mma_split(dk, ldcol8(&sm.dA[tqc][s], Cfg::LDA, ok), fb);
           }
         }
-        const float4 l4 = *(const float4 *)&sm.lT[TT32<C>::at(cw, j * 16 + 4 * g)];
-        const float4 k4 = *(const float4 *)&sm.koT[TT32<C>::at(cw, j * 16 + 4 * g)];
+        const float4 l4 = ldf4(&sm.lT[TT32<C>::at(cw, j * 16 + 4 * g)]);
+        const float4 k4 = ldf4(&sm.koT[TT32<C>::at(cw, j * 16 + 4 * g)]);
         const float ll[4] = {l4.x, l4.y, l4.z, l4.w};
         const float kk[4] = {k4.x, k4.y, k4.z, k4.w};
         const float Lj = sm.Lb[j][cw];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int ss = j * 16 + 4 * g + r;
-          u[j][r] -= kk[r] * dk[r];  // k dk = (k e^{L_j - ell}) Z
+          u[j][r] = -kk[r] * dk[r];  // k dk = (k e^{L_j - ell}) Z
           float val = dk[r] * __expf(Lj - ll[r]);
           if (direct && ss < len) {
             float a = 0.f;
@@ -435,10 +384,90 @@ __device__ __forceinline__ void bwd_channel_side(const BwdArgs &args, typename B
             val += a;
             u[j][r] -= to_f32(gk[tok(t0 + ss) + cw]) * a;
           }
-          if (ss < len) gdk[tok(t0 + ss) + cw] = from_f32<TIn>(val);
+          vk[j][r] = val;
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+    }
+    __syncthreads();  // every wave is done with V
+    {
+      const int lane = opaque(tid & 63), n16 = lane & 15, g = lane >> 4, cw = w * 16 + n16;
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm.v[j * 16 + 4 * g + r][cw] = from_f32<TIn>(vk[j][r]);
+    }
+    {
+      const int lane = opaque(tid & 63), n16 = lane & 15, g = lane >> 4, cw = w * 16 + n16;
+      PFrag<TIn> SP[KSD];
+#pragma unroll
+      for (int ks = 0; ks < KSD; ++ks) SP[ks] = to_pfrag<TIn>(Sprev[ks]);
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        f32x4_t dq;
+        acc_zero(dq);
+        const int t = i * 16 + n16;
+        // inter: dY[t][j] S_prev[cw][j], j in the accumulator order of S_prev's fragment
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) {
+          const int j0 = 2 * ks * 16 + 4 * g;
+          const int j1 = (2 * ks + 1 < CB) ? j0 + 16 : j0;  // D = 16: slots 4-7 meet zeros of S_prev
+          mma(dq, ld4x2(&sm.dy[t][j0], &sm.dy[t][j1]), SP[ks]);
+        }
+        const float eP = __expf(sm.Pb[i][cw]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dq[r] *= eP;
+        // intra: sum_s dA[t][s] k_s e^{P_i - b_s}, s < 16(i+1).  The 8 tokens of a
+        // lane's slots lie in one 16-block sb; its factor is e^{P_i - P_{sb+1}}
+        // (sb < i) or e^{-L_i} (sb == i).  Branch-free: invalid lanes are masked.
+        const bool direct = (flags >> i) & 1;
+#pragma unroll
+        for (int ks = 0; ks < KSC; ++ks) {
+          if (ks * 32 < 16 * (i + 1)) {
+            const int s0 = ks * 32 + 8 * g;  // 8 tokens of one 16-block
+            const int sb = s0 >> 4;
+            const bool ok = sb <= i && !(direct && sb == i);
+            const int sbc = sb < NB ? sb : NB - 1;
+            const float ex = (sb < i) ? sm.Pb[i][cw] - sm.Pb[sbc + 1][cw] : -sm.Lb[i][cw];
+            const float gap = __expf(ok ? ex : 0.f);
+            const int s0c = sbc * 16 + (s0 & 15);
+            const float4 k0 = ldf4(&sm.koT[TT32<C>::at(cw, s0c)]);
+            const float4 k1 = ldf4(&sm.koT[TT32<C>::at(cw, s0c + 4)]);
+            Frag fb;
+            fb.v[0] = k0.x * gap; fb.v[1] = k0.y * gap; fb.v[2] = k0.z * gap; fb.v[3] = k0.w * gap;
+            fb.v[4] = k1.x * gap; fb.v[5] = k1.y * gap; fb.v[6] = k1.z * gap; fb.v[7] = k1.w * gap;
+            masked(fb, ok);
+            mma_split(dq, ld8(&sm.dA[t][s0c]), fb);
+          }
+        }
+        const float4 l4 = ldf4(&sm.lT[TT32<C>::at(cw, i * 16 + 4 * g)]);
+        const float4 q4 = ldf4(&sm.qoT[TT32<C>::at(cw, i * 16 + 4 * g)]);
+        const float ll[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float qq[4] = {q4.x, q4.y, q4.z, q4.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tt = i * 16 + 4 * g + r;
+          u[i][r] += qq[r] * dq[r];  // q dq = (q e^{ell}) X
+          float val = dq[r] * __expf(ll[r]);
+          if (direct && tt < len) {
+            float a = 0.f;
+            for (int s = i * 16; s <= tt; ++s)
+              a += to_f32(sm.dA[tt][s]) * to_f32(gk[tok(t0 + s) + cw]) * __expf(ll[r] - sm.lT[TT32<C>::at(cw, s)]);
+            val += a;
+            u[i][r] += to_f32(gq[tok(t0 + tt) + cw]) * a;
+          }
+          vq[i][r] = val;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __syncthreads();  // every wave is done with dA, lT, koT
+    {
+      const int lane = opaque(tid & 63), n16 = lane & 15, g = lane >> 4, cw = w * 16 + n16;
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm.sq[i * 16 + 4 * g + r][cw] = from_f32<TIn>(vq[i][r]);
     }
     {  // dlog_f: reverse cumulative sum of u inside the chunk, plus the carry
       const int lane = opaque(tid & 63), n16 = lane & 15, g = lane >> 4, cw = w * 16 + n16;
@@ -466,9 +495,32 @@ __device__ __forceinline__ void bwd_channel_side(const BwdArgs &args, typename B
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = i * 16 + 4 * g + r;
-          if (t < len) gdl[tok(t0 + t) + cw] = from_f32<TIn>(suf[i][r] + above + rest);
+          vq[i][r] = suf[i][r] + above + rest;  // dq already staged: reuse its registers
         }
         rest += blk;
+      }
+    }
+
+    {
+      const int lane = opaque(tid & 63), n16 = lane & 15, g = lane >> 4, cw = w * 16 + n16;
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm.sl[i * 16 + 4 * g + r][cw] = from_f32<TIn>(vq[i][r]);
+    }
+    __syncthreads();
+    {  // whole-row stores of dk, dq, dlog_f
+      const int tid = opaque(threadIdx.x);
+#pragma unroll
+      for (int it = 0; it < Cfg::NVQ; ++it) {
+        const int idx = tid + it * NT;
+        const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
+        if (idx < Cfg::VQ && row < len) {
+          const size_t off = tok(t0 + row) + col;
+          *(uint4 *)(gdk + off) = *(const uint4 *)&sm.v[row][col];
+          *(uint4 *)(gdq + off) = *(const uint4 *)&sm.sq[row][col];
+          *(uint4 *)(gdl + off) = *(const uint4 *)&sm.sl[row][col];
+        }
       }
     }
 
@@ -480,16 +532,15 @@ __device__ __forceinline__ void bwd_channel_side(const BwdArgs &args, typename B
 #pragma unroll
       for (int ks = 0; ks < KSC; ++ks) {
         const int tq0 = ks * 32 + 8 * g;
+        const bool ok = tq0 < C;
+        const int tqc = ok ? tq0 : 0;
+        const float eP = __expf(sm.Pb[tqc >> 4][cw]);
+        const float4 q0 = ldf4(&sm.qoT[TT32<C>::at(cw, tqc)]);
+        const float4 q1 = ldf4(&sm.qoT[TT32<C>::at(cw, tqc + 4)]);
         Frag f;
-        if (tq0 < C) {
-          const float eP = __expf(sm.Pb[tq0 >> 4][cw]);
-          const float4 q0 = *(const float4 *)&sm.qoT[TT32<C>::at(cw, tq0)];
-          const float4 q1 = *(const float4 *)&sm.qoT[TT32<C>::at(cw, tq0 + 4)];
-          f.v[0] = q0.x * eP; f.v[1] = q0.y * eP; f.v[2] = q0.z * eP; f.v[3] = q0.w * eP;
-          f.v[4] = q1.x * eP; f.v[5] = q1.y * eP; f.v[6] = q1.z * eP; f.v[7] = q1.w * eP;
-        } else {
-          frag_zero(f);
-        }
+        f.v[0] = q0.x * eP; f.v[1] = q0.y * eP; f.v[2] = q0.z * eP; f.v[3] = q0.w * eP;
+        f.v[4] = q1.x * eP; f.v[5] = q1.y * eP; f.v[6] = q1.z * eP; f.v[7] = q1.w * eP;
+        masked(f, ok);
         fqh[ks] = to_pfrag<TIn>(f);
       }
 #pragma unroll
@@ -671,22 +722,17 @@ __device__ __forceinline__ void bwd_value_side(const BwdArgs &args, typename Bwd
 #pragma unroll
         for (int ks = 0; ks < KSD; ++ks) {
           const int c0 = ks * 32 + 8 * g;  // D = 16: lanes with c0 >= D feed zeros
+          const bool ok = c0 < D;
+          const int cc = ok ? c0 : 0;
+          float kv[8];
+          Vec<TIn>::unpack(*(const uint4 *)&sm.ko[s_col][cc], kv);
+          if constexpr (EPV == 4) Vec<TIn>::unpack(*(const uint4 *)&sm.ko[s_col][cc + 4], kv + 4);
+          const float4 g0 = ldf4(&sm.gp[pi][cc]);
+          const float4 g1 = ldf4(&sm.gp[pi][cc + 4]);
           Frag fb;
-          PFrag<TIn> fa;
-          if (c0 < D) {
-            float kv[8];
-            Vec<TIn>::unpack(*(const uint4 *)&sm.ko[s_col][c0], kv);
-            if constexpr (EPV == 4) Vec<TIn>::unpack(*(const uint4 *)&sm.ko[s_col][c0 + 4], kv + 4);
-            const float4 g0 = *(const float4 *)&sm.gp[pi][c0];
-            const float4 g1 = *(const float4 *)&sm.gp[pi][c0 + 4];
-            fb.v[0] = kv[0] * g0.x; fb.v[1] = kv[1] * g0.y; fb.v[2] = kv[2] * g0.z; fb.v[3] = kv[3] * g0.w;
-            fb.v[4] = kv[4] * g1.x; fb.v[5] = kv[5] * g1.y; fb.v[6] = kv[6] * g1.z; fb.v[7] = kv[7] * g1.w;
-            fa = ld8(&sm.qo[t_row][c0]);
-          } else {
-            frag_zero(fb);
-            fa = pfrag_zero<TIn>();
-          }
-          mma(acc, fa, to_pfrag<TIn>(fb));
+          fb.v[0] = kv[0] * g0.x; fb.v[1] = kv[1] * g0.y; fb.v[2] = kv[2] * g0.z; fb.v[3] = kv[3] * g0.w;
+          fb.v[4] = kv[4] * g1.x; fb.v[5] = kv[5] * g1.y; fb.v[6] = kv[6] * g1.z; fb.v[7] = kv[7] * g1.w;
+          mma(acc, masked(ld8(&sm.qo[t_row][cc]), ok), to_pfrag<TIn>(fb));
         }
       } else {
 #pragma unroll
@@ -746,21 +792,29 @@ __device__ __forceinline__ void bwd_value_side(const BwdArgs &args, typename Bwd
         for (int ks = 0; ks < KSC; ++ks) {
           if (ks * 32 + 32 > 16 * j) {
             const int t0f = ks * 32 + 8 * g;
-            const PFrag<TIn> fa = (t0f >= 16 * j && t0f < C) ? ld8(&sm.At[s][t0f]) : pfrag_zero<TIn>();
-            mma(acc, fa, fdyT[ks]);
+            const bool ok = t0f >= 16 * j && t0f < C;
+            mma(acc, masked(ld8(&sm.At[s][ok ? t0f : 0]), ok), fdyT[ks]);
           }
         }
+        // staged in ko (dead since the score tiles) and stored as whole rows below
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int ss = j * 16 + 4 * g + r;
-          if (ss < len) gdv[tok(t0 + ss) + jw] = from_f32<TIn>(acc[r]);
-        }
+        for (int r = 0; r < 4; ++r) sm.ko[j * 16 + 4 * g + r][jw] = from_f32<TIn>(acc[r]);
         __builtin_amdgcn_sched_barrier(0);
+      }
+      __syncthreads();
+      {
+        const int tid = opaque(threadIdx.x);
+#pragma unroll
+        for (int it = 0; it < Cfg::NVQ; ++it) {
+          const int idx = tid + it * NT;
+          const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
+          if (idx < Cfg::VQ && row < len) *(uint4 *)(gdv + tok(t0 + row) + col) = *(const uint4 *)&sm.ko[row][col];
+        }
       }
       // Lam[c][jw] <- e^{Gamma} Lam + sum_t (q e^b)[t][c] dY[t][jw]
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        const float4 g4 = *(const float4 *)&sm.Pb[NB][cb * 16 + 4 * g];
+        const float4 g4 = ldf4(&sm.Pb[NB][cb * 16 + 4 * g]);
         Lam[cb][0] *= __expf(g4.x);
         Lam[cb][1] *= __expf(g4.y);
         Lam[cb][2] *= __expf(g4.z);
@@ -769,8 +823,8 @@ __device__ __forceinline__ void bwd_value_side(const BwdArgs &args, typename Bwd
 #pragma unroll
         for (int ks = 0; ks < KSC; ++ks) {
           const int tq0 = ks * 32 + 8 * g;
-          const PFrag<TIn> fa = (tq0 < C) ? ldT8<C>(sm.qhT, crow, tq0) : pfrag_zero<TIn>();
-          mma(Lam[cb], fa, fdyT[ks]);
+          const bool ok = tq0 < C;
+          mma(Lam[cb], masked(ldT8<C>(sm.qhT, crow, ok ? tq0 : 0), ok), fdyT[ks]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }

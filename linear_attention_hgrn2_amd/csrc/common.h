@@ -146,12 +146,13 @@ __device__ __forceinline__ void mma(f32x4_t &acc, const PFrag<float> &a, const P
 // ld4x2: slots 0-3 from p0 and 4-7 from p1 (each 4 consecutive elements).
 __device__ __forceinline__ PFrag<bf16_t> ld8(const bf16_t *p) {
   PFrag<bf16_t> f;
-  f.x = *(const bf16x8_t *)p;
+  f.x = *(const bf16x8_t *)__builtin_assume_aligned(p, 16);
   return f;
 }
 __device__ __forceinline__ PFrag<float> ld8(const float *p) {
   PFrag<float> f;
-  const float4 a = ((const float4 *)p)[0], b = ((const float4 *)p)[1];
+  const float4 *q = (const float4 *)__builtin_assume_aligned(p, 16);
+  const float4 a = q[0], b = q[1];
   f.x[0] = a.x; f.x[1] = a.y; f.x[2] = a.z; f.x[3] = a.w;
   f.x[4] = b.x; f.x[5] = b.y; f.x[6] = b.z; f.x[7] = b.w;
   return f;
@@ -161,34 +162,68 @@ __device__ __forceinline__ PFrag<bf16_t> ld4x2(const bf16_t *p0, const bf16_t *p
     uint2 u[2];
     bf16x8_t v;
   } t;
-  t.u[0] = *(const uint2 *)p0;
-  t.u[1] = *(const uint2 *)p1;
+  t.u[0] = *(const uint2 *)__builtin_assume_aligned(p0, 8);
+  t.u[1] = *(const uint2 *)__builtin_assume_aligned(p1, 8);
   PFrag<bf16_t> f;
   f.x = t.v;
   return f;
 }
 __device__ __forceinline__ PFrag<float> ld4x2(const float *p0, const float *p1) {
   PFrag<float> f;
-  const float4 a = *(const float4 *)p0, b = *(const float4 *)p1;
+  const float4 a = *(const float4 *)__builtin_assume_aligned(p0, 16);
+  const float4 b = *(const float4 *)__builtin_assume_aligned(p1, 16);
   f.x[0] = a.x; f.x[1] = a.y; f.x[2] = a.z; f.x[3] = a.w;
   f.x[4] = b.x; f.x[5] = b.y; f.x[6] = b.z; f.x[7] = b.w;
   return f;
 }
+// Zero a fragment on lanes where `valid` is false, without branching (the
+// bits are masked, so even inf/NaN inputs become exact zeros).
+__device__ __forceinline__ PFrag<bf16_t> masked(const PFrag<bf16_t> &f, bool valid) {
+  union {
+    bf16x8_t v;
+    uint32_t u[4];
+  } t;
+  t.v = f.x;
+  const uint32_t m = valid ? 0xffffffffu : 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) t.u[i] &= m;
+  PFrag<bf16_t> r;
+  r.x = t.v;
+  return r;
+}
+__device__ __forceinline__ PFrag<float> masked(const PFrag<float> &f, bool valid) {
+  const uint32_t m = valid ? 0xffffffffu : 0u;
+  PFrag<float> r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r.x[i] = __uint_as_float(__float_as_uint(f.x[i]) & m);
+  return r;
+}
+__device__ __forceinline__ void masked(Frag &f, bool valid) {
+  const uint32_t m = valid ? 0xffffffffu : 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f.v[i] = __uint_as_float(__float_as_uint(f.v[i]) & m);
+}
+
 // Gather 8 elements p[0], p[stride], ..., p[7 * stride] (a column of a
-// row-major LDS tile) straight into MFMA form; lanes with `valid` false get
-// zeros.  bf16 elements are loaded as 16-bit halves without a float round trip.
+// row-major LDS tile) straight into MFMA form.  The caller passes an
+// in-bounds p for every lane; lanes with `valid` false get zeros.  bf16
+// elements are loaded as 16-bit halves without a float round trip.
 __device__ __forceinline__ PFrag<bf16_t> ldcol8(const bf16_t *p, int stride, bool valid) {
   PFrag<bf16_t> f;
-  const __bf16 z = (__bf16)0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) f.x[i] = valid ? __builtin_bit_cast(__bf16, p[i * stride].bits) : z;
-  return f;
+  for (int i = 0; i < 8; ++i) f.x[i] = __builtin_bit_cast(__bf16, p[i * stride].bits);
+  return masked(f, valid);
 }
 __device__ __forceinline__ PFrag<float> ldcol8(const float *p, int stride, bool valid) {
   PFrag<float> f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) f.x[i] = valid ? p[i * stride] : 0.f;
-  return f;
+  for (int i = 0; i < 8; ++i) f.x[i] = p[i * stride];
+  return masked(f, valid);
+}
+
+// 16-byte aligned float4 load from LDS (the tiles guarantee the alignment).
+__device__ __forceinline__ float4 ldf4(const float *p) {
+  return *(const float4 *)__builtin_assume_aligned(p, 16);
 }
 
 template <typename Op> __device__ __forceinline__ PFrag<Op> pfrag_zero() {

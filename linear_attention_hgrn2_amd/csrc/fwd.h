@@ -57,7 +57,13 @@ struct FwdCfg {
   static constexpr int NVQ = (VQ + NT - 1) / NT;
   static constexpr int NVV = (VV + NT - 1) / NT;
   struct Smem {
-    float l[C][LDL];          // block-local inclusive prefix of floored log f
+    union {
+      float l[C][LDL];        // block-local inclusive prefix of floored log f
+      struct {                // after the score tiles: output staging
+        TIn ys[C][LDV];       // y slice
+        TIn ss[D][LDV];       // chunk-boundary state slice
+      };
+    };
     TIn qo[C][LDN];           // q e^{ell}
     TIn ko[C][LDN];           // k e^{L_j - ell}
     TIn khT[D * TTile<TIn, C>::LD];  // (k e^{Gamma - b})^T (TTile layout)
@@ -270,28 +276,17 @@ __global__ __launch_bounds__(4 * DVT) void hgrn2_fwd_kernel(FwdArgs args) {
 #pragma unroll
         for (int ks = 0; ks < KSD; ++ks) {
           const int c0 = ks * 32 + 8 * g;
-          Frag fa, fb;
-          if (c0 < D) {
-            float kv[8], qv[8];
-            Vec<TIn>::unpack(*(const uint4 *)&sm.ko[s_row][c0], kv);
-            Vec<TIn>::unpack(*(const uint4 *)&sm.qo[t_col][c0], qv);
-            if constexpr (EPV == 4) {
-              Vec<TIn>::unpack(*(const uint4 *)&sm.ko[s_row][c0 + 4], kv + 4);
-              Vec<TIn>::unpack(*(const uint4 *)&sm.qo[t_col][c0 + 4], qv + 4);
-            }
-            const float4 g0 = *(const float4 *)&sm.gp[pi][c0];
-            const float4 g1 = *(const float4 *)&sm.gp[pi][c0 + 4];
-            const float gv8[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-#pragma unroll
-            for (int x = 0; x < 8; ++x) {
-              fa.v[x] = kv[x] * gv8[x];
-              fb.v[x] = qv[x];
-            }
-          } else {
-            frag_zero(fa);
-            frag_zero(fb);
-          }
-          Mma<TIn>::run(acc, fa, fb);
+          const bool ok = c0 < D;  // D = 16: lanes past the channels feed zeros
+          const int cc = ok ? c0 : 0;
+          float kv[8];
+          Vec<TIn>::unpack(*(const uint4 *)&sm.ko[s_row][cc], kv);
+          if constexpr (EPV == 4) Vec<TIn>::unpack(*(const uint4 *)&sm.ko[s_row][cc + 4], kv + 4);
+          const float4 g0 = ldf4(&sm.gp[pi][cc]);
+          const float4 g1 = ldf4(&sm.gp[pi][cc + 4]);
+          Frag fa;
+          fa.v[0] = kv[0] * g0.x; fa.v[1] = kv[1] * g0.y; fa.v[2] = kv[2] * g0.z; fa.v[3] = kv[3] * g0.w;
+          fa.v[4] = kv[4] * g1.x; fa.v[5] = kv[5] * g1.y; fa.v[6] = kv[6] * g1.z; fa.v[7] = kv[7] * g1.w;
+          mma(acc, to_pfrag<TIn>(fa), masked(ld8(&sm.qo[t_col][cc]), ok));
         }
       } else {
         // wide in-block decay: A[t][s] = sum_c q_t k_s e^{ell_t - ell_s}, every exponent <= 0
@@ -334,7 +329,8 @@ __global__ __launch_bounds__(4 * DVT) void hgrn2_fwd_kernel(FwdArgs args) {
       for (int ks = 0; ks < KSC; ++ks) {
         if (ks * 32 < 16 * (tb + 1)) {
           const int s0 = ks * 32 + 8 * g;
-          mma(Y[tb], (s0 < 16 * (tb + 1) && s0 < C) ? ld8(&sm.a[t][s0]) : pfrag_zero<TIn>(), fv[ks]);
+          const bool ok = s0 < 16 * (tb + 1) && s0 < C;
+          mma(Y[tb], masked(ld8(&sm.a[t][ok ? s0 : 0]), ok), fv[ks]);
         }
       }
       // channels in the accumulator order of S (slots 0-3: block 2ks, 4-7: block 2ks+1)
@@ -345,7 +341,7 @@ __global__ __launch_bounds__(4 * DVT) void hgrn2_fwd_kernel(FwdArgs args) {
         for (int hf = 0; hf < 2; ++hf) {
           const int cb = 2 * ks + hf;
           if (cb < CB) {
-            const float4 e4 = *(const float4 *)&sm.ePb[tb][cb * 16 + 4 * g];
+            const float4 e4 = ldf4(&sm.ePb[tb][cb * 16 + 4 * g]);
             fb.v[4 * hf + 0] = S[cb][0] * e4.x;
             fb.v[4 * hf + 1] = S[cb][1] * e4.y;
             fb.v[4 * hf + 2] = S[cb][2] * e4.z;
@@ -364,7 +360,7 @@ __global__ __launch_bounds__(4 * DVT) void hgrn2_fwd_kernel(FwdArgs args) {
     // ---- S <- e^Gamma S + (k e^{Gamma-b})^T V
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      const float4 e4 = *(const float4 *)&sm.eG[cb * 16 + 4 * g];
+      const float4 e4 = ldf4(&sm.eG[cb * 16 + 4 * g]);
       S[cb][0] *= e4.x;
       S[cb][1] *= e4.y;
       S[cb][2] *= e4.z;
@@ -373,22 +369,47 @@ __global__ __launch_bounds__(4 * DVT) void hgrn2_fwd_kernel(FwdArgs args) {
 #pragma unroll
       for (int ks = 0; ks < KSC; ++ks) {
         const int s0 = ks * 32 + 8 * g;
-        mma(S[cb], (s0 < C) ? ldT8<C>(sm.khT, c, s0) : pfrag_zero<TIn>(), fv[ks]);
+        const bool ok = s0 < C;
+        mma(S[cb], masked(ldT8<C>(sm.khT, c, ok ? s0 : 0), ok), fv[ks]);
       }
     }
 
-    // ---- outputs
-    if (gy) {
+    // ---- outputs, staged in the dead prefix tile and stored as whole rows
+    // (the accumulators hold one column per lane, so direct stores would be
+    // scattered 2-byte writes)
 #pragma unroll
-      for (int tb = 0; tb < NB; ++tb)
+    for (int tb = 0; tb < NB; ++tb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = tb * 16 + 4 * g + r;
-          if (t < len) gy[tok(t0 + t) + jcol] = from_f32<TIn>(Y[tb][r]);
+      for (int r = 0; r < 4; ++r) sm.ys[tb * 16 + 4 * g + r][w * 16 + n16] = from_f32<TIn>(Y[tb][r]);
+    if (gst) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm.ss[cb * 16 + 4 * g + r][w * 16 + n16] = from_f32<TIn>(S[cb][r]);
+    }
+    }
+    __syncthreads();
+    {
+      const int tid = opaque(threadIdx.x);
+      if (gy) {
+#pragma unroll
+        for (int it = 0; it < Cfg::NVV; ++it) {
+          const int idx = tid + it * NT;
+          const int row = idx / (DVT / EPV), col = (idx % (DVT / EPV)) * EPV;
+          if (idx < Cfg::VV && row < len) *(uint4 *)(gy + tok(t0 + row) + j0 + col) = *(const uint4 *)&sm.ys[row][col];
         }
+      }
+      if (gst) {
+        TIn *st = gst + ((size_t)bh * (N + 1) + n + 1) * SS;
+        constexpr int VS = D * DVT / EPV;
+#pragma unroll
+        for (int it = 0; it < (VS + NT - 1) / NT; ++it) {
+          const int idx = tid + it * NT;
+          const int row = idx / (DVT / EPV), col = (idx % (DVT / EPV)) * EPV;
+          if (idx < VS) *(uint4 *)(st + (size_t)row * D + j0 + col) = *(const uint4 *)&sm.ss[row][col];
+        }
+      }
     }
-    }
-    if (gst) store_state(n + 1);
   }
   if (args.ht) {
 #pragma unroll
