@@ -27,6 +27,16 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_SUMMARY = os.path.join(PROFILES, "hgrn2_traffic_train_bf16_B8H16T4096.txt")
+CALIB_BYTES = 1 << 30          # the --calib-copy device copy: 1 GiB read, 1 GiB written
+
+# the commands whose output --summarize turns into the files under profiles/
+TRACE_CMD = ("rocprofv3 --kernel-trace --stats -d gpurun_out/trace -o run --output-format csv "
+             "-- python3 bench.py --steps 5 --warmup 1 --no-cpu")
+PMC_CMD = ("rocprofv3 --pmc {ctr} -d gpurun_out/{dir} -o run --output-format csv "
+           "-- python3 bench.py --only train --steps 2 --warmup 1 --no-cpu --calib-copy")
+
 
 def parse():
     p = argparse.ArgumentParser()
@@ -38,7 +48,37 @@ def parse():
     p.add_argument("--only", choices=["train", "decode", "all"], default="all")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 1 GiB device copy (calibrates profiler byte counters)")
+    p.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                   help="write the profiles/ summaries from rocprofv3 csv output and exit")
     return p.parse_args()
+
+
+def kernel_source_digest() -> str:
+    """Digest of the kernel sources; a traffic figure taken on other sources is void."""
+    import hashlib
+    csrc = os.path.join(ROOT, "linear_attention_hgrn2_amd", "csrc")
+    h = hashlib.sha256()
+    for n in sorted(os.listdir(csrc)):
+        if n.endswith((".h", ".hip", ".cpp")):
+            h.update(n.encode())
+            with open(os.path.join(csrc, n), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` (calibrated FETCH_SIZE + WRITE_SIZE) from the
+    committed counter summary, or None if it is missing or was taken on other sources."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            lines = f.read().splitlines()
+    except OSError:
+        return None
+    kv = dict(l.split(": ", 1) for l in lines if ": " in l and not l.startswith(" "))
+    if kv.get("source_digest") != kernel_source_digest():
+        return None
+    v = kv.get("traffic_bytes_per_launch " + kernel)
+    return None if v is None else float(v)
 
 
 def log(*a):
@@ -106,24 +146,20 @@ def bench_train(torch, m, args):
         step(i)
     torch.cuda.synchronize()
     log("warmup done")
-    # timed region: exactly `steps` steps, bracketed by synchronisation
+    # timed region: exactly `steps` steps, bracketed by synchronisation; the
+    # events around each launch are recorded on the stream the kernels run on
+    timer = KernelTimer(torch)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record()
     for i in range(args.steps):
-        step(i)
+        step(i, timer)
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
-    log("timed: %.3f ms/step" % ms)
-    # per-kernel durations (separate pass with events between the two launches)
-    timer = KernelTimer(torch)
-    for i in range(args.steps):
-        step(i, timer)
-    torch.cuda.synchronize()
     fwd_ms, bwd_ms = timer.mean_ms("fwd"), timer.mean_ms("bwd")
-    log("fwd %.3f ms, bwd %.3f ms" % (fwd_ms, bwd_ms))
+    log("timed: %.3f ms/step (fwd %.3f ms, bwd %.3f ms)" % (ms, fwd_ms, bwd_ms))
     return dict(w=w, ms=ms, fwd_ms=fwd_ms, bwd_ms=bwd_ms, host=sets[0]["host"])
 
 
@@ -154,33 +190,116 @@ def bench_decode(torch, m, args):
     return dict(ms=ms, gbs=gbs, bytes=2 * state_bytes + vec_bytes)
 
 
-def cpu_baseline(res):
-    """The float64 oracle on a bounded sample of the same workload: whole
-    sequences (all T tokens) of some (b, h) pairs, forward + backward."""
+def cpu_baseline(res, min_seconds=10.0, max_reps=8):
+    """The float64 oracle on the host cores over the same training batch (all
+    (b, h) sequences, all tokens, forward + backward), repeated until about
+    `min_seconds` of CPU time has passed; the rate is the mean over repetitions."""
     import oracle
     import synth
     w = res["w"]
     d = res["host"]
     threads = oracle.threads()
-    nslice = w.B * w.H                     # the whole batch: a few seconds of CPU time
-    pairs = [(i // w.H, i % w.H) for i in range(nslice)]
-    from tests.gpu_util import select_bh
     x = {n: synth.to_f64(d[n], "bf16") for n in ("q", "k", "v", "log_f", "dy")}
-    sub = {n: select_bh(x[n], pairs) for n in x}
-    t0 = time.time()
-    oracle.forward(sub["q"], sub["k"], sub["v"], sub["log_f"], None)
-    oracle.backward(sub["q"], sub["k"], sub["v"], sub["log_f"], sub["dy"], None, None)
+    reps, t0 = 0, time.time()
+    while reps < max_reps and (reps == 0 or time.time() - t0 < min_seconds):
+        oracle.forward(x["q"], x["k"], x["v"], x["log_f"], None)
+        oracle.backward(x["q"], x["k"], x["v"], x["log_f"], x["dy"], None, None)
+        reps += 1
     dt = time.time() - t0
-    token_heads = nslice * w.T
-    tokens_per_s = token_heads / w.H / dt
-    log("cpu oracle: %d (b,h) sequences of T=%d in %.2f s on %d threads" % (nslice, w.T, dt, threads))
+    tokens_per_s = reps * w.B * w.T / dt
+    log("cpu oracle: %d x the B%d T%d batch in %.2f s on %d threads" % (reps, w.B, w.T, dt, threads))
     return {"value": tokens_per_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "%d of %d (b,h) sequences, all %d tokens each, fwd+bwd in float64 (%.1f s)"
-                      % (nslice, w.B * w.H, w.T, dt)}
+            "sample": "the whole B%d H%d T%d batch, fwd+bwd in float64, %d repetitions (%.1f s)"
+                      % (w.B, w.H, w.T, reps, dt)}
+
+
+def _csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _short(name: str) -> str:
+    n = name.split("(")[0]
+    return n.replace("void ", "").replace("hgrn2::", "")
+
+
+def summarize(trace_dir, fetch_dir, write_dir):
+    """profiles/ summaries from the csv output of TRACE_CMD and the two PMC_CMD runs."""
+    digest = kernel_source_digest()
+    # kernel-trace statistics
+    rows = _csv(os.path.join(trace_dir, "run_kernel_stats.csv"))
+    out = ["rocprofv3 kernel-trace statistics, HGRN2 training step (B8 H16 T4096 d128 bf16 chunk64)",
+           "and decode step (B256 H16 d128 fp32 state)",
+           "command: " + TRACE_CMD, "source_digest: " + digest, "",
+           "%-52s %6s %12s %10s %10s %10s %6s" % ("kernel", "calls", "total_us", "avg_us",
+                                                    "min_us", "max_us", "pct")]
+    for r in rows:
+        out.append("%-52s %6d %12.1f %10.1f %10.1f %10.1f %6.2f" % (
+            _short(r["Name"])[:52], int(r["Calls"]), float(r["TotalDurationNs"]) / 1e3,
+            float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+            float(r["Percentage"])))
+    kt = _csv(os.path.join(trace_dir, "run_kernel_trace.csv"))
+    seen = set()
+    out.append("")
+    for r in kt:
+        n = _short(r["Kernel_Name"])
+        if n in seen or not n.startswith("hgrn2_"):
+            continue
+        seen.add(n)
+        out.append("  %s: grid %s wg %s vgpr %s agpr %s sgpr %s lds %s scratch %s" % tuple(
+            [n] + [r.get(c, "?") for c in ("Grid_Size_X", "Workgroup_Size_X", "VGPR_Count",
+                                           "Accum_VGPR_Count", "SGPR_Count", "LDS_Block_Size",
+                                           "Scratch_Size")]))
+    name = os.path.join(PROFILES, "hgrn2_kernels_train_bf16_B8H16T4096_decode_B256H16.txt")
+    with open(name, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+    # HBM traffic from FETCH_SIZE / WRITE_SIZE (KiB per dispatch)
+    def per_kernel(d, ctr):
+        acc = {}
+        for r in _csv(os.path.join(d, "run_counter_collection.csv")):
+            if r["Counter_Name"] == ctr:
+                acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    copy = [k for k in fetch if "copyBuffer" in k]
+    assert copy, "the counter runs need --calib-copy"
+    f_fac = CALIB_BYTES / (fetch[copy[0]] * 1024)
+    w_fac = CALIB_BYTES / (write[copy[0]] * 1024)
+    w = __import__("synth").WORKLOADS["train_bf16"]
+    tok = w.B * w.T * w.H * w.D * 2
+    st = w.B * w.H * (w.T // w.chunk + 1) * w.D * w.D * 2
+    alg = {"hgrn2_fwd_kernel": (4 * tok, tok + st), "hgrn2_bwd_kernel": (5 * tok + st, 4 * tok)}
+    out = ["HBM traffic per launch, HGRN2 training step (B8 H16 T4096 d128 bf16 chunk64)",
+           "fetch command: " + PMC_CMD.format(ctr="FETCH_SIZE", dir="fetch"),
+           "write command: " + PMC_CMD.format(ctr="WRITE_SIZE", dir="write"),
+           "calibration: a 1 GiB device copy reads FETCH_SIZE %.0f KiB and WRITE_SIZE %.0f KiB"
+           % (fetch[copy[0]], write[copy[0]]),
+           "fetch_scale: %.4f" % f_fac, "write_scale: %.4f" % w_fac,
+           "source_digest: " + digest, ""]
+    for k in fetch:
+        short = _short(k).split("<")[0]
+        if short not in alg:
+            continue
+        fb, wb = fetch[k] * 1024 * f_fac, write[k] * 1024 * w_fac
+        ar, aw = alg[short]
+        out.append("  %s: read %.1f MB (algorithmic %.1f), written %.1f MB (algorithmic %.1f), "
+                   "total / algorithmic = %.3f" % (_short(k), fb / 1e6, ar / 1e6, wb / 1e6, aw / 1e6,
+                                                   (fb + wb) / (ar + aw)))
+        out.append("traffic_bytes_per_launch %s: %.0f" % (short, fb + wb))
+    with open(TRAFFIC_SUMMARY, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
 
 
 def main():
     args = parse()
+    if args.summarize:
+        summarize(*args.summarize)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -215,7 +334,8 @@ def main():
         ach = kbytes / (kms * 1e-3) / 1e9
         out["roofline"] = {"kernel": "hgrn2_%s_kernel" % dom, "bound": "hbm", "achieved": ach,
                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
-                           "traffic": None, "ms": kms, "algorithmic_bytes": kbytes}
+                           "traffic": measured_traffic("hgrn2_%s_kernel" % dom), "ms": kms,
+                           "algorithmic_bytes": kbytes, "source_digest": kernel_source_digest()}
         out["kernels"] = {
             "fwd": {"ms": res["fwd_ms"], "bytes": fwd_bytes, "GBps": fwd_bytes / res["fwd_ms"] / 1e6,
                     "TFLOPs": fwd_flop / res["fwd_ms"] / 1e9},
