@@ -128,6 +128,8 @@ def bench_train(torch, m, args):
     y = torch.empty((B, T, H, D), dtype=torch.bfloat16, device=dev)
     states = torch.empty(m.states_shape(B, T, H, D, C), dtype=torch.bfloat16, device=dev)
     grads = [torch.empty((B, T, H, D), dtype=torch.bfloat16, device=dev) for _ in range(4)]
+    ws = torch.empty(int(m.lib().hgrn2_bwd_workspace_bytes(B, T, H, D, D, C, 1, 1)), dtype=torch.uint8,
+                     device=dev)
 
     def step(i, timer=None):
         s = sets[i % len(sets)]
@@ -138,7 +140,7 @@ def bench_train(torch, m, args):
             timer.stop(t)
             t = timer.start("bwd")
         m.bwd(s["q"], s["k"], s["v"], s["log_f"], s["dy"], None, None, states, chunk=C,
-              want_dh0=False, dq=grads[0], dk=grads[1], dv=grads[2], dlog_f=grads[3])
+              want_dh0=False, dq=grads[0], dk=grads[1], dv=grads[2], dlog_f=grads[3], ws=ws)
         if timer:
             timer.stop(t)
 

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define HGRN2_ABI_VERSION 1
+#define HGRN2_ABI_VERSION 2
 
 typedef enum {
   HGRN2_OK = 0,
@@ -84,26 +84,37 @@ int hgrn2_num_chunks(int T, int chunk);
  * input dtype anyway.  Returns 0 for invalid arguments. */
 size_t hgrn2_states_bytes(int B, int T, int H, int DK, int DV, int chunk, int dtype);
 
-/* Workspace bytes hgrn2_bwd needs: 0 when the caller passes states_in,
- * hgrn2_states_bytes(...) when it passes states_in = NULL (the states are
- * then recomputed into the workspace). */
+/* Workspace bytes hgrn2_fwd needs: 0 when the caller passes states_out,
+ * hgrn2_states_bytes(...) when it passes states_out = NULL (the chunk-boundary
+ * states are then written to the workspace, which the per-chunk outputs read). */
+size_t hgrn2_fwd_workspace_bytes(int B, int T, int H, int DK, int DV, int chunk, int dtype,
+                                 int have_states);
+
+/* Workspace bytes hgrn2_bwd needs: the state adjoint at every chunk end,
+ * B*H*N*DK*DV*sizeof(dtype), plus hgrn2_states_bytes(...) when the caller
+ * passes states_in = NULL (the states are then recomputed into the workspace). */
 size_t hgrn2_bwd_workspace_bytes(int B, int T, int H, int DK, int DV, int chunk, int dtype,
                                  int have_states);
 
 /*
  * Chunked forward (HGRN2 summary §3.2 p.5, chunkwise form of the recurrence).
+ * Two launches on `stream`: a scan over the chunks of every (b, h) that
+ * writes each chunk-boundary state, then the outputs of all chunks in
+ * parallel from those states.
  *   q, k, log_f : [B,T,H,DK] dtype      v : [B,T,H,DV] dtype
  *   h0          : [B,H,DK,DV] float32, or NULL for a zero initial state
- *   y           : [B,T,H,DV] dtype (written)
+ *   y           : [B,T,H,DV] dtype (written), or NULL (states and ht only)
  *   ht          : [B,H,DK,DV] float32 final state, or NULL (not wanted).
  *                 ht may alias h0.
  *   states_out  : hgrn2_states_bytes() bytes of chunk-boundary states (input
- *                 dtype) for the backward, or NULL (inference).
+ *                 dtype) for the backward, or NULL (then they go to ws).
+ *   ws, ws_bytes: workspace (see hgrn2_fwd_workspace_bytes); may be NULL/0
+ *                 when states_out is given.
  */
 hgrn2_status hgrn2_fwd(int B, int T, int H, int DK, int DV, int chunk, int dtype,
                        const void *q, const void *k, const void *v, const void *log_f,
-                       const float *h0, void *y, float *ht, void *states_out,
-                       void *stream);
+                       const float *h0, void *y, float *ht, void *states_out, void *ws,
+                       size_t ws_bytes, void *stream);
 
 /*
  * Chunked backward by reverse chunk scan of the state adjoint, for the loss

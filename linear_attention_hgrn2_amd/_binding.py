@@ -50,9 +50,11 @@ def _lib():
         lib.hgrn2_num_chunks.restype = I
         lib.hgrn2_states_bytes.argtypes = [I, I, I, I, I, I, I]
         lib.hgrn2_states_bytes.restype = Z
+        lib.hgrn2_fwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
+        lib.hgrn2_fwd_workspace_bytes.restype = Z
         lib.hgrn2_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
         lib.hgrn2_bwd_workspace_bytes.restype = Z
-        lib.hgrn2_fwd.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P]
+        lib.hgrn2_fwd.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, Z, P]
         lib.hgrn2_fwd.restype = I
         lib.hgrn2_bwd.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
         lib.hgrn2_bwd.restype = I
@@ -107,8 +109,12 @@ def states_shape(B, T, H, D, chunk):
 
 
 def fwd(q, k, v, log_f, h0=None, *, chunk=64, want_ht=True, want_states=False,
-        y=None, ht=None, states=None):
-    """Chunked forward.  Returns (y, ht or None, states or None)."""
+        y=None, ht=None, states=None, ws=None):
+    """Chunked forward.  Returns (y, ht or None, states or None).
+
+    Without `states` the chunk-boundary states go to a workspace (`ws`, a
+    uint8 CUDA tensor of at least hgrn2_fwd_workspace_bytes, allocated here
+    if not given)."""
     B, T, H, D = q.shape
     dt = q.dtype
     if dt not in _DT:
@@ -127,8 +133,14 @@ def fwd(q, k, v, log_f, h0=None, *, chunk=64, want_ht=True, want_states=False,
     if states is not None and (tuple(states.shape) != states_shape(B, T, H, D, chunk)
                                or states.dtype != dt or not states.is_contiguous()):
         raise ValueError("states: expected %s %s" % (dt, states_shape(B, T, H, D, chunk)))
+    ws_bytes = 0
+    if states is None:
+        need = int(_lib().hgrn2_fwd_workspace_bytes(B, T, H, D, D, chunk, _DT[dt], 0))
+        if ws is None:
+            ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_bytes = ws.numel() * ws.element_size()
     st = _lib().hgrn2_fwd(B, T, H, D, D, chunk, _DT[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(log_f),
-                          _ptr(h0), _ptr(y), _ptr(ht), _ptr(states), _stream())
+                          _ptr(h0), _ptr(y), _ptr(ht), _ptr(states), _ptr(ws), ws_bytes, _stream())
     _check(st, "hgrn2_fwd")
     return y, ht, states
 
@@ -151,15 +163,13 @@ def bwd(q, k, v, log_f, dy, h0=None, dht=None, states=None, *, chunk=64, want_dh
     if want_dh0 and dh0 is None:
         dh0 = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
     _st("dh0", dh0, B, H, D)
-    ws_bytes = 0
-    if states is None:
-        need = int(_lib().hgrn2_bwd_workspace_bytes(B, T, H, D, D, chunk, _DT[dt], 0))
-        if ws is None:
-            ws = torch.empty(need, dtype=torch.uint8, device=q.device)
-        ws_bytes = ws.numel() * ws.element_size()
-    elif (tuple(states.shape) != states_shape(B, T, H, D, chunk) or states.dtype != dt
-          or not states.is_contiguous()):
+    if states is not None and (tuple(states.shape) != states_shape(B, T, H, D, chunk) or states.dtype != dt
+                               or not states.is_contiguous()):
         raise ValueError("states: expected %s %s" % (dt, states_shape(B, T, H, D, chunk)))
+    need = int(_lib().hgrn2_bwd_workspace_bytes(B, T, H, D, D, chunk, _DT[dt], int(states is not None)))
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = ws.numel() * ws.element_size()
     st = _lib().hgrn2_bwd(B, T, H, D, D, chunk, _DT[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(log_f),
                           _ptr(h0), _ptr(states), _ptr(dy), _ptr(dht), _ptr(dq), _ptr(dk),
                           _ptr(dv), _ptr(dlog_f), _ptr(dh0), _ptr(ws), ws_bytes, _stream())

@@ -89,6 +89,21 @@ hgrn2_status hip_status(hipError_t e, const char *what) {
   return fail(HGRN2_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
+bool fwd_exists(int dtype, int D, int C) {
+  return hgrn2::dispatch_scan(dtype, D, C, false, nullptr, nullptr) == hipSuccess &&
+         hgrn2::dispatch_scan(dtype, D, C, true, nullptr, nullptr) == hipSuccess &&
+         hgrn2::dispatch_chunk_fwd(dtype, D, C, nullptr, nullptr) == hipSuccess;
+}
+
+bool bwd_exists(int dtype, int D, int C) {
+  return hgrn2::dispatch_chunk_bwd(dtype, D, C, nullptr, nullptr) == hipSuccess;
+}
+
+// bytes of the state adjoints at every chunk end, [B, H, N, DK, DV] in the input dtype
+size_t adjoint_bytes(int B, int T, int H, int DK, int DV, int chunk, int dtype) {
+  return (size_t)B * H * (size_t)((T + chunk - 1) / chunk) * DK * DV * dsize(dtype);
+}
+
 }  // namespace
 
 extern "C" {
@@ -110,7 +125,7 @@ const char *hgrn2_last_error(void) { return g_last_error.c_str(); }
 
 int hgrn2_supported(int D, int chunk, int dtype) {
   if (!valid_d(D) || !valid_chunk(chunk) || !valid_dtype(dtype)) return 0;
-  return hgrn2::fwd_exists(dtype, D, chunk) && hgrn2::bwd_exists(dtype, D, chunk) ? 1 : 0;
+  return fwd_exists(dtype, D, chunk) && bwd_exists(dtype, D, chunk) ? 1 : 0;
 }
 
 int hgrn2_num_chunks(int T, int chunk) {
@@ -124,48 +139,76 @@ size_t hgrn2_states_bytes(int B, int T, int H, int DK, int DV, int chunk, int dt
   return (size_t)B * H * (N + 1) * DK * DV * dsize(dtype);
 }
 
-size_t hgrn2_bwd_workspace_bytes(int B, int T, int H, int DK, int DV, int chunk, int dtype,
+size_t hgrn2_fwd_workspace_bytes(int B, int T, int H, int DK, int DV, int chunk, int dtype,
                                  int have_states) {
   return have_states ? 0 : hgrn2_states_bytes(B, T, H, DK, DV, chunk, dtype);
 }
 
+size_t hgrn2_bwd_workspace_bytes(int B, int T, int H, int DK, int DV, int chunk, int dtype,
+                                 int have_states) {
+  if (B <= 0 || T <= 0 || H <= 0 || DK <= 0 || DV <= 0 || chunk <= 0 || !valid_dtype(dtype)) return 0;
+  return adjoint_bytes(B, T, H, DK, DV, chunk, dtype) +
+         (have_states ? 0 : hgrn2_states_bytes(B, T, H, DK, DV, chunk, dtype));
+}
+
 hgrn2_status hgrn2_fwd(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
                        const void *k, const void *v, const void *log_f, const float *h0, void *y,
-                       float *ht, void *states_out, void *stream) {
+                       float *ht, void *states_out, void *ws, size_t ws_bytes, void *stream) {
   hgrn2_status st = check_common(B, T, H, DK, DV, chunk, dtype);
   if (st != HGRN2_OK) return st;
-  st = check_ptrs({{"q", q}, {"k", k}, {"v", v}, {"log_f", log_f}, {"y", y}},
-                  {{"h0", h0}, {"ht", ht}, {"states_out", states_out}});
+  st = check_ptrs({{"q", q}, {"k", k}, {"v", v}, {"log_f", log_f}},
+                  {{"h0", h0}, {"y", y}, {"ht", ht}, {"states_out", states_out}, {"ws", ws}});
   if (st != HGRN2_OK) return st;
-  if (!hgrn2::fwd_exists(dtype, DK, chunk))
+  if (!fwd_exists(dtype, DK, chunk))
     return fail(HGRN2_ERR_UNSUPPORTED, "no forward kernel for this D, chunk and dtype");
   const size_t tok = (size_t)B * T * H * DK * dsize(dtype);
   const size_t sb = (size_t)B * H * DK * DV * sizeof(float);
   const size_t stb = hgrn2_states_bytes(B, T, H, DK, DV, chunk, dtype);
+  void *states = states_out;
+  if (!states) {
+    if (!ws || ws_bytes < stb)
+      return fail(HGRN2_ERR_WORKSPACE, "states_out is NULL: need a workspace of hgrn2_states_bytes()");
+    states = ws;
+  }
   // ht may be exactly h0 (each workgroup reads its slice of h0 before it
   // writes the same slice of ht); any other overlap is an error.
   const Range ins[] = {{"q", q, tok}, {"k", k, tok}, {"v", v, tok}, {"log_f", log_f, tok},
                        {"h0", (ht == h0) ? nullptr : h0, sb}};
-  const Range outs[] = {{"y", y, tok}, {"ht", ht, sb}, {"states_out", states_out, stb}};
+  const Range outs[] = {{"y", y, tok}, {"ht", ht, sb}, {states_out ? "states_out" : "ws", states, stb}};
   std::string msg;
   if (!check_aliasing(ins, 5, outs, 3, msg)) return fail(HGRN2_ERR_INVALID_ARG, msg);
-  if (ht == h0 && ht && overlap(Range{"y", y, tok}, Range{"h0", h0, sb}))
-    return fail(HGRN2_ERR_INVALID_ARG, "y overlaps h0");
+  if (ht == h0 && ht && (overlap(Range{"y", y, tok}, Range{"h0", h0, sb}) ||
+                         overlap(Range{"states", states, stb}, Range{"h0", h0, sb})))
+    return fail(HGRN2_ERR_INVALID_ARG, "an output overlaps h0");
 
-  hgrn2::FwdArgs a;
-  a.B = B;
-  a.T = T;
-  a.H = H;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.log_f = log_f;
-  a.h0 = h0;
-  a.y = y;
-  a.ht = ht;
-  a.states = states_out;
-  a.N = hgrn2_num_chunks(T, chunk);
-  return hip_status(hgrn2::dispatch_fwd(dtype, DK, chunk, a, (hipStream_t)stream), "hgrn2_fwd");
+  const int N = hgrn2_num_chunks(T, chunk);
+  hgrn2::ScanArgs sa;
+  sa.B = B;
+  sa.T = T;
+  sa.H = H;
+  sa.N = N;
+  sa.x = k;
+  sa.z = v;
+  sa.log_f = log_f;
+  sa.s_in = h0;
+  sa.states = states;
+  sa.s_out = ht;
+  st = hip_status(hgrn2::dispatch_scan(dtype, DK, chunk, false, &sa, (hipStream_t)stream),
+                  "hgrn2_fwd (state scan)");
+  if (st != HGRN2_OK || !y) return st;
+  hgrn2::ChunkFwdArgs ca;
+  ca.B = B;
+  ca.T = T;
+  ca.H = H;
+  ca.N = N;
+  ca.q = q;
+  ca.k = k;
+  ca.v = v;
+  ca.log_f = log_f;
+  ca.states = states;
+  ca.y = y;
+  return hip_status(hgrn2::dispatch_chunk_fwd(dtype, DK, chunk, &ca, (hipStream_t)stream),
+                    "hgrn2_fwd (chunk outputs)");
 }
 
 hgrn2_status hgrn2_bwd(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
@@ -179,62 +222,75 @@ hgrn2_status hgrn2_bwd(int B, int T, int H, int DK, int DV, int chunk, int dtype
                    {"dk", dk}, {"dv", dv}, {"dlog_f", dlog_f}},
                   {{"h0", h0}, {"states_in", states_in}, {"dht", dht}, {"dh0", dh0}, {"ws", ws}});
   if (st != HGRN2_OK) return st;
-  if (!hgrn2::bwd_exists(dtype, DK, chunk) || !hgrn2::fwd_exists(dtype, DK, chunk))
+  if (!bwd_exists(dtype, DK, chunk) || !fwd_exists(dtype, DK, chunk))
     return fail(HGRN2_ERR_UNSUPPORTED, "no backward kernel for this D, chunk and dtype");
   const size_t tok = (size_t)B * T * H * DK * dsize(dtype);
   const size_t sb = (size_t)B * H * DK * DV * sizeof(float);
   const size_t stb = hgrn2_states_bytes(B, T, H, DK, DV, chunk, dtype);
+  const size_t lamb = adjoint_bytes(B, T, H, DK, DV, chunk, dtype);
+  const size_t need = lamb + (states_in ? 0 : stb);
+  if (!ws || ws_bytes < need)
+    return fail(HGRN2_ERR_WORKSPACE, "workspace smaller than hgrn2_bwd_workspace_bytes()");
   const void *states = states_in;
-  if (!states) {
-    if (!ws || ws_bytes < stb)
-      return fail(HGRN2_ERR_WORKSPACE, "states_in is NULL: need a workspace of hgrn2_states_bytes()");
-  }
   const Range ins[] = {{"q", q, tok},   {"k", k, tok},   {"v", v, tok},          {"log_f", log_f, tok},
                        {"h0", h0, sb},  {"dy", dy, tok}, {"dht", dht, sb},       {"states_in", states_in, stb}};
   const Range outs[] = {{"dq", dq, tok},         {"dk", dk, tok},  {"dv", dv, tok},
-                        {"dlog_f", dlog_f, tok}, {"dh0", dh0, sb}, {"ws", states ? nullptr : ws, stb}};
+                        {"dlog_f", dlog_f, tok}, {"dh0", dh0, sb}, {"ws", ws, need}};
   std::string msg;
   if (!check_aliasing(ins, 8, outs, 6, msg)) return fail(HGRN2_ERR_INVALID_ARG, msg);
 
   const int N = hgrn2_num_chunks(T, chunk);
   if (!states) {
-    // recompute the chunk-boundary states with the forward kernel (no outputs)
-    hgrn2::FwdArgs f;
-    f.B = B;
-    f.T = T;
-    f.H = H;
-    f.q = q;
-    f.k = k;
-    f.v = v;
-    f.log_f = log_f;
-    f.h0 = h0;
-    f.y = nullptr;
-    f.ht = nullptr;
-    f.states = ws;
-    f.N = N;
-    hgrn2_status s1 = hip_status(hgrn2::dispatch_fwd(dtype, DK, chunk, f, (hipStream_t)stream),
+    // recompute the chunk-boundary states with the forward state scan
+    void *sws = (char *)ws + lamb;
+    hgrn2::ScanArgs sa;
+    sa.B = B;
+    sa.T = T;
+    sa.H = H;
+    sa.N = N;
+    sa.x = k;
+    sa.z = v;
+    sa.log_f = log_f;
+    sa.s_in = h0;
+    sa.states = sws;
+    sa.s_out = nullptr;
+    hgrn2_status s1 = hip_status(hgrn2::dispatch_scan(dtype, DK, chunk, false, &sa, (hipStream_t)stream),
                                  "hgrn2_bwd (state recompute)");
     if (s1 != HGRN2_OK) return s1;
-    states = ws;
+    states = sws;
   }
-  hgrn2::BwdArgs a;
+  // the state adjoint at every chunk end (reverse scan), then all chunks' gradients
+  hgrn2::ScanArgs ra;
+  ra.B = B;
+  ra.T = T;
+  ra.H = H;
+  ra.N = N;
+  ra.x = q;
+  ra.z = dy;
+  ra.log_f = log_f;
+  ra.s_in = dht;
+  ra.states = ws;
+  ra.s_out = dh0;
+  st = hip_status(hgrn2::dispatch_scan(dtype, DK, chunk, true, &ra, (hipStream_t)stream),
+                  "hgrn2_bwd (adjoint scan)");
+  if (st != HGRN2_OK) return st;
+  hgrn2::ChunkBwdArgs a;
   a.B = B;
   a.T = T;
   a.H = H;
+  a.N = N;
   a.q = q;
   a.k = k;
   a.v = v;
   a.log_f = log_f;
   a.dy = dy;
   a.states = states;
-  a.dht = dht;
+  a.lam = ws;
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
   a.dlog_f = dlog_f;
-  a.dh0 = dh0;
-  a.N = N;
-  return hip_status(hgrn2::dispatch_bwd(dtype, DK, chunk, a, (hipStream_t)stream), "hgrn2_bwd");
+  return hip_status(hgrn2::dispatch_chunk_bwd(dtype, DK, chunk, &a, (hipStream_t)stream), "hgrn2_bwd (chunk gradients)");
 }
 
 hgrn2_status hgrn2_decode_step(int B, int H, int DK, int DV, int dtype, const void *q, const void *k,

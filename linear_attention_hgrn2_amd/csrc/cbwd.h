@@ -1,0 +1,592 @@
+// Per-chunk gradients of the HGRN2 recurrence (gfx950), all chunks in parallel.
+//
+// HGRN2 summary (paperlayer.ai) §3.2: S_t = Diag(f_t) S_{t-1} + k_t^T v_t,
+// y_t = q_t S_t, evaluated chunkwise (§3.2 p.5).  Given the state S at the
+// start of chunk n and the state adjoint Lam at its end (both written by the
+// state scans), with b the in-chunk inclusive prefix of log f and Gamma = b_C:
+//   dA[t][s] = dy_t . v_s                              (s <= t in the chunk)
+//   dq_t = sum_{s<=t} dA[t][s] k_s e^{b_t-b_s} + e^{b_t} (S dy_t^T)
+//   dk_s = sum_{t>=s} dA[t][s] q_t e^{b_t-b_s} + e^{Gamma-b_s} (Lam v_s^T)
+//   dv_s = sum_{t>=s} A[t][s] dy_t + (k_s e^{Gamma-b_s}) Lam
+//   dlog f_r = sum_{t>=r in chunk} (q_t dq_t - k_t dk_t) + rowsum(S_end * Lam)
+// where rowsum(S_end * Lam) = e^Gamma rowsum(S * Lam) + sum_s k_s dk_s^inter
+// carries every later token's contribution.  Exponents are anchored as in the
+// forward: qo = q e^{ell}, ko = k e^{L_j - ell}, gap factors between 16-token
+// sub-blocks; dq = e^{ell} dq', dk = e^{L - ell} dk' with dq', dk' formed from
+// qo, ko and the gaps.  dlog f uses qo dq' - ko dk' with the same rounded qo,
+// ko that entered the products, so the terms that cancel in exact arithmetic
+// cancel here too.  A diagonal block whose decay exceeds kDiagLimit nats is
+// summed directly.
+//
+// One workgroup per (batch, head, chunk); wave w owns 16-token sub-block w and
+// produces all its outputs.  Phases: products from LDS tiles of qo, ko, v, dy
+// (S and Lam fragments straight from memory); then per-token epilogues in the
+// prep layout (lane = CPL channels, sixteen tokens in registers) through an
+// LDS staging area; then the dv term that needs Lam with its rows as k.
+#pragma once
+
+#include "cfwd.h"
+
+namespace hgrn2 {
+
+struct ChunkBwdArgs {
+  int B, T, H, N;
+  const void *q, *k, *v, *log_f, *dy;  // [B,T,H,D]
+  const void *states;                  // [B,H,N+1,D,D]; entry n = state before chunk n
+  const void *lam;                     // [B,H,N,D,D]; entry n = adjoint at the end of chunk n
+  void *dq, *dk, *dv, *dlog_f;         // [B,T,H,D]
+};
+
+template <typename T, int D, int C> struct CbwdCfg {
+  static constexpr int NW = C / 16, NT = 64 * NW, NB = NW;
+  static constexpr int CPL = D > 64 ? D / 64 : 1;
+  static constexpr int LANES = D / CPL;
+  static constexpr int CB = D / 16;
+  static constexpr int KSD = (D + 31) / 32;
+  static constexpr int EPV = 16 / (int)sizeof(T);
+  static constexpr int VT = C * D / EPV, NVT = (VT + NT - 1) / NT;  // 16-byte vectors of a token tile
+  static constexpr int VS = D * D / EPV, NVS = (VS + NT - 1) / NT;
+  static constexpr int LDG = D + 4;  // staging row stride (floats)
+  struct In {
+    T qo[C * D], ko[C * D], v[C * D], dy[C * D];  // RowTile<T, D>
+  };
+  struct Out {
+    union {
+      float stg[NW][16 * LDG];  // per-wave staging of dq' then dk'
+      T lam[D * D];             // RowTile<T, D>, for the dv term
+    } a;
+    float tot[NW][D];    // per-block sums of q dq - k dk
+    float cpart[NW][D];  // per-block sums of ko dk'_inter
+    float rs[D];         // rowsum(S * Lam)
+    T dvs[C * D];        // dv staging, RowTile<T, D>
+  };
+  struct Smem {
+    union {
+      In in;
+      Out out;
+    } u;
+    float Lb[NB][D];
+    float gp[NW][NB][D];  // wave w: gap factor of its pair with block m
+    float fac[NW][2][D];  // wave w: e^{P_w}, e^{Gamma - P_{w+1}}
+    float eG[D];          // e^Gamma
+  };
+};
+
+template <typename T, int D, int C>
+__global__ __launch_bounds__(4 * C) void hgrn2_chunk_bwd_kernel(ChunkBwdArgs a) {
+  using Cfg = CbwdCfg<T, D, C>;
+  constexpr int NW = Cfg::NW, NT = Cfg::NT, NB = Cfg::NB, CPL = Cfg::CPL, CB = Cfg::CB, KSD = Cfg::KSD,
+                EPV = Cfg::EPV, LDG = Cfg::LDG;
+  using XT = RowTile<T, D>;
+  __shared__ typename Cfg::Smem sm;
+
+  const int N = a.N, T_ = a.T, H = a.H;
+  const int bh = blockIdx.x / N, n = blockIdx.x % N;
+  if (bh >= a.B * H) return;
+  const int b = bh / H, h = bh % H;
+  const int t0 = n * C, len = min(C, T_ - t0);
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n16 = lane & 15, g = lane >> 4;
+  const bool has_ch = lane < Cfg::LANES;
+  const int c0 = (has_ch ? lane : 0) * CPL;
+
+  const T *gq = (const T *)a.q;
+  const T *gk = (const T *)a.k;
+  const T *gv = (const T *)a.v;
+  const T *gl = (const T *)a.log_f;
+  const T *gdy = (const T *)a.dy;
+  const T *gS = (const T *)a.states + ((size_t)bh * (N + 1) + n) * D * D;
+  const T *gL = (const T *)a.lam + ((size_t)bh * N + n) * D * D;
+  T *gdq = (T *)a.dq;
+  T *gdk = (T *)a.dk;
+  T *gdv = (T *)a.dv;
+  T *gdl = (T *)a.dlog_f;
+  auto tok = [&](int t) { return (((size_t)b * T_ + t) * H + h) * D; };
+  auto ldtok = [&](const T *base, int t) {  // this lane's CPL elements of token t of the chunk (0 past the end)
+    Pack<T, CPL> p;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) p.v[e] = from_f32<T>(0.f);
+    if (t < len && has_ch) p = ldpack<T, CPL>(base + tok(t0 + t) + c0);
+    return p;
+  };
+
+  // =============== phase 0: tiles of v and dy; qo, ko in the prep layout
+#pragma unroll
+  for (int i = 0; i < Cfg::NVT; ++i) {
+    const int idx = tid + i * NT;
+    const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
+    uint4 x = make_uint4(0, 0, 0, 0), y = x;
+    if (idx < Cfg::VT && row < len) {
+      x = *(const uint4 *)(gv + tok(t0 + row) + col);
+      y = *(const uint4 *)(gdy + tok(t0 + row) + col);
+    }
+    if (idx < Cfg::VT) {
+      *(uint4 *)&sm.u.in.v[XT::at(row, col)] = x;
+      *(uint4 *)&sm.u.in.dy[XT::at(row, col)] = y;
+    }
+  }
+  bool wide = false;
+  {
+    Pack<T, CPL> pq[16], pk[16], pl[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      pq[t] = ldtok(gq, 16 * w + t);
+      pk[t] = ldtok(gk, 16 * w + t);
+      pl[t] = ldtok(gl, 16 * w + t);
+    }
+    float l[16][CPL], L[CPL];
+    block_prefix<T, CPL>(pl, l, L);
+    if (has_ch) {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        Pack<T, CPL> oq, ok;
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+          oq.v[e] = from_f32<T>(to_f32(pq[t].v[e]) * __expf(l[t][e]));
+          ok.v[e] = from_f32<T>(to_f32(pk[t].v[e]) * __expf(L[e] - l[t][e]));
+        }
+        stpack<T, CPL>(&sm.u.in.qo[XT::at(16 * w + t, c0)], oq);
+        stpack<T, CPL>(&sm.u.in.ko[XT::at(16 * w + t, c0)], ok);
+      }
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) {
+        sm.Lb[w][c0 + e] = L[e];
+        wide |= -L[e] > kDiagLimit;
+      }
+    }
+  }
+  wide = __ballot(wide) != 0;
+  __syncthreads();  // B1
+
+  // =============== phase 1a: this wave's gap factors and exponential factors
+  if (has_ch) {
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) {
+      const int c = c0 + e;
+      float P[NB + 1], Pw = 0.f, Pw1 = 0.f;
+      P[0] = 0.f;
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const float Li = sm.Lb[i][c];
+        P[i + 1] = P[i] + Li;
+        Pw += (i < w) ? Li : 0.f;
+        Pw1 += (i <= w) ? Li : 0.f;
+      }
+      const float G = P[NB], Lw = sm.Lb[w][c];
+#pragma unroll
+      for (int m = 0; m < NB; ++m) {
+        float x;
+        if (m < w) x = Pw - P[m + 1];
+        else if (m == w) x = fminf(-Lw, 80.f);
+        else x = P[m] - Pw1;
+        sm.gp[w][m][c] = __expf(x);
+      }
+      sm.fac[w][0][c] = __expf(Pw);
+      sm.fac[w][1][c] = __expf(G - Pw1);
+      if (w == 0) sm.eG[c] = __expf(G);
+    }
+  }
+  wave_lds_sync();
+
+  // =============== phase 1b: products
+  f32x4_t DQ[CB], DK[CB], DV[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    acc_zero(DQ[cb]);
+    acc_zero(DK[cb]);
+    acc_zero(DV[cb]);
+  }
+  const T *qo = sm.u.in.qo, *ko = sm.u.in.ko, *tv = sm.u.in.v, *tdy = sm.u.in.dy;
+
+  // (a) dq' intra: pairs (w, m <= w).  dA^T tile: rows s in m, columns t in w.
+#pragma unroll
+  for (int m = 0; m < NB; ++m) {
+    if (m > w || (m == w && wide)) continue;  // wave-uniform
+    f32x4_t X;
+    acc_zero(X);
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks) {
+      const int jj = 32 * ks + 8 * g;
+      const bool ok = jj < D;
+      const int j = ok ? jj : 0;
+      mma(X, masked(row8<D>(tv, 16 * m + n16, j), ok), masked(row8<D>(tdy, 16 * w + n16, j), ok));
+    }
+    if (m == w) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (4 * g + r > n16) X[r] = 0.f;  // s > t
+    }
+    const PFrag4<T> fa = acc_to_frag4<T>(X);  // lane (g, t): k-slots s = 16m + 4g + r
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      f32x4_t tmp;
+      acc_zero(tmp);
+      mma16(tmp, fa, tr4<D>(ko, 16 * m, 16 * cb));
+      const float gpf = sm.gp[w][m][16 * cb + n16];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) DQ[cb][r] += gpf * tmp[r];
+    }
+  }
+
+  // (b) dk' intra and (c) scores for dv: pairs (m >= w, w).  Tiles: rows t in m, columns s in w.
+#pragma unroll
+  for (int m = 0; m < NB; ++m) {
+    if (m < w) continue;
+    const bool direct = (m == w) && wide;
+    if (!direct) {
+      f32x4_t X;
+      acc_zero(X);
+#pragma unroll
+      for (int ks = 0; ks < KSD; ++ks) {
+        const int jj = 32 * ks + 8 * g;
+        const bool ok = jj < D;
+        const int j = ok ? jj : 0;
+        mma(X, masked(row8<D>(tdy, 16 * m + n16, j), ok), masked(row8<D>(tv, 16 * w + n16, j), ok));
+      }
+      if (m == w) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (4 * g + r < n16) X[r] = 0.f;  // t < s
+      }
+      const PFrag4<T> fa = acc_to_frag4<T>(X);  // lane (g, s): k-slots t = 16m + 4g + r
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        f32x4_t tmp;
+        acc_zero(tmp);
+        mma16(tmp, fa, tr4<D>(qo, 16 * m, 16 * cb));
+        const float gpf = sm.gp[w][m][16 * cb + n16];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) DK[cb][r] += gpf * tmp[r];
+      }
+    }
+    // scores A[t][s] = sum_c qo_t (ko_s gap), lane (g, s) holds t = 16m + 4g + r
+    f32x4_t A;
+    acc_zero(A);
+    if (!direct) {
+#pragma unroll
+      for (int ks = 0; ks < KSD; ++ks) {
+        const int cc = 32 * ks + 8 * g;
+        const bool ok = cc < D;
+        const int c = ok ? cc : 0;
+        float kv[8];
+        unpack8(row8<D>(ko, 16 * w + n16, c), kv);
+        const float4 g0 = ldf4(&sm.gp[w][m][c]), g1 = ldf4(&sm.gp[w][m][c + 4]);
+        Frag fb;
+        fb.v[0] = kv[0] * g0.x; fb.v[1] = kv[1] * g0.y; fb.v[2] = kv[2] * g0.z; fb.v[3] = kv[3] * g0.w;
+        fb.v[4] = kv[4] * g1.x; fb.v[5] = kv[5] * g1.y; fb.v[6] = kv[6] * g1.z; fb.v[7] = kv[7] * g1.w;
+        masked(fb, ok);
+        mma(A, masked(row8<D>(qo, 16 * m + n16, c), ok), to_pfrag<T>(fb));
+      }
+      if (m == w) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (4 * g + r < n16) A[r] = 0.f;
+      }
+    } else {
+      // wide in-block decay: A[t][s] summed directly (every exponent <= 0)
+      for (int t = 0; t < 16; ++t) {
+        const bool tv_ = (16 * w + t < len) && has_ch;
+        float qt[CPL], ex[CPL];
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+          qt[e] = 0.f;
+          ex[e] = 0.f;
+        }
+        if (tv_) {
+          const Pack<T, CPL> p = ldpack<T, CPL>(gq + tok(t0 + 16 * w + t) + c0);
+#pragma unroll
+          for (int e = 0; e < CPL; ++e) qt[e] = to_f32(p.v[e]);
+        }
+        for (int s = t; s >= 0; --s) {
+          float part = 0.f;
+          if (tv_) {
+            const Pack<T, CPL> pk = ldpack<T, CPL>(gk + tok(t0 + 16 * w + s) + c0);
+            const Pack<T, CPL> pl = ldpack<T, CPL>(gl + tok(t0 + 16 * w + s) + c0);
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) {
+              part += qt[e] * to_f32(pk.v[e]) * __expf(ex[e]);
+              ex[e] += floor_logf(to_f32(pl.v[e]));
+            }
+          }
+          const float tot = wave_sum(part);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (n16 == s && 4 * g + r == t) A[r] = tot;
+        }
+      }
+    }
+    // dv intra += A^T dy over this block of t
+    const PFrag4<T> fa = acc_to_frag4<T>(A);
+#pragma unroll
+    for (int jb = 0; jb < CB; ++jb) mma16(DV[jb], fa, tr4<D>(tdy, 16 * m, 16 * jb));
+  }
+
+  // (d) inter terms from S and Lam rows straight from memory, rowsum(S * Lam), carry partials
+  PFrag<T> dyA[KSD], vA[KSD];
+#pragma unroll
+  for (int ks = 0; ks < KSD; ++ks) {
+    const int jj = 32 * ks + 8 * g;
+    const bool ok = jj < D;
+    const int j = ok ? jj : 0;
+    dyA[ks] = masked(row8<D>(tdy, 16 * w + n16, j), ok);
+    vA[ks] = masked(row8<D>(tv, 16 * w + n16, j), ok);
+  }
+  float cp[CB];                   // sum over this block of ko dk'_inter, channel 16 cb + n
+  float rsv[(CB + NW - 1) / NW];  // rowsum(S * Lam) of the channel blocks cb = w + NW i
+  // S and Lam rows of one channel block, software-pipelined one block ahead (the
+  // compiler barrier keeps every block's loads from being hoisted at once)
+  PFrag<T> sfb[2][KSD], lfb[2][KSD];
+  auto load_rows = [&](PFrag<T> (&sf)[KSD], PFrag<T> (&lf)[KSD], int cb) {
+    const int c = 16 * cb + n16;
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks) {
+      const int jj = 32 * ks + 8 * g;
+      const bool ok = jj < D;
+      const int j = ok ? jj : 0;
+      sf[ks] = masked(gload8(gS + (size_t)c * D + j), ok);
+      lf[ks] = masked(gload8(gL + (size_t)c * D + j), ok);
+    }
+  };
+  load_rows(sfb[0], lfb[0], 0);
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    if (cb + 1 < CB) load_rows(sfb[(cb + 1) & 1], lfb[(cb + 1) & 1], cb + 1);
+    asm volatile("" ::: "memory");
+    const PFrag<T>(&sf)[KSD] = sfb[cb & 1];
+    const PFrag<T>(&lf)[KSD] = lfb[cb & 1];
+    const int c = 16 * cb + n16;
+    f32x4_t tq, tk;
+    acc_zero(tq);
+    acc_zero(tk);
+    float rsum = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks) {
+      mma(tq, dyA[ks], sf[ks]);
+      mma(tk, vA[ks], lf[ks]);
+      if (cb % NW == w) {
+        float sv[8], lv[8];
+        unpack8(sf[ks], sv);
+        unpack8(lf[ks], lv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) rsum += sv[i] * lv[i];
+      }
+    }
+    const float eP = sm.fac[w][0][c], eK = sm.fac[w][1][c];
+    float ckp = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      DQ[cb][r] += eP * tq[r];
+      const float x = eK * tk[r];
+      DK[cb][r] += x;
+      ckp += to_f32(ko[XT::at(16 * w + 4 * g + r, c)]) * x;  // ko as it entered the products
+    }
+    cp[cb] = group_sum(ckp);
+    if (cb % NW == w) rsv[cb / NW] = group_sum(rsum);
+  }
+  // kh = ko e^{Gamma - P_{w+1}} (k = channels) for the dv term, read before the tiles die
+  PFrag<T> khA[KSD];
+#pragma unroll
+  for (int ks = 0; ks < KSD; ++ks) {
+    const int cc = 32 * ks + 8 * g;
+    const bool ok = cc < D;
+    const int c = ok ? cc : 0;
+    float kv[8];
+    unpack8(row8<D>(ko, 16 * w + n16, c), kv);
+    const float4 e0 = ldf4(&sm.fac[w][1][c]), e1 = ldf4(&sm.fac[w][1][c + 4]);
+    Frag f;
+    f.v[0] = kv[0] * e0.x; f.v[1] = kv[1] * e0.y; f.v[2] = kv[2] * e0.z; f.v[3] = kv[3] * e0.w;
+    f.v[4] = kv[4] * e1.x; f.v[5] = kv[5] * e1.y; f.v[6] = kv[6] * e1.z; f.v[7] = kv[7] * e1.w;
+    masked(f, ok);
+    khA[ks] = to_pfrag<T>(f);
+  }
+  __syncthreads();  // B2: the input tiles are dead
+
+  auto &out = sm.u.out;
+  // =============== phase 2: dv += kh Lam (Lam rows as k)
+#pragma unroll
+  for (int i = 0; i < Cfg::NVS; ++i) {
+    const int idx = tid + i * NT;
+    const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
+    if (idx < Cfg::VS) *(uint4 *)&out.a.lam[XT::at(row, col)] = *(const uint4 *)(gL + (size_t)row * D + col);
+    if (i % 4 == 3) asm volatile("" ::: "memory");  // bounds the loads in flight
+  }
+  __syncthreads();
+#pragma unroll
+  for (int jb = 0; jb < CB; ++jb)
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks) {
+      if constexpr (D >= 32) {
+        mma(DV[jb], khA[ks], tr8<D>(out.a.lam, 32 * ks, 16 * jb));
+      } else {
+        mma(DV[jb], khA[ks], masked(tr8<D>(out.a.lam, (g < 2) ? 0 : -8 * g, 16 * jb), g < 2));
+      }
+    }
+  T *dvs = out.dvs;
+#pragma unroll
+  for (int jb = 0; jb < CB; ++jb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dvs[XT::at(16 * w + 4 * g + r, 16 * jb + n16)] = from_f32<T>(DV[jb][r]);
+  wave_lds_sync();
+  constexpr int RV = 16 * D / EPV;
+#pragma unroll
+  for (int i = 0; i < (RV + 63) / 64; ++i) {
+    const int idx = lane + 64 * i;
+    const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
+    const int t = 16 * w + row;
+    if (idx < RV && t < len) *(uint4 *)(gdv + tok(t0 + t) + col) = *(const uint4 *)&dvs[XT::at(t, col)];
+  }
+  __syncthreads();  // every wave is done with Lam, which the staging overwrites
+
+  // =============== phase 2 (after the dv term): epilogue of dq, dk and dlog f in the prep layout
+  if (g == 0) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      out.cpart[w][16 * cb + n16] = cp[cb];
+      if (cb % NW == w) out.rs[16 * cb + n16] = rsv[cb / NW];
+    }
+  }
+  float *stg = out.a.stg[w];
+  // stage dq'
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) stg[(4 * g + r) * LDG + 16 * cb + n16] = DQ[cb][r];
+  wave_lds_sync();
+  float X[16][CPL];
+  float l[16][CPL], L[CPL];
+  {
+    Pack<T, CPL> pl[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) pl[t] = ldtok(gl, 16 * w + t);
+    block_prefix<T, CPL>(pl, l, L);
+  }
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    const int tt = 16 * w + t;
+    const Pack<T, CPL> pq = ldtok(gq, tt);
+    float dqd[CPL];
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) dqd[e] = 0.f;
+    if (wide) {
+      // direct diagonal block: sum_{s <= t} dA[t][s] k_s e^{ell_t - ell_s}
+      float ex[CPL];
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) ex[e] = 0.f;
+      const Pack<T, CPL> pdy = ldtok(gdy, tt);
+      for (int s = t; s >= 0; --s) {
+        const Pack<T, CPL> pv = ldtok(gv, 16 * w + s);
+        const Pack<T, CPL> pk = ldtok(gk, 16 * w + s);
+        const Pack<T, CPL> pls = ldtok(gl, 16 * w + s);
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) part += to_f32(pdy.v[e]) * to_f32(pv.v[e]);
+        const float dA = wave_sum(part);
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+          dqd[e] += dA * to_f32(pk.v[e]) * __expf(ex[e]);
+          ex[e] += floor_logf(to_f32(pls.v[e]));
+        }
+      }
+    }
+    Pack<T, CPL> o;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) {
+      const float el = __expf(l[t][e]);
+      const float qor = to_f32(from_f32<T>(to_f32(pq.v[e]) * el));  // qo as it entered the products
+      const float d1 = stg[t * LDG + c0 + e];
+      o.v[e] = from_f32<T>(el * d1 + dqd[e]);
+      X[t][e] = qor * d1 + to_f32(pq.v[e]) * dqd[e];
+    }
+    if (tt < len && has_ch) stpack<T, CPL>(gdq + tok(t0 + tt) + c0, o);
+  }
+  wave_lds_sync();
+  // stage dk'
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) stg[(4 * g + r) * LDG + 16 * cb + n16] = DK[cb][r];
+  wave_lds_sync();
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    const int ss = 16 * w + s;
+    const Pack<T, CPL> pk = ldtok(gk, ss);
+    Pack<T, CPL> o;
+    float dkd[CPL];
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) dkd[e] = 0.f;
+    if (wide) {
+      // direct diagonal block: sum_{t >= s} dA[t][s] q_t e^{ell_t - ell_s}
+      float ex[CPL];
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) ex[e] = 0.f;
+      const Pack<T, CPL> pv = ldtok(gv, ss);
+      for (int t = s; t < 16; ++t) {
+        const Pack<T, CPL> pdy = ldtok(gdy, 16 * w + t);
+        const Pack<T, CPL> pq = ldtok(gq, 16 * w + t);
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) part += to_f32(pdy.v[e]) * to_f32(pv.v[e]);
+        const float dA = wave_sum(part);
+        if (t > s) {
+          const Pack<T, CPL> plt = ldtok(gl, 16 * w + t);
+#pragma unroll
+          for (int e = 0; e < CPL; ++e) ex[e] += floor_logf(to_f32(plt.v[e]));
+        }
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) dkd[e] += dA * to_f32(pq.v[e]) * __expf(ex[e]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) {
+      const float ek = __expf(L[e] - l[s][e]);
+      const float kor = to_f32(from_f32<T>(to_f32(pk.v[e]) * ek));  // ko as it entered the products
+      const float d1 = stg[s * LDG + c0 + e];
+      o.v[e] = from_f32<T>(ek * d1 + dkd[e]);
+      X[s][e] -= kor * d1 + to_f32(pk.v[e]) * dkd[e];
+    }
+    if (ss < len && has_ch) stpack<T, CPL>(gdk + tok(t0 + ss) + c0, o);
+  }
+  // block sums of X
+  if (has_ch) {
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) {
+      float s = 0.f;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) s += X[t][e];
+      out.tot[w][c0 + e] = s;
+    }
+  }
+  __syncthreads();  // B3: tot, cpart, rs complete; staging dead
+  if (has_ch) {
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) {
+      const int c = c0 + e;
+      float carry = sm.eG[c] * out.rs[c];
+#pragma unroll
+      for (int i = 0; i < NW; ++i) carry += out.cpart[i][c] + ((i > w) ? out.tot[i][c] : 0.f);
+      float sfx = carry;
+#pragma unroll
+      for (int t = 15; t >= 0; --t) {
+        sfx += X[t][e];
+        X[t][e] = sfx;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int tt = 16 * w + t;
+      Pack<T, CPL> o;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) o.v[e] = from_f32<T>(X[t][e]);
+      if (tt < len) stpack<T, CPL>(gdl + tok(t0 + tt) + c0, o);
+    }
+  }
+
+}
+
+template <typename T, int D, int C>
+hipError_t launch_chunk_bwd(const ChunkBwdArgs &a, hipStream_t stream) {
+  using Cfg = CbwdCfg<T, D, C>;
+  hipLaunchKernelGGL((hgrn2_chunk_bwd_kernel<T, D, C>), dim3(a.B * a.H * a.N), dim3(Cfg::NT), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace hgrn2

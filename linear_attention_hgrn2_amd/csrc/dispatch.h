@@ -1,20 +1,49 @@
-// Internal dispatch table between the C ABI and the kernel templates.
+// Internal dispatch between the C ABI and the kernel templates.
 #pragma once
 
 #include <hip/hip_runtime.h>
 
-#include "bwd.h"
+#include "cbwd.h"
+#include "cfwd.h"
 #include "decode.h"
-#include "fwd.h"
+#include "scan.h"
 
 namespace hgrn2 {
 
+// Runs Op<T, D, C>::run(args...) for the runtime (dtype, D, chunk), or
+// returns hipErrorNotSupported when the combination has no instance.
+template <template <typename, int, int> class Op, typename T, int D, typename... A>
+hipError_t run_c(int C, A... args) {
+  switch (C) {
+    case 16: return Op<T, D, 16>::run(args...);
+    case 32: return Op<T, D, 32>::run(args...);
+    case 64: return Op<T, D, 64>::run(args...);
+  }
+  return hipErrorNotSupported;
+}
+template <template <typename, int, int> class Op, typename T, typename... A>
+hipError_t run_d(int D, int C, A... args) {
+  switch (D) {
+    case 16: return run_c<Op, T, 16>(C, args...);
+    case 32: return run_c<Op, T, 32>(C, args...);
+    case 64: return run_c<Op, T, 64>(C, args...);
+    case 128: return run_c<Op, T, 128>(C, args...);
+  }
+  return hipErrorNotSupported;
+}
+template <template <typename, int, int> class Op, typename... A>
+hipError_t run_config(int dtype, int D, int C, A... args) {
+  if (dtype == 0) return run_d<Op, float>(D, C, args...);
+  if (dtype == 1) return run_d<Op, bf16_t>(D, C, args...);
+  return hipErrorNotSupported;
+}
+
 // Each returns hipErrorNotSupported (without launching) when no kernel
-// exists for the combination, else the launch status.
-hipError_t dispatch_fwd(int dtype, int D, int C, const FwdArgs &a, hipStream_t s);
-hipError_t dispatch_bwd(int dtype, int D, int C, const BwdArgs &a, hipStream_t s);
+// exists for the combination, else the launch status.  A null args pointer
+// only asks whether the kernel exists.
+hipError_t dispatch_scan(int dtype, int D, int C, bool reverse, const ScanArgs *a, hipStream_t s);
+hipError_t dispatch_chunk_fwd(int dtype, int D, int C, const ChunkFwdArgs *a, hipStream_t s);
+hipError_t dispatch_chunk_bwd(int dtype, int D, int C, const ChunkBwdArgs *a, hipStream_t s);
 hipError_t dispatch_decode(int dtype, int D, const DecodeArgs &a, hipStream_t s);
-bool fwd_exists(int dtype, int D, int C);
-bool bwd_exists(int dtype, int D, int C);
 
 }  // namespace hgrn2

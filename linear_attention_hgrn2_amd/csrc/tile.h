@@ -1,0 +1,240 @@
+// LDS tiles and operand loaders for the sequence-parallel chunk kernels (gfx950).
+//
+// Row tiles hold [rows][W] elements with each row's 16-byte chunks XOR-swizzled
+// by the row index, so sixteen lanes that read the same logical chunk of
+// sixteen consecutive rows hit distinct banks without padding.
+//
+// Operand fragments follow the convention in common.h (lane l = 16g + n; an
+// operand fragment carries k-slots, an accumulator holds rows 4g + r of
+// column n).  Three ways to fill a fragment from a row tile:
+//   row8  : A[m][k] with k along the row (8 consecutive elements),
+//   tr8   : B[k][n] with k along the rows, one column per lane (the gfx950
+//           transposing LDS read, two per fragment for 16-bit data),
+//   tr4   : the accumulator arrangement (rows r0 + 4g + j, column n0 + n),
+//           which is also the k-slot order of a 16-deep product.
+#pragma once
+
+#include "common.h"
+
+namespace hgrn2 {
+
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+
+template <typename T, int W> struct RowTile {
+  static constexpr int EPV = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+  static constexpr int NCH = W / EPV;              // chunks per row
+  static_assert(NCH >= 1 && (NCH & (NCH - 1)) == 0, "row width");
+  __device__ static __forceinline__ int at(int r, int c) {
+    return r * W + ((((c / EPV) ^ r) & (NCH - 1)) * EPV) + (c % EPV);
+  }
+};
+
+// ------------------------------------------------------------ 4-slot fragments (16-deep products)
+template <typename Op> struct PFrag4;
+template <> struct PFrag4<bf16_t> {
+  v4s_t x;
+};
+template <> struct PFrag4<float> {
+  float x[4];
+};
+__device__ __forceinline__ void mma16(f32x4_t &acc, const PFrag4<bf16_t> &a, const PFrag4<bf16_t> &b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.x, b.x, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma16(f32x4_t &acc, const PFrag4<float> &a, const PFrag4<float> &b) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x[i], b.x[i], acc, 0, 0, 0);
+}
+template <typename Op> __device__ __forceinline__ PFrag4<Op> acc_to_frag4(const f32x4_t &a);
+template <> __device__ __forceinline__ PFrag4<bf16_t> acc_to_frag4<bf16_t>(const f32x4_t &a) {
+  PFrag4<bf16_t> f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f.x[i] = __builtin_bit_cast(short, (__bf16)a[i]);
+  return f;
+}
+template <> __device__ __forceinline__ PFrag4<float> acc_to_frag4<float>(const f32x4_t &a) {
+  PFrag4<float> f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f.x[i] = a[i];
+  return f;
+}
+// an 8-slot fragment whose slots 0-3 and 4-7 come from two accumulators
+template <typename Op> __device__ __forceinline__ PFrag<Op> accs_to_frag(const f32x4_t &a, const f32x4_t &b) {
+  Frag f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f.v[i] = a[i];
+    f.v[4 + i] = b[i];
+  }
+  return to_pfrag<Op>(f);
+}
+
+// ------------------------------------------------------------ loaders
+// row8: elements c0..c0+7 of row r (c0 a multiple of 8)
+template <int W> __device__ __forceinline__ PFrag<bf16_t> row8(const bf16_t *t, int r, int c0) {
+  return ld8(t + RowTile<bf16_t, W>::at(r, c0));
+}
+template <int W> __device__ __forceinline__ PFrag<float> row8(const float *t, int r, int c0) {
+  return ld4x2(t + RowTile<float, W>::at(r, c0), t + RowTile<float, W>::at(r, c0 + 4));
+}
+
+// one transposing read: lane (g, n) receives t[rows(g, j)][n0 + n] for j = 0..3,
+// where lane (g, i) of the group supplies row rows(g, i >> 2) at column
+// n0 + 4 (i & 3) (gfx950 ds_read_b64_tr_b16 semantics)
+template <int W>
+__device__ __forceinline__ v4s_t tr_read(const bf16_t *t, int row_of_lane, int n0, int lane) {
+  const int c = n0 + 4 * (lane & 3);
+  const bf16_t *p = t + RowTile<bf16_t, W>::at(row_of_lane, c);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t *)(p));
+}
+
+// tr4: accumulator arrangement, rows r0 + 4g + j, column n0 + n
+template <int W> __device__ __forceinline__ PFrag4<bf16_t> tr4(const bf16_t *t, int r0, int n0) {
+  const int lane = lane_id(), g = lane >> 4, i = lane & 15;
+  PFrag4<bf16_t> f;
+  f.x = tr_read<W>(t, r0 + 4 * g + (i >> 2), n0, i);
+  return f;
+}
+template <int W> __device__ __forceinline__ PFrag4<float> tr4(const float *t, int r0, int n0) {
+  const int lane = lane_id(), g = lane >> 4, n = lane & 15;
+  PFrag4<float> f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) f.x[j] = t[RowTile<float, W>::at(r0 + 4 * g + j, n0 + n)];
+  return f;
+}
+
+// tr8, standard k order: slots i <-> rows r0 + 8g + i, column n0 + n
+template <int W> __device__ __forceinline__ PFrag<bf16_t> tr8(const bf16_t *t, int r0, int n0) {
+  const int lane = lane_id(), g = lane >> 4, i = lane & 15;
+  union {
+    v4s_t h[2];
+    bf16x8_t v;
+  } u;
+  u.h[0] = tr_read<W>(t, r0 + 8 * g + (i >> 2), n0, i);
+  u.h[1] = tr_read<W>(t, r0 + 8 * g + 4 + (i >> 2), n0, i);
+  PFrag<bf16_t> f;
+  f.x = u.v;
+  return f;
+}
+template <int W> __device__ __forceinline__ PFrag<float> tr8(const float *t, int r0, int n0) {
+  const int lane = lane_id(), g = lane >> 4, n = lane & 15;
+  PFrag<float> f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f.x[j] = t[RowTile<float, W>::at(r0 + 8 * g + j, n0 + n)];
+  return f;
+}
+
+// tr8, accumulator k order: slots 0-3 <-> rows ra + 4g + j, slots 4-7 <-> rows rb + 4g + j
+// (pairs with an operand built by accs_to_frag)
+template <int W> __device__ __forceinline__ PFrag<bf16_t> tr8acc(const bf16_t *t, int ra, int rb, int n0) {
+  const int lane = lane_id(), g = lane >> 4, i = lane & 15;
+  union {
+    v4s_t h[2];
+    bf16x8_t v;
+  } u;
+  u.h[0] = tr_read<W>(t, ra + 4 * g + (i >> 2), n0, i);
+  u.h[1] = tr_read<W>(t, rb + 4 * g + (i >> 2), n0, i);
+  PFrag<bf16_t> f;
+  f.x = u.v;
+  return f;
+}
+template <int W> __device__ __forceinline__ PFrag<float> tr8acc(const float *t, int ra, int rb, int n0) {
+  const int lane = lane_id(), g = lane >> 4, n = lane & 15;
+  PFrag<float> f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f.x[j] = t[RowTile<float, W>::at(ra + 4 * g + j, n0 + n)];
+    f.x[4 + j] = t[RowTile<float, W>::at(rb + 4 * g + j, n0 + n)];
+  }
+  return f;
+}
+
+// 8 consecutive elements of a row-major global matrix as an operand fragment
+__device__ __forceinline__ PFrag<bf16_t> gload8(const bf16_t *p) {
+  PFrag<bf16_t> f;
+  f.x = *(const bf16x8_t *)__builtin_assume_aligned(p, 16);
+  return f;
+}
+__device__ __forceinline__ PFrag<float> gload8(const float *p) {
+  PFrag<float> f;
+  const float4 *q = (const float4 *)__builtin_assume_aligned(p, 16);
+  const float4 a = q[0], b = q[1];
+  f.x[0] = a.x; f.x[1] = a.y; f.x[2] = a.z; f.x[3] = a.w;
+  f.x[4] = b.x; f.x[5] = b.y; f.x[6] = b.z; f.x[7] = b.w;
+  return f;
+}
+__device__ __forceinline__ void unpack8(const PFrag<bf16_t> &f, float *o) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = (float)f.x[i];
+}
+__device__ __forceinline__ void unpack8(const PFrag<float> &f, float *o) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = f.x[i];
+}
+
+// ------------------------------------------------------------ small groups of elements
+// N consecutive elements moved as one 2-, 4-, 8- or 16-byte access
+template <typename T, int N> struct Pack {
+  T v[N];
+};
+template <typename T, int N> __device__ __forceinline__ Pack<T, N> ldpack(const T *p) {
+  Pack<T, N> r;
+  constexpr int BYTES = (int)sizeof(T) * N;
+  if constexpr (BYTES == 2) {
+    const uint16_t u = *(const uint16_t *)__builtin_assume_aligned(p, 2);
+    __builtin_memcpy(&r, &u, 2);
+  } else if constexpr (BYTES == 4) {
+    const uint32_t u = *(const uint32_t *)__builtin_assume_aligned(p, 4);
+    __builtin_memcpy(&r, &u, 4);
+  } else if constexpr (BYTES == 8) {
+    const uint2 u = *(const uint2 *)__builtin_assume_aligned(p, 8);
+    __builtin_memcpy(&r, &u, 8);
+  } else {
+    static_assert(BYTES == 16, "pack size");
+    const uint4 u = *(const uint4 *)__builtin_assume_aligned(p, 16);
+    __builtin_memcpy(&r, &u, 16);
+  }
+  return r;
+}
+template <typename T, int N> __device__ __forceinline__ void stpack(T *p, const Pack<T, N> &r) {
+  constexpr int BYTES = (int)sizeof(T) * N;
+  if constexpr (BYTES == 2) {
+    uint16_t u;
+    __builtin_memcpy(&u, &r, 2);
+    *(uint16_t *)__builtin_assume_aligned(p, 2) = u;
+  } else if constexpr (BYTES == 4) {
+    uint32_t u;
+    __builtin_memcpy(&u, &r, 4);
+    *(uint32_t *)__builtin_assume_aligned(p, 4) = u;
+  } else if constexpr (BYTES == 8) {
+    uint2 u;
+    __builtin_memcpy(&u, &r, 8);
+    *(uint2 *)__builtin_assume_aligned(p, 8) = u;
+  } else {
+    static_assert(BYTES == 16, "pack size");
+    uint4 u;
+    __builtin_memcpy(&u, &r, 16);
+    *(uint4 *)__builtin_assume_aligned(p, 16) = u;
+  }
+}
+
+// ------------------------------------------------------------ wave-level helpers
+// Orders this wave's earlier LDS accesses before its later ones, for data
+// one lane writes and another lane of the same wave reads.
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+// sum over the four lane groups g (lanes n, n + 16, n + 32, n + 48)
+__device__ __forceinline__ float group_sum(float x) {
+  x += __shfl_xor(x, 16, 64);
+  x += __shfl_xor(x, 32, 64);
+  return x;
+}
+
+}  // namespace hgrn2

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.hgrn2_abi_version() == 1
+    assert lib.hgrn2_abi_version() == 2
     for s in range(5):
         assert lib.hgrn2_status_string(s).startswith(b"HGRN2_")
 
@@ -46,8 +46,12 @@ def test_sizes(lib):
     assert lib.hgrn2_states_bytes(8, 4096, 16, 128, 128, 64, 0) == 8 * 16 * 65 * 128 * 128 * 4
     assert lib.hgrn2_states_bytes(8, 4096, 16, 128, 128, 64, 1) == 8 * 16 * 65 * 128 * 128 * 2
     assert lib.hgrn2_states_bytes(8, 4096, 16, 128, 128, 64, 5) == 0
-    assert lib.hgrn2_bwd_workspace_bytes(1, 100, 1, 16, 16, 16, 0, 1) == 0
-    assert lib.hgrn2_bwd_workspace_bytes(1, 100, 1, 16, 16, 16, 0, 0) == 8 * 16 * 16 * 4
+    # the adjoint at each of the 7 chunk ends, plus the 8 chunk-boundary states when recomputed
+    assert lib.hgrn2_bwd_workspace_bytes(1, 100, 1, 16, 16, 16, 0, 1) == 7 * 16 * 16 * 4
+    assert lib.hgrn2_bwd_workspace_bytes(1, 100, 1, 16, 16, 16, 0, 0) == (7 + 8) * 16 * 16 * 4
+    assert lib.hgrn2_bwd_workspace_bytes(1, 100, 1, 16, 16, 16, 1, 1) == 7 * 16 * 16 * 2
+    assert lib.hgrn2_fwd_workspace_bytes(1, 100, 1, 16, 16, 16, 0, 1) == 0
+    assert lib.hgrn2_fwd_workspace_bytes(1, 100, 1, 16, 16, 16, 0, 0) == 8 * 16 * 16 * 4
     assert lib.hgrn2_supported(128, 64, 1) == 1
     assert lib.hgrn2_supported(48, 64, 1) == 0
     assert lib.hgrn2_supported(128, 128, 1) == 0
@@ -58,10 +62,10 @@ FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation
 
 def _fwd(lib, **kw):
     a = dict(B=1, T=10, H=1, DK=16, DV=16, chunk=16, dt=0, q=FAKE, k=FAKE + 0x1000, v=FAKE + 0x2000,
-             lf=FAKE + 0x3000, h0=None, y=FAKE + 0x4000, ht=None, st=None)
+             lf=FAKE + 0x3000, h0=None, y=FAKE + 0x4000, ht=None, st=None, ws=None, wsb=0)
     a.update(kw)
     return lib.hgrn2_fwd(a["B"], a["T"], a["H"], a["DK"], a["DV"], a["chunk"], a["dt"], a["q"], a["k"],
-                         a["v"], a["lf"], a["h0"], a["y"], a["ht"], a["st"], None)
+                         a["v"], a["lf"], a["h0"], a["y"], a["ht"], a["st"], a["ws"], a["wsb"], None)
 
 
 def test_fwd_rejections(lib):
@@ -74,22 +78,34 @@ def test_fwd_rejections(lib):
     assert _fwd(lib, DK=48, DV=48) == 2
     assert _fwd(lib, DK=16, DV=32) == 2
     assert _fwd(lib, chunk=24) == 2
-    assert _fwd(lib, y=FAKE) == 1                      # y aliases q
-    assert _fwd(lib, dt=0, DK=128, DV=128, chunk=64) == 2   # float32 d128 chunk 64 has no kernel
+    assert _fwd(lib, y=FAKE, st=FAKE + 0x8000) == 1    # y aliases q
+    assert _fwd(lib) == 3                              # no states_out and no workspace
+    assert _fwd(lib, ws=FAKE + 0x8000, wsb=100) == 3   # workspace too small
+    assert _fwd(lib, st=FAKE + 0x2000) == 1            # states_out overlaps v
 
 
 def test_bwd_rejections(lib):
     P = [FAKE + i * 0x100000 for i in range(12)]
-    # states_in NULL and no workspace
-    r = lib.hgrn2_bwd(1, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], P[3], None, None, P[4], None,
+    # no workspace (the adjoint states always need one)
+    r = lib.hgrn2_bwd(1, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], P[3], None, P[9], P[4], None,
                       P[5], P[6], P[7], P[8], None, None, 0, None)
+    assert r == 3
+    # states_in NULL: the workspace must also hold the recomputed states
+    need = lib.hgrn2_bwd_workspace_bytes(1, 10, 1, 16, 16, 16, 0, 1)
+    r = lib.hgrn2_bwd(1, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], P[3], None, None, P[4], None,
+                      P[5], P[6], P[7], P[8], None, P[10], need, None)
     assert r == 3
     # dq aliases dy
     r = lib.hgrn2_bwd(1, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], P[3], None, P[9], P[4], None,
-                      P[4], P[6], P[7], P[8], None, None, 0, None)
+                      P[4], P[6], P[7], P[8], None, P[10], need, None)
     assert r == 1
+    # dq NULL
     r = lib.hgrn2_bwd(1, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], P[3], None, P[9], P[4], None,
-                      None, P[6], P[7], P[8], None, None, 0, None)
+                      None, P[6], P[7], P[8], None, P[10], need, None)
+    assert r == 1
+    # workspace overlaps an output
+    r = lib.hgrn2_bwd(1, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], P[3], None, P[9], P[4], None,
+                      P[5], P[6], P[7], P[8], None, P[8], need, None)
     assert r == 1
 
 
