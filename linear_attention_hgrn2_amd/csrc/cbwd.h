@@ -47,28 +47,32 @@ template <typename T, int D, int C> struct CbwdCfg {
   static constexpr int VT = C * D / EPV, NVT = (VT + NT - 1) / NT;  // 16-byte vectors of a token tile
   static constexpr int VS = D * D / EPV, NVS = (VS + NT - 1) / NT;
   static constexpr int LDG = D + 4;  // staging row stride (floats)
+  static constexpr int LD = RowTile<T, D>::LD;
   struct In {
-    T qo[C * D], ko[C * D], v[C * D], dy[C * D];  // RowTile<T, D>
+    float Lb[NB][D];  // sub-block totals of log f
+    T gp[NW][NB][D];  // wave w: gap factor of its pair with block m (the same
+                      // rounded value on both sides of a pair)
+    T qo[C * LD], ko[C * LD], v[C * LD], dy[C * LD];  // RowTile<T, D>
+  };
+  struct SL {
+    T S[D * LD];  // RowTile<T, D>: the chunk's initial state (row c, column j)
+    T L[D * LD];  // RowTile<T, D>: the adjoint at the chunk end
   };
   struct Out {
-    union {
-      float stg[NW][16 * LDG];  // per-wave staging of dq' then dk'
-      T lam[D * D];             // RowTile<T, D>, for the dv term
-    } a;
-    float tot[NW][D];    // per-block sums of q dq - k dk
-    float cpart[NW][D];  // per-block sums of ko dk'_inter
-    float rs[D];         // rowsum(S * Lam)
-    T dvs[C * D];        // dv staging, RowTile<T, D>
+    float stg[2][NW][16 * LDG];  // per-wave staging of dq' and dk'
+    float tot[NW][D];            // per-block sums of q dq - k dk
+    float cpart[NW][D];          // per-block sums of ko dk'_inter
+    float rs[D];                 // rowsum(S * Lam)
   };
   struct Smem {
-    union {
-      In in;
-      Out out;
-    } u;
-    float Lb[NB][D];
-    float gp[NW][NB][D];  // wave w: gap factor of its pair with block m
     float fac[NW][2][D];  // wave w: e^{P_w}, e^{Gamma - P_{w+1}}
     float eG[D];          // e^Gamma
+    union {
+      In in;            // scores and intra-chunk products
+      SL sl;            // then the inter-chunk products
+      T dvs[C * LD];    // then the dv staging (RowTile<T, D>)
+      Out out;          // then the epilogues
+    } u;
   };
 };
 
@@ -100,12 +104,24 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_bwd_kernel(ChunkBwdArgs a) 
   T *gdk = (T *)a.dk;
   T *gdv = (T *)a.dv;
   T *gdl = (T *)a.dlog_f;
-  auto tok = [&](int t) { return (((size_t)b * T_ + t) * H + h) * D; };
+  // chunk-uniform base pointers; per-lane 32-bit element offsets within the chunk
+  const size_t cbase = (((size_t)b * T_ + t0) * H + h) * D;
+  const uint32_t HD = (uint32_t)H * D;
+  gq += cbase;
+  gk += cbase;
+  gv += cbase;
+  gl += cbase;
+  gdy += cbase;
+  gdq += cbase;
+  gdk += cbase;
+  gdv += cbase;
+  gdl += cbase;
+  auto tok = [&](int t) { return (uint32_t)t * HD; };  // token t of the chunk
   auto ldtok = [&](const T *base, int t) {  // this lane's CPL elements of token t of the chunk (0 past the end)
     Pack<T, CPL> p;
 #pragma unroll
     for (int e = 0; e < CPL; ++e) p.v[e] = from_f32<T>(0.f);
-    if (t < len && has_ch) p = ldpack<T, CPL>(base + tok(t0 + t) + c0);
+    if (t < len && has_ch) p = ldpack<T, CPL>(base + (tok(t) + c0));
     return p;
   };
 
@@ -116,8 +132,8 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_bwd_kernel(ChunkBwdArgs a) 
     const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
     uint4 x = make_uint4(0, 0, 0, 0), y = x;
     if (idx < Cfg::VT && row < len) {
-      x = *(const uint4 *)(gv + tok(t0 + row) + col);
-      y = *(const uint4 *)(gdy + tok(t0 + row) + col);
+      x = *(const uint4 *)(gv + (tok(row) + col));
+      y = *(const uint4 *)(gdy + (tok(row) + col));
     }
     if (idx < Cfg::VT) {
       *(uint4 *)&sm.u.in.v[XT::at(row, col)] = x;
@@ -149,7 +165,7 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_bwd_kernel(ChunkBwdArgs a) 
       }
 #pragma unroll
       for (int e = 0; e < CPL; ++e) {
-        sm.Lb[w][c0 + e] = L[e];
+        sm.u.in.Lb[w][c0 + e] = L[e];
         wide |= -L[e] > kDiagLimit;
       }
     }
@@ -166,19 +182,19 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_bwd_kernel(ChunkBwdArgs a) 
       P[0] = 0.f;
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
-        const float Li = sm.Lb[i][c];
+        const float Li = sm.u.in.Lb[i][c];
         P[i + 1] = P[i] + Li;
         Pw += (i < w) ? Li : 0.f;
         Pw1 += (i <= w) ? Li : 0.f;
       }
-      const float G = P[NB], Lw = sm.Lb[w][c];
+      const float G = P[NB], Lw = sm.u.in.Lb[w][c];
 #pragma unroll
       for (int m = 0; m < NB; ++m) {
         float x;
         if (m < w) x = Pw - P[m + 1];
         else if (m == w) x = fminf(-Lw, 80.f);
         else x = P[m] - Pw1;
-        sm.gp[w][m][c] = __expf(x);
+        sm.u.in.gp[w][m][c] = from_f32<T>(__expf(x));
       }
       sm.fac[w][0][c] = __expf(Pw);
       sm.fac[w][1][c] = __expf(G - Pw1);
@@ -221,7 +237,7 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_bwd_kernel(ChunkBwdArgs a) 
       f32x4_t tmp;
       acc_zero(tmp);
       mma16(tmp, fa, tr4<D>(ko, 16 * m, 16 * cb));
-      const float gpf = sm.gp[w][m][16 * cb + n16];
+      const float gpf = to_f32(sm.u.in.gp[w][m][16 * cb + n16]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) DQ[cb][r] += gpf * tmp[r];
     }
@@ -253,7 +269,7 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_bwd_kernel(ChunkBwdArgs a) 
         f32x4_t tmp;
         acc_zero(tmp);
         mma16(tmp, fa, tr4<D>(qo, 16 * m, 16 * cb));
-        const float gpf = sm.gp[w][m][16 * cb + n16];
+        const float gpf = to_f32(sm.u.in.gp[w][m][16 * cb + n16]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) DK[cb][r] += gpf * tmp[r];
       }
@@ -269,10 +285,11 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_bwd_kernel(ChunkBwdArgs a) 
         const int c = ok ? cc : 0;
         float kv[8];
         unpack8(row8<D>(ko, 16 * w + n16, c), kv);
-        const float4 g0 = ldf4(&sm.gp[w][m][c]), g1 = ldf4(&sm.gp[w][m][c + 4]);
+        float gv[8];
+        unpack8(ld8(&sm.u.in.gp[w][m][c]), gv);
         Frag fb;
-        fb.v[0] = kv[0] * g0.x; fb.v[1] = kv[1] * g0.y; fb.v[2] = kv[2] * g0.z; fb.v[3] = kv[3] * g0.w;
-        fb.v[4] = kv[4] * g1.x; fb.v[5] = kv[5] * g1.y; fb.v[6] = kv[6] * g1.z; fb.v[7] = kv[7] * g1.w;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) fb.v[i] = kv[i] * gv[i];
         masked(fb, ok);
         mma(A, masked(row8<D>(qo, 16 * m + n16, c), ok), to_pfrag<T>(fb));
       }
@@ -292,15 +309,15 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_bwd_kernel(ChunkBwdArgs a) 
           ex[e] = 0.f;
         }
         if (tv_) {
-          const Pack<T, CPL> p = ldpack<T, CPL>(gq + tok(t0 + 16 * w + t) + c0);
+          const Pack<T, CPL> p = ldpack<T, CPL>(gq + (tok(16 * w + t) + c0));
 #pragma unroll
           for (int e = 0; e < CPL; ++e) qt[e] = to_f32(p.v[e]);
         }
         for (int s = t; s >= 0; --s) {
           float part = 0.f;
           if (tv_) {
-            const Pack<T, CPL> pk = ldpack<T, CPL>(gk + tok(t0 + 16 * w + s) + c0);
-            const Pack<T, CPL> pl = ldpack<T, CPL>(gl + tok(t0 + 16 * w + s) + c0);
+            const Pack<T, CPL> pk = ldpack<T, CPL>(gk + (tok(16 * w + s) + c0));
+            const Pack<T, CPL> pl = ldpack<T, CPL>(gl + (tok(16 * w + s) + c0));
 #pragma unroll
             for (int e = 0; e < CPL; ++e) {
               part += qt[e] * to_f32(pk.v[e]) * __expf(ex[e]);
@@ -320,8 +337,10 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_bwd_kernel(ChunkBwdArgs a) 
     for (int jb = 0; jb < CB; ++jb) mma16(DV[jb], fa, tr4<D>(tdy, 16 * m, 16 * jb));
   }
 
-  // (d) inter terms from S and Lam rows straight from memory, rowsum(S * Lam), carry partials
-  PFrag<T> dyA[KSD], vA[KSD];
+  // (d) inter-chunk terms.  This wave's rows of dy, v and kh = ko e^{Gamma - P_{w+1}}
+  // and its ko in the accumulator arrangement stay in registers while S and Lam
+  // replace the tiles in LDS.
+  PFrag<T> dyA[KSD], vA[KSD], khA[KSD];
 #pragma unroll
   for (int ks = 0; ks < KSD; ++ks) {
     const int jj = 32 * ks + 8 * g;
@@ -329,46 +348,59 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_bwd_kernel(ChunkBwdArgs a) 
     const int j = ok ? jj : 0;
     dyA[ks] = masked(row8<D>(tdy, 16 * w + n16, j), ok);
     vA[ks] = masked(row8<D>(tv, 16 * w + n16, j), ok);
+    float kv[8];
+    unpack8(row8<D>(ko, 16 * w + n16, j), kv);
+    const float4 e0 = ldf4(&sm.fac[w][1][j]), e1 = ldf4(&sm.fac[w][1][j + 4]);
+    Frag f;
+    f.v[0] = kv[0] * e0.x; f.v[1] = kv[1] * e0.y; f.v[2] = kv[2] * e0.z; f.v[3] = kv[3] * e0.w;
+    f.v[4] = kv[4] * e1.x; f.v[5] = kv[5] * e1.y; f.v[6] = kv[6] * e1.z; f.v[7] = kv[7] * e1.w;
+    masked(f, ok);
+    khA[ks] = to_pfrag<T>(f);
   }
-  float cp[CB];                   // sum over this block of ko dk'_inter, channel 16 cb + n
-  float rsv[(CB + NW - 1) / NW];  // rowsum(S * Lam) of the channel blocks cb = w + NW i
-  // S and Lam rows of one channel block, software-pipelined one block ahead (the
-  // compiler barrier keeps every block's loads from being hoisted at once)
-  PFrag<T> sfb[2][KSD], lfb[2][KSD];
-  auto load_rows = [&](PFrag<T> (&sf)[KSD], PFrag<T> (&lf)[KSD], int cb) {
+  Quad<T> kq[CB];  // ko[16w + 4g + r][16 cb + n], as it entered the products
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) kq[cb].set(r, ko[XT::at(16 * w + 4 * g + r, 16 * cb + n16)]);
+  __syncthreads();  // B2: the tiles are dead
+  T *sS = sm.u.sl.S, *sL = sm.u.sl.L;
+#pragma unroll
+  for (int i = 0; i < Cfg::NVS; ++i) {
+    const int idx = tid + i * NT;
+    const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
+    if (idx < Cfg::VS) {
+      *(uint4 *)&sS[XT::at(row, col)] = *(const uint4 *)(gS + (size_t)row * D + col);
+      *(uint4 *)&sL[XT::at(row, col)] = *(const uint4 *)(gL + (size_t)row * D + col);
+    }
+    if (i % 4 == 3) asm volatile("" ::: "memory");  // bounds the loads in flight
+  }
+  __syncthreads();  // B3
+
+  // rowsum(S * Lam) of this wave's channel blocks cb = w + NW i: the diagonal of
+  // the 16 x 16 block S Lam^T, on lane (n >> 2, n)
+  constexpr int RSN = (CB + NW - 1) / NW;
+  float rsv[RSN];
+  float cp[CB];  // sum over this block of ko dk'_inter, channel 16 cb + n
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
     const int c = 16 * cb + n16;
+    f32x4_t tq, tk, dg;
+    acc_zero(tq);
+    acc_zero(tk);
+    acc_zero(dg);
 #pragma unroll
     for (int ks = 0; ks < KSD; ++ks) {
       const int jj = 32 * ks + 8 * g;
       const bool ok = jj < D;
       const int j = ok ? jj : 0;
-      sf[ks] = masked(gload8(gS + (size_t)c * D + j), ok);
-      lf[ks] = masked(gload8(gL + (size_t)c * D + j), ok);
+      const PFrag<T> sf = masked(row8<D>(sS, c, j), ok), lf = masked(row8<D>(sL, c, j), ok);
+      mma(tq, dyA[ks], sf);
+      mma(tk, vA[ks], lf);
+      if (cb % NW == w) mma(dg, sf, lf);
     }
-  };
-  load_rows(sfb[0], lfb[0], 0);
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb) {
-    if (cb + 1 < CB) load_rows(sfb[(cb + 1) & 1], lfb[(cb + 1) & 1], cb + 1);
-    asm volatile("" ::: "memory");
-    const PFrag<T>(&sf)[KSD] = sfb[cb & 1];
-    const PFrag<T>(&lf)[KSD] = lfb[cb & 1];
-    const int c = 16 * cb + n16;
-    f32x4_t tq, tk;
-    acc_zero(tq);
-    acc_zero(tk);
-    float rsum = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KSD; ++ks) {
-      mma(tq, dyA[ks], sf[ks]);
-      mma(tk, vA[ks], lf[ks]);
-      if (cb % NW == w) {
-        float sv[8], lv[8];
-        unpack8(sf[ks], sv);
-        unpack8(lf[ks], lv);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) rsum += sv[i] * lv[i];
-      }
+    if (cb % NW == w) {
+      const int r = n16 & 3;
+      rsv[cb / NW] = (r == 0) ? dg[0] : (r == 1) ? dg[1] : (r == 2) ? dg[2] : dg[3];
     }
     const float eP = sm.fac[w][0][c], eK = sm.fac[w][1][c];
     float ckp = 0.f;
@@ -377,50 +409,25 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_bwd_kernel(ChunkBwdArgs a) 
       DQ[cb][r] += eP * tq[r];
       const float x = eK * tk[r];
       DK[cb][r] += x;
-      ckp += to_f32(ko[XT::at(16 * w + 4 * g + r, c)]) * x;  // ko as it entered the products
+      ckp += kq[cb].get(r) * x;
     }
     cp[cb] = group_sum(ckp);
-    if (cb % NW == w) rsv[cb / NW] = group_sum(rsum);
   }
-  // kh = ko e^{Gamma - P_{w+1}} (k = channels) for the dv term, read before the tiles die
-  PFrag<T> khA[KSD];
-#pragma unroll
-  for (int ks = 0; ks < KSD; ++ks) {
-    const int cc = 32 * ks + 8 * g;
-    const bool ok = cc < D;
-    const int c = ok ? cc : 0;
-    float kv[8];
-    unpack8(row8<D>(ko, 16 * w + n16, c), kv);
-    const float4 e0 = ldf4(&sm.fac[w][1][c]), e1 = ldf4(&sm.fac[w][1][c + 4]);
-    Frag f;
-    f.v[0] = kv[0] * e0.x; f.v[1] = kv[1] * e0.y; f.v[2] = kv[2] * e0.z; f.v[3] = kv[3] * e0.w;
-    f.v[4] = kv[4] * e1.x; f.v[5] = kv[5] * e1.y; f.v[6] = kv[6] * e1.z; f.v[7] = kv[7] * e1.w;
-    masked(f, ok);
-    khA[ks] = to_pfrag<T>(f);
-  }
-  __syncthreads();  // B2: the input tiles are dead
-
-  auto &out = sm.u.out;
-  // =============== phase 2: dv += kh Lam (Lam rows as k)
-#pragma unroll
-  for (int i = 0; i < Cfg::NVS; ++i) {
-    const int idx = tid + i * NT;
-    const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
-    if (idx < Cfg::VS) *(uint4 *)&out.a.lam[XT::at(row, col)] = *(const uint4 *)(gL + (size_t)row * D + col);
-    if (i % 4 == 3) asm volatile("" ::: "memory");  // bounds the loads in flight
-  }
-  __syncthreads();
+  // dv += kh Lam (Lam rows as k)
 #pragma unroll
   for (int jb = 0; jb < CB; ++jb)
 #pragma unroll
     for (int ks = 0; ks < KSD; ++ks) {
       if constexpr (D >= 32) {
-        mma(DV[jb], khA[ks], tr8<D>(out.a.lam, 32 * ks, 16 * jb));
+        mma(DV[jb], khA[ks], tr8<D>(sL, 32 * ks, 16 * jb));
       } else {
-        mma(DV[jb], khA[ks], masked(tr8<D>(out.a.lam, (g < 2) ? 0 : -8 * g, 16 * jb), g < 2));
+        mma(DV[jb], khA[ks], masked(tr8<D>(sL, (g < 2) ? 0 : -8 * g, 16 * jb), g < 2));
       }
     }
-  T *dvs = out.dvs;
+  __syncthreads();  // B4: S and Lam are dead
+
+  // =============== phase 2: dv out, then the epilogues of dq, dk and dlog f
+  T *dvs = sm.u.dvs;
 #pragma unroll
   for (int jb = 0; jb < CB; ++jb)
 #pragma unroll
@@ -432,154 +439,183 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_bwd_kernel(ChunkBwdArgs a) 
     const int idx = lane + 64 * i;
     const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
     const int t = 16 * w + row;
-    if (idx < RV && t < len) *(uint4 *)(gdv + tok(t0 + t) + col) = *(const uint4 *)&dvs[XT::at(t, col)];
+    if (idx < RV && t < len) *(uint4 *)(gdv + (tok(t) + col)) = *(const uint4 *)&dvs[XT::at(t, col)];
   }
-  __syncthreads();  // every wave is done with Lam, which the staging overwrites
+  __syncthreads();  // B5: the dv staging is dead
 
-  // =============== phase 2 (after the dv term): epilogue of dq, dk and dlog f in the prep layout
+  auto &out = sm.u.out;
   if (g == 0) {
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      out.cpart[w][16 * cb + n16] = cp[cb];
-      if (cb % NW == w) out.rs[16 * cb + n16] = rsv[cb / NW];
-    }
+    for (int cb = 0; cb < CB; ++cb) out.cpart[w][16 * cb + n16] = cp[cb];
+
   }
-  float *stg = out.a.stg[w];
-  // stage dq'
+  if (g == (n16 >> 2)) {
+#pragma unroll
+    for (int i = 0; i < RSN; ++i)
+      if (w + NW * i < CB) out.rs[16 * (w + NW * i) + n16] = rsv[i];
+  }
+  float *sq = out.stg[0][w], *sk = out.stg[1][w];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) stg[(4 * g + r) * LDG + 16 * cb + n16] = DQ[cb][r];
+    for (int r = 0; r < 4; ++r) {
+      sq[(4 * g + r) * LDG + 16 * cb + n16] = DQ[cb][r];
+      sk[(4 * g + r) * LDG + 16 * cb + n16] = DK[cb][r];
+    }
   wave_lds_sync();
+  // per token (prep layout): dq = e^{ell} dq', dk = e^{L - ell} dk', and
+  // X = q dq - k dk formed with qo, ko exactly as they entered the products.
+  // A wave whose diagonal block is summed directly takes a slow path that
+  // keeps X in its staging rows instead of registers.
   float X[16][CPL];
-  float l[16][CPL], L[CPL];
-  {
+  if (!wide) {
     Pack<T, CPL> pl[16];
+    float L[CPL], ell[CPL];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) pl[t] = ldtok(gl, 16 * w + t);
-    block_prefix<T, CPL>(pl, l, L);
-  }
+    for (int e = 0; e < CPL; ++e) L[e] = ell[e] = 0.f;
 #pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    const int tt = 16 * w + t;
-    const Pack<T, CPL> pq = ldtok(gq, tt);
-    float dqd[CPL];
+    for (int t = 0; t < 16; ++t) {
+      pl[t] = ldtok(gl, 16 * w + t);
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) dqd[e] = 0.f;
-    if (wide) {
-      // direct diagonal block: sum_{s <= t} dA[t][s] k_s e^{ell_t - ell_s}
-      float ex[CPL];
-#pragma unroll
-      for (int e = 0; e < CPL; ++e) ex[e] = 0.f;
-      const Pack<T, CPL> pdy = ldtok(gdy, tt);
-      for (int s = t; s >= 0; --s) {
-        const Pack<T, CPL> pv = ldtok(gv, 16 * w + s);
-        const Pack<T, CPL> pk = ldtok(gk, 16 * w + s);
-        const Pack<T, CPL> pls = ldtok(gl, 16 * w + s);
-        float part = 0.f;
-#pragma unroll
-        for (int e = 0; e < CPL; ++e) part += to_f32(pdy.v[e]) * to_f32(pv.v[e]);
-        const float dA = wave_sum(part);
-#pragma unroll
-        for (int e = 0; e < CPL; ++e) {
-          dqd[e] += dA * to_f32(pk.v[e]) * __expf(ex[e]);
-          ex[e] += floor_logf(to_f32(pls.v[e]));
-        }
-      }
-    }
-    Pack<T, CPL> o;
-#pragma unroll
-    for (int e = 0; e < CPL; ++e) {
-      const float el = __expf(l[t][e]);
-      const float qor = to_f32(from_f32<T>(to_f32(pq.v[e]) * el));  // qo as it entered the products
-      const float d1 = stg[t * LDG + c0 + e];
-      o.v[e] = from_f32<T>(el * d1 + dqd[e]);
-      X[t][e] = qor * d1 + to_f32(pq.v[e]) * dqd[e];
-    }
-    if (tt < len && has_ch) stpack<T, CPL>(gdq + tok(t0 + tt) + c0, o);
-  }
-  wave_lds_sync();
-  // stage dk'
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) stg[(4 * g + r) * LDG + 16 * cb + n16] = DK[cb][r];
-  wave_lds_sync();
-#pragma unroll
-  for (int s = 0; s < 16; ++s) {
-    const int ss = 16 * w + s;
-    const Pack<T, CPL> pk = ldtok(gk, ss);
-    Pack<T, CPL> o;
-    float dkd[CPL];
-#pragma unroll
-    for (int e = 0; e < CPL; ++e) dkd[e] = 0.f;
-    if (wide) {
-      // direct diagonal block: sum_{t >= s} dA[t][s] q_t e^{ell_t - ell_s}
-      float ex[CPL];
-#pragma unroll
-      for (int e = 0; e < CPL; ++e) ex[e] = 0.f;
-      const Pack<T, CPL> pv = ldtok(gv, ss);
-      for (int t = s; t < 16; ++t) {
-        const Pack<T, CPL> pdy = ldtok(gdy, 16 * w + t);
-        const Pack<T, CPL> pq = ldtok(gq, 16 * w + t);
-        float part = 0.f;
-#pragma unroll
-        for (int e = 0; e < CPL; ++e) part += to_f32(pdy.v[e]) * to_f32(pv.v[e]);
-        const float dA = wave_sum(part);
-        if (t > s) {
-          const Pack<T, CPL> plt = ldtok(gl, 16 * w + t);
-#pragma unroll
-          for (int e = 0; e < CPL; ++e) ex[e] += floor_logf(to_f32(plt.v[e]));
-        }
-#pragma unroll
-        for (int e = 0; e < CPL; ++e) dkd[e] += dA * to_f32(pq.v[e]) * __expf(ex[e]);
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < CPL; ++e) {
-      const float ek = __expf(L[e] - l[s][e]);
-      const float kor = to_f32(from_f32<T>(to_f32(pk.v[e]) * ek));  // ko as it entered the products
-      const float d1 = stg[s * LDG + c0 + e];
-      o.v[e] = from_f32<T>(ek * d1 + dkd[e]);
-      X[s][e] -= kor * d1 + to_f32(pk.v[e]) * dkd[e];
-    }
-    if (ss < len && has_ch) stpack<T, CPL>(gdk + tok(t0 + ss) + c0, o);
-  }
-  // block sums of X
-  if (has_ch) {
-#pragma unroll
-    for (int e = 0; e < CPL; ++e) {
-      float s = 0.f;
-#pragma unroll
-      for (int t = 0; t < 16; ++t) s += X[t][e];
-      out.tot[w][c0 + e] = s;
-    }
-  }
-  __syncthreads();  // B3: tot, cpart, rs complete; staging dead
-  if (has_ch) {
-#pragma unroll
-    for (int e = 0; e < CPL; ++e) {
-      const int c = c0 + e;
-      float carry = sm.eG[c] * out.rs[c];
-#pragma unroll
-      for (int i = 0; i < NW; ++i) carry += out.cpart[i][c] + ((i > w) ? out.tot[i][c] : 0.f);
-      float sfx = carry;
-#pragma unroll
-      for (int t = 15; t >= 0; --t) {
-        sfx += X[t][e];
-        X[t][e] = sfx;
-      }
+      for (int e = 0; e < CPL; ++e) L[e] += floor_logf(to_f32(pl[t].v[e]));
     }
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       const int tt = 16 * w + t;
-      Pack<T, CPL> o;
+      const Pack<T, CPL> pq = ldtok(gq, tt), pk = ldtok(gk, tt);
+      Pack<T, CPL> oq, ok;
 #pragma unroll
-      for (int e = 0; e < CPL; ++e) o.v[e] = from_f32<T>(X[t][e]);
-      if (tt < len) stpack<T, CPL>(gdl + tok(t0 + tt) + c0, o);
+      for (int e = 0; e < CPL; ++e) {
+        ell[e] += floor_logf(to_f32(pl[t].v[e]));
+        const float el = __expf(ell[e]), ek = __expf(L[e] - ell[e]);
+        const float qor = to_f32(from_f32<T>(to_f32(pq.v[e]) * el));
+        const float kor = to_f32(from_f32<T>(to_f32(pk.v[e]) * ek));
+        const float d1 = sq[t * LDG + c0 + e], d2 = sk[t * LDG + c0 + e];
+        oq.v[e] = from_f32<T>(el * d1);
+        ok.v[e] = from_f32<T>(ek * d2);
+        X[t][e] = qor * d1 - kor * d2;
+      }
+      if (tt < len && has_ch) {
+        stpack<T, CPL>(gdq + (tok(tt) + c0), oq);
+        stpack<T, CPL>(gdk + (tok(tt) + c0), ok);
+      }
+    }
+    if (has_ch) {
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) {
+        float s_ = 0.f;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) s_ += X[t][e];
+        out.tot[w][c0 + e] = s_;
+      }
+    }
+  } else {
+    // diagonal block summed directly: dq_t adds sum_{s <= t} dA[t][s] k_s e^{ell_t - ell_s},
+    // dk_t adds sum_{u >= t} dA[u][t] q_u e^{ell_u - ell_t} (every exponent <= 0)
+    float L[CPL], ell[CPL], tot[CPL];
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) L[e] = ell[e] = tot[e] = 0.f;
+    for (int t = 0; t < 16; ++t) {
+      const Pack<T, CPL> p = ldtok(gl, 16 * w + t);
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) L[e] += floor_logf(to_f32(p.v[e]));
+    }
+    for (int t = 0; t < 16; ++t) {
+      const int tt = 16 * w + t;
+      const Pack<T, CPL> pq = ldtok(gq, tt), pk = ldtok(gk, tt), plt = ldtok(gl, tt);
+      const Pack<T, CPL> pdy = ldtok(gdy, tt), pv = ldtok(gv, tt);
+      float dqd[CPL], dkd[CPL], ex[CPL];
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) {
+        ell[e] += floor_logf(to_f32(plt.v[e]));
+        dqd[e] = dkd[e] = ex[e] = 0.f;
+      }
+      for (int s_ = t; s_ >= 0; --s_) {
+        const Pack<T, CPL> pvs = ldtok(gv, 16 * w + s_), pks = ldtok(gk, 16 * w + s_);
+        const Pack<T, CPL> pls = ldtok(gl, 16 * w + s_);
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) part += to_f32(pdy.v[e]) * to_f32(pvs.v[e]);
+        const float dA = wave_sum(part);
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+          dqd[e] += dA * to_f32(pks.v[e]) * __expf(ex[e]);
+          ex[e] += floor_logf(to_f32(pls.v[e]));
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) ex[e] = 0.f;
+      for (int u = t; u < 16; ++u) {
+        const Pack<T, CPL> pdu = ldtok(gdy, 16 * w + u), pqu = ldtok(gq, 16 * w + u);
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) part += to_f32(pdu.v[e]) * to_f32(pv.v[e]);
+        const float dA = wave_sum(part);
+        if (u > t) {
+          const Pack<T, CPL> plu = ldtok(gl, 16 * w + u);
+#pragma unroll
+          for (int e = 0; e < CPL; ++e) ex[e] += floor_logf(to_f32(plu.v[e]));
+        }
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) dkd[e] += dA * to_f32(pqu.v[e]) * __expf(ex[e]);
+      }
+      Pack<T, CPL> oq, ok;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) {
+        const float el = __expf(ell[e]), ek = __expf(L[e] - ell[e]);
+        const float qv = to_f32(pq.v[e]), kv = to_f32(pk.v[e]);
+        const float qor = to_f32(from_f32<T>(qv * el)), kor = to_f32(from_f32<T>(kv * ek));
+        const float d1 = sq[t * LDG + c0 + e], d2 = sk[t * LDG + c0 + e];
+        oq.v[e] = from_f32<T>(el * d1 + dqd[e]);
+        ok.v[e] = from_f32<T>(ek * d2 + dkd[e]);
+        const float x = (qor * d1 + qv * dqd[e]) - (kor * d2 + kv * dkd[e]);
+        if (has_ch) sq[t * LDG + c0 + e] = x;  // X_t replaces the consumed dq'_t
+        tot[e] += x;
+      }
+      if (tt < len && has_ch) {
+        stpack<T, CPL>(gdq + (tok(tt) + c0), oq);
+        stpack<T, CPL>(gdk + (tok(tt) + c0), ok);
+      }
+    }
+    if (has_ch)
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) out.tot[w][c0 + e] = tot[e];
+  }
+  __syncthreads();  // B6: tot, cpart, rs complete
+  if (has_ch) {
+    float carry[CPL];
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) {
+      const int c = c0 + e;
+      carry[e] = sm.eG[c] * out.rs[c];
+#pragma unroll
+      for (int i = 0; i < NW; ++i) carry[e] += out.cpart[i][c] + ((i > w) ? out.tot[i][c] : 0.f);
+    }
+    if (!wide) {
+#pragma unroll
+      for (int t = 15; t >= 0; --t) {
+        const int tt = 16 * w + t;
+        Pack<T, CPL> o;
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+          carry[e] += X[t][e];
+          o.v[e] = from_f32<T>(carry[e]);
+        }
+        if (tt < len) stpack<T, CPL>(gdl + (tok(tt) + c0), o);
+      }
+    } else {
+      for (int t = 15; t >= 0; --t) {
+        const int tt = 16 * w + t;
+        Pack<T, CPL> o;
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+          carry[e] += sq[t * LDG + c0 + e];
+          o.v[e] = from_f32<T>(carry[e]);
+        }
+        if (tt < len) stpack<T, CPL>(gdl + (tok(tt) + c0), o);
+      }
     }
   }
-
 }
 
 template <typename T, int D, int C>

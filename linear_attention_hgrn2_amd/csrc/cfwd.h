@@ -39,15 +39,16 @@ template <typename T, int D, int C> struct CfwdCfg {
   static constexpr int NPAIR = NB * (NB + 1) / 2;
   static constexpr int VV = C * D / EPV, NVV = (VV + NT - 1) / NT;
   static constexpr int VS = D * D / EPV, NVS = (VS + NT - 1) / NT;
+  static constexpr int LD = RowTile<T, D>::LD;
   struct KV {
-    T ko[C * D];
-    T v[C * D];
+    T ko[C * LD];
+    T v[C * LD];
   };
   struct Smem {
-    T qo[C * D];  // RowTile<T, D>; later the y staging of each wave's rows
+    T qo[C * LD];  // RowTile<T, D>; later the y staging of each wave's rows
     union {
-      KV kv;       // scores and the intra-chunk product
-      T S[D * D];  // then the chunk's initial state
+      KV kv;        // scores and the intra-chunk product
+      T S[D * LD];  // then the chunk's initial state
     } u;
     float Lb[NB][D];
     float gp[NPAIR][D];
@@ -95,7 +96,15 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_fwd_kernel(ChunkFwdArgs a) 
   const T *gl = (const T *)a.log_f;
   const T *gs = (const T *)a.states + ((size_t)bh * (N + 1) + n) * D * D;
   T *gy = (T *)a.y;
-  auto tok = [&](int t) { return (((size_t)b * T_ + t) * H + h) * D; };
+  // chunk-uniform base pointers; per-lane 32-bit element offsets within the chunk
+  const size_t cbase = (((size_t)b * T_ + t0) * H + h) * D;
+  const uint32_t HD = (uint32_t)H * D;
+  gq += cbase;
+  gk += cbase;
+  gv += cbase;
+  gl += cbase;
+  gy += cbase;
+  auto tok = [&](int t) { return (uint32_t)t * HD; };  // token t of the chunk
 
   // ---- loads: the state tile first (used last), v, then this wave's q, k, log f
   uint4 ps[Cfg::NVS];
@@ -109,7 +118,7 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_fwd_kernel(ChunkFwdArgs a) 
     const int idx = tid + i * NT;
     const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (idx < Cfg::VV && row < len) v = *(const uint4 *)(gv + tok(t0 + row) + col);
+    if (idx < Cfg::VV && row < len) v = *(const uint4 *)(gv + (tok(row) + col));
     if (idx < Cfg::VV) *(uint4 *)&sm.u.kv.v[XT::at(row, col)] = v;
   }
   float l[16][CPL], L[CPL];
@@ -122,9 +131,9 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_fwd_kernel(ChunkFwdArgs a) 
 #pragma unroll
       for (int e = 0; e < CPL; ++e) pq[t].v[e] = pk[t].v[e] = pl[t].v[e] = from_f32<T>(0.f);
       if (tt < len && has_ch) {
-        pq[t] = ldpack<T, CPL>(gq + tok(t0 + tt) + c0);
-        pk[t] = ldpack<T, CPL>(gk + tok(t0 + tt) + c0);
-        pl[t] = ldpack<T, CPL>(gl + tok(t0 + tt) + c0);
+        pq[t] = ldpack<T, CPL>(gq + (tok(tt) + c0));
+        pk[t] = ldpack<T, CPL>(gk + (tok(tt) + c0));
+        pl[t] = ldpack<T, CPL>(gl + (tok(tt) + c0));
       }
     }
     block_prefix<T, CPL>(pl, l, L);
@@ -192,15 +201,15 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_fwd_kernel(ChunkFwdArgs a) 
           ex[e] = 0.f;
         }
         if (tv) {
-          const Pack<T, CPL> pq = ldpack<T, CPL>(gq + tok(t0 + 16 * w + t) + c0);
+          const Pack<T, CPL> pq = ldpack<T, CPL>(gq + (tok(16 * w + t) + c0));
 #pragma unroll
           for (int e = 0; e < CPL; ++e) qt[e] = to_f32(pq.v[e]);
         }
         for (int s = t; s >= 0; --s) {
           float part = 0.f;
           if (tv) {
-            const Pack<T, CPL> pk = ldpack<T, CPL>(gk + tok(t0 + 16 * w + s) + c0);
-            const Pack<T, CPL> pl = ldpack<T, CPL>(gl + tok(t0 + 16 * w + s) + c0);
+            const Pack<T, CPL> pk = ldpack<T, CPL>(gk + (tok(16 * w + s) + c0));
+            const Pack<T, CPL> pl = ldpack<T, CPL>(gl + (tok(16 * w + s) + c0));
 #pragma unroll
             for (int e = 0; e < CPL; ++e) {
               part += qt[e] * to_f32(pk.v[e]) * __expf(ex[e]);
@@ -304,7 +313,7 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_fwd_kernel(ChunkFwdArgs a) 
     const int idx = lane + 64 * i;
     const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
     const int t = 16 * w + row;
-    if (idx < RV && t < len) *(uint4 *)(gy + tok(t0 + t) + col) = *(const uint4 *)&sm.qo[XT::at(t, col)];
+    if (idx < RV && t < len) *(uint4 *)(gy + (tok(t) + col)) = *(const uint4 *)&sm.qo[XT::at(t, col)];
   }
 }
 

@@ -45,8 +45,8 @@ template <typename T, int D, int C, bool REV> struct ScanCfg {
   static constexpr int VZ = C * DJ / EPV;               // 16-byte vectors of one z slice
   static constexpr int NVZ = (VZ + NT - 1) / NT;
   struct Smem {
-    T x[C * D];      // decayed x, RowTile<T, D>
-    T z[2][C * DJ];  // z slice, RowTile<T, DJ>, double-buffered
+    T x[C * RowTile<T, D>::LD];      // decayed x, RowTile<T, D>
+    T z[2][C * RowTile<T, DJ>::LD];  // z slice, RowTile<T, DJ>, double-buffered
     float Lb[NW][D]; // sub-block totals of log f
     float eG[D];     // e^Gamma
   };

@@ -1,8 +1,9 @@
 // LDS tiles and operand loaders for the sequence-parallel chunk kernels (gfx950).
 //
-// Row tiles hold [rows][W] elements with each row's 16-byte chunks XOR-swizzled
-// by the row index, so sixteen lanes that read the same logical chunk of
-// sixteen consecutive rows hit distinct banks without padding.
+// Row tiles hold [rows][W] elements with every row padded by 16 bytes: the
+// row stride then moves each row four banks on, so sixteen lanes reading one
+// 16-byte chunk of sixteen consecutive rows hit distinct banks, and every
+// address of a tile is one per-lane base plus a compile-time offset.
 //
 // Operand fragments follow the convention in common.h (lane l = 16g + n; an
 // operand fragment carries k-slots, an accumulator holds rows 4g + r of
@@ -22,11 +23,8 @@ typedef short v4s_t __attribute__((ext_vector_type(4)));
 
 template <typename T, int W> struct RowTile {
   static constexpr int EPV = 16 / (int)sizeof(T);  // elements per 16-byte chunk
-  static constexpr int NCH = W / EPV;              // chunks per row
-  static_assert(NCH >= 1 && (NCH & (NCH - 1)) == 0, "row width");
-  __device__ static __forceinline__ int at(int r, int c) {
-    return r * W + ((((c / EPV) ^ r) & (NCH - 1)) * EPV) + (c % EPV);
-  }
+  static constexpr int LD = W + EPV;               // row stride in elements
+  __device__ static __forceinline__ int at(int r, int c) { return r * LD + c; }
 };
 
 // ------------------------------------------------------------ 4-slot fragments (16-deep products)
@@ -216,6 +214,24 @@ template <typename T, int N> __device__ __forceinline__ void stpack(T *p, const 
     *(uint4 *)__builtin_assume_aligned(p, 16) = u;
   }
 }
+
+// four values of T kept packed in registers (bf16: two per 32-bit register)
+template <typename T> struct Quad;
+template <> struct Quad<bf16_t> {
+  uint32_t u[2] = {0u, 0u};
+  __device__ __forceinline__ void set(int i, bf16_t x) {
+    const uint32_t b = x.bits;
+    u[i >> 1] = (i & 1) ? ((u[i >> 1] & 0xffffu) | (b << 16)) : ((u[i >> 1] & 0xffff0000u) | b);
+  }
+  __device__ __forceinline__ float get(int i) const {
+    return __uint_as_float((i & 1) ? (u[i >> 1] & 0xffff0000u) : (u[i >> 1] << 16));
+  }
+};
+template <> struct Quad<float> {
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  __device__ __forceinline__ void set(int i, float x) { v[i] = x; }
+  __device__ __forceinline__ float get(int i) const { return v[i]; }
+};
 
 // ------------------------------------------------------------ wave-level helpers
 // Orders this wave's earlier LDS accesses before its later ones, for data
