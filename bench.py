@@ -2,8 +2,11 @@
 
 One step = one training pass over one batch of the H16 d128 T4096 workload
 (B8 H16 T4096, d_k = d_v = 128, bf16, chunk 64): hgrn2_fwd (saving the
-chunk-boundary states) followed by hgrn2_bwd.  Three resident input sets
-(forget-gate lower bound 0, 0.3, 0.6) are rotated across steps.  The decode
+chunk-boundary states) followed by hgrn2_bwd, issued as the four single
+launches they are made of (state scan, per-chunk outputs, adjoint scan,
+per-chunk gradients) so that HIP events on the launch stream bracket each
+kernel.  Three resident input sets (forget-gate lower bound 0, 0.3, 0.6) are
+rotated across steps.  The decode
 step (B256 H16 d128, float32 state) is timed as well and reported in HBM
 GB/s.  Inputs are seeded synthetic data generated on the host and copied to
 HBM before timing.
@@ -119,6 +122,40 @@ class KernelTimer:
         return float(np.mean([s.elapsed_time(e) for s, e in self.pairs[name]]))
 
 
+# the four launches of one training step, in order, with the kernel each one runs
+TRAIN_KERNELS = (("scan", "hgrn2_scan_kernel (forward)"), ("cfwd", "hgrn2_chunk_fwd_kernel"),
+                 ("scan_rev", "hgrn2_scan_kernel (reverse)"), ("cbwd", "hgrn2_chunk_bwd_kernel"))
+
+
+def kernel_label(name: str):
+    """rocprofv3 kernel name -> one of TRAIN_KERNELS' labels, "decode", or None."""
+    n = _short(name)
+    if n.startswith("hgrn2_scan_kernel"):
+        return "scan_rev" if "true" in n else "scan"
+    if n.startswith("hgrn2_chunk_fwd_kernel"):
+        return "cfwd"
+    if n.startswith("hgrn2_chunk_bwd_kernel"):
+        return "cbwd"
+    if n.startswith("hgrn2_decode_kernel"):
+        return "decode"
+    return None
+
+
+def train_algorithmic_bytes(w):
+    """Algorithmic HBM bytes per launch of each training kernel: every tensor
+    the launch reads or writes, once.  tok = one bf16 [B,T,H,D] tensor; a
+    state or adjoint entry is one bf16 [D,D] matrix per (b,h)."""
+    tok = w.B * w.T * w.H * w.D * 2
+    N = w.T // w.chunk
+    ent = w.B * w.H * w.D * w.D * 2
+    return {
+        "scan": 3 * tok + (N + 1) * ent,                 # k, v, log_f in; states 0..N out
+        "cfwd": 4 * tok + N * ent + tok,                 # q, k, v, log_f, states 0..N-1 in; y out
+        "scan_rev": 3 * tok + N * ent,                   # q, dy, log_f in; adjoints 1..N out
+        "cbwd": 5 * tok + 2 * N * ent + 4 * tok,         # q, k, v, log_f, dy, states, adjoints in; 4 grads out
+    }
+
+
 def bench_train(torch, m, args):
     import synth
     w = synth.WORKLOADS["train_bf16"]
@@ -127,22 +164,24 @@ def bench_train(torch, m, args):
     dev = sets[0]["q"].device
     y = torch.empty((B, T, H, D), dtype=torch.bfloat16, device=dev)
     states = torch.empty(m.states_shape(B, T, H, D, C), dtype=torch.bfloat16, device=dev)
+    lam = torch.empty(m.adjoints_shape(B, T, H, D, C), dtype=torch.bfloat16, device=dev)
     grads = [torch.empty((B, T, H, D), dtype=torch.bfloat16, device=dev) for _ in range(4)]
-    ws = torch.empty(int(m.lib().hgrn2_bwd_workspace_bytes(B, T, H, D, D, C, 1, 1)), dtype=torch.uint8,
-                     device=dev)
 
     def step(i, timer=None):
         s = sets[i % len(sets)]
-        t = timer.start("fwd") if timer else None
-        m.fwd(s["q"], s["k"], s["v"], s["log_f"], None, chunk=C, want_ht=False,
-              y=y, states=states)
-        if timer:
-            timer.stop(t)
-            t = timer.start("bwd")
-        m.bwd(s["q"], s["k"], s["v"], s["log_f"], s["dy"], None, None, states, chunk=C,
-              want_dh0=False, dq=grads[0], dk=grads[1], dv=grads[2], dlog_f=grads[3], ws=ws)
-        if timer:
-            timer.stop(t)
+        calls = (
+            lambda: m.fwd(s["q"], s["k"], s["v"], s["log_f"], None, chunk=C, want_ht=False, want_y=False,
+                          states=states),
+            lambda: m.fwd_chunk(s["q"], s["k"], s["v"], s["log_f"], states, chunk=C, y=y),
+            lambda: m.bwd_adjoint(s["q"], s["log_f"], s["dy"], None, chunk=C, adjoints=lam),
+            lambda: m.bwd_chunk(s["q"], s["k"], s["v"], s["log_f"], s["dy"], states, lam, chunk=C,
+                                dq=grads[0], dk=grads[1], dv=grads[2], dlog_f=grads[3]),
+        )
+        for (label, _), call in zip(TRAIN_KERNELS, calls):
+            t = timer.start(label) if timer else None
+            call()
+            if timer:
+                timer.stop(t)
 
     for i in range(args.warmup):
         step(i)
@@ -160,9 +199,9 @@ def bench_train(torch, m, args):
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
-    fwd_ms, bwd_ms = timer.mean_ms("fwd"), timer.mean_ms("bwd")
-    log("timed: %.3f ms/step (fwd %.3f ms, bwd %.3f ms)" % (ms, fwd_ms, bwd_ms))
-    return dict(w=w, ms=ms, fwd_ms=fwd_ms, bwd_ms=bwd_ms, host=sets[0]["host"])
+    kms = {label: timer.mean_ms(label) for label, _ in TRAIN_KERNELS}
+    log("timed: %.3f ms/step (%s)" % (ms, ", ".join("%s %.3f ms" % kv for kv in kms.items())))
+    return dict(w=w, ms=ms, kernel_ms=kms, host=sets[0]["host"])
 
 
 def bench_decode(torch, m, args):
@@ -229,6 +268,7 @@ def _short(name: str) -> str:
 def summarize(trace_dir, fetch_dir, write_dir):
     """profiles/ summaries from the csv output of TRACE_CMD and the two PMC_CMD runs."""
     digest = kernel_source_digest()
+    os.makedirs(PROFILES, exist_ok=True)
     # kernel-trace statistics
     rows = _csv(os.path.join(trace_dir, "run_kernel_stats.csv"))
     out = ["rocprofv3 kernel-trace statistics, HGRN2 training step (B8 H16 T4096 d128 bf16 chunk64)",
@@ -236,11 +276,20 @@ def summarize(trace_dir, fetch_dir, write_dir):
            "command: " + TRACE_CMD, "source_digest: " + digest, "",
            "%-52s %6s %12s %10s %10s %10s %6s" % ("kernel", "calls", "total_us", "avg_us",
                                                     "min_us", "max_us", "pct")]
+    alg = train_algorithmic_bytes(__import__("synth").WORKLOADS["train_bf16"])
+    rates = []
     for r in rows:
         out.append("%-52s %6d %12.1f %10.1f %10.1f %10.1f %6.2f" % (
             _short(r["Name"])[:52], int(r["Calls"]), float(r["TotalDurationNs"]) / 1e3,
             float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
             float(r["Percentage"])))
+        label = kernel_label(r["Name"])
+        if label in alg:
+            gbs = alg[label] / float(r["AverageNs"])
+            rates.append("  %-9s algorithmic %7.1f MB per launch / average %8.1f us = %7.1f GB/s "
+                         "(%.1f%% of %.0f GB/s)" % (label, alg[label] / 1e6, float(r["AverageNs"]) / 1e3,
+                                                   gbs, 100 * gbs / HBM_PEAK_GBS, HBM_PEAK_GBS))
+    out += [""] + rates
     kt = _csv(os.path.join(trace_dir, "run_kernel_trace.csv"))
     seen = set()
     out.append("")
@@ -271,10 +320,6 @@ def summarize(trace_dir, fetch_dir, write_dir):
     assert copy, "the counter runs need --calib-copy"
     f_fac = CALIB_BYTES / (fetch[copy[0]] * 1024)
     w_fac = CALIB_BYTES / (write[copy[0]] * 1024)
-    w = __import__("synth").WORKLOADS["train_bf16"]
-    tok = w.B * w.T * w.H * w.D * 2
-    st = w.B * w.H * (w.T // w.chunk + 1) * w.D * w.D * 2
-    alg = {"hgrn2_fwd_kernel": (4 * tok, tok + st), "hgrn2_bwd_kernel": (5 * tok + st, 4 * tok)}
     out = ["HBM traffic per launch, HGRN2 training step (B8 H16 T4096 d128 bf16 chunk64)",
            "fetch command: " + PMC_CMD.format(ctr="FETCH_SIZE", dir="fetch"),
            "write command: " + PMC_CMD.format(ctr="WRITE_SIZE", dir="write"),
@@ -283,15 +328,14 @@ def summarize(trace_dir, fetch_dir, write_dir):
            "fetch_scale: %.4f" % f_fac, "write_scale: %.4f" % w_fac,
            "source_digest: " + digest, ""]
     for k in fetch:
-        short = _short(k).split("<")[0]
-        if short not in alg:
+        label = kernel_label(k)
+        if label not in alg:
             continue
         fb, wb = fetch[k] * 1024 * f_fac, write[k] * 1024 * w_fac
-        ar, aw = alg[short]
-        out.append("  %s: read %.1f MB (algorithmic %.1f), written %.1f MB (algorithmic %.1f), "
-                   "total / algorithmic = %.3f" % (_short(k), fb / 1e6, ar / 1e6, wb / 1e6, aw / 1e6,
-                                                   (fb + wb) / (ar + aw)))
-        out.append("traffic_bytes_per_launch %s: %.0f" % (short, fb + wb))
+        out.append("  %s (%s): read %.1f MB, written %.1f MB, total %.1f MB; algorithmic %.1f MB; "
+                   "total / algorithmic = %.3f" % (_short(k), label, fb / 1e6, wb / 1e6, (fb + wb) / 1e6,
+                                                   alg[label] / 1e6, (fb + wb) / alg[label]))
+        out.append("traffic_bytes_per_launch %s: %.0f" % (label, fb + wb))
     with open(TRAFFIC_SUMMARY, "w") as f:
         f.write("\n".join(out) + "\n")
     print("\n".join(out))
@@ -323,28 +367,22 @@ def main():
         out["config"] = {"workload": "train_bf16: B8 H16 T4096 d128 chunk64 fwd(states)+bwd",
                          "global_batch": w.B, "seq_len": w.T, "heads": w.H, "head_dim": w.D,
                          "chunk": w.chunk, "parallelism": "none (1 GPU)"}
-        tok = w.B * w.T * w.H * w.D * 2                 # one bf16 [B,T,H,D] tensor
-        st = w.B * w.H * (w.T // w.chunk + 1) * w.D * w.D * 2   # bf16 chunk-boundary states
-        fwd_bytes = 4 * tok + tok + st                  # q,k,v,log_f in; y, states out
-        bwd_bytes = 5 * tok + st + 4 * tok              # q,k,v,log_f,dy,states in; 4 grads out
+        alg = train_algorithmic_bytes(w)
+        kms = res["kernel_ms"]
         th = w.B * w.T * w.H
-        fwd_flop = th * (w.chunk * 2 * w.D + 4 * w.D * w.D)
-        bwd_flop = th * (5 * w.chunk * w.D + 8 * w.D * w.D)
-        dom = "bwd" if res["bwd_ms"] >= res["fwd_ms"] else "fwd"
-        kms = res[dom + "_ms"]
-        kbytes = bwd_bytes if dom == "bwd" else fwd_bytes
-        ach = kbytes / (kms * 1e-3) / 1e9
-        out["roofline"] = {"kernel": "hgrn2_%s_kernel" % dom, "bound": "hbm", "achieved": ach,
-                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
-                           "traffic": measured_traffic("hgrn2_%s_kernel" % dom), "ms": kms,
-                           "algorithmic_bytes": kbytes, "source_digest": kernel_source_digest()}
-        out["kernels"] = {
-            "fwd": {"ms": res["fwd_ms"], "bytes": fwd_bytes, "GBps": fwd_bytes / res["fwd_ms"] / 1e6,
-                    "TFLOPs": fwd_flop / res["fwd_ms"] / 1e9},
-            "bwd": {"ms": res["bwd_ms"], "bytes": bwd_bytes, "GBps": bwd_bytes / res["bwd_ms"] / 1e6,
-                    "TFLOPs": bwd_flop / res["bwd_ms"] / 1e9},
-            "mfma_frac_step": (fwd_flop + bwd_flop) / (res["ms"] * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
-        }
+        step_flop = th * (w.chunk * 2 * w.D + 4 * w.D * w.D) + th * (5 * w.chunk * w.D + 8 * w.D * w.D)
+        dom = max(kms, key=kms.get)
+        ach = alg[dom] / (kms[dom] * 1e-3) / 1e9
+        kname = dict(TRAIN_KERNELS)[dom]
+        out["roofline"] = {"kernel": kname, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic(dom),
+                           "ms": kms[dom], "algorithmic_bytes": alg[dom],
+                           "source_digest": kernel_source_digest()}
+        out["kernels"] = {label: {"kernel": kn, "ms": kms[label], "bytes": alg[label],
+                                  "GBps": alg[label] / kms[label] / 1e6,
+                                  "frac_hbm": alg[label] / kms[label] / 1e6 / HBM_PEAK_GBS}
+                          for label, kn in TRAIN_KERNELS}
+        out["mfma_frac_step"] = step_flop / (res["ms"] * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)
     if args.only in ("decode", "all"):
         dres = bench_decode(torch, m, args)
         out["decode"] = {"workload": "decode_f32: B256 H16 d128, float32 state", "ms": dres["ms"],

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define HGRN2_ABI_VERSION 2
+#define HGRN2_ABI_VERSION 3
 
 typedef enum {
   HGRN2_OK = 0,
@@ -100,7 +100,8 @@ size_t hgrn2_bwd_workspace_bytes(int B, int T, int H, int DK, int DV, int chunk,
  * Chunked forward (HGRN2 summary §3.2 p.5, chunkwise form of the recurrence).
  * Two launches on `stream`: a scan over the chunks of every (b, h) that
  * writes each chunk-boundary state, then the outputs of all chunks in
- * parallel from those states.
+ * parallel from those states (the second is hgrn2_fwd_chunk).  With y = NULL
+ * only the scan runs (one launch).
  *   q, k, log_f : [B,T,H,DK] dtype      v : [B,T,H,DV] dtype
  *   h0          : [B,H,DK,DV] float32, or NULL for a zero initial state
  *   y           : [B,T,H,DV] dtype (written), or NULL (states and ht only)
@@ -118,7 +119,9 @@ hgrn2_status hgrn2_fwd(int B, int T, int H, int DK, int DV, int chunk, int dtype
 
 /*
  * Chunked backward by reverse chunk scan of the state adjoint, for the loss
- * L = sum(y * dy) + sum(ht * dht).  Gradients are partial derivatives with k
+ * L = sum(y * dy) + sum(ht * dht).  Launches on `stream`: the forward state
+ * scan when states_in is NULL, then hgrn2_bwd_adjoint (adjoints into the
+ * front of ws), then hgrn2_bwd_chunk.  Gradients are partial derivatives with k
  * and log_f independent; a caller that ties k = 1 - exp(log_f) adds
  * -exp(log_f) * dk to dlog_f itself.
  *   q, k, v, log_f, h0 : as passed to hgrn2_fwd (same chunk size)
@@ -128,14 +131,54 @@ hgrn2_status hgrn2_fwd(int B, int T, int H, int DK, int DV, int chunk, int dtype
  *   dht         : [B,H,DK,DV] float32, or NULL (zero)
  *   dq, dk, dlog_f : [B,T,H,DK] dtype (written)   dv : [B,T,H,DV] dtype (written)
  *   dh0         : [B,H,DK,DV] float32 (written), or NULL (not wanted)
- *   ws, ws_bytes: workspace (see hgrn2_bwd_workspace_bytes); may be NULL/0
- *                 when states_in is given.
+ *   ws, ws_bytes: workspace of at least hgrn2_bwd_workspace_bytes() bytes
+ *                 (always needed: it holds the adjoints).
  */
 hgrn2_status hgrn2_bwd(int B, int T, int H, int DK, int DV, int chunk, int dtype,
                        const void *q, const void *k, const void *v, const void *log_f,
                        const float *h0, const void *states_in, const void *dy,
                        const float *dht, void *dq, void *dk, void *dv, void *dlog_f,
                        float *dh0, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The single launches that hgrn2_fwd and hgrn2_bwd are made of, for callers
+ * that schedule or time them one by one.  Same conventions and checks as the
+ * composite calls; each enqueues exactly one kernel.
+ *
+ * hgrn2_fwd_chunk: y of every chunk from the chunk-boundary states that
+ * hgrn2_fwd(..., y = NULL, states_out = states, ...) wrote (chunkwise form,
+ * HGRN2 summary §3.2 p.5): y = (in-chunk decayed scores) v + (q scaled by the
+ * in-chunk cumulative decay) S_{start of chunk}.
+ *   states : [B,H,N+1,DK,DV] dtype, read      y : [B,T,H,DV] dtype, written
+ */
+hgrn2_status hgrn2_fwd_chunk(int B, int T, int H, int DK, int DV, int chunk, int dtype,
+                             const void *q, const void *k, const void *v, const void *log_f,
+                             const void *states, void *y, void *stream);
+
+/*
+ * hgrn2_bwd_adjoint: the gradient of the loss with respect to the state at
+ * every chunk end, by a reverse scan over the chunks (the adjoint of the
+ * recurrence: Lambda_{t-1} = Diag(f_t) Lambda_t + q_t^T dy_t, from
+ * Lambda_T = dht).
+ *   adjoints : [B,H,N,DK,DV] dtype (written): entry n is the adjoint of the
+ *              state after chunk n+1 (n = 0..N-1), B*H*N*DK*DV*sizeof(dtype)
+ *              bytes (= hgrn2_bwd_workspace_bytes(..., have_states = 1)).
+ *   dht      : [B,H,DK,DV] float32, or NULL (zero)
+ *   dh0      : [B,H,DK,DV] float32 (written), or NULL (not wanted)
+ */
+hgrn2_status hgrn2_bwd_adjoint(int B, int T, int H, int DK, int DV, int chunk, int dtype,
+                               const void *q, const void *log_f, const void *dy,
+                               const float *dht, void *adjoints, float *dh0, void *stream);
+
+/*
+ * hgrn2_bwd_chunk: dq, dk, dv and dlog_f of every chunk, all chunks in
+ * parallel, from the chunk-boundary states (states, as for hgrn2_fwd_chunk)
+ * and the adjoints that hgrn2_bwd_adjoint wrote.  Outputs as for hgrn2_bwd.
+ */
+hgrn2_status hgrn2_bwd_chunk(int B, int T, int H, int DK, int DV, int chunk, int dtype,
+                             const void *q, const void *k, const void *v, const void *log_f,
+                             const void *states, const void *adjoints, const void *dy, void *dq,
+                             void *dk, void *dv, void *dlog_f, void *stream);
 
 /*
  * One recurrent decode step (HGRN2 summary §1, recurrent inference): for every

@@ -58,6 +58,12 @@ def _lib():
         lib.hgrn2_fwd.restype = I
         lib.hgrn2_bwd.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
         lib.hgrn2_bwd.restype = I
+        lib.hgrn2_fwd_chunk.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P]
+        lib.hgrn2_fwd_chunk.restype = I
+        lib.hgrn2_bwd_adjoint.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P]
+        lib.hgrn2_bwd_adjoint.restype = I
+        lib.hgrn2_bwd_chunk.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P]
+        lib.hgrn2_bwd_chunk.restype = I
         lib.hgrn2_decode_step.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P]
         lib.hgrn2_decode_step.restype = I
         _handle = lib
@@ -108,13 +114,13 @@ def states_shape(B, T, H, D, chunk):
     return (B, H, num_chunks(T, chunk) + 1, D, D)
 
 
-def fwd(q, k, v, log_f, h0=None, *, chunk=64, want_ht=True, want_states=False,
+def fwd(q, k, v, log_f, h0=None, *, chunk=64, want_ht=True, want_states=False, want_y=True,
         y=None, ht=None, states=None, ws=None):
-    """Chunked forward.  Returns (y, ht or None, states or None).
+    """Chunked forward.  Returns (y or None, ht or None, states or None).
 
     Without `states` the chunk-boundary states go to a workspace (`ws`, a
     uint8 CUDA tensor of at least hgrn2_fwd_workspace_bytes, allocated here
-    if not given)."""
+    if not given).  want_y=False runs the state scan alone (no y)."""
     B, T, H, D = q.shape
     dt = q.dtype
     if dt not in _DT:
@@ -122,9 +128,10 @@ def fwd(q, k, v, log_f, h0=None, *, chunk=64, want_ht=True, want_states=False,
     for n, t in (("q", q), ("k", k), ("v", v), ("log_f", log_f)):
         _tok(n, t, B, T, H, D, dt)
     _st("h0", h0, B, H, D)
-    if y is None:
+    if want_y and y is None:
         y = torch.empty_like(q)
-    _tok("y", y, B, T, H, D, dt)
+    if y is not None:
+        _tok("y", y, B, T, H, D, dt)
     if want_ht and ht is None:
         ht = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
     _st("ht", ht, B, H, D)
@@ -175,6 +182,79 @@ def bwd(q, k, v, log_f, dy, h0=None, dht=None, states=None, *, chunk=64, want_dh
                           _ptr(dv), _ptr(dlog_f), _ptr(dh0), _ptr(ws), ws_bytes, _stream())
     _check(st, "hgrn2_bwd")
     return dq, dk, dv, dlog_f, dh0
+
+
+def _states_ok(states, B, T, H, D, chunk, dt):
+    if (states is None or tuple(states.shape) != states_shape(B, T, H, D, chunk) or states.dtype != dt
+            or not states.is_contiguous()):
+        raise ValueError("states: expected a contiguous %s tensor of shape %s"
+                         % (dt, states_shape(B, T, H, D, chunk)))
+
+
+def adjoints_shape(B, T, H, D, chunk):
+    return (B, H, num_chunks(T, chunk), D, D)
+
+
+def fwd_chunk(q, k, v, log_f, states, *, chunk=64, y=None):
+    """The per-chunk output launch of hgrn2_fwd alone (states from
+    fwd(..., want_states=True) or fwd with y computed elsewhere).  Returns y."""
+    B, T, H, D = q.shape
+    dt = q.dtype
+    for n, t in (("q", q), ("k", k), ("v", v), ("log_f", log_f)):
+        _tok(n, t, B, T, H, D, dt)
+    _states_ok(states, B, T, H, D, chunk, dt)
+    y = torch.empty_like(q) if y is None else y
+    _tok("y", y, B, T, H, D, dt)
+    st = _lib().hgrn2_fwd_chunk(B, T, H, D, D, chunk, _DT[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(log_f),
+                                _ptr(states), _ptr(y), _stream())
+    _check(st, "hgrn2_fwd_chunk")
+    return y
+
+
+def bwd_adjoint(q, log_f, dy, dht=None, *, chunk=64, adjoints=None, dh0=None, want_dh0=False):
+    """The reverse adjoint scan of hgrn2_bwd alone.  Returns (adjoints, dh0 or None)."""
+    B, T, H, D = q.shape
+    dt = q.dtype
+    for n, t in (("q", q), ("log_f", log_f), ("dy", dy)):
+        _tok(n, t, B, T, H, D, dt)
+    _st("dht", dht, B, H, D)
+    if adjoints is None:
+        adjoints = torch.empty(adjoints_shape(B, T, H, D, chunk), dtype=dt, device=q.device)
+    if tuple(adjoints.shape) != adjoints_shape(B, T, H, D, chunk) or adjoints.dtype != dt \
+            or not adjoints.is_contiguous():
+        raise ValueError("adjoints: expected a contiguous %s tensor of shape %s"
+                         % (dt, adjoints_shape(B, T, H, D, chunk)))
+    if want_dh0 and dh0 is None:
+        dh0 = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+    _st("dh0", dh0, B, H, D)
+    st = _lib().hgrn2_bwd_adjoint(B, T, H, D, D, chunk, _DT[dt], _ptr(q), _ptr(log_f), _ptr(dy), _ptr(dht),
+                                  _ptr(adjoints), _ptr(dh0), _stream())
+    _check(st, "hgrn2_bwd_adjoint")
+    return adjoints, dh0
+
+
+def bwd_chunk(q, k, v, log_f, dy, states, adjoints, *, chunk=64, dq=None, dk=None, dv=None, dlog_f=None):
+    """The per-chunk gradient launch of hgrn2_bwd alone.  Returns (dq, dk, dv, dlog_f)."""
+    B, T, H, D = q.shape
+    dt = q.dtype
+    for n, t in (("q", q), ("k", k), ("v", v), ("log_f", log_f), ("dy", dy)):
+        _tok(n, t, B, T, H, D, dt)
+    _states_ok(states, B, T, H, D, chunk, dt)
+    if tuple(adjoints.shape) != adjoints_shape(B, T, H, D, chunk) or adjoints.dtype != dt \
+            or not adjoints.is_contiguous():
+        raise ValueError("adjoints: expected a contiguous %s tensor of shape %s"
+                         % (dt, adjoints_shape(B, T, H, D, chunk)))
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    dlog_f = torch.empty_like(log_f) if dlog_f is None else dlog_f
+    for n, t in (("dq", dq), ("dk", dk), ("dv", dv), ("dlog_f", dlog_f)):
+        _tok(n, t, B, T, H, D, dt)
+    st = _lib().hgrn2_bwd_chunk(B, T, H, D, D, chunk, _DT[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(log_f),
+                                _ptr(states), _ptr(adjoints), _ptr(dy), _ptr(dq), _ptr(dk), _ptr(dv),
+                                _ptr(dlog_f), _stream())
+    _check(st, "hgrn2_bwd_chunk")
+    return dq, dk, dv, dlog_f
 
 
 def decode_step(q, k, v, log_f, state, *, y=None):

@@ -104,6 +104,64 @@ size_t adjoint_bytes(int B, int T, int H, int DK, int DV, int chunk, int dtype) 
   return (size_t)B * H * (size_t)((T + chunk - 1) / chunk) * DK * DV * dsize(dtype);
 }
 
+
+hgrn2_status launch_scan(int dtype, int D, int chunk, bool reverse, int B, int T, int H, const void *x,
+                         const void *z, const void *log_f, const float *s_in, void *states, float *s_out,
+                         void *stream, const char *what) {
+  hgrn2::ScanArgs sa;
+  sa.B = B;
+  sa.T = T;
+  sa.H = H;
+  sa.N = (T + chunk - 1) / chunk;
+  sa.x = x;
+  sa.z = z;
+  sa.log_f = log_f;
+  sa.s_in = s_in;
+  sa.states = states;
+  sa.s_out = s_out;
+  return hip_status(hgrn2::dispatch_scan(dtype, D, chunk, reverse, &sa, (hipStream_t)stream), what);
+}
+
+hgrn2_status launch_chunk_fwd(int dtype, int D, int chunk, int B, int T, int H, const void *q, const void *k,
+                              const void *v, const void *log_f, const void *states, void *y, void *stream,
+                              const char *what) {
+  hgrn2::ChunkFwdArgs ca;
+  ca.B = B;
+  ca.T = T;
+  ca.H = H;
+  ca.N = (T + chunk - 1) / chunk;
+  ca.q = q;
+  ca.k = k;
+  ca.v = v;
+  ca.log_f = log_f;
+  ca.states = states;
+  ca.y = y;
+  return hip_status(hgrn2::dispatch_chunk_fwd(dtype, D, chunk, &ca, (hipStream_t)stream), what);
+}
+
+hgrn2_status launch_chunk_bwd(int dtype, int D, int chunk, int B, int T, int H, const void *q, const void *k,
+                              const void *v, const void *log_f, const void *dy, const void *states,
+                              const void *lam, void *dq, void *dk, void *dv, void *dlog_f, void *stream,
+                              const char *what) {
+  hgrn2::ChunkBwdArgs a;
+  a.B = B;
+  a.T = T;
+  a.H = H;
+  a.N = (T + chunk - 1) / chunk;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.log_f = log_f;
+  a.dy = dy;
+  a.states = states;
+  a.lam = lam;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dlog_f = dlog_f;
+  return hip_status(hgrn2::dispatch_chunk_bwd(dtype, D, chunk, &a, (hipStream_t)stream), what);
+}
+
 }  // namespace
 
 extern "C" {
@@ -181,34 +239,11 @@ hgrn2_status hgrn2_fwd(int B, int T, int H, int DK, int DV, int chunk, int dtype
                          overlap(Range{"states", states, stb}, Range{"h0", h0, sb})))
     return fail(HGRN2_ERR_INVALID_ARG, "an output overlaps h0");
 
-  const int N = hgrn2_num_chunks(T, chunk);
-  hgrn2::ScanArgs sa;
-  sa.B = B;
-  sa.T = T;
-  sa.H = H;
-  sa.N = N;
-  sa.x = k;
-  sa.z = v;
-  sa.log_f = log_f;
-  sa.s_in = h0;
-  sa.states = states;
-  sa.s_out = ht;
-  st = hip_status(hgrn2::dispatch_scan(dtype, DK, chunk, false, &sa, (hipStream_t)stream),
-                  "hgrn2_fwd (state scan)");
+  st = launch_scan(dtype, DK, chunk, false, B, T, H, k, v, log_f, h0, states, ht, stream,
+                   "hgrn2_fwd (state scan)");
   if (st != HGRN2_OK || !y) return st;
-  hgrn2::ChunkFwdArgs ca;
-  ca.B = B;
-  ca.T = T;
-  ca.H = H;
-  ca.N = N;
-  ca.q = q;
-  ca.k = k;
-  ca.v = v;
-  ca.log_f = log_f;
-  ca.states = states;
-  ca.y = y;
-  return hip_status(hgrn2::dispatch_chunk_fwd(dtype, DK, chunk, &ca, (hipStream_t)stream),
-                    "hgrn2_fwd (chunk outputs)");
+  return launch_chunk_fwd(dtype, DK, chunk, B, T, H, q, k, v, log_f, states, y, stream,
+                          "hgrn2_fwd (chunk outputs)");
 }
 
 hgrn2_status hgrn2_bwd(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
@@ -239,58 +274,83 @@ hgrn2_status hgrn2_bwd(int B, int T, int H, int DK, int DV, int chunk, int dtype
   std::string msg;
   if (!check_aliasing(ins, 8, outs, 6, msg)) return fail(HGRN2_ERR_INVALID_ARG, msg);
 
-  const int N = hgrn2_num_chunks(T, chunk);
   if (!states) {
     // recompute the chunk-boundary states with the forward state scan
     void *sws = (char *)ws + lamb;
-    hgrn2::ScanArgs sa;
-    sa.B = B;
-    sa.T = T;
-    sa.H = H;
-    sa.N = N;
-    sa.x = k;
-    sa.z = v;
-    sa.log_f = log_f;
-    sa.s_in = h0;
-    sa.states = sws;
-    sa.s_out = nullptr;
-    hgrn2_status s1 = hip_status(hgrn2::dispatch_scan(dtype, DK, chunk, false, &sa, (hipStream_t)stream),
-                                 "hgrn2_bwd (state recompute)");
-    if (s1 != HGRN2_OK) return s1;
+    st = launch_scan(dtype, DK, chunk, false, B, T, H, k, v, log_f, h0, sws, nullptr, stream,
+                     "hgrn2_bwd (state recompute)");
+    if (st != HGRN2_OK) return st;
     states = sws;
   }
   // the state adjoint at every chunk end (reverse scan), then all chunks' gradients
-  hgrn2::ScanArgs ra;
-  ra.B = B;
-  ra.T = T;
-  ra.H = H;
-  ra.N = N;
-  ra.x = q;
-  ra.z = dy;
-  ra.log_f = log_f;
-  ra.s_in = dht;
-  ra.states = ws;
-  ra.s_out = dh0;
-  st = hip_status(hgrn2::dispatch_scan(dtype, DK, chunk, true, &ra, (hipStream_t)stream),
-                  "hgrn2_bwd (adjoint scan)");
+  st = launch_scan(dtype, DK, chunk, true, B, T, H, q, dy, log_f, dht, ws, dh0, stream,
+                   "hgrn2_bwd (adjoint scan)");
   if (st != HGRN2_OK) return st;
-  hgrn2::ChunkBwdArgs a;
-  a.B = B;
-  a.T = T;
-  a.H = H;
-  a.N = N;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.log_f = log_f;
-  a.dy = dy;
-  a.states = states;
-  a.lam = ws;
-  a.dq = dq;
-  a.dk = dk;
-  a.dv = dv;
-  a.dlog_f = dlog_f;
-  return hip_status(hgrn2::dispatch_chunk_bwd(dtype, DK, chunk, &a, (hipStream_t)stream), "hgrn2_bwd (chunk gradients)");
+  return launch_chunk_bwd(dtype, DK, chunk, B, T, H, q, k, v, log_f, dy, states, ws, dq, dk, dv, dlog_f,
+                          stream, "hgrn2_bwd (chunk gradients)");
+}
+
+hgrn2_status hgrn2_fwd_chunk(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
+                             const void *k, const void *v, const void *log_f, const void *states, void *y,
+                             void *stream) {
+  hgrn2_status st = check_common(B, T, H, DK, DV, chunk, dtype);
+  if (st != HGRN2_OK) return st;
+  st = check_ptrs({{"q", q}, {"k", k}, {"v", v}, {"log_f", log_f}, {"states", states}, {"y", y}}, {});
+  if (st != HGRN2_OK) return st;
+  if (hgrn2::dispatch_chunk_fwd(dtype, DK, chunk, nullptr, nullptr) != hipSuccess)
+    return fail(HGRN2_ERR_UNSUPPORTED, "no forward kernel for this D, chunk and dtype");
+  const size_t tok = (size_t)B * T * H * DK * dsize(dtype);
+  const size_t stb = hgrn2_states_bytes(B, T, H, DK, DV, chunk, dtype);
+  const Range ins[] = {{"q", q, tok}, {"k", k, tok}, {"v", v, tok}, {"log_f", log_f, tok}, {"states", states, stb}};
+  const Range outs[] = {{"y", y, tok}};
+  std::string msg;
+  if (!check_aliasing(ins, 5, outs, 1, msg)) return fail(HGRN2_ERR_INVALID_ARG, msg);
+  return launch_chunk_fwd(dtype, DK, chunk, B, T, H, q, k, v, log_f, states, y, stream, "hgrn2_fwd_chunk");
+}
+
+hgrn2_status hgrn2_bwd_adjoint(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
+                               const void *log_f, const void *dy, const float *dht, void *adjoints, float *dh0,
+                               void *stream) {
+  hgrn2_status st = check_common(B, T, H, DK, DV, chunk, dtype);
+  if (st != HGRN2_OK) return st;
+  st = check_ptrs({{"q", q}, {"log_f", log_f}, {"dy", dy}, {"adjoints", adjoints}}, {{"dht", dht}, {"dh0", dh0}});
+  if (st != HGRN2_OK) return st;
+  if (hgrn2::dispatch_scan(dtype, DK, chunk, true, nullptr, nullptr) != hipSuccess)
+    return fail(HGRN2_ERR_UNSUPPORTED, "no adjoint scan kernel for this D, chunk and dtype");
+  const size_t tok = (size_t)B * T * H * DK * dsize(dtype);
+  const size_t sb = (size_t)B * H * DK * DV * sizeof(float);
+  const size_t lamb = adjoint_bytes(B, T, H, DK, DV, chunk, dtype);
+  const Range ins[] = {{"q", q, tok}, {"log_f", log_f, tok}, {"dy", dy, tok}, {"dht", dht, sb}};
+  const Range outs[] = {{"adjoints", adjoints, lamb}, {"dh0", dh0, sb}};
+  std::string msg;
+  if (!check_aliasing(ins, 4, outs, 2, msg)) return fail(HGRN2_ERR_INVALID_ARG, msg);
+  return launch_scan(dtype, DK, chunk, true, B, T, H, q, dy, log_f, dht, adjoints, dh0, stream,
+                     "hgrn2_bwd_adjoint");
+}
+
+hgrn2_status hgrn2_bwd_chunk(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
+                             const void *k, const void *v, const void *log_f, const void *states,
+                             const void *adjoints, const void *dy, void *dq, void *dk, void *dv, void *dlog_f,
+                             void *stream) {
+  hgrn2_status st = check_common(B, T, H, DK, DV, chunk, dtype);
+  if (st != HGRN2_OK) return st;
+  st = check_ptrs({{"q", q}, {"k", k}, {"v", v}, {"log_f", log_f}, {"states", states}, {"adjoints", adjoints},
+                   {"dy", dy}, {"dq", dq}, {"dk", dk}, {"dv", dv}, {"dlog_f", dlog_f}},
+                  {});
+  if (st != HGRN2_OK) return st;
+  if (!bwd_exists(dtype, DK, chunk))
+    return fail(HGRN2_ERR_UNSUPPORTED, "no backward kernel for this D, chunk and dtype");
+  const size_t tok = (size_t)B * T * H * DK * dsize(dtype);
+  const size_t stb = hgrn2_states_bytes(B, T, H, DK, DV, chunk, dtype);
+  const size_t lamb = adjoint_bytes(B, T, H, DK, DV, chunk, dtype);
+  const Range ins[] = {{"q", q, tok},           {"k", k, tok},   {"v", v, tok},
+                       {"log_f", log_f, tok},   {"dy", dy, tok}, {"states", states, stb},
+                       {"adjoints", adjoints, lamb}};
+  const Range outs[] = {{"dq", dq, tok}, {"dk", dk, tok}, {"dv", dv, tok}, {"dlog_f", dlog_f, tok}};
+  std::string msg;
+  if (!check_aliasing(ins, 7, outs, 4, msg)) return fail(HGRN2_ERR_INVALID_ARG, msg);
+  return launch_chunk_bwd(dtype, DK, chunk, B, T, H, q, k, v, log_f, dy, states, adjoints, dq, dk, dv, dlog_f,
+                          stream, "hgrn2_bwd_chunk");
 }
 
 hgrn2_status hgrn2_decode_step(int B, int H, int DK, int DV, int dtype, const void *q, const void *k,

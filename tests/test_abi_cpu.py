@@ -25,7 +25,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("hgrn2_fwd", "hgrn2_bwd", "hgrn2_decode_step"):
+    for n in ("hgrn2_fwd", "hgrn2_bwd", "hgrn2_decode_step", "hgrn2_fwd_chunk", "hgrn2_bwd_adjoint",
+              "hgrn2_bwd_chunk"):
         assert n in names
 
 
@@ -35,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.hgrn2_abi_version() == 2
+    assert lib.hgrn2_abi_version() == 3
     for s in range(5):
         assert lib.hgrn2_status_string(s).startswith(b"HGRN2_")
 
@@ -107,6 +108,27 @@ def test_bwd_rejections(lib):
     r = lib.hgrn2_bwd(1, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], P[3], None, P[9], P[4], None,
                       P[5], P[6], P[7], P[8], None, P[8], need, None)
     assert r == 1
+
+
+def test_staged_rejections(lib):
+    P = [FAKE + i * 0x100000 for i in range(14)]
+    # hgrn2_fwd_chunk: y aliases q; states NULL; unsupported D; good arguments never reach here
+    assert lib.hgrn2_fwd_chunk(1, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], P[3], P[4], P[0], None) == 1
+    assert lib.hgrn2_fwd_chunk(1, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], P[3], None, P[5], None) == 1
+    assert lib.hgrn2_fwd_chunk(1, 10, 1, 48, 48, 16, 0, P[0], P[1], P[2], P[3], P[4], P[5], None) == 2
+    assert lib.hgrn2_fwd_chunk(1, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], P[3], P[4] + 8, P[5], None) == 1
+    # hgrn2_bwd_adjoint: adjoints NULL; adjoints overlap dy; dh0 overlaps adjoints
+    assert lib.hgrn2_bwd_adjoint(1, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], None, None, None, None) == 1
+    assert lib.hgrn2_bwd_adjoint(1, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], None, P[2], None, None) == 1
+    assert lib.hgrn2_bwd_adjoint(1, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], None, P[3], P[3], None) == 1
+    assert lib.hgrn2_bwd_adjoint(1, 10, 1, 16, 16, 24, 0, P[0], P[1], P[2], None, P[3], None, None) == 2
+    # hgrn2_bwd_chunk: dv aliases the adjoints; dlog_f NULL
+    assert lib.hgrn2_bwd_chunk(1, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7],
+                               P[8], P[5], P[10], None) == 1
+    assert lib.hgrn2_bwd_chunk(1, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7],
+                               P[8], P[9], None, None) == 1
+    assert lib.hgrn2_bwd_chunk(0, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7],
+                               P[8], P[9], P[10], None) == 1
 
 
 def test_decode_rejections(lib):

@@ -166,3 +166,33 @@ def test_decode(dtype, D):
     es = np.linalg.norm(to_host64(S) - Sr) / np.linalg.norm(Sr)
     print("decode D=%d %s: y %.3e state %.3e" % (D, dtype, ey, es), flush=True)
     assert ey <= TOL[dtype] and es <= 1e-5
+
+
+# ------------------------------------------------------------ staged launches
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_staged_launches_equal_composite_calls(dtype):
+    """hgrn2_fwd_chunk, hgrn2_bwd_adjoint and hgrn2_bwd_chunk run the kernels
+    hgrn2_fwd / hgrn2_bwd are made of, in the same order on the same inputs,
+    so their results are bit-for-bit those of the composite calls (which the
+    other tests hold to the oracle)."""
+    m = _hip()
+    import torch
+    d = _case(dtype, B=2, T=3 * 64 + 11, H=3, D=64, lam=0.3, h0std=0.5, qscale=1.0)
+    C = 64
+    q, k, v, lf, dy = (to_dev(d[n], dtype) for n in ("q", "k", "v", "log_f", "dy"))
+    h0 = to_dev(d["h0"], "f32")
+    rng = np.random.default_rng(d["seed"] + 99)
+    dht = to_dev((rng.standard_normal(tuple(h0.shape)) * 0.5).astype(np.float32), "f32")
+    y, ht, states = m.fwd(q, k, v, lf, h0, chunk=C, want_states=True)
+    dq, dk, dv, dl, dh0 = m.bwd(q, k, v, lf, dy, h0, dht, states, chunk=C)
+    _, ht2, states2 = m.fwd(q, k, v, lf, h0, chunk=C, want_states=True, y=torch.empty_like(y))
+    y2 = m.fwd_chunk(q, k, v, lf, states2, chunk=C)
+    lam, dh02 = m.bwd_adjoint(q, lf, dy, dht, chunk=C, want_dh0=True)
+    g2 = m.bwd_chunk(q, k, v, lf, dy, states2, lam, chunk=C)
+    torch.cuda.synchronize()
+    assert torch.equal(states, states2) and torch.equal(ht, ht2)
+    assert torch.equal(y, y2)
+    assert torch.equal(dh0, dh02)
+    for a, b in zip((dq, dk, dv, dl), g2):
+        assert torch.equal(a, b)
