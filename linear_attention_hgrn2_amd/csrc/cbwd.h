@@ -77,7 +77,7 @@ template <typename T, int D, int C> struct CbwdCfg {
 };
 
 template <typename T, int D, int C>
-__global__ __launch_bounds__(4 * C) void hgrn2_chunk_bwd_kernel(ChunkBwdArgs a) {
+__global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void hgrn2_chunk_bwd_kernel(ChunkBwdArgs a) {
   using Cfg = CbwdCfg<T, D, C>;
   constexpr int NW = Cfg::NW, NT = Cfg::NT, NB = Cfg::NB, CPL = Cfg::CPL, CB = Cfg::CB, KSD = Cfg::KSD,
                 EPV = Cfg::EPV, LDG = Cfg::LDG;
@@ -93,35 +93,33 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_bwd_kernel(ChunkBwdArgs a) 
   const bool has_ch = lane < Cfg::LANES;
   const int c0 = (has_ch ? lane : 0) * CPL;
 
-  const T *gq = (const T *)a.q;
-  const T *gk = (const T *)a.k;
-  const T *gv = (const T *)a.v;
-  const T *gl = (const T *)a.log_f;
-  const T *gdy = (const T *)a.dy;
-  const T *gS = (const T *)a.states + ((size_t)bh * (N + 1) + n) * D * D;
-  const T *gL = (const T *)a.lam + ((size_t)bh * N + n) * D * D;
-  T *gdq = (T *)a.dq;
-  T *gdk = (T *)a.dk;
-  T *gdv = (T *)a.dv;
-  T *gdl = (T *)a.dlog_f;
-  // chunk-uniform base pointers; per-lane 32-bit element offsets within the chunk
-  const size_t cbase = (((size_t)b * T_ + t0) * H + h) * D;
-  const uint32_t HD = (uint32_t)H * D;
-  gq += cbase;
-  gk += cbase;
-  gv += cbase;
-  gl += cbase;
-  gdy += cbase;
-  gdq += cbase;
-  gdk += cbase;
-  gdv += cbase;
-  gdl += cbase;
-  auto tok = [&](int t) { return (uint32_t)t * HD; };  // token t of the chunk
-  auto ldtok = [&](const T *base, int t) {  // this lane's CPL elements of token t of the chunk (0 past the end)
-    Pack<T, CPL> p;
+  // chunk-uniform byte bases; every per-lane offset is a 32-bit byte offset from one of them
+  const size_t cbase = (((size_t)b * T_ + t0) * H + h) * D * sizeof(T);
+  const char *gq = (const char *)a.q + cbase;
+  const char *gk = (const char *)a.k + cbase;
+  const char *gv = (const char *)a.v + cbase;
+  const char *gl = (const char *)a.log_f + cbase;
+  const char *gdy = (const char *)a.dy + cbase;
+  const char *gS = (const char *)a.states + ((size_t)bh * (N + 1) + n) * D * D * sizeof(T);
+  const char *gL = (const char *)a.lam + ((size_t)bh * N + n) * D * D * sizeof(T);
+  char *gdq = (char *)a.dq + cbase;
+  char *gdk = (char *)a.dk + cbase;
+  char *gdv = (char *)a.dv + cbase;
+  char *gdl = (char *)a.dlog_f + cbase;
+  const uint32_t HDB = (uint32_t)H * D * sizeof(T);
+  const uint32_t c0b = (uint32_t)c0 * sizeof(T);
+  auto tok = [&](int t) { return (uint32_t)t * HDB; };  // byte offset of token t of the chunk
+  auto gp_ = [](const char *base, uint32_t off) { return (const T *)(base + off); };
+  auto gw_ = [](char *base, uint32_t off) { return (T *)(base + off); };
+  // this lane's CPL elements of token t of the chunk (0 past the end); the load
+  // itself is unconditional, from a clamped token, so it never blocks the
+  // compiler's tracking of loads in flight
+  auto ldtok = [&](const char *base, int t) {
+    Pack<T, CPL> p = ldpack<T, CPL>(gp_(base, tok(min(t, len - 1)) + c0b));
+    if (!(t < len && has_ch)) {
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) p.v[e] = from_f32<T>(0.f);
-    if (t < len && has_ch) p = ldpack<T, CPL>(base + (tok(t) + c0));
+      for (int e = 0; e < CPL; ++e) p.v[e] = from_f32<T>(0.f);
+    }
     return p;
   };
 
@@ -130,11 +128,9 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_bwd_kernel(ChunkBwdArgs a) 
   for (int i = 0; i < Cfg::NVT; ++i) {
     const int idx = tid + i * NT;
     const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
-    uint4 x = make_uint4(0, 0, 0, 0), y = x;
-    if (idx < Cfg::VT && row < len) {
-      x = *(const uint4 *)(gv + (tok(row) + col));
-      y = *(const uint4 *)(gdy + (tok(row) + col));
-    }
+    const uint32_t off = tok(min(row, len - 1)) + (uint32_t)col * sizeof(T);
+    uint4 x = *(const uint4 *)(gv + off), y = *(const uint4 *)(gdy + off);
+    if (row >= len) x = y = make_uint4(0, 0, 0, 0);
     if (idx < Cfg::VT) {
       *(uint4 *)&sm.u.in.v[XT::at(row, col)] = x;
       *(uint4 *)&sm.u.in.dy[XT::at(row, col)] = y;
@@ -309,15 +305,15 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_bwd_kernel(ChunkBwdArgs a) 
           ex[e] = 0.f;
         }
         if (tv_) {
-          const Pack<T, CPL> p = ldpack<T, CPL>(gq + (tok(16 * w + t) + c0));
+          const Pack<T, CPL> p = ldpack<T, CPL>(gp_(gq, tok(16 * w + t) + c0b));
 #pragma unroll
           for (int e = 0; e < CPL; ++e) qt[e] = to_f32(p.v[e]);
         }
         for (int s = t; s >= 0; --s) {
           float part = 0.f;
           if (tv_) {
-            const Pack<T, CPL> pk = ldpack<T, CPL>(gk + (tok(16 * w + s) + c0));
-            const Pack<T, CPL> pl = ldpack<T, CPL>(gl + (tok(16 * w + s) + c0));
+            const Pack<T, CPL> pk = ldpack<T, CPL>(gp_(gk, tok(16 * w + s) + c0b));
+            const Pack<T, CPL> pl = ldpack<T, CPL>(gp_(gl, tok(16 * w + s) + c0b));
 #pragma unroll
             for (int e = 0; e < CPL; ++e) {
               part += qt[e] * to_f32(pk.v[e]) * __expf(ex[e]);
@@ -369,8 +365,9 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_bwd_kernel(ChunkBwdArgs a) 
     const int idx = tid + i * NT;
     const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
     if (idx < Cfg::VS) {
-      *(uint4 *)&sS[XT::at(row, col)] = *(const uint4 *)(gS + (size_t)row * D + col);
-      *(uint4 *)&sL[XT::at(row, col)] = *(const uint4 *)(gL + (size_t)row * D + col);
+      const uint32_t off = (uint32_t)(row * D + col) * sizeof(T);
+      *(uint4 *)&sS[XT::at(row, col)] = *(const uint4 *)(gS + off);
+      *(uint4 *)&sL[XT::at(row, col)] = *(const uint4 *)(gL + off);
     }
     if (i % 4 == 3) asm volatile("" ::: "memory");  // bounds the loads in flight
   }
@@ -439,7 +436,7 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_bwd_kernel(ChunkBwdArgs a) 
     const int idx = lane + 64 * i;
     const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
     const int t = 16 * w + row;
-    if (idx < RV && t < len) *(uint4 *)(gdv + (tok(t) + col)) = *(const uint4 *)&dvs[XT::at(t, col)];
+    if (idx < RV && t < len) *(uint4 *)(gdv + (tok(t) + (uint32_t)col * sizeof(T))) = *(const uint4 *)&dvs[XT::at(t, col)];
   }
   __syncthreads();  // B5: the dv staging is dead
 
@@ -496,8 +493,8 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_bwd_kernel(ChunkBwdArgs a) 
         X[t][e] = qor * d1 - kor * d2;
       }
       if (tt < len && has_ch) {
-        stpack<T, CPL>(gdq + (tok(tt) + c0), oq);
-        stpack<T, CPL>(gdk + (tok(tt) + c0), ok);
+        stpack<T, CPL>(gw_(gdq, tok(tt) + c0b), oq);
+        stpack<T, CPL>(gw_(gdk, tok(tt) + c0b), ok);
       }
     }
     if (has_ch) {
@@ -573,8 +570,8 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_bwd_kernel(ChunkBwdArgs a) 
         tot[e] += x;
       }
       if (tt < len && has_ch) {
-        stpack<T, CPL>(gdq + (tok(tt) + c0), oq);
-        stpack<T, CPL>(gdk + (tok(tt) + c0), ok);
+        stpack<T, CPL>(gw_(gdq, tok(tt) + c0b), oq);
+        stpack<T, CPL>(gw_(gdk, tok(tt) + c0b), ok);
       }
     }
     if (has_ch)
@@ -601,7 +598,7 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_bwd_kernel(ChunkBwdArgs a) 
           carry[e] += X[t][e];
           o.v[e] = from_f32<T>(carry[e]);
         }
-        if (tt < len) stpack<T, CPL>(gdl + (tok(tt) + c0), o);
+        if (tt < len) stpack<T, CPL>(gw_(gdl, tok(tt) + c0b), o);
       }
     } else {
       for (int t = 15; t >= 0; --t) {
@@ -612,7 +609,7 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_bwd_kernel(ChunkBwdArgs a) 
           carry[e] += sq[t * LDG + c0 + e];
           o.v[e] = from_f32<T>(carry[e]);
         }
-        if (tt < len) stpack<T, CPL>(gdl + (tok(tt) + c0), o);
+        if (tt < len) stpack<T, CPL>(gw_(gdl, tok(tt) + c0b), o);
       }
     }
   }
