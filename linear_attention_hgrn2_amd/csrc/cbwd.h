@@ -93,30 +93,25 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
   const bool has_ch = lane < Cfg::LANES;
   const int c0 = (has_ch ? lane : 0) * CPL;
 
-  // chunk-uniform byte bases; every per-lane offset is a 32-bit byte offset from one of them
+  // buffer windows over this chunk's rows: offsets are 32-bit byte offsets
+  // from the chunk's first row; rows past the end of the sequence read as zero
+  // and their stores are dropped
   const size_t cbase = (((size_t)b * T_ + t0) * H + h) * D * sizeof(T);
-  const char *gq = (const char *)a.q + cbase;
-  const char *gk = (const char *)a.k + cbase;
-  const char *gv = (const char *)a.v + cbase;
-  const char *gl = (const char *)a.log_f + cbase;
-  const char *gdy = (const char *)a.dy + cbase;
-  const char *gS = (const char *)a.states + ((size_t)bh * (N + 1) + n) * D * D * sizeof(T);
-  const char *gL = (const char *)a.lam + ((size_t)bh * N + n) * D * D * sizeof(T);
-  char *gdq = (char *)a.dq + cbase;
-  char *gdk = (char *)a.dk + cbase;
-  char *gdv = (char *)a.dv + cbase;
-  char *gdl = (char *)a.dlog_f + cbase;
   const uint32_t HDB = (uint32_t)H * D * sizeof(T);
+  const uint32_t rows = (uint32_t)len * HDB;
+  const GBuf bq((const char *)a.q + cbase, rows), bk((const char *)a.k + cbase, rows);
+  const GBuf bv((const char *)a.v + cbase, rows), bl((const char *)a.log_f + cbase, rows);
+  const GBuf bdy((const char *)a.dy + cbase, rows);
+  const GBuf bdq((char *)a.dq + cbase, rows), bdk((char *)a.dk + cbase, rows);
+  const GBuf bdv((char *)a.dv + cbase, rows), bdl((char *)a.dlog_f + cbase, rows);
+  const GBuf bS((const char *)a.states + ((size_t)bh * (N + 1) + n) * D * D * sizeof(T), D * D * sizeof(T));
+  const GBuf bL((const char *)a.lam + ((size_t)bh * N + n) * D * D * sizeof(T), D * D * sizeof(T));
   const uint32_t c0b = (uint32_t)c0 * sizeof(T);
   auto tok = [&](int t) { return (uint32_t)t * HDB; };  // byte offset of token t of the chunk
-  auto gp_ = [](const char *base, uint32_t off) { return (const T *)(base + off); };
-  auto gw_ = [](char *base, uint32_t off) { return (T *)(base + off); };
-  // this lane's CPL elements of token t of the chunk (0 past the end); the load
-  // itself is unconditional, from a clamped token, so it never blocks the
-  // compiler's tracking of loads in flight
-  auto ldtok = [&](const char *base, int t) {
-    Pack<T, CPL> p = ldpack<T, CPL>(gp_(base, tok(min(t, len - 1)) + c0b));
-    if (!(t < len && has_ch)) {
+  // this lane's CPL elements of token t of the chunk (0 past the end)
+  auto ldtok = [&](const GBuf &buf, int t) {
+    Pack<T, CPL> p = buf.template ldpack<T, CPL>(tok(t) + c0b);
+    if (!has_ch) {
 #pragma unroll
       for (int e = 0; e < CPL; ++e) p.v[e] = from_f32<T>(0.f);
     }
@@ -128,9 +123,8 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
   for (int i = 0; i < Cfg::NVT; ++i) {
     const int idx = tid + i * NT;
     const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
-    const uint32_t off = tok(min(row, len - 1)) + (uint32_t)col * sizeof(T);
-    uint4 x = *(const uint4 *)(gv + off), y = *(const uint4 *)(gdy + off);
-    if (row >= len) x = y = make_uint4(0, 0, 0, 0);
+    const uint32_t off = tok(row) + (uint32_t)col * sizeof(T);
+    const uint4 x = bv.ld16(off), y = bdy.ld16(off);
     if (idx < Cfg::VT) {
       *(uint4 *)&sm.u.in.v[XT::at(row, col)] = x;
       *(uint4 *)&sm.u.in.dy[XT::at(row, col)] = y;
@@ -141,9 +135,9 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
     Pack<T, CPL> pq[16], pk[16], pl[16];
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      pq[t] = ldtok(gq, 16 * w + t);
-      pk[t] = ldtok(gk, 16 * w + t);
-      pl[t] = ldtok(gl, 16 * w + t);
+      pq[t] = ldtok(bq, 16 * w + t);
+      pk[t] = ldtok(bk, 16 * w + t);
+      pl[t] = ldtok(bl, 16 * w + t);
     }
     float l[16][CPL], L[CPL];
     block_prefix<T, CPL>(pl, l, L);
@@ -305,15 +299,15 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
           ex[e] = 0.f;
         }
         if (tv_) {
-          const Pack<T, CPL> p = ldpack<T, CPL>(gp_(gq, tok(16 * w + t) + c0b));
+          const Pack<T, CPL> p = bq.template ldpack<T, CPL>(tok(16 * w + t) + c0b);
 #pragma unroll
           for (int e = 0; e < CPL; ++e) qt[e] = to_f32(p.v[e]);
         }
         for (int s = t; s >= 0; --s) {
           float part = 0.f;
           if (tv_) {
-            const Pack<T, CPL> pk = ldpack<T, CPL>(gp_(gk, tok(16 * w + s) + c0b));
-            const Pack<T, CPL> pl = ldpack<T, CPL>(gp_(gl, tok(16 * w + s) + c0b));
+            const Pack<T, CPL> pk = bk.template ldpack<T, CPL>(tok(16 * w + s) + c0b);
+            const Pack<T, CPL> pl = bl.template ldpack<T, CPL>(tok(16 * w + s) + c0b);
 #pragma unroll
             for (int e = 0; e < CPL; ++e) {
               part += qt[e] * to_f32(pk.v[e]) * __expf(ex[e]);
@@ -366,8 +360,8 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
     const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
     if (idx < Cfg::VS) {
       const uint32_t off = (uint32_t)(row * D + col) * sizeof(T);
-      *(uint4 *)&sS[XT::at(row, col)] = *(const uint4 *)(gS + off);
-      *(uint4 *)&sL[XT::at(row, col)] = *(const uint4 *)(gL + off);
+      *(uint4 *)&sS[XT::at(row, col)] = bS.ld16(off);
+      *(uint4 *)&sL[XT::at(row, col)] = bL.ld16(off);
     }
     if (i % 4 == 3) asm volatile("" ::: "memory");  // bounds the loads in flight
   }
@@ -436,7 +430,7 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
     const int idx = lane + 64 * i;
     const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
     const int t = 16 * w + row;
-    if (idx < RV && t < len) *(uint4 *)(gdv + (tok(t) + (uint32_t)col * sizeof(T))) = *(const uint4 *)&dvs[XT::at(t, col)];
+    if (idx < RV) bdv.st16(tok(t) + (uint32_t)col * sizeof(T), *(const uint4 *)&dvs[XT::at(t, col)]);
   }
   __syncthreads();  // B5: the dv staging is dead
 
@@ -472,14 +466,14 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
     for (int e = 0; e < CPL; ++e) L[e] = ell[e] = 0.f;
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      pl[t] = ldtok(gl, 16 * w + t);
+      pl[t] = ldtok(bl, 16 * w + t);
 #pragma unroll
       for (int e = 0; e < CPL; ++e) L[e] += floor_logf(to_f32(pl[t].v[e]));
     }
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       const int tt = 16 * w + t;
-      const Pack<T, CPL> pq = ldtok(gq, tt), pk = ldtok(gk, tt);
+      const Pack<T, CPL> pq = ldtok(bq, tt), pk = ldtok(bk, tt);
       Pack<T, CPL> oq, ok;
 #pragma unroll
       for (int e = 0; e < CPL; ++e) {
@@ -492,9 +486,9 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
         ok.v[e] = from_f32<T>(ek * d2);
         X[t][e] = qor * d1 - kor * d2;
       }
-      if (tt < len && has_ch) {
-        stpack<T, CPL>(gw_(gdq, tok(tt) + c0b), oq);
-        stpack<T, CPL>(gw_(gdk, tok(tt) + c0b), ok);
+      if (has_ch) {
+        bdq.stpack<T, CPL>(tok(tt) + c0b, oq);
+        bdk.stpack<T, CPL>(tok(tt) + c0b, ok);
       }
     }
     if (has_ch) {
@@ -513,14 +507,14 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
     for (int e = 0; e < CPL; ++e) L[e] = ell[e] = tot[e] = 0.f;
     for (int t = 0; t < 16; ++t) {
-      const Pack<T, CPL> p = ldtok(gl, 16 * w + t);
+      const Pack<T, CPL> p = ldtok(bl, 16 * w + t);
 #pragma unroll
       for (int e = 0; e < CPL; ++e) L[e] += floor_logf(to_f32(p.v[e]));
     }
     for (int t = 0; t < 16; ++t) {
       const int tt = 16 * w + t;
-      const Pack<T, CPL> pq = ldtok(gq, tt), pk = ldtok(gk, tt), plt = ldtok(gl, tt);
-      const Pack<T, CPL> pdy = ldtok(gdy, tt), pv = ldtok(gv, tt);
+      const Pack<T, CPL> pq = ldtok(bq, tt), pk = ldtok(bk, tt), plt = ldtok(bl, tt);
+      const Pack<T, CPL> pdy = ldtok(bdy, tt), pv = ldtok(bv, tt);
       float dqd[CPL], dkd[CPL], ex[CPL];
 #pragma unroll
       for (int e = 0; e < CPL; ++e) {
@@ -528,8 +522,8 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
         dqd[e] = dkd[e] = ex[e] = 0.f;
       }
       for (int s_ = t; s_ >= 0; --s_) {
-        const Pack<T, CPL> pvs = ldtok(gv, 16 * w + s_), pks = ldtok(gk, 16 * w + s_);
-        const Pack<T, CPL> pls = ldtok(gl, 16 * w + s_);
+        const Pack<T, CPL> pvs = ldtok(bv, 16 * w + s_), pks = ldtok(bk, 16 * w + s_);
+        const Pack<T, CPL> pls = ldtok(bl, 16 * w + s_);
         float part = 0.f;
 #pragma unroll
         for (int e = 0; e < CPL; ++e) part += to_f32(pdy.v[e]) * to_f32(pvs.v[e]);
@@ -543,13 +537,13 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
       for (int e = 0; e < CPL; ++e) ex[e] = 0.f;
       for (int u = t; u < 16; ++u) {
-        const Pack<T, CPL> pdu = ldtok(gdy, 16 * w + u), pqu = ldtok(gq, 16 * w + u);
+        const Pack<T, CPL> pdu = ldtok(bdy, 16 * w + u), pqu = ldtok(bq, 16 * w + u);
         float part = 0.f;
 #pragma unroll
         for (int e = 0; e < CPL; ++e) part += to_f32(pdu.v[e]) * to_f32(pv.v[e]);
         const float dA = wave_sum(part);
         if (u > t) {
-          const Pack<T, CPL> plu = ldtok(gl, 16 * w + u);
+          const Pack<T, CPL> plu = ldtok(bl, 16 * w + u);
 #pragma unroll
           for (int e = 0; e < CPL; ++e) ex[e] += floor_logf(to_f32(plu.v[e]));
         }
@@ -569,9 +563,9 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
         if (has_ch) sq[t * LDG + c0 + e] = x;  // X_t replaces the consumed dq'_t
         tot[e] += x;
       }
-      if (tt < len && has_ch) {
-        stpack<T, CPL>(gw_(gdq, tok(tt) + c0b), oq);
-        stpack<T, CPL>(gw_(gdk, tok(tt) + c0b), ok);
+      if (has_ch) {
+        bdq.stpack<T, CPL>(tok(tt) + c0b, oq);
+        bdk.stpack<T, CPL>(tok(tt) + c0b, ok);
       }
     }
     if (has_ch)
@@ -598,7 +592,7 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
           carry[e] += X[t][e];
           o.v[e] = from_f32<T>(carry[e]);
         }
-        if (tt < len) stpack<T, CPL>(gw_(gdl, tok(tt) + c0b), o);
+        bdl.stpack<T, CPL>(tok(tt) + c0b, o);
       }
     } else {
       for (int t = 15; t >= 0; --t) {
@@ -609,7 +603,7 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
           carry[e] += sq[t * LDG + c0 + e];
           o.v[e] = from_f32<T>(carry[e]);
         }
-        if (tt < len) stpack<T, CPL>(gw_(gdl, tok(tt) + c0b), o);
+        bdl.stpack<T, CPL>(tok(tt) + c0b, o);
       }
     }
   }

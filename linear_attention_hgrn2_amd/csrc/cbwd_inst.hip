@@ -1,5 +1,8 @@
 // Instantiations of the per-chunk gradients.
 #include "dispatch.h"
+#include "cbwd_res.h"
+
+#include <type_traits>
 
 namespace hgrn2 {
 
@@ -7,7 +10,12 @@ template <typename T, int D, int C> struct ChunkBwdOp {
   static hipError_t run(const ChunkBwdArgs *a, hipStream_t s) {
     static_assert(sizeof(typename CbwdCfg<T, D, C>::Smem) <= 160 * 1024, "LDS");
     if (!a) return hipSuccess;
-    return launch_chunk_bwd<T, D, C>(*a, s);
+    if constexpr (std::is_same<T, bf16_t>::value && D == 128 && C == 64) {
+      static_assert(sizeof(CbwdResCfg::Smem) <= 160 * 1024, "LDS");
+      return launch_chunk_bwd_res(*a, s);
+    } else {
+      return launch_chunk_bwd<T, D, C>(*a, s);
+    }
   }
 };
 

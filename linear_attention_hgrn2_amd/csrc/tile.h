@@ -86,11 +86,14 @@ __device__ __forceinline__ v4s_t tr_read(const bf16_t *t, int row_of_lane, int n
 }
 
 // tr4: accumulator arrangement, rows r0 + 4g + j, column n0 + n
-template <int W> __device__ __forceinline__ PFrag4<bf16_t> tr4(const bf16_t *t, int r0, int n0) {
-  const int lane = lane_id(), g = lane >> 4, i = lane & 15;
+template <int W> __device__ __forceinline__ PFrag4<bf16_t> tr4(const bf16_t *t, int r0, int n0, int lane) {
+  const int g = lane >> 4, i = lane & 15;
   PFrag4<bf16_t> f;
   f.x = tr_read<W>(t, r0 + 4 * g + (i >> 2), n0, i);
   return f;
+}
+template <int W> __device__ __forceinline__ PFrag4<bf16_t> tr4(const bf16_t *t, int r0, int n0) {
+  return tr4<W>(t, r0, n0, lane_id());
 }
 template <int W> __device__ __forceinline__ PFrag4<float> tr4(const float *t, int r0, int n0) {
   const int lane = lane_id(), g = lane >> 4, n = lane & 15;
@@ -252,5 +255,92 @@ __device__ __forceinline__ float group_sum(float x) {
   x += __shfl_xor(x, 32, 64);
   return x;
 }
+
+// A window of a global tensor addressed by 32-bit byte offsets through a
+// buffer descriptor (base and size in scalar registers).  Loads at offsets at
+// or past `bytes` return zero and stores there are dropped, which masks the
+// rows of a partial chunk without branches or per-lane address arithmetic.
+struct GBuf {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ __forceinline__ GBuf(const void *base, uint32_t bytes)
+      : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000)) {}
+  __device__ __forceinline__ uint4 ld16(uint32_t off) const {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  }
+  __device__ __forceinline__ void st16(uint32_t off, const uint4 &v) const {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), v), r, off, 0, 0);
+  }
+  // 8 consecutive elements as a matrix-core operand fragment
+  __device__ __forceinline__ PFrag<bf16_t> frag8(const bf16_t *, uint32_t off) const {
+    PFrag<bf16_t> f;
+    f.x = __builtin_bit_cast(bf16x8_t, ld16(off));
+    return f;
+  }
+  __device__ __forceinline__ PFrag<float> frag8(const float *, uint32_t off) const {
+    const float4 a = __builtin_bit_cast(float4, ld16(off)), b = __builtin_bit_cast(float4, ld16(off + 16));
+    PFrag<float> f;
+    f.x[0] = a.x; f.x[1] = a.y; f.x[2] = a.z; f.x[3] = a.w;
+    f.x[4] = b.x; f.x[5] = b.y; f.x[6] = b.z; f.x[7] = b.w;
+    return f;
+  }
+  template <typename T, int N> __device__ __forceinline__ Pack<T, N> ldpack(uint32_t off) const {
+    Pack<T, N> p;
+    constexpr int BYTES = (int)sizeof(T) * N;
+    if constexpr (BYTES == 2) {
+      const unsigned short u = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+      __builtin_memcpy(&p, &u, 2);
+    } else if constexpr (BYTES == 4) {
+      const uint32_t u = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+      __builtin_memcpy(&p, &u, 4);
+    } else if constexpr (BYTES == 8) {
+      const auto u = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+      __builtin_memcpy(&p, &u, 8);
+    } else {
+      static_assert(BYTES == 16, "pack size");
+      const uint4 u = ld16(off);
+      __builtin_memcpy(&p, &u, 16);
+    }
+    return p;
+  }
+  template <typename T, int N> __device__ __forceinline__ void stpack(uint32_t off, const Pack<T, N> &p) const {
+    constexpr int BYTES = (int)sizeof(T) * N;
+    if constexpr (BYTES == 2) {
+      unsigned short u;
+      __builtin_memcpy(&u, &p, 2);
+      __builtin_amdgcn_raw_buffer_store_b16(u, r, off, 0, 0);
+    } else if constexpr (BYTES == 4) {
+      uint32_t u;
+      __builtin_memcpy(&u, &p, 4);
+      __builtin_amdgcn_raw_buffer_store_b32(u, r, off, 0, 0);
+    } else if constexpr (BYTES == 8) {
+      decltype(__builtin_amdgcn_raw_buffer_load_b64(r, 0, 0, 0)) u;
+      __builtin_memcpy(&u, &p, 8);
+      __builtin_amdgcn_raw_buffer_store_b64(u, r, off, 0, 0);
+    } else {
+      static_assert(BYTES == 16, "pack size");
+      uint4 u;
+      __builtin_memcpy(&u, &p, 16);
+      st16(off, u);
+    }
+  }
+};
+
+// An asynchronous copy of 16 bytes per lane from a buffer window straight into
+// LDS: lane i's bytes land at lds_base + 16 i (lds_base is the same for the
+// whole wave).  Issued as a plain instruction so that the compiler does not
+// make the next LDS access wait for it: the caller waits for the vector-memory
+// counter to drain (and synchronises the workgroup) before anything reads the
+// destination, and touches nothing there before.  No register receives data.
+__device__ __forceinline__ void lds_dma16(const GBuf &b, uint32_t off, const void *lds_base) {
+  const uint32_t m =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char *)lds_base);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds" ::"v"(off), "s"(m), "s"(b.r)
+               : "memory", "m0");
+#pragma clang diagnostic pop
+}
+// Waits until every vector-memory load of this wave, copies into LDS included, has landed.
+__device__ __forceinline__ void vm_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 }  // namespace hgrn2

@@ -147,6 +147,28 @@ def test_bwd_extreme_gates():
         _bwd_check(d, 16, label="extreme")
 
 
+def test_bwd_extreme_gates_d128():
+    """d = 128, chunk 64 in bfloat16 (the training shape's kernel): blocks whose
+    in-block decay forces the directly summed diagonal, a full reset and the
+    -200 floor, in several chunks."""
+    d = _case("bf16", B=1, T=300, H=2, D=128, lam=0.0, h0std=0.3, qscale=1.0)
+    lf = synth.to_f64(d["log_f"], "bf16")
+    lf[0, 3, 0, :] = -np.inf
+    lf[0, 20, 1, 2] = -200.0
+    lf[0, 40:44, 0, 1] = -30.0
+    lf[0, 70:80, 1, :] = -9.0
+    lf[0, 200:216, 0, 5] = -5.0
+    d["log_f"] = synth.f32_to_bf16_bits(lf.astype(np.float32))
+    _bwd_check(d, 64, label="extreme d128")
+
+
+def test_bwd_many_chunks_per_workgroup():
+    """More chunks than workgroups at d = 128, chunk 64 (bfloat16), with a
+    ragged last chunk: each workgroup walks several chunks."""
+    d = _case("bf16", B=3, T=20 * 64 + 13, H=5, D=128, lam=0.3, h0std=0.2, qscale=1.0)
+    _bwd_check(d, 64, label="many chunks")
+
+
 # ------------------------------------------------------------------- decode
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
