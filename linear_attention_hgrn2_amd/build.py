@@ -31,6 +31,11 @@ FLAGS = [
     "-Wno-unused-command-line-argument", "-Wno-shadow",
 ]
 
+# sources whose matrix-core accumulators stay in ordinary vector registers
+# (their per-step float32 updates of the state would otherwise move it
+# between register files twice per step)
+VGPR_MFMA = {"scan_inst.hip", "cfwd_inst.hip"}
+
 
 def hipcc() -> str:
     p = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -43,6 +48,8 @@ def _compile(src: str) -> str:
     os.makedirs(BUILD, exist_ok=True)
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc(), "-c", os.path.join(CSRC, src), "-o", obj] + FLAGS
+    if src in VGPR_MFMA:
+        cmd += ["-mllvm", "-amdgpu-mfma-vgpr-form"]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)

@@ -47,8 +47,8 @@ template <typename T, int D, int C, bool REV> struct ScanCfg {
   static constexpr int VZ = C * D / EPV;             // 16-byte vectors of one z tile
   static constexpr int NVZ = (VZ + NT - 1) / NT;
   struct Smem {
-    T x[C * RowTile<T, CS>::LD];     // decayed x of this slice's channels
-    T z[2][C * RowTile<T, D>::LD];   // z rows, double-buffered
+    T x[C * RowTile<T, CS, 32>::LD];    // decayed x of this slice's channels
+    T z[2][C * RowTile<T, D, 32>::LD];  // z rows, double-buffered
     float Lb[NW][CS];                // sub-block totals of log f
     float eG[CS];                    // e^Gamma
   };
@@ -59,8 +59,9 @@ __global__ __launch_bounds__(4 * C) void hgrn2_scan_kernel(ScanArgs a) {
   using Cfg = ScanCfg<T, D, C, REV>;
   constexpr int NW = Cfg::NW, NT = Cfg::NT, CS = Cfg::CS, NS = Cfg::NS, GL = Cfg::GL, TPG = Cfg::TPG,
                 JB = Cfg::JB, EPV = Cfg::EPV;
-  using XT = RowTile<T, CS>;
-  using ZT = RowTile<T, D>;
+  // rows padded by 32 bytes: the transposing operand reads are conflict-free
+  using XT = RowTile<T, CS, 32>;
+  using ZT = RowTile<T, D, 32>;
   __shared__ typename Cfg::Smem sm;
 
   // slices of one (b, h) get ids equal mod 8: they run on one XCD and share its L2
@@ -76,12 +77,22 @@ __global__ __launch_bounds__(4 * C) void hgrn2_scan_kernel(ScanArgs a) {
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n16 = lane & 15, g = lane >> 4;
   const int cl = lane % CS, gi = lane / CS;  // prep layout: channel, token run
 
-  const T *gx = (const T *)a.x;
-  const T *gz = (const T *)a.z;
-  const T *gl = (const T *)a.log_f;
-  T *gst = (T *)a.states;
   const size_t SS = (size_t)D * D;
-  auto tok = [&](int t) { return (((size_t)b * T_ + t) * H + h) * D; };
+  const uint32_t HDB = (uint32_t)H * D * sizeof(T);  // bytes from one token to the next
+  // buffer window over the rows of chunk n: rows past the end of the sequence read as zero
+  auto win = [&](const void *base, int n) {
+    const int t0 = n * C;
+    return GBuf((const char *)base + (((size_t)b * T_ + t0) * H + h) * D * sizeof(T),
+                (uint32_t)min(C, T_ - t0) * HDB);
+  };
+  // per-lane byte offsets within a chunk window (the same for every chunk)
+  const uint32_t xoff = (uint32_t)(16 * w + TPG * gi) * HDB + (uint32_t)(cs0 + cl) * sizeof(T);
+  uint32_t zoff[Cfg::NVZ];
+#pragma unroll
+  for (int i = 0; i < Cfg::NVZ; ++i) {
+    const int idc = min(tid + i * NT, Cfg::VZ - 1);
+    zoff[i] = (uint32_t)(idc / (D / EPV)) * HDB + (uint32_t)((idc % (D / EPV)) * EPV) * sizeof(T);
+  }
 
   // ---- state tiles: tile q = w + NW * i (q < NTILE) covers S^T rows (j) 16 jb.. and columns (c) cs0 + 16 cb..
   f32x4_t S[Cfg::TPW];
@@ -97,9 +108,10 @@ __global__ __launch_bounds__(4 * C) void hgrn2_scan_kernel(ScanArgs a) {
       acc_zero(S[i]);
     }
   }
+  // this (b, h)'s entries of the state buffer; entry `slot` at a scalar offset
+  const int nst = REV ? N : N + 1;
+  const GBuf bst((const char *)a.states + (size_t)bh * nst * SS * sizeof(T), (uint32_t)(nst * SS * sizeof(T)));
   auto store_tiles = [&](int slot) {
-    const int nst = REV ? N : N + 1;
-    T *st = gst + ((size_t)bh * nst + slot) * SS;
 #pragma unroll
     for (int i = 0; i < Cfg::TPW; ++i) {
       const int q = w + NW * i;
@@ -109,7 +121,7 @@ __global__ __launch_bounds__(4 * C) void hgrn2_scan_kernel(ScanArgs a) {
         Pack<T, 4> p;
 #pragma unroll
         for (int r = 0; r < 4; ++r) p.v[r] = from_f32<T>(S[i][r]);
-        stpack<T, 4>(st + (size_t)c * D + j, p);
+        bst.stpack<T, 4>((uint32_t)(c * D + j) * sizeof(T), p, (uint32_t)(slot * SS * sizeof(T)));
       }
     }
   };
@@ -119,38 +131,30 @@ __global__ __launch_bounds__(4 * C) void hgrn2_scan_kernel(ScanArgs a) {
   // this lane's channel and token run; the z tile
   using XP = T[TPG];
   using ZP = uint4[Cfg::NVZ];
-  // Loads are unconditional: rows past the end re-read the last row and are
-  // zeroed where they are consumed, so the number of loads in flight is fixed
-  // and waiting for one register set never waits for the other.
+  // Loads go through buffer windows: rows past the end of the sequence read
+  // as zero (log f = 0, x = 0, z = 0 contribute nothing), so nothing is masked
+  // where they are consumed and every step issues the same loads.
   auto prefetch = [&](XP &px, XP &pl, ZP &pz, int n) {
-    const int t0 = n * C, len = min(C, T_ - t0);
-    const T *cx = gx + tok(t0) + cs0 + cl, *clf = gl + tok(t0) + cs0 + cl, *cz = gz + tok(t0);
-    const uint32_t HD = (uint32_t)H * D;
+    const GBuf bx = win(a.x, n), bl = win(a.log_f, n), bz = win(a.z, n);
 #pragma unroll
     for (int i = 0; i < TPG; ++i) {
-      const uint32_t off = (uint32_t)min(16 * w + TPG * gi + i, len - 1) * HD;
-      px[i] = cx[off];
-      pl[i] = clf[off];
+      px[i] = bx.ldpack<T, 1>(xoff + (uint32_t)i * HDB).v[0];
+      pl[i] = bl.ldpack<T, 1>(xoff + (uint32_t)i * HDB).v[0];
     }
 #pragma unroll
-    for (int i = 0; i < Cfg::NVZ; ++i) {
-      const int idc = min(tid + i * NT, Cfg::VZ - 1);
-      const int row = idc / (D / EPV), col = (idc % (D / EPV)) * EPV;
-      pz[i] = *(const uint4 *)(cz + ((uint32_t)min(row, len - 1) * HD + col));
-    }
+    for (int i = 0; i < Cfg::NVZ; ++i) pz[i] = bz.ld16(zoff[i]);
   };
 
   // one chunk: consumes (px, pl, pz), then refills them with the chunk two steps on
   auto step = [&](XP &px, XP &pl, ZP &pz, int it) {
     const int n = REV ? N - 1 - it : it;
-    const int len = min(C, T_ - n * C);
     T *zs = sm.z[it & 1];
     // ---- block-local prefix of the floored log f: within the lane's run, then across runs
     float l[TPG];
     float run = 0.f;
 #pragma unroll
     for (int i = 0; i < TPG; ++i) {
-      run += (16 * w + TPG * gi + i < len) ? floor_logf(to_f32(pl[i])) : 0.f;
+      run += floor_logf(to_f32(pl[i]));
       l[i] = run;
     }
     float incl = run;
@@ -166,7 +170,7 @@ __global__ __launch_bounds__(4 * C) void hgrn2_scan_kernel(ScanArgs a) {
     for (int i = 0; i < Cfg::NVZ; ++i) {
       const int idx = tid + i * NT;
       const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
-      if (idx < Cfg::VZ) *(uint4 *)&zs[ZT::at(row, col)] = (row < len) ? pz[i] : make_uint4(0, 0, 0, 0);
+      if (idx < Cfg::VZ) *(uint4 *)&zs[ZT::at(row, col)] = pz[i];
     }
     __syncthreads();
     // ---- decayed x: forward x e^{Gamma - b_t}, backward x e^{b_t}
@@ -183,8 +187,7 @@ __global__ __launch_bounds__(4 * C) void hgrn2_scan_kernel(ScanArgs a) {
       for (int i = 0; i < TPG; ++i) {
         const float b_t = P + excl + l[i];
         const float ex = REV ? b_t : fminf(G - b_t, 0.f);
-        const float xv = (16 * w + TPG * gi + i < len) ? to_f32(px[i]) : 0.f;
-        sm.x[XT::at(16 * w + TPG * gi + i, cl)] = from_f32<T>(xv * __expf(ex));
+        sm.x[XT::at(16 * w + TPG * gi + i, cl)] = from_f32<T>(to_f32(px[i]) * __expf(ex));
       }
     }
     // this register set is consumed: fetch the chunk two steps on into it (the
@@ -205,9 +208,9 @@ __global__ __launch_bounds__(4 * C) void hgrn2_scan_kernel(ScanArgs a) {
         if constexpr (C % 32 == 0) {
 #pragma unroll
           for (int ks = 0; ks < C / 32; ++ks)
-            mma(S[i], tr8<D>(zs, 32 * ks, 16 * jb), tr8<CS>(sm.x, 32 * ks, 16 * cb));
+            mma(S[i], tr8<D, 32>(zs, 32 * ks, 16 * jb), tr8<CS, 32>(sm.x, 32 * ks, 16 * cb));
         } else {
-          mma16(S[i], tr4<D>(zs, 0, 16 * jb), tr4<CS>(sm.x, 0, 16 * cb));
+          mma16(S[i], tr4<D, 32>(zs, 0, 16 * jb), tr4<CS, 32>(sm.x, 0, 16 * cb));
         }
       }
     }

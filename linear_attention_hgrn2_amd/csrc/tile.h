@@ -21,9 +21,13 @@ namespace hgrn2 {
 
 typedef short v4s_t __attribute__((ext_vector_type(4)));
 
-template <typename T, int W> struct RowTile {
+// Row-major tile of W columns padded by PADB bytes per row.  16 bytes shifts
+// consecutive rows by 4 banks (16-row reads of 16 bytes per lane are
+// conflict-free); 32 bytes by 8 banks (8-row transposing reads of 32 bytes per
+// row are).
+template <typename T, int W, int PADB = 16> struct RowTile {
   static constexpr int EPV = 16 / (int)sizeof(T);  // elements per 16-byte chunk
-  static constexpr int LD = W + EPV;               // row stride in elements
+  static constexpr int LD = W + PADB / (int)sizeof(T);  // row stride in elements
   __device__ static __forceinline__ int at(int r, int c) { return r * LD + c; }
 };
 
@@ -68,83 +72,83 @@ template <typename Op> __device__ __forceinline__ PFrag<Op> accs_to_frag(const f
 
 // ------------------------------------------------------------ loaders
 // row8: elements c0..c0+7 of row r (c0 a multiple of 8)
-template <int W> __device__ __forceinline__ PFrag<bf16_t> row8(const bf16_t *t, int r, int c0) {
-  return ld8(t + RowTile<bf16_t, W>::at(r, c0));
+template <int W, int PADB = 16> __device__ __forceinline__ PFrag<bf16_t> row8(const bf16_t *t, int r, int c0) {
+  return ld8(t + RowTile<bf16_t, W, PADB>::at(r, c0));
 }
-template <int W> __device__ __forceinline__ PFrag<float> row8(const float *t, int r, int c0) {
-  return ld4x2(t + RowTile<float, W>::at(r, c0), t + RowTile<float, W>::at(r, c0 + 4));
+template <int W, int PADB = 16> __device__ __forceinline__ PFrag<float> row8(const float *t, int r, int c0) {
+  return ld4x2(t + RowTile<float, W, PADB>::at(r, c0), t + RowTile<float, W, PADB>::at(r, c0 + 4));
 }
 
 // one transposing read: lane (g, n) receives t[rows(g, j)][n0 + n] for j = 0..3,
 // where lane (g, i) of the group supplies row rows(g, i >> 2) at column
 // n0 + 4 (i & 3) (gfx950 ds_read_b64_tr_b16 semantics)
-template <int W>
+template <int W, int PADB = 16>
 __device__ __forceinline__ v4s_t tr_read(const bf16_t *t, int row_of_lane, int n0, int lane) {
   const int c = n0 + 4 * (lane & 3);
-  const bf16_t *p = t + RowTile<bf16_t, W>::at(row_of_lane, c);
+  const bf16_t *p = t + RowTile<bf16_t, W, PADB>::at(row_of_lane, c);
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t *)(p));
 }
 
 // tr4: accumulator arrangement, rows r0 + 4g + j, column n0 + n
-template <int W> __device__ __forceinline__ PFrag4<bf16_t> tr4(const bf16_t *t, int r0, int n0, int lane) {
+template <int W, int PADB = 16> __device__ __forceinline__ PFrag4<bf16_t> tr4(const bf16_t *t, int r0, int n0, int lane) {
   const int g = lane >> 4, i = lane & 15;
   PFrag4<bf16_t> f;
-  f.x = tr_read<W>(t, r0 + 4 * g + (i >> 2), n0, i);
+  f.x = tr_read<W, PADB>(t, r0 + 4 * g + (i >> 2), n0, i);
   return f;
 }
-template <int W> __device__ __forceinline__ PFrag4<bf16_t> tr4(const bf16_t *t, int r0, int n0) {
-  return tr4<W>(t, r0, n0, lane_id());
+template <int W, int PADB = 16> __device__ __forceinline__ PFrag4<bf16_t> tr4(const bf16_t *t, int r0, int n0) {
+  return tr4<W, PADB>(t, r0, n0, lane_id());
 }
-template <int W> __device__ __forceinline__ PFrag4<float> tr4(const float *t, int r0, int n0) {
+template <int W, int PADB = 16> __device__ __forceinline__ PFrag4<float> tr4(const float *t, int r0, int n0) {
   const int lane = lane_id(), g = lane >> 4, n = lane & 15;
   PFrag4<float> f;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) f.x[j] = t[RowTile<float, W>::at(r0 + 4 * g + j, n0 + n)];
+  for (int j = 0; j < 4; ++j) f.x[j] = t[RowTile<float, W, PADB>::at(r0 + 4 * g + j, n0 + n)];
   return f;
 }
 
 // tr8, standard k order: slots i <-> rows r0 + 8g + i, column n0 + n
-template <int W> __device__ __forceinline__ PFrag<bf16_t> tr8(const bf16_t *t, int r0, int n0) {
+template <int W, int PADB = 16> __device__ __forceinline__ PFrag<bf16_t> tr8(const bf16_t *t, int r0, int n0) {
   const int lane = lane_id(), g = lane >> 4, i = lane & 15;
   union {
     v4s_t h[2];
     bf16x8_t v;
   } u;
-  u.h[0] = tr_read<W>(t, r0 + 8 * g + (i >> 2), n0, i);
-  u.h[1] = tr_read<W>(t, r0 + 8 * g + 4 + (i >> 2), n0, i);
+  u.h[0] = tr_read<W, PADB>(t, r0 + 8 * g + (i >> 2), n0, i);
+  u.h[1] = tr_read<W, PADB>(t, r0 + 8 * g + 4 + (i >> 2), n0, i);
   PFrag<bf16_t> f;
   f.x = u.v;
   return f;
 }
-template <int W> __device__ __forceinline__ PFrag<float> tr8(const float *t, int r0, int n0) {
+template <int W, int PADB = 16> __device__ __forceinline__ PFrag<float> tr8(const float *t, int r0, int n0) {
   const int lane = lane_id(), g = lane >> 4, n = lane & 15;
   PFrag<float> f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) f.x[j] = t[RowTile<float, W>::at(r0 + 8 * g + j, n0 + n)];
+  for (int j = 0; j < 8; ++j) f.x[j] = t[RowTile<float, W, PADB>::at(r0 + 8 * g + j, n0 + n)];
   return f;
 }
 
 // tr8, accumulator k order: slots 0-3 <-> rows ra + 4g + j, slots 4-7 <-> rows rb + 4g + j
 // (pairs with an operand built by accs_to_frag)
-template <int W> __device__ __forceinline__ PFrag<bf16_t> tr8acc(const bf16_t *t, int ra, int rb, int n0) {
+template <int W, int PADB = 16> __device__ __forceinline__ PFrag<bf16_t> tr8acc(const bf16_t *t, int ra, int rb, int n0) {
   const int lane = lane_id(), g = lane >> 4, i = lane & 15;
   union {
     v4s_t h[2];
     bf16x8_t v;
   } u;
-  u.h[0] = tr_read<W>(t, ra + 4 * g + (i >> 2), n0, i);
-  u.h[1] = tr_read<W>(t, rb + 4 * g + (i >> 2), n0, i);
+  u.h[0] = tr_read<W, PADB>(t, ra + 4 * g + (i >> 2), n0, i);
+  u.h[1] = tr_read<W, PADB>(t, rb + 4 * g + (i >> 2), n0, i);
   PFrag<bf16_t> f;
   f.x = u.v;
   return f;
 }
-template <int W> __device__ __forceinline__ PFrag<float> tr8acc(const float *t, int ra, int rb, int n0) {
+template <int W, int PADB = 16> __device__ __forceinline__ PFrag<float> tr8acc(const float *t, int ra, int rb, int n0) {
   const int lane = lane_id(), g = lane >> 4, n = lane & 15;
   PFrag<float> f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    f.x[j] = t[RowTile<float, W>::at(ra + 4 * g + j, n0 + n)];
-    f.x[4 + j] = t[RowTile<float, W>::at(rb + 4 * g + j, n0 + n)];
+    f.x[j] = t[RowTile<float, W, PADB>::at(ra + 4 * g + j, n0 + n)];
+    f.x[4 + j] = t[RowTile<float, W, PADB>::at(rb + 4 * g + j, n0 + n)];
   }
   return f;
 }
@@ -264,11 +268,13 @@ struct GBuf {
   __amdgpu_buffer_rsrc_t r;
   __device__ __forceinline__ GBuf(const void *base, uint32_t bytes)
       : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000)) {}
-  __device__ __forceinline__ uint4 ld16(uint32_t off) const {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  // soff is a scalar byte offset added to every lane's; unlike off it is not
+  // part of the range check, so it only carries offsets known to be in range
+  __device__ __forceinline__ uint4 ld16(uint32_t off, uint32_t soff = 0) const {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
   }
-  __device__ __forceinline__ void st16(uint32_t off, const uint4 &v) const {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), v), r, off, 0, 0);
+  __device__ __forceinline__ void st16(uint32_t off, const uint4 &v, uint32_t soff = 0) const {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), v), r, off, soff, 0);
   }
   // 8 consecutive elements as a matrix-core operand fragment
   __device__ __forceinline__ PFrag<bf16_t> frag8(const bf16_t *, uint32_t off) const {
@@ -283,44 +289,45 @@ struct GBuf {
     f.x[4] = b.x; f.x[5] = b.y; f.x[6] = b.z; f.x[7] = b.w;
     return f;
   }
-  template <typename T, int N> __device__ __forceinline__ Pack<T, N> ldpack(uint32_t off) const {
+  template <typename T, int N> __device__ __forceinline__ Pack<T, N> ldpack(uint32_t off, uint32_t soff = 0) const {
     Pack<T, N> p;
     constexpr int BYTES = (int)sizeof(T) * N;
     if constexpr (BYTES == 2) {
-      const unsigned short u = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+      const unsigned short u = __builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0);
       __builtin_memcpy(&p, &u, 2);
     } else if constexpr (BYTES == 4) {
-      const uint32_t u = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+      const uint32_t u = __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0);
       __builtin_memcpy(&p, &u, 4);
     } else if constexpr (BYTES == 8) {
-      const auto u = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+      const auto u = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0);
       __builtin_memcpy(&p, &u, 8);
     } else {
       static_assert(BYTES == 16, "pack size");
-      const uint4 u = ld16(off);
+      const uint4 u = ld16(off, soff);
       __builtin_memcpy(&p, &u, 16);
     }
     return p;
   }
-  template <typename T, int N> __device__ __forceinline__ void stpack(uint32_t off, const Pack<T, N> &p) const {
+  template <typename T, int N>
+  __device__ __forceinline__ void stpack(uint32_t off, const Pack<T, N> &p, uint32_t soff = 0) const {
     constexpr int BYTES = (int)sizeof(T) * N;
     if constexpr (BYTES == 2) {
       unsigned short u;
       __builtin_memcpy(&u, &p, 2);
-      __builtin_amdgcn_raw_buffer_store_b16(u, r, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16(u, r, off, soff, 0);
     } else if constexpr (BYTES == 4) {
       uint32_t u;
       __builtin_memcpy(&u, &p, 4);
-      __builtin_amdgcn_raw_buffer_store_b32(u, r, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(u, r, off, soff, 0);
     } else if constexpr (BYTES == 8) {
       decltype(__builtin_amdgcn_raw_buffer_load_b64(r, 0, 0, 0)) u;
       __builtin_memcpy(&u, &p, 8);
-      __builtin_amdgcn_raw_buffer_store_b64(u, r, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(u, r, off, soff, 0);
     } else {
       static_assert(BYTES == 16, "pack size");
       uint4 u;
       __builtin_memcpy(&u, &p, 16);
-      st16(off, u);
+      st16(off, u, soff);
     }
   }
 };
