@@ -124,7 +124,7 @@ class KernelTimer:
 
 # the four launches of one training step, in order, with the kernel each one runs
 TRAIN_KERNELS = (("scan", "hgrn2_scan_kernel (forward)"), ("cfwd", "hgrn2_chunk_fwd_kernel"),
-                 ("scan_rev", "hgrn2_scan_kernel (reverse)"), ("cbwd", "hgrn2_chunk_bwd_kernel"))
+                 ("scan_rev", "hgrn2_scan_kernel (reverse)"), ("cbwd", "hgrn2_chunk_bwd_res_kernel"))
 
 
 def kernel_label(name: str):
@@ -134,7 +134,7 @@ def kernel_label(name: str):
         return "scan_rev" if "true" in n else "scan"
     if n.startswith("hgrn2_chunk_fwd_kernel"):
         return "cfwd"
-    if n.startswith("hgrn2_chunk_bwd_kernel"):
+    if n.startswith("hgrn2_chunk_bwd"):
         return "cbwd"
     if n.startswith("hgrn2_decode_kernel"):
         return "decode"

@@ -253,6 +253,24 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave (lane 0 first): a
+// Kogge-Stone scan within each row of 16 lanes by DPP row shifts, then the
+// row totals carried forward by the row broadcasts of lanes 15 and 31.
+// Lanes a shift or broadcast does not reach add 0.
+template <int CTRL, int ROW_MASK> __device__ __forceinline__ float dpp_add(float x) {
+  const int y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, false);
+  return x + __int_as_float(y);
+}
+__device__ __forceinline__ float wave_incl_scan(float x) {
+  x = dpp_add<0x111, 0xf>(x);  // row_shr:1
+  x = dpp_add<0x112, 0xf>(x);  // row_shr:2
+  x = dpp_add<0x114, 0xf>(x);  // row_shr:4
+  x = dpp_add<0x118, 0xf>(x);  // row_shr:8
+  x = dpp_add<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+  x = dpp_add<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
 // sum over the four lane groups g (lanes n, n + 16, n + 32, n + 48)
 __device__ __forceinline__ float group_sum(float x) {
   x += __shfl_xor(x, 16, 64);
@@ -301,10 +319,14 @@ struct GBuf {
     } else if constexpr (BYTES == 8) {
       const auto u = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0);
       __builtin_memcpy(&p, &u, 8);
-    } else {
-      static_assert(BYTES == 16, "pack size");
+    } else if constexpr (BYTES == 16) {
       const uint4 u = ld16(off, soff);
       __builtin_memcpy(&p, &u, 16);
+    } else {
+      static_assert(BYTES == 32, "pack size");
+      const uint4 u0 = ld16(off, soff), u1 = ld16(off + 16, soff);
+      __builtin_memcpy(&p, &u0, 16);
+      __builtin_memcpy((char *)&p + 16, &u1, 16);
     }
     return p;
   }
