@@ -450,7 +450,7 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int idx = lane + 64 * i, t = 16 * w + (idx >> 3), col = 64 * hh + 8 * (idx & 7);
-        bdv.st16(tok(t) + (uint32_t)col * sizeof(T), *(const uint4 *)&dvs[XT::at(t, col)]);
+        bdv.st16<kStream>(tok(t) + (uint32_t)col * sizeof(T), *(const uint4 *)&dvs[XT::at(t, col)]);
       }
     }
     auto &ep = sm.u.e;
@@ -488,8 +488,8 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
         X[t][e] = to_f32(qr.v[e]) * dd1[e] - to_f32(kr.v[e]) * dd2[e];
       }
       if (!wide) {
-        bdq.stpack<T, 2>(tok(tt) + (uint32_t)c0 * sizeof(T), oq);
-        bdk.stpack<T, 2>(tok(tt) + (uint32_t)c0 * sizeof(T), ok);
+        bdq.stpack<T, 2, kStream>(tok(tt) + (uint32_t)c0 * sizeof(T), oq);
+        bdk.stpack<T, 2, kStream>(tok(tt) + (uint32_t)c0 * sizeof(T), ok);
       }
     }
     if (wide) {
@@ -542,8 +542,8 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
           ok.v[e] = from_f32<T>(ek * dd2[e] + dkd[e]);
           X[t][e] += to_f32(pqt.v[e]) * dqd[e] - to_f32(pkt.v[e]) * dkd[e];
         }
-        bdq.stpack<T, 2>(tok(tt) + cb2, oq);
-        bdk.stpack<T, 2>(tok(tt) + cb2, ok);
+        bdq.stpack<T, 2, kStream>(tok(tt) + cb2, oq);
+        bdk.stpack<T, 2, kStream>(tok(tt) + cb2, ok);
       }
     }
 #pragma unroll
@@ -576,7 +576,7 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
           carry[e] += X[t][e];
           o.v[e] = from_f32<T>(carry[e]);
         }
-        bdl.stpack<T, 2>(tok(16 * w + 8 * hh + t) + (uint32_t)c0 * sizeof(T), o);
+        bdl.stpack<T, 2, kStream>(tok(16 * w + 8 * hh + t) + (uint32_t)c0 * sizeof(T), o);
       }
     }
   }

@@ -313,7 +313,10 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_fwd_kernel(ChunkFwdArgs a) 
     const int idx = lane + 64 * i;
     const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
     const int t = 16 * w + row;
-    if (idx < RV && t < len) *(uint4 *)(gy + (tok(t) + col)) = *(const uint4 *)&sm.qo[XT::at(t, col)];
+    if (idx < RV && t < len) {
+      const uint4 u = *(const uint4 *)&sm.qo[XT::at(t, col)];
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, u), (u32x4_t *)(gy + (tok(t) + col)));
+    }
   }
 }
 

@@ -22,6 +22,7 @@ namespace hgrn2 {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 struct bf16_t {  // storage type of a bfloat16 value in memory
   uint16_t bits;

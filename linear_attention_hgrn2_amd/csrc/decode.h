@@ -6,7 +6,8 @@
 // accesses, consecutive threads on consecutive columns, so every wavefront
 // instruction covers whole rows) and a strided set of rows; all of its row
 // loads are issued before any of them is used.  The column sums of q S are
-// reduced through LDS.
+// reduced through LDS.  State stores are non-temporal (streamed past the
+// caches), which lifts the write rate of this read-once/write-once pattern.
 #pragma once
 
 #include "common.h"
@@ -70,7 +71,8 @@ __global__ __launch_bounds__(256) void hgrn2_decode_kernel(DecodeArgs a) {
     x.y = f * x.y + kc * v1;
     x.z = f * x.z + kc * v2;
     x.w = f * x.w + kc * v3;
-    S[(size_t)c * CG + cg] = x;
+    // non-temporal: the state is written once per step and not read back here
+    __builtin_nontemporal_store(f32x4_t{x.x, x.y, x.z, x.w}, (f32x4_t *)&S[(size_t)c * CG + cg]);
     acc.x += qc * x.x;
     acc.y += qc * x.y;
     acc.z += qc * x.z;

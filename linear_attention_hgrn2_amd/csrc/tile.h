@@ -282,6 +282,8 @@ __device__ __forceinline__ float group_sum(float x) {
 // buffer descriptor (base and size in scalar registers).  Loads at offsets at
 // or past `bytes` return zero and stores there are dropped, which masks the
 // rows of a partial chunk without branches or per-lane address arithmetic.
+constexpr int kStream = 2;  // buffer-store cache policy: non-temporal
+
 struct GBuf {
   __amdgpu_buffer_rsrc_t r;
   __device__ __forceinline__ GBuf(const void *base, uint32_t bytes)
@@ -291,8 +293,10 @@ struct GBuf {
   __device__ __forceinline__ uint4 ld16(uint32_t off, uint32_t soff = 0) const {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
   }
-  __device__ __forceinline__ void st16(uint32_t off, const uint4 &v, uint32_t soff = 0) const {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), v), r, off, soff, 0);
+  // stores take a cache policy: kStream (non-temporal) for outputs that are
+  // written once and not read again by this kernel
+  template <int POL = 0> __device__ __forceinline__ void st16(uint32_t off, const uint4 &v, uint32_t soff = 0) const {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), v), r, off, soff, POL);
   }
   // 8 consecutive elements as a matrix-core operand fragment
   __device__ __forceinline__ PFrag<bf16_t> frag8(const bf16_t *, uint32_t off) const {
@@ -330,26 +334,26 @@ struct GBuf {
     }
     return p;
   }
-  template <typename T, int N>
+  template <typename T, int N, int POL = 0>
   __device__ __forceinline__ void stpack(uint32_t off, const Pack<T, N> &p, uint32_t soff = 0) const {
     constexpr int BYTES = (int)sizeof(T) * N;
     if constexpr (BYTES == 2) {
       unsigned short u;
       __builtin_memcpy(&u, &p, 2);
-      __builtin_amdgcn_raw_buffer_store_b16(u, r, off, soff, 0);
+      __builtin_amdgcn_raw_buffer_store_b16(u, r, off, soff, POL);
     } else if constexpr (BYTES == 4) {
       uint32_t u;
       __builtin_memcpy(&u, &p, 4);
-      __builtin_amdgcn_raw_buffer_store_b32(u, r, off, soff, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(u, r, off, soff, POL);
     } else if constexpr (BYTES == 8) {
       decltype(__builtin_amdgcn_raw_buffer_load_b64(r, 0, 0, 0)) u;
       __builtin_memcpy(&u, &p, 8);
-      __builtin_amdgcn_raw_buffer_store_b64(u, r, off, soff, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(u, r, off, soff, POL);
     } else {
       static_assert(BYTES == 16, "pack size");
       uint4 u;
       __builtin_memcpy(&u, &p, 16);
-      st16(off, u, soff);
+      st16<POL>(off, u, soff);
     }
   }
 };
