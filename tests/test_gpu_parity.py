@@ -218,3 +218,94 @@ def test_staged_launches_equal_composite_calls(dtype):
     assert torch.equal(dh0, dh02)
     for a, b in zip((dq, dk, dv, dl), g2):
         assert torch.equal(a, b)
+
+
+# ------------------------------------------------- fixed-order bitwise checks
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_repeat_runs_are_bitwise_equal(dtype):
+    """No kernel reorders its arithmetic between runs (no atomics, a fixed chunk
+    to workgroup assignment): two identical calls give identical bits."""
+    m = _hip()
+    import torch
+    d = _case(dtype, B=3, T=5 * 64 + 9, H=5, D=128, lam=0.3, h0std=0.5, qscale=1.0)
+    q, k, v, lf, dy = (to_dev(d[n], dtype) for n in ("q", "k", "v", "log_f", "dy"))
+    h0 = to_dev(d["h0"], "f32")
+    outs = []
+    for _ in range(2):
+        y, ht, st = m.fwd(q, k, v, lf, h0, chunk=64, want_states=True)
+        g = m.bwd(q, k, v, lf, dy, h0, ht * 0.5, st, chunk=64)
+        outs.append((y, ht, st) + tuple(g))
+    torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_state_carry_split_is_bitwise(dtype):
+    """Splitting a sequence at a multiple of the chunk and carrying the final
+    state in as the next call's initial state repeats the same operations in
+    the same order: outputs and final state match bit for bit."""
+    m = _hip()
+    import torch
+    C, T1 = 64, 3 * 64
+    d = _case(dtype, B=2, T=T1 + 2 * 64 + 21, H=3, D=128, lam=0.5, h0std=0.3, qscale=1.0)
+    q, k, v, lf = (to_dev(d[n], dtype) for n in ("q", "k", "v", "log_f"))
+    h0 = to_dev(d["h0"], "f32")
+    y, ht, _ = m.fwd(q, k, v, lf, h0, chunk=C)
+    part = lambda t, a, b: t[:, a:b].contiguous()
+    y1, ht1, _ = m.fwd(*(part(t, 0, T1) for t in (q, k, v, lf)), h0, chunk=C)
+    y2, ht2, _ = m.fwd(*(part(t, T1, d["T"]) for t in (q, k, v, lf)), ht1, chunk=C)
+    torch.cuda.synchronize()
+    assert torch.equal(y[:, :T1], y1)
+    assert torch.equal(y[:, T1:], y2)
+    assert torch.equal(ht, ht2)
+
+
+def test_chunk_sizes_agree_with_each_other():
+    """Chunks of 16, 32 and 64 tokens (bfloat16, d = 128) each meet the oracle's
+    tolerance and agree with one another within it."""
+    m = _hip()
+    import torch
+    d = _case("bf16", B=2, T=4 * 64 + 5, H=2, D=128, lam=0.3, h0std=0.3, qscale=1.0)
+    q, k, v, lf, dy = (to_dev(d[n], "bf16") for n in ("q", "k", "v", "log_f", "dy"))
+    h0 = to_dev(d["h0"], "f32")
+    res = {}
+    for C in (16, 32, 64):
+        y, ht, st = m.fwd(q, k, v, lf, h0, chunk=C, want_states=True)
+        g = m.bwd(q, k, v, lf, dy, h0, None, st, chunk=C)
+        res[C] = (y, ht) + tuple(g)
+    torch.cuda.synchronize()
+    x = inputs64(d)
+    yr, htr = oracle.forward(x["q"], x["k"], x["v"], x["log_f"], x["h0"])
+    gr = oracle.backward(x["q"], x["k"], x["v"], x["log_f"], x["dy"], x["h0"], None)
+    refs = (yr, htr) + tuple(gr)
+    for C, outs in res.items():
+        for i, (o, r) in enumerate(zip(outs, refs)):
+            tm = i not in (1, 6)
+            assert slice_rel(to_host64(o), r, token_major=tm) <= TOL["bf16"], (C, i)
+    for i in range(len(refs)):
+        tm = i not in (1, 6)
+        for C in (16, 32):
+            e = slice_rel(to_host64(res[C][i]), to_host64(res[64][i]), token_major=tm)
+            print("chunk %d vs 64, output %d: %.3e" % (C, i, e), flush=True)
+            assert e <= TOL["bf16"], (C, i, e)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_equals_forward_at_one_token(dtype):
+    """A decode step is the chunked forward at T = 1 from the same state."""
+    m = _hip()
+    import torch
+    d = synth.generate_decode("decode_f32", B=4, H=3, D=128, seed=21)
+    conv = (lambda a: a) if dtype == "f32" else (lambda a: synth.f32_to_bf16_bits(a))
+    q, k, v, lf = (to_dev(conv(d[n]), dtype) for n in ("q", "k", "v", "log_f"))
+    S = to_dev(d["state"], "f32")
+    yf, htf, _ = m.fwd(q[:, None].contiguous(), k[:, None].contiguous(), v[:, None].contiguous(),
+                       lf[:, None].contiguous(), S.clone(), chunk=16)
+    yd = m.decode_step(q, k, v, lf, S)
+    torch.cuda.synchronize()
+    ey = np.linalg.norm(to_host64(yd) - to_host64(yf[:, 0])) / np.linalg.norm(to_host64(yf[:, 0]))
+    es = np.linalg.norm(to_host64(S) - to_host64(htf)) / np.linalg.norm(to_host64(htf))
+    print("decode vs forward at T=1 %s: y %.3e state %.3e" % (dtype, ey, es), flush=True)
+    assert ey <= TOL[dtype] and es <= 1e-5
