@@ -39,6 +39,9 @@ TRACE_CMD = ("rocprofv3 --kernel-trace --stats -d gpurun_out/trace -o run --outp
              "-- python3 bench.py --steps 5 --warmup 1 --no-cpu")
 PMC_CMD = ("rocprofv3 --pmc {ctr} -d gpurun_out/{dir} -o run --output-format csv "
            "-- python3 bench.py --only train --steps 2 --warmup 1 --no-cpu --calib-copy")
+MFMA_CMD = ("rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 MfmaUtil -d gpurun_out/mfma -o run "
+            "--output-format csv -- python3 bench.py --only train --steps 2 --warmup 1 --no-cpu")
+MFMA_SUMMARY = os.path.join(PROFILES, "hgrn2_mfma_train_bf16_B8H16T4096.txt")
 
 
 def parse():
@@ -51,8 +54,9 @@ def parse():
     p.add_argument("--only", choices=["train", "decode", "all"], default="all")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 1 GiB device copy (calibrates profiler byte counters)")
-    p.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
-                   help="write the profiles/ summaries from rocprofv3 csv output and exit")
+    p.add_argument("--summarize", nargs="+", metavar="DIR",
+                   help="TRACE_DIR FETCH_DIR WRITE_DIR [MFMA_DIR]: write the profiles/ summaries "
+                        "from rocprofv3 csv output and exit")
     return p.parse_args()
 
 
@@ -265,8 +269,9 @@ def _short(name: str) -> str:
     return n.replace("void ", "").replace("hgrn2::", "")
 
 
-def summarize(trace_dir, fetch_dir, write_dir):
-    """profiles/ summaries from the csv output of TRACE_CMD and the two PMC_CMD runs."""
+def summarize(trace_dir, fetch_dir, write_dir, mfma_dir=None):
+    """profiles/ summaries from the csv output of TRACE_CMD, the two PMC_CMD runs
+    and (optionally) the MFMA_CMD run."""
     digest = kernel_source_digest()
     os.makedirs(PROFILES, exist_ok=True)
     # kernel-trace statistics
@@ -337,6 +342,43 @@ def summarize(trace_dir, fetch_dir, write_dir):
                                                    alg[label] / 1e6, (fb + wb) / alg[label]))
         out.append("traffic_bytes_per_launch %s: %.0f" % (label, fb + wb))
     with open(TRAFFIC_SUMMARY, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
+    if mfma_dir:
+        summarize_mfma(mfma_dir, {kernel_label(r["Name"]): float(r["AverageNs"]) for r in rows}, digest)
+
+
+def summarize_mfma(mfma_dir, avg_ns, digest):
+    """Matrix-core work the counters saw per launch: executed bf16 MFMA flops
+    (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512), the rate over the kernel-trace average
+    duration against the dense bf16 peak, and MfmaUtil (busy share of the
+    matrix cores while the kernel ran)."""
+    acc = {}
+    for r in _csv(os.path.join(mfma_dir, "run_counter_collection.csv")):
+        label = kernel_label(r["Kernel_Name"])
+        if label is None or label == "decode":
+            continue
+        acc.setdefault((label, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    w = __import__("synth").WORKLOADS["train_bf16"]
+    th = w.B * w.T * w.H
+    alg_flop = {"scan": th * 2 * w.D * w.D, "cfwd": th * (w.chunk * 2 * w.D + 2 * w.D * w.D),
+                "scan_rev": th * 2 * w.D * w.D, "cbwd": th * (5 * w.chunk * w.D + 6 * w.D * w.D)}
+    out = ["Matrix-core work per launch, HGRN2 training step (B8 H16 T4096 d128 bf16 chunk64)",
+           "command: " + MFMA_CMD, "durations: the kernel-trace averages of " + TRACE_CMD,
+           "peak: %.0f TFLOP/s dense bf16" % BF16_PEAK_TFLOPS, "source_digest: " + digest, "",
+           "%-9s %14s %14s %10s %10s %10s" % ("kernel", "executed_GFLOP", "algorithmic", "TFLOP/s",
+                                              "of_peak", "MfmaUtil")]
+    for label, _ in TRAIN_KERNELS:
+        mops = acc.get((label, "SQ_INSTS_VALU_MFMA_MOPS_BF16"))
+        util = acc.get((label, "MfmaUtil"))
+        if not mops or label not in avg_ns:
+            continue
+        flop = sum(mops) / len(mops) * 512
+        rate = flop / (avg_ns[label] * 1e-9) / 1e12
+        out.append("%-9s %14.2f %14.2f %10.1f %9.2f%% %9.2f%%" % (
+            label, flop / 1e9, alg_flop[label] / 1e9, rate, 100 * rate / BF16_PEAK_TFLOPS,
+            sum(util) / len(util) if util else float("nan")))
+    with open(MFMA_SUMMARY, "w") as f:
         f.write("\n".join(out) + "\n")
     print("\n".join(out))
 
