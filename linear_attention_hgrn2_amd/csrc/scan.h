@@ -51,6 +51,7 @@ template <typename T, int D, int C, bool REV> struct ScanCfg {
     T z[2][C * RowTile<T, D, 32>::LD];  // z rows, double-buffered
     float Lb[NW][CS];                // sub-block totals of log f
     float eG[CS];                    // e^Gamma
+    T st[CS * RowTile<T, D>::LD];    // a state awaiting its store, rows c of the slice
   };
 };
 
@@ -111,21 +112,40 @@ __global__ __launch_bounds__(4 * C) void hgrn2_scan_kernel(ScanArgs a) {
   // this (b, h)'s entries of the state buffer; entry `slot` at a scalar offset
   const int nst = REV ? N : N + 1;
   const GBuf bst((const char *)a.states + (size_t)bh * nst * SS * sizeof(T), (uint32_t)(nst * SS * sizeof(T)));
-  auto store_tiles = [&](int slot) {
+  // States leave through LDS: the tiles are written there (stage), and after
+  // the next barrier every thread stores two 16-byte pieces of whole rows
+  // (flush), so each store instruction writes complete 256-byte rows instead
+  // of 8-byte pieces of sixteen rows.
+  using STT = RowTile<T, D>;
+  constexpr int VST = CS * D / EPV;  // 16-byte vectors of the slice's state rows
+  int pend = -1;                     // entry staged and not yet stored
+  auto stage = [&](int slot) {
 #pragma unroll
     for (int i = 0; i < Cfg::TPW; ++i) {
       const int q = w + NW * i;
       if (q < Cfg::NTILE) {
         const int jb = q % JB, cb = q / JB;
-        const int c = cs0 + cb * 16 + n16, j = jb * 16 + 4 * g;
         Pack<T, 4> p;
 #pragma unroll
         for (int r = 0; r < 4; ++r) p.v[r] = from_f32<T>(S[i][r]);
-        bst.stpack<T, 4>((uint32_t)(c * D + j) * sizeof(T), p, (uint32_t)(slot * SS * sizeof(T)));
+        *(Pack<T, 4> *)&sm.st[STT::at(cb * 16 + n16, jb * 16 + 4 * g)] = p;
       }
     }
+    pend = slot;
   };
-  if (!REV) store_tiles(0);
+  auto flush = [&]() {
+    if (pend < 0) return;
+#pragma unroll
+    for (int i = 0; i < (VST + NT - 1) / NT; ++i) {
+      const int idx = tid + i * NT;
+      const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
+      if (idx < VST)
+        bst.st16((uint32_t)((cs0 + row) * D + col) * sizeof(T), *(const uint4 *)&sm.st[STT::at(row, col)],
+                 (uint32_t)(pend * SS * sizeof(T)));
+    }
+    pend = -1;
+  };
+  if (!REV) stage(0);
 
   // ---- register prefetch, two chunks ahead in two register sets: x, log f of
   // this lane's channel and token run; the z tile
@@ -190,12 +210,13 @@ __global__ __launch_bounds__(4 * C) void hgrn2_scan_kernel(ScanArgs a) {
         sm.x[XT::at(16 * w + TPG * gi + i, cl)] = from_f32<T>(to_f32(px[i]) * __expf(ex));
       }
     }
+    flush();  // the state staged in the previous step (read here, rewritten after the next barrier)
     // this register set is consumed: fetch the chunk two steps on into it (the
     // last chunk again near the end, so every step issues the same loads)
     prefetch(px, pl, pz, REV ? max(n - 2, 0) : min(n + 2, N - 1));
     __syncthreads();
     // ---- the adjoint at the end of chunk n is the value before its update
-    if (REV) store_tiles(n);
+    if (REV) stage(n);
     // ---- S^T <- S^T Diag(e^Gamma) + z^T xd
 #pragma unroll
     for (int i = 0; i < Cfg::TPW; ++i) {
@@ -214,7 +235,7 @@ __global__ __launch_bounds__(4 * C) void hgrn2_scan_kernel(ScanArgs a) {
         }
       }
     }
-    if (!REV) store_tiles(n + 1);
+    if (!REV) stage(n + 1);
   };
 
   T px0[TPG], pl0[TPG], px1[TPG], pl1[TPG];
@@ -227,6 +248,8 @@ __global__ __launch_bounds__(4 * C) void hgrn2_scan_kernel(ScanArgs a) {
     step(px1, pl1, pz1, it + 1);
   }
   if (it < N) step(px0, pl0, pz0, it);
+  __syncthreads();
+  flush();
   if (a.s_out) {
 #pragma unroll
     for (int i = 0; i < Cfg::TPW; ++i) {
