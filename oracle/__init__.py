@@ -24,7 +24,8 @@ _SRC = os.path.join(_HERE, "hgrn2_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle_hgrn2.so")
 _lib = None
 
-__all__ = ["build", "forward", "backward", "decode_step", "threads", "Oracle", "default"]
+__all__ = ["build", "forward", "backward", "decode_step", "forward_tied", "backward_tied",
+           "decode_step_tied", "tied_k", "threads", "Oracle", "default"]
 
 
 def build(force: bool = True) -> str:
@@ -139,3 +140,34 @@ def decode_step(q, k, v, log_f, state):
     """One recurrent step: returns (y [B,H,DV], new state [B,H,DK,DV]); the
     input state array is not modified."""
     return _load().decode_step(q, k, v, log_f, state)
+
+
+# ------------------------------------------------------------------ tied gates
+# HGRN2 ties the input gate to the forget gate, k = 1 - f (HGRN2 summary,
+# paperlayer.ai, §2.1 and §3.2).  With log_f the only gate input, k is a
+# function of it, and the loss reaches log_f both through the decay and
+# through k: d/dlog_f = (partial through the decay) + (dk/dlog_f) * dk with
+# dk/dlog_f = -exp(log_f).
+
+
+def tied_k(log_f):
+    """k = 1 - f = -expm1(log_f), float64, without cancellation for f near 1."""
+    return -np.expm1(np.asarray(log_f, dtype=np.float64))
+
+
+def forward_tied(q, v, log_f, h0=None):
+    """forward() with k = 1 - exp(log_f)."""
+    return forward(q, tied_k(log_f), v, log_f, h0)
+
+
+def backward_tied(q, v, log_f, dy, h0=None, dht=None):
+    """(dq, dv, dlog_f, dh0) with k = 1 - exp(log_f): dlog_f is the total
+    derivative, the partial through the decay minus exp(log_f) * dk."""
+    lf = np.asarray(log_f, dtype=np.float64)
+    dq, dk, dv, dl, dh0 = backward(q, tied_k(lf), v, lf, dy, h0, dht)
+    return dq, dv, dl - np.exp(lf) * dk, dh0
+
+
+def decode_step_tied(q, v, log_f, state):
+    """decode_step() with k = 1 - exp(log_f)."""
+    return decode_step(q, tied_k(log_f), v, log_f, state)

@@ -294,6 +294,69 @@ def pin_bwd_limits(orc):
     assert rel(dh0[0, 0], Q.T @ dY) < 1e-12
 
 
+# ---------------------------------------------------------------- tied gates
+
+def _loss_tied(orc, q, v, lf, h0, dy, dht):
+    import oracle as o
+    y, ht = orc.forward(q, o.tied_k(lf), v, lf, h0)
+    return float((y * dy).sum() + (ht * dht).sum())
+
+
+def pin_tied_finite_differences(orc):
+    """k = 1 - exp(log_f): central differences of the loss in (q, v, log_f, h0),
+    with k recomputed from every perturbed log_f, against backward_tied."""
+    import oracle as o
+    q, _, v, lf, h0 = rand_inputs(17, B=1, T=8, H=2, DK=3, DV=2)
+    r = _rng(18)
+    dy = r.standard_normal(v.shape)
+    dht = r.standard_normal(h0.shape)
+    grads = o.backward_tied(q, v, lf, dy, h0, dht)
+    args = [q, v, lf, h0]
+    eps = 1e-6
+    for ai, g in enumerate(grads):
+        x = args[ai]
+        num = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            old = x[idx]
+            x[idx] = old + eps
+            lp = _loss_tied(orc, *args, dy, dht)
+            x[idx] = old - eps
+            lm = _loss_tied(orc, *args, dy, dht)
+            x[idx] = old
+            num[idx] = (lp - lm) / (2 * eps)
+        assert rel(g, num) < 1e-7, ("input", ai, rel(g, num))
+
+
+def pin_tied_autograd(orc):
+    """Tied gradients against torch float64 autograd through a plain loop that
+    forms k = 1 - exp(log_f) itself."""
+    import torch
+    import oracle as o
+    q, _, v, lf, h0 = rand_inputs(19, B=2, T=11, H=2, DK=4, DV=3)
+    r = _rng(20)
+    dy = r.standard_normal(v.shape)
+    dht = r.standard_normal(h0.shape)
+    ts = [torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, v, lf, h0)]
+    tq, tv, tl, th = ts
+    tk = 1.0 - torch.exp(tl)
+    S = th
+    ys = []
+    for t in range(q.shape[1]):
+        S = torch.exp(tl[:, t])[..., :, None] * S + tk[:, t][..., :, None] * tv[:, t][..., None, :]
+        ys.append(torch.einsum("bhc,bhcj->bhj", tq[:, t], S))
+    Y = torch.stack(ys, dim=1)
+    L = (Y * torch.tensor(dy)).sum() + (S * torch.tensor(dht)).sum()
+    L.backward()
+    got = o.backward_tied(q, v, lf, dy, h0, dht)
+    for g, t in zip(got, ts):
+        assert rel(g, t.grad.numpy()) < 1e-12
+    y, ht = o.forward_tied(q, v, lf, h0)
+    assert rel(y, Y.detach().numpy()) < 1e-13 and rel(ht, S.detach().numpy()) < 1e-13
+
+
 ALL_PINS = [pin_closed_form, pin_limit_f_one, pin_limit_f_zero, pin_scalar_scan,
             pin_golden_exact, pin_linearity, pin_state_carry, pin_decode,
-            pin_finite_differences, pin_autograd, pin_dlogf_identity, pin_bwd_limits]
+            pin_finite_differences, pin_autograd, pin_dlogf_identity, pin_bwd_limits,
+            pin_tied_finite_differences, pin_tied_autograd]
