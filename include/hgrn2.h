@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define HGRN2_ABI_VERSION 3
+#define HGRN2_ABI_VERSION 4
 
 typedef enum {
   HGRN2_OK = 0,
@@ -191,6 +191,36 @@ hgrn2_status hgrn2_bwd_chunk(int B, int T, int H, int DK, int DV, int chunk, int
 hgrn2_status hgrn2_decode_step(int B, int H, int DK, int DV, int dtype, const void *q,
                                const void *k, const void *v, const void *log_f,
                                float *state, void *y, void *stream);
+
+/*
+ * Tied gates.  HGRN2 ties the input gate to the forget gate, k = 1 - f
+ * (HGRN2 summary §2.1 and §3.2 p.5).  These entry points take no k: the
+ * kernels form k = -expm1(log_f) from log_f itself (exact near f = 1), which
+ * saves one token tensor of reads per launch that used k.  The backward
+ * returns the total derivative with respect to log_f,
+ *     dlog_f = (partial through the decay) - exp(log_f) * (partial wrt k),
+ * and no dk.  Everything else (layouts, states, workspaces, errors) is as for
+ * the untied calls with the same names.
+ */
+hgrn2_status hgrn2_fwd_tied(int B, int T, int H, int DK, int DV, int chunk, int dtype,
+                            const void *q, const void *v, const void *log_f, const float *h0,
+                            void *y, float *ht, void *states_out, void *ws, size_t ws_bytes,
+                            void *stream);
+hgrn2_status hgrn2_bwd_tied(int B, int T, int H, int DK, int DV, int chunk, int dtype,
+                            const void *q, const void *v, const void *log_f, const float *h0,
+                            const void *states_in, const void *dy, const float *dht, void *dq,
+                            void *dv, void *dlog_f, float *dh0, void *ws, size_t ws_bytes,
+                            void *stream);
+hgrn2_status hgrn2_fwd_chunk_tied(int B, int T, int H, int DK, int DV, int chunk, int dtype,
+                                  const void *q, const void *v, const void *log_f,
+                                  const void *states, void *y, void *stream);
+hgrn2_status hgrn2_bwd_chunk_tied(int B, int T, int H, int DK, int DV, int chunk, int dtype,
+                                  const void *q, const void *v, const void *log_f,
+                                  const void *states, const void *adjoints, const void *dy,
+                                  void *dq, void *dv, void *dlog_f, void *stream);
+hgrn2_status hgrn2_decode_step_tied(int B, int H, int DK, int DV, int dtype, const void *q,
+                                    const void *v, const void *log_f, float *state, void *y,
+                                    void *stream);
 
 #ifdef __cplusplus
 }

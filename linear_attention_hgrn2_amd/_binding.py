@@ -64,6 +64,16 @@ def _lib():
         lib.hgrn2_bwd_adjoint.restype = I
         lib.hgrn2_bwd_chunk.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P]
         lib.hgrn2_bwd_chunk.restype = I
+        lib.hgrn2_fwd_tied.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, Z, P]
+        lib.hgrn2_fwd_tied.restype = I
+        lib.hgrn2_bwd_tied.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
+        lib.hgrn2_bwd_tied.restype = I
+        lib.hgrn2_fwd_chunk_tied.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P]
+        lib.hgrn2_fwd_chunk_tied.restype = I
+        lib.hgrn2_bwd_chunk_tied.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P]
+        lib.hgrn2_bwd_chunk_tied.restype = I
+        lib.hgrn2_decode_step_tied.argtypes = [I, I, I, I, I, P, P, P, P, P, P]
+        lib.hgrn2_decode_step_tied.restype = I
         lib.hgrn2_decode_step.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P]
         lib.hgrn2_decode_step.restype = I
         _handle = lib
@@ -270,6 +280,126 @@ def decode_step(q, k, v, log_f, state, *, y=None):
     st = _lib().hgrn2_decode_step(B, H, D, D, _DT[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(log_f),
                                   _ptr(state), _ptr(y), _stream())
     _check(st, "hgrn2_decode_step")
+    return y
+
+
+# ------------------------------------------------------------------ tied gates
+# k = 1 - exp(log_f) is formed in the kernels; the backward returns the total
+# derivative with respect to log_f and no dk.
+
+def fwd_tied(q, v, log_f, h0=None, *, chunk=64, want_ht=True, want_states=False, want_y=True,
+             y=None, ht=None, states=None, ws=None):
+    """Chunked forward with tied gates.  Returns (y or None, ht or None, states or None)."""
+    B, T, H, D = q.shape
+    dt = q.dtype
+    if dt not in _DT:
+        raise ValueError("dtype must be float32 or bfloat16")
+    for n, t in (("q", q), ("v", v), ("log_f", log_f)):
+        _tok(n, t, B, T, H, D, dt)
+    _st("h0", h0, B, H, D)
+    if want_y and y is None:
+        y = torch.empty_like(q)
+    if y is not None:
+        _tok("y", y, B, T, H, D, dt)
+    if want_ht and ht is None:
+        ht = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+    _st("ht", ht, B, H, D)
+    if want_states and states is None:
+        states = torch.empty(states_shape(B, T, H, D, chunk), dtype=dt, device=q.device)
+    if states is not None:
+        _states_ok(states, B, T, H, D, chunk, dt)
+    ws_bytes = 0
+    if states is None:
+        need = int(_lib().hgrn2_fwd_workspace_bytes(B, T, H, D, D, chunk, _DT[dt], 0))
+        if ws is None:
+            ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_bytes = ws.numel() * ws.element_size()
+    st = _lib().hgrn2_fwd_tied(B, T, H, D, D, chunk, _DT[dt], _ptr(q), _ptr(v), _ptr(log_f), _ptr(h0),
+                               _ptr(y), _ptr(ht), _ptr(states), _ptr(ws), ws_bytes, _stream())
+    _check(st, "hgrn2_fwd_tied")
+    return y, ht, states
+
+
+def bwd_tied(q, v, log_f, dy, h0=None, dht=None, states=None, *, chunk=64, want_dh0=True,
+             dq=None, dv=None, dlog_f=None, dh0=None, ws=None):
+    """Chunked backward with tied gates.  Returns (dq, dv, dlog_f total, dh0 or None)."""
+    B, T, H, D = q.shape
+    dt = q.dtype
+    for n, t in (("q", q), ("v", v), ("log_f", log_f), ("dy", dy)):
+        _tok(n, t, B, T, H, D, dt)
+    _st("h0", h0, B, H, D)
+    _st("dht", dht, B, H, D)
+    dq = torch.empty_like(q) if dq is None else dq
+    dv = torch.empty_like(v) if dv is None else dv
+    dlog_f = torch.empty_like(log_f) if dlog_f is None else dlog_f
+    for n, t in (("dq", dq), ("dv", dv), ("dlog_f", dlog_f)):
+        _tok(n, t, B, T, H, D, dt)
+    if want_dh0 and dh0 is None:
+        dh0 = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+    _st("dh0", dh0, B, H, D)
+    if states is not None:
+        _states_ok(states, B, T, H, D, chunk, dt)
+    need = int(_lib().hgrn2_bwd_workspace_bytes(B, T, H, D, D, chunk, _DT[dt], int(states is not None)))
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = ws.numel() * ws.element_size()
+    st = _lib().hgrn2_bwd_tied(B, T, H, D, D, chunk, _DT[dt], _ptr(q), _ptr(v), _ptr(log_f), _ptr(h0),
+                               _ptr(states), _ptr(dy), _ptr(dht), _ptr(dq), _ptr(dv), _ptr(dlog_f), _ptr(dh0),
+                               _ptr(ws), ws_bytes, _stream())
+    _check(st, "hgrn2_bwd_tied")
+    return dq, dv, dlog_f, dh0
+
+
+def fwd_chunk_tied(q, v, log_f, states, *, chunk=64, y=None):
+    """The per-chunk output launch of hgrn2_fwd_tied alone.  Returns y."""
+    B, T, H, D = q.shape
+    dt = q.dtype
+    for n, t in (("q", q), ("v", v), ("log_f", log_f)):
+        _tok(n, t, B, T, H, D, dt)
+    _states_ok(states, B, T, H, D, chunk, dt)
+    y = torch.empty_like(q) if y is None else y
+    _tok("y", y, B, T, H, D, dt)
+    st = _lib().hgrn2_fwd_chunk_tied(B, T, H, D, D, chunk, _DT[dt], _ptr(q), _ptr(v), _ptr(log_f),
+                                     _ptr(states), _ptr(y), _stream())
+    _check(st, "hgrn2_fwd_chunk_tied")
+    return y
+
+
+def bwd_chunk_tied(q, v, log_f, dy, states, adjoints, *, chunk=64, dq=None, dv=None, dlog_f=None):
+    """The per-chunk gradient launch of hgrn2_bwd_tied alone.  Returns (dq, dv, dlog_f total)."""
+    B, T, H, D = q.shape
+    dt = q.dtype
+    for n, t in (("q", q), ("v", v), ("log_f", log_f), ("dy", dy)):
+        _tok(n, t, B, T, H, D, dt)
+    _states_ok(states, B, T, H, D, chunk, dt)
+    if tuple(adjoints.shape) != adjoints_shape(B, T, H, D, chunk) or adjoints.dtype != dt \
+            or not adjoints.is_contiguous():
+        raise ValueError("adjoints: expected a contiguous %s tensor of shape %s"
+                         % (dt, adjoints_shape(B, T, H, D, chunk)))
+    dq = torch.empty_like(q) if dq is None else dq
+    dv = torch.empty_like(v) if dv is None else dv
+    dlog_f = torch.empty_like(log_f) if dlog_f is None else dlog_f
+    for n, t in (("dq", dq), ("dv", dv), ("dlog_f", dlog_f)):
+        _tok(n, t, B, T, H, D, dt)
+    st = _lib().hgrn2_bwd_chunk_tied(B, T, H, D, D, chunk, _DT[dt], _ptr(q), _ptr(v), _ptr(log_f), _ptr(states),
+                                     _ptr(adjoints), _ptr(dy), _ptr(dq), _ptr(dv), _ptr(dlog_f), _stream())
+    _check(st, "hgrn2_bwd_chunk_tied")
+    return dq, dv, dlog_f
+
+
+def decode_step_tied(q, v, log_f, state, *, y=None):
+    """One recurrent step with k = 1 - exp(log_f); `state` is updated in place.  Returns y."""
+    B, H, D = q.shape
+    dt = q.dtype
+    for n, t in (("q", q), ("v", v), ("log_f", log_f)):
+        if t.shape != (B, H, D) or t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s: expected a contiguous %s CUDA tensor of shape %s" % (n, dt, (B, H, D)))
+    _st("state", state, B, H, D)
+    if y is None:
+        y = torch.empty_like(q)
+    st = _lib().hgrn2_decode_step_tied(B, H, D, D, _DT[dt], _ptr(q), _ptr(v), _ptr(log_f), _ptr(state), _ptr(y),
+                                       _stream())
+    _check(st, "hgrn2_decode_step_tied")
     return y
 
 

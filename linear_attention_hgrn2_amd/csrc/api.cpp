@@ -89,14 +89,14 @@ hgrn2_status hip_status(hipError_t e, const char *what) {
   return fail(HGRN2_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-bool fwd_exists(int dtype, int D, int C) {
-  return hgrn2::dispatch_scan(dtype, D, C, false, nullptr, nullptr) == hipSuccess &&
-         hgrn2::dispatch_scan(dtype, D, C, true, nullptr, nullptr) == hipSuccess &&
-         hgrn2::dispatch_chunk_fwd(dtype, D, C, nullptr, nullptr) == hipSuccess;
+bool fwd_exists(int dtype, int D, int C, bool tied = false) {
+  return hgrn2::dispatch_scan(dtype, D, C, false, tied, nullptr, nullptr) == hipSuccess &&
+         hgrn2::dispatch_scan(dtype, D, C, true, false, nullptr, nullptr) == hipSuccess &&
+         hgrn2::dispatch_chunk_fwd(dtype, D, C, tied, nullptr, nullptr) == hipSuccess;
 }
 
-bool bwd_exists(int dtype, int D, int C) {
-  return hgrn2::dispatch_chunk_bwd(dtype, D, C, nullptr, nullptr) == hipSuccess;
+bool bwd_exists(int dtype, int D, int C, bool tied = false) {
+  return hgrn2::dispatch_chunk_bwd(dtype, D, C, tied, nullptr, nullptr) == hipSuccess;
 }
 
 // bytes of the state adjoints at every chunk end, [B, H, N, DK, DV] in the input dtype
@@ -105,7 +105,7 @@ size_t adjoint_bytes(int B, int T, int H, int DK, int DV, int chunk, int dtype) 
 }
 
 
-hgrn2_status launch_scan(int dtype, int D, int chunk, bool reverse, int B, int T, int H, const void *x,
+hgrn2_status launch_scan(int dtype, int D, int chunk, bool reverse, bool tied, int B, int T, int H, const void *x,
                          const void *z, const void *log_f, const float *s_in, void *states, float *s_out,
                          void *stream, const char *what) {
   hgrn2::ScanArgs sa;
@@ -119,10 +119,10 @@ hgrn2_status launch_scan(int dtype, int D, int chunk, bool reverse, int B, int T
   sa.s_in = s_in;
   sa.states = states;
   sa.s_out = s_out;
-  return hip_status(hgrn2::dispatch_scan(dtype, D, chunk, reverse, &sa, (hipStream_t)stream), what);
+  return hip_status(hgrn2::dispatch_scan(dtype, D, chunk, reverse, tied, &sa, (hipStream_t)stream), what);
 }
 
-hgrn2_status launch_chunk_fwd(int dtype, int D, int chunk, int B, int T, int H, const void *q, const void *k,
+hgrn2_status launch_chunk_fwd(int dtype, int D, int chunk, bool tied, int B, int T, int H, const void *q, const void *k,
                               const void *v, const void *log_f, const void *states, void *y, void *stream,
                               const char *what) {
   hgrn2::ChunkFwdArgs ca;
@@ -136,10 +136,10 @@ hgrn2_status launch_chunk_fwd(int dtype, int D, int chunk, int B, int T, int H, 
   ca.log_f = log_f;
   ca.states = states;
   ca.y = y;
-  return hip_status(hgrn2::dispatch_chunk_fwd(dtype, D, chunk, &ca, (hipStream_t)stream), what);
+  return hip_status(hgrn2::dispatch_chunk_fwd(dtype, D, chunk, tied, &ca, (hipStream_t)stream), what);
 }
 
-hgrn2_status launch_chunk_bwd(int dtype, int D, int chunk, int B, int T, int H, const void *q, const void *k,
+hgrn2_status launch_chunk_bwd(int dtype, int D, int chunk, bool tied, int B, int T, int H, const void *q, const void *k,
                               const void *v, const void *log_f, const void *dy, const void *states,
                               const void *lam, void *dq, void *dk, void *dv, void *dlog_f, void *stream,
                               const char *what) {
@@ -159,7 +159,7 @@ hgrn2_status launch_chunk_bwd(int dtype, int D, int chunk, int B, int T, int H, 
   a.dk = dk;
   a.dv = dv;
   a.dlog_f = dlog_f;
-  return hip_status(hgrn2::dispatch_chunk_bwd(dtype, D, chunk, &a, (hipStream_t)stream), what);
+  return hip_status(hgrn2::dispatch_chunk_bwd(dtype, D, chunk, tied, &a, (hipStream_t)stream), what);
 }
 
 }  // namespace
@@ -209,15 +209,25 @@ size_t hgrn2_bwd_workspace_bytes(int B, int T, int H, int DK, int DV, int chunk,
          (have_states ? 0 : hgrn2_states_bytes(B, T, H, DK, DV, chunk, dtype));
 }
 
-hgrn2_status hgrn2_fwd(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
-                       const void *k, const void *v, const void *log_f, const float *h0, void *y,
-                       float *ht, void *states_out, void *ws, size_t ws_bytes, void *stream) {
+// ---- implementations shared by the independent-gate and tied-gate entry
+// points.  tied: k = 1 - exp(log f) is formed in the kernels (k is NULL), and
+// the backward writes the total dlog f and no dk (dk is NULL).
+
+static hgrn2_status need_k(bool tied, const void *k, const char *name) {
+  if (tied) return HGRN2_OK;
+  return check_ptrs({{name, k}}, {});
+}
+
+static hgrn2_status fwd_impl(bool tied, const char *fn, int B, int T, int H, int DK, int DV, int chunk, int dtype,
+                             const void *q, const void *k, const void *v, const void *log_f, const float *h0,
+                             void *y, float *ht, void *states_out, void *ws, size_t ws_bytes, void *stream) {
   hgrn2_status st = check_common(B, T, H, DK, DV, chunk, dtype);
   if (st != HGRN2_OK) return st;
-  st = check_ptrs({{"q", q}, {"k", k}, {"v", v}, {"log_f", log_f}},
+  st = check_ptrs({{"q", q}, {"v", v}, {"log_f", log_f}},
                   {{"h0", h0}, {"y", y}, {"ht", ht}, {"states_out", states_out}, {"ws", ws}});
+  if (st == HGRN2_OK) st = need_k(tied, k, "k");
   if (st != HGRN2_OK) return st;
-  if (!fwd_exists(dtype, DK, chunk))
+  if (!fwd_exists(dtype, DK, chunk, tied))
     return fail(HGRN2_ERR_UNSUPPORTED, "no forward kernel for this D, chunk and dtype");
   const size_t tok = (size_t)B * T * H * DK * dsize(dtype);
   const size_t sb = (size_t)B * H * DK * DV * sizeof(float);
@@ -230,7 +240,7 @@ hgrn2_status hgrn2_fwd(int B, int T, int H, int DK, int DV, int chunk, int dtype
   }
   // ht may be exactly h0 (each workgroup reads its slice of h0 before it
   // writes the same slice of ht); any other overlap is an error.
-  const Range ins[] = {{"q", q, tok}, {"k", k, tok}, {"v", v, tok}, {"log_f", log_f, tok},
+  const Range ins[] = {{"q", q, tok}, {"k", tied ? nullptr : k, tok}, {"v", v, tok}, {"log_f", log_f, tok},
                        {"h0", (ht == h0) ? nullptr : h0, sb}};
   const Range outs[] = {{"y", y, tok}, {"ht", ht, sb}, {states_out ? "states_out" : "ws", states, stb}};
   std::string msg;
@@ -239,25 +249,24 @@ hgrn2_status hgrn2_fwd(int B, int T, int H, int DK, int DV, int chunk, int dtype
                          overlap(Range{"states", states, stb}, Range{"h0", h0, sb})))
     return fail(HGRN2_ERR_INVALID_ARG, "an output overlaps h0");
 
-  st = launch_scan(dtype, DK, chunk, false, B, T, H, k, v, log_f, h0, states, ht, stream,
-                   "hgrn2_fwd (state scan)");
+  st = launch_scan(dtype, DK, chunk, false, tied, B, T, H, tied ? nullptr : k, v, log_f, h0, states, ht, stream,
+                   fn);
   if (st != HGRN2_OK || !y) return st;
-  return launch_chunk_fwd(dtype, DK, chunk, B, T, H, q, k, v, log_f, states, y, stream,
-                          "hgrn2_fwd (chunk outputs)");
+  return launch_chunk_fwd(dtype, DK, chunk, tied, B, T, H, q, tied ? nullptr : k, v, log_f, states, y, stream, fn);
 }
 
-hgrn2_status hgrn2_bwd(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
-                       const void *k, const void *v, const void *log_f, const float *h0,
-                       const void *states_in, const void *dy, const float *dht, void *dq,
-                       void *dk, void *dv, void *dlog_f, float *dh0, void *ws, size_t ws_bytes,
-                       void *stream) {
+static hgrn2_status bwd_impl(bool tied, const char *fn, int B, int T, int H, int DK, int DV, int chunk, int dtype,
+                             const void *q, const void *k, const void *v, const void *log_f, const float *h0,
+                             const void *states_in, const void *dy, const float *dht, void *dq, void *dk, void *dv,
+                             void *dlog_f, float *dh0, void *ws, size_t ws_bytes, void *stream) {
   hgrn2_status st = check_common(B, T, H, DK, DV, chunk, dtype);
   if (st != HGRN2_OK) return st;
-  st = check_ptrs({{"q", q}, {"k", k}, {"v", v}, {"log_f", log_f}, {"dy", dy}, {"dq", dq},
-                   {"dk", dk}, {"dv", dv}, {"dlog_f", dlog_f}},
+  st = check_ptrs({{"q", q}, {"v", v}, {"log_f", log_f}, {"dy", dy}, {"dq", dq}, {"dv", dv}, {"dlog_f", dlog_f}},
                   {{"h0", h0}, {"states_in", states_in}, {"dht", dht}, {"dh0", dh0}, {"ws", ws}});
+  if (st == HGRN2_OK) st = need_k(tied, k, "k");
+  if (st == HGRN2_OK) st = need_k(tied, dk, "dk");
   if (st != HGRN2_OK) return st;
-  if (!bwd_exists(dtype, DK, chunk) || !fwd_exists(dtype, DK, chunk))
+  if (!bwd_exists(dtype, DK, chunk, tied) || !fwd_exists(dtype, DK, chunk, tied))
     return fail(HGRN2_ERR_UNSUPPORTED, "no backward kernel for this D, chunk and dtype");
   const size_t tok = (size_t)B * T * H * DK * dsize(dtype);
   const size_t sb = (size_t)B * H * DK * DV * sizeof(float);
@@ -266,6 +275,7 @@ hgrn2_status hgrn2_bwd(int B, int T, int H, int DK, int DV, int chunk, int dtype
   const size_t need = lamb + (states_in ? 0 : stb);
   if (!ws || ws_bytes < need)
     return fail(HGRN2_ERR_WORKSPACE, "workspace smaller than hgrn2_bwd_workspace_bytes()");
+  if (tied) k = dk = nullptr;
   const void *states = states_in;
   const Range ins[] = {{"q", q, tok},   {"k", k, tok},   {"v", v, tok},          {"log_f", log_f, tok},
                        {"h0", h0, sb},  {"dy", dy, tok}, {"dht", dht, sb},       {"states_in", states_in, stb}};
@@ -277,69 +287,52 @@ hgrn2_status hgrn2_bwd(int B, int T, int H, int DK, int DV, int chunk, int dtype
   if (!states) {
     // recompute the chunk-boundary states with the forward state scan
     void *sws = (char *)ws + lamb;
-    st = launch_scan(dtype, DK, chunk, false, B, T, H, k, v, log_f, h0, sws, nullptr, stream,
-                     "hgrn2_bwd (state recompute)");
+    st = launch_scan(dtype, DK, chunk, false, tied, B, T, H, k, v, log_f, h0, sws, nullptr, stream, fn);
     if (st != HGRN2_OK) return st;
     states = sws;
   }
   // the state adjoint at every chunk end (reverse scan), then all chunks' gradients
-  st = launch_scan(dtype, DK, chunk, true, B, T, H, q, dy, log_f, dht, ws, dh0, stream,
-                   "hgrn2_bwd (adjoint scan)");
+  st = launch_scan(dtype, DK, chunk, true, false, B, T, H, q, dy, log_f, dht, ws, dh0, stream, fn);
   if (st != HGRN2_OK) return st;
-  return launch_chunk_bwd(dtype, DK, chunk, B, T, H, q, k, v, log_f, dy, states, ws, dq, dk, dv, dlog_f,
-                          stream, "hgrn2_bwd (chunk gradients)");
+  return launch_chunk_bwd(dtype, DK, chunk, tied, B, T, H, q, k, v, log_f, dy, states, ws, dq, dk, dv, dlog_f,
+                          stream, fn);
 }
 
-hgrn2_status hgrn2_fwd_chunk(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
-                             const void *k, const void *v, const void *log_f, const void *states, void *y,
-                             void *stream) {
+static hgrn2_status fwd_chunk_impl(bool tied, const char *fn, int B, int T, int H, int DK, int DV, int chunk,
+                                   int dtype, const void *q, const void *k, const void *v, const void *log_f,
+                                   const void *states, void *y, void *stream) {
   hgrn2_status st = check_common(B, T, H, DK, DV, chunk, dtype);
   if (st != HGRN2_OK) return st;
-  st = check_ptrs({{"q", q}, {"k", k}, {"v", v}, {"log_f", log_f}, {"states", states}, {"y", y}}, {});
+  st = check_ptrs({{"q", q}, {"v", v}, {"log_f", log_f}, {"states", states}, {"y", y}}, {});
+  if (st == HGRN2_OK) st = need_k(tied, k, "k");
   if (st != HGRN2_OK) return st;
-  if (hgrn2::dispatch_chunk_fwd(dtype, DK, chunk, nullptr, nullptr) != hipSuccess)
+  if (hgrn2::dispatch_chunk_fwd(dtype, DK, chunk, tied, nullptr, nullptr) != hipSuccess)
     return fail(HGRN2_ERR_UNSUPPORTED, "no forward kernel for this D, chunk and dtype");
+  if (tied) k = nullptr;
   const size_t tok = (size_t)B * T * H * DK * dsize(dtype);
   const size_t stb = hgrn2_states_bytes(B, T, H, DK, DV, chunk, dtype);
   const Range ins[] = {{"q", q, tok}, {"k", k, tok}, {"v", v, tok}, {"log_f", log_f, tok}, {"states", states, stb}};
   const Range outs[] = {{"y", y, tok}};
   std::string msg;
   if (!check_aliasing(ins, 5, outs, 1, msg)) return fail(HGRN2_ERR_INVALID_ARG, msg);
-  return launch_chunk_fwd(dtype, DK, chunk, B, T, H, q, k, v, log_f, states, y, stream, "hgrn2_fwd_chunk");
+  return launch_chunk_fwd(dtype, DK, chunk, tied, B, T, H, q, k, v, log_f, states, y, stream, fn);
 }
 
-hgrn2_status hgrn2_bwd_adjoint(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
-                               const void *log_f, const void *dy, const float *dht, void *adjoints, float *dh0,
-                               void *stream) {
+static hgrn2_status bwd_chunk_impl(bool tied, const char *fn, int B, int T, int H, int DK, int DV, int chunk,
+                                   int dtype, const void *q, const void *k, const void *v, const void *log_f,
+                                   const void *states, const void *adjoints, const void *dy, void *dq, void *dk,
+                                   void *dv, void *dlog_f, void *stream) {
   hgrn2_status st = check_common(B, T, H, DK, DV, chunk, dtype);
   if (st != HGRN2_OK) return st;
-  st = check_ptrs({{"q", q}, {"log_f", log_f}, {"dy", dy}, {"adjoints", adjoints}}, {{"dht", dht}, {"dh0", dh0}});
-  if (st != HGRN2_OK) return st;
-  if (hgrn2::dispatch_scan(dtype, DK, chunk, true, nullptr, nullptr) != hipSuccess)
-    return fail(HGRN2_ERR_UNSUPPORTED, "no adjoint scan kernel for this D, chunk and dtype");
-  const size_t tok = (size_t)B * T * H * DK * dsize(dtype);
-  const size_t sb = (size_t)B * H * DK * DV * sizeof(float);
-  const size_t lamb = adjoint_bytes(B, T, H, DK, DV, chunk, dtype);
-  const Range ins[] = {{"q", q, tok}, {"log_f", log_f, tok}, {"dy", dy, tok}, {"dht", dht, sb}};
-  const Range outs[] = {{"adjoints", adjoints, lamb}, {"dh0", dh0, sb}};
-  std::string msg;
-  if (!check_aliasing(ins, 4, outs, 2, msg)) return fail(HGRN2_ERR_INVALID_ARG, msg);
-  return launch_scan(dtype, DK, chunk, true, B, T, H, q, dy, log_f, dht, adjoints, dh0, stream,
-                     "hgrn2_bwd_adjoint");
-}
-
-hgrn2_status hgrn2_bwd_chunk(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
-                             const void *k, const void *v, const void *log_f, const void *states,
-                             const void *adjoints, const void *dy, void *dq, void *dk, void *dv, void *dlog_f,
-                             void *stream) {
-  hgrn2_status st = check_common(B, T, H, DK, DV, chunk, dtype);
-  if (st != HGRN2_OK) return st;
-  st = check_ptrs({{"q", q}, {"k", k}, {"v", v}, {"log_f", log_f}, {"states", states}, {"adjoints", adjoints},
-                   {"dy", dy}, {"dq", dq}, {"dk", dk}, {"dv", dv}, {"dlog_f", dlog_f}},
+  st = check_ptrs({{"q", q}, {"v", v}, {"log_f", log_f}, {"states", states}, {"adjoints", adjoints}, {"dy", dy},
+                   {"dq", dq}, {"dv", dv}, {"dlog_f", dlog_f}},
                   {});
+  if (st == HGRN2_OK) st = need_k(tied, k, "k");
+  if (st == HGRN2_OK) st = need_k(tied, dk, "dk");
   if (st != HGRN2_OK) return st;
-  if (!bwd_exists(dtype, DK, chunk))
+  if (!bwd_exists(dtype, DK, chunk, tied))
     return fail(HGRN2_ERR_UNSUPPORTED, "no backward kernel for this D, chunk and dtype");
+  if (tied) k = dk = nullptr;
   const size_t tok = (size_t)B * T * H * DK * dsize(dtype);
   const size_t stb = hgrn2_states_bytes(B, T, H, DK, DV, chunk, dtype);
   const size_t lamb = adjoint_bytes(B, T, H, DK, DV, chunk, dtype);
@@ -349,18 +342,21 @@ hgrn2_status hgrn2_bwd_chunk(int B, int T, int H, int DK, int DV, int chunk, int
   const Range outs[] = {{"dq", dq, tok}, {"dk", dk, tok}, {"dv", dv, tok}, {"dlog_f", dlog_f, tok}};
   std::string msg;
   if (!check_aliasing(ins, 7, outs, 4, msg)) return fail(HGRN2_ERR_INVALID_ARG, msg);
-  return launch_chunk_bwd(dtype, DK, chunk, B, T, H, q, k, v, log_f, dy, states, adjoints, dq, dk, dv, dlog_f,
-                          stream, "hgrn2_bwd_chunk");
+  return launch_chunk_bwd(dtype, DK, chunk, tied, B, T, H, q, k, v, log_f, dy, states, adjoints, dq, dk, dv,
+                          dlog_f, stream, fn);
 }
 
-hgrn2_status hgrn2_decode_step(int B, int H, int DK, int DV, int dtype, const void *q, const void *k,
-                               const void *v, const void *log_f, float *state, void *y, void *stream) {
+static hgrn2_status decode_impl(bool tied, const char *fn, int B, int H, int DK, int DV, int dtype, const void *q,
+                                const void *k, const void *v, const void *log_f, float *state, void *y,
+                                void *stream) {
   if (B <= 0 || H <= 0) return fail(HGRN2_ERR_INVALID_ARG, "B and H must be >= 1");
   if ((long long)B * H > (1LL << 30)) return fail(HGRN2_ERR_INVALID_ARG, "problem too large");
   if (!valid_dtype(dtype)) return fail(HGRN2_ERR_INVALID_ARG, "dtype must be HGRN2_F32 or HGRN2_BF16");
   if (DK != DV || !valid_d(DK)) return fail(HGRN2_ERR_UNSUPPORTED, "need DK == DV in {16, 32, 64, 128}");
-  hgrn2_status st = check_ptrs({{"q", q}, {"k", k}, {"v", v}, {"log_f", log_f}, {"state", state}, {"y", y}}, {});
+  hgrn2_status st = check_ptrs({{"q", q}, {"v", v}, {"log_f", log_f}, {"state", state}, {"y", y}}, {});
+  if (st == HGRN2_OK) st = need_k(tied, k, "k");
   if (st != HGRN2_OK) return st;
+  if (tied) k = nullptr;
   const size_t vec = (size_t)B * H * DK * dsize(dtype);
   const size_t sb = (size_t)B * H * DK * DV * sizeof(float);
   const Range ins[] = {{"q", q, vec}, {"k", k, vec}, {"v", v, vec}, {"log_f", log_f, vec}};
@@ -376,7 +372,100 @@ hgrn2_status hgrn2_decode_step(int B, int H, int DK, int DV, int dtype, const vo
   a.log_f = log_f;
   a.state = state;
   a.y = y;
-  return hip_status(hgrn2::dispatch_decode(dtype, DK, a, (hipStream_t)stream), "hgrn2_decode_step");
+  return hip_status(hgrn2::dispatch_decode(dtype, DK, tied, a, (hipStream_t)stream), fn);
+}
+
+// ---- independent gates
+
+hgrn2_status hgrn2_fwd(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
+                       const void *k, const void *v, const void *log_f, const float *h0, void *y,
+                       float *ht, void *states_out, void *ws, size_t ws_bytes, void *stream) {
+  return fwd_impl(false, "hgrn2_fwd", B, T, H, DK, DV, chunk, dtype, q, k, v, log_f, h0, y, ht, states_out, ws,
+                  ws_bytes, stream);
+}
+
+hgrn2_status hgrn2_bwd(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
+                       const void *k, const void *v, const void *log_f, const float *h0,
+                       const void *states_in, const void *dy, const float *dht, void *dq,
+                       void *dk, void *dv, void *dlog_f, float *dh0, void *ws, size_t ws_bytes,
+                       void *stream) {
+  return bwd_impl(false, "hgrn2_bwd", B, T, H, DK, DV, chunk, dtype, q, k, v, log_f, h0, states_in, dy, dht, dq, dk,
+                  dv, dlog_f, dh0, ws, ws_bytes, stream);
+}
+
+hgrn2_status hgrn2_fwd_chunk(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
+                             const void *k, const void *v, const void *log_f, const void *states, void *y,
+                             void *stream) {
+  return fwd_chunk_impl(false, "hgrn2_fwd_chunk", B, T, H, DK, DV, chunk, dtype, q, k, v, log_f, states, y,
+                        stream);
+}
+
+hgrn2_status hgrn2_bwd_adjoint(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
+                               const void *log_f, const void *dy, const float *dht, void *adjoints, float *dh0,
+                               void *stream) {
+  hgrn2_status st = check_common(B, T, H, DK, DV, chunk, dtype);
+  if (st != HGRN2_OK) return st;
+  st = check_ptrs({{"q", q}, {"log_f", log_f}, {"dy", dy}, {"adjoints", adjoints}}, {{"dht", dht}, {"dh0", dh0}});
+  if (st != HGRN2_OK) return st;
+  if (hgrn2::dispatch_scan(dtype, DK, chunk, true, false, nullptr, nullptr) != hipSuccess)
+    return fail(HGRN2_ERR_UNSUPPORTED, "no adjoint scan kernel for this D, chunk and dtype");
+  const size_t tok = (size_t)B * T * H * DK * dsize(dtype);
+  const size_t sb = (size_t)B * H * DK * DV * sizeof(float);
+  const size_t lamb = adjoint_bytes(B, T, H, DK, DV, chunk, dtype);
+  const Range ins[] = {{"q", q, tok}, {"log_f", log_f, tok}, {"dy", dy, tok}, {"dht", dht, sb}};
+  const Range outs[] = {{"adjoints", adjoints, lamb}, {"dh0", dh0, sb}};
+  std::string msg;
+  if (!check_aliasing(ins, 4, outs, 2, msg)) return fail(HGRN2_ERR_INVALID_ARG, msg);
+  return launch_scan(dtype, DK, chunk, true, false, B, T, H, q, dy, log_f, dht, adjoints, dh0, stream,
+                     "hgrn2_bwd_adjoint");
+}
+
+hgrn2_status hgrn2_bwd_chunk(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
+                             const void *k, const void *v, const void *log_f, const void *states,
+                             const void *adjoints, const void *dy, void *dq, void *dk, void *dv, void *dlog_f,
+                             void *stream) {
+  return bwd_chunk_impl(false, "hgrn2_bwd_chunk", B, T, H, DK, DV, chunk, dtype, q, k, v, log_f, states, adjoints,
+                        dy, dq, dk, dv, dlog_f, stream);
+}
+
+hgrn2_status hgrn2_decode_step(int B, int H, int DK, int DV, int dtype, const void *q, const void *k,
+                               const void *v, const void *log_f, float *state, void *y, void *stream) {
+  return decode_impl(false, "hgrn2_decode_step", B, H, DK, DV, dtype, q, k, v, log_f, state, y, stream);
+}
+
+// ---- tied gates (k = 1 - exp(log f))
+
+hgrn2_status hgrn2_fwd_tied(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
+                            const void *v, const void *log_f, const float *h0, void *y, float *ht,
+                            void *states_out, void *ws, size_t ws_bytes, void *stream) {
+  return fwd_impl(true, "hgrn2_fwd_tied", B, T, H, DK, DV, chunk, dtype, q, nullptr, v, log_f, h0, y, ht,
+                  states_out, ws, ws_bytes, stream);
+}
+
+hgrn2_status hgrn2_bwd_tied(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
+                            const void *v, const void *log_f, const float *h0, const void *states_in,
+                            const void *dy, const float *dht, void *dq, void *dv, void *dlog_f, float *dh0,
+                            void *ws, size_t ws_bytes, void *stream) {
+  return bwd_impl(true, "hgrn2_bwd_tied", B, T, H, DK, DV, chunk, dtype, q, nullptr, v, log_f, h0, states_in, dy,
+                  dht, dq, nullptr, dv, dlog_f, dh0, ws, ws_bytes, stream);
+}
+
+hgrn2_status hgrn2_fwd_chunk_tied(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
+                                  const void *v, const void *log_f, const void *states, void *y, void *stream) {
+  return fwd_chunk_impl(true, "hgrn2_fwd_chunk_tied", B, T, H, DK, DV, chunk, dtype, q, nullptr, v, log_f, states,
+                        y, stream);
+}
+
+hgrn2_status hgrn2_bwd_chunk_tied(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
+                                  const void *v, const void *log_f, const void *states, const void *adjoints,
+                                  const void *dy, void *dq, void *dv, void *dlog_f, void *stream) {
+  return bwd_chunk_impl(true, "hgrn2_bwd_chunk_tied", B, T, H, DK, DV, chunk, dtype, q, nullptr, v, log_f, states,
+                        adjoints, dy, dq, nullptr, dv, dlog_f, stream);
+}
+
+hgrn2_status hgrn2_decode_step_tied(int B, int H, int DK, int DV, int dtype, const void *q, const void *v,
+                                    const void *log_f, float *state, void *y, void *stream) {
+  return decode_impl(true, "hgrn2_decode_step_tied", B, H, DK, DV, dtype, q, nullptr, v, log_f, state, y, stream);
 }
 
 }  // extern "C"

@@ -16,7 +16,8 @@
 // qo, ko and the gaps.  dlog f uses qo dq' - ko dk' with the same rounded qo,
 // ko that entered the products, so the terms that cancel in exact arithmetic
 // cancel here too.  A diagonal block whose decay exceeds kDiagLimit nats is
-// summed directly.
+// summed directly.  With tied gates (k = 1 - f) k is formed from log f,
+// dk is not written, and dlog f is the total derivative dlog f - f dk.
 //
 // One workgroup per (batch, head, chunk); wave w owns 16-token sub-block w and
 // produces all its outputs.  Phases: products from LDS tiles of qo, ko, v, dy
@@ -76,7 +77,7 @@ template <typename T, int D, int C> struct CbwdCfg {
   };
 };
 
-template <typename T, int D, int C>
+template <typename T, int D, int C, bool TIED>
 __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void hgrn2_chunk_bwd_kernel(ChunkBwdArgs a) {
   using Cfg = CbwdCfg<T, D, C>;
   constexpr int NW = Cfg::NW, NT = Cfg::NT, NB = Cfg::NB, CPL = Cfg::CPL, CB = Cfg::CB, KSD = Cfg::KSD,
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       pq[t] = ldtok(bq, 16 * w + t);
-      pk[t] = ldtok(bk, 16 * w + t);
+      if constexpr (!TIED) pk[t] = ldtok(bk, 16 * w + t);
       pl[t] = ldtok(bl, 16 * w + t);
     }
     float l[16][CPL], L[CPL];
@@ -148,7 +149,7 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
         for (int e = 0; e < CPL; ++e) {
           oq.v[e] = from_f32<T>(to_f32(pq[t].v[e]) * __expf(l[t][e]));
-          ok.v[e] = from_f32<T>(to_f32(pk[t].v[e]) * __expf(L[e] - l[t][e]));
+          ok.v[e] = from_f32<T>(k_of<TIED>(pk[t].v[e], pl[t].v[e]) * __expf(L[e] - l[t][e]));
         }
         stpack<T, CPL>(&sm.u.in.qo[XT::at(16 * w + t, c0)], oq);
         stpack<T, CPL>(&sm.u.in.ko[XT::at(16 * w + t, c0)], ok);
@@ -306,11 +307,12 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
         for (int s = t; s >= 0; --s) {
           float part = 0.f;
           if (tv_) {
-            const Pack<T, CPL> pk = bk.template ldpack<T, CPL>(tok(16 * w + s) + c0b);
+            Pack<T, CPL> pk;
+            if constexpr (!TIED) pk = bk.template ldpack<T, CPL>(tok(16 * w + s) + c0b);
             const Pack<T, CPL> pl = bl.template ldpack<T, CPL>(tok(16 * w + s) + c0b);
 #pragma unroll
             for (int e = 0; e < CPL; ++e) {
-              part += qt[e] * to_f32(pk.v[e]) * __expf(ex[e]);
+              part += qt[e] * k_of<TIED>(pk.v[e], pl.v[e]) * __expf(ex[e]);
               ex[e] += floor_logf(to_f32(pl.v[e]));
             }
           }
@@ -473,22 +475,26 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       const int tt = 16 * w + t;
-      const Pack<T, CPL> pq = ldtok(bq, tt), pk = ldtok(bk, tt);
+      const Pack<T, CPL> pq = ldtok(bq, tt);
+      Pack<T, CPL> pk;
+      if constexpr (!TIED) pk = ldtok(bk, tt);
       Pack<T, CPL> oq, ok;
 #pragma unroll
       for (int e = 0; e < CPL; ++e) {
         ell[e] += floor_logf(to_f32(pl[t].v[e]));
         const float el = __expf(ell[e]), ek = __expf(L[e] - ell[e]);
         const float qor = to_f32(from_f32<T>(to_f32(pq.v[e]) * el));
-        const float kor = to_f32(from_f32<T>(to_f32(pk.v[e]) * ek));
+        const float kor = to_f32(from_f32<T>(k_of<TIED>(pk.v[e], pl[t].v[e]) * ek));
         const float d1 = sq[t * LDG + c0 + e], d2 = sk[t * LDG + c0 + e];
         oq.v[e] = from_f32<T>(el * d1);
         ok.v[e] = from_f32<T>(ek * d2);
         X[t][e] = qor * d1 - kor * d2;
+        // tied gates: f dk, subtracted from dlog f below (replaces the consumed dk'_t)
+        if (TIED && has_ch) sk[t * LDG + c0 + e] = __expf(floor_logf(to_f32(pl[t].v[e]))) * (ek * d2);
       }
       if (has_ch) {
         bdq.stpack<T, CPL>(tok(tt) + c0b, oq);
-        bdk.stpack<T, CPL>(tok(tt) + c0b, ok);
+        if constexpr (!TIED) bdk.stpack<T, CPL>(tok(tt) + c0b, ok);
       }
     }
     if (has_ch) {
@@ -513,7 +519,9 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
     }
     for (int t = 0; t < 16; ++t) {
       const int tt = 16 * w + t;
-      const Pack<T, CPL> pq = ldtok(bq, tt), pk = ldtok(bk, tt), plt = ldtok(bl, tt);
+      const Pack<T, CPL> pq = ldtok(bq, tt), plt = ldtok(bl, tt);
+      Pack<T, CPL> pk;
+      if constexpr (!TIED) pk = ldtok(bk, tt);
       const Pack<T, CPL> pdy = ldtok(bdy, tt), pv = ldtok(bv, tt);
       float dqd[CPL], dkd[CPL], ex[CPL];
 #pragma unroll
@@ -522,15 +530,16 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
         dqd[e] = dkd[e] = ex[e] = 0.f;
       }
       for (int s_ = t; s_ >= 0; --s_) {
-        const Pack<T, CPL> pvs = ldtok(bv, 16 * w + s_), pks = ldtok(bk, 16 * w + s_);
-        const Pack<T, CPL> pls = ldtok(bl, 16 * w + s_);
+        const Pack<T, CPL> pvs = ldtok(bv, 16 * w + s_), pls = ldtok(bl, 16 * w + s_);
+        Pack<T, CPL> pks;
+        if constexpr (!TIED) pks = ldtok(bk, 16 * w + s_);
         float part = 0.f;
 #pragma unroll
         for (int e = 0; e < CPL; ++e) part += to_f32(pdy.v[e]) * to_f32(pvs.v[e]);
         const float dA = wave_sum(part);
 #pragma unroll
         for (int e = 0; e < CPL; ++e) {
-          dqd[e] += dA * to_f32(pks.v[e]) * __expf(ex[e]);
+          dqd[e] += dA * k_of<TIED>(pks.v[e], pls.v[e]) * __expf(ex[e]);
           ex[e] += floor_logf(to_f32(pls.v[e]));
         }
       }
@@ -554,18 +563,19 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
       for (int e = 0; e < CPL; ++e) {
         const float el = __expf(ell[e]), ek = __expf(L[e] - ell[e]);
-        const float qv = to_f32(pq.v[e]), kv = to_f32(pk.v[e]);
+        const float qv = to_f32(pq.v[e]), kv = k_of<TIED>(pk.v[e], plt.v[e]);
         const float qor = to_f32(from_f32<T>(qv * el)), kor = to_f32(from_f32<T>(kv * ek));
         const float d1 = sq[t * LDG + c0 + e], d2 = sk[t * LDG + c0 + e];
         oq.v[e] = from_f32<T>(el * d1 + dqd[e]);
         ok.v[e] = from_f32<T>(ek * d2 + dkd[e]);
         const float x = (qor * d1 + qv * dqd[e]) - (kor * d2 + kv * dkd[e]);
         if (has_ch) sq[t * LDG + c0 + e] = x;  // X_t replaces the consumed dq'_t
+        if (TIED && has_ch) sk[t * LDG + c0 + e] = __expf(floor_logf(to_f32(plt.v[e]))) * (ek * d2 + dkd[e]);
         tot[e] += x;
       }
       if (has_ch) {
         bdq.stpack<T, CPL>(tok(tt) + c0b, oq);
-        bdk.stpack<T, CPL>(tok(tt) + c0b, ok);
+        if constexpr (!TIED) bdk.stpack<T, CPL>(tok(tt) + c0b, ok);
       }
     }
     if (has_ch)
@@ -590,7 +600,7 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
         for (int e = 0; e < CPL; ++e) {
           carry[e] += X[t][e];
-          o.v[e] = from_f32<T>(carry[e]);
+          o.v[e] = from_f32<T>(TIED ? carry[e] - sk[t * LDG + c0 + e] : carry[e]);
         }
         bdl.stpack<T, CPL>(tok(tt) + c0b, o);
       }
@@ -601,7 +611,7 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
         for (int e = 0; e < CPL; ++e) {
           carry[e] += sq[t * LDG + c0 + e];
-          o.v[e] = from_f32<T>(carry[e]);
+          o.v[e] = from_f32<T>(TIED ? carry[e] - sk[t * LDG + c0 + e] : carry[e]);
         }
         bdl.stpack<T, CPL>(tok(tt) + c0b, o);
       }
@@ -609,10 +619,10 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
   }
 }
 
-template <typename T, int D, int C>
+template <typename T, int D, int C, bool TIED>
 hipError_t launch_chunk_bwd(const ChunkBwdArgs &a, hipStream_t stream) {
   using Cfg = CbwdCfg<T, D, C>;
-  hipLaunchKernelGGL((hgrn2_chunk_bwd_kernel<T, D, C>), dim3(a.B * a.H * a.N), dim3(Cfg::NT), 0, stream, a);
+  hipLaunchKernelGGL((hgrn2_chunk_bwd_kernel<T, D, C, TIED>), dim3(a.B * a.H * a.N), dim3(Cfg::NT), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -19,7 +19,9 @@
 //     epilogue).
 // S and Lam are stored unpadded with each row's 16-byte chunks permuted by
 // XOR with (row & 15), which the copy realises by permuting its source
-// addresses; reads of 16 consecutive rows then never share a bank.
+// addresses; reads of 16 consecutive rows then never share a bank.  With tied
+// gates (k = 1 - f) k is formed from log f, dk is not written, and dlog f is
+// the total derivative dlog f - f dk.
 #pragma once
 
 #include "cbwd.h"
@@ -89,6 +91,7 @@ __device__ __forceinline__ PFrag<bf16_t> res_tr8(const bf16_t *m, int r0, int n0
 
 __device__ __forceinline__ int res_pair_i(int p) { return p >= 6 ? 3 : p >= 3 ? 2 : p >= 1 ? 1 : 0; }
 
+template <bool TIED>
 __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a) {
   using Cfg = CbwdResCfg;
   using T = bf16_t;
@@ -127,7 +130,7 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
     // lane-dependent offsets are recomputed per use (never kept live across the loop)
     const int tid = opaque((int)threadIdx.x), c0 = 2 * (tid & 63);
     const Chunk k = chunk_of(ci);
-    const GBuf bq = win(a.q, k), bk = win(a.k, k), bv = win(a.v, k), bl = win(a.log_f, k), bdy = win(a.dy, k);
+    const GBuf bq = win(a.q, k), bv = win(a.v, k), bl = win(a.log_f, k), bdy = win(a.dy, k);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int idx = tid + NT * i;
@@ -139,7 +142,7 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
     for (int t = 0; t < 8; ++t) {
       const uint32_t off = tok(16 * w + 8 * hh + t) + (uint32_t)c0 * sizeof(T);
       pq[t] = bq.ldpack<T, 2>(off);
-      pk[t] = bk.ldpack<T, 2>(off);
+      if constexpr (!TIED) pk[t] = win(a.k, k).template ldpack<T, 2>(off);
       pl[t] = bl.ldpack<T, 2>(off);
     }
   };
@@ -162,7 +165,7 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
       *(uint4 *)&sm.v[XT::at(row, col)] = pv[i];
       *(uint4 *)&sm.dy[XT::at(row, col)] = pdy[i];
     }
-    float l[8][2], Lw[2];
+    float l[8][2], Lw[2], hoff[2] = {0.f, 0.f};  // hoff: prefix before this wave's first token
     {
       float run[2] = {0.f, 0.f};
 #pragma unroll
@@ -186,6 +189,7 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
         const float first = sm.u.a.x.Lh[w][0][c0 + e];
         Lw[e] = first + sm.u.a.x.Lh[w][1][c0 + e];
         if (hh == 1) {
+          hoff[e] = first;
 #pragma unroll
           for (int t = 0; t < 8; ++t) l[t][e] += first;
         }
@@ -199,7 +203,7 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           oq.v[e] = from_f32<T>(to_f32(pq[t].v[e]) * __expf(l[t][e]));
-          ok.v[e] = from_f32<T>(to_f32(pk[t].v[e]) * __expf(Lw[e] - l[t][e]));
+          ok.v[e] = from_f32<T>(k_of<TIED>(pk[t].v[e], pl[t].v[e]) * __expf(Lw[e] - l[t][e]));
         }
         *(Pack<T, 2> *)&sm.qo[XT::at(tt, c0)] = oq;
         *(Pack<T, 2> *)&sm.ko[XT::at(tt, c0)] = ok;
@@ -313,17 +317,19 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
           }
         } else {
           // wide in-block decay: A[t][s] summed directly (every exponent <= 0)
-          const GBuf bq = win(a.q, k), bk = win(a.k, k), bl = win(a.log_f, k);
+          const GBuf bq = win(a.q, k), bl = win(a.log_f, k);
           for (int t = 0; t < 16; ++t) {
             const Pack<T, 2> pt = bq.ldpack<T, 2>(tok(16 * i + t) + (uint32_t)c0 * sizeof(T));
             float ex[2] = {0.f, 0.f};
             for (int s = t; s >= 0; --s) {
               const uint32_t off = tok(16 * i + s) + (uint32_t)c0 * sizeof(T);
-              const Pack<T, 2> pks = bk.ldpack<T, 2>(off), pls = bl.ldpack<T, 2>(off);
+              const Pack<T, 2> pls = bl.ldpack<T, 2>(off);
+              Pack<T, 2> pks;
+              if constexpr (!TIED) pks = win(a.k, k).template ldpack<T, 2>(off);
               float part = 0.f;
 #pragma unroll
               for (int e = 0; e < 2; ++e) {
-                part += to_f32(pt.v[e]) * to_f32(pks.v[e]) * __expf(ex[e]);
+                part += to_f32(pt.v[e]) * k_of<TIED>(pks.v[e], pls.v[e]) * __expf(ex[e]);
                 ex[e] += floor_logf(to_f32(pls.v[e]));
               }
               const float tot = wave_sum(part);
@@ -486,33 +492,40 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
         oq.v[e] = from_f32<T>(el * dd1[e]);
         ok.v[e] = from_f32<T>(ek * dd2[e]);
         X[t][e] = to_f32(qr.v[e]) * dd1[e] - to_f32(kr.v[e]) * dd2[e];
+        // tied gates: f dk (f from the prefix), subtracted from dlog f in P6; it
+        // replaces the consumed dk'_t
+        if (TIED && !wide)
+          ep.stg[1][tt][c0 + e] = __expf(l[t][e] - (t ? l[t - 1][e] : hoff[e])) * (ek * dd2[e]);
       }
       if (!wide) {
         bdq.stpack<T, 2, kStream>(tok(tt) + (uint32_t)c0 * sizeof(T), oq);
-        bdk.stpack<T, 2, kStream>(tok(tt) + (uint32_t)c0 * sizeof(T), ok);
+        if constexpr (!TIED) bdk.stpack<T, 2, kStream>(tok(tt) + (uint32_t)c0 * sizeof(T), ok);
       }
     }
     if (wide) {
       // diagonal block summed directly: dq_t adds sum_{s <= t} dA[t][s] k_s e^{ell_t - ell_s},
       // dk_t adds sum_{u >= t} dA[u][t] q_u e^{ell_u - ell_t} (every exponent <= 0)
-      const GBuf bq = win(a.q, k), bk = win(a.k, k), bv = win(a.v, k), bl = win(a.log_f, k),
-                 bdy = win(a.dy, k);
+      const GBuf bq = win(a.q, k), bv = win(a.v, k), bl = win(a.log_f, k), bdy = win(a.dy, k);
       const uint32_t cb2 = (uint32_t)c0 * sizeof(T);
       for (int t = 0; t < 8; ++t) {
         const int tb = 8 * hh + t, tt = 16 * w + tb;
-        const Pack<T, 2> pqt = bq.ldpack<T, 2>(tok(tt) + cb2), pkt = bk.ldpack<T, 2>(tok(tt) + cb2);
+        const Pack<T, 2> pqt = bq.ldpack<T, 2>(tok(tt) + cb2), plt = bl.ldpack<T, 2>(tok(tt) + cb2);
+        Pack<T, 2> pkt;
+        if constexpr (!TIED) pkt = win(a.k, k).template ldpack<T, 2>(tok(tt) + cb2);
         const Pack<T, 2> pdy = bdy.ldpack<T, 2>(tok(tt) + cb2), pvt = bv.ldpack<T, 2>(tok(tt) + cb2);
         float dqd[2] = {0.f, 0.f}, dkd[2] = {0.f, 0.f}, ex[2] = {0.f, 0.f};
         for (int s_ = tb; s_ >= 0; --s_) {
           const uint32_t off = tok(16 * w + s_) + cb2;
-          const Pack<T, 2> pvs = bv.ldpack<T, 2>(off), pks = bk.ldpack<T, 2>(off), pls = bl.ldpack<T, 2>(off);
+          const Pack<T, 2> pvs = bv.ldpack<T, 2>(off), pls = bl.ldpack<T, 2>(off);
+          Pack<T, 2> pks;
+          if constexpr (!TIED) pks = win(a.k, k).template ldpack<T, 2>(off);
           float part = 0.f;
 #pragma unroll
           for (int e = 0; e < 2; ++e) part += to_f32(pdy.v[e]) * to_f32(pvs.v[e]);
           const float dA = wave_sum(part);
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
-            dqd[e] += dA * to_f32(pks.v[e]) * __expf(ex[e]);
+            dqd[e] += dA * k_of<TIED>(pks.v[e], pls.v[e]) * __expf(ex[e]);
             ex[e] += floor_logf(to_f32(pls.v[e]));
           }
         }
@@ -540,10 +553,11 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
           const float el = __expf(l[t][e]), ek = __expf(Lw[e] - l[t][e]);
           oq.v[e] = from_f32<T>(el * dd1[e] + dqd[e]);
           ok.v[e] = from_f32<T>(ek * dd2[e] + dkd[e]);
-          X[t][e] += to_f32(pqt.v[e]) * dqd[e] - to_f32(pkt.v[e]) * dkd[e];
+          X[t][e] += to_f32(pqt.v[e]) * dqd[e] - k_of<TIED>(pkt.v[e], plt.v[e]) * dkd[e];
+          if (TIED) ep.stg[1][tt][c0 + e] = __expf(floor_logf(to_f32(plt.v[e]))) * (ek * dd2[e] + dkd[e]);
         }
         bdq.stpack<T, 2, kStream>(tok(tt) + cb2, oq);
-        bdk.stpack<T, 2, kStream>(tok(tt) + cb2, ok);
+        if constexpr (!TIED) bdk.stpack<T, 2, kStream>(tok(tt) + cb2, ok);
       }
     }
 #pragma unroll
@@ -574,7 +588,7 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           carry[e] += X[t][e];
-          o.v[e] = from_f32<T>(carry[e]);
+          o.v[e] = from_f32<T>(TIED ? carry[e] - ep.stg[1][16 * w + 8 * hh + t][c0 + e] : carry[e]);
         }
         bdl.stpack<T, 2, kStream>(tok(16 * w + 8 * hh + t) + (uint32_t)c0 * sizeof(T), o);
       }
@@ -590,9 +604,10 @@ inline int res_grid(int nchunks) {
   return nchunks < cus ? nchunks : cus;
 }
 
-inline hipError_t launch_chunk_bwd_res(const ChunkBwdArgs &a, hipStream_t stream) {
+template <bool TIED>
+hipError_t launch_chunk_bwd_res(const ChunkBwdArgs &a, hipStream_t stream) {
   const int nc = a.B * a.H * a.N;
-  hipLaunchKernelGGL(hgrn2_chunk_bwd_res_kernel, dim3(res_grid(nc)), dim3(CbwdResCfg::NT), 0, stream, a);
+  hipLaunchKernelGGL(hgrn2_chunk_bwd_res_kernel<TIED>, dim3(res_grid(nc)), dim3(CbwdResCfg::NT), 0, stream, a);
   return hipGetLastError();
 }
 

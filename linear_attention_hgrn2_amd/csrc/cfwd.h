@@ -73,7 +73,7 @@ __device__ __forceinline__ void block_prefix(const Pack<T, CPL> *pl, float (*l)[
     }
 }
 
-template <typename T, int D, int C>
+template <typename T, int D, int C, bool TIED>
 __global__ __launch_bounds__(4 * C) void hgrn2_chunk_fwd_kernel(ChunkFwdArgs a) {
   using Cfg = CfwdCfg<T, D, C>;
   constexpr int NW = Cfg::NW, NT = Cfg::NT, NB = Cfg::NB, CPL = Cfg::CPL, CB = Cfg::CB, KSD = Cfg::KSD,
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_fwd_kernel(ChunkFwdArgs a) 
       for (int e = 0; e < CPL; ++e) pq[t].v[e] = pk[t].v[e] = pl[t].v[e] = from_f32<T>(0.f);
       if (tt < len && has_ch) {
         pq[t] = ldpack<T, CPL>(gq + (tok(tt) + c0));
-        pk[t] = ldpack<T, CPL>(gk + (tok(tt) + c0));
+        if constexpr (!TIED) pk[t] = ldpack<T, CPL>(gk + (tok(tt) + c0));
         pl[t] = ldpack<T, CPL>(gl + (tok(tt) + c0));
       }
     }
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_fwd_kernel(ChunkFwdArgs a) 
 #pragma unroll
         for (int e = 0; e < CPL; ++e) {
           oq.v[e] = from_f32<T>(to_f32(pq[t].v[e]) * __expf(l[t][e]));
-          ok.v[e] = from_f32<T>(to_f32(pk[t].v[e]) * __expf(L[e] - l[t][e]));
+          ok.v[e] = from_f32<T>(k_of<TIED>(pk[t].v[e], pl[t].v[e]) * __expf(L[e] - l[t][e]));
         }
         stpack<T, CPL>(&sm.qo[XT::at(16 * w + t, c0)], oq);
         stpack<T, CPL>(&sm.u.kv.ko[XT::at(16 * w + t, c0)], ok);
@@ -208,11 +208,12 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_fwd_kernel(ChunkFwdArgs a) 
         for (int s = t; s >= 0; --s) {
           float part = 0.f;
           if (tv) {
-            const Pack<T, CPL> pk = ldpack<T, CPL>(gk + (tok(16 * w + s) + c0));
+            Pack<T, CPL> pk;
+            if constexpr (!TIED) pk = ldpack<T, CPL>(gk + (tok(16 * w + s) + c0));
             const Pack<T, CPL> pl = ldpack<T, CPL>(gl + (tok(16 * w + s) + c0));
 #pragma unroll
             for (int e = 0; e < CPL; ++e) {
-              part += qt[e] * to_f32(pk.v[e]) * __expf(ex[e]);
+              part += qt[e] * k_of<TIED>(pk.v[e], pl.v[e]) * __expf(ex[e]);
               ex[e] += floor_logf(to_f32(pl.v[e]));  // the factor of s - 1 includes f_s
             }
           }
@@ -320,10 +321,10 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_fwd_kernel(ChunkFwdArgs a) 
   }
 }
 
-template <typename T, int D, int C>
+template <typename T, int D, int C, bool TIED>
 hipError_t launch_chunk_fwd(const ChunkFwdArgs &a, hipStream_t stream) {
   using Cfg = CfwdCfg<T, D, C>;
-  hipLaunchKernelGGL((hgrn2_chunk_fwd_kernel<T, D, C>), dim3(a.B * a.H * a.N), dim3(Cfg::NT), 0, stream, a);
+  hipLaunchKernelGGL((hgrn2_chunk_fwd_kernel<T, D, C, TIED>), dim3(a.B * a.H * a.N), dim3(Cfg::NT), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -313,4 +313,15 @@ constexpr float kDiagLimit = 64.f;
 
 __device__ __forceinline__ float floor_logf(float x) { return fmaxf(x, kLogFloor); }
 
+// HGRN2's tied input gate k = 1 - f (HGRN2 summary, paperlayer.ai, §2.1 and
+// §3.2) from log f, as -expm1(log f): no cancellation for f near 1.  A zero
+// log f (a row past the end of the sequence) gives k = 0.
+__device__ __forceinline__ float tied_k(float log_f) { return -expm1f(floor_logf(log_f)); }
+
+// k of a token: loaded (independent gates) or formed from its log f (tied)
+template <bool TIED, typename T> __device__ __forceinline__ float k_of(T k, T log_f) {
+  if constexpr (TIED) return tied_k(to_f32(log_f));
+  else return to_f32(k);
+}
+
 }  // namespace hgrn2

@@ -1,6 +1,7 @@
 // Recurrent decode step (HGRN2 summary, paperlayer.ai, §1: recurrent
 // inference with linear cost; §3.2: state update and readout):
-//   S <- Diag(exp(log_f)) S + k^T v   (in place),   y = q S.
+//   S <- Diag(exp(log_f)) S + k^T v   (in place),   y = q S
+// (k = 1 - exp(log_f) with tied gates).
 // Pure HBM streaming: each (b, h) state (D*D float32) is read once and written
 // once.  One workgroup per (b, h); a thread owns a 4-column group (16-byte
 // accesses, consecutive threads on consecutive columns, so every wavefront
@@ -29,7 +30,7 @@ template <int D> struct DecodeCfg {
   static_assert(D % RG == 0, "row split");
 };
 
-template <typename TIn, int D>
+template <typename TIn, int D, bool TIED>
 __global__ __launch_bounds__(256) void hgrn2_decode_kernel(DecodeArgs a) {
   using Cfg = DecodeCfg<D>;
   constexpr int CG = Cfg::CG, RG = Cfg::RG, PASSES = Cfg::PASSES;
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(256) void hgrn2_decode_kernel(DecodeArgs a) {
 
   for (int c = tid; c < D; c += Cfg::NT) {
     s_q[c] = to_f32(gq[c]);
-    s_k[c] = to_f32(gk[c]);
+    s_k[c] = TIED ? tied_k(to_f32(gl[c])) : to_f32(gk[c]);
     s_f[c] = __expf(floor_logf(to_f32(gl[c])));
   }
   const float v0 = to_f32(gv[4 * cg + 0]), v1 = to_f32(gv[4 * cg + 1]),
@@ -97,9 +98,9 @@ __global__ __launch_bounds__(256) void hgrn2_decode_kernel(DecodeArgs a) {
   }
 }
 
-template <typename TIn, int D>
+template <typename TIn, int D, bool TIED>
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
-  hipLaunchKernelGGL((hgrn2_decode_kernel<TIn, D>), dim3(a.B * a.H), dim3(DecodeCfg<D>::NT), 0,
+  hipLaunchKernelGGL((hgrn2_decode_kernel<TIn, D, TIED>), dim3(a.B * a.H), dim3(DecodeCfg<D>::NT), 0,
                      stream, a);
   return hipGetLastError();
 }

@@ -41,9 +41,11 @@ hipError_t run_config(int dtype, int D, int C, A... args) {
 // Each returns hipErrorNotSupported (without launching) when no kernel
 // exists for the combination, else the launch status.  A null args pointer
 // only asks whether the kernel exists.
-hipError_t dispatch_scan(int dtype, int D, int C, bool reverse, const ScanArgs *a, hipStream_t s);
-hipError_t dispatch_chunk_fwd(int dtype, int D, int C, const ChunkFwdArgs *a, hipStream_t s);
-hipError_t dispatch_chunk_bwd(int dtype, int D, int C, const ChunkBwdArgs *a, hipStream_t s);
-hipError_t dispatch_decode(int dtype, int D, const DecodeArgs &a, hipStream_t s);
+// `tied`: k = 1 - exp(log f) is formed in the kernel (k pointers unused) and
+// the backward writes the total dlog f and no dk.
+hipError_t dispatch_scan(int dtype, int D, int C, bool reverse, bool tied, const ScanArgs *a, hipStream_t s);
+hipError_t dispatch_chunk_fwd(int dtype, int D, int C, bool tied, const ChunkFwdArgs *a, hipStream_t s);
+hipError_t dispatch_chunk_bwd(int dtype, int D, int C, bool tied, const ChunkBwdArgs *a, hipStream_t s);
+hipError_t dispatch_decode(int dtype, int D, bool tied, const DecodeArgs &a, hipStream_t s);
 
 }  // namespace hgrn2

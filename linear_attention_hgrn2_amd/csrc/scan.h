@@ -5,7 +5,8 @@
 // product write each step.  Over one chunk of C tokens with in-chunk
 // inclusive prefix b_t of log f and total Gamma = b_C, the state advances as
 //   S <- Diag(e^Gamma) S + sum_t Diag(e^{Gamma - b_t}) x_t^T z_t
-// with (x, z) = (k, v).  Walked backwards with (x, z) = (q, dy) and weights
+// with (x, z) = (k, v); with tied gates k = 1 - f is formed from log f
+// instead of read.  Walked backwards with (x, z) = (q, dy) and weights
 // e^{b_t}, the same pass carries the state adjoint Lambda (the gradient of the
 // loss with respect to the state at a chunk end):
 //   Lambda <- Diag(e^Gamma) Lambda + sum_t Diag(e^{b_t}) q_t^T dy_t.
@@ -55,7 +56,7 @@ template <typename T, int D, int C, bool REV> struct ScanCfg {
   };
 };
 
-template <typename T, int D, int C, bool REV>
+template <typename T, int D, int C, bool REV, bool TIED>
 __global__ __launch_bounds__(4 * C) void hgrn2_scan_kernel(ScanArgs a) {
   using Cfg = ScanCfg<T, D, C, REV>;
   constexpr int NW = Cfg::NW, NT = Cfg::NT, CS = Cfg::CS, NS = Cfg::NS, GL = Cfg::GL, TPG = Cfg::TPG,
@@ -155,10 +156,10 @@ __global__ __launch_bounds__(4 * C) void hgrn2_scan_kernel(ScanArgs a) {
   // as zero (log f = 0, x = 0, z = 0 contribute nothing), so nothing is masked
   // where they are consumed and every step issues the same loads.
   auto prefetch = [&](XP &px, XP &pl, ZP &pz, int n) {
-    const GBuf bx = win(a.x, n), bl = win(a.log_f, n), bz = win(a.z, n);
+    const GBuf bl = win(a.log_f, n), bz = win(a.z, n);
 #pragma unroll
     for (int i = 0; i < TPG; ++i) {
-      px[i] = bx.ldpack<T, 1>(xoff + (uint32_t)i * HDB).v[0];
+      if constexpr (!TIED) px[i] = win(a.x, n).template ldpack<T, 1>(xoff + (uint32_t)i * HDB).v[0];
       pl[i] = bl.ldpack<T, 1>(xoff + (uint32_t)i * HDB).v[0];
     }
 #pragma unroll
@@ -207,7 +208,7 @@ __global__ __launch_bounds__(4 * C) void hgrn2_scan_kernel(ScanArgs a) {
       for (int i = 0; i < TPG; ++i) {
         const float b_t = P + excl + l[i];
         const float ex = REV ? b_t : fminf(G - b_t, 0.f);
-        sm.x[XT::at(16 * w + TPG * gi + i, cl)] = from_f32<T>(to_f32(px[i]) * __expf(ex));
+        sm.x[XT::at(16 * w + TPG * gi + i, cl)] = from_f32<T>(k_of<TIED>(px[i], pl[i]) * __expf(ex));
       }
     }
     flush();  // the state staged in the previous step (read here, rewritten after the next barrier)
@@ -263,11 +264,12 @@ __global__ __launch_bounds__(4 * C) void hgrn2_scan_kernel(ScanArgs a) {
   }
 }
 
-template <typename T, int D, int C, bool REV>
+template <typename T, int D, int C, bool REV, bool TIED = false>
 hipError_t launch_scan(const ScanArgs &a, hipStream_t stream) {
+  static_assert(!(REV && TIED), "the adjoint scan reads q, not k");
   using Cfg = ScanCfg<T, D, C, REV>;
   const int groups = (a.B * a.H + 7) / 8;
-  hipLaunchKernelGGL((hgrn2_scan_kernel<T, D, C, REV>), dim3(groups * 8 * Cfg::NS), dim3(Cfg::NT), 0, stream, a);
+  hipLaunchKernelGGL((hgrn2_scan_kernel<T, D, C, REV, TIED>), dim3(groups * 8 * Cfg::NS), dim3(Cfg::NT), 0, stream, a);
   return hipGetLastError();
 }
 

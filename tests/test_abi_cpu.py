@@ -26,7 +26,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("hgrn2_fwd", "hgrn2_bwd", "hgrn2_decode_step", "hgrn2_fwd_chunk", "hgrn2_bwd_adjoint",
-              "hgrn2_bwd_chunk"):
+              "hgrn2_bwd_chunk", "hgrn2_fwd_tied", "hgrn2_bwd_tied", "hgrn2_fwd_chunk_tied",
+              "hgrn2_bwd_chunk_tied", "hgrn2_decode_step_tied"):
         assert n in names
 
 
@@ -36,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.hgrn2_abi_version() == 3
+    assert lib.hgrn2_abi_version() == 4
     for s in range(5):
         assert lib.hgrn2_status_string(s).startswith(b"HGRN2_")
 
@@ -129,6 +130,31 @@ def test_staged_rejections(lib):
                                P[8], P[9], None, None) == 1
     assert lib.hgrn2_bwd_chunk(0, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7],
                                P[8], P[9], P[10], None) == 1
+
+
+def test_tied_rejections(lib):
+    P = [FAKE + i * 0x100000 for i in range(14)]
+    # hgrn2_fwd_tied: q NULL; y aliases v; unsupported chunk; no states and no workspace
+    assert lib.hgrn2_fwd_tied(1, 10, 1, 16, 16, 16, 0, None, P[1], P[2], None, P[3], None, P[4], None, 0,
+                              None) == 1
+    assert lib.hgrn2_fwd_tied(1, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], None, P[1], None, P[4], None, 0,
+                              None) == 1
+    assert lib.hgrn2_fwd_tied(1, 10, 1, 16, 16, 24, 0, P[0], P[1], P[2], None, P[3], None, P[4], None, 0,
+                              None) == 2
+    assert lib.hgrn2_fwd_tied(1, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], None, P[3], None, None, None, 0,
+                              None) == 3
+    # hgrn2_bwd_tied: no workspace; dlog_f aliases dy
+    assert lib.hgrn2_bwd_tied(1, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], None, P[9], P[3], None, P[4], P[5],
+                              P[6], None, None, 0, None) == 3
+    need = lib.hgrn2_bwd_workspace_bytes(1, 10, 1, 16, 16, 16, 0, 1)
+    assert lib.hgrn2_bwd_tied(1, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], None, P[9], P[3], None, P[4], P[5],
+                              P[3], None, P[10], need, None) == 1
+    # the staged tied launches and the tied decode step
+    assert lib.hgrn2_fwd_chunk_tied(1, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], P[3], P[0], None) == 1
+    assert lib.hgrn2_bwd_chunk_tied(1, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], P[3], P[4], P[5], P[6], None,
+                                    P[8], None) == 1
+    assert lib.hgrn2_decode_step_tied(1, 1, 24, 24, 0, P[0], P[1], P[2], P[3], P[4], None) == 2
+    assert lib.hgrn2_decode_step_tied(1, 1, 16, 16, 0, P[0], P[1], P[2], P[3], P[0], None) == 1
 
 
 def test_decode_rejections(lib):
