@@ -6,7 +6,9 @@ chunk-boundary states) followed by hgrn2_bwd, issued as the four single
 launches they are made of (state scan, per-chunk outputs, adjoint scan,
 per-chunk gradients) so that HIP events on the launch stream bracket each
 kernel.  Three resident input sets (forget-gate lower bound 0, 0.3, 0.6) are
-rotated across steps.  The decode
+rotated across steps.  The same step with tied gates (k = 1 - f formed in the
+kernels, hgrn2_fwd_tied / hgrn2_bwd_tied) is timed next on the same inputs and
+reported under "tied"; the headline value is the untied step.  The decode
 step (B256 H16 d128, float32 state) is timed as well and reported in HBM
 GB/s.  Inputs are seeded synthetic data generated on the host and copied to
 HBM before timing.
@@ -129,19 +131,34 @@ class KernelTimer:
 # the four launches of one training step, in order, with the kernel each one runs
 TRAIN_KERNELS = (("scan", "hgrn2_scan_kernel (forward)"), ("cfwd", "hgrn2_chunk_fwd_kernel"),
                  ("scan_rev", "hgrn2_scan_kernel (reverse)"), ("cbwd", "hgrn2_chunk_bwd_res_kernel"))
+# the same with tied gates (k = 1 - f formed in the kernels; the adjoint scan never reads k)
+TIED_KERNELS = (("scan_tied", "hgrn2_scan_kernel (forward, tied)"),
+                ("cfwd_tied", "hgrn2_chunk_fwd_kernel (tied)"),
+                ("scan_rev", "hgrn2_scan_kernel (reverse)"),
+                ("cbwd_tied", "hgrn2_chunk_bwd_res_kernel (tied)"))
+
+
+def _template_args(n: str):
+    if "<" not in n:
+        return []
+    return [a.strip() for a in n[n.index("<") + 1:n.rindex(">")].split(",")]
 
 
 def kernel_label(name: str):
-    """rocprofv3 kernel name -> one of TRAIN_KERNELS' labels, "decode", or None."""
+    """rocprofv3 kernel name -> a label of TRAIN_KERNELS or TIED_KERNELS, "decode[_tied]", or None.
+    Template arguments: scan <T, D, C, REV, TIED>; chunk kernels <T, D, C, TIED> or <TIED>;
+    decode <T, D, TIED>."""
     n = _short(name)
+    a = _template_args(n)
+    tied = "_tied" if a and a[-1] == "true" else ""
     if n.startswith("hgrn2_scan_kernel"):
-        return "scan_rev" if "true" in n else "scan"
+        return "scan_rev" if len(a) > 3 and a[3] == "true" else "scan" + tied
     if n.startswith("hgrn2_chunk_fwd_kernel"):
-        return "cfwd"
+        return "cfwd" + tied
     if n.startswith("hgrn2_chunk_bwd"):
-        return "cbwd"
+        return "cbwd" + tied
     if n.startswith("hgrn2_decode_kernel"):
-        return "decode"
+        return "decode" + tied
     return None
 
 
@@ -157,23 +174,28 @@ def train_algorithmic_bytes(w):
         "cfwd": 4 * tok + N * ent + tok,                 # q, k, v, log_f, states 0..N-1 in; y out
         "scan_rev": 3 * tok + N * ent,                   # q, dy, log_f in; adjoints 1..N out
         "cbwd": 5 * tok + 2 * N * ent + 4 * tok,         # q, k, v, log_f, dy, states, adjoints in; 4 grads out
+        # tied gates: no k read, no dk written
+        "scan_tied": 2 * tok + (N + 1) * ent,
+        "cfwd_tied": 3 * tok + N * ent + tok,
+        "cbwd_tied": 4 * tok + 2 * N * ent + 3 * tok,
     }
 
 
-def bench_train(torch, m, args):
+def bench_train(torch, m, args, sets, tied=False):
+    """Times `args.steps` training steps (after `args.warmup` untimed ones) with
+    untied gates (k an input) or tied gates (k = 1 - f formed in the kernels)."""
     import synth
     w = synth.WORKLOADS["train_bf16"]
     B, T, H, D, C = w.B, w.T, w.H, w.D, w.chunk
-    sets = make_train_sets(torch, w, synth.TRAIN_LAMBDAS)
     dev = sets[0]["q"].device
     y = torch.empty((B, T, H, D), dtype=torch.bfloat16, device=dev)
     states = torch.empty(m.states_shape(B, T, H, D, C), dtype=torch.bfloat16, device=dev)
     lam = torch.empty(m.adjoints_shape(B, T, H, D, C), dtype=torch.bfloat16, device=dev)
     grads = [torch.empty((B, T, H, D), dtype=torch.bfloat16, device=dev) for _ in range(4)]
+    kernels = TIED_KERNELS if tied else TRAIN_KERNELS
 
-    def step(i, timer=None):
-        s = sets[i % len(sets)]
-        calls = (
+    def calls_untied(s):
+        return (
             lambda: m.fwd(s["q"], s["k"], s["v"], s["log_f"], None, chunk=C, want_ht=False, want_y=False,
                           states=states),
             lambda: m.fwd_chunk(s["q"], s["k"], s["v"], s["log_f"], states, chunk=C, y=y),
@@ -181,7 +203,20 @@ def bench_train(torch, m, args):
             lambda: m.bwd_chunk(s["q"], s["k"], s["v"], s["log_f"], s["dy"], states, lam, chunk=C,
                                 dq=grads[0], dk=grads[1], dv=grads[2], dlog_f=grads[3]),
         )
-        for (label, _), call in zip(TRAIN_KERNELS, calls):
+
+    def calls_tied(s):
+        return (
+            lambda: m.fwd_tied(s["q"], s["v"], s["log_f"], None, chunk=C, want_ht=False, want_y=False,
+                               states=states),
+            lambda: m.fwd_chunk_tied(s["q"], s["v"], s["log_f"], states, chunk=C, y=y),
+            lambda: m.bwd_adjoint(s["q"], s["log_f"], s["dy"], None, chunk=C, adjoints=lam),
+            lambda: m.bwd_chunk_tied(s["q"], s["v"], s["log_f"], s["dy"], states, lam, chunk=C,
+                                     dq=grads[0], dv=grads[2], dlog_f=grads[3]),
+        )
+
+    def step(i, timer=None):
+        s = sets[i % len(sets)]
+        for (label, _), call in zip(kernels, (calls_tied if tied else calls_untied)(s)):
             t = timer.start(label) if timer else None
             call()
             if timer:
@@ -190,7 +225,7 @@ def bench_train(torch, m, args):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    log("warmup done")
+    log("warmup done" + (" (tied)" if tied else ""))
     # timed region: exactly `steps` steps, bracketed by synchronisation; the
     # events around each launch are recorded on the stream the kernels run on
     timer = KernelTimer(torch)
@@ -203,8 +238,9 @@ def bench_train(torch, m, args):
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
-    kms = {label: timer.mean_ms(label) for label, _ in TRAIN_KERNELS}
-    log("timed: %.3f ms/step (%s)" % (ms, ", ".join("%s %.3f ms" % kv for kv in kms.items())))
+    kms = {label: timer.mean_ms(label) for label, _ in kernels}
+    log("timed%s: %.3f ms/step (%s)" % (" (tied)" if tied else "", ms,
+                                       ", ".join("%s %.3f ms" % kv for kv in kms.items())))
     return dict(w=w, ms=ms, kernel_ms=kms, host=sets[0]["host"])
 
 
@@ -356,19 +392,21 @@ def summarize_mfma(mfma_dir, avg_ns, digest):
     acc = {}
     for r in _csv(os.path.join(mfma_dir, "run_counter_collection.csv")):
         label = kernel_label(r["Kernel_Name"])
-        if label is None or label == "decode":
+        if label is None or label.startswith("decode"):
             continue
         acc.setdefault((label, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
     w = __import__("synth").WORKLOADS["train_bf16"]
     th = w.B * w.T * w.H
     alg_flop = {"scan": th * 2 * w.D * w.D, "cfwd": th * (w.chunk * 2 * w.D + 2 * w.D * w.D),
                 "scan_rev": th * 2 * w.D * w.D, "cbwd": th * (5 * w.chunk * w.D + 6 * w.D * w.D)}
+    for label in ("scan", "cfwd", "cbwd"):       # tied gates change no contraction
+        alg_flop[label + "_tied"] = alg_flop[label]
     out = ["Matrix-core work per launch, HGRN2 training step (B8 H16 T4096 d128 bf16 chunk64)",
            "command: " + MFMA_CMD, "durations: the kernel-trace averages of " + TRACE_CMD,
            "peak: %.0f TFLOP/s dense bf16" % BF16_PEAK_TFLOPS, "source_digest: " + digest, "",
            "%-9s %14s %14s %10s %10s %10s" % ("kernel", "executed_GFLOP", "algorithmic", "TFLOP/s",
                                               "of_peak", "MfmaUtil")]
-    for label, _ in TRAIN_KERNELS:
+    for label in dict(TRAIN_KERNELS + TIED_KERNELS):
         mops = acc.get((label, "SQ_INSTS_VALU_MFMA_MOPS_BF16"))
         util = acc.get((label, "MfmaUtil"))
         if not mops or label not in avg_ns:
@@ -401,7 +439,10 @@ def main():
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
     res = None
     if args.only in ("train", "all"):
-        res = bench_train(torch, m, args)
+        import synth
+        sets = make_train_sets(torch, synth.WORKLOADS["train_bf16"], synth.TRAIN_LAMBDAS)
+        res = bench_train(torch, m, args, sets)
+        tres = bench_train(torch, m, args, sets, tied=True)
         w = res["w"]
         tokens = w.B * w.T
         out["value"] = tokens / (res["ms"] * 1e-3)
@@ -425,6 +466,13 @@ def main():
                                   "frac_hbm": alg[label] / kms[label] / 1e6 / HBM_PEAK_GBS}
                           for label, kn in TRAIN_KERNELS}
         out["mfma_frac_step"] = step_flop / (res["ms"] * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)
+        tk = tres["kernel_ms"]
+        out["tied"] = {"workload": "train_bf16 with tied gates (k = 1 - f): fwd(states)+bwd, total dlog_f",
+                       "value": tokens / (tres["ms"] * 1e-3), "unit": "tokens/s", "ms_per_step": tres["ms"],
+                       "kernels": {label: {"kernel": kn, "ms": tk[label], "bytes": alg[label],
+                                           "GBps": alg[label] / tk[label] / 1e6,
+                                           "frac_hbm": alg[label] / tk[label] / 1e6 / HBM_PEAK_GBS}
+                                   for label, kn in TIED_KERNELS}}
     if args.only in ("decode", "all"):
         dres = bench_decode(torch, m, args)
         out["decode"] = {"workload": "decode_f32: B256 H16 d128, float32 state", "ms": dres["ms"],

@@ -17,10 +17,10 @@
 // Rows of the state evolve independently (each row is one decay channel), so
 // one workgroup owns one (batch, head, CS-row slice) and holds those rows of
 // the state, transposed (S^T[j][c], every column j), in float32 matrix-core
-// accumulators.  Per chunk a workgroup only decays its own CS channels: wave
-// w takes the chunk's 16-token sub-block w, lane = one channel and a run of
-// consecutive tokens; the z rows (v or dy) are shared through L2 by the
-// slices of one head, which run on one XCD.
+// accumulators.  Per chunk a workgroup only decays its own CS channels: thread
+// tid takes channel tid % CS and the run tid / CS of TPR consecutive tokens;
+// the z rows (v or dy) are shared through L2 by the slices of one head, which
+// run on one XCD.
 #pragma once
 
 #include "tile.h"
@@ -36,11 +36,16 @@ struct ScanArgs {
 };
 
 template <typename T, int D, int C, bool REV> struct ScanCfg {
-  static constexpr int NW = C / 16, NT = 64 * NW;
-  static constexpr int CS = D < 32 ? D : 32;     // state rows (channels) per workgroup
+  // state rows (channels) per workgroup.  At d = 128, bf16, chunk 64, 64 rows
+  // make each 128-byte line of x and log f belong to one workgroup and halve
+  // the re-reads of the z rows; eight waves then keep two per SIMD.
+  static constexpr bool WIDE = D >= 128 && C == 64 && sizeof(T) == 2;
+  static constexpr int CS = WIDE ? 64 : (D < 32 ? D : 32);
+  static constexpr int NW = WIDE ? 8 : C / 16, NT = 64 * NW;
   static constexpr int NS = D / CS;               // slices per (b, h)
-  static constexpr int GL = 64 / CS;              // lane groups per wave in the prep layout
-  static constexpr int TPG = 16 / GL;             // consecutive tokens per lane
+  static constexpr int NR = NT / CS;              // runs of consecutive tokens per chunk
+  static constexpr int TPR = C / NR;              // tokens per run (per lane)
+  static_assert(NR * TPR == C, "runs tile the chunk");
   static constexpr int JB = D / 16, CBS = CS / 16;
   static constexpr int NTILE = JB * CBS;
   static constexpr int TPW = (NTILE + NW - 1) / NW;  // state tiles per wave
@@ -50,16 +55,16 @@ template <typename T, int D, int C, bool REV> struct ScanCfg {
   struct Smem {
     T x[C * RowTile<T, CS, 32>::LD];    // decayed x of this slice's channels
     T z[2][C * RowTile<T, D, 32>::LD];  // z rows, double-buffered
-    float Lb[NW][CS];                // sub-block totals of log f
+    float Lr[NR][CS];                // run totals of log f
     float eG[CS];                    // e^Gamma
     T st[CS * RowTile<T, D>::LD];    // a state awaiting its store, rows c of the slice
   };
 };
 
 template <typename T, int D, int C, bool REV, bool TIED>
-__global__ __launch_bounds__(4 * C) void hgrn2_scan_kernel(ScanArgs a) {
+__global__ __launch_bounds__((ScanCfg<T, D, C, REV>::NT)) void hgrn2_scan_kernel(ScanArgs a) {
   using Cfg = ScanCfg<T, D, C, REV>;
-  constexpr int NW = Cfg::NW, NT = Cfg::NT, CS = Cfg::CS, NS = Cfg::NS, GL = Cfg::GL, TPG = Cfg::TPG,
+  constexpr int NW = Cfg::NW, NT = Cfg::NT, CS = Cfg::CS, NS = Cfg::NS, NR = Cfg::NR, TPR = Cfg::TPR,
                 JB = Cfg::JB, EPV = Cfg::EPV;
   // rows padded by 32 bytes: the transposing operand reads are conflict-free
   using XT = RowTile<T, CS, 32>;
@@ -77,7 +82,7 @@ __global__ __launch_bounds__(4 * C) void hgrn2_scan_kernel(ScanArgs a) {
   const int T_ = a.T, H = a.H, N = a.N;
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n16 = lane & 15, g = lane >> 4;
-  const int cl = lane % CS, gi = lane / CS;  // prep layout: channel, token run
+  const int cl = tid % CS, ri = tid / CS;  // prep layout: channel, run of TPR tokens
 
   const size_t SS = (size_t)D * D;
   const uint32_t HDB = (uint32_t)H * D * sizeof(T);  // bytes from one token to the next
@@ -88,7 +93,7 @@ __global__ __launch_bounds__(4 * C) void hgrn2_scan_kernel(ScanArgs a) {
                 (uint32_t)min(C, T_ - t0) * HDB);
   };
   // per-lane byte offsets within a chunk window (the same for every chunk)
-  const uint32_t xoff = (uint32_t)(16 * w + TPG * gi) * HDB + (uint32_t)(cs0 + cl) * sizeof(T);
+  const uint32_t xoff = (uint32_t)(ri * TPR) * HDB + (uint32_t)(cs0 + cl) * sizeof(T);
   uint32_t zoff[Cfg::NVZ];
 #pragma unroll
   for (int i = 0; i < Cfg::NVZ; ++i) {
@@ -150,7 +155,7 @@ __global__ __launch_bounds__(4 * C) void hgrn2_scan_kernel(ScanArgs a) {
 
   // ---- register prefetch, two chunks ahead in two register sets: x, log f of
   // this lane's channel and token run; the z tile
-  using XP = T[TPG];
+  using XP = T[TPR];
   using ZP = uint4[Cfg::NVZ];
   // Loads go through buffer windows: rows past the end of the sequence read
   // as zero (log f = 0, x = 0, z = 0 contribute nothing), so nothing is masked
@@ -158,7 +163,7 @@ __global__ __launch_bounds__(4 * C) void hgrn2_scan_kernel(ScanArgs a) {
   auto prefetch = [&](XP &px, XP &pl, ZP &pz, int n) {
     const GBuf bl = win(a.log_f, n), bz = win(a.z, n);
 #pragma unroll
-    for (int i = 0; i < TPG; ++i) {
+    for (int i = 0; i < TPR; ++i) {
       if constexpr (!TIED) px[i] = win(a.x, n).template ldpack<T, 1>(xoff + (uint32_t)i * HDB).v[0];
       pl[i] = bl.ldpack<T, 1>(xoff + (uint32_t)i * HDB).v[0];
     }
@@ -170,23 +175,15 @@ __global__ __launch_bounds__(4 * C) void hgrn2_scan_kernel(ScanArgs a) {
   auto step = [&](XP &px, XP &pl, ZP &pz, int it) {
     const int n = REV ? N - 1 - it : it;
     T *zs = sm.z[it & 1];
-    // ---- block-local prefix of the floored log f: within the lane's run, then across runs
-    float l[TPG];
+    // ---- chunk-local prefix of the floored log f: within the lane's run, then across runs
+    float l[TPR];
     float run = 0.f;
 #pragma unroll
-    for (int i = 0; i < TPG; ++i) {
+    for (int i = 0; i < TPR; ++i) {
       run += floor_logf(to_f32(pl[i]));
       l[i] = run;
     }
-    float incl = run;
-#pragma unroll
-    for (int d = 1; d < GL; d <<= 1) {
-      const float y = __shfl_up(incl, d * CS, 64);
-      if (gi >= d) incl += y;
-    }
-    const float excl = incl - run;                          // sum of earlier runs of the block
-    const float Lw = __shfl(incl, (GL - 1) * CS + cl, 64);  // the block total
-    if (gi == 0) sm.Lb[w][cl] = Lw;
+    sm.Lr[ri][cl] = run;
 #pragma unroll
     for (int i = 0; i < Cfg::NVZ; ++i) {
       const int idx = tid + i * NT;
@@ -196,19 +193,19 @@ __global__ __launch_bounds__(4 * C) void hgrn2_scan_kernel(ScanArgs a) {
     __syncthreads();
     // ---- decayed x: forward x e^{Gamma - b_t}, backward x e^{b_t}
     {
-      float P = 0.f, G = 0.f;
+      float P = 0.f, G = 0.f;  // earlier runs' total, chunk total
 #pragma unroll
-      for (int i = 0; i < NW; ++i) {
-        const float L = sm.Lb[i][cl];
-        P += (i < w) ? L : 0.f;
+      for (int r = 0; r < NR; ++r) {
+        const float L = sm.Lr[r][cl];
+        P += (r < ri) ? L : 0.f;
         G += L;
       }
-      if (w == 0 && gi == 0) sm.eG[cl] = __expf(G);
+      if (ri == 0) sm.eG[cl] = __expf(G);
 #pragma unroll
-      for (int i = 0; i < TPG; ++i) {
-        const float b_t = P + excl + l[i];
+      for (int i = 0; i < TPR; ++i) {
+        const float b_t = P + l[i];
         const float ex = REV ? b_t : fminf(G - b_t, 0.f);
-        sm.x[XT::at(16 * w + TPG * gi + i, cl)] = from_f32<T>(k_of<TIED>(px[i], pl[i]) * __expf(ex));
+        sm.x[XT::at(ri * TPR + i, cl)] = from_f32<T>(k_of<TIED>(px[i], pl[i]) * __expf(ex));
       }
     }
     flush();  // the state staged in the previous step (read here, rewritten after the next barrier)
@@ -239,7 +236,7 @@ __global__ __launch_bounds__(4 * C) void hgrn2_scan_kernel(ScanArgs a) {
     if (!REV) stage(n + 1);
   };
 
-  T px0[TPG], pl0[TPG], px1[TPG], pl1[TPG];
+  T px0[TPR], pl0[TPR], px1[TPR], pl1[TPR];
   uint4 pz0[Cfg::NVZ], pz1[Cfg::NVZ];
   prefetch(px0, pl0, pz0, REV ? N - 1 : 0);
   prefetch(px1, pl1, pz1, REV ? max(N - 2, 0) : min(1, N - 1));
