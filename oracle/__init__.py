@@ -25,7 +25,8 @@ _LIB = os.path.join(_HERE, "liboracle_hgrn2.so")
 _lib = None
 
 __all__ = ["build", "forward", "backward", "decode_step", "forward_tied", "backward_tied",
-           "decode_step_tied", "tied_k", "threads", "Oracle", "default"]
+           "decode_step_tied", "tied_k", "gate_log_f", "gate_k", "gate_partials", "forward_gate",
+           "backward_gate", "decode_step_gate", "threads", "Oracle", "default"]
 
 
 def build(force: bool = True) -> str:
@@ -171,3 +172,77 @@ def backward_tied(q, v, log_f, dy, h0=None, dht=None):
 def decode_step_tied(q, v, log_f, state):
     """decode_step() with k = 1 - exp(log_f)."""
     return decode_step(q, tied_k(log_f), v, log_f, state)
+
+
+# ------------------------------------------------------------------ gate from its pre-activation
+# HGRN's forget gate has an additive lower bound: the gate learns a residual
+# above a lower bound lam that the layer supplies (HGRN2 summary,
+# paperlayer.ai, §2.2: lower bounds per layer, forget gate learning residuals
+# above them).  Read here as
+#     f = lam + (1 - lam) * sigmoid(z),      k = 1 - f = (1 - lam) * sigmoid(-z),
+# with z [B,T,H,DK] the pre-activation and lam [H,DK] the lower bound of each
+# head channel.  The loss reaches z and lam through log f (the decay) and
+# through k (the tied input gate); the chain rule over the partial gradients
+# of the recurrence gives dz and dlam (summed over batch and time).
+
+
+def _sig_pair(z):
+    """(sigmoid(z), sigmoid(-z)) in float64 without overflow."""
+    z = np.asarray(z, dtype=np.float64)
+    e = np.exp(-np.abs(z))
+    hi, lo = 1.0 / (1.0 + e), e / (1.0 + e)
+    return np.where(z >= 0, hi, lo), np.where(z >= 0, lo, hi)
+
+
+def gate_log_f(z, lam):
+    """log f = log(lam + (1 - lam) sigmoid(z)), float64, stable for any z:
+    for z >= 0 (u = e^-z <= 1) it is log1p(lam u) - log1p(u); for z < 0
+    (u = e^z < 1) it is log(lam + u) - log1p(u).  lam broadcasts over [..., H, DK]."""
+    z = np.asarray(z, dtype=np.float64)
+    lam = np.broadcast_to(np.asarray(lam, dtype=np.float64), z.shape)
+    u = np.exp(-np.abs(z))
+    with np.errstate(divide="ignore"):
+        neg = np.log(lam + u) - np.log1p(u)
+    pos = np.log1p(lam * u) - np.log1p(u)
+    return np.where(z >= 0, pos, neg)
+
+
+def gate_k(z, lam):
+    """k = 1 - f = (1 - lam) sigmoid(-z), float64."""
+    lam = np.asarray(lam, dtype=np.float64)
+    return (1.0 - lam) * _sig_pair(z)[1]
+
+
+def gate_partials(z, lam):
+    """(dlog_f/dz, dk/dz, dlog_f/dlam, dk/dlam) at every element, float64:
+    with s = sigmoid(z), s' = sigmoid(-z), f = lam + (1 - lam) s:
+    dlog_f/dz = (1 - lam) s s' / f,  dk/dz = -(1 - lam) s s',
+    dlog_f/dlam = s' / f,            dk/dlam = -s'."""
+    z = np.asarray(z, dtype=np.float64)
+    lam = np.broadcast_to(np.asarray(lam, dtype=np.float64), z.shape)
+    s, sp = _sig_pair(z)
+    f = lam + (1.0 - lam) * s
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(lam == 0.0, 1.0, (1.0 - lam) * s / f)   # (1 - lam) s / f, -> 1 as lam -> 0
+        dl_dlam = sp / f
+    return ratio * sp, -(1.0 - lam) * s * sp, dl_dlam, -sp
+
+
+def forward_gate(q, v, z, lam, h0=None):
+    """forward() with log f and k formed from the pre-activation z and the lower bound lam [H,DK]."""
+    return forward(q, gate_k(z, lam), v, gate_log_f(z, lam), h0)
+
+
+def backward_gate(q, v, z, lam, dy, h0=None, dht=None):
+    """(dq, dv, dz, dlam, dh0): dz [B,T,H,DK] and dlam [H,DK] by the chain rule
+    through log f and k; dlam sums over batch and time."""
+    dq, dk, dv, dl, dh0 = backward(q, gate_k(z, lam), v, gate_log_f(z, lam), dy, h0, dht)
+    a, b, c, d = gate_partials(z, lam)
+    dz = dl * a + dk * b
+    dlam = (dl * c + dk * d).sum(axis=(0, 1))
+    return dq, dv, dz, dlam, dh0
+
+
+def decode_step_gate(q, v, z, lam, state):
+    """decode_step() with log f and k formed from z [B,H,DK] and lam [H,DK]."""
+    return decode_step(q, gate_k(z, lam), v, gate_log_f(z, lam), state)

@@ -138,7 +138,9 @@ def generate(w: Workload | str, *, lam: float | None = None, seed: int | None = 
     """Draw one workload's inputs.  Sizes may be overridden for small parity cases.
 
     Returns a dict of numpy arrays in storage form (float32, or uint16 bfloat16
-    bits) plus metadata: q, k, v, log_f [B,T,H,D]; h0 [B,H,D,D] float32 or
+    bits) plus metadata: q, k, v, log_f [B,T,H,D]; z [B,T,H,D], the gate
+    pre-activation that log_f and k were made from (rounded on its own, for
+    callers that pass the pre-activation instead); h0 [B,H,D,D] float32 or
     None; dy [B,T,H,D] or None."""
     if isinstance(w, str):
         w = WORKLOADS[w]
@@ -152,7 +154,6 @@ def generate(w: Workload | str, *, lam: float | None = None, seed: int | None = 
     shape = (B, T, H, D)
     z = rng.standard_normal(shape)
     log_f, k = _gates(z, lam)
-    del z
     q = rng.standard_normal(shape) * w.qscale
     v = rng.standard_normal(shape) * w.qscale
     h0 = None
@@ -162,7 +163,7 @@ def generate(w: Workload | str, *, lam: float | None = None, seed: int | None = 
     if w.train:
         dy = _store(rng.standard_normal(shape), w.dtype)
     return dict(q=_store(q, w.dtype), k=_store(k, w.dtype), v=_store(v, w.dtype),
-                log_f=_store(log_f, w.dtype), h0=h0, dy=dy, dtype=w.dtype,
+                log_f=_store(log_f, w.dtype), z=_store(z, w.dtype), h0=h0, dy=dy, dtype=w.dtype,
                 B=B, T=T, H=H, D=D, chunk=w.chunk, lam=lam, seed=seed, name=w.name)
 
 
@@ -185,5 +186,15 @@ def generate_decode(w: Workload | str = "decode_f32", *, seed: int | None = None
     v = rng.standard_normal(shape) * w.qscale
     state = (rng.standard_normal((B, H, D, D)) * w.h0std).astype(np.float32)
     return dict(q=q.astype(np.float32), k=k.astype(np.float32), v=v.astype(np.float32),
-                log_f=log_f.astype(np.float32), state=state, dtype="f32",
+                log_f=log_f.astype(np.float32), z=z.astype(np.float32), state=state, dtype="f32",
                 B=B, H=H, D=D, seed=seed, name=w.name)
+
+
+def lower_bounds(H: int, D: int, lam: float, spread: float = 0.0, seed: int = 7) -> np.ndarray:
+    """A per-channel forget-gate lower bound [H, D] float32: lam everywhere, or
+    lam + spread * U(-1, 1) clipped to [0, 0.99] when spread > 0 (a separate
+    PCG64 stream, so the other inputs do not change)."""
+    if spread <= 0.0:
+        return np.full((H, D), lam, dtype=np.float32)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return np.clip(lam + spread * rng.uniform(-1.0, 1.0, (H, D)), 0.0, 0.99).astype(np.float32)

@@ -356,7 +356,99 @@ def pin_tied_autograd(orc):
     assert rel(y, Y.detach().numpy()) < 1e-13 and rel(ht, S.detach().numpy()) < 1e-13
 
 
+# ---------------------------------------------------------------- gate from its pre-activation
+
+def _gate_inputs(seed, B=1, T=7, H=2, DK=3, DV=2):
+    r = _rng(seed)
+    q = r.standard_normal((B, T, H, DK))
+    v = r.standard_normal((B, T, H, DV))
+    z = r.standard_normal((B, T, H, DK)) * 1.5
+    lam = r.uniform(0.0, 0.9, (H, DK))
+    h0 = r.standard_normal((B, H, DK, DV))
+    return q, v, z, lam, h0
+
+
+def pin_gate_log_sigmoid(orc):
+    """With lam = 0 the gate is a plain sigmoid: log f is torch's logsigmoid and
+    k is sigmoid(-z), over a range that overflows a naive exp; with lam > 0, log f
+    and k against the direct formula at moderate z, and f + k = 1."""
+    import torch
+    import oracle as o
+    z = np.concatenate([np.linspace(-700.0, 700.0, 2801), [-1e-9, 0.0, 1e-9]])
+    tz = torch.tensor(z, dtype=torch.float64)
+    assert np.max(np.abs(o.gate_log_f(z, 0.0) - torch.nn.functional.logsigmoid(tz).numpy())) < 1e-13
+    assert np.max(np.abs(o.gate_k(z, 0.0) - torch.sigmoid(-tz).numpy())) < 1e-15
+    zm = np.linspace(-30.0, 30.0, 601)
+    for lam in (0.1, 0.5, 0.97):
+        direct = np.log(lam + (1.0 - lam) * torch.sigmoid(torch.tensor(zm, dtype=torch.float64)).numpy())
+        assert np.max(np.abs(o.gate_log_f(zm, lam) - direct)) < 1e-14, lam
+        assert np.max(np.abs(np.exp(o.gate_log_f(zm, lam)) + o.gate_k(zm, lam) - 1.0)) < 1e-14, lam
+        assert np.all(o.gate_log_f(zm, lam) >= np.log(lam) - 1e-15)   # f never falls below lam
+
+
+def _loss_gate(orc, q, v, z, lam, h0, dy, dht):
+    import oracle as o
+    y, ht = orc.forward(q, o.gate_k(z, lam), v, o.gate_log_f(z, lam), h0)
+    return float((y * dy).sum() + (ht * dht).sum())
+
+
+def pin_gate_finite_differences(orc):
+    """Central differences of the loss in (q, v, z, lam, h0) against backward_gate."""
+    import oracle as o
+    q, v, z, lam, h0 = _gate_inputs(23)
+    r = _rng(24)
+    dy = r.standard_normal(v.shape)
+    dht = r.standard_normal(h0.shape)
+    dq, dv, dz, dlam, dh0 = o.backward_gate(q, v, z, lam, dy, h0, dht)
+    args = [q, v, z, lam, h0]
+    eps = 1e-6
+    for ai, g in enumerate((dq, dv, dz, dlam, dh0)):
+        x = args[ai]
+        num = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            old = x[idx]
+            x[idx] = old + eps
+            lp = _loss_gate(orc, *args, dy, dht)
+            x[idx] = old - eps
+            lm = _loss_gate(orc, *args, dy, dht)
+            x[idx] = old
+            num[idx] = (lp - lm) / (2 * eps)
+        assert rel(g, num) < 1e-7, ("input", ai, rel(g, num))
+
+
+def pin_gate_autograd(orc):
+    """Gate-mode gradients against torch float64 autograd through a plain loop
+    that forms f = lam + (1 - lam) sigmoid(z) and k = 1 - f itself."""
+    import torch
+    import oracle as o
+    q, v, z, lam, h0 = _gate_inputs(25, B=2, T=9, H=2, DK=4, DV=3)
+    r = _rng(26)
+    dy = r.standard_normal(v.shape)
+    dht = r.standard_normal(h0.shape)
+    ts = [torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, v, z, lam, h0)]
+    tq, tv, tz, tlam, th = ts
+    f = tlam + (1.0 - tlam) * torch.sigmoid(tz)
+    tk = 1.0 - f
+    S = th
+    ys = []
+    for t in range(q.shape[1]):
+        S = f[:, t][..., :, None] * S + tk[:, t][..., :, None] * tv[:, t][..., None, :]
+        ys.append(torch.einsum("bhc,bhcj->bhj", tq[:, t], S))
+    Y = torch.stack(ys, dim=1)
+    L = (Y * torch.tensor(dy)).sum() + (S * torch.tensor(dht)).sum()
+    L.backward()
+    got = o.backward_gate(q, v, z, lam, dy, h0, dht)
+    for g, t in zip(got, ts):
+        assert rel(g, t.grad.numpy()) < 1e-12
+    y, ht = o.forward_gate(q, v, z, lam, h0)
+    assert rel(y, Y.detach().numpy()) < 1e-13 and rel(ht, S.detach().numpy()) < 1e-13
+
+
 ALL_PINS = [pin_closed_form, pin_limit_f_one, pin_limit_f_zero, pin_scalar_scan,
             pin_golden_exact, pin_linearity, pin_state_carry, pin_decode,
             pin_finite_differences, pin_autograd, pin_dlogf_identity, pin_bwd_limits,
-            pin_tied_finite_differences, pin_tied_autograd]
+            pin_tied_finite_differences, pin_tied_autograd,
+            pin_gate_log_sigmoid, pin_gate_finite_differences, pin_gate_autograd]
+GATE_PINS = [pin_gate_log_sigmoid, pin_gate_finite_differences, pin_gate_autograd]

@@ -70,3 +70,53 @@ def test_pins_catch_mutant(tmp_path, name, old, new):
         except Exception as e:  # a crash or NaN also counts as detected
             caught.append(pin.__name__ + ":" + type(e).__name__)
     assert caught, "mutant %s passed every pin" % name
+
+
+# Plausible mistakes in the gate-mode chain rule and gate formula of the
+# oracle (its Python part); each replaces one oracle function for the duration
+# of the test and must fail at least one gate pin.
+def _gate_mutants():
+    import numpy as np
+    o = oracle
+    good_p, good_l, good_k = o.gate_partials, o.gate_log_f, o.gate_k
+
+    def no_inv_f(z, lam):
+        a, b, c, d = good_p(z, lam)
+        f = np.exp(good_l(z, lam))
+        return a * f, b, c * f, d
+
+    def dk_dz_sign(z, lam):
+        a, b, c, d = good_p(z, lam)
+        return a, -b, c, d
+
+    def dlam_from_dz(z, lam):
+        a, b, c, d = good_p(z, lam)
+        return a, b, a, b
+
+    def no_one_minus_lam(z, lam):
+        a, b, c, d = good_p(z, lam)
+        lam = np.asarray(lam, dtype=np.float64)
+        return a / (1.0 - lam), b / (1.0 - lam), c, d
+
+    def logf_no_lam(z, lam):
+        return good_l(z, 0.0 * np.asarray(lam))
+
+    def k_untied(z, lam):
+        return good_k(z, 0.0 * np.asarray(lam))
+
+    return [("gate_partials", no_inv_f), ("gate_partials", dk_dz_sign), ("gate_partials", dlam_from_dz),
+            ("gate_partials", no_one_minus_lam), ("gate_log_f", logf_no_lam), ("gate_k", k_untied)]
+
+
+@pytest.mark.parametrize("which", range(6))
+def test_gate_pins_catch_mutant(which, monkeypatch):
+    name, fn = _gate_mutants()[which]
+    monkeypatch.setattr(oracle, name, fn)
+    orc = oracle.default()
+    caught = []
+    for pin in pins.GATE_PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, "gate mutant %d (%s) passed every gate pin" % (which, name)
