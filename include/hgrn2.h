@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define HGRN2_ABI_VERSION 4
+#define HGRN2_ABI_VERSION 5
 
 typedef enum {
   HGRN2_OK = 0,
@@ -221,6 +221,45 @@ hgrn2_status hgrn2_bwd_chunk_tied(int B, int T, int H, int DK, int DV, int chunk
 hgrn2_status hgrn2_decode_step_tied(int B, int H, int DK, int DV, int dtype, const void *q,
                                     const void *v, const void *log_f, float *state, void *y,
                                     void *stream);
+
+/*
+ * Gate from its pre-activation.  HGRN's forget gate has an additive lower
+ * bound per layer and learns a residual above it (HGRN2 summary §2.2: lower
+ * bounds built per layer, the forget gate learning residuals above them); with
+ * the input gate tied as above:
+ *     f = lb + (1 - lb) * sigmoid(z),        k = 1 - f = (1 - lb) * sigmoid(-z).
+ * These entry points take the pre-activation z [B, T, H, DK] (input dtype, in
+ * place of log_f) and the lower bound lower_bound [H, DK] (float32, one value
+ * per head channel, 0 <= lb < 1; a scalar bound is the same value everywhere;
+ * 4-byte aligned) and form log f and k in the kernels, so no log_f or k
+ * tensor is ever written or read.  Rows past the end of the sequence decay
+ * nothing.  Precondition: z finite.
+ *
+ * hgrn2_bwd_gate returns, with G = dlog_f - f dk the total derivative through
+ * log f (the tied-gate backward's dlog_f) and s = sigmoid(z), s' = sigmoid(-z):
+ *     dz            = G (1 - lb) s s' / f                    [B, T, H, DK], input dtype
+ *     dlower_bound  = sum over b and t of G s' / f            [H, DK], float32, overwritten
+ * and no dk.  dlower_bound is summed per chunk into the workspace and then over
+ * chunks in a fixed order (repeat runs agree bit for bit).  Its workspace is
+ * hgrn2_bwd_gate_workspace_bytes() (the untied size plus B*H*N*DK floats).
+ * For lb = 0 and z below about -88, f underflows in float32 and the dlb term
+ * of that token is infinite (its exact value exceeds the float32 range).
+ * Everything else (layouts, states, errors) is as for the untied calls.
+ */
+size_t hgrn2_bwd_gate_workspace_bytes(int B, int T, int H, int DK, int DV, int chunk, int dtype,
+                                      int have_states);
+hgrn2_status hgrn2_fwd_gate(int B, int T, int H, int DK, int DV, int chunk, int dtype,
+                            const void *q, const void *v, const void *z, const float *lower_bound,
+                            const float *h0, void *y, float *ht, void *states_out, void *ws,
+                            size_t ws_bytes, void *stream);
+hgrn2_status hgrn2_bwd_gate(int B, int T, int H, int DK, int DV, int chunk, int dtype,
+                            const void *q, const void *v, const void *z, const float *lower_bound,
+                            const float *h0, const void *states_in, const void *dy,
+                            const float *dht, void *dq, void *dv, void *dz, float *dlower_bound,
+                            float *dh0, void *ws, size_t ws_bytes, void *stream);
+hgrn2_status hgrn2_decode_step_gate(int B, int H, int DK, int DV, int dtype, const void *q,
+                                    const void *v, const void *z, const float *lower_bound,
+                                    float *state, void *y, void *stream);
 
 #ifdef __cplusplus
 }

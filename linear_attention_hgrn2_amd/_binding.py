@@ -76,6 +76,14 @@ def _lib():
         lib.hgrn2_decode_step_tied.restype = I
         lib.hgrn2_decode_step.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P]
         lib.hgrn2_decode_step.restype = I
+        lib.hgrn2_bwd_gate_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
+        lib.hgrn2_bwd_gate_workspace_bytes.restype = Z
+        lib.hgrn2_fwd_gate.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, Z, P]
+        lib.hgrn2_fwd_gate.restype = I
+        lib.hgrn2_bwd_gate.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
+        lib.hgrn2_bwd_gate.restype = I
+        lib.hgrn2_decode_step_gate.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P]
+        lib.hgrn2_decode_step_gate.restype = I
         _handle = lib
     return _handle
 
@@ -400,6 +408,101 @@ def decode_step_tied(q, v, log_f, state, *, y=None):
     st = _lib().hgrn2_decode_step_tied(B, H, D, D, _DT[dt], _ptr(q), _ptr(v), _ptr(log_f), _ptr(state), _ptr(y),
                                        _stream())
     _check(st, "hgrn2_decode_step_tied")
+    return y
+
+
+def _lb(lower_bound, H, D, device):
+    if lower_bound.shape != (H, D) or lower_bound.dtype != torch.float32 or not lower_bound.is_contiguous() \
+            or lower_bound.device != device:
+        raise ValueError("lower_bound: expected a contiguous float32 tensor of shape %s on %s" % ((H, D), device))
+
+
+def fwd_gate(q, v, z, lower_bound, h0=None, *, chunk=64, want_ht=True, want_states=False, want_y=True,
+             y=None, ht=None, states=None, ws=None):
+    """Chunked forward with the gate formed from its pre-activation z and the
+    lower bound [H, D] (f = lb + (1 - lb) sigmoid(z), k = 1 - f).
+    Returns (y or None, ht or None, states or None)."""
+    B, T, H, D = q.shape
+    dt = q.dtype
+    if dt not in _DT:
+        raise ValueError("dtype must be float32 or bfloat16")
+    for n, t in (("q", q), ("v", v), ("z", z)):
+        _tok(n, t, B, T, H, D, dt)
+    _lb(lower_bound, H, D, q.device)
+    _st("h0", h0, B, H, D)
+    if want_y and y is None:
+        y = torch.empty_like(q)
+    if y is not None:
+        _tok("y", y, B, T, H, D, dt)
+    if want_ht and ht is None:
+        ht = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+    _st("ht", ht, B, H, D)
+    if want_states and states is None:
+        states = torch.empty(states_shape(B, T, H, D, chunk), dtype=dt, device=q.device)
+    if states is not None:
+        _states_ok(states, B, T, H, D, chunk, dt)
+    ws_bytes = 0
+    if states is None:
+        need = int(_lib().hgrn2_fwd_workspace_bytes(B, T, H, D, D, chunk, _DT[dt], 0))
+        if ws is None:
+            ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_bytes = ws.numel() * ws.element_size()
+    st = _lib().hgrn2_fwd_gate(B, T, H, D, D, chunk, _DT[dt], _ptr(q), _ptr(v), _ptr(z), _ptr(lower_bound),
+                               _ptr(h0), _ptr(y), _ptr(ht), _ptr(states), _ptr(ws), ws_bytes, _stream())
+    _check(st, "hgrn2_fwd_gate")
+    return y, ht, states
+
+
+def bwd_gate(q, v, z, lower_bound, dy, h0=None, dht=None, states=None, *, chunk=64, want_dh0=True,
+             dq=None, dv=None, dz=None, dlower_bound=None, dh0=None, ws=None):
+    """Chunked backward with the gate formed from its pre-activation.
+    Returns (dq, dv, dz, dlower_bound [H, D] float32, dh0 or None)."""
+    B, T, H, D = q.shape
+    dt = q.dtype
+    for n, t in (("q", q), ("v", v), ("z", z), ("dy", dy)):
+        _tok(n, t, B, T, H, D, dt)
+    _lb(lower_bound, H, D, q.device)
+    _st("h0", h0, B, H, D)
+    _st("dht", dht, B, H, D)
+    dq = torch.empty_like(q) if dq is None else dq
+    dv = torch.empty_like(v) if dv is None else dv
+    dz = torch.empty_like(z) if dz is None else dz
+    for n, t in (("dq", dq), ("dv", dv), ("dz", dz)):
+        _tok(n, t, B, T, H, D, dt)
+    if dlower_bound is None:
+        dlower_bound = torch.empty((H, D), dtype=torch.float32, device=q.device)
+    _lb(dlower_bound, H, D, q.device)
+    if want_dh0 and dh0 is None:
+        dh0 = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+    _st("dh0", dh0, B, H, D)
+    if states is not None:
+        _states_ok(states, B, T, H, D, chunk, dt)
+    need = int(_lib().hgrn2_bwd_gate_workspace_bytes(B, T, H, D, D, chunk, _DT[dt], int(states is not None)))
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = ws.numel() * ws.element_size()
+    st = _lib().hgrn2_bwd_gate(B, T, H, D, D, chunk, _DT[dt], _ptr(q), _ptr(v), _ptr(z), _ptr(lower_bound),
+                               _ptr(h0), _ptr(states), _ptr(dy), _ptr(dht), _ptr(dq), _ptr(dv), _ptr(dz),
+                               _ptr(dlower_bound), _ptr(dh0), _ptr(ws), ws_bytes, _stream())
+    _check(st, "hgrn2_bwd_gate")
+    return dq, dv, dz, dlower_bound, dh0
+
+
+def decode_step_gate(q, v, z, lower_bound, state, *, y=None):
+    """One recurrent step with the gate formed from z [B, H, D] and the lower
+    bound [H, D]; `state` is updated in place.  Returns y."""
+    B, H, D = q.shape
+    dt = q.dtype
+    for n, t in (("q", q), ("v", v), ("z", z)):
+        if t.shape != (B, H, D) or t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s: expected a contiguous %s CUDA tensor of shape %s" % (n, dt, (B, H, D)))
+    _lb(lower_bound, H, D, q.device)
+    _st("state", state, B, H, D)
+    if y is None:
+        y = torch.empty_like(q)
+    st = _lib().hgrn2_decode_step_gate(B, H, D, D, _DT[dt], _ptr(q), _ptr(v), _ptr(z), _ptr(lower_bound),
+                                       _ptr(state), _ptr(y), _stream())
+    _check(st, "hgrn2_decode_step_gate")
     return y
 
 

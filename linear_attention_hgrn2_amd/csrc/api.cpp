@@ -89,14 +89,26 @@ hgrn2_status hip_status(hipError_t e, const char *what) {
   return fail(HGRN2_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-bool fwd_exists(int dtype, int D, int C, bool tied = false) {
-  return hgrn2::dispatch_scan(dtype, D, C, false, tied, nullptr, nullptr) == hipSuccess &&
-         hgrn2::dispatch_scan(dtype, D, C, true, false, nullptr, nullptr) == hipSuccess &&
-         hgrn2::dispatch_chunk_fwd(dtype, D, C, tied, nullptr, nullptr) == hipSuccess;
+using hgrn2::kGate;
+using hgrn2::kTied;
+using hgrn2::kUntied;
+
+// the adjoint scan reads log f (formed from z in gate mode) and never k
+int adjoint_gm(int gm) { return gm == kGate ? kGate : kUntied; }
+
+bool fwd_exists(int dtype, int D, int C, int gm = kUntied) {
+  return hgrn2::dispatch_scan(dtype, D, C, false, gm, nullptr, nullptr) == hipSuccess &&
+         hgrn2::dispatch_scan(dtype, D, C, true, adjoint_gm(gm), nullptr, nullptr) == hipSuccess &&
+         hgrn2::dispatch_chunk_fwd(dtype, D, C, gm, nullptr, nullptr) == hipSuccess;
 }
 
-bool bwd_exists(int dtype, int D, int C, bool tied = false) {
-  return hgrn2::dispatch_chunk_bwd(dtype, D, C, tied, nullptr, nullptr) == hipSuccess;
+bool bwd_exists(int dtype, int D, int C, int gm = kUntied) {
+  return hgrn2::dispatch_chunk_bwd(dtype, D, C, gm, nullptr, nullptr) == hipSuccess;
+}
+
+// bytes of the per-chunk lower-bound gradient sums (gate mode), [B, H, N, DK] float32
+size_t dlb_part_bytes(int B, int T, int H, int DK, int chunk) {
+  return (size_t)B * H * (size_t)((T + chunk - 1) / chunk) * DK * sizeof(float);
 }
 
 // bytes of the state adjoints at every chunk end, [B, H, N, DK, DV] in the input dtype
@@ -105,9 +117,9 @@ size_t adjoint_bytes(int B, int T, int H, int DK, int DV, int chunk, int dtype) 
 }
 
 
-hgrn2_status launch_scan(int dtype, int D, int chunk, bool reverse, bool tied, int B, int T, int H, const void *x,
-                         const void *z, const void *log_f, const float *s_in, void *states, float *s_out,
-                         void *stream, const char *what) {
+hgrn2_status launch_scan(int dtype, int D, int chunk, bool reverse, int gm, int B, int T, int H, const void *x,
+                         const void *z, const void *log_f, const float *lb, const float *s_in, void *states,
+                         float *s_out, void *stream, const char *what) {
   hgrn2::ScanArgs sa;
   sa.B = B;
   sa.T = T;
@@ -116,15 +128,16 @@ hgrn2_status launch_scan(int dtype, int D, int chunk, bool reverse, bool tied, i
   sa.x = x;
   sa.z = z;
   sa.log_f = log_f;
+  sa.lb = lb;
   sa.s_in = s_in;
   sa.states = states;
   sa.s_out = s_out;
-  return hip_status(hgrn2::dispatch_scan(dtype, D, chunk, reverse, tied, &sa, (hipStream_t)stream), what);
+  return hip_status(hgrn2::dispatch_scan(dtype, D, chunk, reverse, gm, &sa, (hipStream_t)stream), what);
 }
 
-hgrn2_status launch_chunk_fwd(int dtype, int D, int chunk, bool tied, int B, int T, int H, const void *q, const void *k,
-                              const void *v, const void *log_f, const void *states, void *y, void *stream,
-                              const char *what) {
+hgrn2_status launch_chunk_fwd(int dtype, int D, int chunk, int gm, int B, int T, int H, const void *q, const void *k,
+                              const void *v, const void *log_f, const float *lb, const void *states, void *y,
+                              void *stream, const char *what) {
   hgrn2::ChunkFwdArgs ca;
   ca.B = B;
   ca.T = T;
@@ -134,15 +147,16 @@ hgrn2_status launch_chunk_fwd(int dtype, int D, int chunk, bool tied, int B, int
   ca.k = k;
   ca.v = v;
   ca.log_f = log_f;
+  ca.lb = lb;
   ca.states = states;
   ca.y = y;
-  return hip_status(hgrn2::dispatch_chunk_fwd(dtype, D, chunk, tied, &ca, (hipStream_t)stream), what);
+  return hip_status(hgrn2::dispatch_chunk_fwd(dtype, D, chunk, gm, &ca, (hipStream_t)stream), what);
 }
 
-hgrn2_status launch_chunk_bwd(int dtype, int D, int chunk, bool tied, int B, int T, int H, const void *q, const void *k,
-                              const void *v, const void *log_f, const void *dy, const void *states,
-                              const void *lam, void *dq, void *dk, void *dv, void *dlog_f, void *stream,
-                              const char *what) {
+hgrn2_status launch_chunk_bwd(int dtype, int D, int chunk, int gm, int B, int T, int H, const void *q, const void *k,
+                              const void *v, const void *log_f, const float *lb, const void *dy, const void *states,
+                              const void *lam, void *dq, void *dk, void *dv, void *dlog_f, float *dlb_part,
+                              void *stream, const char *what) {
   hgrn2::ChunkBwdArgs a;
   a.B = B;
   a.T = T;
@@ -159,7 +173,9 @@ hgrn2_status launch_chunk_bwd(int dtype, int D, int chunk, bool tied, int B, int
   a.dk = dk;
   a.dv = dv;
   a.dlog_f = dlog_f;
-  return hip_status(hgrn2::dispatch_chunk_bwd(dtype, D, chunk, tied, &a, (hipStream_t)stream), what);
+  a.lb = lb;
+  a.dlb = dlb_part;
+  return hip_status(hgrn2::dispatch_chunk_bwd(dtype, D, chunk, gm, &a, (hipStream_t)stream), what);
 }
 
 }  // namespace
@@ -209,25 +225,40 @@ size_t hgrn2_bwd_workspace_bytes(int B, int T, int H, int DK, int DV, int chunk,
          (have_states ? 0 : hgrn2_states_bytes(B, T, H, DK, DV, chunk, dtype));
 }
 
-// ---- implementations shared by the independent-gate and tied-gate entry
-// points.  tied: k = 1 - exp(log f) is formed in the kernels (k is NULL), and
-// the backward writes the total dlog f and no dk (dk is NULL).
+// ---- implementations shared by the entry points of the three gate modes.
+// kTied: k = 1 - exp(log f) is formed in the kernels (k is NULL), and the
+// backward writes the total dlog f and no dk (dk is NULL).  kGate: the log_f
+// pointer carries the pre-activation z, lb [H, DK] the lower bound; log f and
+// k are formed in the kernels, and the backward writes dz (through the dlog_f
+// pointer) and dlb [H, DK].
 
-static hgrn2_status need_k(bool tied, const void *k, const char *name) {
-  if (tied) return HGRN2_OK;
+static hgrn2_status need_k(int gm, const void *k, const char *name) {
+  if (gm != kUntied) return HGRN2_OK;
   return check_ptrs({{name, k}}, {});
 }
 
-static hgrn2_status fwd_impl(bool tied, const char *fn, int B, int T, int H, int DK, int DV, int chunk, int dtype,
-                             const void *q, const void *k, const void *v, const void *log_f, const float *h0,
-                             void *y, float *ht, void *states_out, void *ws, size_t ws_bytes, void *stream) {
+static hgrn2_status need_lb(int gm, const void *lb, const char *name) {
+  if (gm != kGate) return HGRN2_OK;
+  if (!lb) return fail(HGRN2_ERR_INVALID_ARG, std::string(name) + " is NULL");
+  if (((uintptr_t)lb & 3u) != 0) return fail(HGRN2_ERR_INVALID_ARG, std::string(name) + " is not 4-byte aligned");
+  return HGRN2_OK;
+}
+
+static const char *gate_name(int gm) { return gm == kGate ? "z" : "log_f"; }
+static const char *dgate_name(int gm) { return gm == kGate ? "dz" : "dlog_f"; }
+
+static hgrn2_status fwd_impl(int gm, const char *fn, int B, int T, int H, int DK, int DV, int chunk, int dtype,
+                             const void *q, const void *k, const void *v, const void *log_f, const float *lb,
+                             const float *h0, void *y, float *ht, void *states_out, void *ws, size_t ws_bytes,
+                             void *stream) {
   hgrn2_status st = check_common(B, T, H, DK, DV, chunk, dtype);
   if (st != HGRN2_OK) return st;
-  st = check_ptrs({{"q", q}, {"v", v}, {"log_f", log_f}},
+  st = check_ptrs({{"q", q}, {"v", v}, {gate_name(gm), log_f}},
                   {{"h0", h0}, {"y", y}, {"ht", ht}, {"states_out", states_out}, {"ws", ws}});
-  if (st == HGRN2_OK) st = need_k(tied, k, "k");
+  if (st == HGRN2_OK) st = need_k(gm, k, "k");
+  if (st == HGRN2_OK) st = need_lb(gm, lb, "lower_bound");
   if (st != HGRN2_OK) return st;
-  if (!fwd_exists(dtype, DK, chunk, tied))
+  if (!fwd_exists(dtype, DK, chunk, gm))
     return fail(HGRN2_ERR_UNSUPPORTED, "no forward kernel for this D, chunk and dtype");
   const size_t tok = (size_t)B * T * H * DK * dsize(dtype);
   const size_t sb = (size_t)B * H * DK * DV * sizeof(float);
@@ -240,85 +271,105 @@ static hgrn2_status fwd_impl(bool tied, const char *fn, int B, int T, int H, int
   }
   // ht may be exactly h0 (each workgroup reads its slice of h0 before it
   // writes the same slice of ht); any other overlap is an error.
-  const Range ins[] = {{"q", q, tok}, {"k", tied ? nullptr : k, tok}, {"v", v, tok}, {"log_f", log_f, tok},
-                       {"h0", (ht == h0) ? nullptr : h0, sb}};
+  const size_t lbb = (size_t)H * DK * sizeof(float);
+  const Range ins[] = {{"q", q, tok},
+                       {"k", gm != kUntied ? nullptr : k, tok},
+                       {"v", v, tok},
+                       {gate_name(gm), log_f, tok},
+                       {"h0", (ht == h0) ? nullptr : h0, sb},
+                       {"lower_bound", gm == kGate ? lb : nullptr, lbb}};
   const Range outs[] = {{"y", y, tok}, {"ht", ht, sb}, {states_out ? "states_out" : "ws", states, stb}};
   std::string msg;
-  if (!check_aliasing(ins, 5, outs, 3, msg)) return fail(HGRN2_ERR_INVALID_ARG, msg);
+  if (!check_aliasing(ins, 6, outs, 3, msg)) return fail(HGRN2_ERR_INVALID_ARG, msg);
   if (ht == h0 && ht && (overlap(Range{"y", y, tok}, Range{"h0", h0, sb}) ||
                          overlap(Range{"states", states, stb}, Range{"h0", h0, sb})))
     return fail(HGRN2_ERR_INVALID_ARG, "an output overlaps h0");
 
-  st = launch_scan(dtype, DK, chunk, false, tied, B, T, H, tied ? nullptr : k, v, log_f, h0, states, ht, stream,
-                   fn);
+  if (gm != kUntied) k = nullptr;
+  if (gm != kGate) lb = nullptr;
+  st = launch_scan(dtype, DK, chunk, false, gm, B, T, H, k, v, log_f, lb, h0, states, ht, stream, fn);
   if (st != HGRN2_OK || !y) return st;
-  return launch_chunk_fwd(dtype, DK, chunk, tied, B, T, H, q, tied ? nullptr : k, v, log_f, states, y, stream, fn);
+  return launch_chunk_fwd(dtype, DK, chunk, gm, B, T, H, q, k, v, log_f, lb, states, y, stream, fn);
 }
 
-static hgrn2_status bwd_impl(bool tied, const char *fn, int B, int T, int H, int DK, int DV, int chunk, int dtype,
-                             const void *q, const void *k, const void *v, const void *log_f, const float *h0,
-                             const void *states_in, const void *dy, const float *dht, void *dq, void *dk, void *dv,
-                             void *dlog_f, float *dh0, void *ws, size_t ws_bytes, void *stream) {
+static hgrn2_status bwd_impl(int gm, const char *fn, int B, int T, int H, int DK, int DV, int chunk, int dtype,
+                             const void *q, const void *k, const void *v, const void *log_f, const float *lb,
+                             const float *h0, const void *states_in, const void *dy, const float *dht, void *dq,
+                             void *dk, void *dv, void *dlog_f, float *dlb, float *dh0, void *ws, size_t ws_bytes,
+                             void *stream) {
   hgrn2_status st = check_common(B, T, H, DK, DV, chunk, dtype);
   if (st != HGRN2_OK) return st;
-  st = check_ptrs({{"q", q}, {"v", v}, {"log_f", log_f}, {"dy", dy}, {"dq", dq}, {"dv", dv}, {"dlog_f", dlog_f}},
+  st = check_ptrs({{"q", q}, {"v", v}, {gate_name(gm), log_f}, {"dy", dy}, {"dq", dq}, {"dv", dv},
+                   {dgate_name(gm), dlog_f}},
                   {{"h0", h0}, {"states_in", states_in}, {"dht", dht}, {"dh0", dh0}, {"ws", ws}});
-  if (st == HGRN2_OK) st = need_k(tied, k, "k");
-  if (st == HGRN2_OK) st = need_k(tied, dk, "dk");
+  if (st == HGRN2_OK) st = need_k(gm, k, "k");
+  if (st == HGRN2_OK) st = need_k(gm, dk, "dk");
+  if (st == HGRN2_OK) st = need_lb(gm, lb, "lower_bound");
+  if (st == HGRN2_OK) st = need_lb(gm, dlb, "dlower_bound");
   if (st != HGRN2_OK) return st;
-  if (!bwd_exists(dtype, DK, chunk, tied) || !fwd_exists(dtype, DK, chunk, tied))
+  if (!bwd_exists(dtype, DK, chunk, gm) || !fwd_exists(dtype, DK, chunk, gm))
     return fail(HGRN2_ERR_UNSUPPORTED, "no backward kernel for this D, chunk and dtype");
   const size_t tok = (size_t)B * T * H * DK * dsize(dtype);
   const size_t sb = (size_t)B * H * DK * DV * sizeof(float);
   const size_t stb = hgrn2_states_bytes(B, T, H, DK, DV, chunk, dtype);
   const size_t lamb = adjoint_bytes(B, T, H, DK, DV, chunk, dtype);
-  const size_t need = lamb + (states_in ? 0 : stb);
+  const size_t partb = gm == kGate ? dlb_part_bytes(B, T, H, DK, chunk) : 0;
+  const size_t need = lamb + partb + (states_in ? 0 : stb);
   if (!ws || ws_bytes < need)
     return fail(HGRN2_ERR_WORKSPACE, "workspace smaller than hgrn2_bwd_workspace_bytes()");
-  if (tied) k = dk = nullptr;
+  if (gm != kUntied) k = dk = nullptr;
+  if (gm != kGate) lb = dlb = nullptr;
+  const size_t lbb = (size_t)H * DK * sizeof(float);
   const void *states = states_in;
-  const Range ins[] = {{"q", q, tok},   {"k", k, tok},   {"v", v, tok},          {"log_f", log_f, tok},
-                       {"h0", h0, sb},  {"dy", dy, tok}, {"dht", dht, sb},       {"states_in", states_in, stb}};
-  const Range outs[] = {{"dq", dq, tok},         {"dk", dk, tok},  {"dv", dv, tok},
-                        {"dlog_f", dlog_f, tok}, {"dh0", dh0, sb}, {"ws", ws, need}};
+  const Range ins[] = {{"q", q, tok},           {"k", k, tok},          {"v", v, tok},
+                       {gate_name(gm), log_f, tok}, {"h0", h0, sb},     {"dy", dy, tok},
+                       {"dht", dht, sb},        {"states_in", states_in, stb}, {"lower_bound", lb, lbb}};
+  const Range outs[] = {{"dq", dq, tok},  {"dk", dk, tok},          {"dv", dv, tok}, {dgate_name(gm), dlog_f, tok},
+                        {"dh0", dh0, sb}, {"dlower_bound", dlb, lbb}, {"ws", ws, need}};
   std::string msg;
-  if (!check_aliasing(ins, 8, outs, 6, msg)) return fail(HGRN2_ERR_INVALID_ARG, msg);
+  if (!check_aliasing(ins, 9, outs, 7, msg)) return fail(HGRN2_ERR_INVALID_ARG, msg);
 
+  // workspace: adjoints, then (gate mode) the per-chunk dlb sums, then (if
+  // not given) the recomputed states
+  float *part = gm == kGate ? (float *)((char *)ws + lamb) : nullptr;
   if (!states) {
     // recompute the chunk-boundary states with the forward state scan
-    void *sws = (char *)ws + lamb;
-    st = launch_scan(dtype, DK, chunk, false, tied, B, T, H, k, v, log_f, h0, sws, nullptr, stream, fn);
+    void *sws = (char *)ws + lamb + partb;
+    st = launch_scan(dtype, DK, chunk, false, gm, B, T, H, k, v, log_f, lb, h0, sws, nullptr, stream, fn);
     if (st != HGRN2_OK) return st;
     states = sws;
   }
   // the state adjoint at every chunk end (reverse scan), then all chunks' gradients
-  st = launch_scan(dtype, DK, chunk, true, false, B, T, H, q, dy, log_f, dht, ws, dh0, stream, fn);
+  st = launch_scan(dtype, DK, chunk, true, adjoint_gm(gm), B, T, H, q, dy, log_f, lb, dht, ws, dh0, stream, fn);
   if (st != HGRN2_OK) return st;
-  return launch_chunk_bwd(dtype, DK, chunk, tied, B, T, H, q, k, v, log_f, dy, states, ws, dq, dk, dv, dlog_f,
-                          stream, fn);
+  st = launch_chunk_bwd(dtype, DK, chunk, gm, B, T, H, q, k, v, log_f, lb, dy, states, ws, dq, dk, dv, dlog_f, part,
+                        stream, fn);
+  if (st != HGRN2_OK || gm != kGate) return st;
+  return hip_status(hgrn2::dispatch_dlb_reduce(B, H, hgrn2_num_chunks(T, chunk), DK, part, dlb, (hipStream_t)stream),
+                    fn);
 }
 
-static hgrn2_status fwd_chunk_impl(bool tied, const char *fn, int B, int T, int H, int DK, int DV, int chunk,
+static hgrn2_status fwd_chunk_impl(int gm, const char *fn, int B, int T, int H, int DK, int DV, int chunk,
                                    int dtype, const void *q, const void *k, const void *v, const void *log_f,
                                    const void *states, void *y, void *stream) {
   hgrn2_status st = check_common(B, T, H, DK, DV, chunk, dtype);
   if (st != HGRN2_OK) return st;
   st = check_ptrs({{"q", q}, {"v", v}, {"log_f", log_f}, {"states", states}, {"y", y}}, {});
-  if (st == HGRN2_OK) st = need_k(tied, k, "k");
+  if (st == HGRN2_OK) st = need_k(gm, k, "k");
   if (st != HGRN2_OK) return st;
-  if (hgrn2::dispatch_chunk_fwd(dtype, DK, chunk, tied, nullptr, nullptr) != hipSuccess)
+  if (hgrn2::dispatch_chunk_fwd(dtype, DK, chunk, gm, nullptr, nullptr) != hipSuccess)
     return fail(HGRN2_ERR_UNSUPPORTED, "no forward kernel for this D, chunk and dtype");
-  if (tied) k = nullptr;
+  if (gm != kUntied) k = nullptr;
   const size_t tok = (size_t)B * T * H * DK * dsize(dtype);
   const size_t stb = hgrn2_states_bytes(B, T, H, DK, DV, chunk, dtype);
   const Range ins[] = {{"q", q, tok}, {"k", k, tok}, {"v", v, tok}, {"log_f", log_f, tok}, {"states", states, stb}};
   const Range outs[] = {{"y", y, tok}};
   std::string msg;
   if (!check_aliasing(ins, 5, outs, 1, msg)) return fail(HGRN2_ERR_INVALID_ARG, msg);
-  return launch_chunk_fwd(dtype, DK, chunk, tied, B, T, H, q, k, v, log_f, states, y, stream, fn);
+  return launch_chunk_fwd(dtype, DK, chunk, gm, B, T, H, q, k, v, log_f, nullptr, states, y, stream, fn);
 }
 
-static hgrn2_status bwd_chunk_impl(bool tied, const char *fn, int B, int T, int H, int DK, int DV, int chunk,
+static hgrn2_status bwd_chunk_impl(int gm, const char *fn, int B, int T, int H, int DK, int DV, int chunk,
                                    int dtype, const void *q, const void *k, const void *v, const void *log_f,
                                    const void *states, const void *adjoints, const void *dy, void *dq, void *dk,
                                    void *dv, void *dlog_f, void *stream) {
@@ -327,12 +378,12 @@ static hgrn2_status bwd_chunk_impl(bool tied, const char *fn, int B, int T, int 
   st = check_ptrs({{"q", q}, {"v", v}, {"log_f", log_f}, {"states", states}, {"adjoints", adjoints}, {"dy", dy},
                    {"dq", dq}, {"dv", dv}, {"dlog_f", dlog_f}},
                   {});
-  if (st == HGRN2_OK) st = need_k(tied, k, "k");
-  if (st == HGRN2_OK) st = need_k(tied, dk, "dk");
+  if (st == HGRN2_OK) st = need_k(gm, k, "k");
+  if (st == HGRN2_OK) st = need_k(gm, dk, "dk");
   if (st != HGRN2_OK) return st;
-  if (!bwd_exists(dtype, DK, chunk, tied))
+  if (!bwd_exists(dtype, DK, chunk, gm))
     return fail(HGRN2_ERR_UNSUPPORTED, "no backward kernel for this D, chunk and dtype");
-  if (tied) k = dk = nullptr;
+  if (gm != kUntied) k = dk = nullptr;
   const size_t tok = (size_t)B * T * H * DK * dsize(dtype);
   const size_t stb = hgrn2_states_bytes(B, T, H, DK, DV, chunk, dtype);
   const size_t lamb = adjoint_bytes(B, T, H, DK, DV, chunk, dtype);
@@ -342,27 +393,31 @@ static hgrn2_status bwd_chunk_impl(bool tied, const char *fn, int B, int T, int 
   const Range outs[] = {{"dq", dq, tok}, {"dk", dk, tok}, {"dv", dv, tok}, {"dlog_f", dlog_f, tok}};
   std::string msg;
   if (!check_aliasing(ins, 7, outs, 4, msg)) return fail(HGRN2_ERR_INVALID_ARG, msg);
-  return launch_chunk_bwd(dtype, DK, chunk, tied, B, T, H, q, k, v, log_f, dy, states, adjoints, dq, dk, dv,
-                          dlog_f, stream, fn);
+  return launch_chunk_bwd(dtype, DK, chunk, gm, B, T, H, q, k, v, log_f, nullptr, dy, states, adjoints, dq, dk, dv,
+                          dlog_f, nullptr, stream, fn);
 }
 
-static hgrn2_status decode_impl(bool tied, const char *fn, int B, int H, int DK, int DV, int dtype, const void *q,
-                                const void *k, const void *v, const void *log_f, float *state, void *y,
-                                void *stream) {
+static hgrn2_status decode_impl(int gm, const char *fn, int B, int H, int DK, int DV, int dtype, const void *q,
+                                const void *k, const void *v, const void *log_f, const float *lb, float *state,
+                                void *y, void *stream) {
   if (B <= 0 || H <= 0) return fail(HGRN2_ERR_INVALID_ARG, "B and H must be >= 1");
   if ((long long)B * H > (1LL << 30)) return fail(HGRN2_ERR_INVALID_ARG, "problem too large");
   if (!valid_dtype(dtype)) return fail(HGRN2_ERR_INVALID_ARG, "dtype must be HGRN2_F32 or HGRN2_BF16");
   if (DK != DV || !valid_d(DK)) return fail(HGRN2_ERR_UNSUPPORTED, "need DK == DV in {16, 32, 64, 128}");
-  hgrn2_status st = check_ptrs({{"q", q}, {"v", v}, {"log_f", log_f}, {"state", state}, {"y", y}}, {});
-  if (st == HGRN2_OK) st = need_k(tied, k, "k");
+  hgrn2_status st = check_ptrs({{"q", q}, {"v", v}, {gate_name(gm), log_f}, {"state", state}, {"y", y}}, {});
+  if (st == HGRN2_OK) st = need_k(gm, k, "k");
+  if (st == HGRN2_OK) st = need_lb(gm, lb, "lower_bound");
   if (st != HGRN2_OK) return st;
-  if (tied) k = nullptr;
+  if (gm != kUntied) k = nullptr;
+  if (gm != kGate) lb = nullptr;
   const size_t vec = (size_t)B * H * DK * dsize(dtype);
   const size_t sb = (size_t)B * H * DK * DV * sizeof(float);
-  const Range ins[] = {{"q", q, vec}, {"k", k, vec}, {"v", v, vec}, {"log_f", log_f, vec}};
+  const size_t lbb = (size_t)H * DK * sizeof(float);
+  const Range ins[] = {{"q", q, vec}, {"k", k, vec}, {"v", v, vec}, {gate_name(gm), log_f, vec},
+                       {"lower_bound", lb, lbb}};
   const Range outs[] = {{"y", y, vec}, {"state", state, sb}};
   std::string msg;
-  if (!check_aliasing(ins, 4, outs, 2, msg)) return fail(HGRN2_ERR_INVALID_ARG, msg);
+  if (!check_aliasing(ins, 5, outs, 2, msg)) return fail(HGRN2_ERR_INVALID_ARG, msg);
   hgrn2::DecodeArgs a;
   a.B = B;
   a.H = H;
@@ -370,9 +425,10 @@ static hgrn2_status decode_impl(bool tied, const char *fn, int B, int H, int DK,
   a.k = k;
   a.v = v;
   a.log_f = log_f;
+  a.lb = lb;
   a.state = state;
   a.y = y;
-  return hip_status(hgrn2::dispatch_decode(dtype, DK, tied, a, (hipStream_t)stream), fn);
+  return hip_status(hgrn2::dispatch_decode(dtype, DK, gm, a, (hipStream_t)stream), fn);
 }
 
 // ---- independent gates
@@ -380,8 +436,8 @@ static hgrn2_status decode_impl(bool tied, const char *fn, int B, int H, int DK,
 hgrn2_status hgrn2_fwd(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
                        const void *k, const void *v, const void *log_f, const float *h0, void *y,
                        float *ht, void *states_out, void *ws, size_t ws_bytes, void *stream) {
-  return fwd_impl(false, "hgrn2_fwd", B, T, H, DK, DV, chunk, dtype, q, k, v, log_f, h0, y, ht, states_out, ws,
-                  ws_bytes, stream);
+  return fwd_impl(kUntied, "hgrn2_fwd", B, T, H, DK, DV, chunk, dtype, q, k, v, log_f, nullptr, h0, y, ht,
+                  states_out, ws, ws_bytes, stream);
 }
 
 hgrn2_status hgrn2_bwd(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
@@ -389,14 +445,14 @@ hgrn2_status hgrn2_bwd(int B, int T, int H, int DK, int DV, int chunk, int dtype
                        const void *states_in, const void *dy, const float *dht, void *dq,
                        void *dk, void *dv, void *dlog_f, float *dh0, void *ws, size_t ws_bytes,
                        void *stream) {
-  return bwd_impl(false, "hgrn2_bwd", B, T, H, DK, DV, chunk, dtype, q, k, v, log_f, h0, states_in, dy, dht, dq, dk,
-                  dv, dlog_f, dh0, ws, ws_bytes, stream);
+  return bwd_impl(kUntied, "hgrn2_bwd", B, T, H, DK, DV, chunk, dtype, q, k, v, log_f, nullptr, h0, states_in, dy,
+                  dht, dq, dk, dv, dlog_f, nullptr, dh0, ws, ws_bytes, stream);
 }
 
 hgrn2_status hgrn2_fwd_chunk(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
                              const void *k, const void *v, const void *log_f, const void *states, void *y,
                              void *stream) {
-  return fwd_chunk_impl(false, "hgrn2_fwd_chunk", B, T, H, DK, DV, chunk, dtype, q, k, v, log_f, states, y,
+  return fwd_chunk_impl(kUntied, "hgrn2_fwd_chunk", B, T, H, DK, DV, chunk, dtype, q, k, v, log_f, states, y,
                         stream);
 }
 
@@ -407,7 +463,7 @@ hgrn2_status hgrn2_bwd_adjoint(int B, int T, int H, int DK, int DV, int chunk, i
   if (st != HGRN2_OK) return st;
   st = check_ptrs({{"q", q}, {"log_f", log_f}, {"dy", dy}, {"adjoints", adjoints}}, {{"dht", dht}, {"dh0", dh0}});
   if (st != HGRN2_OK) return st;
-  if (hgrn2::dispatch_scan(dtype, DK, chunk, true, false, nullptr, nullptr) != hipSuccess)
+  if (hgrn2::dispatch_scan(dtype, DK, chunk, true, kUntied, nullptr, nullptr) != hipSuccess)
     return fail(HGRN2_ERR_UNSUPPORTED, "no adjoint scan kernel for this D, chunk and dtype");
   const size_t tok = (size_t)B * T * H * DK * dsize(dtype);
   const size_t sb = (size_t)B * H * DK * DV * sizeof(float);
@@ -416,7 +472,7 @@ hgrn2_status hgrn2_bwd_adjoint(int B, int T, int H, int DK, int DV, int chunk, i
   const Range outs[] = {{"adjoints", adjoints, lamb}, {"dh0", dh0, sb}};
   std::string msg;
   if (!check_aliasing(ins, 4, outs, 2, msg)) return fail(HGRN2_ERR_INVALID_ARG, msg);
-  return launch_scan(dtype, DK, chunk, true, false, B, T, H, q, dy, log_f, dht, adjoints, dh0, stream,
+  return launch_scan(dtype, DK, chunk, true, kUntied, B, T, H, q, dy, log_f, nullptr, dht, adjoints, dh0, stream,
                      "hgrn2_bwd_adjoint");
 }
 
@@ -424,13 +480,13 @@ hgrn2_status hgrn2_bwd_chunk(int B, int T, int H, int DK, int DV, int chunk, int
                              const void *k, const void *v, const void *log_f, const void *states,
                              const void *adjoints, const void *dy, void *dq, void *dk, void *dv, void *dlog_f,
                              void *stream) {
-  return bwd_chunk_impl(false, "hgrn2_bwd_chunk", B, T, H, DK, DV, chunk, dtype, q, k, v, log_f, states, adjoints,
+  return bwd_chunk_impl(kUntied, "hgrn2_bwd_chunk", B, T, H, DK, DV, chunk, dtype, q, k, v, log_f, states, adjoints,
                         dy, dq, dk, dv, dlog_f, stream);
 }
 
 hgrn2_status hgrn2_decode_step(int B, int H, int DK, int DV, int dtype, const void *q, const void *k,
                                const void *v, const void *log_f, float *state, void *y, void *stream) {
-  return decode_impl(false, "hgrn2_decode_step", B, H, DK, DV, dtype, q, k, v, log_f, state, y, stream);
+  return decode_impl(kUntied, "hgrn2_decode_step", B, H, DK, DV, dtype, q, k, v, log_f, nullptr, state, y, stream);
 }
 
 // ---- tied gates (k = 1 - exp(log f))
@@ -438,7 +494,7 @@ hgrn2_status hgrn2_decode_step(int B, int H, int DK, int DV, int dtype, const vo
 hgrn2_status hgrn2_fwd_tied(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
                             const void *v, const void *log_f, const float *h0, void *y, float *ht,
                             void *states_out, void *ws, size_t ws_bytes, void *stream) {
-  return fwd_impl(true, "hgrn2_fwd_tied", B, T, H, DK, DV, chunk, dtype, q, nullptr, v, log_f, h0, y, ht,
+  return fwd_impl(kTied, "hgrn2_fwd_tied", B, T, H, DK, DV, chunk, dtype, q, nullptr, v, log_f, nullptr, h0, y, ht,
                   states_out, ws, ws_bytes, stream);
 }
 
@@ -446,26 +502,55 @@ hgrn2_status hgrn2_bwd_tied(int B, int T, int H, int DK, int DV, int chunk, int 
                             const void *v, const void *log_f, const float *h0, const void *states_in,
                             const void *dy, const float *dht, void *dq, void *dv, void *dlog_f, float *dh0,
                             void *ws, size_t ws_bytes, void *stream) {
-  return bwd_impl(true, "hgrn2_bwd_tied", B, T, H, DK, DV, chunk, dtype, q, nullptr, v, log_f, h0, states_in, dy,
-                  dht, dq, nullptr, dv, dlog_f, dh0, ws, ws_bytes, stream);
+  return bwd_impl(kTied, "hgrn2_bwd_tied", B, T, H, DK, DV, chunk, dtype, q, nullptr, v, log_f, nullptr, h0,
+                  states_in, dy, dht, dq, nullptr, dv, dlog_f, nullptr, dh0, ws, ws_bytes, stream);
 }
 
 hgrn2_status hgrn2_fwd_chunk_tied(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
                                   const void *v, const void *log_f, const void *states, void *y, void *stream) {
-  return fwd_chunk_impl(true, "hgrn2_fwd_chunk_tied", B, T, H, DK, DV, chunk, dtype, q, nullptr, v, log_f, states,
+  return fwd_chunk_impl(kTied, "hgrn2_fwd_chunk_tied", B, T, H, DK, DV, chunk, dtype, q, nullptr, v, log_f, states,
                         y, stream);
 }
 
 hgrn2_status hgrn2_bwd_chunk_tied(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
                                   const void *v, const void *log_f, const void *states, const void *adjoints,
                                   const void *dy, void *dq, void *dv, void *dlog_f, void *stream) {
-  return bwd_chunk_impl(true, "hgrn2_bwd_chunk_tied", B, T, H, DK, DV, chunk, dtype, q, nullptr, v, log_f, states,
+  return bwd_chunk_impl(kTied, "hgrn2_bwd_chunk_tied", B, T, H, DK, DV, chunk, dtype, q, nullptr, v, log_f, states,
                         adjoints, dy, dq, nullptr, dv, dlog_f, stream);
 }
 
 hgrn2_status hgrn2_decode_step_tied(int B, int H, int DK, int DV, int dtype, const void *q, const void *v,
                                     const void *log_f, float *state, void *y, void *stream) {
-  return decode_impl(true, "hgrn2_decode_step_tied", B, H, DK, DV, dtype, q, nullptr, v, log_f, state, y, stream);
+  return decode_impl(kTied, "hgrn2_decode_step_tied", B, H, DK, DV, dtype, q, nullptr, v, log_f, nullptr, state, y,
+                     stream);
+}
+
+// ---- gate from its pre-activation (f = lb + (1 - lb) sigmoid(z), k = 1 - f)
+
+size_t hgrn2_bwd_gate_workspace_bytes(int B, int T, int H, int DK, int DV, int chunk, int dtype, int have_states) {
+  const size_t base = hgrn2_bwd_workspace_bytes(B, T, H, DK, DV, chunk, dtype, have_states);
+  return base ? base + dlb_part_bytes(B, T, H, DK, chunk) : 0;
+}
+
+hgrn2_status hgrn2_fwd_gate(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
+                            const void *v, const void *z, const float *lower_bound, const float *h0, void *y,
+                            float *ht, void *states_out, void *ws, size_t ws_bytes, void *stream) {
+  return fwd_impl(kGate, "hgrn2_fwd_gate", B, T, H, DK, DV, chunk, dtype, q, nullptr, v, z, lower_bound, h0, y, ht,
+                  states_out, ws, ws_bytes, stream);
+}
+
+hgrn2_status hgrn2_bwd_gate(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
+                            const void *v, const void *z, const float *lower_bound, const float *h0,
+                            const void *states_in, const void *dy, const float *dht, void *dq, void *dv, void *dz,
+                            float *dlower_bound, float *dh0, void *ws, size_t ws_bytes, void *stream) {
+  return bwd_impl(kGate, "hgrn2_bwd_gate", B, T, H, DK, DV, chunk, dtype, q, nullptr, v, z, lower_bound, h0,
+                  states_in, dy, dht, dq, nullptr, dv, dz, dlower_bound, dh0, ws, ws_bytes, stream);
+}
+
+hgrn2_status hgrn2_decode_step_gate(int B, int H, int DK, int DV, int dtype, const void *q, const void *v,
+                                    const void *z, const float *lower_bound, float *state, void *y, void *stream) {
+  return decode_impl(kGate, "hgrn2_decode_step_gate", B, H, DK, DV, dtype, q, nullptr, v, z, lower_bound, state, y,
+                     stream);
 }
 
 }  // extern "C"

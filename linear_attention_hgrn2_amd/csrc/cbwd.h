@@ -17,7 +17,10 @@
 // ko that entered the products, so the terms that cancel in exact arithmetic
 // cancel here too.  A diagonal block whose decay exceeds kDiagLimit nats is
 // summed directly.  With tied gates (k = 1 - f) k is formed from log f,
-// dk is not written, and dlog f is the total derivative dlog f - f dk.
+// dk is not written, and dlog f is the total derivative G = dlog f - f dk.
+// With the gate pre-activation z as input (f = lb + (1 - lb) sigmoid(z)), log
+// f and k are formed from z, the output is dz = G dlog f/dz, and each chunk
+// writes its sums over tokens of G dlog f/dlb (reduced over chunks later).
 //
 // One workgroup per (batch, head, chunk); wave w owns 16-token sub-block w and
 // produces all its outputs.  Phases: products from LDS tiles of qo, ko, v, dy
@@ -32,10 +35,12 @@ namespace hgrn2 {
 
 struct ChunkBwdArgs {
   int B, T, H, N;
-  const void *q, *k, *v, *log_f, *dy;  // [B,T,H,D]
+  const void *q, *k, *v, *log_f, *dy;  // [B,T,H,D]; log_f holds z in gate mode
   const void *states;                  // [B,H,N+1,D,D]; entry n = state before chunk n
   const void *lam;                     // [B,H,N,D,D]; entry n = adjoint at the end of chunk n
-  void *dq, *dk, *dv, *dlog_f;         // [B,T,H,D]
+  void *dq, *dk, *dv, *dlog_f;         // [B,T,H,D]; dlog_f receives dz in gate mode
+  const float *lb;                     // gate mode: lower bound of f, [H,D]
+  float *dlb;                          // gate mode: per-chunk sums [B,H,N,D]
 };
 
 template <typename T, int D, int C> struct CbwdCfg {
@@ -77,7 +82,7 @@ template <typename T, int D, int C> struct CbwdCfg {
   };
 };
 
-template <typename T, int D, int C, bool TIED>
+template <typename T, int D, int C, int GM>
 __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void hgrn2_chunk_bwd_kernel(ChunkBwdArgs a) {
   using Cfg = CbwdCfg<T, D, C>;
   constexpr int NW = Cfg::NW, NT = Cfg::NT, NB = Cfg::NB, CPL = Cfg::CPL, CB = Cfg::CB, KSD = Cfg::KSD,
@@ -93,6 +98,9 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n16 = lane & 15, g = lane >> 4;
   const bool has_ch = lane < Cfg::LANES;
   const int c0 = (has_ch ? lane : 0) * CPL;
+  float lbv[CPL];  // gate mode: lower bounds of this lane's channels
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) lbv[e] = GM == kGate ? a.lb[h * D + c0 + e] : 0.f;
 
   // buffer windows over this chunk's rows: offsets are 32-bit byte offsets
   // from the chunk's first row; rows past the end of the sequence read as zero
@@ -137,11 +145,11 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       pq[t] = ldtok(bq, 16 * w + t);
-      if constexpr (!TIED) pk[t] = ldtok(bk, 16 * w + t);
+      if constexpr (GM == kUntied) pk[t] = ldtok(bk, 16 * w + t);
       pl[t] = ldtok(bl, 16 * w + t);
     }
     float l[16][CPL], L[CPL];
-    block_prefix<T, CPL>(pl, l, L);
+    block_prefix<GM, T, CPL>(pl, l, L, lbv, len - 16 * w);
     if (has_ch) {
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
@@ -149,7 +157,7 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
         for (int e = 0; e < CPL; ++e) {
           oq.v[e] = from_f32<T>(to_f32(pq[t].v[e]) * __expf(l[t][e]));
-          ok.v[e] = from_f32<T>(k_of<TIED>(pk[t].v[e], pl[t].v[e]) * __expf(L[e] - l[t][e]));
+          ok.v[e] = from_f32<T>(k_of<GM>(pk[t].v[e], pl[t].v[e], lbv[e]) * __expf(L[e] - l[t][e]));
         }
         stpack<T, CPL>(&sm.u.in.qo[XT::at(16 * w + t, c0)], oq);
         stpack<T, CPL>(&sm.u.in.ko[XT::at(16 * w + t, c0)], ok);
@@ -308,12 +316,12 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
           float part = 0.f;
           if (tv_) {
             Pack<T, CPL> pk;
-            if constexpr (!TIED) pk = bk.template ldpack<T, CPL>(tok(16 * w + s) + c0b);
+            if constexpr (GM == kUntied) pk = bk.template ldpack<T, CPL>(tok(16 * w + s) + c0b);
             const Pack<T, CPL> pl = bl.template ldpack<T, CPL>(tok(16 * w + s) + c0b);
 #pragma unroll
             for (int e = 0; e < CPL; ++e) {
-              part += qt[e] * k_of<TIED>(pk.v[e], pl.v[e]) * __expf(ex[e]);
-              ex[e] += floor_logf(to_f32(pl.v[e]));
+              part += qt[e] * k_of<GM>(pk.v[e], pl.v[e], lbv[e]) * __expf(ex[e]);
+              ex[e] += lf_of<GM>(to_f32(pl.v[e]), lbv[e]);
             }
           }
           const float tot = wave_sum(part);
@@ -470,31 +478,32 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
     for (int t = 0; t < 16; ++t) {
       pl[t] = ldtok(bl, 16 * w + t);
 #pragma unroll
-      for (int e = 0; e < CPL; ++e) L[e] += floor_logf(to_f32(pl[t].v[e]));
+      for (int e = 0; e < CPL; ++e) L[e] += lf_of<GM>(to_f32(pl[t].v[e]), lbv[e], 16 * w + t < len);
     }
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       const int tt = 16 * w + t;
       const Pack<T, CPL> pq = ldtok(bq, tt);
       Pack<T, CPL> pk;
-      if constexpr (!TIED) pk = ldtok(bk, tt);
+      if constexpr (GM == kUntied) pk = ldtok(bk, tt);
       Pack<T, CPL> oq, ok;
 #pragma unroll
       for (int e = 0; e < CPL; ++e) {
-        ell[e] += floor_logf(to_f32(pl[t].v[e]));
+        const float lft = lf_of<GM>(to_f32(pl[t].v[e]), lbv[e], tt < len);
+        ell[e] += lft;
         const float el = __expf(ell[e]), ek = __expf(L[e] - ell[e]);
         const float qor = to_f32(from_f32<T>(to_f32(pq.v[e]) * el));
-        const float kor = to_f32(from_f32<T>(k_of<TIED>(pk.v[e], pl[t].v[e]) * ek));
+        const float kor = to_f32(from_f32<T>(k_of<GM>(pk.v[e], pl[t].v[e], lbv[e]) * ek));
         const float d1 = sq[t * LDG + c0 + e], d2 = sk[t * LDG + c0 + e];
         oq.v[e] = from_f32<T>(el * d1);
         ok.v[e] = from_f32<T>(ek * d2);
         X[t][e] = qor * d1 - kor * d2;
-        // tied gates: f dk, subtracted from dlog f below (replaces the consumed dk'_t)
-        if (TIED && has_ch) sk[t * LDG + c0 + e] = __expf(floor_logf(to_f32(pl[t].v[e]))) * (ek * d2);
+        // k tied to f: f dk, subtracted from dlog f below (replaces the consumed dk'_t)
+        if (GM != kUntied && has_ch) sk[t * LDG + c0 + e] = __expf(lft) * (ek * d2);
       }
       if (has_ch) {
         bdq.stpack<T, CPL>(tok(tt) + c0b, oq);
-        if constexpr (!TIED) bdk.stpack<T, CPL>(tok(tt) + c0b, ok);
+        if constexpr (GM == kUntied) bdk.stpack<T, CPL>(tok(tt) + c0b, ok);
       }
     }
     if (has_ch) {
@@ -515,32 +524,32 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
     for (int t = 0; t < 16; ++t) {
       const Pack<T, CPL> p = ldtok(bl, 16 * w + t);
 #pragma unroll
-      for (int e = 0; e < CPL; ++e) L[e] += floor_logf(to_f32(p.v[e]));
+      for (int e = 0; e < CPL; ++e) L[e] += lf_of<GM>(to_f32(p.v[e]), lbv[e], 16 * w + t < len);
     }
     for (int t = 0; t < 16; ++t) {
       const int tt = 16 * w + t;
       const Pack<T, CPL> pq = ldtok(bq, tt), plt = ldtok(bl, tt);
       Pack<T, CPL> pk;
-      if constexpr (!TIED) pk = ldtok(bk, tt);
+      if constexpr (GM == kUntied) pk = ldtok(bk, tt);
       const Pack<T, CPL> pdy = ldtok(bdy, tt), pv = ldtok(bv, tt);
       float dqd[CPL], dkd[CPL], ex[CPL];
 #pragma unroll
       for (int e = 0; e < CPL; ++e) {
-        ell[e] += floor_logf(to_f32(plt.v[e]));
+        ell[e] += lf_of<GM>(to_f32(plt.v[e]), lbv[e], tt < len);
         dqd[e] = dkd[e] = ex[e] = 0.f;
       }
       for (int s_ = t; s_ >= 0; --s_) {
         const Pack<T, CPL> pvs = ldtok(bv, 16 * w + s_), pls = ldtok(bl, 16 * w + s_);
         Pack<T, CPL> pks;
-        if constexpr (!TIED) pks = ldtok(bk, 16 * w + s_);
+        if constexpr (GM == kUntied) pks = ldtok(bk, 16 * w + s_);
         float part = 0.f;
 #pragma unroll
         for (int e = 0; e < CPL; ++e) part += to_f32(pdy.v[e]) * to_f32(pvs.v[e]);
         const float dA = wave_sum(part);
 #pragma unroll
         for (int e = 0; e < CPL; ++e) {
-          dqd[e] += dA * k_of<TIED>(pks.v[e], pls.v[e]) * __expf(ex[e]);
-          ex[e] += floor_logf(to_f32(pls.v[e]));
+          dqd[e] += dA * k_of<GM>(pks.v[e], pls.v[e], lbv[e]) * __expf(ex[e]);
+          ex[e] += lf_of<GM>(to_f32(pls.v[e]), lbv[e], 16 * w + s_ < len);
         }
       }
 #pragma unroll
@@ -554,7 +563,7 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
         if (u > t) {
           const Pack<T, CPL> plu = ldtok(bl, 16 * w + u);
 #pragma unroll
-          for (int e = 0; e < CPL; ++e) ex[e] += floor_logf(to_f32(plu.v[e]));
+          for (int e = 0; e < CPL; ++e) ex[e] += lf_of<GM>(to_f32(plu.v[e]), lbv[e], 16 * w + u < len);
         }
 #pragma unroll
         for (int e = 0; e < CPL; ++e) dkd[e] += dA * to_f32(pqu.v[e]) * __expf(ex[e]);
@@ -563,19 +572,20 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
       for (int e = 0; e < CPL; ++e) {
         const float el = __expf(ell[e]), ek = __expf(L[e] - ell[e]);
-        const float qv = to_f32(pq.v[e]), kv = k_of<TIED>(pk.v[e], plt.v[e]);
+        const float qv = to_f32(pq.v[e]), kv = k_of<GM>(pk.v[e], plt.v[e], lbv[e]);
         const float qor = to_f32(from_f32<T>(qv * el)), kor = to_f32(from_f32<T>(kv * ek));
         const float d1 = sq[t * LDG + c0 + e], d2 = sk[t * LDG + c0 + e];
         oq.v[e] = from_f32<T>(el * d1 + dqd[e]);
         ok.v[e] = from_f32<T>(ek * d2 + dkd[e]);
         const float x = (qor * d1 + qv * dqd[e]) - (kor * d2 + kv * dkd[e]);
         if (has_ch) sq[t * LDG + c0 + e] = x;  // X_t replaces the consumed dq'_t
-        if (TIED && has_ch) sk[t * LDG + c0 + e] = __expf(floor_logf(to_f32(plt.v[e]))) * (ek * d2 + dkd[e]);
+        if (GM != kUntied && has_ch)
+          sk[t * LDG + c0 + e] = __expf(lf_of<GM>(to_f32(plt.v[e]), lbv[e], tt < len)) * (ek * d2 + dkd[e]);
         tot[e] += x;
       }
       if (has_ch) {
         bdq.stpack<T, CPL>(tok(tt) + c0b, oq);
-        if constexpr (!TIED) bdk.stpack<T, CPL>(tok(tt) + c0b, ok);
+        if constexpr (GM == kUntied) bdk.stpack<T, CPL>(tok(tt) + c0b, ok);
       }
     }
     if (has_ch)
@@ -583,6 +593,12 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
       for (int e = 0; e < CPL; ++e) out.tot[w][c0 + e] = tot[e];
   }
   __syncthreads();  // B6: tot, cpart, rs complete
+  // dlog f = reverse in-chunk sum of X plus the carry; k tied to f subtracts
+  // f dk; gate mode turns that total G into dz and sums G dlog f/dlb over the
+  // chunk's tokens
+  float dlbs[CPL];
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) dlbs[e] = 0.f;
   if (has_ch) {
     float carry[CPL];
 #pragma unroll
@@ -592,37 +608,59 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
       for (int i = 0; i < NW; ++i) carry[e] += out.cpart[i][c] + ((i > w) ? out.tot[i][c] : 0.f);
     }
+    auto emit = [&](int t, const float *cr) {
+      const int tt = 16 * w + t;
+      Pack<T, CPL> o;
+      Pack<T, CPL> pz;
+      if constexpr (GM == kGate) pz = ldtok(bl, tt);
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) {
+        float G = GM == kUntied ? cr[e] : cr[e] - sk[t * LDG + c0 + e];
+        if constexpr (GM == kGate) {
+          const GateGrad gg = gate_grad(to_f32(pz.v[e]), lbv[e]);
+          if (tt < len) dlbs[e] += G * gg.dlb;
+          G *= gg.dz;
+        }
+        o.v[e] = from_f32<T>(G);
+      }
+      bdl.stpack<T, CPL>(tok(tt) + c0b, o);
+    };
     if (!wide) {
 #pragma unroll
       for (int t = 15; t >= 0; --t) {
-        const int tt = 16 * w + t;
-        Pack<T, CPL> o;
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) {
-          carry[e] += X[t][e];
-          o.v[e] = from_f32<T>(TIED ? carry[e] - sk[t * LDG + c0 + e] : carry[e]);
-        }
-        bdl.stpack<T, CPL>(tok(tt) + c0b, o);
+        for (int e = 0; e < CPL; ++e) carry[e] += X[t][e];
+        emit(t, carry);
       }
     } else {
       for (int t = 15; t >= 0; --t) {
-        const int tt = 16 * w + t;
-        Pack<T, CPL> o;
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) {
-          carry[e] += sq[t * LDG + c0 + e];
-          o.v[e] = from_f32<T>(TIED ? carry[e] - sk[t * LDG + c0 + e] : carry[e]);
-        }
-        bdl.stpack<T, CPL>(tok(tt) + c0b, o);
+        for (int e = 0; e < CPL; ++e) carry[e] += sq[t * LDG + c0 + e];
+        emit(t, carry);
       }
+    }
+  }
+  if constexpr (GM == kGate) {
+    // per-wave sums into row 0 of the wave's (consumed) dq' staging, then one
+    // fixed-order sum over the waves per channel
+    if (has_ch) {
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) sq[c0 + e] = dlbs[e];
+    }
+    __syncthreads();
+    for (int c = tid; c < D; c += NT) {
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < NW; ++i) acc += out.stg[0][i][c];
+      a.dlb[((size_t)bh * N + n) * D + c] = acc;
     }
   }
 }
 
-template <typename T, int D, int C, bool TIED>
+template <typename T, int D, int C, int GM>
 hipError_t launch_chunk_bwd(const ChunkBwdArgs &a, hipStream_t stream) {
   using Cfg = CbwdCfg<T, D, C>;
-  hipLaunchKernelGGL((hgrn2_chunk_bwd_kernel<T, D, C, TIED>), dim3(a.B * a.H * a.N), dim3(Cfg::NT), 0, stream, a);
+  hipLaunchKernelGGL((hgrn2_chunk_bwd_kernel<T, D, C, GM>), dim3(a.B * a.H * a.N), dim3(Cfg::NT), 0, stream, a);
   return hipGetLastError();
 }
 

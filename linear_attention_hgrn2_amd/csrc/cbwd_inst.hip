@@ -7,20 +7,26 @@
 namespace hgrn2 {
 
 template <typename T, int D, int C> struct ChunkBwdOp {
-  static hipError_t run(bool tied, const ChunkBwdArgs *a, hipStream_t s) {
-    static_assert(sizeof(typename CbwdCfg<T, D, C>::Smem) <= 160 * 1024, "LDS");
-    if (!a) return hipSuccess;
+  template <int GM> static hipError_t go(const ChunkBwdArgs &a, hipStream_t s) {
     if constexpr (std::is_same<T, bf16_t>::value && D == 128 && C == 64) {
       static_assert(sizeof(CbwdResCfg::Smem) <= 160 * 1024, "LDS");
-      return tied ? launch_chunk_bwd_res<true>(*a, s) : launch_chunk_bwd_res<false>(*a, s);
+      return launch_chunk_bwd_res<GM>(a, s);
     } else {
-      return tied ? launch_chunk_bwd<T, D, C, true>(*a, s) : launch_chunk_bwd<T, D, C, false>(*a, s);
+      return launch_chunk_bwd<T, D, C, GM>(a, s);
     }
+  }
+  static hipError_t run(int gm, const ChunkBwdArgs *a, hipStream_t s) {
+    static_assert(sizeof(typename CbwdCfg<T, D, C>::Smem) <= 160 * 1024, "LDS");
+    if (gm < kUntied || gm > kGate) return hipErrorNotSupported;
+    if (!a) return hipSuccess;
+    if (gm == kTied) return go<kTied>(*a, s);
+    if (gm == kGate) return go<kGate>(*a, s);
+    return go<kUntied>(*a, s);
   }
 };
 
-hipError_t dispatch_chunk_bwd(int dtype, int D, int C, bool tied, const ChunkBwdArgs *a, hipStream_t s) {
-  return run_config<ChunkBwdOp>(dtype, D, C, tied, a, s);
+hipError_t dispatch_chunk_bwd(int dtype, int D, int C, int gm, const ChunkBwdArgs *a, hipStream_t s) {
+  return run_config<ChunkBwdOp>(dtype, D, C, gm, a, s);
 }
 
 }  // namespace hgrn2

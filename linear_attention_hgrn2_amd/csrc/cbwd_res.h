@@ -21,7 +21,9 @@
 // XOR with (row & 15), which the copy realises by permuting its source
 // addresses; reads of 16 consecutive rows then never share a bank.  With tied
 // gates (k = 1 - f) k is formed from log f, dk is not written, and dlog f is
-// the total derivative dlog f - f dk.
+// the total derivative G = dlog f - f dk; with the gate pre-activation as input
+// the output is dz = G dlog f/dz and each chunk writes its token sums of
+// G dlog f/dlb, f being recovered from the block-local prefix of log f.
 #pragma once
 
 #include "cbwd.h"
@@ -91,7 +93,7 @@ __device__ __forceinline__ PFrag<bf16_t> res_tr8(const bf16_t *m, int r0, int n0
 
 __device__ __forceinline__ int res_pair_i(int p) { return p >= 6 ? 3 : p >= 3 ? 2 : p >= 1 ? 1 : 0; }
 
-template <bool TIED>
+template <int GM>
 __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a) {
   using Cfg = CbwdResCfg;
   using T = bf16_t;
@@ -142,7 +144,7 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
     for (int t = 0; t < 8; ++t) {
       const uint32_t off = tok(16 * w + 8 * hh + t) + (uint32_t)c0 * sizeof(T);
       pq[t] = bq.ldpack<T, 2>(off);
-      if constexpr (!TIED) pk[t] = win(a.k, k).template ldpack<T, 2>(off);
+      if constexpr (GM == kUntied) pk[t] = win(a.k, k).template ldpack<T, 2>(off);
       pl[t] = bl.ldpack<T, 2>(off);
     }
   };
@@ -157,6 +159,15 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
     // does not hoist every address of the body out of the loop
     const int tid = opaque((int)threadIdx.x), lane = tid & 63, n16 = lane & 15, g = lane >> 4;
     const int c0 = 2 * lane;  // prep / epilogue channels c0, c0 + 1
+    // gate mode: lower bounds of channels c0, c0 + 1, loaded where they are
+    // used (short live ranges)
+    auto lbs = [&](float *o) {
+      const int cc = 2 * (opaque((int)threadIdx.x) & 63);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) o[e] = GM == kGate ? a.lb[(k.bh % H) * D + cc + e] : 0.f;
+    };
+    float lb2[2];
+    lbs(lb2);
 
     // ---- P0a: v, dy tiles; half-block totals of log f
 #pragma unroll
@@ -172,7 +183,7 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
       for (int t = 0; t < 8; ++t)
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          run[e] += floor_logf(to_f32(pl[t].v[e]));
+          run[e] += lf_of<GM>(to_f32(pl[t].v[e]), lb2[e], 16 * w + 8 * hh + t < k.len);
           l[t][e] = run[e];
         }
       sm.u.a.x.Lh[w][hh][c0] = run[0];
@@ -203,7 +214,7 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           oq.v[e] = from_f32<T>(to_f32(pq[t].v[e]) * __expf(l[t][e]));
-          ok.v[e] = from_f32<T>(k_of<TIED>(pk[t].v[e], pl[t].v[e]) * __expf(Lw[e] - l[t][e]));
+          ok.v[e] = from_f32<T>(k_of<GM>(pk[t].v[e], pl[t].v[e], lb2[e]) * __expf(Lw[e] - l[t][e]));
         }
         *(Pack<T, 2> *)&sm.qo[XT::at(tt, c0)] = oq;
         *(Pack<T, 2> *)&sm.ko[XT::at(tt, c0)] = ok;
@@ -318,6 +329,8 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
         } else {
           // wide in-block decay: A[t][s] summed directly (every exponent <= 0)
           const GBuf bq = win(a.q, k), bl = win(a.log_f, k);
+          float lb2[2];
+          lbs(lb2);
           for (int t = 0; t < 16; ++t) {
             const Pack<T, 2> pt = bq.ldpack<T, 2>(tok(16 * i + t) + (uint32_t)c0 * sizeof(T));
             float ex[2] = {0.f, 0.f};
@@ -325,12 +338,12 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
               const uint32_t off = tok(16 * i + s) + (uint32_t)c0 * sizeof(T);
               const Pack<T, 2> pls = bl.ldpack<T, 2>(off);
               Pack<T, 2> pks;
-              if constexpr (!TIED) pks = win(a.k, k).template ldpack<T, 2>(off);
+              if constexpr (GM == kUntied) pks = win(a.k, k).template ldpack<T, 2>(off);
               float part = 0.f;
 #pragma unroll
               for (int e = 0; e < 2; ++e) {
-                part += to_f32(pt.v[e]) * k_of<TIED>(pks.v[e], pls.v[e]) * __expf(ex[e]);
-                ex[e] += floor_logf(to_f32(pls.v[e]));
+                part += to_f32(pt.v[e]) * k_of<GM>(pks.v[e], pls.v[e], lb2[e]) * __expf(ex[e]);
+                ex[e] += lf_of<GM>(to_f32(pls.v[e]), lb2[e], 16 * i + s < k.len);
               }
               const float tot = wave_sum(part);
 #pragma unroll
@@ -492,14 +505,14 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
         oq.v[e] = from_f32<T>(el * dd1[e]);
         ok.v[e] = from_f32<T>(ek * dd2[e]);
         X[t][e] = to_f32(qr.v[e]) * dd1[e] - to_f32(kr.v[e]) * dd2[e];
-        // tied gates: f dk (f from the prefix), subtracted from dlog f in P6; it
-        // replaces the consumed dk'_t
-        if (TIED && !wide)
+        // k tied to f: f dk (f from the prefix), subtracted from dlog f in P6;
+        // it replaces the consumed dk'_t
+        if (GM != kUntied && !wide)
           ep.stg[1][tt][c0 + e] = __expf(l[t][e] - (t ? l[t - 1][e] : hoff[e])) * (ek * dd2[e]);
       }
       if (!wide) {
         bdq.stpack<T, 2, kStream>(tok(tt) + (uint32_t)c0 * sizeof(T), oq);
-        if constexpr (!TIED) bdk.stpack<T, 2, kStream>(tok(tt) + (uint32_t)c0 * sizeof(T), ok);
+        if constexpr (GM == kUntied) bdk.stpack<T, 2, kStream>(tok(tt) + (uint32_t)c0 * sizeof(T), ok);
       }
     }
     if (wide) {
@@ -507,26 +520,28 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
       // dk_t adds sum_{u >= t} dA[u][t] q_u e^{ell_u - ell_t} (every exponent <= 0)
       const GBuf bq = win(a.q, k), bv = win(a.v, k), bl = win(a.log_f, k), bdy = win(a.dy, k);
       const uint32_t cb2 = (uint32_t)c0 * sizeof(T);
+      float lb2[2];
+      lbs(lb2);
       for (int t = 0; t < 8; ++t) {
         const int tb = 8 * hh + t, tt = 16 * w + tb;
         const Pack<T, 2> pqt = bq.ldpack<T, 2>(tok(tt) + cb2), plt = bl.ldpack<T, 2>(tok(tt) + cb2);
         Pack<T, 2> pkt;
-        if constexpr (!TIED) pkt = win(a.k, k).template ldpack<T, 2>(tok(tt) + cb2);
+        if constexpr (GM == kUntied) pkt = win(a.k, k).template ldpack<T, 2>(tok(tt) + cb2);
         const Pack<T, 2> pdy = bdy.ldpack<T, 2>(tok(tt) + cb2), pvt = bv.ldpack<T, 2>(tok(tt) + cb2);
         float dqd[2] = {0.f, 0.f}, dkd[2] = {0.f, 0.f}, ex[2] = {0.f, 0.f};
         for (int s_ = tb; s_ >= 0; --s_) {
           const uint32_t off = tok(16 * w + s_) + cb2;
           const Pack<T, 2> pvs = bv.ldpack<T, 2>(off), pls = bl.ldpack<T, 2>(off);
           Pack<T, 2> pks;
-          if constexpr (!TIED) pks = win(a.k, k).template ldpack<T, 2>(off);
+          if constexpr (GM == kUntied) pks = win(a.k, k).template ldpack<T, 2>(off);
           float part = 0.f;
 #pragma unroll
           for (int e = 0; e < 2; ++e) part += to_f32(pdy.v[e]) * to_f32(pvs.v[e]);
           const float dA = wave_sum(part);
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
-            dqd[e] += dA * k_of<TIED>(pks.v[e], pls.v[e]) * __expf(ex[e]);
-            ex[e] += floor_logf(to_f32(pls.v[e]));
+            dqd[e] += dA * k_of<GM>(pks.v[e], pls.v[e], lb2[e]) * __expf(ex[e]);
+            ex[e] += lf_of<GM>(to_f32(pls.v[e]), lb2[e], 16 * w + s_ < k.len);
           }
         }
         ex[0] = ex[1] = 0.f;
@@ -540,7 +555,7 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
           if (u > tb) {
             const Pack<T, 2> plu = bl.ldpack<T, 2>(off);
 #pragma unroll
-            for (int e = 0; e < 2; ++e) ex[e] += floor_logf(to_f32(plu.v[e]));
+            for (int e = 0; e < 2; ++e) ex[e] += lf_of<GM>(to_f32(plu.v[e]), lb2[e], 16 * w + u < k.len);
           }
 #pragma unroll
           for (int e = 0; e < 2; ++e) dkd[e] += dA * to_f32(pqu.v[e]) * __expf(ex[e]);
@@ -553,11 +568,12 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
           const float el = __expf(l[t][e]), ek = __expf(Lw[e] - l[t][e]);
           oq.v[e] = from_f32<T>(el * dd1[e] + dqd[e]);
           ok.v[e] = from_f32<T>(ek * dd2[e] + dkd[e]);
-          X[t][e] += to_f32(pqt.v[e]) * dqd[e] - k_of<TIED>(pkt.v[e], plt.v[e]) * dkd[e];
-          if (TIED) ep.stg[1][tt][c0 + e] = __expf(floor_logf(to_f32(plt.v[e]))) * (ek * dd2[e] + dkd[e]);
+          X[t][e] += to_f32(pqt.v[e]) * dqd[e] - k_of<GM>(pkt.v[e], plt.v[e], lb2[e]) * dkd[e];
+          if (GM != kUntied)
+            ep.stg[1][tt][c0 + e] = __expf(lf_of<GM>(to_f32(plt.v[e]), lb2[e], tt < k.len)) * (ek * dd2[e] + dkd[e]);
         }
         bdq.stpack<T, 2, kStream>(tok(tt) + cb2, oq);
-        if constexpr (!TIED) bdk.stpack<T, 2, kStream>(tok(tt) + cb2, ok);
+        if constexpr (GM == kUntied) bdk.stpack<T, 2, kStream>(tok(tt) + cb2, ok);
       }
     }
 #pragma unroll
@@ -569,10 +585,13 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
     }
     __syncthreads();  // B8: tot, cpart, rs complete
 
-    // ---- P6: dlog f = reverse cumulative sum of X within the chunk + carry
+    // ---- P6: dlog f = reverse cumulative sum of X within the chunk + carry;
+    // k tied to f subtracts f dk; gate mode turns that total G into dz and sums
+    // G dlog f/dlb over the chunk's tokens
     {
       const GBuf bdl = win(a.dlog_f, k);
-      float carry[2];
+      float carry[2], dlbs[2] = {0.f, 0.f}, lb2[2];
+      lbs(lb2);
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int c = c0 + e;
@@ -584,13 +603,38 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
       }
 #pragma unroll
       for (int t = 7; t >= 0; --t) {
+        const int tt = 16 * w + 8 * hh + t;
         Pack<T, 2> o;
+        Pack<T, 2> pz;
+        if constexpr (GM == kGate)
+          if (wide) pz = win(a.log_f, k).template ldpack<T, 2>(tok(tt) + (uint32_t)c0 * sizeof(T));
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           carry[e] += X[t][e];
-          o.v[e] = from_f32<T>(TIED ? carry[e] - ep.stg[1][16 * w + 8 * hh + t][c0 + e] : carry[e]);
+          float G = GM == kUntied ? carry[e] : carry[e] - ep.stg[1][tt][c0 + e];
+          if constexpr (GM == kGate) {
+            const GateGrad gg = wide ? gate_grad(to_f32(pz.v[e]), lb2[e])
+                                     : gate_grad_lf(l[t][e] - (t ? l[t - 1][e] : hoff[e]), lb2[e]);
+            if (tt < k.len) dlbs[e] += G * gg.dlb;
+            G *= gg.dz;
+          }
+          o.v[e] = from_f32<T>(G);
         }
-        bdl.stpack<T, 2, kStream>(tok(16 * w + 8 * hh + t) + (uint32_t)c0 * sizeof(T), o);
+        bdl.stpack<T, 2, kStream>(tok(tt) + (uint32_t)c0 * sizeof(T), o);
+      }
+      if constexpr (GM == kGate) {
+        // per-wave sums into the consumed dq' staging, then a fixed-order sum
+        // over the eight waves per channel (read before the next chunk's B1,
+        // after which the copies into S may land there)
+        ep.stg[0][wv][c0] = dlbs[0];
+        ep.stg[0][wv][c0 + 1] = dlbs[1];
+        __syncthreads();  // B9
+        if (tid < D) {
+          float acc = 0.f;
+#pragma unroll
+          for (int o = 0; o < NWV; ++o) acc += ep.stg[0][o][tid];
+          a.dlb[((size_t)k.bh * N + k.n) * D + tid] = acc;
+        }
       }
     }
   }
@@ -604,10 +648,10 @@ inline int res_grid(int nchunks) {
   return nchunks < cus ? nchunks : cus;
 }
 
-template <bool TIED>
+template <int GM>
 hipError_t launch_chunk_bwd_res(const ChunkBwdArgs &a, hipStream_t stream) {
   const int nc = a.B * a.H * a.N;
-  hipLaunchKernelGGL(hgrn2_chunk_bwd_res_kernel<TIED>, dim3(res_grid(nc)), dim3(CbwdResCfg::NT), 0, stream, a);
+  hipLaunchKernelGGL(hgrn2_chunk_bwd_res_kernel<GM>, dim3(res_grid(nc)), dim3(CbwdResCfg::NT), 0, stream, a);
   return hipGetLastError();
 }
 

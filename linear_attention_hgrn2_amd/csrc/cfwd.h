@@ -24,7 +24,8 @@ namespace hgrn2 {
 
 struct ChunkFwdArgs {
   int B, T, H, N;
-  const void *q, *k, *v, *log_f;  // [B,T,H,D]
+  const void *q, *k, *v, *log_f;  // [B,T,H,D]; log_f holds the gate pre-activation in gate mode
+  const float *lb;                // gate mode: lower bound of f, [H,D]
   const void *states;             // [B,H,N+1,D,D] input dtype; entry n = state before chunk n
   void *y;                        // [B,T,H,D]
 };
@@ -59,21 +60,23 @@ template <typename T, int D, int C> struct CfwdCfg {
 __host__ __device__ constexpr int pair_ij(int i, int j) { return i * (i + 1) / 2 + j; }
 
 // Sixteen tokens of one lane's CPL channels: the block-local inclusive prefix
-// of the floored log f, in registers.
-template <typename T, int CPL>
-__device__ __forceinline__ void block_prefix(const Pack<T, CPL> *pl, float (*l)[CPL], float *L) {
+// of the floored log f, in registers.  Tokens from `nvalid` on lie past the
+// end of the sequence (they matter only in gate mode, where log f is formed).
+template <int GM, typename T, int CPL>
+__device__ __forceinline__ void block_prefix(const Pack<T, CPL> *pl, float (*l)[CPL], float *L, const float *lb,
+                                             int nvalid) {
 #pragma unroll
   for (int e = 0; e < CPL; ++e) L[e] = 0.f;
 #pragma unroll
   for (int t = 0; t < 16; ++t)
 #pragma unroll
     for (int e = 0; e < CPL; ++e) {
-      L[e] += floor_logf(to_f32(pl[t].v[e]));
+      L[e] += lf_of<GM>(to_f32(pl[t].v[e]), lb[e], t < nvalid);
       l[t][e] = L[e];
     }
 }
 
-template <typename T, int D, int C, bool TIED>
+template <typename T, int D, int C, int GM>
 __global__ __launch_bounds__(4 * C) void hgrn2_chunk_fwd_kernel(ChunkFwdArgs a) {
   using Cfg = CfwdCfg<T, D, C>;
   constexpr int NW = Cfg::NW, NT = Cfg::NT, NB = Cfg::NB, CPL = Cfg::CPL, CB = Cfg::CB, KSD = Cfg::KSD,
@@ -89,6 +92,9 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_fwd_kernel(ChunkFwdArgs a) 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n16 = lane & 15, g = lane >> 4;
   const bool has_ch = lane < Cfg::LANES;
   const int c0 = (has_ch ? lane : 0) * CPL;
+  float lbv[CPL];  // gate mode: lower bounds of this lane's channels
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) lbv[e] = GM == kGate ? a.lb[h * D + c0 + e] : 0.f;
 
   const T *gq = (const T *)a.q;
   const T *gk = (const T *)a.k;
@@ -132,11 +138,11 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_fwd_kernel(ChunkFwdArgs a) 
       for (int e = 0; e < CPL; ++e) pq[t].v[e] = pk[t].v[e] = pl[t].v[e] = from_f32<T>(0.f);
       if (tt < len && has_ch) {
         pq[t] = ldpack<T, CPL>(gq + (tok(tt) + c0));
-        if constexpr (!TIED) pk[t] = ldpack<T, CPL>(gk + (tok(tt) + c0));
+        if constexpr (GM == kUntied) pk[t] = ldpack<T, CPL>(gk + (tok(tt) + c0));
         pl[t] = ldpack<T, CPL>(gl + (tok(tt) + c0));
       }
     }
-    block_prefix<T, CPL>(pl, l, L);
+    block_prefix<GM, T, CPL>(pl, l, L, lbv, len - 16 * w);
     if (has_ch) {
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
@@ -144,7 +150,7 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_fwd_kernel(ChunkFwdArgs a) 
 #pragma unroll
         for (int e = 0; e < CPL; ++e) {
           oq.v[e] = from_f32<T>(to_f32(pq[t].v[e]) * __expf(l[t][e]));
-          ok.v[e] = from_f32<T>(k_of<TIED>(pk[t].v[e], pl[t].v[e]) * __expf(L[e] - l[t][e]));
+          ok.v[e] = from_f32<T>(k_of<GM>(pk[t].v[e], pl[t].v[e], lbv[e]) * __expf(L[e] - l[t][e]));
         }
         stpack<T, CPL>(&sm.qo[XT::at(16 * w + t, c0)], oq);
         stpack<T, CPL>(&sm.u.kv.ko[XT::at(16 * w + t, c0)], ok);
@@ -209,12 +215,12 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_fwd_kernel(ChunkFwdArgs a) 
           float part = 0.f;
           if (tv) {
             Pack<T, CPL> pk;
-            if constexpr (!TIED) pk = ldpack<T, CPL>(gk + (tok(16 * w + s) + c0));
+            if constexpr (GM == kUntied) pk = ldpack<T, CPL>(gk + (tok(16 * w + s) + c0));
             const Pack<T, CPL> pl = ldpack<T, CPL>(gl + (tok(16 * w + s) + c0));
 #pragma unroll
             for (int e = 0; e < CPL; ++e) {
-              part += qt[e] * k_of<TIED>(pk.v[e], pl.v[e]) * __expf(ex[e]);
-              ex[e] += floor_logf(to_f32(pl.v[e]));  // the factor of s - 1 includes f_s
+              part += qt[e] * k_of<GM>(pk.v[e], pl.v[e], lbv[e]) * __expf(ex[e]);
+              ex[e] += lf_of<GM>(to_f32(pl.v[e]), lbv[e]);  // the factor of s - 1 includes f_s
             }
           }
           const float tot = wave_sum(part);
@@ -321,10 +327,10 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_fwd_kernel(ChunkFwdArgs a) 
   }
 }
 
-template <typename T, int D, int C, bool TIED>
+template <typename T, int D, int C, int GM>
 hipError_t launch_chunk_fwd(const ChunkFwdArgs &a, hipStream_t stream) {
   using Cfg = CfwdCfg<T, D, C>;
-  hipLaunchKernelGGL((hgrn2_chunk_fwd_kernel<T, D, C, TIED>), dim3(a.B * a.H * a.N), dim3(Cfg::NT), 0, stream, a);
+  hipLaunchKernelGGL((hgrn2_chunk_fwd_kernel<T, D, C, GM>), dim3(a.B * a.H * a.N), dim3(Cfg::NT), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -4,15 +4,18 @@
 namespace hgrn2 {
 
 template <typename T, int D, int C> struct ChunkFwdOp {
-  static hipError_t run(bool tied, const ChunkFwdArgs *a, hipStream_t s) {
+  static hipError_t run(int gm, const ChunkFwdArgs *a, hipStream_t s) {
     static_assert(sizeof(typename CfwdCfg<T, D, C>::Smem) <= 160 * 1024, "LDS");
+    if (gm < kUntied || gm > kGate) return hipErrorNotSupported;
     if (!a) return hipSuccess;
-    return tied ? launch_chunk_fwd<T, D, C, true>(*a, s) : launch_chunk_fwd<T, D, C, false>(*a, s);
+    if (gm == kTied) return launch_chunk_fwd<T, D, C, kTied>(*a, s);
+    if (gm == kGate) return launch_chunk_fwd<T, D, C, kGate>(*a, s);
+    return launch_chunk_fwd<T, D, C, kUntied>(*a, s);
   }
 };
 
-hipError_t dispatch_chunk_fwd(int dtype, int D, int C, bool tied, const ChunkFwdArgs *a, hipStream_t s) {
-  return run_config<ChunkFwdOp>(dtype, D, C, tied, a, s);
+hipError_t dispatch_chunk_fwd(int dtype, int D, int C, int gm, const ChunkFwdArgs *a, hipStream_t s) {
+  return run_config<ChunkFwdOp>(dtype, D, C, gm, a, s);
 }
 
 }  // namespace hgrn2

@@ -313,14 +313,76 @@ constexpr float kDiagLimit = 64.f;
 
 __device__ __forceinline__ float floor_logf(float x) { return fmaxf(x, kLogFloor); }
 
-// HGRN2's tied input gate k = 1 - f (HGRN2 summary, paperlayer.ai, §2.1 and
-// §3.2) from log f, as -expm1(log f): no cancellation for f near 1.  A zero
-// log f (a row past the end of the sequence) gives k = 0.
+// How the gate arrives at a kernel (a template argument of every kernel):
+//   kUntied  k and log f are separate inputs;
+//   kTied    log f is the input and k = 1 - f (HGRN2 summary, paperlayer.ai,
+//            §2.1 and §3.2: the input gate tied to the forget gate);
+//   kGate    the gate pre-activation z and a per-channel lower bound lb are
+//            the inputs: f = lb + (1 - lb) sigmoid(z), k = 1 - f (§2.2: a
+//            forget gate that learns a residual above a lower bound).
+enum GateMode : int { kUntied = 0, kTied = 1, kGate = 2 };
+
+// HGRN2's tied input gate k = 1 - f from log f, as -expm1(log f): no
+// cancellation for f near 1.  A zero log f (a row past the end of the
+// sequence) gives k = 0.
 __device__ __forceinline__ float tied_k(float log_f) { return -expm1f(floor_logf(log_f)); }
 
-// k of a token: loaded (independent gates) or formed from its log f (tied)
-template <bool TIED, typename T> __device__ __forceinline__ float k_of(T k, T log_f) {
-  if constexpr (TIED) return tied_k(to_f32(log_f));
+// log f for f = lb + (1 - lb) sigmoid(z), for any z.  With u = e^{-|z|} in
+// (0, 1]: z >= 0 gives log1p(lb u) - log1p(u), z < 0 gives
+// log(lb + u) - log1p(u) (which is z - log1p(u) when lb = 0).
+__device__ __forceinline__ float gate_log_f(float z, float lb) {
+  const float u = __expf(-fabsf(z));
+  const float a = z >= 0.f ? log1pf(lb * u) : (lb > 0.f ? __logf(lb + u) : z);
+  return a - log1pf(u);
+}
+
+// k = 1 - f = (1 - lb) sigmoid(-z), without cancellation
+__device__ __forceinline__ float gate_k(float z, float lb) {
+  const float u = __expf(-fabsf(z));
+  return (1.f - lb) * ((z >= 0.f ? u : 1.f) / (1.f + u));
+}
+
+// Factors that turn the total derivative with respect to log f (with k = 1 - f
+// tied to it), G = dlog f - f dk, into the gradients of the gate inputs:
+//   dz = G (1 - lb) s s' / f,   dlb (one token) = G s' / f,
+// with s = sigmoid(z), s' = sigmoid(-z), f = lb + (1 - lb) s.
+struct GateGrad {
+  float dz, dlb;
+};
+// from the pre-activation itself
+__device__ __forceinline__ GateGrad gate_grad(float z, float lb) {
+  const float u = __expf(-fabsf(z));
+  const float r = 1.f / (1.f + u);
+  const float s = z >= 0.f ? r : u * r, sp = z >= 0.f ? u * r : r;
+  const float f = fmaxf(lb + (1.f - lb) * s, 1e-38f);
+  GateGrad g;
+  g.dz = lb > 0.f ? (1.f - lb) * s * sp / f : sp;  // (1 - lb) s / f = 1 when lb = 0
+  g.dlb = sp / f;
+  return g;
+}
+// from log f (floored) when z is no longer at hand: s' = (1 - f) / (1 - lb)
+// and (1 - lb) s = f - lb, with 1 - f = -expm1(log f)
+__device__ __forceinline__ GateGrad gate_grad_lf(float lf, float lb) {
+  const float f = fmaxf(__expf(lf), 1e-38f), omf = -expm1f(lf);
+  const float inv = 1.f / ((1.f - lb) * f);
+  GateGrad g;
+  g.dz = lb > 0.f ? (f - lb) * omf * inv : omf;
+  g.dlb = omf * inv;
+  return g;
+}
+
+// log f of a gate input x (floored).  kGate: x is the pre-activation and rows
+// past the end of the sequence (valid = false) must decay nothing, log f = 0;
+// the other modes read log f itself, which is 0 there already.
+template <int GM> __device__ __forceinline__ float lf_of(float x, float lb, bool valid = true) {
+  if constexpr (GM == kGate) return valid ? floor_logf(gate_log_f(x, lb)) : 0.f;
+  else return floor_logf(x);
+}
+
+// k of a token: loaded (kUntied) or formed from the gate input x
+template <int GM, typename T> __device__ __forceinline__ float k_of(T k, T x, float lb = 0.f) {
+  if constexpr (GM == kTied) return tied_k(to_f32(x));
+  else if constexpr (GM == kGate) return gate_k(to_f32(x), lb);
   else return to_f32(k);
 }
 

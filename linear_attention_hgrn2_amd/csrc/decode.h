@@ -1,7 +1,8 @@
 // Recurrent decode step (HGRN2 summary, paperlayer.ai, §1: recurrent
 // inference with linear cost; §3.2: state update and readout):
 //   S <- Diag(exp(log_f)) S + k^T v   (in place),   y = q S
-// (k = 1 - exp(log_f) with tied gates).
+// (k = 1 - exp(log_f) with tied gates; log f and k from the pre-activation z
+// and the lower bound lb in gate mode, f = lb + (1 - lb) sigmoid(z)).
 // Pure HBM streaming: each (b, h) state (D*D float32) is read once and written
 // once.  One workgroup per (b, h); a thread owns a 4-column group (16-byte
 // accesses, consecutive threads on consecutive columns, so every wavefront
@@ -17,7 +18,8 @@ namespace hgrn2 {
 
 struct DecodeArgs {
   int B, H;
-  const void *q, *k, *v, *log_f;
+  const void *q, *k, *v, *log_f;  // log_f holds z in gate mode
+  const float *lb;                // gate mode: lower bound of f, [H,D]
   float *state;
   void *y;
 };
@@ -30,7 +32,7 @@ template <int D> struct DecodeCfg {
   static_assert(D % RG == 0, "row split");
 };
 
-template <typename TIn, int D, bool TIED>
+template <typename TIn, int D, int GM>
 __global__ __launch_bounds__(256) void hgrn2_decode_kernel(DecodeArgs a) {
   using Cfg = DecodeCfg<D>;
   constexpr int CG = Cfg::CG, RG = Cfg::RG, PASSES = Cfg::PASSES;
@@ -54,9 +56,10 @@ __global__ __launch_bounds__(256) void hgrn2_decode_kernel(DecodeArgs a) {
   for (int p = 0; p < PASSES; ++p) st[p] = S[(size_t)(p * RG + rg) * CG + cg];
 
   for (int c = tid; c < D; c += Cfg::NT) {
+    const float lbc = GM == kGate ? a.lb[(bh % a.H) * D + c] : 0.f;
     s_q[c] = to_f32(gq[c]);
-    s_k[c] = TIED ? tied_k(to_f32(gl[c])) : to_f32(gk[c]);
-    s_f[c] = __expf(floor_logf(to_f32(gl[c])));
+    s_k[c] = k_of<GM>(GM == kUntied ? gk[c] : gl[c], gl[c], lbc);
+    s_f[c] = __expf(lf_of<GM>(to_f32(gl[c]), lbc));
   }
   const float v0 = to_f32(gv[4 * cg + 0]), v1 = to_f32(gv[4 * cg + 1]),
               v2 = to_f32(gv[4 * cg + 2]), v3 = to_f32(gv[4 * cg + 3]);
@@ -98,9 +101,9 @@ __global__ __launch_bounds__(256) void hgrn2_decode_kernel(DecodeArgs a) {
   }
 }
 
-template <typename TIn, int D, bool TIED>
+template <typename TIn, int D, int GM>
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
-  hipLaunchKernelGGL((hgrn2_decode_kernel<TIn, D, TIED>), dim3(a.B * a.H), dim3(DecodeCfg<D>::NT), 0,
+  hipLaunchKernelGGL((hgrn2_decode_kernel<TIn, D, GM>), dim3(a.B * a.H), dim3(DecodeCfg<D>::NT), 0,
                      stream, a);
   return hipGetLastError();
 }

@@ -1,22 +1,42 @@
-// Instantiations of the recurrent decode step for every supported (dtype, D).
+// Instantiations of the recurrent decode step for every supported (dtype, D),
+// and of the lower-bound gradient reduction.
 #include "dispatch.h"
+#include "dlb.h"
 
 namespace hgrn2 {
 
-template <typename TIn, bool TIED>
+template <typename TIn, int GM>
 static hipError_t decode_d(int D, const DecodeArgs &a, hipStream_t s) {
   switch (D) {
-    case 16: return launch_decode<TIn, 16, TIED>(a, s);
-    case 32: return launch_decode<TIn, 32, TIED>(a, s);
-    case 64: return launch_decode<TIn, 64, TIED>(a, s);
-    case 128: return launch_decode<TIn, 128, TIED>(a, s);
+    case 16: return launch_decode<TIn, 16, GM>(a, s);
+    case 32: return launch_decode<TIn, 32, GM>(a, s);
+    case 64: return launch_decode<TIn, 64, GM>(a, s);
+    case 128: return launch_decode<TIn, 128, GM>(a, s);
   }
   return hipErrorNotSupported;
 }
 
-hipError_t dispatch_decode(int dtype, int D, bool tied, const DecodeArgs &a, hipStream_t s) {
-  if (dtype == 0) return tied ? decode_d<float, true>(D, a, s) : decode_d<float, false>(D, a, s);
-  if (dtype == 1) return tied ? decode_d<bf16_t, true>(D, a, s) : decode_d<bf16_t, false>(D, a, s);
+template <typename TIn>
+static hipError_t decode_t(int D, int gm, const DecodeArgs &a, hipStream_t s) {
+  if (gm == kTied) return decode_d<TIn, kTied>(D, a, s);
+  if (gm == kGate) return decode_d<TIn, kGate>(D, a, s);
+  if (gm == kUntied) return decode_d<TIn, kUntied>(D, a, s);
+  return hipErrorNotSupported;
+}
+
+hipError_t dispatch_decode(int dtype, int D, int gm, const DecodeArgs &a, hipStream_t s) {
+  if (dtype == 0) return decode_t<float>(D, gm, a, s);
+  if (dtype == 1) return decode_t<bf16_t>(D, gm, a, s);
+  return hipErrorNotSupported;
+}
+
+hipError_t dispatch_dlb_reduce(int B, int H, int N, int D, const float *part, float *dlb, hipStream_t s) {
+  switch (D) {
+    case 16: return launch_dlb_reduce<16>(B, H, N, part, dlb, s);
+    case 32: return launch_dlb_reduce<32>(B, H, N, part, dlb, s);
+    case 64: return launch_dlb_reduce<64>(B, H, N, part, dlb, s);
+    case 128: return launch_dlb_reduce<128>(B, H, N, part, dlb, s);
+  }
   return hipErrorNotSupported;
 }
 

@@ -41,11 +41,15 @@ hipError_t run_config(int dtype, int D, int C, A... args) {
 // Each returns hipErrorNotSupported (without launching) when no kernel
 // exists for the combination, else the launch status.  A null args pointer
 // only asks whether the kernel exists.
-// `tied`: k = 1 - exp(log f) is formed in the kernel (k pointers unused) and
-// the backward writes the total dlog f and no dk.
-hipError_t dispatch_scan(int dtype, int D, int C, bool reverse, bool tied, const ScanArgs *a, hipStream_t s);
-hipError_t dispatch_chunk_fwd(int dtype, int D, int C, bool tied, const ChunkFwdArgs *a, hipStream_t s);
-hipError_t dispatch_chunk_bwd(int dtype, int D, int C, bool tied, const ChunkBwdArgs *a, hipStream_t s);
-hipError_t dispatch_decode(int dtype, int D, bool tied, const DecodeArgs &a, hipStream_t s);
+// `gm` is a GateMode: kUntied (k and log f are inputs), kTied (k = 1 - f
+// formed from log f; the backward writes the total dlog f and no dk) or kGate
+// (log f and k formed from the pre-activation and the lower bound; the
+// backward writes dz and per-chunk sums of dlb, and no dk).
+hipError_t dispatch_scan(int dtype, int D, int C, bool reverse, int gm, const ScanArgs *a, hipStream_t s);
+hipError_t dispatch_chunk_fwd(int dtype, int D, int C, int gm, const ChunkFwdArgs *a, hipStream_t s);
+hipError_t dispatch_chunk_bwd(int dtype, int D, int C, int gm, const ChunkBwdArgs *a, hipStream_t s);
+hipError_t dispatch_decode(int dtype, int D, int gm, const DecodeArgs &a, hipStream_t s);
+// dlb[h][c] = sum over b and chunks n of part[(b H + h) N + n][c], in a fixed order
+hipError_t dispatch_dlb_reduce(int B, int H, int N, int D, const float *part, float *dlb, hipStream_t s);
 
 }  // namespace hgrn2

@@ -1,0 +1,45 @@
+// Sum of the per-chunk lower-bound gradients over batch and chunks (gate
+// mode): dlb[h][c] = sum_{b, n} part[(b H + h) N + n][c].  The lower bound of
+// a head channel is shared by every token, so its gradient sums the
+// per-token terms (HGRN2 summary, paperlayer.ai, §2.2: per-layer lower
+// bounds).  Small and HBM-bound (one read of B H N D floats); the order of
+// the additions is fixed, so repeated runs agree bit for bit.
+#pragma once
+
+#include "common.h"
+
+namespace hgrn2 {
+
+// One workgroup per (head, group of CG channels); RG row groups of threads
+// split the B N rows of that head in a fixed interleave and are combined in
+// LDS in a fixed order.
+template <int D>
+__global__ __launch_bounds__(256) void hgrn2_dlb_reduce_kernel(int B, int H, int N, const float *part, float *dlb) {
+  constexpr int CG = D < 64 ? D : 64, RG = 256 / CG;
+  __shared__ float acc[RG][CG];
+  const int h = blockIdx.x / (D / CG), c = (blockIdx.x % (D / CG)) * CG + threadIdx.x % CG;
+  const int rg = threadIdx.x / CG;
+  const int rows = B * N;
+  float s = 0.f;
+  for (int r = rg; r < rows; r += RG) {
+    const int b = r / N, n = r % N;
+    s += part[(((size_t)b * H + h) * N + n) * D + c];
+  }
+  acc[rg][threadIdx.x % CG] = s;
+  __syncthreads();
+  if (rg == 0) {
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < RG; ++i) t += acc[i][threadIdx.x];
+    dlb[h * D + c] = t;
+  }
+}
+
+template <int D>
+hipError_t launch_dlb_reduce(int B, int H, int N, const float *part, float *dlb, hipStream_t stream) {
+  hipLaunchKernelGGL(hgrn2_dlb_reduce_kernel<D>, dim3(H * (D / (D < 64 ? D : 64))), dim3(256), 0, stream, B, H, N,
+                     part, dlb);
+  return hipGetLastError();
+}
+
+}  // namespace hgrn2

@@ -6,7 +6,8 @@
 // inclusive prefix b_t of log f and total Gamma = b_C, the state advances as
 //   S <- Diag(e^Gamma) S + sum_t Diag(e^{Gamma - b_t}) x_t^T z_t
 // with (x, z) = (k, v); with tied gates k = 1 - f is formed from log f
-// instead of read.  Walked backwards with (x, z) = (q, dy) and weights
+// instead of read, and from the gate pre-activation both log f and k are
+// formed (rows past the end of the sequence then decay nothing).  Walked backwards with (x, z) = (q, dy) and weights
 // e^{b_t}, the same pass carries the state adjoint Lambda (the gradient of the
 // loss with respect to the state at a chunk end):
 //   Lambda <- Diag(e^Gamma) Lambda + sum_t Diag(e^{b_t}) q_t^T dy_t.
@@ -29,7 +30,8 @@ namespace hgrn2 {
 
 struct ScanArgs {
   int B, T, H, N;
-  const void *x, *z, *log_f;  // [B,T,H,D]
+  const void *x, *z, *log_f;  // [B,T,H,D]; log_f holds the gate pre-activation in gate mode
+  const float *lb;            // gate mode: lower bound of f, [H,D]
   const float *s_in;          // initial state (h0 or dht), [B,H,D,D] float32, or null
   void *states;               // forward: [B,H,N+1,D,D]; backward: [B,H,N,D,D]; input dtype
   float *s_out;               // final state (ht or dh0), or null
@@ -61,7 +63,7 @@ template <typename T, int D, int C, bool REV> struct ScanCfg {
   };
 };
 
-template <typename T, int D, int C, bool REV, bool TIED>
+template <typename T, int D, int C, bool REV, int GM>
 __global__ __launch_bounds__((ScanCfg<T, D, C, REV>::NT)) void hgrn2_scan_kernel(ScanArgs a) {
   using Cfg = ScanCfg<T, D, C, REV>;
   constexpr int NW = Cfg::NW, NT = Cfg::NT, CS = Cfg::CS, NS = Cfg::NS, NR = Cfg::NR, TPR = Cfg::TPR,
@@ -83,6 +85,7 @@ __global__ __launch_bounds__((ScanCfg<T, D, C, REV>::NT)) void hgrn2_scan_kernel
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n16 = lane & 15, g = lane >> 4;
   const int cl = tid % CS, ri = tid / CS;  // prep layout: channel, run of TPR tokens
+  const float lbv = GM == kGate ? a.lb[h * D + cs0 + cl] : 0.f;
 
   const size_t SS = (size_t)D * D;
   const uint32_t HDB = (uint32_t)H * D * sizeof(T);  // bytes from one token to the next
@@ -164,7 +167,7 @@ __global__ __launch_bounds__((ScanCfg<T, D, C, REV>::NT)) void hgrn2_scan_kernel
     const GBuf bl = win(a.log_f, n), bz = win(a.z, n);
 #pragma unroll
     for (int i = 0; i < TPR; ++i) {
-      if constexpr (!TIED) px[i] = win(a.x, n).template ldpack<T, 1>(xoff + (uint32_t)i * HDB).v[0];
+      if constexpr (REV || GM == kUntied) px[i] = win(a.x, n).template ldpack<T, 1>(xoff + (uint32_t)i * HDB).v[0];
       pl[i] = bl.ldpack<T, 1>(xoff + (uint32_t)i * HDB).v[0];
     }
 #pragma unroll
@@ -180,7 +183,7 @@ __global__ __launch_bounds__((ScanCfg<T, D, C, REV>::NT)) void hgrn2_scan_kernel
     float run = 0.f;
 #pragma unroll
     for (int i = 0; i < TPR; ++i) {
-      run += floor_logf(to_f32(pl[i]));
+      run += lf_of<GM>(to_f32(pl[i]), lbv, n * C + ri * TPR + i < T_);
       l[i] = run;
     }
     sm.Lr[ri][cl] = run;
@@ -205,7 +208,8 @@ __global__ __launch_bounds__((ScanCfg<T, D, C, REV>::NT)) void hgrn2_scan_kernel
       for (int i = 0; i < TPR; ++i) {
         const float b_t = P + l[i];
         const float ex = REV ? b_t : fminf(G - b_t, 0.f);
-        sm.x[XT::at(ri * TPR + i, cl)] = from_f32<T>(k_of<TIED>(px[i], pl[i]) * __expf(ex));
+        const float xv = REV ? to_f32(px[i]) : k_of<GM>(px[i], pl[i], lbv);
+        sm.x[XT::at(ri * TPR + i, cl)] = from_f32<T>(xv * __expf(ex));
       }
     }
     flush();  // the state staged in the previous step (read here, rewritten after the next barrier)
@@ -261,12 +265,12 @@ __global__ __launch_bounds__((ScanCfg<T, D, C, REV>::NT)) void hgrn2_scan_kernel
   }
 }
 
-template <typename T, int D, int C, bool REV, bool TIED = false>
+template <typename T, int D, int C, bool REV, int GM = kUntied>
 hipError_t launch_scan(const ScanArgs &a, hipStream_t stream) {
-  static_assert(!(REV && TIED), "the adjoint scan reads q, not k");
+  static_assert(!(REV && GM == kTied), "the adjoint scan reads q, not k: run it untied");
   using Cfg = ScanCfg<T, D, C, REV>;
   const int groups = (a.B * a.H + 7) / 8;
-  hipLaunchKernelGGL((hgrn2_scan_kernel<T, D, C, REV, TIED>), dim3(groups * 8 * Cfg::NS), dim3(Cfg::NT), 0, stream, a);
+  hipLaunchKernelGGL((hgrn2_scan_kernel<T, D, C, REV, GM>), dim3(groups * 8 * Cfg::NS), dim3(Cfg::NT), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -4,15 +4,20 @@
 namespace hgrn2 {
 
 template <typename T, int D, int C> struct ScanOp {
-  static hipError_t run(bool reverse, bool tied, const ScanArgs *a, hipStream_t s) {
-    if (!a) return reverse && tied ? hipErrorNotSupported : hipSuccess;
-    if (reverse) return tied ? hipErrorNotSupported : launch_scan<T, D, C, true>(*a, s);
-    return tied ? launch_scan<T, D, C, false, true>(*a, s) : launch_scan<T, D, C, false>(*a, s);
+  // the adjoint scan never reads k: it runs in the untied form or, when log f
+  // has to be formed from the gate pre-activation, in gate mode
+  static hipError_t run(bool reverse, int gm, const ScanArgs *a, hipStream_t s) {
+    if (gm < kUntied || gm > kGate || (reverse && gm == kTied)) return hipErrorNotSupported;
+    if (!a) return hipSuccess;
+    if (reverse) return gm == kGate ? launch_scan<T, D, C, true, kGate>(*a, s) : launch_scan<T, D, C, true>(*a, s);
+    if (gm == kTied) return launch_scan<T, D, C, false, kTied>(*a, s);
+    if (gm == kGate) return launch_scan<T, D, C, false, kGate>(*a, s);
+    return launch_scan<T, D, C, false>(*a, s);
   }
 };
 
-hipError_t dispatch_scan(int dtype, int D, int C, bool reverse, bool tied, const ScanArgs *a, hipStream_t s) {
-  return run_config<ScanOp>(dtype, D, C, reverse, tied, a, s);
+hipError_t dispatch_scan(int dtype, int D, int C, bool reverse, int gm, const ScanArgs *a, hipStream_t s) {
+  return run_config<ScanOp>(dtype, D, C, reverse, gm, a, s);
 }
 
 }  // namespace hgrn2

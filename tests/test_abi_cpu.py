@@ -27,7 +27,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("hgrn2_fwd", "hgrn2_bwd", "hgrn2_decode_step", "hgrn2_fwd_chunk", "hgrn2_bwd_adjoint",
               "hgrn2_bwd_chunk", "hgrn2_fwd_tied", "hgrn2_bwd_tied", "hgrn2_fwd_chunk_tied",
-              "hgrn2_bwd_chunk_tied", "hgrn2_decode_step_tied"):
+              "hgrn2_bwd_chunk_tied", "hgrn2_decode_step_tied", "hgrn2_fwd_gate", "hgrn2_bwd_gate",
+              "hgrn2_decode_step_gate", "hgrn2_bwd_gate_workspace_bytes"):
         assert n in names
 
 
@@ -37,7 +38,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.hgrn2_abi_version() == 4
+    assert lib.hgrn2_abi_version() == 5
     for s in range(5):
         assert lib.hgrn2_status_string(s).startswith(b"HGRN2_")
 
@@ -155,6 +156,34 @@ def test_tied_rejections(lib):
                                     P[8], None) == 1
     assert lib.hgrn2_decode_step_tied(1, 1, 24, 24, 0, P[0], P[1], P[2], P[3], P[4], None) == 2
     assert lib.hgrn2_decode_step_tied(1, 1, 16, 16, 0, P[0], P[1], P[2], P[3], P[0], None) == 1
+
+
+def test_gate_rejections(lib):
+    P = [FAKE + i * 0x100000 for i in range(16)]
+    # hgrn2_fwd_gate: lower_bound NULL; lower_bound misaligned; y aliases z; lower_bound aliases y
+    assert lib.hgrn2_fwd_gate(1, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], None, None, P[3], None, P[4], None, 0,
+                              None) == 1
+    assert lib.hgrn2_fwd_gate(1, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], P[5] + 2, None, P[3], None, P[4], None, 0,
+                              None) == 1
+    assert lib.hgrn2_fwd_gate(1, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], P[5], None, P[2], None, P[4], None, 0,
+                              None) == 1
+    assert lib.hgrn2_fwd_gate(1, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], P[3], None, P[3], None, P[4], None, 0,
+                              None) == 1
+    # the gate backward's workspace adds B*H*N*DK floats for the per-chunk dlb sums
+    base = lib.hgrn2_bwd_workspace_bytes(2, 10, 3, 16, 16, 16, 0, 1)
+    gate = lib.hgrn2_bwd_gate_workspace_bytes(2, 10, 3, 16, 16, 16, 0, 1)
+    assert gate == base + 2 * 3 * 1 * 16 * 4
+    assert lib.hgrn2_bwd_gate_workspace_bytes(0, 10, 3, 16, 16, 16, 0, 1) == 0
+    args = lambda dlb, ws, wsb: (1, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], P[3], None, P[9], P[4], None,
+                                 P[5], P[6], P[7], dlb, None, ws, wsb, None)
+    need = lib.hgrn2_bwd_gate_workspace_bytes(1, 10, 1, 16, 16, 16, 0, 1)
+    assert lib.hgrn2_bwd_gate(*args(None, P[10], need)) == 1                       # dlower_bound NULL
+    assert lib.hgrn2_bwd_gate(*args(P[11], P[10], lib.hgrn2_bwd_workspace_bytes(1, 10, 1, 16, 16, 16, 0, 1))) == 3
+    assert lib.hgrn2_bwd_gate(*args(P[7], P[10], need)) == 1                       # dlower_bound aliases dz
+    assert lib.hgrn2_bwd_gate(*args(P[3], P[10], need)) == 1                       # dlower_bound aliases lower_bound
+    # decode: lower_bound NULL, unsupported D
+    assert lib.hgrn2_decode_step_gate(1, 1, 16, 16, 0, P[0], P[1], P[2], None, P[4], P[5], None) == 1
+    assert lib.hgrn2_decode_step_gate(1, 1, 24, 24, 0, P[0], P[1], P[2], P[3], P[4], P[5], None) == 2
 
 
 def test_decode_rejections(lib):
