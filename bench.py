@@ -8,7 +8,10 @@ per-chunk gradients) so that HIP events on the launch stream bracket each
 kernel.  Three resident input sets (forget-gate lower bound 0, 0.3, 0.6) are
 rotated across steps.  The same step with tied gates (k = 1 - f formed in the
 kernels, hgrn2_fwd_tied / hgrn2_bwd_tied) is timed next on the same inputs and
-reported under "tied"; the headline value is the untied step.  The decode
+reported under "tied", then the step with the gate formed from its
+pre-activation z and a per-channel lower bound (hgrn2_fwd_gate /
+hgrn2_bwd_gate, its two calls timed) under "gate"; the headline value is the
+untied step.  The decode
 step (B256 H16 d128, float32 state) is timed as well and reported in HBM
 GB/s.  Inputs are seeded synthetic data generated on the host and copied to
 HBM before timing.
@@ -100,7 +103,7 @@ def make_train_sets(torch, w, lams):
     sets = []
     for i, lam in enumerate(lams):
         d = synth.generate(w, lam=lam, seed=w.seed + 10 * i)
-        sets.append({n: to_dev(d[n], "bf16") for n in ("q", "k", "v", "log_f", "dy")})
+        sets.append({n: to_dev(d[n], "bf16") for n in ("q", "k", "v", "log_f", "z", "dy")})
         sets[-1]["host"] = d if i == 0 else None
         log("inputs ready: lambda=%.1f" % lam)
     return sets
@@ -136,6 +139,9 @@ TIED_KERNELS = (("scan_tied", "hgrn2_scan_kernel (forward, tied)"),
                 ("cfwd_tied", "hgrn2_chunk_fwd_kernel (tied)"),
                 ("scan_rev", "hgrn2_scan_kernel (reverse)"),
                 ("cbwd_tied", "hgrn2_chunk_bwd_res_kernel (tied)"))
+# the gate-from-pre-activation step, as its two composite calls
+GATE_CALLS = (("fwd_gate", "hgrn2_fwd_gate: state scan + per-chunk outputs"),
+              ("bwd_gate", "hgrn2_bwd_gate: adjoint scan + per-chunk gradients + lower-bound sum"))
 
 
 def _template_args(n: str):
@@ -144,21 +150,27 @@ def _template_args(n: str):
     return [a.strip() for a in n[n.index("<") + 1:n.rindex(">")].split(",")]
 
 
+GATE_SUFFIX = {"0": "", "1": "_tied", "2": "_gate"}
+
+
 def kernel_label(name: str):
-    """rocprofv3 kernel name -> a label of TRAIN_KERNELS or TIED_KERNELS, "decode[_tied]", or None.
-    Template arguments: scan <T, D, C, REV, TIED>; chunk kernels <T, D, C, TIED> or <TIED>;
-    decode <T, D, TIED>."""
+    """rocprofv3 kernel name -> a label of TRAIN_KERNELS, TIED_KERNELS or GATE_KERNELS,
+    "decode[_tied|_gate]", "dlb", or None.  The last template argument is the gate
+    mode (0 untied, 1 tied, 2 gate): scan <T, D, C, REV, GM>; chunk kernels
+    <T, D, C, GM> or <GM>; decode <T, D, GM>."""
     n = _short(name)
     a = _template_args(n)
-    tied = "_tied" if a and a[-1] == "true" else ""
+    sfx = GATE_SUFFIX.get(a[-1], "") if a else ""
     if n.startswith("hgrn2_scan_kernel"):
-        return "scan_rev" if len(a) > 3 and a[3] == "true" else "scan" + tied
+        return ("scan_rev" if len(a) > 3 and a[3] == "true" else "scan") + sfx
     if n.startswith("hgrn2_chunk_fwd_kernel"):
-        return "cfwd" + tied
+        return "cfwd" + sfx
     if n.startswith("hgrn2_chunk_bwd"):
-        return "cbwd" + tied
+        return "cbwd" + sfx
     if n.startswith("hgrn2_decode_kernel"):
-        return "decode" + tied
+        return "decode" + sfx
+    if n.startswith("hgrn2_dlb_reduce_kernel"):
+        return "dlb"
     return None
 
 
@@ -178,12 +190,22 @@ def train_algorithmic_bytes(w):
         "scan_tied": 2 * tok + (N + 1) * ent,
         "cfwd_tied": 3 * tok + N * ent + tok,
         "cbwd_tied": 4 * tok + 2 * N * ent + 3 * tok,
+        # gate from z: as tied (z in place of log f); the gradient launch also
+        # writes one float per (b, h, chunk, channel) of lower-bound sums, which
+        # the reduction reads back
+        "scan_gate": 2 * tok + (N + 1) * ent,
+        "cfwd_gate": 3 * tok + N * ent + tok,
+        "scan_rev_gate": 3 * tok + N * ent,
+        "cbwd_gate": 4 * tok + 2 * N * ent + 3 * tok + w.B * w.H * N * w.D * 4,
+        "dlb": w.B * w.H * N * w.D * 4 + w.H * w.D * 4,
     }
 
 
-def bench_train(torch, m, args, sets, tied=False):
+def bench_train(torch, m, args, sets, mode="untied"):
     """Times `args.steps` training steps (after `args.warmup` untimed ones) with
-    untied gates (k an input) or tied gates (k = 1 - f formed in the kernels)."""
+    untied gates (k an input), tied gates (k = 1 - f formed in the kernels; the
+    four single launches are timed), or the gate formed from its pre-activation
+    (the two composite calls are timed)."""
     import synth
     w = synth.WORKLOADS["train_bf16"]
     B, T, H, D, C = w.B, w.T, w.H, w.D, w.chunk
@@ -192,7 +214,14 @@ def bench_train(torch, m, args, sets, tied=False):
     states = torch.empty(m.states_shape(B, T, H, D, C), dtype=torch.bfloat16, device=dev)
     lam = torch.empty(m.adjoints_shape(B, T, H, D, C), dtype=torch.bfloat16, device=dev)
     grads = [torch.empty((B, T, H, D), dtype=torch.bfloat16, device=dev) for _ in range(4)]
-    kernels = TIED_KERNELS if tied else TRAIN_KERNELS
+    kernels = {"untied": TRAIN_KERNELS, "tied": TIED_KERNELS, "gate": GATE_CALLS}[mode]
+    lbd = dlbd = ws = None   # gate mode: lower bound [H, D], its gradient, the workspace
+    if mode == "gate":
+        import synth
+        lbd = torch.from_numpy(synth.lower_bounds(H, D, 0.3, 0.25, seed=11)).to(dev)
+        dlbd = torch.empty_like(lbd)
+        ws = torch.empty(int(m.lib().hgrn2_bwd_gate_workspace_bytes(B, T, H, D, D, C, 1, 1)),
+                         dtype=torch.uint8, device=dev)
 
     def calls_untied(s):
         return (
@@ -214,9 +243,18 @@ def bench_train(torch, m, args, sets, tied=False):
                                      dq=grads[0], dv=grads[2], dlog_f=grads[3]),
         )
 
+    def calls_gate(s):
+        return (
+            lambda: m.fwd_gate(s["q"], s["v"], s["z"], lbd, None, chunk=C, want_ht=False, states=states),
+            lambda: m.bwd_gate(s["q"], s["v"], s["z"], lbd, s["dy"], None, None, states, chunk=C, want_dh0=False,
+                               dq=grads[0], dv=grads[2], dz=grads[3], dlower_bound=dlbd, ws=ws),
+        )
+
+    pick = {"untied": calls_untied, "tied": calls_tied, "gate": calls_gate}[mode]
+
     def step(i, timer=None):
         s = sets[i % len(sets)]
-        for (label, _), call in zip(kernels, (calls_tied if tied else calls_untied)(s)):
+        for (label, _), call in zip(kernels, pick(s)):
             t = timer.start(label) if timer else None
             call()
             if timer:
@@ -225,7 +263,7 @@ def bench_train(torch, m, args, sets, tied=False):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    log("warmup done" + (" (tied)" if tied else ""))
+    log("warmup done (%s)" % mode)
     # timed region: exactly `steps` steps, bracketed by synchronisation; the
     # events around each launch are recorded on the stream the kernels run on
     timer = KernelTimer(torch)
@@ -239,8 +277,7 @@ def bench_train(torch, m, args, sets, tied=False):
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
     kms = {label: timer.mean_ms(label) for label, _ in kernels}
-    log("timed%s: %.3f ms/step (%s)" % (" (tied)" if tied else "", ms,
-                                       ", ".join("%s %.3f ms" % kv for kv in kms.items())))
+    log("timed (%s): %.3f ms/step (%s)" % (mode, ms, ", ".join("%s %.3f ms" % kv for kv in kms.items())))
     return dict(w=w, ms=ms, kernel_ms=kms, host=sets[0]["host"])
 
 
@@ -399,14 +436,16 @@ def summarize_mfma(mfma_dir, avg_ns, digest):
     th = w.B * w.T * w.H
     alg_flop = {"scan": th * 2 * w.D * w.D, "cfwd": th * (w.chunk * 2 * w.D + 2 * w.D * w.D),
                 "scan_rev": th * 2 * w.D * w.D, "cbwd": th * (5 * w.chunk * w.D + 6 * w.D * w.D)}
-    for label in ("scan", "cfwd", "cbwd"):       # tied gates change no contraction
+    for label in ("scan", "cfwd", "cbwd"):       # tied gates and the gate from z change no contraction
         alg_flop[label + "_tied"] = alg_flop[label]
+        alg_flop[label + "_gate"] = alg_flop[label]
+    alg_flop["scan_rev_gate"] = alg_flop["scan_rev"]
     out = ["Matrix-core work per launch, HGRN2 training step (B8 H16 T4096 d128 bf16 chunk64)",
            "command: " + MFMA_CMD, "durations: the kernel-trace averages of " + TRACE_CMD,
            "peak: %.0f TFLOP/s dense bf16" % BF16_PEAK_TFLOPS, "source_digest: " + digest, "",
            "%-9s %14s %14s %10s %10s %10s" % ("kernel", "executed_GFLOP", "algorithmic", "TFLOP/s",
                                               "of_peak", "MfmaUtil")]
-    for label in dict(TRAIN_KERNELS + TIED_KERNELS):
+    for label in list(dict(TRAIN_KERNELS + TIED_KERNELS)) + ["scan_gate", "cfwd_gate", "scan_rev_gate", "cbwd_gate"]:
         mops = acc.get((label, "SQ_INSTS_VALU_MFMA_MOPS_BF16"))
         util = acc.get((label, "MfmaUtil"))
         if not mops or label not in avg_ns:
@@ -442,7 +481,8 @@ def main():
         import synth
         sets = make_train_sets(torch, synth.WORKLOADS["train_bf16"], synth.TRAIN_LAMBDAS)
         res = bench_train(torch, m, args, sets)
-        tres = bench_train(torch, m, args, sets, tied=True)
+        tres = bench_train(torch, m, args, sets, mode="tied")
+        gres = bench_train(torch, m, args, sets, mode="gate")
         w = res["w"]
         tokens = w.B * w.T
         out["value"] = tokens / (res["ms"] * 1e-3)
@@ -473,6 +513,11 @@ def main():
                                            "GBps": alg[label] / tk[label] / 1e6,
                                            "frac_hbm": alg[label] / tk[label] / 1e6 / HBM_PEAK_GBS}
                                    for label, kn in TIED_KERNELS}}
+        gk = gres["kernel_ms"]
+        out["gate"] = {"workload": "train_bf16 with the gate formed from its pre-activation z and a lower bound "
+                                   "[H, D] (f = lb + (1 - lb) sigmoid(z), k = 1 - f): fwd(states)+bwd, dz and dlb",
+                       "value": tokens / (gres["ms"] * 1e-3), "unit": "tokens/s", "ms_per_step": gres["ms"],
+                       "calls_ms": {label: gk[label] for label, _ in GATE_CALLS}}
     if args.only in ("decode", "all"):
         dres = bench_decode(torch, m, args)
         out["decode"] = {"workload": "decode_f32: B256 H16 d128, float32 state", "ms": dres["ms"],

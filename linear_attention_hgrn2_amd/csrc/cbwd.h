@@ -148,8 +148,8 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
       if constexpr (GM == kUntied) pk[t] = ldtok(bk, 16 * w + t);
       pl[t] = ldtok(bl, 16 * w + t);
     }
-    float l[16][CPL], L[CPL];
-    block_prefix<GM, T, CPL>(pl, l, L, lbv, len - 16 * w);
+    float l[16][CPL], L[CPL], kk[16][CPL];
+    block_prefix<GM, T, CPL>(pk, pl, l, L, kk, lbv, len - 16 * w);
     if (has_ch) {
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
         for (int e = 0; e < CPL; ++e) {
           oq.v[e] = from_f32<T>(to_f32(pq[t].v[e]) * __expf(l[t][e]));
-          ok.v[e] = from_f32<T>(k_of<GM>(pk[t].v[e], pl[t].v[e], lbv[e]) * __expf(L[e] - l[t][e]));
+          ok.v[e] = from_f32<T>(kk[t][e] * __expf(L[e] - l[t][e]));
         }
         stpack<T, CPL>(&sm.u.in.qo[XT::at(16 * w + t, c0)], oq);
         stpack<T, CPL>(&sm.u.in.ko[XT::at(16 * w + t, c0)], ok);
@@ -320,8 +320,10 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
             const Pack<T, CPL> pl = bl.template ldpack<T, CPL>(tok(16 * w + s) + c0b);
 #pragma unroll
             for (int e = 0; e < CPL; ++e) {
-              part += qt[e] * k_of<GM>(pk.v[e], pl.v[e], lbv[e]) * __expf(ex[e]);
-              ex[e] += lf_of<GM>(to_f32(pl.v[e]), lbv[e]);
+              float lf, kv;
+              lf_k<GM>(pk.v[e], pl.v[e], lbv[e], true, lf, kv);
+              part += qt[e] * kv * __expf(ex[e]);
+              ex[e] += lf;
             }
           }
           const float tot = wave_sum(part);
@@ -489,11 +491,12 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
       Pack<T, CPL> oq, ok;
 #pragma unroll
       for (int e = 0; e < CPL; ++e) {
-        const float lft = lf_of<GM>(to_f32(pl[t].v[e]), lbv[e], tt < len);
+        float lft, kv;
+        lf_k<GM>(pk.v[e], pl[t].v[e], lbv[e], tt < len, lft, kv);
         ell[e] += lft;
         const float el = __expf(ell[e]), ek = __expf(L[e] - ell[e]);
         const float qor = to_f32(from_f32<T>(to_f32(pq.v[e]) * el));
-        const float kor = to_f32(from_f32<T>(k_of<GM>(pk.v[e], pl[t].v[e], lbv[e]) * ek));
+        const float kor = to_f32(from_f32<T>(kv * ek));
         const float d1 = sq[t * LDG + c0 + e], d2 = sk[t * LDG + c0 + e];
         oq.v[e] = from_f32<T>(el * d1);
         ok.v[e] = from_f32<T>(ek * d2);

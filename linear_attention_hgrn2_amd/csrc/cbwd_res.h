@@ -60,6 +60,7 @@ struct CbwdResCfg {
     T gp[NB][NB][D];      // gap factor of a block pair (symmetric)
     float fac[NB][2][D];  // block w: e^{P_w}, e^{Gamma - P_{w+1}}
     float eG[D];          // e^Gamma
+    float lbc[2][D];      // gate mode: lower bounds of this chunk and the next (by parity)
   };
 };
 
@@ -128,6 +129,7 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
   // ---- register prefetch of a chunk's token rows
   uint4 pv[2], pdy[2];               // tile vectors idx = tid + NT i: row idx >> 4, column 8 (idx & 15)
   Pack<T, 2> pq[8], pk[8], pl[8];    // tokens 16 w + 8 hh + t, channels c0, c0 + 1
+  float plb[2];                      // gate mode: lower bounds of channels c0, c0 + 1
   auto prefetch = [&](int ci) {
     // lane-dependent offsets are recomputed per use (never kept live across the loop)
     const int tid = opaque((int)threadIdx.x), c0 = 2 * (tid & 63);
@@ -147,24 +149,37 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
       if constexpr (GM == kUntied) pk[t] = win(a.k, k).template ldpack<T, 2>(off);
       pl[t] = bl.ldpack<T, 2>(off);
     }
+    if constexpr (GM == kGate) {
+      plb[0] = a.lb[(k.bh % H) * D + c0];
+      plb[1] = a.lb[(k.bh % H) * D + c0 + 1];
+    }
   };
 
   const int G = gridDim.x;
   int ci = blockIdx.x;
   if (ci < NC) prefetch(ci);
-  for (; ci < NC; ci += G) {
+  if constexpr (GM == kGate) {
+    // the first chunk's lower bounds (later chunks': staged in P3 of the chunk before)
+    if (ci < NC && wv == 0) {
+      const int cc = 2 * (int)(threadIdx.x & 63);
+      sm.lbc[0][cc] = plb[0];
+      sm.lbc[0][cc + 1] = plb[1];
+    }
+  }
+  int par = 0;  // parity of this workgroup's chunk count: the lbc slot of the current chunk
+  for (; ci < NC; ci += G, par ^= 1) {
     const Chunk k = chunk_of(ci);
     __syncthreads();  // B0: the previous chunk's LDS reads are done
     // lane-dependent values are derived anew each chunk so that the compiler
     // does not hoist every address of the body out of the loop
     const int tid = opaque((int)threadIdx.x), lane = tid & 63, n16 = lane & 15, g = lane >> 4;
     const int c0 = 2 * lane;  // prep / epilogue channels c0, c0 + 1
-    // gate mode: lower bounds of channels c0, c0 + 1, loaded where they are
-    // used (short live ranges)
+    // gate mode: lower bounds of channels c0, c0 + 1 (prefetched with the
+    // token rows and staged in LDS; read where they are used)
     auto lbs = [&](float *o) {
       const int cc = 2 * (opaque((int)threadIdx.x) & 63);
 #pragma unroll
-      for (int e = 0; e < 2; ++e) o[e] = GM == kGate ? a.lb[(k.bh % H) * D + cc + e] : 0.f;
+      for (int e = 0; e < 2; ++e) o[e] = GM == kGate ? sm.lbc[par][cc + e] : 0.f;
     };
     float lb2[2];
     lbs(lb2);
@@ -177,13 +192,16 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
       *(uint4 *)&sm.dy[XT::at(row, col)] = pdy[i];
     }
     float l[8][2], Lw[2], hoff[2] = {0.f, 0.f};  // hoff: prefix before this wave's first token
+    float kf[8][2];                                 // k of the tokens (loaded, or formed with log f)
     {
       float run[2] = {0.f, 0.f};
 #pragma unroll
       for (int t = 0; t < 8; ++t)
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          run[e] += lf_of<GM>(to_f32(pl[t].v[e]), lb2[e], 16 * w + 8 * hh + t < k.len);
+          float lf;
+          lf_k<GM>(pk[t].v[e], pl[t].v[e], lb2[e], 16 * w + 8 * hh + t < k.len, lf, kf[t][e]);
+          run[e] += lf;
           l[t][e] = run[e];
         }
       sm.u.a.x.Lh[w][hh][c0] = run[0];
@@ -214,7 +232,7 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           oq.v[e] = from_f32<T>(to_f32(pq[t].v[e]) * __expf(l[t][e]));
-          ok.v[e] = from_f32<T>(k_of<GM>(pk[t].v[e], pl[t].v[e], lb2[e]) * __expf(Lw[e] - l[t][e]));
+          ok.v[e] = from_f32<T>(kf[t][e] * __expf(Lw[e] - l[t][e]));
         }
         *(Pack<T, 2> *)&sm.qo[XT::at(tt, c0)] = oq;
         *(Pack<T, 2> *)&sm.ko[XT::at(tt, c0)] = ok;
@@ -406,8 +424,15 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
     }
 
     // ---- P3: inter-chunk products (S and Lam must have landed)
-    vm_drain();       // this wave's copies are in LDS
+    vm_drain();       // this wave's copies are in LDS (and its prefetched registers have landed)
     __syncthreads();  // B5: and every other wave's
+    if constexpr (GM == kGate) {
+      // the next chunk's lower bounds into the other slot (read after the next B0)
+      if (wv == 0 && ci + G < NC) {
+        sm.lbc[par ^ 1][c0] = plb[0];
+        sm.lbc[par ^ 1][c0 + 1] = plb[1];
+      }
+    }
     const T *sS = sm.u.a.S, *sL = sm.u.a.L;
     float rsv = 0.f, cp[4];
 #pragma unroll
@@ -601,26 +626,43 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
 #pragma unroll
         for (int o = 0; o < NWV; ++o) carry[e] += (o > wv) ? ep.tot[o][c] : 0.f;
       }
-#pragma unroll
-      for (int t = 7; t >= 0; --t) {
+      // one token: its total G, then (gate mode) dz and its dlb term
+      auto emit = [&](int t, const GateGrad *gg) {
         const int tt = 16 * w + 8 * hh + t;
         Pack<T, 2> o;
-        Pack<T, 2> pz;
-        if constexpr (GM == kGate)
-          if (wide) pz = win(a.log_f, k).template ldpack<T, 2>(tok(tt) + (uint32_t)c0 * sizeof(T));
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           carry[e] += X[t][e];
           float G = GM == kUntied ? carry[e] : carry[e] - ep.stg[1][tt][c0 + e];
           if constexpr (GM == kGate) {
-            const GateGrad gg = wide ? gate_grad(to_f32(pz.v[e]), lb2[e])
-                                     : gate_grad_lf(l[t][e] - (t ? l[t - 1][e] : hoff[e]), lb2[e]);
-            if (tt < k.len) dlbs[e] += G * gg.dlb;
-            G *= gg.dz;
+            if (tt < k.len) dlbs[e] += G * gg[e].dlb;
+            G *= gg[e].dz;
           }
           o.v[e] = from_f32<T>(G);
         }
         bdl.stpack<T, 2, kStream>(tok(tt) + (uint32_t)c0 * sizeof(T), o);
+      };
+      if (GM != kGate || !wide) {
+        // f of each token from the block-local prefix of log f
+#pragma unroll
+        for (int t = 7; t >= 0; --t) {
+          GateGrad gg[2];
+          if constexpr (GM == kGate) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) gg[e] = gate_grad_lf(l[t][e] - (t ? l[t - 1][e] : hoff[e]), lb2[e]);
+          }
+          emit(t, gg);
+        }
+      } else {
+        // a directly summed block: f from z itself
+        for (int t = 7; t >= 0; --t) {
+          const Pack<T, 2> pz =
+              win(a.log_f, k).template ldpack<T, 2>(tok(16 * w + 8 * hh + t) + (uint32_t)c0 * sizeof(T));
+          GateGrad gg[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) gg[e] = gate_grad(to_f32(pz.v[e]), lb2[e]);
+          emit(t, gg);
+        }
       }
       if constexpr (GM == kGate) {
         // per-wave sums into the consumed dq' staging, then a fixed-order sum

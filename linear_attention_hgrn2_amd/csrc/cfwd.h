@@ -62,16 +62,19 @@ __host__ __device__ constexpr int pair_ij(int i, int j) { return i * (i + 1) / 2
 // Sixteen tokens of one lane's CPL channels: the block-local inclusive prefix
 // of the floored log f, in registers.  Tokens from `nvalid` on lie past the
 // end of the sequence (they matter only in gate mode, where log f is formed).
+// kk receives k of every token (loaded, or formed with log f).
 template <int GM, typename T, int CPL>
-__device__ __forceinline__ void block_prefix(const Pack<T, CPL> *pl, float (*l)[CPL], float *L, const float *lb,
-                                             int nvalid) {
+__device__ __forceinline__ void block_prefix(const Pack<T, CPL> *pk, const Pack<T, CPL> *pl, float (*l)[CPL],
+                                             float *L, float (*kk)[CPL], const float *lb, int nvalid) {
 #pragma unroll
   for (int e = 0; e < CPL; ++e) L[e] = 0.f;
 #pragma unroll
   for (int t = 0; t < 16; ++t)
 #pragma unroll
     for (int e = 0; e < CPL; ++e) {
-      L[e] += lf_of<GM>(to_f32(pl[t].v[e]), lb[e], t < nvalid);
+      float lf;
+      lf_k<GM>(pk[t].v[e], pl[t].v[e], lb[e], t < nvalid, lf, kk[t][e]);
+      L[e] += lf;
       l[t][e] = L[e];
     }
 }
@@ -142,7 +145,8 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_fwd_kernel(ChunkFwdArgs a) 
         pl[t] = ldpack<T, CPL>(gl + (tok(tt) + c0));
       }
     }
-    block_prefix<GM, T, CPL>(pl, l, L, lbv, len - 16 * w);
+    float kk[16][CPL];
+    block_prefix<GM, T, CPL>(pk, pl, l, L, kk, lbv, len - 16 * w);
     if (has_ch) {
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
@@ -150,7 +154,7 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_fwd_kernel(ChunkFwdArgs a) 
 #pragma unroll
         for (int e = 0; e < CPL; ++e) {
           oq.v[e] = from_f32<T>(to_f32(pq[t].v[e]) * __expf(l[t][e]));
-          ok.v[e] = from_f32<T>(k_of<GM>(pk[t].v[e], pl[t].v[e], lbv[e]) * __expf(L[e] - l[t][e]));
+          ok.v[e] = from_f32<T>(kk[t][e] * __expf(L[e] - l[t][e]));
         }
         stpack<T, CPL>(&sm.qo[XT::at(16 * w + t, c0)], oq);
         stpack<T, CPL>(&sm.u.kv.ko[XT::at(16 * w + t, c0)], ok);
@@ -219,8 +223,10 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_fwd_kernel(ChunkFwdArgs a) 
             const Pack<T, CPL> pl = ldpack<T, CPL>(gl + (tok(16 * w + s) + c0));
 #pragma unroll
             for (int e = 0; e < CPL; ++e) {
-              part += qt[e] * k_of<GM>(pk.v[e], pl.v[e], lbv[e]) * __expf(ex[e]);
-              ex[e] += lf_of<GM>(to_f32(pl.v[e]), lbv[e]);  // the factor of s - 1 includes f_s
+              float lf, kv;
+              lf_k<GM>(pk.v[e], pl.v[e], lbv[e], true, lf, kv);
+              part += qt[e] * kv * __expf(ex[e]);
+              ex[e] += lf;  // the factor of s - 1 includes f_s
             }
           }
           const float tot = wave_sum(part);

@@ -327,19 +327,35 @@ enum GateMode : int { kUntied = 0, kTied = 1, kGate = 2 };
 // sequence) gives k = 0.
 __device__ __forceinline__ float tied_k(float log_f) { return -expm1f(floor_logf(log_f)); }
 
-// log f for f = lb + (1 - lb) sigmoid(z), for any z.  With u = e^{-|z|} in
-// (0, 1]: z >= 0 gives log1p(lb u) - log1p(u), z < 0 gives
-// log(lb + u) - log1p(u) (which is z - log1p(u) when lb = 0).
+// The gate from its pre-activation, f = lb + (1 - lb) sigmoid(z), evaluated
+// with one exponential, one hardware reciprocal and one logarithm: with
+// u = e^{-|z|} in (0, 1] and r = 1 / (1 + u),
+//   sigmoid(z) = r (z >= 0) or u r (z < 0),  sigmoid(-z) = u r or r,
+//   f = (1 + lb u) r (z >= 0)  or  (lb + u) r (z < 0),
+// and for lb = 0, z < 0, log f = z + log r (no underflow of u r).  Every
+// quantity is a product or sum of positive terms (no cancellation); log f
+// carries an absolute error of a few 1e-8, which is what the decays see.
+struct GateParts {
+  float u, r;
+};
+__device__ __forceinline__ GateParts gate_parts(float z) {
+  GateParts p;
+  p.u = __expf(-fabsf(z));
+  p.r = __builtin_amdgcn_rcpf(1.f + p.u);
+  return p;
+}
+
 __device__ __forceinline__ float gate_log_f(float z, float lb) {
-  const float u = __expf(-fabsf(z));
-  const float a = z >= 0.f ? log1pf(lb * u) : (lb > 0.f ? __logf(lb + u) : z);
-  return a - log1pf(u);
+  const GateParts p = gate_parts(z);
+  const bool neg0 = z < 0.f && lb == 0.f;
+  const float arg = neg0 ? p.r : (z >= 0.f ? fmaf(lb, p.u, 1.f) : lb + p.u) * p.r;
+  return __logf(arg) + (neg0 ? z : 0.f);
 }
 
 // k = 1 - f = (1 - lb) sigmoid(-z), without cancellation
 __device__ __forceinline__ float gate_k(float z, float lb) {
-  const float u = __expf(-fabsf(z));
-  return (1.f - lb) * ((z >= 0.f ? u : 1.f) / (1.f + u));
+  const GateParts p = gate_parts(z);
+  return (1.f - lb) * (z >= 0.f ? p.u * p.r : p.r);
 }
 
 // Factors that turn the total derivative with respect to log f (with k = 1 - f
@@ -351,20 +367,33 @@ struct GateGrad {
 };
 // from the pre-activation itself
 __device__ __forceinline__ GateGrad gate_grad(float z, float lb) {
-  const float u = __expf(-fabsf(z));
-  const float r = 1.f / (1.f + u);
-  const float s = z >= 0.f ? r : u * r, sp = z >= 0.f ? u * r : r;
-  const float f = fmaxf(lb + (1.f - lb) * s, 1e-38f);
+  const GateParts p = gate_parts(z);
+  const float s = z >= 0.f ? p.r : p.u * p.r, sp = z >= 0.f ? p.u * p.r : p.r;
+  const float inv = __builtin_amdgcn_rcpf(fmaxf(lb + (1.f - lb) * s, 1e-30f));
   GateGrad g;
-  g.dz = lb > 0.f ? (1.f - lb) * s * sp / f : sp;  // (1 - lb) s / f = 1 when lb = 0
-  g.dlb = sp / f;
+  g.dz = lb > 0.f ? (1.f - lb) * s * sp * inv : sp;  // (1 - lb) s / f = 1 when lb = 0
+  g.dlb = sp * inv;
   return g;
 }
+// 1 - e^x for x <= 0 without cancellation: a Taylor polynomial of e^x - 1 to
+// the x^7 term for x >= -1/4 (truncation below 4e-10 relative), 1 - e^x below
+// (e^x < 0.78 there, so the subtraction loses under two bits)
+__device__ __forceinline__ float one_minus_exp(float x, float ex) {
+  float p = fmaf(x, 1.f / 5040.f, 1.f / 720.f);
+  p = fmaf(x, p, 1.f / 120.f);
+  p = fmaf(x, p, 1.f / 24.f);
+  p = fmaf(x, p, 1.f / 6.f);
+  p = fmaf(x, p, 0.5f);
+  p = fmaf(x, p, 1.f);
+  return x >= -0.25f ? -x * p : 1.f - ex;
+}
+
 // from log f (floored) when z is no longer at hand: s' = (1 - f) / (1 - lb)
-// and (1 - lb) s = f - lb, with 1 - f = -expm1(log f)
+// and (1 - lb) s = f - lb
 __device__ __forceinline__ GateGrad gate_grad_lf(float lf, float lb) {
-  const float f = fmaxf(__expf(lf), 1e-38f), omf = -expm1f(lf);
-  const float inv = 1.f / ((1.f - lb) * f);
+  const float ex = __expf(lf);
+  const float f = fmaxf(ex, 1e-30f), omf = one_minus_exp(lf, ex);
+  const float inv = __builtin_amdgcn_rcpf((1.f - lb) * f);
   GateGrad g;
   g.dz = lb > 0.f ? (f - lb) * omf * inv : omf;
   g.dlb = omf * inv;
@@ -377,6 +406,23 @@ __device__ __forceinline__ GateGrad gate_grad_lf(float lf, float lb) {
 template <int GM> __device__ __forceinline__ float lf_of(float x, float lb, bool valid = true) {
   if constexpr (GM == kGate) return valid ? floor_logf(gate_log_f(x, lb)) : 0.f;
   else return floor_logf(x);
+}
+
+// log f and k of one token together (the gate pieces computed once):
+// kUntied loads k, kTied forms k = -expm1(log f), kGate forms both from z.
+template <int GM, typename T>
+__device__ __forceinline__ void lf_k(T k, T x, float lb, bool valid, float &lf, float &kv) {
+  if constexpr (GM == kGate) {
+    const float z = to_f32(x);
+    const GateParts p = gate_parts(z);
+    const bool neg0 = z < 0.f && lb == 0.f;
+    const float arg = neg0 ? p.r : (z >= 0.f ? fmaf(lb, p.u, 1.f) : lb + p.u) * p.r;
+    lf = valid ? floor_logf(__logf(arg) + (neg0 ? z : 0.f)) : 0.f;
+    kv = (1.f - lb) * (z >= 0.f ? p.u * p.r : p.r);
+  } else {
+    lf = floor_logf(to_f32(x));
+    kv = GM == kTied ? -expm1f(lf) : to_f32(k);
+  }
 }
 
 // k of a token: loaded (kUntied) or formed from the gate input x

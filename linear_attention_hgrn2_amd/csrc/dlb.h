@@ -10,22 +10,26 @@
 
 namespace hgrn2 {
 
-// One workgroup per (head, group of CG channels); RG row groups of threads
-// split the B N rows of that head in a fixed interleave and are combined in
-// LDS in a fixed order.
+// One workgroup of 1024 threads per (head, group of CG channels): RG row
+// groups split the B N rows of that head in a fixed interleave, each thread
+// keeping four independent partial sums (four loads in flight), and the row
+// groups are combined in LDS in a fixed order.
 template <int D>
-__global__ __launch_bounds__(256) void hgrn2_dlb_reduce_kernel(int B, int H, int N, const float *part, float *dlb) {
-  constexpr int CG = D < 64 ? D : 64, RG = 256 / CG;
+__global__ __launch_bounds__(1024) void hgrn2_dlb_reduce_kernel(int B, int H, int N, const float *part, float *dlb) {
+  constexpr int CG = D < 64 ? D : 64, RG = 1024 / CG;
   __shared__ float acc[RG][CG];
   const int h = blockIdx.x / (D / CG), c = (blockIdx.x % (D / CG)) * CG + threadIdx.x % CG;
   const int rg = threadIdx.x / CG;
   const int rows = B * N;
-  float s = 0.f;
-  for (int r = rg; r < rows; r += RG) {
-    const int b = r / N, n = r % N;
-    s += part[(((size_t)b * H + h) * N + n) * D + c];
+  auto at = [&](int r) { return part[(((size_t)(r / N) * H + h) * N + (r % N)) * D + c]; };
+  float s[4] = {0.f, 0.f, 0.f, 0.f};
+  int r = rg;
+  for (; r + 3 * RG < rows; r += 4 * RG) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] += at(r + i * RG);
   }
-  acc[rg][threadIdx.x % CG] = s;
+  for (; r < rows; r += RG) s[0] += at(r);
+  acc[rg][threadIdx.x % CG] = (s[0] + s[1]) + (s[2] + s[3]);
   __syncthreads();
   if (rg == 0) {
     float t = 0.f;
@@ -37,7 +41,7 @@ __global__ __launch_bounds__(256) void hgrn2_dlb_reduce_kernel(int B, int H, int
 
 template <int D>
 hipError_t launch_dlb_reduce(int B, int H, int N, const float *part, float *dlb, hipStream_t stream) {
-  hipLaunchKernelGGL(hgrn2_dlb_reduce_kernel<D>, dim3(H * (D / (D < 64 ? D : 64))), dim3(256), 0, stream, B, H, N,
+  hipLaunchKernelGGL(hgrn2_dlb_reduce_kernel<D>, dim3(H * (D / (D < 64 ? D : 64))), dim3(1024), 0, stream, B, H, N,
                      part, dlb);
   return hipGetLastError();
 }

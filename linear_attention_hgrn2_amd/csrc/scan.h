@@ -179,11 +179,14 @@ __global__ __launch_bounds__((ScanCfg<T, D, C, REV>::NT)) void hgrn2_scan_kernel
     const int n = REV ? N - 1 - it : it;
     T *zs = sm.z[it & 1];
     // ---- chunk-local prefix of the floored log f: within the lane's run, then across runs
-    float l[TPR];
+    float l[TPR], kx[TPR];  // kx: k of the run's tokens (forward; formed with log f)
     float run = 0.f;
 #pragma unroll
     for (int i = 0; i < TPR; ++i) {
-      run += lf_of<GM>(to_f32(pl[i]), lbv, n * C + ri * TPR + i < T_);
+      float lf;
+      if constexpr (REV) lf = lf_of<GM>(to_f32(pl[i]), lbv, n * C + ri * TPR + i < T_);
+      else lf_k<GM>(px[i], pl[i], lbv, n * C + ri * TPR + i < T_, lf, kx[i]);
+      run += lf;
       l[i] = run;
     }
     sm.Lr[ri][cl] = run;
@@ -208,7 +211,7 @@ __global__ __launch_bounds__((ScanCfg<T, D, C, REV>::NT)) void hgrn2_scan_kernel
       for (int i = 0; i < TPR; ++i) {
         const float b_t = P + l[i];
         const float ex = REV ? b_t : fminf(G - b_t, 0.f);
-        const float xv = REV ? to_f32(px[i]) : k_of<GM>(px[i], pl[i], lbv);
+        const float xv = REV ? to_f32(px[i]) : kx[i];
         sm.x[XT::at(ri * TPR + i, cl)] = from_f32<T>(xv * __expf(ex));
       }
     }

@@ -78,6 +78,14 @@ def test_gate_shapes(dtype, D, C):
     _check(d, C)
 
 
+@pytest.mark.parametrize("lam,spread", [(0.0, 0.0), (0.97, 0.02)])
+def test_gate_lower_bound_regimes_f32(lam, spread):
+    """float32 (tolerance 1e-4) with no lower bound and with gates near one,
+    where log f is small and its absolute accuracy matters most."""
+    d = _case("f32", B=2, T=5 * 64 + 3, H=3, D=64, lam=lam, spread=spread, h0std=0.2)
+    _check(d, 64, label="f32 lam=%.2f+-%.2f" % (lam, spread))
+
+
 @pytest.mark.parametrize("lam,spread", [(0.0, 0.0), (0.5, 0.45), (0.97, 0.02)])
 def test_gate_lower_bound_regimes_d128(lam, spread):
     """No lower bound (plain sigmoid gate), bounds spread over (0.05, 0.95), and
