@@ -58,7 +58,8 @@ def parse():
     p.add_argument("--decode-steps", type=int, default=50)
     p.add_argument("--only", choices=["train", "decode", "all"], default="all")
     p.add_argument("--calib-copy", action="store_true",
-                   help="also run a plain 1 GiB device copy (calibrates profiler byte counters)")
+                   help="also run a plain 1 GiB elementwise pass, read once and written once "
+                        "(calibrates profiler byte counters)")
     p.add_argument("--summarize", nargs="+", metavar="DIR",
                    help="TRACE_DIR FETCH_DIR WRITE_DIR [MFMA_DIR]: write the profiles/ summaries "
                         "from rocprofv3 csv output and exit")
@@ -394,15 +395,15 @@ def summarize(trace_dir, fetch_dir, write_dir, mfma_dir=None):
         return {k: sum(v) / len(v) for k, v in acc.items()}
 
     fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
-    copy = [k for k in fetch if "copyBuffer" in k]
+    copy = [k for k in fetch if "MulFunctor" in k and k in write]
     assert copy, "the counter runs need --calib-copy"
     f_fac = CALIB_BYTES / (fetch[copy[0]] * 1024)
     w_fac = CALIB_BYTES / (write[copy[0]] * 1024)
     out = ["HBM traffic per launch, HGRN2 training step (B8 H16 T4096 d128 bf16 chunk64)",
            "fetch command: " + PMC_CMD.format(ctr="FETCH_SIZE", dir="fetch"),
            "write command: " + PMC_CMD.format(ctr="WRITE_SIZE", dir="write"),
-           "calibration: a 1 GiB device copy reads FETCH_SIZE %.0f KiB and WRITE_SIZE %.0f KiB"
-           % (fetch[copy[0]], write[copy[0]]),
+           "calibration: a 1 GiB elementwise pass (torch.mul, 1 GiB read, 1 GiB written) reads "
+           "FETCH_SIZE %.0f KiB and WRITE_SIZE %.0f KiB" % (fetch[copy[0]], write[copy[0]]),
            "fetch_scale: %.4f" % f_fac, "write_scale: %.4f" % w_fac,
            "source_digest: " + digest, ""]
     for k in fetch:
@@ -530,11 +531,14 @@ def main():
             out["ms_per_step"] = dres["ms"]
             out["config"] = {"workload": "decode_f32: B256 H16 d128"}
     if args.calib_copy:
+        # torch's elementwise multiply: a grid over every XCD reading 1 GiB and
+        # writing 1 GiB (the runtime's copy kernel has been seen to spread over
+        # fewer XCDs, which skews per-XCD counters)
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
         dst = torch.empty_like(src)
         src.fill_(1.0)
         for _ in range(3):
-            dst.copy_(src)
+            torch.mul(src, 2.0, out=dst)
         torch.cuda.synchronize()
     if res is not None and not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(res)
