@@ -26,7 +26,8 @@ _lib = None
 
 __all__ = ["build", "forward", "backward", "decode_step", "forward_tied", "backward_tied",
            "decode_step_tied", "tied_k", "gate_log_f", "gate_k", "gate_partials", "forward_gate",
-           "backward_gate", "decode_step_gate", "threads", "Oracle", "default"]
+           "backward_gate", "decode_step_gate", "hgrn1_forward", "hgrn1_backward", "threads", "Oracle",
+           "default"]
 
 
 def build(force: bool = True) -> str:
@@ -246,3 +247,39 @@ def backward_gate(q, v, z, lam, dy, h0=None, dht=None):
 def decode_step_gate(q, v, z, lam, state):
     """decode_step() with log f and k formed from z [B,H,DK] and lam [H,DK]."""
     return decode_step(q, gate_k(z, lam), v, gate_log_f(z, lam), state)
+
+
+# ------------------------------------------------------------------ HGRN1 elementwise recurrence
+# HGRN's gated linear RNN (HGRN2 summary, paperlayer.ai, §2.1): per channel c,
+#     h_t[c] = f_t[c] h_{t-1}[c] + k_t[c] v_t[c],     y_t[c] = q_t[c] h_t[c],
+# with the input gate k = 1 - f in HGRN1 itself (tied) and q the output gate.
+# It is the HGRN2 recurrence with d_k = d_v = 1 and every channel its own
+# head, so it runs through the same step loop: [B, T, C] becomes
+# [B, T, C, 1] with C heads.
+
+
+def _h1(x):
+    return None if x is None else np.asarray(x, dtype=np.float64)[..., None]
+
+
+def hgrn1_forward(q, k, v, log_f, h0=None, tied=False):
+    """(y [B,T,C], hT [B,C]).  tied: k = 1 - exp(log_f) (k is ignored)."""
+    lf = np.asarray(log_f, dtype=np.float64)
+    kk = tied_k(lf) if tied else k
+    h0_ = None if h0 is None else np.asarray(h0, dtype=np.float64)[..., None, None]
+    y, ht = forward(_h1(q), _h1(kk), _h1(v), _h1(lf), h0_)
+    return y[..., 0], ht[..., 0, 0]
+
+
+def hgrn1_backward(q, k, v, log_f, dy, h0=None, dht=None, tied=False):
+    """(dq, dk or None, dv, dlog_f, dh0) of the loss sum(y dy) + sum(hT dht);
+    tied: dlog_f is the total derivative (dlog_f - f dk) and dk is None."""
+    lf = np.asarray(log_f, dtype=np.float64)
+    kk = tied_k(lf) if tied else k
+    h0_ = None if h0 is None else np.asarray(h0, dtype=np.float64)[..., None, None]
+    dht_ = None if dht is None else np.asarray(dht, dtype=np.float64)[..., None, None]
+    dq, dk, dv, dl, dh0 = backward(_h1(q), _h1(kk), _h1(v), _h1(lf), _h1(dy), h0_, dht_)
+    dq, dk, dv, dl, dh0 = dq[..., 0], dk[..., 0], dv[..., 0], dl[..., 0], dh0[..., 0, 0]
+    if tied:
+        return dq, None, dv, dl - np.exp(lf) * dk, dh0
+    return dq, dk, dv, dl, dh0

@@ -446,9 +446,66 @@ def pin_gate_autograd(orc):
     assert rel(y, Y.detach().numpy()) < 1e-13 and rel(ht, S.detach().numpy()) < 1e-13
 
 
+# ---------------------------------------------------------------- HGRN1 elementwise recurrence
+
+def pin_hgrn1_geometric(orc):
+    """HGRN1 with a constant gate f and a constant input i, tied (k = 1 - f),
+    output gate 1: h_t = f^t h0 + (1 - f^t) i, the closed form of a first-order
+    linear recurrence with constant coefficients."""
+    import oracle as o
+    B, T, C = 2, 23, 5
+    r = _rng(31)
+    f = r.uniform(0.2, 0.99, (1, 1, C))
+    i = r.standard_normal((B, 1, C))
+    h0 = r.standard_normal((B, C))
+    lf = np.broadcast_to(np.log(f), (B, T, C)).copy()
+    v = np.broadcast_to(i, (B, T, C)).copy()
+    q = np.ones((B, T, C))
+    y, hT = o.hgrn1_forward(q, None, v, lf, h0, tied=True)
+    tt = np.arange(1, T + 1)[None, :, None]
+    ref = f ** tt * h0[:, None, :] + (1.0 - f ** tt) * i
+    assert rel(y, ref) < 1e-13 and rel(hT, ref[:, -1]) < 1e-13
+
+
+def pin_hgrn1_finite_differences(orc):
+    """HGRN1 gradients (untied and tied) against central differences of the loss
+    sum(y dy) + sum(hT dht) in every input."""
+    import oracle as o
+    B, T, C = 1, 9, 3
+    r = _rng(32)
+    q, k, v = (r.standard_normal((B, T, C)) for _ in range(3))
+    lf = r.uniform(-1.5, 0.0, (B, T, C))
+    h0 = r.standard_normal((B, C))
+    dy = r.standard_normal((B, T, C))
+    dht = r.standard_normal((B, C))
+    for tied in (False, True):
+        def loss(q, k, v, lf, h0):
+            y, hT = o.hgrn1_forward(q, k, v, lf, h0, tied=tied)
+            return float((y * dy).sum() + (hT * dht).sum())
+        dq, dk, dv, dl, dh0 = o.hgrn1_backward(q, k, v, lf, dy, h0, dht, tied=tied)
+        args = [q, k, v, lf, h0]
+        for ai, g in ((0, dq), (1, dk), (2, dv), (3, dl), (4, dh0)):
+            if g is None:
+                continue
+            x = args[ai]
+            num = np.zeros_like(x)
+            it = np.nditer(x, flags=["multi_index"])
+            for _ in it:
+                idx = it.multi_index
+                old = x[idx]
+                x[idx] = old + 1e-6
+                lp = loss(*args)
+                x[idx] = old - 1e-6
+                lm = loss(*args)
+                x[idx] = old
+                num[idx] = (lp - lm) / 2e-6
+            assert rel(g, num) < 1e-7, (tied, ai, rel(g, num))
+
+
 ALL_PINS = [pin_closed_form, pin_limit_f_one, pin_limit_f_zero, pin_scalar_scan,
             pin_golden_exact, pin_linearity, pin_state_carry, pin_decode,
             pin_finite_differences, pin_autograd, pin_dlogf_identity, pin_bwd_limits,
             pin_tied_finite_differences, pin_tied_autograd,
-            pin_gate_log_sigmoid, pin_gate_finite_differences, pin_gate_autograd]
+            pin_gate_log_sigmoid, pin_gate_finite_differences, pin_gate_autograd,
+            pin_hgrn1_geometric, pin_hgrn1_finite_differences]
 GATE_PINS = [pin_gate_log_sigmoid, pin_gate_finite_differences, pin_gate_autograd]
