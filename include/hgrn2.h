@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define HGRN2_ABI_VERSION 5
+#define HGRN2_ABI_VERSION 6
 
 typedef enum {
   HGRN2_OK = 0,
@@ -260,6 +260,39 @@ hgrn2_status hgrn2_bwd_gate(int B, int T, int H, int DK, int DV, int chunk, int 
 hgrn2_status hgrn2_decode_step_gate(int B, int H, int DK, int DV, int dtype, const void *q,
                                     const void *v, const void *z, const float *lower_bound,
                                     float *state, void *y, void *stream);
+
+/*
+ * HGRN1: the elementwise gated linear recurrence that HGRN2 expands (HGRN2
+ * summary §2.1), per channel c of [B, T, C] tensors:
+ *     h_t[c] = f_t[c] h_{t-1}[c] + k_t[c] v_t[c],     y_t[c] = q_t[c] h_t[c],
+ * f = exp(log_f), q the output gate, v the input; tied = 1 ties the input gate
+ * to the forget gate, k = 1 - f (HGRN1's own form; k and dk are then NULL and
+ * dlog_f is the total derivative dlog_f - f dk).  It is HGRN2's recurrence
+ * with d_k = d_v = 1.  C = the channels of a token row (heads times head
+ * width), any even C >= 2; any B, T >= 1.  Token tensors [B, T, C] in dtype,
+ * 16-byte aligned; h0, hT, dht, dh0 float32 [B, C] (optional, NULL = zero /
+ * not written).
+ *
+ * The sequence is scanned in segments of 32 tokens.  states_out (optional)
+ * receives the state entering every segment, float32 [B, S, C] with
+ * S = ceil(T / 32) (hgrn1_states_bytes()); hgrn1_bwd takes it as states_in or,
+ * with NULL, recomputes it in the workspace.  Workspaces: hgrn1_fwd_workspace_bytes(),
+ * hgrn1_bwd_workspace_bytes() (have_states = whether states_out / states_in is
+ * passed).  Each call enqueues three kernels (segment summaries, a serial pass
+ * over segments per channel, the segments again), five for a backward that
+ * recomputes the states.  Errors as for the other calls; C odd is
+ * HGRN2_ERR_UNSUPPORTED.
+ */
+size_t hgrn1_states_bytes(int B, int T, int C);
+size_t hgrn1_fwd_workspace_bytes(int B, int T, int C, int have_states);
+size_t hgrn1_bwd_workspace_bytes(int B, int T, int C, int have_states);
+hgrn2_status hgrn1_fwd(int B, int T, int C, int dtype, int tied, const void *q, const void *k,
+                       const void *v, const void *log_f, const float *h0, void *y, float *hT,
+                       float *states_out, void *ws, size_t ws_bytes, void *stream);
+hgrn2_status hgrn1_bwd(int B, int T, int C, int dtype, int tied, const void *q, const void *k,
+                       const void *v, const void *log_f, const float *h0, const float *states_in,
+                       const void *dy, const float *dht, void *dq, void *dk, void *dv,
+                       void *dlog_f, float *dh0, void *ws, size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -84,6 +84,16 @@ def _lib():
         lib.hgrn2_bwd_gate.restype = I
         lib.hgrn2_decode_step_gate.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P]
         lib.hgrn2_decode_step_gate.restype = I
+        for n in ("hgrn1_states_bytes",):
+            getattr(lib, n).argtypes = [I, I, I]
+            getattr(lib, n).restype = Z
+        for n in ("hgrn1_fwd_workspace_bytes", "hgrn1_bwd_workspace_bytes"):
+            getattr(lib, n).argtypes = [I, I, I, I]
+            getattr(lib, n).restype = Z
+        lib.hgrn1_fwd.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, P, Z, P]
+        lib.hgrn1_fwd.restype = I
+        lib.hgrn1_bwd.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
+        lib.hgrn1_bwd.restype = I
         _handle = lib
     return _handle
 
@@ -504,6 +514,82 @@ def decode_step_gate(q, v, z, lower_bound, state, *, y=None):
                                        _ptr(state), _ptr(y), _stream())
     _check(st, "hgrn2_decode_step_gate")
     return y
+
+
+def _tok3(name, t, B, T, C, dtype):
+    if t.shape != (B, T, C) or t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+        raise ValueError("%s: expected a contiguous %s CUDA tensor of shape %s" % (name, dtype, (B, T, C)))
+
+
+def _vec(name, t, B, C):
+    if t is None:
+        return
+    if t.shape != (B, C) or t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError("%s: expected a contiguous float32 CUDA tensor of shape %s" % (name, (B, C)))
+
+
+def hgrn1_states_shape(B, T, C):
+    return (B, (T + 31) // 32, C)
+
+
+def hgrn1_fwd(q, k, v, log_f, h0=None, *, tied=False, want_ht=True, want_states=False, y=None, ht=None,
+              states=None, ws=None):
+    """HGRN1 elementwise recurrence over [B, T, C] tensors (k = 1 - exp(log_f)
+    when tied; k is then ignored).  Returns (y, hT or None, states or None)."""
+    B, T, C = q.shape
+    dt = q.dtype
+    if dt not in _DT:
+        raise ValueError("dtype must be float32 or bfloat16")
+    for n, t in (("q", q), ("v", v), ("log_f", log_f)) + ((("k", k),) if not tied else ()):
+        _tok3(n, t, B, T, C, dt)
+    _vec("h0", h0, B, C)
+    y = torch.empty_like(q) if y is None else y
+    _tok3("y", y, B, T, C, dt)
+    if want_ht and ht is None:
+        ht = torch.empty((B, C), dtype=torch.float32, device=q.device)
+    _vec("hT", ht, B, C)
+    if want_states and states is None:
+        states = torch.empty(hgrn1_states_shape(B, T, C), dtype=torch.float32, device=q.device)
+    need = int(_lib().hgrn1_fwd_workspace_bytes(B, T, C, int(states is not None)))
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = _lib().hgrn1_fwd(B, T, C, _DT[dt], int(tied), _ptr(q), None if tied else _ptr(k), _ptr(v), _ptr(log_f),
+                          _ptr(h0), _ptr(y), _ptr(ht), _ptr(states), _ptr(ws), ws.numel(), _stream())
+    _check(st, "hgrn1_fwd")
+    return y, ht, states
+
+
+def hgrn1_bwd(q, k, v, log_f, dy, h0=None, dht=None, states=None, *, tied=False, want_dh0=True,
+              dq=None, dk=None, dv=None, dlog_f=None, dh0=None, ws=None):
+    """Backward of hgrn1_fwd.  Returns (dq, dk or None (tied), dv, dlog_f, dh0 or None);
+    tied: dlog_f is the total derivative."""
+    B, T, C = q.shape
+    dt = q.dtype
+    for n, t in (("q", q), ("v", v), ("log_f", log_f), ("dy", dy)) + ((("k", k),) if not tied else ()):
+        _tok3(n, t, B, T, C, dt)
+    _vec("h0", h0, B, C)
+    _vec("dht", dht, B, C)
+    dq = torch.empty_like(q) if dq is None else dq
+    dv = torch.empty_like(q) if dv is None else dv
+    dlog_f = torch.empty_like(q) if dlog_f is None else dlog_f
+    if not tied and dk is None:
+        dk = torch.empty_like(q)
+    for n, t in (("dq", dq), ("dv", dv), ("dlog_f", dlog_f)) + ((("dk", dk),) if not tied else ()):
+        _tok3(n, t, B, T, C, dt)
+    if want_dh0 and dh0 is None:
+        dh0 = torch.empty((B, C), dtype=torch.float32, device=q.device)
+    _vec("dh0", dh0, B, C)
+    if states is not None and (tuple(states.shape) != hgrn1_states_shape(B, T, C) or states.dtype != torch.float32
+                               or not states.is_contiguous()):
+        raise ValueError("states: expected a contiguous float32 tensor of shape %s" % (hgrn1_states_shape(B, T, C),))
+    need = int(_lib().hgrn1_bwd_workspace_bytes(B, T, C, int(states is not None)))
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = _lib().hgrn1_bwd(B, T, C, _DT[dt], int(tied), _ptr(q), None if tied else _ptr(k), _ptr(v), _ptr(log_f),
+                          _ptr(h0), _ptr(states), _ptr(dy), _ptr(dht), _ptr(dq), None if tied else _ptr(dk),
+                          _ptr(dv), _ptr(dlog_f), _ptr(dh0), _ptr(ws), ws.numel(), _stream())
+    _check(st, "hgrn1_bwd")
+    return dq, (None if tied else dk), dv, dlog_f, dh0
 
 
 class HGRN2Chunk(torch.autograd.Function):

@@ -553,4 +553,138 @@ hgrn2_status hgrn2_decode_step_gate(int B, int H, int DK, int DV, int dtype, con
                      stream);
 }
 
+// ---- HGRN1 elementwise scan
+
+static hgrn2_status h1_check(int B, int T, int C, int dtype, int tied) {
+  if (B <= 0 || T <= 0 || C <= 0) return fail(HGRN2_ERR_INVALID_ARG, "B, T and C must be >= 1");
+  if ((long long)B * T * C > (1LL << 40) || (long long)B * C > (1LL << 30))
+    return fail(HGRN2_ERR_INVALID_ARG, "problem too large");
+  if (!valid_dtype(dtype)) return fail(HGRN2_ERR_INVALID_ARG, "dtype must be HGRN2_F32 or HGRN2_BF16");
+  if (tied != 0 && tied != 1) return fail(HGRN2_ERR_INVALID_ARG, "tied must be 0 or 1");
+  if (C % 2 != 0) return fail(HGRN2_ERR_UNSUPPORTED, "C must be even");
+  return HGRN2_OK;
+}
+
+size_t hgrn1_states_bytes(int B, int T, int C) {
+  if (B <= 0 || T <= 0 || C <= 0) return 0;
+  return (size_t)B * hgrn2::h1_segments(T) * C * sizeof(float);
+}
+
+size_t hgrn1_fwd_workspace_bytes(int B, int T, int C, int have_states) {
+  const size_t sb = hgrn1_states_bytes(B, T, C);
+  return 2 * sb + (have_states ? 0 : sb);
+}
+
+size_t hgrn1_bwd_workspace_bytes(int B, int T, int C, int have_states) {
+  const size_t sb = hgrn1_states_bytes(B, T, C);
+  return 3 * sb + (have_states ? 0 : sb);
+}
+
+static hgrn2::H1Args h1_args(int B, int T, int C) {
+  hgrn2::H1Args a{};
+  a.B = B;
+  a.T = T;
+  a.C = C;
+  a.S = hgrn2::h1_segments(T);
+  return a;
+}
+
+static hgrn2_status h1_launch(int op, int dtype, int gm, const hgrn2::H1Args &a, void *stream, const char *fn) {
+  return hip_status(hgrn2::dispatch_hgrn1(op, dtype, gm, a, (hipStream_t)stream), fn);
+}
+
+hgrn2_status hgrn1_fwd(int B, int T, int C, int dtype, int tied, const void *q, const void *k, const void *v,
+                       const void *log_f, const float *h0, void *y, float *hT, float *states_out, void *ws,
+                       size_t ws_bytes, void *stream) {
+  const char *fn = "hgrn1_fwd";
+  hgrn2_status st = h1_check(B, T, C, dtype, tied);
+  if (st != HGRN2_OK) return st;
+  st = check_ptrs({{"q", q}, {"v", v}, {"log_f", log_f}, {"y", y}},
+                  {{"h0", h0}, {"hT", hT}, {"states_out", states_out}, {"ws", ws}});
+  if (st == HGRN2_OK) st = need_k(tied ? kTied : kUntied, k, "k");
+  if (st != HGRN2_OK) return st;
+  const size_t tok = (size_t)B * T * C * dsize(dtype), sb = hgrn1_states_bytes(B, T, C),
+               hb = (size_t)B * C * sizeof(float);
+  const size_t need = hgrn1_fwd_workspace_bytes(B, T, C, states_out != nullptr);
+  if (!ws || ws_bytes < need) return fail(HGRN2_ERR_WORKSPACE, "workspace smaller than hgrn1_fwd_workspace_bytes()");
+  if (tied) k = nullptr;
+  const Range ins[] = {{"q", q, tok}, {"k", k, tok}, {"v", v, tok}, {"log_f", log_f, tok}, {"h0", h0, hb}};
+  const Range outs[] = {{"y", y, tok}, {"hT", hT, hb}, {"states_out", states_out, sb}, {"ws", ws, need}};
+  std::string msg;
+  if (!check_aliasing(ins, 5, outs, 4, msg)) return fail(HGRN2_ERR_INVALID_ARG, msg);
+  hgrn2::H1Args a = h1_args(B, T, C);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.log_f = log_f;
+  a.s_in = h0;
+  a.A = (float *)ws;
+  a.Bs = (float *)((char *)ws + sb);
+  a.carry = states_out ? states_out : (float *)((char *)ws + 2 * sb);
+  a.s_out = hT;
+  a.y = y;
+  const int gm = tied ? kTied : kUntied;
+  if ((st = h1_launch(hgrn2::kH1SummaryFwd, dtype, gm, a, stream, fn)) != HGRN2_OK) return st;
+  if ((st = h1_launch(hgrn2::kH1CarryFwd, dtype, gm, a, stream, fn)) != HGRN2_OK) return st;
+  return h1_launch(hgrn2::kH1FinalFwd, dtype, gm, a, stream, fn);
+}
+
+hgrn2_status hgrn1_bwd(int B, int T, int C, int dtype, int tied, const void *q, const void *k, const void *v,
+                       const void *log_f, const float *h0, const float *states_in, const void *dy, const float *dht,
+                       void *dq, void *dk, void *dv, void *dlog_f, float *dh0, void *ws, size_t ws_bytes,
+                       void *stream) {
+  const char *fn = "hgrn1_bwd";
+  hgrn2_status st = h1_check(B, T, C, dtype, tied);
+  if (st != HGRN2_OK) return st;
+  st = check_ptrs({{"q", q}, {"v", v}, {"log_f", log_f}, {"dy", dy}, {"dq", dq}, {"dv", dv}, {"dlog_f", dlog_f}},
+                  {{"h0", h0}, {"states_in", states_in}, {"dht", dht}, {"dh0", dh0}, {"ws", ws}});
+  const int gm = tied ? kTied : kUntied;
+  if (st == HGRN2_OK) st = need_k(gm, k, "k");
+  if (st == HGRN2_OK) st = need_k(gm, dk, "dk");
+  if (st != HGRN2_OK) return st;
+  const size_t tok = (size_t)B * T * C * dsize(dtype), sb = hgrn1_states_bytes(B, T, C),
+               hb = (size_t)B * C * sizeof(float);
+  const size_t need = hgrn1_bwd_workspace_bytes(B, T, C, states_in != nullptr);
+  if (!ws || ws_bytes < need) return fail(HGRN2_ERR_WORKSPACE, "workspace smaller than hgrn1_bwd_workspace_bytes()");
+  if (tied) k = dk = nullptr;
+  const Range ins[] = {{"q", q, tok},   {"k", k, tok},   {"v", v, tok},   {"log_f", log_f, tok},
+                       {"h0", h0, hb},  {"dy", dy, tok}, {"dht", dht, hb}, {"states_in", states_in, sb}};
+  const Range outs[] = {{"dq", dq, tok}, {"dk", dk, tok}, {"dv", dv, tok}, {"dlog_f", dlog_f, tok},
+                        {"dh0", dh0, hb}, {"ws", ws, need}};
+  std::string msg;
+  if (!check_aliasing(ins, 8, outs, 6, msg)) return fail(HGRN2_ERR_INVALID_ARG, msg);
+  hgrn2::H1Args a = h1_args(B, T, C);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.log_f = log_f;
+  a.dy = dy;
+  a.A = (float *)ws;
+  a.Bs = (float *)((char *)ws + sb);
+  float *rcarry = (float *)((char *)ws + 2 * sb);
+  const float *fcarry = states_in;
+  if (!fcarry) {
+    // recompute the forward carries (the states entering every segment)
+    float *fc = (float *)((char *)ws + 3 * sb);
+    a.s_in = h0;
+    a.carry = fc;
+    a.s_out = nullptr;
+    if ((st = h1_launch(hgrn2::kH1SummaryFwd, dtype, gm, a, stream, fn)) != HGRN2_OK) return st;
+    if ((st = h1_launch(hgrn2::kH1CarryFwd, dtype, gm, a, stream, fn)) != HGRN2_OK) return st;
+    fcarry = fc;
+  }
+  // reverse: the gradient entering every segment from the right, then the gradients
+  a.s_in = dht;
+  a.carry = rcarry;
+  a.s_out = dh0;
+  a.fcarry = fcarry;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dlog_f = dlog_f;
+  if ((st = h1_launch(hgrn2::kH1SummaryRev, dtype, gm, a, stream, fn)) != HGRN2_OK) return st;
+  if ((st = h1_launch(hgrn2::kH1CarryRev, dtype, gm, a, stream, fn)) != HGRN2_OK) return st;
+  return h1_launch(hgrn2::kH1FinalBwd, dtype, gm, a, stream, fn);
+}
+
 }  // extern "C"

@@ -6,6 +6,7 @@
 #include "cbwd.h"
 #include "cfwd.h"
 #include "decode.h"
+#include "hgrn1.h"
 #include "scan.h"
 
 namespace hgrn2 {
@@ -51,5 +52,8 @@ hipError_t dispatch_chunk_bwd(int dtype, int D, int C, int gm, const ChunkBwdArg
 hipError_t dispatch_decode(int dtype, int D, int gm, const DecodeArgs &a, hipStream_t s);
 // dlb[h][c] = sum over b and chunks n of part[(b H + h) N + n][c], in a fixed order
 hipError_t dispatch_dlb_reduce(int B, int H, int N, int D, const float *part, float *dlb, hipStream_t s);
+// one pass of the HGRN1 elementwise scan (gm: kUntied or kTied)
+enum H1Op : int { kH1SummaryFwd, kH1SummaryRev, kH1CarryFwd, kH1CarryRev, kH1FinalFwd, kH1FinalBwd };
+hipError_t dispatch_hgrn1(int op, int dtype, int gm, const H1Args &a, hipStream_t s);
 
 }  // namespace hgrn2

@@ -20,7 +20,7 @@ def lib():
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(hgrn2_[a-z0-9_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(hgrn[12]_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_declares_the_entry_points():
@@ -28,7 +28,8 @@ def test_header_declares_the_entry_points():
     for n in ("hgrn2_fwd", "hgrn2_bwd", "hgrn2_decode_step", "hgrn2_fwd_chunk", "hgrn2_bwd_adjoint",
               "hgrn2_bwd_chunk", "hgrn2_fwd_tied", "hgrn2_bwd_tied", "hgrn2_fwd_chunk_tied",
               "hgrn2_bwd_chunk_tied", "hgrn2_decode_step_tied", "hgrn2_fwd_gate", "hgrn2_bwd_gate",
-              "hgrn2_decode_step_gate", "hgrn2_bwd_gate_workspace_bytes"):
+              "hgrn2_decode_step_gate", "hgrn2_bwd_gate_workspace_bytes", "hgrn1_fwd", "hgrn1_bwd",
+              "hgrn1_states_bytes", "hgrn1_fwd_workspace_bytes", "hgrn1_bwd_workspace_bytes"):
         assert n in names
 
 
@@ -38,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.hgrn2_abi_version() == 5
+    assert lib.hgrn2_abi_version() == 6
     for s in range(5):
         assert lib.hgrn2_status_string(s).startswith(b"HGRN2_")
 
@@ -184,6 +185,27 @@ def test_gate_rejections(lib):
     # decode: lower_bound NULL, unsupported D
     assert lib.hgrn2_decode_step_gate(1, 1, 16, 16, 0, P[0], P[1], P[2], None, P[4], P[5], None) == 1
     assert lib.hgrn2_decode_step_gate(1, 1, 24, 24, 0, P[0], P[1], P[2], P[3], P[4], P[5], None) == 2
+
+
+def test_hgrn1_rejections(lib):
+    P = [FAKE + i * 0x100000 for i in range(16)]
+    S = lib.hgrn1_states_bytes(2, 70, 6)
+    assert S == 2 * 3 * 6 * 4
+    assert lib.hgrn1_fwd_workspace_bytes(2, 70, 6, 1) == 2 * S
+    assert lib.hgrn1_fwd_workspace_bytes(2, 70, 6, 0) == 3 * S
+    assert lib.hgrn1_bwd_workspace_bytes(2, 70, 6, 0) == 4 * S
+    ws = 4 * S
+    # hgrn1_fwd: odd C; tied must be 0/1; k NULL untied; y aliases v; small workspace
+    assert lib.hgrn1_fwd(2, 70, 5, 0, 0, P[0], P[1], P[2], P[3], None, P[4], None, None, P[9], ws, None) == 2
+    assert lib.hgrn1_fwd(2, 70, 6, 0, 2, P[0], P[1], P[2], P[3], None, P[4], None, None, P[9], ws, None) == 1
+    assert lib.hgrn1_fwd(2, 70, 6, 0, 0, P[0], None, P[2], P[3], None, P[4], None, None, P[9], ws, None) == 1
+    assert lib.hgrn1_fwd(2, 70, 6, 0, 1, P[0], None, P[2], P[3], None, P[2], None, None, P[9], ws, None) == 1
+    assert lib.hgrn1_fwd(2, 70, 6, 0, 1, P[0], None, P[2], P[3], None, P[4], None, None, P[9], S, None) == 3
+    # hgrn1_bwd: dk NULL untied; dlog_f aliases dy
+    assert lib.hgrn1_bwd(2, 70, 6, 0, 0, P[0], P[1], P[2], P[3], None, None, P[4], None, P[5], None, P[6],
+                         P[7], None, P[9], ws, None) == 1
+    assert lib.hgrn1_bwd(2, 70, 6, 0, 1, P[0], None, P[2], P[3], None, None, P[4], None, P[5], None, P[6],
+                         P[4], None, P[9], ws, None) == 1
 
 
 def test_decode_rejections(lib):
