@@ -172,6 +172,14 @@ def kernel_label(name: str):
         return "decode" + sfx
     if n.startswith("hgrn2_dlb_reduce_kernel"):
         return "dlb"
+    if n.startswith("hgrn1_"):
+        rev = len(a) > 2 and a[2] == "true"
+        for key, lab in (("summary", "h1_summary_rev" if rev else "h1_summary"), ("final_fwd", "h1_final_fwd"),
+                         ("final_bwd", "h1_final_bwd")):
+            if n.startswith("hgrn1_" + key):
+                return lab
+        if n.startswith("hgrn1_carry"):
+            return "h1_carry_rev" if a and a[0] == "true" else "h1_carry"
     return None
 
 
@@ -200,6 +208,73 @@ def train_algorithmic_bytes(w):
         "cbwd_gate": 4 * tok + 2 * N * ent + 3 * tok + w.B * w.H * N * w.D * 4,
         "dlb": w.B * w.H * N * w.D * 4 + w.H * w.D * 4,
     }
+
+
+def hgrn1_algorithmic_bytes(B, T, C):
+    """Bytes per launch of the HGRN1 kernels, tied, bf16: tok = one [B,T,C] tensor,
+    seg = one float per (b, segment, channel)."""
+    tok = B * T * C * 2
+    seg = B * ((T + 31) // 32) * C * 4
+    return {
+        "h1_summary": 2 * tok + 2 * seg,          # v, log_f in; A, Bs out
+        "h1_carry": 2 * seg + seg + B * C * 4,    # A, Bs in; carries, hT out
+        "h1_final_fwd": 3 * tok + seg + tok,      # q, v, log_f, carries in; y out
+        "h1_summary_rev": 3 * tok + 2 * seg,      # q, dy, log_f in; A, Bs out
+        "h1_carry_rev": 2 * seg + seg + B * C * 4,
+        "h1_final_bwd": 4 * tok + 2 * seg + 3 * tok,  # q, v, log_f, dy, both carries in; dq, dv, dlog_f out
+    }
+
+
+def bench_hgrn1(torch, m, args, sets):
+    """The HGRN1 elementwise recurrence on the training workload's tensors read
+    as [B, T, C] (C = H d channels), tied, bf16: hgrn1_fwd (saving the segment
+    states) then hgrn1_bwd; each call event-timed."""
+    import synth
+    w = synth.WORKLOADS["train_bf16"]
+    B, T, C = w.B, w.T, w.H * w.D
+    dev = sets[0]["q"].device
+    st = torch.empty((B, (T + 31) // 32, C), dtype=torch.float32, device=dev)
+    y = torch.empty((B, T, C), dtype=torch.bfloat16, device=dev)
+    g = [torch.empty((B, T, C), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    wsf = torch.empty(int(m.lib().hgrn1_fwd_workspace_bytes(B, T, C, 1)), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(int(m.lib().hgrn1_bwd_workspace_bytes(B, T, C, 1)), dtype=torch.uint8, device=dev)
+    views = [{n: s[n].view(B, T, C) for n in ("q", "v", "log_f", "dy")} for s in sets]
+    calls = lambda s: (
+        lambda: m.hgrn1_fwd(s["q"], None, s["v"], s["log_f"], None, tied=True, want_ht=False, y=y, states=st,
+                            ws=wsf),
+        lambda: m.hgrn1_bwd(s["q"], None, s["v"], s["log_f"], s["dy"], None, None, st, tied=True, want_dh0=False,
+                            dq=g[0], dv=g[1], dlog_f=g[2], ws=wsb))
+    labels = ("hgrn1_fwd", "hgrn1_bwd")
+
+    def step(i, timer=None):
+        for label, call in zip(labels, calls(views[i % len(views)])):
+            t = timer.start(label) if timer else None
+            call()
+            if timer:
+                timer.stop(t)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    timer = KernelTimer(torch)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(args.steps):
+        step(i, timer)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    kms = {label: timer.mean_ms(label) for label in labels}
+    log("timed (hgrn1): %.3f ms/step (%s)" % (ms, ", ".join("%s %.3f ms" % kv for kv in kms.items())))
+    alg = hgrn1_algorithmic_bytes(B, T, C)
+    tok = B * T * C * 2
+    return {"workload": "hgrn1_bf16: B8 T4096 C2048 (the training tensors read as [B, T, C]), tied, "
+                        "fwd(states)+bwd", "value": B * T / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+            "calls_ms": kms, "algorithmic_bytes_step": sum(alg.values()),
+            "compulsory_bytes_step": 11 * tok,
+            "GBps_step": sum(alg.values()) / (ms * 1e-3) / 1e9}
 
 
 def bench_train(torch, m, args, sets, mode="untied"):
@@ -355,7 +430,9 @@ def summarize(trace_dir, fetch_dir, write_dir, mfma_dir=None):
            "command: " + TRACE_CMD, "source_digest: " + digest, "",
            "%-52s %6s %12s %10s %10s %10s %6s" % ("kernel", "calls", "total_us", "avg_us",
                                                     "min_us", "max_us", "pct")]
-    alg = train_algorithmic_bytes(__import__("synth").WORKLOADS["train_bf16"])
+    _w = __import__("synth").WORKLOADS["train_bf16"]
+    alg = train_algorithmic_bytes(_w)
+    alg.update(hgrn1_algorithmic_bytes(_w.B, _w.T, _w.H * _w.D))
     rates = []
     for r in rows:
         out.append("%-52s %6d %12.1f %10.1f %10.1f %10.1f %6.2f" % (
@@ -484,6 +561,7 @@ def main():
         res = bench_train(torch, m, args, sets)
         tres = bench_train(torch, m, args, sets, mode="tied")
         gres = bench_train(torch, m, args, sets, mode="gate")
+        h1res = bench_hgrn1(torch, m, args, sets)
         w = res["w"]
         tokens = w.B * w.T
         out["value"] = tokens / (res["ms"] * 1e-3)
@@ -519,6 +597,7 @@ def main():
                                    "[H, D] (f = lb + (1 - lb) sigmoid(z), k = 1 - f): fwd(states)+bwd, dz and dlb",
                        "value": tokens / (gres["ms"] * 1e-3), "unit": "tokens/s", "ms_per_step": gres["ms"],
                        "calls_ms": {label: gk[label] for label, _ in GATE_CALLS}}
+        out["hgrn1"] = h1res
     if args.only in ("decode", "all"):
         dres = bench_decode(torch, m, args)
         out["decode"] = {"workload": "decode_f32: B256 H16 d128, float32 state", "ms": dres["ms"],

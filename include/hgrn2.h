@@ -273,15 +273,16 @@ hgrn2_status hgrn2_decode_step_gate(int B, int H, int DK, int DV, int dtype, con
  * 16-byte aligned; h0, hT, dht, dh0 float32 [B, C] (optional, NULL = zero /
  * not written).
  *
- * The sequence is scanned in segments of 32 tokens.  states_out (optional)
- * receives the state entering every segment, float32 [B, S, C] with
- * S = ceil(T / 32) (hgrn1_states_bytes()); hgrn1_bwd takes it as states_in or,
- * with NULL, recomputes it in the workspace.  Workspaces: hgrn1_fwd_workspace_bytes(),
- * hgrn1_bwd_workspace_bytes() (have_states = whether states_out / states_in is
- * passed).  Each call enqueues three kernels (segment summaries, a serial pass
- * over segments per channel, the segments again), five for a backward that
- * recomputes the states.  Errors as for the other calls; C odd is
- * HGRN2_ERR_UNSUPPORTED.
+ * The sequence is scanned in segments of 32 tokens, eight segments to a
+ * group.  states_out (optional) receives the state entering every segment,
+ * float32 [B, S, C] with S = ceil(T / 32) (hgrn1_states_bytes()); hgrn1_bwd
+ * takes it as states_in or, with NULL, recomputes what it needs in the
+ * workspace.  Workspaces: hgrn1_fwd_workspace_bytes(), hgrn1_bwd_workspace_bytes()
+ * (have_states = whether states_in is passed to the backward; the forward's
+ * size does not depend on it).  Each call enqueues three kernels (summaries of
+ * every group of segments, a serial pass over the groups per channel, the
+ * segments again), five for a backward that recomputes the states.  Errors as
+ * for the other calls; C odd is HGRN2_ERR_UNSUPPORTED.
  */
 size_t hgrn1_states_bytes(int B, int T, int C);
 size_t hgrn1_fwd_workspace_bytes(int B, int T, int C, int have_states);

@@ -570,14 +570,35 @@ size_t hgrn1_states_bytes(int B, int T, int C) {
   return (size_t)B * hgrn2::h1_segments(T) * C * sizeof(float);
 }
 
+// one direction's summaries: segment prefixes (2 [B,S,C]) and group totals
+// and carries (3 [B,NG,C]), float32
+static size_t h1_sum_bytes(int B, int T, int C) {
+  const int S = hgrn2::h1_segments(T), NG = hgrn2::h1_groups(S);
+  return ((size_t)2 * S + (size_t)3 * NG) * B * C * sizeof(float);
+}
+
 size_t hgrn1_fwd_workspace_bytes(int B, int T, int C, int have_states) {
-  const size_t sb = hgrn1_states_bytes(B, T, C);
-  return 2 * sb + (have_states ? 0 : sb);
+  (void)have_states;
+  if (B <= 0 || T <= 0 || C <= 0) return 0;
+  return h1_sum_bytes(B, T, C);
 }
 
 size_t hgrn1_bwd_workspace_bytes(int B, int T, int C, int have_states) {
-  const size_t sb = hgrn1_states_bytes(B, T, C);
-  return 3 * sb + (have_states ? 0 : sb);
+  if (B <= 0 || T <= 0 || C <= 0) return 0;
+  return h1_sum_bytes(B, T, C) * (have_states ? 1 : 2);
+}
+
+static hgrn2::H1Sum h1_sum_at(void *base, int B, int T, int C) {
+  const int S = hgrn2::h1_segments(T), NG = hgrn2::h1_groups(S);
+  const size_t sb = (size_t)B * S * C, gb = (size_t)B * NG * C;
+  float *f = (float *)base;
+  hgrn2::H1Sum u;
+  u.PA = f;
+  u.PB = f + sb;
+  u.GA = f + 2 * sb;
+  u.GB = f + 2 * sb + gb;
+  u.gc = f + 2 * sb + 2 * gb;
+  return u;
 }
 
 static hgrn2::H1Args h1_args(int B, int T, int C) {
@@ -586,6 +607,7 @@ static hgrn2::H1Args h1_args(int B, int T, int C) {
   a.T = T;
   a.C = C;
   a.S = hgrn2::h1_segments(T);
+  a.NG = hgrn2::h1_groups(a.S);
   return a;
 }
 
@@ -618,10 +640,9 @@ hgrn2_status hgrn1_fwd(int B, int T, int C, int dtype, int tied, const void *q, 
   a.v = v;
   a.log_f = log_f;
   a.s_in = h0;
-  a.A = (float *)ws;
-  a.Bs = (float *)((char *)ws + sb);
-  a.carry = states_out ? states_out : (float *)((char *)ws + 2 * sb);
   a.s_out = hT;
+  a.sum = h1_sum_at(ws, B, T, C);
+  a.states = states_out;
   a.y = y;
   const int gm = tied ? kTied : kUntied;
   if ((st = h1_launch(hgrn2::kH1SummaryFwd, dtype, gm, a, stream, fn)) != HGRN2_OK) return st;
@@ -659,25 +680,21 @@ hgrn2_status hgrn1_bwd(int B, int T, int C, int dtype, int tied, const void *q, 
   a.v = v;
   a.log_f = log_f;
   a.dy = dy;
-  a.A = (float *)ws;
-  a.Bs = (float *)((char *)ws + sb);
-  float *rcarry = (float *)((char *)ws + 2 * sb);
-  const float *fcarry = states_in;
-  if (!fcarry) {
-    // recompute the forward carries (the states entering every segment)
-    float *fc = (float *)((char *)ws + 3 * sb);
+  a.states = const_cast<float *>(states_in);  // read only by the final backward
+  if (!states_in) {
+    // the forward summaries and group carries; the final backward combines them
+    // into the state entering each segment
+    a.sum = h1_sum_at((char *)ws + h1_sum_bytes(B, T, C), B, T, C);
     a.s_in = h0;
-    a.carry = fc;
     a.s_out = nullptr;
     if ((st = h1_launch(hgrn2::kH1SummaryFwd, dtype, gm, a, stream, fn)) != HGRN2_OK) return st;
     if ((st = h1_launch(hgrn2::kH1CarryFwd, dtype, gm, a, stream, fn)) != HGRN2_OK) return st;
-    fcarry = fc;
+    a.fsum = a.sum;
   }
   // reverse: the gradient entering every segment from the right, then the gradients
+  a.sum = h1_sum_at(ws, B, T, C);
   a.s_in = dht;
-  a.carry = rcarry;
   a.s_out = dh0;
-  a.fcarry = fcarry;
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;

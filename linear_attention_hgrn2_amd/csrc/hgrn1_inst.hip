@@ -7,10 +7,10 @@ namespace hgrn2 {
 template <typename T, int GM> static hipError_t h1_run(int op, const H1Args &a, hipStream_t s) {
   switch (op) {
     case kH1SummaryFwd:
-      hipLaunchKernelGGL((hgrn1_summary_kernel<T, GM, false>), h1_seg_grid(a), dim3(kH1Pairs), 0, s, a);
+      hipLaunchKernelGGL((hgrn1_summary_kernel<T, GM, false>), h1_sum_grid(a), dim3(64 * kH1Grp), 0, s, a);
       break;
     case kH1SummaryRev:
-      hipLaunchKernelGGL((hgrn1_summary_kernel<T, kUntied, true>), h1_seg_grid(a), dim3(kH1Pairs), 0, s, a);
+      hipLaunchKernelGGL((hgrn1_summary_kernel<T, kUntied, true>), h1_sum_grid(a), dim3(64 * kH1Grp), 0, s, a);
       break;
     case kH1CarryFwd:
       hipLaunchKernelGGL((hgrn1_carry_kernel<false>), h1_chan_grid(a), dim3(256), 0, s, a);

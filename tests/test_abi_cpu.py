@@ -190,17 +190,21 @@ def test_gate_rejections(lib):
 def test_hgrn1_rejections(lib):
     P = [FAKE + i * 0x100000 for i in range(16)]
     S = lib.hgrn1_states_bytes(2, 70, 6)
-    assert S == 2 * 3 * 6 * 4
-    assert lib.hgrn1_fwd_workspace_bytes(2, 70, 6, 1) == 2 * S
-    assert lib.hgrn1_fwd_workspace_bytes(2, 70, 6, 0) == 3 * S
-    assert lib.hgrn1_bwd_workspace_bytes(2, 70, 6, 0) == 4 * S
-    ws = 4 * S
+    assert S == 2 * 3 * 6 * 4                      # 3 segments of 32 tokens
+    G = 2 * 1 * 6 * 4                              # one group of segments
+    assert lib.hgrn1_fwd_workspace_bytes(2, 70, 6, 1) == 2 * S + 3 * G
+    assert lib.hgrn1_fwd_workspace_bytes(2, 70, 6, 0) == 2 * S + 3 * G
+    assert lib.hgrn1_bwd_workspace_bytes(2, 70, 6, 1) == 2 * S + 3 * G
+    assert lib.hgrn1_bwd_workspace_bytes(2, 70, 6, 0) == 2 * (2 * S + 3 * G)
+    ws = 4 * S + 6 * G
     # hgrn1_fwd: odd C; tied must be 0/1; k NULL untied; y aliases v; small workspace
     assert lib.hgrn1_fwd(2, 70, 5, 0, 0, P[0], P[1], P[2], P[3], None, P[4], None, None, P[9], ws, None) == 2
     assert lib.hgrn1_fwd(2, 70, 6, 0, 2, P[0], P[1], P[2], P[3], None, P[4], None, None, P[9], ws, None) == 1
     assert lib.hgrn1_fwd(2, 70, 6, 0, 0, P[0], None, P[2], P[3], None, P[4], None, None, P[9], ws, None) == 1
     assert lib.hgrn1_fwd(2, 70, 6, 0, 1, P[0], None, P[2], P[3], None, P[2], None, None, P[9], ws, None) == 1
     assert lib.hgrn1_fwd(2, 70, 6, 0, 1, P[0], None, P[2], P[3], None, P[4], None, None, P[9], S, None) == 3
+    assert lib.hgrn1_bwd(2, 70, 6, 0, 1, P[0], None, P[2], P[3], None, None, P[4], None, P[5], None, P[6],
+                         P[7], None, P[9], 2 * S + 3 * G, None) == 3
     # hgrn1_bwd: dk NULL untied; dlog_f aliases dy
     assert lib.hgrn1_bwd(2, 70, 6, 0, 0, P[0], P[1], P[2], P[3], None, None, P[4], None, P[5], None, P[6],
                          P[7], None, P[9], ws, None) == 1
