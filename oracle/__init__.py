@@ -26,8 +26,8 @@ _lib = None
 
 __all__ = ["build", "forward", "backward", "decode_step", "forward_tied", "backward_tied",
            "decode_step_tied", "tied_k", "gate_log_f", "gate_k", "gate_partials", "forward_gate",
-           "backward_gate", "decode_step_gate", "hgrn1_forward", "hgrn1_backward", "threads", "Oracle",
-           "default"]
+           "backward_gate", "decode_step_gate", "hgrn1_forward", "hgrn1_backward", "forward_scalar",
+           "backward_scalar", "decode_step_scalar", "threads", "Oracle", "default"]
 
 
 def build(force: bool = True) -> str:
@@ -283,3 +283,33 @@ def hgrn1_backward(q, k, v, log_f, dy, h0=None, dht=None, tied=False):
     if tied:
         return dq, None, dv, dl - np.exp(lf) * dk, dh0
     return dq, dk, dv, dl, dh0
+
+
+# ------------------------------------------------------------------ scalar decay per head
+# The per-head scalar decay that other models use in place of HGRN2's
+# per-channel gate (HGRN2 summary, paperlayer.ai, §5: Mamba2, xLSTM and Gated
+# Retention share one decay per head; HGRN2 keeps one per dimension): one
+# log a_t per (b, t, h), the same for every row of that head's state.  The
+# recurrence is HGRN2's with log_f[..., c] = log a for every channel c, and the
+# gradient of log a sums the per-channel one over the channels.
+
+
+def _bcast(log_a, D):
+    la = np.asarray(log_a, dtype=np.float64)
+    return np.repeat(la[..., None], D, axis=-1)
+
+
+def forward_scalar(q, k, v, log_a, h0=None):
+    """forward() with one log decay per (b, t, h), log_a [B,T,H]."""
+    return forward(q, k, v, _bcast(log_a, np.shape(q)[-1]), h0)
+
+
+def backward_scalar(q, k, v, log_a, dy, h0=None, dht=None):
+    """(dq, dk, dv, dlog_a [B,T,H], dh0)."""
+    dq, dk, dv, dl, dh0 = backward(q, k, v, _bcast(log_a, np.shape(q)[-1]), dy, h0, dht)
+    return dq, dk, dv, dl.sum(axis=-1), dh0
+
+
+def decode_step_scalar(q, k, v, log_a, state):
+    """decode_step() with log_a [B,H]."""
+    return decode_step(q, k, v, _bcast(log_a, np.shape(q)[-1]), state)

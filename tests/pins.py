@@ -502,10 +502,61 @@ def pin_hgrn1_finite_differences(orc):
             assert rel(g, num) < 1e-7, (tied, ai, rel(g, num))
 
 
+# ---------------------------------------------------------------- scalar decay per head
+
+def pin_scalar_decay_autograd(orc):
+    """Scalar-decay gradients against torch float64 autograd through a plain
+    loop that scales the whole state by one a_t per head."""
+    import torch
+    import oracle as o
+    q, k, v, _, h0 = rand_inputs(41, B=2, T=10, H=2, DK=4, DV=3)
+    r = _rng(42)
+    la = r.uniform(-1.5, 0.0, q.shape[:3])
+    dy = r.standard_normal(v.shape)
+    dht = r.standard_normal(h0.shape)
+    ts = [torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v, la, h0)]
+    tq, tk, tv, tla, th = ts
+    S = th
+    ys = []
+    for t in range(q.shape[1]):
+        S = torch.exp(tla[:, t])[..., None, None] * S + tk[:, t][..., :, None] * tv[:, t][..., None, :]
+        ys.append(torch.einsum("bhc,bhcj->bhj", tq[:, t], S))
+    Y = torch.stack(ys, dim=1)
+    L = (Y * torch.tensor(dy)).sum() + (S * torch.tensor(dht)).sum()
+    L.backward()
+    got = o.backward_scalar(q, k, v, la, dy, h0, dht)
+    for g, t in zip(got, ts):
+        assert rel(g, t.grad.numpy()) < 1e-12
+    y, ht = o.forward_scalar(q, k, v, la, h0)
+    assert rel(y, Y.detach().numpy()) < 1e-13 and rel(ht, S.detach().numpy()) < 1e-13
+
+
+def pin_scalar_decay_finite_differences(orc):
+    """Central differences of the loss in log_a against backward_scalar's dlog_a."""
+    import oracle as o
+    q, k, v, _, h0 = rand_inputs(43, B=1, T=7, H=2, DK=3, DV=2)
+    r = _rng(44)
+    la = r.uniform(-1.5, 0.0, q.shape[:3])
+    dy = r.standard_normal(v.shape)
+    dht = r.standard_normal(h0.shape)
+    g = o.backward_scalar(q, k, v, la, dy, h0, dht)[3]
+    num = np.zeros_like(la)
+    for idx in np.ndindex(la.shape):
+        old = la[idx]
+        la[idx] = old + 1e-6
+        yp, hp = orc.forward(q, k, v, np.repeat(la[..., None], 3, axis=-1), h0)
+        la[idx] = old - 1e-6
+        ym, hm = orc.forward(q, k, v, np.repeat(la[..., None], 3, axis=-1), h0)
+        la[idx] = old
+        num[idx] = (((yp - ym) * dy).sum() + ((hp - hm) * dht).sum()) / 2e-6
+    assert rel(g, num) < 1e-7
+
+
 ALL_PINS = [pin_closed_form, pin_limit_f_one, pin_limit_f_zero, pin_scalar_scan,
             pin_golden_exact, pin_linearity, pin_state_carry, pin_decode,
             pin_finite_differences, pin_autograd, pin_dlogf_identity, pin_bwd_limits,
             pin_tied_finite_differences, pin_tied_autograd,
             pin_gate_log_sigmoid, pin_gate_finite_differences, pin_gate_autograd,
-            pin_hgrn1_geometric, pin_hgrn1_finite_differences]
+            pin_hgrn1_geometric, pin_hgrn1_finite_differences,
+            pin_scalar_decay_autograd, pin_scalar_decay_finite_differences]
 GATE_PINS = [pin_gate_log_sigmoid, pin_gate_finite_differences, pin_gate_autograd]
