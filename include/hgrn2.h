@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define HGRN2_ABI_VERSION 6
+#define HGRN2_ABI_VERSION 7
 
 typedef enum {
   HGRN2_OK = 0,
@@ -260,6 +260,31 @@ hgrn2_status hgrn2_bwd_gate(int B, int T, int H, int DK, int DV, int chunk, int 
 hgrn2_status hgrn2_decode_step_gate(int B, int H, int DK, int DV, int dtype, const void *q,
                                     const void *v, const void *z, const float *lower_bound,
                                     float *state, void *y, void *stream);
+
+/*
+ * One decay per head.  Other models share one forget-gate value across a
+ * head's state (HGRN2 summary §5: Mamba2, xLSTM and Gated Retention share one
+ * decay per head for tensor-core efficiency, where HGRN2 keeps one per
+ * dimension).  These entry points take log_a [B, T, H] (input dtype; decode:
+ * [B, H]) in place of log_f, the same for every row of head h's state:
+ *     S_t = a_t S_{t-1} + k_t^T v_t,        y_t = q_t S_t,
+ * with k an input.  The backward returns dlog_a [B, T, H] (input dtype), the
+ * sum over the head's channels of the per-channel derivative, and dk.  The
+ * log-decay bytes shrink by D.  Everything else (layouts, states, workspaces,
+ * errors, gate preconditions on log_a) is as for the untied calls.
+ */
+hgrn2_status hgrn2_fwd_scalar(int B, int T, int H, int DK, int DV, int chunk, int dtype,
+                              const void *q, const void *k, const void *v, const void *log_a,
+                              const float *h0, void *y, float *ht, void *states_out, void *ws,
+                              size_t ws_bytes, void *stream);
+hgrn2_status hgrn2_bwd_scalar(int B, int T, int H, int DK, int DV, int chunk, int dtype,
+                              const void *q, const void *k, const void *v, const void *log_a,
+                              const float *h0, const void *states_in, const void *dy,
+                              const float *dht, void *dq, void *dk, void *dv, void *dlog_a,
+                              float *dh0, void *ws, size_t ws_bytes, void *stream);
+hgrn2_status hgrn2_decode_step_scalar(int B, int H, int DK, int DV, int dtype, const void *q,
+                                      const void *k, const void *v, const void *log_a, float *state,
+                                      void *y, void *stream);
 
 /*
  * HGRN1: the elementwise gated linear recurrence that HGRN2 expands (HGRN2

@@ -11,15 +11,16 @@ kernels in ``csrc/``); this package is its thin Python binding:
   fwd_gate / bwd_gate / decode_step_gate        gate from its pre-activation z and a lower bound:
                                                 f = lb + (1 - lb) sigmoid(z), k = 1 - f
   decode_step(q, k, v, log_f, state)            one recurrent step, in place
+  fwd_scalar / bwd_scalar / decode_step_scalar  one decay per head, log_a [B, T, H]
   hgrn1_fwd / hgrn1_bwd                         the HGRN1 elementwise recurrence over [B, T, C]
   hgrn2_chunk(q, k, v, log_f, h0, chunk)        autograd wrapper
 """
 from ._binding import (BF16, F32, HGRN2Chunk, HGRN2Error, LIB_PATH, adjoints_shape, bwd, bwd_adjoint,
-                       bwd_chunk, bwd_chunk_tied, bwd_gate, bwd_tied, decode_step, decode_step_gate,
-                       decode_step_tied, fwd, fwd_chunk, fwd_chunk_tied, fwd_gate, fwd_tied, hgrn1_bwd, hgrn1_fwd,
+                       bwd_chunk, bwd_chunk_tied, bwd_gate, bwd_scalar, bwd_tied, decode_step, decode_step_gate,
+                       decode_step_scalar, decode_step_tied, fwd_scalar, fwd, fwd_chunk, fwd_chunk_tied, fwd_gate, fwd_tied, hgrn1_bwd, hgrn1_fwd,
                        hgrn1_states_shape, hgrn2_chunk, lib, num_chunks, states_shape, supported)
 
 __all__ = ["fwd", "bwd", "fwd_chunk", "bwd_adjoint", "bwd_chunk", "adjoints_shape", "decode_step",
            "fwd_tied", "bwd_tied", "fwd_chunk_tied", "bwd_chunk_tied", "decode_step_tied",
-           "fwd_gate", "bwd_gate", "decode_step_gate", "hgrn1_fwd", "hgrn1_bwd", "hgrn1_states_shape", "hgrn2_chunk", "HGRN2Chunk", "HGRN2Error", "supported",
+           "fwd_gate", "bwd_gate", "decode_step_gate", "fwd_scalar", "bwd_scalar", "decode_step_scalar", "hgrn1_fwd", "hgrn1_bwd", "hgrn1_states_shape", "hgrn2_chunk", "HGRN2Chunk", "HGRN2Error", "supported",
            "num_chunks", "states_shape", "lib", "LIB_PATH", "F32", "BF16"]

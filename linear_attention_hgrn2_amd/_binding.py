@@ -90,6 +90,12 @@ def _lib():
         for n in ("hgrn1_fwd_workspace_bytes", "hgrn1_bwd_workspace_bytes"):
             getattr(lib, n).argtypes = [I, I, I, I]
             getattr(lib, n).restype = Z
+        lib.hgrn2_fwd_scalar.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, Z, P]
+        lib.hgrn2_fwd_scalar.restype = I
+        lib.hgrn2_bwd_scalar.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
+        lib.hgrn2_bwd_scalar.restype = I
+        lib.hgrn2_decode_step_scalar.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P]
+        lib.hgrn2_decode_step_scalar.restype = I
         lib.hgrn1_fwd.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, P, Z, P]
         lib.hgrn1_fwd.restype = I
         lib.hgrn1_bwd.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
@@ -513,6 +519,92 @@ def decode_step_gate(q, v, z, lower_bound, state, *, y=None):
     st = _lib().hgrn2_decode_step_gate(B, H, D, D, _DT[dt], _ptr(q), _ptr(v), _ptr(z), _ptr(lower_bound),
                                        _ptr(state), _ptr(y), _stream())
     _check(st, "hgrn2_decode_step_gate")
+    return y
+
+
+def fwd_scalar(q, k, v, log_a, h0=None, *, chunk=64, want_ht=True, want_states=False, want_y=True,
+               y=None, ht=None, states=None, ws=None):
+    """Chunked forward with one decay per head, log_a [B, T, H].
+    Returns (y or None, ht or None, states or None)."""
+    B, T, H, D = q.shape
+    dt = q.dtype
+    if dt not in _DT:
+        raise ValueError("dtype must be float32 or bfloat16")
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _tok(n, t, B, T, H, D, dt)
+    _tok3("log_a", log_a, B, T, H, dt)
+    _st("h0", h0, B, H, D)
+    if want_y and y is None:
+        y = torch.empty_like(q)
+    if y is not None:
+        _tok("y", y, B, T, H, D, dt)
+    if want_ht and ht is None:
+        ht = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+    _st("ht", ht, B, H, D)
+    if want_states and states is None:
+        states = torch.empty(states_shape(B, T, H, D, chunk), dtype=dt, device=q.device)
+    if states is not None:
+        _states_ok(states, B, T, H, D, chunk, dt)
+    ws_bytes = 0
+    if states is None:
+        need = int(_lib().hgrn2_fwd_workspace_bytes(B, T, H, D, D, chunk, _DT[dt], 0))
+        if ws is None:
+            ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_bytes = ws.numel() * ws.element_size()
+    st = _lib().hgrn2_fwd_scalar(B, T, H, D, D, chunk, _DT[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(h0),
+                                 _ptr(y), _ptr(ht), _ptr(states), _ptr(ws), ws_bytes, _stream())
+    _check(st, "hgrn2_fwd_scalar")
+    return y, ht, states
+
+
+def bwd_scalar(q, k, v, log_a, dy, h0=None, dht=None, states=None, *, chunk=64, want_dh0=True,
+               dq=None, dk=None, dv=None, dlog_a=None, dh0=None, ws=None):
+    """Chunked backward with one decay per head.  Returns (dq, dk, dv, dlog_a [B, T, H], dh0 or None)."""
+    B, T, H, D = q.shape
+    dt = q.dtype
+    for n, t in (("q", q), ("k", k), ("v", v), ("dy", dy)):
+        _tok(n, t, B, T, H, D, dt)
+    _tok3("log_a", log_a, B, T, H, dt)
+    _st("h0", h0, B, H, D)
+    _st("dht", dht, B, H, D)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    dlog_a = torch.empty_like(log_a) if dlog_a is None else dlog_a
+    for n, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _tok(n, t, B, T, H, D, dt)
+    _tok3("dlog_a", dlog_a, B, T, H, dt)
+    if want_dh0 and dh0 is None:
+        dh0 = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+    _st("dh0", dh0, B, H, D)
+    if states is not None:
+        _states_ok(states, B, T, H, D, chunk, dt)
+    need = int(_lib().hgrn2_bwd_workspace_bytes(B, T, H, D, D, chunk, _DT[dt], int(states is not None)))
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = ws.numel() * ws.element_size()
+    st = _lib().hgrn2_bwd_scalar(B, T, H, D, D, chunk, _DT[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(h0),
+                                 _ptr(states), _ptr(dy), _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dlog_a),
+                                 _ptr(dh0), _ptr(ws), ws_bytes, _stream())
+    _check(st, "hgrn2_bwd_scalar")
+    return dq, dk, dv, dlog_a, dh0
+
+
+def decode_step_scalar(q, k, v, log_a, state, *, y=None):
+    """One recurrent step with one decay per head, log_a [B, H]; `state` is updated in place.  Returns y."""
+    B, H, D = q.shape
+    dt = q.dtype
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        if t.shape != (B, H, D) or t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s: expected a contiguous %s CUDA tensor of shape %s" % (n, dt, (B, H, D)))
+    if log_a.shape != (B, H) or log_a.dtype != dt or not log_a.is_cuda or not log_a.is_contiguous():
+        raise ValueError("log_a: expected a contiguous %s CUDA tensor of shape %s" % (dt, (B, H)))
+    _st("state", state, B, H, D)
+    if y is None:
+        y = torch.empty_like(q)
+    st = _lib().hgrn2_decode_step_scalar(B, H, D, D, _DT[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(state),
+                                         _ptr(y), _stream())
+    _check(st, "hgrn2_decode_step_scalar")
     return y
 
 

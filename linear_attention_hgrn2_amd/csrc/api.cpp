@@ -90,11 +90,14 @@ hgrn2_status hip_status(hipError_t e, const char *what) {
 }
 
 using hgrn2::kGate;
+using hgrn2::kScalar;
 using hgrn2::kTied;
 using hgrn2::kUntied;
+using hgrn2::reads_k;
 
-// the adjoint scan reads log f (formed from z in gate mode) and never k
-int adjoint_gm(int gm) { return gm == kGate ? kGate : kUntied; }
+// the adjoint scan reads log f (formed from z in gate mode, one per head with
+// a scalar decay) and never k
+int adjoint_gm(int gm) { return gm == kGate || gm == kScalar ? gm : kUntied; }
 
 bool fwd_exists(int dtype, int D, int C, int gm = kUntied) {
   return hgrn2::dispatch_scan(dtype, D, C, false, gm, nullptr, nullptr) == hipSuccess &&
@@ -233,7 +236,7 @@ size_t hgrn2_bwd_workspace_bytes(int B, int T, int H, int DK, int DV, int chunk,
 // pointer) and dlb [H, DK].
 
 static hgrn2_status need_k(int gm, const void *k, const char *name) {
-  if (gm != kUntied) return HGRN2_OK;
+  if (!reads_k(gm)) return HGRN2_OK;
   return check_ptrs({{name, k}}, {});
 }
 
@@ -244,8 +247,10 @@ static hgrn2_status need_lb(int gm, const void *lb, const char *name) {
   return HGRN2_OK;
 }
 
-static const char *gate_name(int gm) { return gm == kGate ? "z" : "log_f"; }
-static const char *dgate_name(int gm) { return gm == kGate ? "dz" : "dlog_f"; }
+static const char *gate_name(int gm) { return gm == kGate ? "z" : gm == kScalar ? "log_a" : "log_f"; }
+static const char *dgate_name(int gm) { return gm == kGate ? "dz" : gm == kScalar ? "dlog_a" : "dlog_f"; }
+// bytes of the log-decay input (and of its gradient): one per head with a scalar decay
+static size_t gate_bytes(int gm, size_t tok, int DK) { return gm == kScalar ? tok / DK : tok; }
 
 static hgrn2_status fwd_impl(int gm, const char *fn, int B, int T, int H, int DK, int DV, int chunk, int dtype,
                              const void *q, const void *k, const void *v, const void *log_f, const float *lb,
@@ -273,9 +278,9 @@ static hgrn2_status fwd_impl(int gm, const char *fn, int B, int T, int H, int DK
   // writes the same slice of ht); any other overlap is an error.
   const size_t lbb = (size_t)H * DK * sizeof(float);
   const Range ins[] = {{"q", q, tok},
-                       {"k", gm != kUntied ? nullptr : k, tok},
+                       {"k", reads_k(gm) ? k : nullptr, tok},
                        {"v", v, tok},
-                       {gate_name(gm), log_f, tok},
+                       {gate_name(gm), log_f, gate_bytes(gm, tok, DK)},
                        {"h0", (ht == h0) ? nullptr : h0, sb},
                        {"lower_bound", gm == kGate ? lb : nullptr, lbb}};
   const Range outs[] = {{"y", y, tok}, {"ht", ht, sb}, {states_out ? "states_out" : "ws", states, stb}};
@@ -285,7 +290,7 @@ static hgrn2_status fwd_impl(int gm, const char *fn, int B, int T, int H, int DK
                          overlap(Range{"states", states, stb}, Range{"h0", h0, sb})))
     return fail(HGRN2_ERR_INVALID_ARG, "an output overlaps h0");
 
-  if (gm != kUntied) k = nullptr;
+  if (!reads_k(gm)) k = nullptr;
   if (gm != kGate) lb = nullptr;
   st = launch_scan(dtype, DK, chunk, false, gm, B, T, H, k, v, log_f, lb, h0, states, ht, stream, fn);
   if (st != HGRN2_OK || !y) return st;
@@ -317,14 +322,14 @@ static hgrn2_status bwd_impl(int gm, const char *fn, int B, int T, int H, int DK
   const size_t need = lamb + partb + (states_in ? 0 : stb);
   if (!ws || ws_bytes < need)
     return fail(HGRN2_ERR_WORKSPACE, "workspace smaller than hgrn2_bwd_workspace_bytes()");
-  if (gm != kUntied) k = dk = nullptr;
+  if (!reads_k(gm)) k = dk = nullptr;
   if (gm != kGate) lb = dlb = nullptr;
-  const size_t lbb = (size_t)H * DK * sizeof(float);
+  const size_t lbb = (size_t)H * DK * sizeof(float), gb = gate_bytes(gm, tok, DK);
   const void *states = states_in;
   const Range ins[] = {{"q", q, tok},           {"k", k, tok},          {"v", v, tok},
-                       {gate_name(gm), log_f, tok}, {"h0", h0, sb},     {"dy", dy, tok},
+                       {gate_name(gm), log_f, gb}, {"h0", h0, sb},     {"dy", dy, tok},
                        {"dht", dht, sb},        {"states_in", states_in, stb}, {"lower_bound", lb, lbb}};
-  const Range outs[] = {{"dq", dq, tok},  {"dk", dk, tok},          {"dv", dv, tok}, {dgate_name(gm), dlog_f, tok},
+  const Range outs[] = {{"dq", dq, tok},  {"dk", dk, tok},          {"dv", dv, tok}, {dgate_name(gm), dlog_f, gb},
                         {"dh0", dh0, sb}, {"dlower_bound", dlb, lbb}, {"ws", ws, need}};
   std::string msg;
   if (!check_aliasing(ins, 9, outs, 7, msg)) return fail(HGRN2_ERR_INVALID_ARG, msg);
@@ -359,7 +364,7 @@ static hgrn2_status fwd_chunk_impl(int gm, const char *fn, int B, int T, int H, 
   if (st != HGRN2_OK) return st;
   if (hgrn2::dispatch_chunk_fwd(dtype, DK, chunk, gm, nullptr, nullptr) != hipSuccess)
     return fail(HGRN2_ERR_UNSUPPORTED, "no forward kernel for this D, chunk and dtype");
-  if (gm != kUntied) k = nullptr;
+  if (!reads_k(gm)) k = nullptr;
   const size_t tok = (size_t)B * T * H * DK * dsize(dtype);
   const size_t stb = hgrn2_states_bytes(B, T, H, DK, DV, chunk, dtype);
   const Range ins[] = {{"q", q, tok}, {"k", k, tok}, {"v", v, tok}, {"log_f", log_f, tok}, {"states", states, stb}};
@@ -383,7 +388,7 @@ static hgrn2_status bwd_chunk_impl(int gm, const char *fn, int B, int T, int H, 
   if (st != HGRN2_OK) return st;
   if (!bwd_exists(dtype, DK, chunk, gm))
     return fail(HGRN2_ERR_UNSUPPORTED, "no backward kernel for this D, chunk and dtype");
-  if (gm != kUntied) k = dk = nullptr;
+  if (!reads_k(gm)) k = dk = nullptr;
   const size_t tok = (size_t)B * T * H * DK * dsize(dtype);
   const size_t stb = hgrn2_states_bytes(B, T, H, DK, DV, chunk, dtype);
   const size_t lamb = adjoint_bytes(B, T, H, DK, DV, chunk, dtype);
@@ -408,12 +413,12 @@ static hgrn2_status decode_impl(int gm, const char *fn, int B, int H, int DK, in
   if (st == HGRN2_OK) st = need_k(gm, k, "k");
   if (st == HGRN2_OK) st = need_lb(gm, lb, "lower_bound");
   if (st != HGRN2_OK) return st;
-  if (gm != kUntied) k = nullptr;
+  if (!reads_k(gm)) k = nullptr;
   if (gm != kGate) lb = nullptr;
   const size_t vec = (size_t)B * H * DK * dsize(dtype);
   const size_t sb = (size_t)B * H * DK * DV * sizeof(float);
   const size_t lbb = (size_t)H * DK * sizeof(float);
-  const Range ins[] = {{"q", q, vec}, {"k", k, vec}, {"v", v, vec}, {gate_name(gm), log_f, vec},
+  const Range ins[] = {{"q", q, vec}, {"k", k, vec}, {"v", v, vec}, {gate_name(gm), log_f, gate_bytes(gm, vec, DK)},
                        {"lower_bound", lb, lbb}};
   const Range outs[] = {{"y", y, vec}, {"state", state, sb}};
   std::string msg;
@@ -550,6 +555,29 @@ hgrn2_status hgrn2_bwd_gate(int B, int T, int H, int DK, int DV, int chunk, int 
 hgrn2_status hgrn2_decode_step_gate(int B, int H, int DK, int DV, int dtype, const void *q, const void *v,
                                     const void *z, const float *lower_bound, float *state, void *y, void *stream) {
   return decode_impl(kGate, "hgrn2_decode_step_gate", B, H, DK, DV, dtype, q, nullptr, v, z, lower_bound, state, y,
+                     stream);
+}
+
+// ---- one decay per head (log a [B,T,H])
+
+hgrn2_status hgrn2_fwd_scalar(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
+                              const void *k, const void *v, const void *log_a, const float *h0, void *y, float *ht,
+                              void *states_out, void *ws, size_t ws_bytes, void *stream) {
+  return fwd_impl(kScalar, "hgrn2_fwd_scalar", B, T, H, DK, DV, chunk, dtype, q, k, v, log_a, nullptr, h0, y, ht,
+                  states_out, ws, ws_bytes, stream);
+}
+
+hgrn2_status hgrn2_bwd_scalar(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
+                              const void *k, const void *v, const void *log_a, const float *h0,
+                              const void *states_in, const void *dy, const float *dht, void *dq, void *dk, void *dv,
+                              void *dlog_a, float *dh0, void *ws, size_t ws_bytes, void *stream) {
+  return bwd_impl(kScalar, "hgrn2_bwd_scalar", B, T, H, DK, DV, chunk, dtype, q, k, v, log_a, nullptr, h0,
+                  states_in, dy, dht, dq, dk, dv, dlog_a, nullptr, dh0, ws, ws_bytes, stream);
+}
+
+hgrn2_status hgrn2_decode_step_scalar(int B, int H, int DK, int DV, int dtype, const void *q, const void *k,
+                                      const void *v, const void *log_a, float *state, void *y, void *stream) {
+  return decode_impl(kScalar, "hgrn2_decode_step_scalar", B, H, DK, DV, dtype, q, k, v, log_a, nullptr, state, y,
                      stream);
 }
 

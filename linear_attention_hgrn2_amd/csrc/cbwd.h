@@ -117,9 +117,19 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
   const GBuf bL((const char *)a.lam + ((size_t)bh * N + n) * D * D * sizeof(T), D * D * sizeof(T));
   const uint32_t c0b = (uint32_t)c0 * sizeof(T);
   auto tok = [&](int t) { return (uint32_t)t * HDB; };  // byte offset of token t of the chunk
+  // the chunk's log decays: per channel, or one per head broadcast (kScalar)
+  const LfRows<GM> lr = lf_rows<GM, T>(a.log_f, b, T_, H, h, D, t0, len);
   // this lane's CPL elements of token t of the chunk (0 past the end)
   auto ldtok = [&](const GBuf &buf, int t) {
     Pack<T, CPL> p = buf.template ldpack<T, CPL>(tok(t) + c0b);
+    if (!has_ch) {
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) p.v[e] = from_f32<T>(0.f);
+    }
+    return p;
+  };
+  auto ldlf = [&](int t) {
+    Pack<T, CPL> p = lr.template ld<T, CPL>(t, c0b);
     if (!has_ch) {
 #pragma unroll
       for (int e = 0; e < CPL; ++e) p.v[e] = from_f32<T>(0.f);
@@ -145,8 +155,8 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       pq[t] = ldtok(bq, 16 * w + t);
-      if constexpr (GM == kUntied) pk[t] = ldtok(bk, 16 * w + t);
-      pl[t] = ldtok(bl, 16 * w + t);
+      if constexpr (reads_k(GM)) pk[t] = ldtok(bk, 16 * w + t);
+      pl[t] = ldlf(16 * w + t);
     }
     float l[16][CPL], L[CPL], kk[16][CPL];
     block_prefix<GM, T, CPL>(pk, pl, l, L, kk, lbv, len - 16 * w);
@@ -316,8 +326,8 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
           float part = 0.f;
           if (tv_) {
             Pack<T, CPL> pk;
-            if constexpr (GM == kUntied) pk = bk.template ldpack<T, CPL>(tok(16 * w + s) + c0b);
-            const Pack<T, CPL> pl = bl.template ldpack<T, CPL>(tok(16 * w + s) + c0b);
+            if constexpr (reads_k(GM)) pk = bk.template ldpack<T, CPL>(tok(16 * w + s) + c0b);
+            const Pack<T, CPL> pl = lr.template ld<T, CPL>(16 * w + s, c0b);
 #pragma unroll
             for (int e = 0; e < CPL; ++e) {
               float lf, kv;
@@ -478,7 +488,7 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
     for (int e = 0; e < CPL; ++e) L[e] = ell[e] = 0.f;
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      pl[t] = ldtok(bl, 16 * w + t);
+      pl[t] = ldlf(16 * w + t);
 #pragma unroll
       for (int e = 0; e < CPL; ++e) L[e] += lf_of<GM>(to_f32(pl[t].v[e]), lbv[e], 16 * w + t < len);
     }
@@ -487,7 +497,7 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
       const int tt = 16 * w + t;
       const Pack<T, CPL> pq = ldtok(bq, tt);
       Pack<T, CPL> pk;
-      if constexpr (GM == kUntied) pk = ldtok(bk, tt);
+      if constexpr (reads_k(GM)) pk = ldtok(bk, tt);
       Pack<T, CPL> oq, ok;
 #pragma unroll
       for (int e = 0; e < CPL; ++e) {
@@ -502,11 +512,11 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
         ok.v[e] = from_f32<T>(ek * d2);
         X[t][e] = qor * d1 - kor * d2;
         // k tied to f: f dk, subtracted from dlog f below (replaces the consumed dk'_t)
-        if (GM != kUntied && has_ch) sk[t * LDG + c0 + e] = __expf(lft) * (ek * d2);
+        if (ties_k(GM) && has_ch) sk[t * LDG + c0 + e] = __expf(lft) * (ek * d2);
       }
       if (has_ch) {
         bdq.stpack<T, CPL>(tok(tt) + c0b, oq);
-        if constexpr (GM == kUntied) bdk.stpack<T, CPL>(tok(tt) + c0b, ok);
+        if constexpr (reads_k(GM)) bdk.stpack<T, CPL>(tok(tt) + c0b, ok);
       }
     }
     if (has_ch) {
@@ -525,15 +535,15 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
     for (int e = 0; e < CPL; ++e) L[e] = ell[e] = tot[e] = 0.f;
     for (int t = 0; t < 16; ++t) {
-      const Pack<T, CPL> p = ldtok(bl, 16 * w + t);
+      const Pack<T, CPL> p = ldlf(16 * w + t);
 #pragma unroll
       for (int e = 0; e < CPL; ++e) L[e] += lf_of<GM>(to_f32(p.v[e]), lbv[e], 16 * w + t < len);
     }
     for (int t = 0; t < 16; ++t) {
       const int tt = 16 * w + t;
-      const Pack<T, CPL> pq = ldtok(bq, tt), plt = ldtok(bl, tt);
+      const Pack<T, CPL> pq = ldtok(bq, tt), plt = ldlf(tt);
       Pack<T, CPL> pk;
-      if constexpr (GM == kUntied) pk = ldtok(bk, tt);
+      if constexpr (reads_k(GM)) pk = ldtok(bk, tt);
       const Pack<T, CPL> pdy = ldtok(bdy, tt), pv = ldtok(bv, tt);
       float dqd[CPL], dkd[CPL], ex[CPL];
 #pragma unroll
@@ -542,9 +552,9 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
         dqd[e] = dkd[e] = ex[e] = 0.f;
       }
       for (int s_ = t; s_ >= 0; --s_) {
-        const Pack<T, CPL> pvs = ldtok(bv, 16 * w + s_), pls = ldtok(bl, 16 * w + s_);
+        const Pack<T, CPL> pvs = ldtok(bv, 16 * w + s_), pls = ldlf(16 * w + s_);
         Pack<T, CPL> pks;
-        if constexpr (GM == kUntied) pks = ldtok(bk, 16 * w + s_);
+        if constexpr (reads_k(GM)) pks = ldtok(bk, 16 * w + s_);
         float part = 0.f;
 #pragma unroll
         for (int e = 0; e < CPL; ++e) part += to_f32(pdy.v[e]) * to_f32(pvs.v[e]);
@@ -564,7 +574,7 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
         for (int e = 0; e < CPL; ++e) part += to_f32(pdu.v[e]) * to_f32(pv.v[e]);
         const float dA = wave_sum(part);
         if (u > t) {
-          const Pack<T, CPL> plu = ldtok(bl, 16 * w + u);
+          const Pack<T, CPL> plu = ldlf(16 * w + u);
 #pragma unroll
           for (int e = 0; e < CPL; ++e) ex[e] += lf_of<GM>(to_f32(plu.v[e]), lbv[e], 16 * w + u < len);
         }
@@ -582,13 +592,13 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
         ok.v[e] = from_f32<T>(ek * d2 + dkd[e]);
         const float x = (qor * d1 + qv * dqd[e]) - (kor * d2 + kv * dkd[e]);
         if (has_ch) sq[t * LDG + c0 + e] = x;  // X_t replaces the consumed dq'_t
-        if (GM != kUntied && has_ch)
+        if (ties_k(GM) && has_ch)
           sk[t * LDG + c0 + e] = __expf(lf_of<GM>(to_f32(plt.v[e]), lbv[e], tt < len)) * (ek * d2 + dkd[e]);
         tot[e] += x;
       }
       if (has_ch) {
         bdq.stpack<T, CPL>(tok(tt) + c0b, oq);
-        if constexpr (GM == kUntied) bdk.stpack<T, CPL>(tok(tt) + c0b, ok);
+        if constexpr (reads_k(GM)) bdk.stpack<T, CPL>(tok(tt) + c0b, ok);
       }
     }
     if (has_ch)
@@ -599,9 +609,11 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
   // dlog f = reverse in-chunk sum of X plus the carry; k tied to f subtracts
   // f dk; gate mode turns that total G into dz and sums G dlog f/dlb over the
   // chunk's tokens
-  float dlbs[CPL];
+  float dlbs[CPL], ssum[16];  // ssum: per-head decay, this lane's part of each token's dlog a
 #pragma unroll
   for (int e = 0; e < CPL; ++e) dlbs[e] = 0.f;
+#pragma unroll
+  for (int t = 0; t < 16; ++t) ssum[t] = 0.f;
   if (has_ch) {
     float carry[CPL];
 #pragma unroll
@@ -618,15 +630,16 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
       if constexpr (GM == kGate) pz = ldtok(bl, tt);
 #pragma unroll
       for (int e = 0; e < CPL; ++e) {
-        float G = GM == kUntied ? cr[e] : cr[e] - sk[t * LDG + c0 + e];
+        float G = ties_k(GM) ? cr[e] - sk[t * LDG + c0 + e] : cr[e];
         if constexpr (GM == kGate) {
           const GateGrad gg = gate_grad(to_f32(pz.v[e]), lbv[e]);
           if (tt < len) dlbs[e] += G * gg.dlb;
           G *= gg.dz;
         }
         o.v[e] = from_f32<T>(G);
+        if constexpr (GM == kScalar) ssum[t] += G;
       }
-      bdl.stpack<T, CPL>(tok(tt) + c0b, o);
+      if constexpr (GM != kScalar) bdl.stpack<T, CPL>(tok(tt) + c0b, o);
     };
     if (!wide) {
 #pragma unroll
@@ -636,10 +649,24 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
         emit(t, carry);
       }
     } else {
+#pragma unroll
       for (int t = 15; t >= 0; --t) {
 #pragma unroll
         for (int e = 0; e < CPL; ++e) carry[e] += sq[t * LDG + c0 + e];
         emit(t, carry);
+      }
+    }
+  }
+  if constexpr (GM == kScalar) {
+    // dlog a of each token: the sum over the head's channels, across the wave
+    const GBuf bda((char *)a.dlog_f + (((size_t)b * T_ + t0) * H + h) * sizeof(T), (uint32_t)(len * H * sizeof(T)));
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const float tot = wave_sum(ssum[t]);
+      if (lane == 0) {
+        Pack<T, 1> o;
+        o.v[0] = from_f32<T>(tot);
+        bda.stpack<T, 1>((uint32_t)(16 * w + t) * H * sizeof(T), o);
       }
     }
   }

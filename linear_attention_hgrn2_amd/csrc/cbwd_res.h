@@ -122,6 +122,10 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
     k.cbase = (((size_t)b * T_ + t0) * H + h) * D * sizeof(T);
     return k;
   };
+  // the chunk's log decays: per channel, or one per head broadcast (kScalar)
+  auto lfr = [&](const Chunk &k) {
+    return lf_rows<GM, T>(a.log_f, k.bh / H, T_, H, k.bh % H, D, k.n * C, k.len);
+  };
   auto win = [&](const void *base, const Chunk &k) {
     return GBuf((const char *)base + k.cbase, (uint32_t)k.len * HDB);
   };
@@ -134,7 +138,8 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
     // lane-dependent offsets are recomputed per use (never kept live across the loop)
     const int tid = opaque((int)threadIdx.x), c0 = 2 * (tid & 63);
     const Chunk k = chunk_of(ci);
-    const GBuf bq = win(a.q, k), bv = win(a.v, k), bl = win(a.log_f, k), bdy = win(a.dy, k);
+    const GBuf bq = win(a.q, k), bv = win(a.v, k), bdy = win(a.dy, k);
+    const LfRows<GM> bl = lfr(k);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int idx = tid + NT * i;
@@ -146,8 +151,8 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
     for (int t = 0; t < 8; ++t) {
       const uint32_t off = tok(16 * w + 8 * hh + t) + (uint32_t)c0 * sizeof(T);
       pq[t] = bq.ldpack<T, 2>(off);
-      if constexpr (GM == kUntied) pk[t] = win(a.k, k).template ldpack<T, 2>(off);
-      pl[t] = bl.ldpack<T, 2>(off);
+      if constexpr (reads_k(GM)) pk[t] = win(a.k, k).template ldpack<T, 2>(off);
+      pl[t] = bl.template ld<T, 2>(16 * w + 8 * hh + t, (uint32_t)c0 * sizeof(T));
     }
     if constexpr (GM == kGate) {
       plb[0] = a.lb[(k.bh % H) * D + c0];
@@ -346,7 +351,8 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
           }
         } else {
           // wide in-block decay: A[t][s] summed directly (every exponent <= 0)
-          const GBuf bq = win(a.q, k), bl = win(a.log_f, k);
+          const GBuf bq = win(a.q, k);
+          const LfRows<GM> bl = lfr(k);
           float lb2[2];
           lbs(lb2);
           for (int t = 0; t < 16; ++t) {
@@ -354,9 +360,9 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
             float ex[2] = {0.f, 0.f};
             for (int s = t; s >= 0; --s) {
               const uint32_t off = tok(16 * i + s) + (uint32_t)c0 * sizeof(T);
-              const Pack<T, 2> pls = bl.ldpack<T, 2>(off);
+              const Pack<T, 2> pls = bl.template ld<T, 2>(16 * i + s, (uint32_t)c0 * sizeof(T));
               Pack<T, 2> pks;
-              if constexpr (GM == kUntied) pks = win(a.k, k).template ldpack<T, 2>(off);
+              if constexpr (reads_k(GM)) pks = win(a.k, k).template ldpack<T, 2>(off);
               float part = 0.f;
 #pragma unroll
               for (int e = 0; e < 2; ++e) {
@@ -532,33 +538,34 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
         X[t][e] = to_f32(qr.v[e]) * dd1[e] - to_f32(kr.v[e]) * dd2[e];
         // k tied to f: f dk (f from the prefix), subtracted from dlog f in P6;
         // it replaces the consumed dk'_t
-        if (GM != kUntied && !wide)
+        if (ties_k(GM) && !wide)
           ep.stg[1][tt][c0 + e] = __expf(l[t][e] - (t ? l[t - 1][e] : hoff[e])) * (ek * dd2[e]);
       }
       if (!wide) {
         bdq.stpack<T, 2, kStream>(tok(tt) + (uint32_t)c0 * sizeof(T), oq);
-        if constexpr (GM == kUntied) bdk.stpack<T, 2, kStream>(tok(tt) + (uint32_t)c0 * sizeof(T), ok);
+        if constexpr (reads_k(GM)) bdk.stpack<T, 2, kStream>(tok(tt) + (uint32_t)c0 * sizeof(T), ok);
       }
     }
     if (wide) {
       // diagonal block summed directly: dq_t adds sum_{s <= t} dA[t][s] k_s e^{ell_t - ell_s},
       // dk_t adds sum_{u >= t} dA[u][t] q_u e^{ell_u - ell_t} (every exponent <= 0)
-      const GBuf bq = win(a.q, k), bv = win(a.v, k), bl = win(a.log_f, k), bdy = win(a.dy, k);
+      const GBuf bq = win(a.q, k), bv = win(a.v, k), bdy = win(a.dy, k);
+      const LfRows<GM> bl = lfr(k);
       const uint32_t cb2 = (uint32_t)c0 * sizeof(T);
       float lb2[2];
       lbs(lb2);
       for (int t = 0; t < 8; ++t) {
         const int tb = 8 * hh + t, tt = 16 * w + tb;
-        const Pack<T, 2> pqt = bq.ldpack<T, 2>(tok(tt) + cb2), plt = bl.ldpack<T, 2>(tok(tt) + cb2);
+        const Pack<T, 2> pqt = bq.ldpack<T, 2>(tok(tt) + cb2), plt = bl.template ld<T, 2>(tt, cb2);
         Pack<T, 2> pkt;
-        if constexpr (GM == kUntied) pkt = win(a.k, k).template ldpack<T, 2>(tok(tt) + cb2);
+        if constexpr (reads_k(GM)) pkt = win(a.k, k).template ldpack<T, 2>(tok(tt) + cb2);
         const Pack<T, 2> pdy = bdy.ldpack<T, 2>(tok(tt) + cb2), pvt = bv.ldpack<T, 2>(tok(tt) + cb2);
         float dqd[2] = {0.f, 0.f}, dkd[2] = {0.f, 0.f}, ex[2] = {0.f, 0.f};
         for (int s_ = tb; s_ >= 0; --s_) {
           const uint32_t off = tok(16 * w + s_) + cb2;
-          const Pack<T, 2> pvs = bv.ldpack<T, 2>(off), pls = bl.ldpack<T, 2>(off);
+          const Pack<T, 2> pvs = bv.ldpack<T, 2>(off), pls = bl.template ld<T, 2>(16 * w + s_, cb2);
           Pack<T, 2> pks;
-          if constexpr (GM == kUntied) pks = win(a.k, k).template ldpack<T, 2>(off);
+          if constexpr (reads_k(GM)) pks = win(a.k, k).template ldpack<T, 2>(off);
           float part = 0.f;
 #pragma unroll
           for (int e = 0; e < 2; ++e) part += to_f32(pdy.v[e]) * to_f32(pvs.v[e]);
@@ -578,7 +585,7 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
           for (int e = 0; e < 2; ++e) part += to_f32(pdu.v[e]) * to_f32(pvt.v[e]);
           const float dA = wave_sum(part);
           if (u > tb) {
-            const Pack<T, 2> plu = bl.ldpack<T, 2>(off);
+            const Pack<T, 2> plu = bl.template ld<T, 2>(16 * w + u, cb2);
 #pragma unroll
             for (int e = 0; e < 2; ++e) ex[e] += lf_of<GM>(to_f32(plu.v[e]), lb2[e], 16 * w + u < k.len);
           }
@@ -594,11 +601,11 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
           oq.v[e] = from_f32<T>(el * dd1[e] + dqd[e]);
           ok.v[e] = from_f32<T>(ek * dd2[e] + dkd[e]);
           X[t][e] += to_f32(pqt.v[e]) * dqd[e] - k_of<GM>(pkt.v[e], plt.v[e], lb2[e]) * dkd[e];
-          if (GM != kUntied)
+          if (ties_k(GM))
             ep.stg[1][tt][c0 + e] = __expf(lf_of<GM>(to_f32(plt.v[e]), lb2[e], tt < k.len)) * (ek * dd2[e] + dkd[e]);
         }
         bdq.stpack<T, 2, kStream>(tok(tt) + cb2, oq);
-        if constexpr (GM == kUntied) bdk.stpack<T, 2, kStream>(tok(tt) + cb2, ok);
+        if constexpr (reads_k(GM)) bdk.stpack<T, 2, kStream>(tok(tt) + cb2, ok);
       }
     }
 #pragma unroll
@@ -615,6 +622,9 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
     // G dlog f/dlb over the chunk's tokens
     {
       const GBuf bdl = win(a.dlog_f, k);
+      // per-head decay: dlog a [B,T,H], one value per token
+      const GBuf bda((char *)a.dlog_f + (((size_t)(k.bh / H) * T_ + k.n * C) * H + k.bh % H) * sizeof(T),
+                     (uint32_t)(k.len * H * sizeof(T)));
       float carry[2], dlbs[2] = {0.f, 0.f}, lb2[2];
       lbs(lb2);
 #pragma unroll
@@ -630,17 +640,29 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
       auto emit = [&](int t, const GateGrad *gg) {
         const int tt = 16 * w + 8 * hh + t;
         Pack<T, 2> o;
+        float gs = 0.f;
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           carry[e] += X[t][e];
-          float G = GM == kUntied ? carry[e] : carry[e] - ep.stg[1][tt][c0 + e];
+          float G = ties_k(GM) ? carry[e] - ep.stg[1][tt][c0 + e] : carry[e];
           if constexpr (GM == kGate) {
             if (tt < k.len) dlbs[e] += G * gg[e].dlb;
             G *= gg[e].dz;
           }
           o.v[e] = from_f32<T>(G);
+          gs += G;
         }
-        bdl.stpack<T, 2, kStream>(tok(tt) + (uint32_t)c0 * sizeof(T), o);
+        if constexpr (GM == kScalar) {
+          // dlog a: the sum over the head's channels, across the wave
+          const float tot = wave_sum(gs);
+          if (lane == 0) {
+            Pack<T, 1> oa;
+            oa.v[0] = from_f32<T>(tot);
+            bda.stpack<T, 1, kStream>((uint32_t)tt * H * sizeof(T), oa);
+          }
+        } else {
+          bdl.stpack<T, 2, kStream>(tok(tt) + (uint32_t)c0 * sizeof(T), o);
+        }
       };
       if (GM != kGate || !wide) {
         // f of each token from the block-local prefix of log f

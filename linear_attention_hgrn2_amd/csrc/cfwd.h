@@ -103,6 +103,8 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_fwd_kernel(ChunkFwdArgs a) 
   const T *gk = (const T *)a.k;
   const T *gv = (const T *)a.v;
   const T *gl = (const T *)a.log_f;
+  // one decay per head (kScalar): log a [B,T,H] of this chunk, token stride H
+  const T *gls = (const T *)a.log_f + (((size_t)b * T_ + t0) * H + h);
   const T *gs = (const T *)a.states + ((size_t)bh * (N + 1) + n) * D * D;
   T *gy = (T *)a.y;
   // chunk-uniform base pointers; per-lane 32-bit element offsets within the chunk
@@ -114,6 +116,18 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_fwd_kernel(ChunkFwdArgs a) 
   gl += cbase;
   gy += cbase;
   auto tok = [&](int t) { return (uint32_t)t * HD; };  // token t of the chunk
+  // this lane's CPL log decays of token tt (broadcast from the head's value with kScalar)
+  auto ldlf = [&](int tt) {
+    if constexpr (GM == kScalar) {
+      const T x = gls[(size_t)tt * H];
+      Pack<T, CPL> p;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) p.v[e] = x;
+      return p;
+    } else {
+      return ldpack<T, CPL>(gl + (tok(tt) + c0));
+    }
+  };
 
   // ---- loads: the state tile first (used last), v, then this wave's q, k, log f
   uint4 ps[Cfg::NVS];
@@ -141,8 +155,8 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_fwd_kernel(ChunkFwdArgs a) 
       for (int e = 0; e < CPL; ++e) pq[t].v[e] = pk[t].v[e] = pl[t].v[e] = from_f32<T>(0.f);
       if (tt < len && has_ch) {
         pq[t] = ldpack<T, CPL>(gq + (tok(tt) + c0));
-        if constexpr (GM == kUntied) pk[t] = ldpack<T, CPL>(gk + (tok(tt) + c0));
-        pl[t] = ldpack<T, CPL>(gl + (tok(tt) + c0));
+        if constexpr (reads_k(GM)) pk[t] = ldpack<T, CPL>(gk + (tok(tt) + c0));
+        pl[t] = ldlf(tt);
       }
     }
     float kk[16][CPL];
@@ -219,8 +233,8 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_fwd_kernel(ChunkFwdArgs a) 
           float part = 0.f;
           if (tv) {
             Pack<T, CPL> pk;
-            if constexpr (GM == kUntied) pk = ldpack<T, CPL>(gk + (tok(16 * w + s) + c0));
-            const Pack<T, CPL> pl = ldpack<T, CPL>(gl + (tok(16 * w + s) + c0));
+            if constexpr (reads_k(GM)) pk = ldpack<T, CPL>(gk + (tok(16 * w + s) + c0));
+            const Pack<T, CPL> pl = ldlf(16 * w + s);
 #pragma unroll
             for (int e = 0; e < CPL; ++e) {
               float lf, kv;

@@ -319,8 +319,15 @@ __device__ __forceinline__ float floor_logf(float x) { return fmaxf(x, kLogFloor
 //            §2.1 and §3.2: the input gate tied to the forget gate);
 //   kGate    the gate pre-activation z and a per-channel lower bound lb are
 //            the inputs: f = lb + (1 - lb) sigmoid(z), k = 1 - f (§2.2: a
-//            forget gate that learns a residual above a lower bound).
-enum GateMode : int { kUntied = 0, kTied = 1, kGate = 2 };
+//            forget gate that learns a residual above a lower bound);
+//   kScalar  one log decay per head and token, log a [B,T,H], shared by every
+//            channel of the head (§5: the per-head decay of other models,
+//            against HGRN2's per-channel one); k is an input.
+enum GateMode : int { kUntied = 0, kTied = 1, kGate = 2, kScalar = 3 };
+// k is an input (and the backward writes dk)
+constexpr bool reads_k(int gm) { return gm == kUntied || gm == kScalar; }
+// k is tied to f (the backward writes the total derivative through log f)
+constexpr bool ties_k(int gm) { return gm == kTied || gm == kGate; }
 
 // HGRN2's tied input gate k = 1 - f from log f, as -expm1(log f): no
 // cancellation for f near 1.  A zero log f (a row past the end of the

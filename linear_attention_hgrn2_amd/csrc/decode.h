@@ -47,7 +47,7 @@ __global__ __launch_bounds__(256) void hgrn2_decode_kernel(DecodeArgs a) {
   const TIn *gq = (const TIn *)a.q + (size_t)bh * D;
   const TIn *gk = (const TIn *)a.k + (size_t)bh * D;
   const TIn *gv = (const TIn *)a.v + (size_t)bh * D;
-  const TIn *gl = (const TIn *)a.log_f + (size_t)bh * D;
+  const TIn *gl = (const TIn *)a.log_f + (size_t)bh * D;  // per channel (not kScalar)
   float4 *S = (float4 *)(a.state + (size_t)bh * D * D);
 
   // issue the state loads first: they are the whole cost of the step
@@ -57,9 +57,11 @@ __global__ __launch_bounds__(256) void hgrn2_decode_kernel(DecodeArgs a) {
 
   for (int c = tid; c < D; c += Cfg::NT) {
     const float lbc = GM == kGate ? a.lb[(bh % a.H) * D + c] : 0.f;
+    // the gate input of channel c (one per head with kScalar)
+    const TIn x = GM == kScalar ? ((const TIn *)a.log_f)[bh] : gl[c];
     s_q[c] = to_f32(gq[c]);
-    s_k[c] = k_of<GM>(GM == kUntied ? gk[c] : gl[c], gl[c], lbc);
-    s_f[c] = __expf(lf_of<GM>(to_f32(gl[c]), lbc));
+    s_k[c] = k_of<GM>(reads_k(GM) ? gk[c] : x, x, lbc);
+    s_f[c] = __expf(lf_of<GM>(to_f32(x), lbc));
   }
   const float v0 = to_f32(gv[4 * cg + 0]), v1 = to_f32(gv[4 * cg + 1]),
               v2 = to_f32(gv[4 * cg + 2]), v3 = to_f32(gv[4 * cg + 3]);

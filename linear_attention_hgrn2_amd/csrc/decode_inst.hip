@@ -20,6 +20,7 @@ template <typename TIn>
 static hipError_t decode_t(int D, int gm, const DecodeArgs &a, hipStream_t s) {
   if (gm == kTied) return decode_d<TIn, kTied>(D, a, s);
   if (gm == kGate) return decode_d<TIn, kGate>(D, a, s);
+  if (gm == kScalar) return decode_d<TIn, kScalar>(D, a, s);
   if (gm == kUntied) return decode_d<TIn, kUntied>(D, a, s);
   return hipErrorNotSupported;
 }

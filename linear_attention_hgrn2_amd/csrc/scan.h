@@ -164,11 +164,12 @@ __global__ __launch_bounds__((ScanCfg<T, D, C, REV>::NT)) void hgrn2_scan_kernel
   // as zero (log f = 0, x = 0, z = 0 contribute nothing), so nothing is masked
   // where they are consumed and every step issues the same loads.
   auto prefetch = [&](XP &px, XP &pl, ZP &pz, int n) {
-    const GBuf bl = win(a.log_f, n), bz = win(a.z, n);
+    const LfRows<GM> bl = lf_rows<GM, T>(a.log_f, b, T_, H, h, D, n * C, min(C, T_ - n * C));
+    const GBuf bz = win(a.z, n);
 #pragma unroll
     for (int i = 0; i < TPR; ++i) {
-      if constexpr (REV || GM == kUntied) px[i] = win(a.x, n).template ldpack<T, 1>(xoff + (uint32_t)i * HDB).v[0];
-      pl[i] = bl.ldpack<T, 1>(xoff + (uint32_t)i * HDB).v[0];
+      if constexpr (REV || reads_k(GM)) px[i] = win(a.x, n).template ldpack<T, 1>(xoff + (uint32_t)i * HDB).v[0];
+      pl[i] = bl.template ld<T, 1>(ri * TPR + i, (uint32_t)(cs0 + cl) * sizeof(T)).v[0];
     }
 #pragma unroll
     for (int i = 0; i < Cfg::NVZ; ++i) pz[i] = bz.ld16(zoff[i]);

@@ -5,13 +5,18 @@ namespace hgrn2 {
 
 template <typename T, int D, int C> struct ScanOp {
   // the adjoint scan never reads k: it runs in the untied form or, when log f
-  // has to be formed from the gate pre-activation, in gate mode
+  // is formed from the gate pre-activation or read per head, in that mode
   static hipError_t run(bool reverse, int gm, const ScanArgs *a, hipStream_t s) {
-    if (gm < kUntied || gm > kGate || (reverse && gm == kTied)) return hipErrorNotSupported;
+    if (gm < kUntied || gm > kScalar || (reverse && gm == kTied)) return hipErrorNotSupported;
     if (!a) return hipSuccess;
-    if (reverse) return gm == kGate ? launch_scan<T, D, C, true, kGate>(*a, s) : launch_scan<T, D, C, true>(*a, s);
+    if (reverse) {
+      if (gm == kGate) return launch_scan<T, D, C, true, kGate>(*a, s);
+      if (gm == kScalar) return launch_scan<T, D, C, true, kScalar>(*a, s);
+      return launch_scan<T, D, C, true>(*a, s);
+    }
     if (gm == kTied) return launch_scan<T, D, C, false, kTied>(*a, s);
     if (gm == kGate) return launch_scan<T, D, C, false, kGate>(*a, s);
+    if (gm == kScalar) return launch_scan<T, D, C, false, kScalar>(*a, s);
     return launch_scan<T, D, C, false>(*a, s);
   }
 };

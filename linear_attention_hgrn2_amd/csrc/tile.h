@@ -373,6 +373,34 @@ __device__ __forceinline__ void lds_dma16(const GBuf &b, uint32_t off, const voi
                : "memory", "m0");
 #pragma clang diagnostic pop
 }
+// The log-decay rows of one chunk: one value per channel ([B,T,H,D], element
+// c of token t) or, with one decay per head (kScalar), [B,T,H], the head's
+// value broadcast over its channels.  Rows past the end read as zero.
+template <int GM> struct LfRows {
+  GBuf g;
+  uint32_t ts;  // bytes from one token to the next
+  // elements c .. c + N - 1 of token t (cb = byte offset of element c in a row)
+  template <typename T, int N> __device__ __forceinline__ Pack<T, N> ld(int t, uint32_t cb) const {
+    if constexpr (GM == kScalar) {
+      const T x = g.template ldpack<T, 1>((uint32_t)t * ts).v[0];
+      Pack<T, N> p;
+#pragma unroll
+      for (int e = 0; e < N; ++e) p.v[e] = x;
+      return p;
+    } else {
+      return g.template ldpack<T, N>((uint32_t)t * ts + cb);
+    }
+  }
+};
+template <int GM, typename T>
+__device__ __forceinline__ LfRows<GM> lf_rows(const void *log_f, int b, int T_, int H, int h, int D, int t0,
+                                              int len) {
+  const size_t w = GM == kScalar ? 1 : (size_t)D;
+  return LfRows<GM>{GBuf((const char *)log_f + (((size_t)b * T_ + t0) * H + h) * w * sizeof(T),
+                         (uint32_t)(len * H * w * sizeof(T))),
+                    (uint32_t)(H * w * sizeof(T))};
+}
+
 // Waits until every vector-memory load of this wave, copies into LDS included, has landed.
 __device__ __forceinline__ void vm_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 

@@ -29,7 +29,8 @@ def test_header_declares_the_entry_points():
               "hgrn2_bwd_chunk", "hgrn2_fwd_tied", "hgrn2_bwd_tied", "hgrn2_fwd_chunk_tied",
               "hgrn2_bwd_chunk_tied", "hgrn2_decode_step_tied", "hgrn2_fwd_gate", "hgrn2_bwd_gate",
               "hgrn2_decode_step_gate", "hgrn2_bwd_gate_workspace_bytes", "hgrn1_fwd", "hgrn1_bwd",
-              "hgrn1_states_bytes", "hgrn1_fwd_workspace_bytes", "hgrn1_bwd_workspace_bytes"):
+              "hgrn1_states_bytes", "hgrn1_fwd_workspace_bytes", "hgrn1_bwd_workspace_bytes",
+              "hgrn2_fwd_scalar", "hgrn2_bwd_scalar", "hgrn2_decode_step_scalar"):
         assert n in names
 
 
@@ -39,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.hgrn2_abi_version() == 6
+    assert lib.hgrn2_abi_version() == 7
     for s in range(5):
         assert lib.hgrn2_status_string(s).startswith(b"HGRN2_")
 
@@ -185,6 +186,22 @@ def test_gate_rejections(lib):
     # decode: lower_bound NULL, unsupported D
     assert lib.hgrn2_decode_step_gate(1, 1, 16, 16, 0, P[0], P[1], P[2], None, P[4], P[5], None) == 1
     assert lib.hgrn2_decode_step_gate(1, 1, 24, 24, 0, P[0], P[1], P[2], P[3], P[4], P[5], None) == 2
+
+
+def test_scalar_rejections(lib):
+    P = [FAKE + i * 0x100000 for i in range(16)]
+    # hgrn2_fwd_scalar: k NULL (k is an input); y aliases log_a
+    assert lib.hgrn2_fwd_scalar(1, 10, 1, 16, 16, 16, 0, P[0], None, P[2], P[3], None, P[4], None, P[5], None, 0,
+                                None) == 1
+    assert lib.hgrn2_fwd_scalar(1, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], P[3], None, P[3], None, P[5], None, 0,
+                                None) == 1
+    # hgrn2_bwd_scalar: dk NULL; dlog_a aliases dy
+    need = lib.hgrn2_bwd_workspace_bytes(1, 10, 1, 16, 16, 16, 0, 1)
+    assert lib.hgrn2_bwd_scalar(1, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], P[3], None, P[9], P[4], None, P[5],
+                                None, P[6], P[7], None, P[10], need, None) == 1
+    assert lib.hgrn2_bwd_scalar(1, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], P[3], None, P[9], P[4], None, P[5],
+                                P[8], P[6], P[4], None, P[10], need, None) == 1
+    assert lib.hgrn2_decode_step_scalar(1, 1, 24, 24, 0, P[0], P[1], P[2], P[3], P[4], P[5], None) == 2
 
 
 def test_hgrn1_rejections(lib):
