@@ -10,8 +10,10 @@ rotated across steps.  The same step with tied gates (k = 1 - f formed in the
 kernels, hgrn2_fwd_tied / hgrn2_bwd_tied) is timed next on the same inputs and
 reported under "tied", then the step with the gate formed from its
 pre-activation z and a per-channel lower bound (hgrn2_fwd_gate /
-hgrn2_bwd_gate, its two calls timed) under "gate"; the headline value is the
-untied step.  The decode
+hgrn2_bwd_gate, its two calls timed) under "gate", the step with one decay per
+head (hgrn2_fwd_scalar / hgrn2_bwd_scalar) under "scalar", and the HGRN1
+elementwise recurrence on the same tensors read as [B, T, C] under "hgrn1";
+the headline value is the untied step.  The decode
 step (B256 H16 d128, float32 state) is timed as well and reported in HBM
 GB/s.  Inputs are seeded synthetic data generated on the host and copied to
 HBM before timing.
@@ -143,15 +145,18 @@ TIED_KERNELS = (("scan_tied", "hgrn2_scan_kernel (forward, tied)"),
 # the gate-from-pre-activation step, as its two composite calls
 GATE_CALLS = (("fwd_gate", "hgrn2_fwd_gate: state scan + per-chunk outputs"),
               ("bwd_gate", "hgrn2_bwd_gate: adjoint scan + per-chunk gradients + lower-bound sum"))
+# the one-decay-per-head step, as its two composite calls
+SCALAR_CALLS = (("fwd_scalar", "hgrn2_fwd_scalar: state scan + per-chunk outputs"),
+                ("bwd_scalar", "hgrn2_bwd_scalar: adjoint scan + per-chunk gradients"))
 
 
 def _template_args(n: str):
-    if "<" not in n:
+    if "<" not in n or ">" not in n:
         return []
     return [a.strip() for a in n[n.index("<") + 1:n.rindex(">")].split(",")]
 
 
-GATE_SUFFIX = {"0": "", "1": "_tied", "2": "_gate"}
+GATE_SUFFIX = {"0": "", "1": "_tied", "2": "_gate", "3": "_scalar"}
 
 
 def kernel_label(name: str):
@@ -207,6 +212,11 @@ def train_algorithmic_bytes(w):
         "scan_rev_gate": 3 * tok + N * ent,
         "cbwd_gate": 4 * tok + 2 * N * ent + 3 * tok + w.B * w.H * N * w.D * 4,
         "dlb": w.B * w.H * N * w.D * 4 + w.H * w.D * 4,
+        # one decay per head: log a and dlog a are [B,T,H] (tok / D)
+        "scan_scalar": 2 * tok + tok // w.D + (N + 1) * ent,
+        "cfwd_scalar": 3 * tok + tok // w.D + N * ent + tok,
+        "scan_rev_scalar": 2 * tok + tok // w.D + N * ent,
+        "cbwd_scalar": 4 * tok + tok // w.D + 2 * N * ent + 3 * tok + tok // w.D,
     }
 
 
@@ -290,8 +300,14 @@ def bench_train(torch, m, args, sets, mode="untied"):
     states = torch.empty(m.states_shape(B, T, H, D, C), dtype=torch.bfloat16, device=dev)
     lam = torch.empty(m.adjoints_shape(B, T, H, D, C), dtype=torch.bfloat16, device=dev)
     grads = [torch.empty((B, T, H, D), dtype=torch.bfloat16, device=dev) for _ in range(4)]
-    kernels = {"untied": TRAIN_KERNELS, "tied": TIED_KERNELS, "gate": GATE_CALLS}[mode]
-    lbd = dlbd = ws = None   # gate mode: lower bound [H, D], its gradient, the workspace
+    kernels = {"untied": TRAIN_KERNELS, "tied": TIED_KERNELS, "gate": GATE_CALLS, "scalar": SCALAR_CALLS}[mode]
+    lbd = dlbd = ws = dla = None   # gate mode: lower bound [H, D], its gradient; the workspace; dlog_a
+    if mode == "scalar":
+        for s_ in sets:
+            s_.setdefault("log_a", s_["log_f"][..., 0].contiguous())
+        dla = torch.empty((B, T, H), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(int(m.lib().hgrn2_bwd_workspace_bytes(B, T, H, D, D, C, 1, 1)), dtype=torch.uint8,
+                         device=dev)
     if mode == "gate":
         import synth
         lbd = torch.from_numpy(synth.lower_bounds(H, D, 0.3, 0.25, seed=11)).to(dev)
@@ -326,7 +342,14 @@ def bench_train(torch, m, args, sets, mode="untied"):
                                dq=grads[0], dv=grads[2], dz=grads[3], dlower_bound=dlbd, ws=ws),
         )
 
-    pick = {"untied": calls_untied, "tied": calls_tied, "gate": calls_gate}[mode]
+    def calls_scalar(s):
+        return (
+            lambda: m.fwd_scalar(s["q"], s["k"], s["v"], s["log_a"], None, chunk=C, want_ht=False, states=states),
+            lambda: m.bwd_scalar(s["q"], s["k"], s["v"], s["log_a"], s["dy"], None, None, states, chunk=C,
+                                 want_dh0=False, dq=grads[0], dk=grads[1], dv=grads[2], dlog_a=dla, ws=ws),
+        )
+
+    pick = {"untied": calls_untied, "tied": calls_tied, "gate": calls_gate, "scalar": calls_scalar}[mode]
 
     def step(i, timer=None):
         s = sets[i % len(sets)]
@@ -514,16 +537,17 @@ def summarize_mfma(mfma_dir, avg_ns, digest):
     th = w.B * w.T * w.H
     alg_flop = {"scan": th * 2 * w.D * w.D, "cfwd": th * (w.chunk * 2 * w.D + 2 * w.D * w.D),
                 "scan_rev": th * 2 * w.D * w.D, "cbwd": th * (5 * w.chunk * w.D + 6 * w.D * w.D)}
-    for label in ("scan", "cfwd", "cbwd"):       # tied gates and the gate from z change no contraction
-        alg_flop[label + "_tied"] = alg_flop[label]
-        alg_flop[label + "_gate"] = alg_flop[label]
-    alg_flop["scan_rev_gate"] = alg_flop["scan_rev"]
+    for label in ("scan", "cfwd", "cbwd", "scan_rev"):   # the gate modes change no contraction
+        for sfx in ("_tied", "_gate", "_scalar"):
+            alg_flop[label + sfx] = alg_flop[label]
     out = ["Matrix-core work per launch, HGRN2 training step (B8 H16 T4096 d128 bf16 chunk64)",
            "command: " + MFMA_CMD, "durations: the kernel-trace averages of " + TRACE_CMD,
            "peak: %.0f TFLOP/s dense bf16" % BF16_PEAK_TFLOPS, "source_digest: " + digest, "",
            "%-9s %14s %14s %10s %10s %10s" % ("kernel", "executed_GFLOP", "algorithmic", "TFLOP/s",
                                               "of_peak", "MfmaUtil")]
-    for label in list(dict(TRAIN_KERNELS + TIED_KERNELS)) + ["scan_gate", "cfwd_gate", "scan_rev_gate", "cbwd_gate"]:
+    for label in list(dict(TRAIN_KERNELS + TIED_KERNELS)) + ["scan_gate", "cfwd_gate", "scan_rev_gate", "cbwd_gate",
+                                                          "scan_scalar", "cfwd_scalar", "scan_rev_scalar",
+                                                          "cbwd_scalar"]:
         mops = acc.get((label, "SQ_INSTS_VALU_MFMA_MOPS_BF16"))
         util = acc.get((label, "MfmaUtil"))
         if not mops or label not in avg_ns:
@@ -561,6 +585,7 @@ def main():
         res = bench_train(torch, m, args, sets)
         tres = bench_train(torch, m, args, sets, mode="tied")
         gres = bench_train(torch, m, args, sets, mode="gate")
+        sres = bench_train(torch, m, args, sets, mode="scalar")
         h1res = bench_hgrn1(torch, m, args, sets)
         w = res["w"]
         tokens = w.B * w.T
@@ -597,6 +622,11 @@ def main():
                                    "[H, D] (f = lb + (1 - lb) sigmoid(z), k = 1 - f): fwd(states)+bwd, dz and dlb",
                        "value": tokens / (gres["ms"] * 1e-3), "unit": "tokens/s", "ms_per_step": gres["ms"],
                        "calls_ms": {label: gk[label] for label, _ in GATE_CALLS}}
+        sk_ = sres["kernel_ms"]
+        out["scalar"] = {"workload": "train_bf16 with one decay per head (log_a [B,T,H] = the first channel's "
+                                     "log f): fwd(states)+bwd, dlog_a",
+                         "value": tokens / (sres["ms"] * 1e-3), "unit": "tokens/s", "ms_per_step": sres["ms"],
+                         "calls_ms": {label: sk_[label] for label, _ in SCALAR_CALLS}}
         out["hgrn1"] = h1res
     if args.only in ("decode", "all"):
         dres = bench_decode(torch, m, args)
