@@ -331,7 +331,7 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
             for (int e = 0; e < CPL; ++e) {
               float lf, kv;
-              lf_k<GM>(pk.v[e], pl.v[e], lbv[e], true, lf, kv);
+              lf_k<GM>(pk.v[e], lfe<GM>(pl, e), lbv[e], true, lf, kv);
               part += qt[e] * kv * __expf(ex[e]);
               ex[e] += lf;
             }
@@ -490,7 +490,7 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
     for (int t = 0; t < 16; ++t) {
       pl[t] = ldlf(16 * w + t);
 #pragma unroll
-      for (int e = 0; e < CPL; ++e) L[e] += lf_of<GM>(to_f32(pl[t].v[e]), lbv[e], 16 * w + t < len);
+      for (int e = 0; e < CPL; ++e) L[e] += lf_of<GM>(to_f32(lfe<GM>(pl[t], e)), lbv[e], 16 * w + t < len);
     }
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
@@ -502,7 +502,7 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
       for (int e = 0; e < CPL; ++e) {
         float lft, kv;
-        lf_k<GM>(pk.v[e], pl[t].v[e], lbv[e], tt < len, lft, kv);
+        lf_k<GM>(pk.v[e], lfe<GM>(pl[t], e), lbv[e], tt < len, lft, kv);
         ell[e] += lft;
         const float el = __expf(ell[e]), ek = __expf(L[e] - ell[e]);
         const float qor = to_f32(from_f32<T>(to_f32(pq.v[e]) * el));
@@ -537,7 +537,7 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
     for (int t = 0; t < 16; ++t) {
       const Pack<T, CPL> p = ldlf(16 * w + t);
 #pragma unroll
-      for (int e = 0; e < CPL; ++e) L[e] += lf_of<GM>(to_f32(p.v[e]), lbv[e], 16 * w + t < len);
+      for (int e = 0; e < CPL; ++e) L[e] += lf_of<GM>(to_f32(lfe<GM>(p, e)), lbv[e], 16 * w + t < len);
     }
     for (int t = 0; t < 16; ++t) {
       const int tt = 16 * w + t;
@@ -548,7 +548,7 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
       float dqd[CPL], dkd[CPL], ex[CPL];
 #pragma unroll
       for (int e = 0; e < CPL; ++e) {
-        ell[e] += lf_of<GM>(to_f32(plt.v[e]), lbv[e], tt < len);
+        ell[e] += lf_of<GM>(to_f32(lfe<GM>(plt, e)), lbv[e], tt < len);
         dqd[e] = dkd[e] = ex[e] = 0.f;
       }
       for (int s_ = t; s_ >= 0; --s_) {
@@ -561,8 +561,8 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
         const float dA = wave_sum(part);
 #pragma unroll
         for (int e = 0; e < CPL; ++e) {
-          dqd[e] += dA * k_of<GM>(pks.v[e], pls.v[e], lbv[e]) * __expf(ex[e]);
-          ex[e] += lf_of<GM>(to_f32(pls.v[e]), lbv[e], 16 * w + s_ < len);
+          dqd[e] += dA * k_of<GM>(pks.v[e], lfe<GM>(pls, e), lbv[e]) * __expf(ex[e]);
+          ex[e] += lf_of<GM>(to_f32(lfe<GM>(pls, e)), lbv[e], 16 * w + s_ < len);
         }
       }
 #pragma unroll
@@ -576,7 +576,7 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
         if (u > t) {
           const Pack<T, CPL> plu = ldlf(16 * w + u);
 #pragma unroll
-          for (int e = 0; e < CPL; ++e) ex[e] += lf_of<GM>(to_f32(plu.v[e]), lbv[e], 16 * w + u < len);
+          for (int e = 0; e < CPL; ++e) ex[e] += lf_of<GM>(to_f32(lfe<GM>(plu, e)), lbv[e], 16 * w + u < len);
         }
 #pragma unroll
         for (int e = 0; e < CPL; ++e) dkd[e] += dA * to_f32(pqu.v[e]) * __expf(ex[e]);
@@ -585,7 +585,7 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
       for (int e = 0; e < CPL; ++e) {
         const float el = __expf(ell[e]), ek = __expf(L[e] - ell[e]);
-        const float qv = to_f32(pq.v[e]), kv = k_of<GM>(pk.v[e], plt.v[e], lbv[e]);
+        const float qv = to_f32(pq.v[e]), kv = k_of<GM>(pk.v[e], lfe<GM>(plt, e), lbv[e]);
         const float qor = to_f32(from_f32<T>(qv * el)), kor = to_f32(from_f32<T>(kv * ek));
         const float d1 = sq[t * LDG + c0 + e], d2 = sk[t * LDG + c0 + e];
         oq.v[e] = from_f32<T>(el * d1 + dqd[e]);
@@ -593,7 +593,7 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
         const float x = (qor * d1 + qv * dqd[e]) - (kor * d2 + kv * dkd[e]);
         if (has_ch) sq[t * LDG + c0 + e] = x;  // X_t replaces the consumed dq'_t
         if (ties_k(GM) && has_ch)
-          sk[t * LDG + c0 + e] = __expf(lf_of<GM>(to_f32(plt.v[e]), lbv[e], tt < len)) * (ek * d2 + dkd[e]);
+          sk[t * LDG + c0 + e] = __expf(lf_of<GM>(to_f32(lfe<GM>(plt, e)), lbv[e], tt < len)) * (ek * d2 + dkd[e]);
         tot[e] += x;
       }
       if (has_ch) {

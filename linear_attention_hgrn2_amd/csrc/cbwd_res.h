@@ -133,6 +133,7 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
   // ---- register prefetch of a chunk's token rows
   uint4 pv[2], pdy[2];               // tile vectors idx = tid + NT i: row idx >> 4, column 8 (idx & 15)
   Pack<T, 2> pq[8], pk[8], pl[8];    // tokens 16 w + 8 hh + t, channels c0, c0 + 1
+  T pla;                             // kScalar: log a of token 16 w + 8 hh + (lane & 7)
   float plb[2];                      // gate mode: lower bounds of channels c0, c0 + 1
   auto prefetch = [&](int ci) {
     // lane-dependent offsets are recomputed per use (never kept live across the loop)
@@ -152,8 +153,9 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
       const uint32_t off = tok(16 * w + 8 * hh + t) + (uint32_t)c0 * sizeof(T);
       pq[t] = bq.ldpack<T, 2>(off);
       if constexpr (reads_k(GM)) pk[t] = win(a.k, k).template ldpack<T, 2>(off);
-      pl[t] = bl.template ld<T, 2>(16 * w + 8 * hh + t, (uint32_t)c0 * sizeof(T));
+      if constexpr (GM != kScalar) pl[t] = bl.template ld<T, 2>(16 * w + 8 * hh + t, (uint32_t)c0 * sizeof(T));
     }
+    if constexpr (GM == kScalar) pla = bl.template ld<T, 1>(16 * w + 8 * hh + (tid & 7), 0).v[0];
     if constexpr (GM == kGate) {
       plb[0] = a.lb[(k.bh % H) * D + c0];
       plb[1] = a.lb[(k.bh % H) * D + c0 + 1];
@@ -205,7 +207,8 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           float lf;
-          lf_k<GM>(pk[t].v[e], pl[t].v[e], lb2[e], 16 * w + 8 * hh + t < k.len, lf, kf[t][e]);
+          lf_k<GM>(pk[t].v[e], GM == kScalar ? readlane(pla, t) : pl[t].v[e], lb2[e], 16 * w + 8 * hh + t < k.len, lf,
+                   kf[t][e]);
           run[e] += lf;
           l[t][e] = run[e];
         }
@@ -366,8 +369,8 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
               float part = 0.f;
 #pragma unroll
               for (int e = 0; e < 2; ++e) {
-                part += to_f32(pt.v[e]) * k_of<GM>(pks.v[e], pls.v[e], lb2[e]) * __expf(ex[e]);
-                ex[e] += lf_of<GM>(to_f32(pls.v[e]), lb2[e], 16 * i + s < k.len);
+                part += to_f32(pt.v[e]) * k_of<GM>(pks.v[e], lfe<GM>(pls, e), lb2[e]) * __expf(ex[e]);
+                ex[e] += lf_of<GM>(to_f32(lfe<GM>(pls, e)), lb2[e], 16 * i + s < k.len);
               }
               const float tot = wave_sum(part);
 #pragma unroll
@@ -572,8 +575,8 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
           const float dA = wave_sum(part);
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
-            dqd[e] += dA * k_of<GM>(pks.v[e], pls.v[e], lb2[e]) * __expf(ex[e]);
-            ex[e] += lf_of<GM>(to_f32(pls.v[e]), lb2[e], 16 * w + s_ < k.len);
+            dqd[e] += dA * k_of<GM>(pks.v[e], lfe<GM>(pls, e), lb2[e]) * __expf(ex[e]);
+            ex[e] += lf_of<GM>(to_f32(lfe<GM>(pls, e)), lb2[e], 16 * w + s_ < k.len);
           }
         }
         ex[0] = ex[1] = 0.f;
@@ -587,7 +590,7 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
           if (u > tb) {
             const Pack<T, 2> plu = bl.template ld<T, 2>(16 * w + u, cb2);
 #pragma unroll
-            for (int e = 0; e < 2; ++e) ex[e] += lf_of<GM>(to_f32(plu.v[e]), lb2[e], 16 * w + u < k.len);
+            for (int e = 0; e < 2; ++e) ex[e] += lf_of<GM>(to_f32(lfe<GM>(plu, e)), lb2[e], 16 * w + u < k.len);
           }
 #pragma unroll
           for (int e = 0; e < 2; ++e) dkd[e] += dA * to_f32(pqu.v[e]) * __expf(ex[e]);
@@ -600,9 +603,9 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
           const float el = __expf(l[t][e]), ek = __expf(Lw[e] - l[t][e]);
           oq.v[e] = from_f32<T>(el * dd1[e] + dqd[e]);
           ok.v[e] = from_f32<T>(ek * dd2[e] + dkd[e]);
-          X[t][e] += to_f32(pqt.v[e]) * dqd[e] - k_of<GM>(pkt.v[e], plt.v[e], lb2[e]) * dkd[e];
+          X[t][e] += to_f32(pqt.v[e]) * dqd[e] - k_of<GM>(pkt.v[e], lfe<GM>(plt, e), lb2[e]) * dkd[e];
           if (ties_k(GM))
-            ep.stg[1][tt][c0 + e] = __expf(lf_of<GM>(to_f32(plt.v[e]), lb2[e], tt < k.len)) * (ek * dd2[e] + dkd[e]);
+            ep.stg[1][tt][c0 + e] = __expf(lf_of<GM>(to_f32(lfe<GM>(plt, e)), lb2[e], tt < k.len)) * (ek * dd2[e] + dkd[e]);
         }
         bdq.stpack<T, 2, kStream>(tok(tt) + cb2, oq);
         if constexpr (reads_k(GM)) bdk.stpack<T, 2, kStream>(tok(tt) + cb2, ok);
@@ -636,6 +639,7 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
 #pragma unroll
         for (int o = 0; o < NWV; ++o) carry[e] += (o > wv) ? ep.tot[o][c] : 0.f;
       }
+      float gsum[8];  // kScalar: each token's G summed over this lane's two channels
       // one token: its total G, then (gate mode) dz and its dlb term
       auto emit = [&](int t, const GateGrad *gg) {
         const int tt = 16 * w + 8 * hh + t;
@@ -653,13 +657,7 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
           gs += G;
         }
         if constexpr (GM == kScalar) {
-          // dlog a: the sum over the head's channels, across the wave
-          const float tot = wave_sum(gs);
-          if (lane == 0) {
-            Pack<T, 1> oa;
-            oa.v[0] = from_f32<T>(tot);
-            bda.stpack<T, 1, kStream>((uint32_t)tt * H * sizeof(T), oa);
-          }
+          gsum[t] = gs;
         } else {
           bdl.stpack<T, 2, kStream>(tok(tt) + (uint32_t)c0 * sizeof(T), o);
         }
@@ -684,6 +682,30 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
 #pragma unroll
           for (int e = 0; e < 2; ++e) gg[e] = gate_grad(to_f32(pz.v[e]), lb2[e]);
           emit(t, gg);
+        }
+      }
+      if constexpr (GM == kScalar) {
+        // dlog a of the wave's eight tokens: the sums over the head's 128
+        // channels, all eight reduced across the wave together.  Each exchange
+        // over lane bit 5, 4, 3 hands half of the tokens still held to the
+        // partner lane and adds the partner's half, so that lane bits 5..3
+        // name the token left; the last three exchanges sum the rest.
+        const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
+        float v4[4], v2[2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          v4[i] = (b5 ? gsum[i + 4] : gsum[i]) + __shfl_xor(b5 ? gsum[i] : gsum[i + 4], 32, 64);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          v2[i] = (b4 ? v4[i + 2] : v4[i]) + __shfl_xor(b4 ? v4[i] : v4[i + 2], 16, 64);
+        float tot = (b3 ? v2[1] : v2[0]) + __shfl_xor(b3 ? v2[0] : v2[1], 8, 64);
+        tot += __shfl_xor(tot, 4, 64);
+        tot += __shfl_xor(tot, 2, 64);
+        tot += __shfl_xor(tot, 1, 64);
+        if ((lane & 7) == 0) {
+          Pack<T, 1> oa;
+          oa.v[0] = from_f32<T>(tot);
+          bda.stpack<T, 1, kStream>((uint32_t)(16 * w + 8 * hh + (lane >> 3)) * H * sizeof(T), oa);
         }
       }
       if constexpr (GM == kGate) {

@@ -73,7 +73,7 @@ __device__ __forceinline__ void block_prefix(const Pack<T, CPL> *pk, const Pack<
 #pragma unroll
     for (int e = 0; e < CPL; ++e) {
       float lf;
-      lf_k<GM>(pk[t].v[e], pl[t].v[e], lb[e], t < nvalid, lf, kk[t][e]);
+      lf_k<GM>(pk[t].v[e], lfe<GM>(pl[t], e), lb[e], t < nvalid, lf, kk[t][e]);
       L[e] += lf;
       l[t][e] = L[e];
     }
@@ -116,13 +116,18 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_fwd_kernel(ChunkFwdArgs a) 
   gl += cbase;
   gy += cbase;
   auto tok = [&](int t) { return (uint32_t)t * HD; };  // token t of the chunk
-  // this lane's CPL log decays of token tt (broadcast from the head's value with kScalar)
+  // kScalar: lane j holds log a of this wave's token 16 w + (j & 15) (0 past the end)
+  T las = from_f32<T>(0.f);
+  if constexpr (GM == kScalar) {
+    const int tj = 16 * w + (lane & 15);
+    if (tj < len) las = gls[(size_t)tj * H];
+  }
+  // this lane's CPL log decays of token tt (kScalar: the head's value, element 0,
+  // read through lfe; tt is a token of this wave, the same on every lane)
   auto ldlf = [&](int tt) {
     if constexpr (GM == kScalar) {
-      const T x = gls[(size_t)tt * H];
       Pack<T, CPL> p;
-#pragma unroll
-      for (int e = 0; e < CPL; ++e) p.v[e] = x;
+      p.v[0] = readlane(las, tt - 16 * w);
       return p;
     } else {
       return ldpack<T, CPL>(gl + (tok(tt) + c0));
@@ -238,7 +243,7 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_fwd_kernel(ChunkFwdArgs a) 
 #pragma unroll
             for (int e = 0; e < CPL; ++e) {
               float lf, kv;
-              lf_k<GM>(pk.v[e], pl.v[e], lbv[e], true, lf, kv);
+              lf_k<GM>(pk.v[e], lfe<GM>(pl, e), lbv[e], true, lf, kv);
               part += qt[e] * kv * __expf(ex[e]);
               ex[e] += lf;  // the factor of s - 1 includes f_s
             }

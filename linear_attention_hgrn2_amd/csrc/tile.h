@@ -247,6 +247,16 @@ __device__ __forceinline__ void wave_lds_sync() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
+// What lane i holds, on every lane (i the same on every lane).
+__device__ __forceinline__ float readlane(float x, int i) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), i));
+}
+__device__ __forceinline__ bf16_t readlane(bf16_t x, int i) {
+  bf16_t r;
+  r.bits = (uint16_t)__builtin_amdgcn_readlane((int)x.bits, i);
+  return r;
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
@@ -380,18 +390,23 @@ template <int GM> struct LfRows {
   GBuf g;
   uint32_t ts;  // bytes from one token to the next
   // elements c .. c + N - 1 of token t (cb = byte offset of element c in a row)
+  // (kScalar: the head's value in element 0 only; read the pack through lfe)
   template <typename T, int N> __device__ __forceinline__ Pack<T, N> ld(int t, uint32_t cb) const {
     if constexpr (GM == kScalar) {
-      const T x = g.template ldpack<T, 1>((uint32_t)t * ts).v[0];
       Pack<T, N> p;
-#pragma unroll
-      for (int e = 0; e < N; ++e) p.v[e] = x;
+      p.v[0] = g.template ldpack<T, 1>((uint32_t)t * ts).v[0];
       return p;
     } else {
       return g.template ldpack<T, N>((uint32_t)t * ts + cb);
     }
   }
 };
+// Element e of a log-decay pack.  A kScalar pack carries its one value in
+// element 0 and nothing is copied into the others, so that no instruction
+// right after the load waits for it.
+template <int GM, typename T, int N> __device__ __forceinline__ T lfe(const Pack<T, N> &p, int e) {
+  return GM == kScalar ? p.v[0] : p.v[e];
+}
 template <int GM, typename T>
 __device__ __forceinline__ LfRows<GM> lf_rows(const void *log_f, int b, int T_, int H, int h, int D, int t0,
                                               int len) {
