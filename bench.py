@@ -221,17 +221,21 @@ def train_algorithmic_bytes(w):
 
 
 def hgrn1_algorithmic_bytes(B, T, C):
-    """Bytes per launch of the HGRN1 kernels, tied, bf16: tok = one [B,T,C] tensor,
-    seg = one float per (b, segment, channel)."""
+    """Bytes per launch of the HGRN1 kernels, tied, bf16, segment states saved by
+    the forward: tok = one [B,T,C] tensor, seg = one float per (b, segment of 32
+    tokens, channel), grp = one float per (b, group of 8 segments, channel)."""
+    S = (T + 31) // 32
     tok = B * T * C * 2
-    seg = B * ((T + 31) // 32) * C * 4
+    seg = B * S * C * 4
+    grp = B * ((S + 7) // 8) * C * 4
     return {
-        "h1_summary": 2 * tok + 2 * seg,          # v, log_f in; A, Bs out
-        "h1_carry": 2 * seg + seg + B * C * 4,    # A, Bs in; carries, hT out
-        "h1_final_fwd": 3 * tok + seg + tok,      # q, v, log_f, carries in; y out
-        "h1_summary_rev": 3 * tok + 2 * seg,      # q, dy, log_f in; A, Bs out
-        "h1_carry_rev": 2 * seg + seg + B * C * 4,
-        "h1_final_bwd": 4 * tok + 2 * seg + 3 * tok,  # q, v, log_f, dy, both carries in; dq, dv, dlog_f out
+        "h1_summary": 2 * tok + 2 * seg + 2 * grp,             # v, log_f in; in-group prefixes, group totals out
+        "h1_carry": 2 * grp + grp,                             # group totals in; group carries out
+        "h1_final_fwd": 3 * tok + 2 * seg + grp + tok + seg,   # q, v, log_f, prefixes, carries in; y, states out
+        "h1_summary_rev": 3 * tok + 2 * seg + 2 * grp,         # q, dy, log_f in
+        "h1_carry_rev": 2 * grp + grp,
+        "h1_final_bwd": 4 * tok + seg + 2 * seg + grp + 3 * tok,  # q, v, log_f, dy, states, suffixes, carries in;
+                                                                  # dq, dv, dlog_f out
     }
 
 

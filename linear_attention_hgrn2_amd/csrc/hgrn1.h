@@ -237,7 +237,8 @@ __global__ __launch_bounds__(kH1Pairs) void hgrn1_final_fwd_kernel(H1Args a) {
 // segment, then the adjoint from the gradient entering it from the right, and
 // the gradients.  The segment is walked in two halves of 16 tokens from the
 // right (h at the midpoint first), which halves the registers the recomputed
-// h and the token rows need.
+// h and the token rows need; the first half's rows, read for the midpoint,
+// wait in LDS until its own gradients, so no row is read twice.
 template <typename T, int GM>
 __global__ __launch_bounds__(kH1Pairs) void hgrn1_final_bwd_kernel(H1Args a) {
   constexpr int HS = kH1Seg / 2;
@@ -263,33 +264,39 @@ __global__ __launch_bounds__(kH1Pairs) void hgrn1_final_bwd_kernel(H1Args a) {
       h[e] = fmaf(__expf(lf), h[e], kv * to_f32(pv.v[e]));
     }
   };
+  // the first half's k, v and log f: read once for the midpoint and kept in
+  // this thread's own LDS slots until its gradients
+  __shared__ Pack<T, 2> sk[GM == kUntied ? HS : 1][kH1Pairs], sv[HS][kH1Pairs], sl[HS][kH1Pairs];
+  const int me = (int)threadIdx.x;
   float hmid[2] = {hst.x, hst.y};  // h after the first half
   {
-    Pack<T, 2> pk[HS], pv[HS], pl_[HS];
+    Pack<T, 2> k0[HS], v0[HS], l0[HS];
 #pragma unroll
     for (int i = 0; i < HS; ++i) {
-      if constexpr (GM == kUntied) pk[i] = bk.template ldpack<T, 2>(i * RB + cb);
-      pv[i] = bv.template ldpack<T, 2>(i * RB + cb);
-      pl_[i] = bl.template ldpack<T, 2>(i * RB + cb);
+      if constexpr (GM == kUntied) k0[i] = bk.template ldpack<T, 2>(i * RB + cb);
+      v0[i] = bv.template ldpack<T, 2>(i * RB + cb);
+      l0[i] = bl.template ldpack<T, 2>(i * RB + cb);
     }
 #pragma unroll
-    for (int i = 0; i < HS; ++i) step(pk[i], pv[i], pl_[i], hmid);
+    for (int i = 0; i < HS; ++i) {
+      step(k0[i], v0[i], l0[i], hmid);
+      if constexpr (GM == kUntied) sk[i][me] = k0[i];
+      sv[i][me] = v0[i];
+      sl[i][me] = l0[i];
+    }
   }
   float e_[2] = {gin.x, gin.y};  // gradient reaching h_t from later tokens, f_{t+1} g_{t+1}
-#pragma unroll 1
-  for (int half = 1; half >= 0; --half) {
-    const uint32_t t0 = (uint32_t)(half * HS);
-    Pack<T, 2> pq[HS], pk[HS], pv[HS], pl_[HS], pdy[HS];
+  // the gradients of one half (tokens t0 .. t0 + HS - 1, h0s the state before
+  // it), walked from its last token; pk, pv, pl_ hold the half's rows
+  auto grads = [&](uint32_t t0, const float *h0s, const Pack<T, 2> *pk, const Pack<T, 2> *pv,
+                   const Pack<T, 2> *pl_) {
+    Pack<T, 2> pq[HS], pdy[HS];
 #pragma unroll
     for (int i = 0; i < HS; ++i) {
       const uint32_t off = (t0 + i) * RB + cb;
       pq[i] = bq.template ldpack<T, 2>(off);
-      if constexpr (GM == kUntied) pk[i] = bk.template ldpack<T, 2>(off);
-      pv[i] = bv.template ldpack<T, 2>(off);
-      pl_[i] = bl.template ldpack<T, 2>(off);
       pdy[i] = bdy.template ldpack<T, 2>(off);
     }
-    const float h0s[2] = {half ? hmid[0] : hst.x, half ? hmid[1] : hst.y};
     float hs[HS][2];  // h after each token of the half
     {
       float h[2] = {h0s[0], h0s[1]};
@@ -326,6 +333,28 @@ __global__ __launch_bounds__(kH1Pairs) void hgrn1_final_bwd_kernel(H1Args a) {
         bdl.template stpack<T, 2, kStream>(off, ol);
       }
     }
+  };
+  {
+    Pack<T, 2> k1[HS], v1[HS], l1[HS];
+#pragma unroll
+    for (int i = 0; i < HS; ++i) {
+      const uint32_t off = (HS + i) * RB + cb;
+      if constexpr (GM == kUntied) k1[i] = bk.template ldpack<T, 2>(off);
+      v1[i] = bv.template ldpack<T, 2>(off);
+      l1[i] = bl.template ldpack<T, 2>(off);
+    }
+    grads(HS, hmid, k1, v1, l1);
+  }
+  {
+    Pack<T, 2> k0[HS], v0[HS], l0[HS];
+#pragma unroll
+    for (int i = 0; i < HS; ++i) {
+      if constexpr (GM == kUntied) k0[i] = sk[i][me];
+      v0[i] = sv[i][me];
+      l0[i] = sl[i][me];
+    }
+    const float hfirst[2] = {hst.x, hst.y};
+    grads(0, hfirst, k0, v0, l0);
   }
 }
 
