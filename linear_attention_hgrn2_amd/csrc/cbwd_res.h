@@ -6,7 +6,9 @@
 // same anchored exponents and the same consistently rounded dlog f, but lays
 // the work out for a whole CU:
 //   - one persistent 8-wave workgroup per CU walks chunks; the next chunk's
-//     token rows are prefetched into registers while the current one computes;
+//     token rows are prefetched into registers while the current one computes,
+//     in three groups spread over the chunk's phases (a single burst of every
+//     load fills the CU's memory queues and stalls the waves that issue it);
 //   - the chunk's token tiles (qo, ko, v, dy) and its initial state S and end
 //     adjoint Lam are all resident in LDS at once.  S and Lam arrive by
 //     asynchronous copies straight into LDS, issued when the chunk starts and
@@ -130,41 +132,55 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
     return GBuf((const char *)base + k.cbase, (uint32_t)k.len * HDB);
   };
 
-  // ---- register prefetch of a chunk's token rows
+  // ---- register prefetch of a chunk's token rows, in groups: kPfTiles (v and
+  // dy tiles; gate mode: the lower bounds), kPfK (k), kPfQL (q and log f)
+  constexpr int kPfTiles = 1, kPfK = 2, kPfQL = 4, kPfAll = 7;
+  // vector-memory loads a kPfTiles group and a kPfK group issue, at least
+  constexpr int kPfLoads = 4 + (GM == kGate ? 1 : 0) + (reads_k(GM) ? 8 : 0);
   uint4 pv[2], pdy[2];               // tile vectors idx = tid + NT i: row idx >> 4, column 8 (idx & 15)
   Pack<T, 2> pq[8], pk[8], pl[8];    // tokens 16 w + 8 hh + t, channels c0, c0 + 1
   T pla;                             // kScalar: log a of token 16 w + 8 hh + (lane & 7)
   float plb[2];                      // gate mode: lower bounds of channels c0, c0 + 1
-  auto prefetch = [&](int ci) {
+  auto prefetch = [&](int ci, int part) {
     // lane-dependent offsets are recomputed per use (never kept live across the loop)
     const int tid = opaque((int)threadIdx.x), c0 = 2 * (tid & 63);
     const Chunk k = chunk_of(ci);
     const GBuf bq = win(a.q, k), bv = win(a.v, k), bdy = win(a.dy, k);
     const LfRows<GM> bl = lfr(k);
+    if (part & kPfTiles) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int idx = tid + NT * i;
-      const uint32_t off = tok(idx >> 4) + (uint32_t)(idx & 15) * 16;
-      pv[i] = bv.ld16(off);
-      pdy[i] = bdy.ld16(off);
+      for (int i = 0; i < 2; ++i) {
+        const int idx = tid + NT * i;
+        const uint32_t off = tok(idx >> 4) + (uint32_t)(idx & 15) * 16;
+        pv[i] = bv.ld16(off);
+        pdy[i] = bdy.ld16(off);
+      }
+      if constexpr (GM == kGate) {
+        plb[0] = a.lb[(k.bh % H) * D + c0];
+        plb[1] = a.lb[(k.bh % H) * D + c0 + 1];
+      }
     }
+    if constexpr (reads_k(GM)) {
+      if (part & kPfK) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const uint32_t off = tok(16 * w + 8 * hh + t) + (uint32_t)c0 * sizeof(T);
-      pq[t] = bq.ldpack<T, 2>(off);
-      if constexpr (reads_k(GM)) pk[t] = win(a.k, k).template ldpack<T, 2>(off);
-      if constexpr (GM != kScalar) pl[t] = bl.template ld<T, 2>(16 * w + 8 * hh + t, (uint32_t)c0 * sizeof(T));
+        for (int t = 0; t < 8; ++t)
+          pk[t] = win(a.k, k).template ldpack<T, 2>(tok(16 * w + 8 * hh + t) + (uint32_t)c0 * sizeof(T));
+      }
     }
-    if constexpr (GM == kScalar) pla = bl.template ld<T, 1>(16 * w + 8 * hh + (tid & 7), 0).v[0];
-    if constexpr (GM == kGate) {
-      plb[0] = a.lb[(k.bh % H) * D + c0];
-      plb[1] = a.lb[(k.bh % H) * D + c0 + 1];
+    if (part & kPfQL) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint32_t off = tok(16 * w + 8 * hh + t) + (uint32_t)c0 * sizeof(T);
+        pq[t] = bq.ldpack<T, 2>(off);
+        if constexpr (GM != kScalar) pl[t] = bl.template ld<T, 2>(16 * w + 8 * hh + t, (uint32_t)c0 * sizeof(T));
+      }
+      if constexpr (GM == kScalar) pla = bl.template ld<T, 1>(16 * w + 8 * hh + (tid & 7), 0).v[0];
     }
   };
 
   const int G = gridDim.x;
   int ci = blockIdx.x;
-  if (ci < NC) prefetch(ci);
+  if (ci < NC) prefetch(ci, kPfAll);
   if constexpr (GM == kGate) {
     // the first chunk's lower bounds (later chunks': staged in P3 of the chunk before)
     if (ci < NC && wv == 0) {
@@ -252,7 +268,8 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
     }
     // ---- S and Lam: asynchronous copies straight into LDS (issued after the
     // prefetched registers are consumed, before the next prefetch, so that no
-    // wait of the compiler's for a register load also waits for them).  Wave wv copies
+    // wait of the compiler's for a register load also waits for them, and the
+    // wait for the copies need not wait for the prefetch).  Wave wv copies
     // rows 32 (wv % 4) .. + 31 of S (wv < 4) or Lam (wv >= 4), four rows of
     // 256 bytes per instruction; lane i lands in chunk i % 16 of row 4 j + i / 16
     // and fetches the logical chunk that the swizzle puts there.
@@ -269,9 +286,6 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
         lds_dma16(bs, (uint32_t)(r * D + 8 * q) * sizeof(T), dst + (32 * (wv & 3) + 4 * j) * D);
       }
     }
-
-    // the registers are free: fetch the next chunk's rows
-    if (ci + G < NC) prefetch(ci + G);
     __syncthreads();  // B2
 
     // ---- P0c: gap factors of block w with blocks 2 hh, 2 hh + 1; e^{P_w} (hh = 0)
@@ -303,6 +317,8 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
       if (wv == 0) sm.eG[c] = __expf(G_);
     }
     __syncthreads();  // B3
+    // the registers are free: the next chunk's v and dy tiles (and lower bounds)
+    if (ci + G < NC) prefetch(ci + G, kPfTiles);
 
     const T *qo = sm.qo, *ko = sm.ko, *tv = sm.v, *tdy = sm.dy;
     // ---- P1: the score tiles, tile id = wv + 8 s
@@ -383,6 +399,7 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
       sm.u.a.x.sc[tau][lane] = __builtin_bit_cast(uint2, acc_to_frag4<T>(X).x);
     }
     __syncthreads();  // B4
+    if (ci + G < NC) prefetch(ci + G, kPfK);
 
     // ---- P2: intra-chunk products of block w, channel half hh
     auto sc_frag = [&](int kind, int i, int j) {
@@ -433,7 +450,13 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
     }
 
     // ---- P3: inter-chunk products (S and Lam must have landed)
-    vm_drain();       // this wave's copies are in LDS (and its prefetched registers have landed)
+    // this wave's copies are in LDS: vector-memory operations complete in issue
+    // order, and at least kPfLoads loads were issued after the copies
+    if (ci + G < NC) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPfLoads) : "memory");
+    } else {
+      vm_drain();
+    }
     __syncthreads();  // B5: and every other wave's
     if constexpr (GM == kGate) {
       // the next chunk's lower bounds into the other slot (read after the next B0)
@@ -490,6 +513,7 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
       for (int cb = 0; cb < 4; ++cb) mma(DV[cb], khA, res_tr8(sL, 32 * ks, 64 * hh + 16 * cb, lane));
     }
     __syncthreads();  // B6: S, Lam, the score tiles, v and dy are dead
+    if (ci + G < NC) prefetch(ci + G, kPfQL);
 
     // ---- P4: dv out (staged through the dead v tile), dq' and dk' staging
     {
