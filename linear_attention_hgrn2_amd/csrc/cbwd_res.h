@@ -351,7 +351,12 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
       } else {  // A = qo_i (ko_j gap)^T: rows t in i, columns s in j
         bool wide_i = false;
         if (i == j) wide_i = __ballot(-sm.Lb[i][c0] > kDiagLimit || -sm.Lb[i][c0 + 1] > kDiagLimit) != 0;
-        if (!wide_i) {
+        if (i == j + 1) {
+          // adjacent blocks: the gap factor is e^{P_i - P_i} = 1 exactly
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+            mma(X, row8<D>(qo, 16 * i + n16, 32 * ks + 8 * g), row8<D>(ko, 16 * j + n16, 32 * ks + 8 * g));
+        } else if (!wide_i) {
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks) {
             const int cc = 32 * ks + 8 * g;
