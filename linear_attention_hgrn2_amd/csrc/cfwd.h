@@ -257,6 +257,17 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_fwd_kernel(ChunkFwdArgs a) 
       continue;
     }
     const int pi = pair_ij(w, j);
+    if (j == w - 1) {
+      // adjacent blocks: the gap factor is e^{P_w - P_w} = 1 exactly
+#pragma unroll
+      for (int ks = 0; ks < KSD; ++ks) {
+        const int cc = 32 * ks + 8 * g;
+        const bool ok = cc < D;
+        const int c = ok ? cc : 0;
+        mma(A[j], masked(row8<D>(sm.u.kv.ko, 16 * j + n16, c), ok), masked(row8<D>(sm.qo, 16 * w + n16, c), ok));
+      }
+      continue;
+    }
 #pragma unroll
     for (int ks = 0; ks < KSD; ++ks) {
       const int cc = 32 * ks + 8 * g;
