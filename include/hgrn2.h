@@ -30,7 +30,14 @@
  *   - Supported sizes: DK == DV == D in {16, 32, 64, 128}; chunk in
  *     {16, 32, 64}; any B, H >= 1 and T >= 1 (a partial last chunk is masked).
  *     hgrn2_supported() tells which (D, chunk, dtype) combinations have a
- *     kernel; others return HGRN2_ERR_UNSUPPORTED.
+ *     kernel; others return HGRN2_ERR_UNSUPPORTED.  Kernels address a
+ *     chunk's token rows and one sequence's chunk-boundary states with 32-bit
+ *     byte offsets and launch one workgroup per chunk, so with N =
+ *     ceil(T / chunk) and E the element size a call returns
+ *     HGRN2_ERR_INVALID_ARG ("problem too large") unless B*H*N < 2^31,
+ *     chunk*H*D*E < 2^32 and (N + 1)*D*D*E < 2^32 (bf16, D = 128: T up to
+ *     about 8.4 million tokens per sequence at chunk 64), B*H <= 2^30 and
+ *     B*T*H <= 2^40.
  *   - Gate precondition: log_f <= 0 and not NaN.  -inf (f = 0) is allowed;
  *     kernels floor log_f at -200, where exp() is already 0 in float32.
  *   - Errors: arguments are checked before anything is launched; on an
@@ -294,7 +301,9 @@ hgrn2_status hgrn2_decode_step_scalar(int B, int H, int DK, int DV, int dtype, c
  * to the forget gate, k = 1 - f (HGRN1's own form; k and dk are then NULL and
  * dlog_f is the total derivative dlog_f - f dk).  It is HGRN2's recurrence
  * with d_k = d_v = 1.  C = the channels of a token row (heads times head
- * width), any even C >= 2; any B, T >= 1.  Token tensors [B, T, C] in dtype,
+ * width), any even C >= 2 with 32*C*E < 2^32 (E the element size: a
+ * segment's rows are addressed with 32-bit byte offsets); any B, T >= 1 with
+ * B*C <= 2^30 and B*T*C <= 2^40.  Token tensors [B, T, C] in dtype,
  * 16-byte aligned; h0, hT, dht, dh0 float32 [B, C] (optional, NULL = zero /
  * not written).
  *

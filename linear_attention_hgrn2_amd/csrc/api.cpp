@@ -62,6 +62,14 @@ hgrn2_status check_common(int B, int T, int H, int DK, int DV, int chunk, int dt
   if ((long long)B * H > (1LL << 30) || (long long)B * T * H > (1LL << 40))
     return fail(HGRN2_ERR_INVALID_ARG, "problem too large");
   if (!valid_dtype(dtype)) return fail(HGRN2_ERR_INVALID_ARG, "dtype must be HGRN2_F32 or HGRN2_BF16");
+  {
+    // one workgroup per chunk; 32-bit byte offsets within a chunk's token rows
+    // and within one sequence's chunk-boundary states
+    const long long N = (T + (long long)chunk - 1) / chunk, E = dtype == HGRN2_F32 ? 4 : 2;
+    if ((long long)B * H * N >= (1LL << 31) || (long long)chunk * H * DK * E >= (1LL << 32) ||
+        (N + 1) * DK * DV * E >= (1LL << 32))
+      return fail(HGRN2_ERR_INVALID_ARG, "problem too large");
+  }
   if (DK != DV || !valid_d(DK))
     return fail(HGRN2_ERR_UNSUPPORTED, "need DK == DV in {16, 32, 64, 128}");
   if (!valid_chunk(chunk)) return fail(HGRN2_ERR_UNSUPPORTED, "chunk must be 16, 32 or 64");
@@ -588,6 +596,8 @@ static hgrn2_status h1_check(int B, int T, int C, int dtype, int tied) {
   if ((long long)B * T * C > (1LL << 40) || (long long)B * C > (1LL << 30))
     return fail(HGRN2_ERR_INVALID_ARG, "problem too large");
   if (!valid_dtype(dtype)) return fail(HGRN2_ERR_INVALID_ARG, "dtype must be HGRN2_F32 or HGRN2_BF16");
+  // a segment's 32 token rows are addressed with 32-bit byte offsets
+  if (32LL * C * (dtype == HGRN2_F32 ? 4 : 2) >= (1LL << 32)) return fail(HGRN2_ERR_INVALID_ARG, "problem too large");
   if (tied != 0 && tied != 1) return fail(HGRN2_ERR_INVALID_ARG, "tied must be 0 or 1");
   if (C % 2 != 0) return fail(HGRN2_ERR_UNSUPPORTED, "C must be even");
   return HGRN2_OK;

@@ -244,3 +244,24 @@ def test_product_path_does_not_import_the_oracle():
             if f.endswith((".py", ".h", ".hip", ".cpp")):
                 src = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in src.replace("oracle-free", ""), f
+
+
+def test_size_limits(lib):
+    """Sizes beyond the kernels' 32-bit offsets or grid are rejected before
+    anything is launched: a sequence's chunk-boundary states (N + 1) D^2 E,
+    a chunk's token rows chunk H D E, and one workgroup per chunk B H N."""
+    big = dict(ws=FAKE + 0x10000000, wsb=1 << 62)
+    # (N + 1) * 16 * 16 * 4 >= 2^32 at T = 2^26, chunk 16
+    assert _fwd(lib, T=1 << 26, **big) == 1
+    assert b"too large" in lib.hgrn2_last_error()
+    # chunk * H * 16 * 4 >= 2^32 at H = 2^22
+    assert _fwd(lib, H=1 << 22, **big) == 1
+    assert b"too large" in lib.hgrn2_last_error()
+    # B * H * N >= 2^31
+    assert _fwd(lib, B=1 << 10, H=1 << 10, T=1 << 15, **big) == 1
+    assert b"too large" in lib.hgrn2_last_error()
+    # HGRN1: 32 * C * 4 >= 2^32
+    P = [FAKE + i * 0x100000 for i in range(16)]
+    assert lib.hgrn1_fwd(1, 1, 1 << 25, 0, 1, P[0], None, P[2], P[3], None, P[4], None, None, P[9], 1 << 62,
+                         None) == 1
+    assert b"too large" in lib.hgrn2_last_error()
