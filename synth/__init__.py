@@ -198,3 +198,23 @@ def lower_bounds(H: int, D: int, lam: float, spread: float = 0.0, seed: int = 7)
         return np.full((H, D), lam, dtype=np.float32)
     rng = np.random.Generator(np.random.PCG64(seed))
     return np.clip(lam + spread * rng.uniform(-1.0, 1.0, (H, D)), 0.0, 0.99).astype(np.float32)
+
+
+def large_device_inputs(B: int, T: int, H: int, D: int, *, seed: int, reset_every: int, device="cuda"):
+    """bfloat16 token tensors too large to draw on the host, drawn on `device`
+    with torch's seeded generator: q, k, v ~ N(0, 1)/sqrt(D), dy ~ N(0, 1),
+    log_f ~ -U(0, 0.3), and log_f = -inf (a full reset, f = 0) on every channel
+    of every token t with t % reset_every == 0, so that the sequence splits
+    into independent windows that start from a zero state.  [B, T, H, D] each;
+    returns a dict."""
+    import torch
+    g = torch.Generator(device=device).manual_seed(seed)
+    shape = (B, T, H, D)
+    out = {}
+    for n in ("q", "k", "v"):
+        out[n] = torch.randn(shape, generator=g, device=device, dtype=torch.bfloat16).mul_(1.0 / math.sqrt(D))
+    out["dy"] = torch.randn(shape, generator=g, device=device, dtype=torch.bfloat16)
+    lf = torch.rand(shape, generator=g, device=device, dtype=torch.bfloat16).mul_(-0.3)
+    lf[:, ::reset_every] = float("-inf")
+    out["log_f"] = lf
+    return out
