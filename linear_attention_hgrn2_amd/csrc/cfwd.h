@@ -134,13 +134,7 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_fwd_kernel(ChunkFwdArgs a) 
     }
   };
 
-  // ---- loads: the state tile first (used last), v, then this wave's q, k, log f
-  uint4 ps[Cfg::NVS];
-#pragma unroll
-  for (int i = 0; i < Cfg::NVS; ++i) {
-    const int idx = tid + i * NT;
-    ps[i] = (idx < Cfg::VS) ? *(const uint4 *)(gs + (size_t)idx * EPV) : make_uint4(0, 0, 0, 0);
-  }
+  // ---- loads: v, then this wave's q, k, log f (the state tile, used last, once the prefix is done)
 #pragma unroll
   for (int i = 0; i < Cfg::NVV; ++i) {
     const int idx = tid + i * NT;
@@ -187,6 +181,14 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_fwd_kernel(ChunkFwdArgs a) 
   }
   wide = __ballot(wide) != 0;  // wave-uniform: this wave's diagonal block is summed directly
   __syncthreads();
+
+  // the chunk's initial state, used last
+  uint4 ps[Cfg::NVS];
+#pragma unroll
+  for (int i = 0; i < Cfg::NVS; ++i) {
+    const int idx = tid + i * NT;
+    ps[i] = (idx < Cfg::VS) ? *(const uint4 *)(gs + (size_t)idx * EPV) : make_uint4(0, 0, 0, 0);
+  }
 
   // ---- this wave's gap factors (pairs (w, j <= w)) and e^{P_w}
   if (has_ch) {
