@@ -134,14 +134,16 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_fwd_kernel(ChunkFwdArgs a) 
     }
   };
 
-  // ---- loads: v, then this wave's q, k, log f (the state tile, used last, once the prefix is done)
+  // ---- loads: v, then this wave's q, k, log f, all issued before any is
+  // used (the v tile goes to LDS after them); the state tile, used last, once
+  // the prefix is done.  v rows past the end of the sequence read as zero.
+  const GBuf bvw((const char *)gv, (uint32_t)len * HD * sizeof(T));
+  uint4 pvv[Cfg::NVV];
 #pragma unroll
   for (int i = 0; i < Cfg::NVV; ++i) {
     const int idx = tid + i * NT;
     const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (idx < Cfg::VV && row < len) v = *(const uint4 *)(gv + (tok(row) + col));
-    if (idx < Cfg::VV) *(uint4 *)&sm.u.kv.v[XT::at(row, col)] = v;
+    pvv[i] = idx < Cfg::VV ? bvw.ld16((tok(row) + col) * (uint32_t)sizeof(T)) : make_uint4(0, 0, 0, 0);
   }
   float l[16][CPL], L[CPL];
   bool wide = false;
@@ -157,6 +159,12 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_fwd_kernel(ChunkFwdArgs a) 
         if constexpr (reads_k(GM)) pk[t] = ldpack<T, CPL>(gk + (tok(tt) + c0));
         pl[t] = ldlf(tt);
       }
+    }
+#pragma unroll
+    for (int i = 0; i < Cfg::NVV; ++i) {
+      const int idx = tid + i * NT;
+      const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
+      if (idx < Cfg::VV) *(uint4 *)&sm.u.kv.v[XT::at(row, col)] = pvv[i];
     }
     float kk[16][CPL];
     block_prefix<GM, T, CPL>(pk, pl, l, L, kk, lbv, len - 16 * w);
