@@ -157,8 +157,14 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_fwd_kernel(ChunkFwdArgs a) 
       if (tt < len && has_ch) {
         pq[t] = ldpack<T, CPL>(gq + (tok(tt) + c0));
         if constexpr (reads_k(GM)) pk[t] = ldpack<T, CPL>(gk + (tok(tt) + c0));
-        pl[t] = ldlf(tt);
+        if constexpr (GM != kScalar) pl[t] = ldlf(tt);
       }
+    }
+    if constexpr (GM == kScalar) {
+      // the broadcasts wait for the one log a load: only after every load is issued
+#pragma unroll
+      for (int t = 0; t < 16; ++t)
+        if (16 * w + t < len && has_ch) pl[t] = ldlf(16 * w + t);
     }
 #pragma unroll
     for (int i = 0; i < Cfg::NVV; ++i) {
