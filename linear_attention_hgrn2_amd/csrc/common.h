@@ -329,10 +329,27 @@ constexpr bool reads_k(int gm) { return gm == kUntied || gm == kScalar; }
 // k is tied to f (the backward writes the total derivative through log f)
 constexpr bool ties_k(int gm) { return gm == kTied || gm == kGate; }
 
-// HGRN2's tied input gate k = 1 - f from log f, as -expm1(log f): no
-// cancellation for f near 1.  A zero log f (a row past the end of the
-// sequence) gives k = 0.
-__device__ __forceinline__ float tied_k(float log_f) { return -expm1f(floor_logf(log_f)); }
+// 1 - e^x for x <= 0 without cancellation: a Taylor polynomial of e^x - 1 to
+// the x^7 term for x >= -1/4 (truncation below 4e-10 relative), 1 - e^x below
+// (e^x < 0.78 there, so the subtraction loses under two bits)
+__device__ __forceinline__ float one_minus_exp(float x, float ex) {
+  float p = fmaf(x, 1.f / 5040.f, 1.f / 720.f);
+  p = fmaf(x, p, 1.f / 120.f);
+  p = fmaf(x, p, 1.f / 24.f);
+  p = fmaf(x, p, 1.f / 6.f);
+  p = fmaf(x, p, 0.5f);
+  p = fmaf(x, p, 1.f);
+  return x >= -0.25f ? -x * p : 1.f - ex;
+}
+
+// HGRN2's tied input gate k = 1 - f from log f (floored), without
+// cancellation for f near 1; ex = e^{log f}.  A zero log f (a row past the
+// end of the sequence) gives k = 0.
+__device__ __forceinline__ float tied_k_ex(float lf, float ex) { return one_minus_exp(lf, ex); }
+__device__ __forceinline__ float tied_k(float log_f) {
+  const float lf = floor_logf(log_f);
+  return one_minus_exp(lf, __expf(lf));
+}
 
 // The gate from its pre-activation, f = lb + (1 - lb) sigmoid(z), evaluated
 // with one exponential, one hardware reciprocal and one logarithm: with
@@ -382,19 +399,6 @@ __device__ __forceinline__ GateGrad gate_grad(float z, float lb) {
   g.dlb = sp * inv;
   return g;
 }
-// 1 - e^x for x <= 0 without cancellation: a Taylor polynomial of e^x - 1 to
-// the x^7 term for x >= -1/4 (truncation below 4e-10 relative), 1 - e^x below
-// (e^x < 0.78 there, so the subtraction loses under two bits)
-__device__ __forceinline__ float one_minus_exp(float x, float ex) {
-  float p = fmaf(x, 1.f / 5040.f, 1.f / 720.f);
-  p = fmaf(x, p, 1.f / 120.f);
-  p = fmaf(x, p, 1.f / 24.f);
-  p = fmaf(x, p, 1.f / 6.f);
-  p = fmaf(x, p, 0.5f);
-  p = fmaf(x, p, 1.f);
-  return x >= -0.25f ? -x * p : 1.f - ex;
-}
-
 // from log f (floored) when z is no longer at hand: s' = (1 - f) / (1 - lb)
 // and (1 - lb) s = f - lb
 __device__ __forceinline__ GateGrad gate_grad_lf(float lf, float lb) {
@@ -416,8 +420,10 @@ template <int GM> __device__ __forceinline__ float lf_of(float x, float lb, bool
 }
 
 // log f and k of one token together (the gate pieces computed once):
-// kUntied loads k, kTied forms k = -expm1(log f), kGate forms both from z.
-template <int GM, typename T>
+// kUntied loads k, kTied forms k = 1 - e^{log f}, kGate forms both from z.
+// LIBK: kTied takes k from the library's expm1f (fewer registers live where
+// many tokens are formed at once) instead of the polynomial.
+template <int GM, bool LIBK = false, typename T>
 __device__ __forceinline__ void lf_k(T k, T x, float lb, bool valid, float &lf, float &kv) {
   if constexpr (GM == kGate) {
     const float z = to_f32(x);
@@ -428,7 +434,7 @@ __device__ __forceinline__ void lf_k(T k, T x, float lb, bool valid, float &lf, 
     kv = (1.f - lb) * (z >= 0.f ? p.u * p.r : p.r);
   } else {
     lf = floor_logf(to_f32(x));
-    kv = GM == kTied ? -expm1f(lf) : to_f32(k);
+    kv = GM == kTied ? (LIBK ? -expm1f(lf) : one_minus_exp(lf, __expf(lf))) : to_f32(k);
   }
 }
 

@@ -116,7 +116,7 @@ __global__ __launch_bounds__(64 * kH1Grp) void hgrn1_summary_kernel(H1Args a) {
       if constexpr (REV) {
         h[e] = f * (to_f32(px[i].v[e]) * to_f32(pz[i].v[e]) + h[e]);  // e_t = f_t (q_t dy_t + e_{t+1})
       } else {
-        const float kv = GM == kTied ? -expm1f(lf) : to_f32(px[i].v[e]);
+        const float kv = GM == kTied ? tied_k_ex(lf, f) : to_f32(px[i].v[e]);
         h[e] = fmaf(f, h[e], kv * to_f32(pz[i].v[e]));
       }
     }
@@ -224,9 +224,9 @@ __global__ __launch_bounds__(kH1Pairs) void hgrn1_final_fwd_kernel(H1Args a) {
     Pack<T, 2> o;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const float lf = floor_logf(to_f32(pl_[i].v[e]));
-      const float kv = GM == kTied ? -expm1f(lf) : to_f32(pk[i].v[e]);
-      h[e] = fmaf(__expf(lf), h[e], kv * to_f32(pv[i].v[e]));
+      const float lf = floor_logf(to_f32(pl_[i].v[e])), f = __expf(lf);
+      const float kv = GM == kTied ? tied_k_ex(lf, f) : to_f32(pk[i].v[e]);
+      h[e] = fmaf(f, h[e], kv * to_f32(pv[i].v[e]));
       o.v[e] = from_f32<T>(to_f32(pq[i].v[e]) * h[e]);
     }
     if (pl.valid) by.template stpack<T, 2, kStream>(i * RB + cb, o);
@@ -259,9 +259,9 @@ __global__ __launch_bounds__(kH1Pairs) void hgrn1_final_bwd_kernel(H1Args a) {
   auto step = [&](const Pack<T, 2> &pk, const Pack<T, 2> &pv, const Pack<T, 2> &plf, float *h) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const float lf = floor_logf(to_f32(plf.v[e]));
-      const float kv = GM == kTied ? -expm1f(lf) : to_f32(pk.v[e]);
-      h[e] = fmaf(__expf(lf), h[e], kv * to_f32(pv.v[e]));
+      const float lf = floor_logf(to_f32(plf.v[e])), f = __expf(lf);
+      const float kv = GM == kTied ? tied_k_ex(lf, f) : to_f32(pk.v[e]);
+      h[e] = fmaf(f, h[e], kv * to_f32(pv.v[e]));
     }
   };
   // the first half's k, v and log f: read once for the midpoint and kept in
@@ -313,7 +313,7 @@ __global__ __launch_bounds__(kH1Pairs) void hgrn1_final_bwd_kernel(H1Args a) {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const float lf = floor_logf(to_f32(pl_[i].v[e])), f = __expf(lf);
-        const float kv = GM == kTied ? -expm1f(lf) : to_f32(pk[i].v[e]);
+        const float kv = GM == kTied ? tied_k_ex(lf, f) : to_f32(pk[i].v[e]);
         const float dy = to_f32(pdy[i].v[e]), vv = to_f32(pv[i].v[e]);
         const float g = fmaf(to_f32(pq[i].v[e]), dy, e_[e]);
         const float hp = i ? hs[i - 1][e] : h0s[e];
