@@ -472,32 +472,39 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
     }
     const T *sS = sm.u.a.S, *sL = sm.u.a.L;
     float rsv = 0.f, cp[4];
+    f32x4_t tq[4], tk[4], dg;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      acc_zero(tq[cb]);
+      acc_zero(tk[cb]);
+    }
+    acc_zero(dg);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int j = 32 * ks + 8 * g;
+      const PFrag<T> fdy = row8<D>(tdy, 16 * w + n16, j), fv = row8<D>(tv, 16 * w + n16, j);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int c = 64 * hh + 16 * cb + n16;
+        const PFrag<T> sf = res_row8(sS, c, j), lf = res_row8(sL, c, j);
+        mma(tq[cb], fdy, sf);
+        mma(tk[cb], fv, lf);
+        if (cb == w) mma(dg, sf, lf);
+      }
+    }
+    {
+      const int r = n16 & 3;
+      rsv = (r == 0) ? dg[0] : (r == 1) ? dg[1] : (r == 2) ? dg[2] : dg[3];
+    }
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
       const int c = 64 * hh + 16 * cb + n16;
-      const bool own = (cb == w);  // rowsum(S * Lam) of block 4 hh + w, on lane (n >> 2, n)
-      f32x4_t tq, tk, dg;
-      acc_zero(tq);
-      acc_zero(tk);
-      acc_zero(dg);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int j = 32 * ks + 8 * g;
-        const PFrag<T> sf = res_row8(sS, c, j), lf = res_row8(sL, c, j);
-        mma(tq, row8<D>(tdy, 16 * w + n16, j), sf);
-        mma(tk, row8<D>(tv, 16 * w + n16, j), lf);
-        if (own) mma(dg, sf, lf);
-      }
-      if (own) {
-        const int r = n16 & 3;
-        rsv = (r == 0) ? dg[0] : (r == 1) ? dg[1] : (r == 2) ? dg[2] : dg[3];
-      }
       const float eP = sm.fac[w][0][c], eK = sm.fac[w][1][c];
       float ckp = 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        DQ[cb][r] += eP * tq[r];
-        const float x = eK * tk[r];
+        DQ[cb][r] += eP * tq[cb][r];
+        const float x = eK * tk[cb][r];
         DK[cb][r] += x;
         ckp += to_f32(ko[XT::at(16 * w + 4 * g + r, c)]) * x;  // ko as it entered the products
       }
