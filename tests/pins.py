@@ -552,11 +552,51 @@ def pin_scalar_decay_finite_differences(orc):
     assert rel(g, num) < 1e-7
 
 
+
+def pin_decode_variants(orc):
+    """The tied, gate and per-head decode steps: each is one step of its
+    forward from the given state, and equals the one-step definition written
+    out in numpy (S' = f S + k^T v, y = q S'), with f and k formed directly:
+    f = exp(log f), k = 1 - f (tied); f = lam + (1 - lam) / (1 + e^-z),
+    k = 1 - f (gate); one f per head (scalar)."""
+    import oracle as o
+    q, k, v, lf, h0 = rand_inputs(51, T=1)
+    r = _rng(52)
+    B, _, H, DK = q.shape
+
+    def one_step(f, kk):
+        S = f[..., :, None] * h0 + kk[..., :, None] * v[:, 0][..., None, :]
+        return np.einsum("bhc,bhcj->bhj", q[:, 0], S), S
+
+    # tied
+    yd, Sd = o.decode_step_tied(q[:, 0], v[:, 0], lf[:, 0], h0)
+    y1, h1 = o.forward_tied(q, v, lf, h0)
+    f = np.exp(lf[:, 0])
+    yr, Sr = one_step(f, 1.0 - f)
+    assert rel(yd, y1[:, 0]) < 1e-14 and rel(Sd, h1) < 1e-14
+    assert rel(yd, yr) < 1e-12 and rel(Sd, Sr) < 1e-12
+    # gate from the pre-activation with a per-channel lower bound
+    z = r.normal(0.0, 2.0, (B, 1, H, DK))
+    lam = r.uniform(0.0, 0.9, (H, DK))
+    yd, Sd = o.decode_step_gate(q[:, 0], v[:, 0], z[:, 0], lam, h0)
+    y1, h1 = o.forward_gate(q, v, z, lam, h0)
+    f = lam + (1.0 - lam) / (1.0 + np.exp(-z[:, 0]))
+    yr, Sr = one_step(f, 1.0 - f)
+    assert rel(yd, y1[:, 0]) < 1e-14 and rel(Sd, h1) < 1e-14
+    assert rel(yd, yr) < 1e-12 and rel(Sd, Sr) < 1e-12
+    # one decay per head
+    la = r.uniform(-1.5, 0.0, (B, 1, H))
+    yd, Sd = o.decode_step_scalar(q[:, 0], k[:, 0], v[:, 0], la[:, 0], h0)
+    y1, h1 = o.forward_scalar(q, k, v, la, h0)
+    yr, Sr = one_step(np.repeat(np.exp(la[:, 0])[..., None], DK, axis=-1), k[:, 0])
+    assert rel(yd, y1[:, 0]) < 1e-14 and rel(Sd, h1) < 1e-14
+    assert rel(yd, yr) < 1e-12 and rel(Sd, Sr) < 1e-12
+
 ALL_PINS = [pin_closed_form, pin_limit_f_one, pin_limit_f_zero, pin_scalar_scan,
             pin_golden_exact, pin_linearity, pin_state_carry, pin_decode,
             pin_finite_differences, pin_autograd, pin_dlogf_identity, pin_bwd_limits,
             pin_tied_finite_differences, pin_tied_autograd,
             pin_gate_log_sigmoid, pin_gate_finite_differences, pin_gate_autograd,
             pin_hgrn1_geometric, pin_hgrn1_finite_differences,
-            pin_scalar_decay_autograd, pin_scalar_decay_finite_differences]
+            pin_scalar_decay_autograd, pin_scalar_decay_finite_differences, pin_decode_variants]
 GATE_PINS = [pin_gate_log_sigmoid, pin_gate_finite_differences, pin_gate_autograd]
