@@ -223,8 +223,8 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           float lf;
-          lf_k<GM, true>(pk[t].v[e], GM == kScalar ? readlane(pla, t) : pl[t].v[e], lb2[e],
-                         16 * w + 8 * hh + t < k.len, lf, kf[t][e]);
+          lf_k<GM>(pk[t].v[e], GM == kScalar ? readlane(pla, t) : pl[t].v[e], lb2[e],
+                   16 * w + 8 * hh + t < k.len, lf, kf[t][e]);
           run[e] += lf;
           l[t][e] = run[e];
         }

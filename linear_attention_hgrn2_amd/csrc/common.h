@@ -421,9 +421,7 @@ template <int GM> __device__ __forceinline__ float lf_of(float x, float lb, bool
 
 // log f and k of one token together (the gate pieces computed once):
 // kUntied loads k, kTied forms k = 1 - e^{log f}, kGate forms both from z.
-// LIBK: kTied takes k from the library's expm1f (fewer registers live where
-// many tokens are formed at once) instead of the polynomial.
-template <int GM, bool LIBK = false, typename T>
+template <int GM, typename T>
 __device__ __forceinline__ void lf_k(T k, T x, float lb, bool valid, float &lf, float &kv) {
   if constexpr (GM == kGate) {
     const float z = to_f32(x);
@@ -434,7 +432,7 @@ __device__ __forceinline__ void lf_k(T k, T x, float lb, bool valid, float &lf, 
     kv = (1.f - lb) * (z >= 0.f ? p.u * p.r : p.r);
   } else {
     lf = floor_logf(to_f32(x));
-    kv = GM == kTied ? (LIBK ? -expm1f(lf) : one_minus_exp(lf, __expf(lf))) : to_f32(k);
+    kv = GM == kTied ? one_minus_exp(lf, __expf(lf)) : to_f32(k);
   }
 }
 
