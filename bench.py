@@ -45,7 +45,7 @@ CALIB_BYTES = 1 << 30          # the --calib-copy device copy: 1 GiB read, 1 GiB
 # (rocprofv3 writes under PROF_OUT, a directory relative to the repository root)
 PROF_OUT = os.environ.get("HGRN2_PROF_OUT", "prof_out")
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats -d " + PROF_OUT + "/trace -o run --output-format csv "
-             "-- python3 bench.py --steps 5 --warmup 1 --no-cpu")
+             "-- python3 bench.py --steps 20 --warmup 3 --no-cpu")
 PMC_CMD = ("rocprofv3 --pmc {ctr} -d " + PROF_OUT + "/{dir} -o run --output-format csv "
            "-- python3 bench.py --only train --steps 2 --warmup 1 --no-cpu --calib-copy")
 MFMA_CMD = ("rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 MfmaUtil -d " + PROF_OUT + "/mfma -o run "
