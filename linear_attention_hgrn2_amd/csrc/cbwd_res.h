@@ -322,7 +322,7 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
 
     const T *qo = sm.qo, *ko = sm.ko, *tv = sm.v, *tdy = sm.dy;
     // ---- P1: the score tiles, tile id = wv + 8 s
-#pragma unroll 1
+#pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
       const int tau = wv + NWV * s4;
       if (tau >= Cfg::NTILE) break;
