@@ -13,10 +13,13 @@ pre-activation z and a per-channel lower bound (hgrn2_fwd_gate /
 hgrn2_bwd_gate, its two calls timed) under "gate", the step with one decay per
 head (hgrn2_fwd_scalar / hgrn2_bwd_scalar) under "scalar", and the HGRN1
 elementwise recurrence on the same tensors read as [B, T, C] under "hgrn1";
-the headline value is the untied step.  The decode
-step (B256 H16 d128, float32 state) is timed as well and reported in HBM
-GB/s.  Inputs are seeded synthetic data generated on the host and copied to
-HBM before timing.
+the headline value is the untied step.  The decode step (B256 H16 d128,
+float32 state) is timed as well and reported in HBM GB/s, and the two
+forward-only workloads (B4 H8 T2048 and B1 H32 T32768 with an initial state,
+both d128 bf16 chunk 64) under "fwd_bf16" and "long_bf16", each call after an
+eviction of the caches.  Inputs are seeded synthetic data generated on the
+host and copied to HBM before timing.  The float64 CPU oracle is timed on the
+host cores on the same batches, and its outputs are compared with the GPU's.
 
 Prints ONE JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -60,7 +63,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--decode-steps", type=int, default=50)
-    p.add_argument("--only", choices=["train", "decode", "all"], default="all")
+    p.add_argument("--only", choices=["train", "decode", "fwd_bf16", "long_bf16", "all"], default="all",
+                   help="run one leg only (train: the training step and its variants)")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 1 GiB elementwise pass, read once and written once "
                         "(calibrates profiler byte counters)")
@@ -132,8 +136,15 @@ class KernelTimer:
         e.record()
         self.pairs.setdefault(name, []).append((s, e))
 
+    def times_ms(self, name):
+        return [s.elapsed_time(e) for s, e in self.pairs[name]]
+
     def mean_ms(self, name):
-        return float(np.mean([s.elapsed_time(e) for s, e in self.pairs[name]]))
+        return float(np.mean(self.times_ms(name)))
+
+    def stats(self, name):
+        t = self.times_ms(name)
+        return {"mean": float(np.mean(t)), "median": float(np.median(t)), "min": float(np.min(t)), "n": len(t)}
 
 
 # the four launches of one training step, in order, with the kernel each one runs
@@ -220,6 +231,35 @@ def train_algorithmic_bytes(w):
         "scan_rev_scalar": 2 * tok + tok // w.D + N * ent,
         "cbwd_scalar": 4 * tok + tok // w.D + 2 * N * ent + 3 * tok + tok // w.D,
     }
+
+
+def train_abi_bytes(w):
+    """Bytes per launch counted as the scope table's measurement section does:
+    the tensors of the C ABI each launch reads or writes (q, k, v, log_f, dy,
+    y and the four gradients, once each) plus the chunk-boundary states (an
+    output of hgrn2_fwd, read by the chunk kernels); the adjoint workspace,
+    which stays inside hgrn2_bwd, is left out."""
+    tok = w.B * w.T * w.H * w.D * 2
+    N = w.T // w.chunk
+    ent = w.B * w.H * w.D * w.D * 2
+    return {"scan": 3 * tok + (N + 1) * ent, "cfwd": 4 * tok + N * ent + tok, "scan_rev": 3 * tok,
+            "cbwd": 5 * tok + N * ent + 4 * tok,
+            "scan_tied": 2 * tok + (N + 1) * ent, "cfwd_tied": 3 * tok + N * ent + tok,
+            "cbwd_tied": 4 * tok + N * ent + 3 * tok}
+
+
+def train_step_flop(w):
+    """Algorithmic flops of one training step (forward C(d_k + d_v) + 4 d_k d_v
+    and backward 5 C d + 8 d^2 per token-head; no recompute, no masked work)."""
+    th = w.B * w.T * w.H
+    return th * (w.chunk * 2 * w.D + 4 * w.D * w.D) + th * (5 * w.chunk * w.D + 8 * w.D * w.D)
+
+
+def train_compulsory_bytes(w):
+    """The step's compulsory HBM bytes: the forward reads q, k, v, log_f and
+    writes y; the backward reads q, k, v, log_f, dy and writes dq, dk, dv,
+    dlog_f (14 bf16 token tensors)."""
+    return 14 * w.B * w.T * w.H * w.D * 2
 
 
 def hgrn1_algorithmic_bytes(B, T, C):
@@ -359,11 +399,14 @@ def bench_train(torch, m, args, sets, mode="untied"):
 
     def step(i, timer=None):
         s = sets[i % len(sets)]
+        st = timer.start("step") if timer else None
         for (label, _), call in zip(kernels, pick(s)):
             t = timer.start(label) if timer else None
             call()
             if timer:
                 timer.stop(t)
+        if timer:
+            timer.stop(st)
 
     for i in range(args.warmup):
         step(i)
@@ -382,8 +425,18 @@ def bench_train(torch, m, args, sets, mode="untied"):
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
     kms = {label: timer.mean_ms(label) for label, _ in kernels}
+    kstats = {label: timer.stats(label) for label, _ in kernels}
     log("timed (%s): %.3f ms/step (%s)" % (mode, ms, ", ".join("%s %.3f ms" % kv for kv in kms.items())))
-    return dict(w=w, ms=ms, kernel_ms=kms, host=sets[0]["host"])
+    out = None
+    if mode == "untied":
+        # after the timed region: one more step on the first input set, whose
+        # outputs the CPU oracle checks
+        step(0)
+        torch.cuda.synchronize()
+        out = {"y": y.clone(), "dq": grads[0].clone(), "dk": grads[1].clone(), "dv": grads[2].clone(),
+               "dlog_f": grads[3].clone()}
+    return dict(w=w, ms=ms, kernel_ms=kms, kernel_stats=kstats, step_stats=timer.stats("step"),
+                host=sets[0]["host"], out=out)
 
 
 def bench_decode(torch, m, args):
@@ -400,40 +453,126 @@ def bench_decode(torch, m, args):
     torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
+    timer = KernelTimer(torch)
     a.record()
     for i in range(args.decode_steps):
+        t = timer.start("decode")
         m.decode_step(q, k, v, lf, states[i % 2], y=y)
+        timer.stop(t)
     b.record()
     torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / args.decode_steps
+    ms_loop = a.elapsed_time(b) / args.decode_steps
+    stats = timer.stats("decode")
+    ms = stats["median"]   # one launch, between the events recorded around it on its stream
     state_bytes = w.B * w.H * w.D * w.D * 4
     vec_bytes = 5 * w.B * w.H * w.D * 4          # q, k, v, log_f read; y written
     gbs = (2 * state_bytes + vec_bytes) / (ms * 1e-3) / 1e9
-    log("decode: %.3f ms/step, %.1f GB/s" % (ms, gbs))
-    return dict(ms=ms, gbs=gbs, bytes=2 * state_bytes + vec_bytes)
+    log("decode: median %.3f ms/launch (%.3f ms per step of the loop), %.1f GB/s" % (ms, ms_loop, gbs))
+    return dict(ms=ms, ms_loop=ms_loop, gbs=gbs, bytes=2 * state_bytes + vec_bytes, stats=stats)
+
+
+def _parity(got: dict, refs: dict, layouts: dict, tol: float):
+    """errors() of each GPU output against the oracle's (every slice, row and
+    element; tests/gpu_util.py), and whether all are within `tol`."""
+    from tests.gpu_util import errors, to_host64, worst
+    out = {}
+    for n, r in refs.items():
+        out[n] = errors(to_host64(got[n]), r, layouts.get(n, "token"))
+    ok = all(worst(e) <= tol for e in out.values())
+    return {"tolerance": tol, "pass": bool(ok), "errors": out}
 
 
 def cpu_baseline(res, min_seconds=10.0, max_reps=8):
     """The float64 oracle on the host cores over the same training batch (all
     (b, h) sequences, all tokens, forward + backward), repeated until about
-    `min_seconds` of CPU time has passed; the rate is the mean over repetitions."""
+    `min_seconds` of CPU time has passed; the rate is the mean over
+    repetitions.  The first repetition's outputs are compared with the GPU's
+    outputs for the same batch (the first input set, lower bound 0)."""
     import oracle
     import synth
     w = res["w"]
     d = res["host"]
     threads = oracle.threads()
     x = {n: synth.to_f64(d[n], "bf16") for n in ("q", "k", "v", "log_f", "dy")}
-    reps, t0 = 0, time.time()
+    reps, t0, first = 0, time.time(), None
     while reps < max_reps and (reps == 0 or time.time() - t0 < min_seconds):
-        oracle.forward(x["q"], x["k"], x["v"], x["log_f"], None)
-        oracle.backward(x["q"], x["k"], x["v"], x["log_f"], x["dy"], None, None)
+        yr, _ = oracle.forward(x["q"], x["k"], x["v"], x["log_f"], None)
+        gr = oracle.backward(x["q"], x["k"], x["v"], x["log_f"], x["dy"], None, None)
+        if first is None:
+            first = {"y": yr, "dq": gr[0], "dk": gr[1], "dv": gr[2], "dlog_f": gr[3]}
+        del yr, gr
         reps += 1
     dt = time.time() - t0
     tokens_per_s = reps * w.B * w.T / dt
     log("cpu oracle: %d x the B%d T%d batch in %.2f s on %d threads" % (reps, w.B, w.T, dt, threads))
-    return {"value": tokens_per_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "the whole B%d H%d T%d batch, fwd+bwd in float64, %d repetitions (%.1f s)"
-                      % (w.B, w.H, w.T, reps, dt)}
+    out = {"value": tokens_per_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": "the whole B%d H%d T%d batch (lower bound 0), fwd+bwd in float64, %d repetitions (%.1f s)"
+                     % (w.B, w.H, w.T, reps, dt)}
+    if res.get("out") is not None:
+        del x
+        out["parity"] = _parity(res["out"], first, {}, 2e-2)
+        out["parity"]["compared"] = "y, dq, dk, dv, dlog_f of all %d (b, h) sequences" % (w.B * w.H)
+        log("parity vs oracle: %s" % ("pass" if out["parity"]["pass"] else "FAIL"))
+    return out
+
+
+def bench_fwd_only(torch, m, args, name, cpu=True):
+    """A forward-only workload (hgrn2_fwd: y and the final state, no states
+    kept for a backward), one call per step.  Before each call a 512 MiB fill
+    evicts the inputs from L2 and the 256 MB last-level cache; events bracket
+    the call alone.  The oracle then runs the same batch on the host cores and
+    its outputs are compared with the GPU's."""
+    import synth
+    from tests.gpu_util import to_dev
+    w = synth.WORKLOADS[name]
+    d = synth.generate(w)
+    B, T, H, D, C = w.B, w.T, w.H, w.D, w.chunk
+    q, k, v, lf = (to_dev(d[n], "bf16") for n in ("q", "k", "v", "log_f"))
+    h0 = to_dev(d["h0"], "f32")
+    dev = q.device
+    y = torch.empty_like(q)
+    ht = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(int(m.lib().hgrn2_fwd_workspace_bytes(B, T, H, D, D, C, 1, 0)), dtype=torch.uint8, device=dev)
+    flush = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
+
+    def call():
+        m.fwd(q, k, v, lf, h0, chunk=C, y=y, ht=ht, ws=ws)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    timer = KernelTimer(torch)
+    for i in range(args.steps):
+        flush.fill_(i & 255)
+        t = timer.start("call")
+        call()
+        timer.stop(t)
+    torch.cuda.synchronize()
+    st = timer.stats("call")
+    tok = B * T * H * D * 2
+    sb = B * H * D * D * 4
+    comp = 5 * tok + sb + (sb if h0 is not None else 0)   # q, k, v, log_f in, y out; ht out; h0 in
+    flop = B * T * H * (C * 2 * D + 4 * D * D)
+    log("timed (%s): median %.3f ms, min %.3f ms" % (name, st["median"], st["min"]))
+    res = {"workload": "%s: B%d H%d T%d d%d chunk%d bf16, hgrn2_fwd (y and the final state)%s"
+                       % (name, B, H, T, D, C, ", float32 initial state" if h0 is not None else ""),
+           "value": B * T / (st["median"] * 1e-3), "unit": "tokens/s", "ms": st,
+           "compulsory_bytes": comp, "GBps": comp / (st["median"] * 1e-3) / 1e9,
+           "frac_hbm": comp / (st["median"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "mfma_frac": flop / (st["median"] * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)}
+    if cpu:
+        import oracle
+        x = {n: synth.to_f64(d[n], "bf16") for n in ("q", "k", "v", "log_f")}
+        h064 = None if d["h0"] is None else d["h0"].astype(np.float64)
+        t0 = time.time()
+        yr, htr = oracle.forward(x["q"], x["k"], x["v"], x["log_f"], h064)
+        dt = time.time() - t0
+        res["cpu_oracle"] = {"value": B * T / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+                             "sample": "the whole batch, forward in float64, one repetition (%.1f s)" % dt}
+        del x
+        res["parity"] = _parity({"y": y, "ht": ht}, {"y": yr, "ht": htr}, {"ht": "state"}, 2e-2)
+        log("%s parity vs oracle: %s" % (name, "pass" if res["parity"]["pass"] else "FAIL"))
+    return res
 
 
 def _csv(path):
@@ -585,6 +724,7 @@ def main():
            "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
     res = None
+    dres = None
     if args.only in ("train", "all"):
         import synth
         sets = make_train_sets(torch, synth.WORKLOADS["train_bf16"], synth.TRAIN_LAMBDAS)
@@ -593,51 +733,80 @@ def main():
         gres = bench_train(torch, m, args, sets, mode="gate")
         sres = bench_train(torch, m, args, sets, mode="scalar")
         h1res = bench_hgrn1(torch, m, args, sets)
+        del sets
         w = res["w"]
         tokens = w.B * w.T
         out["value"] = tokens / (res["ms"] * 1e-3)
         out["ms_per_step"] = res["ms"]
+        out["ms_per_step_stats"] = res["step_stats"]
         out["config"] = {"workload": "train_bf16: B8 H16 T4096 d128 chunk64 fwd(states)+bwd",
                          "global_batch": w.B, "seq_len": w.T, "heads": w.H, "head_dim": w.D,
                          "chunk": w.chunk, "parallelism": "none (1 GPU)"}
         alg = train_algorithmic_bytes(w)
+        abi = train_abi_bytes(w)
         kms = res["kernel_ms"]
-        th = w.B * w.T * w.H
-        step_flop = th * (w.chunk * 2 * w.D + 4 * w.D * w.D) + th * (5 * w.chunk * w.D + 8 * w.D * w.D)
+        step_flop = train_step_flop(w)
+        comp = train_compulsory_bytes(w)
         dom = max(kms, key=kms.get)
-        ach = alg[dom] / (kms[dom] * 1e-3) / 1e9
+        ach = abi[dom] / (kms[dom] * 1e-3) / 1e9
         kname = dict(TRAIN_KERNELS)[dom]
         out["roofline"] = {"kernel": kname, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic(dom),
-                           "ms": kms[dom], "algorithmic_bytes": alg[dom],
+                           "ms": kms[dom], "ms_stats": res["kernel_stats"][dom],
+                           "algorithmic_bytes": abi[dom],
+                           "algorithmic_bytes_counts": "the C-ABI tensors the launch reads or writes "
+                                                       "(q, k, v, log_f, dy, dq, dk, dv, dlog_f) and the "
+                                                       "chunk-boundary states",
+                           "design_bytes": alg[dom],
+                           "design_bytes_counts": "every byte the launch moves, the adjoint workspace included",
+                           "design_frac": alg[dom] / (kms[dom] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                            "source_digest": kernel_source_digest()}
-        out["kernels"] = {label: {"kernel": kn, "ms": kms[label], "bytes": alg[label],
-                                  "GBps": alg[label] / kms[label] / 1e6,
-                                  "frac_hbm": alg[label] / kms[label] / 1e6 / HBM_PEAK_GBS}
+        step_s = res["ms"] * 1e-3
+        out["step_roofline"] = {
+            "compulsory_bytes": comp, "compulsory_bytes_counts": "14 bf16 token tensors: the forward reads "
+                                                                 "q, k, v, log_f and writes y; the backward "
+                                                                 "reads q, k, v, log_f, dy and writes the four "
+                                                                 "gradients",
+            "hbm_frac": comp / step_s / 1e9 / HBM_PEAK_GBS,
+            "algorithmic_flop": step_flop,
+            "mfma_frac": step_flop / step_s / (BF16_PEAK_TFLOPS * 1e12),
+            "binding_frac": max(step_flop / (BF16_PEAK_TFLOPS * 1e12), comp / (HBM_PEAK_GBS * 1e9)) / step_s,
+            "moved_bytes": sum(alg[k_] for k_, _ in TRAIN_KERNELS),
+            # at 100% of HBM peak on the compulsory bytes, the MFMA fraction could be at most this
+            "mfma_frac_cap_at_hbm_peak": (step_flop / (BF16_PEAK_TFLOPS * 1e12)) / (comp / (HBM_PEAK_GBS * 1e9))}
+        out["kernels"] = {label: {"kernel": kn, "ms": kms[label], "ms_stats": res["kernel_stats"][label],
+                                  "bytes": abi[label], "design_bytes": alg[label],
+                                  "GBps": abi[label] / kms[label] / 1e6,
+                                  "frac_hbm": abi[label] / kms[label] / 1e6 / HBM_PEAK_GBS}
                           for label, kn in TRAIN_KERNELS}
-        out["mfma_frac_step"] = step_flop / (res["ms"] * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)
+        out["mfma_frac_step"] = out["step_roofline"]["mfma_frac"]
         tk = tres["kernel_ms"]
         out["tied"] = {"workload": "train_bf16 with tied gates (k = 1 - f): fwd(states)+bwd, total dlog_f",
                        "value": tokens / (tres["ms"] * 1e-3), "unit": "tokens/s", "ms_per_step": tres["ms"],
-                       "kernels": {label: {"kernel": kn, "ms": tk[label], "bytes": alg[label],
-                                           "GBps": alg[label] / tk[label] / 1e6,
-                                           "frac_hbm": alg[label] / tk[label] / 1e6 / HBM_PEAK_GBS}
+                       "ms_per_step_stats": tres["step_stats"],
+                       "kernels": {label: {"kernel": kn, "ms": tk[label], "ms_stats": tres["kernel_stats"][label],
+                                           "bytes": abi[label], "design_bytes": alg[label],
+                                           "GBps": abi[label] / tk[label] / 1e6,
+                                           "frac_hbm": abi[label] / tk[label] / 1e6 / HBM_PEAK_GBS}
                                    for label, kn in TIED_KERNELS}}
         gk = gres["kernel_ms"]
         out["gate"] = {"workload": "train_bf16 with the gate formed from its pre-activation z and a lower bound "
                                    "[H, D] (f = lb + (1 - lb) sigmoid(z), k = 1 - f): fwd(states)+bwd, dz and dlb",
                        "value": tokens / (gres["ms"] * 1e-3), "unit": "tokens/s", "ms_per_step": gres["ms"],
+                       "ms_per_step_stats": gres["step_stats"],
                        "calls_ms": {label: gk[label] for label, _ in GATE_CALLS}}
         sk_ = sres["kernel_ms"]
         out["scalar"] = {"workload": "train_bf16 with one decay per head (log_a [B,T,H] = the first channel's "
                                      "log f): fwd(states)+bwd, dlog_a",
                          "value": tokens / (sres["ms"] * 1e-3), "unit": "tokens/s", "ms_per_step": sres["ms"],
+                         "ms_per_step_stats": sres["step_stats"],
                          "calls_ms": {label: sk_[label] for label, _ in SCALAR_CALLS}}
         out["hgrn1"] = h1res
     if args.only in ("decode", "all"):
         dres = bench_decode(torch, m, args)
         out["decode"] = {"workload": "decode_f32: B256 H16 d128, float32 state", "ms": dres["ms"],
-                         "GBps": dres["gbs"], "frac_hbm": dres["gbs"] / HBM_PEAK_GBS,
+                         "ms_is": "the median of per-launch event times", "ms_stats": dres["stats"],
+                         "ms_loop": dres["ms_loop"], "GBps": dres["gbs"], "frac_hbm": dres["gbs"] / HBM_PEAK_GBS,
                          "bytes": dres["bytes"]}
         if res is None:
             out["value"] = dres["gbs"]
@@ -645,6 +814,24 @@ def main():
             out["unit"] = "GB/s"
             out["ms_per_step"] = dres["ms"]
             out["config"] = {"workload": "decode_f32: B256 H16 d128"}
+    for name in ("fwd_bf16", "long_bf16"):
+        if args.only in (name, "all"):
+            out[name] = bench_fwd_only(torch, m, args, name, cpu=not args.no_cpu)
+            if res is None and dres is None and args.only == name:
+                out["metric"] = "fwd tokens/s (%s)" % name
+                out["value"] = out[name]["value"]
+                out["ms_per_step"] = out[name]["ms"]["median"]
+                out["config"] = {"workload": out[name]["workload"]}
+    if res is not None:
+        t = {"train_mfma_frac": {"want": 0.40, "got": out["step_roofline"]["mfma_frac"],
+                                 "met": out["step_roofline"]["mfma_frac"] >= 0.40,
+                                 "cap_at_hbm_peak": out["step_roofline"]["mfma_frac_cap_at_hbm_peak"],
+                                 "why": "the step is bound by HBM bytes: even its compulsory bytes at 100% of "
+                                        "HBM peak leave the matrix cores below the wanted fraction"}}
+        if dres is not None:
+            fr = dres["gbs"] / HBM_PEAK_GBS
+            t["decode_hbm_frac"] = {"want": 0.70, "got": fr, "met": fr >= 0.70}
+        out["target"] = t
     if args.calib_copy:
         # torch's elementwise multiply: a grid over every XCD reading 1 GiB and
         # writing 1 GiB (the runtime's copy kernel has been seen to spread over

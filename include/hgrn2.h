@@ -36,8 +36,11 @@
  *     ceil(T / chunk) and E the element size a call returns
  *     HGRN2_ERR_INVALID_ARG ("problem too large") unless B*H*N < 2^31,
  *     chunk*H*D*E < 2^32 and (N + 1)*D*D*E < 2^32 (bf16, D = 128: T up to
- *     about 8.4 million tokens per sequence at chunk 64), B*H <= 2^30 and
- *     B*T*H <= 2^40.
+ *     about 8.4 million tokens per sequence at chunk 64), B*H <= 2^30,
+ *     B*T*H <= 2^40, and every kernel the call launches has fewer than 2^32
+ *     work-items (the dispatch counts them in 32 bits): B*H*N*4*chunk for the
+ *     chunk kernels, ceil(B*H/8)*8 times at most 2048 (D = 128, chunk 128)
+ *     for the state scans, B*H times min(D*D/4, 256) for the decode step.
  *   - Gate precondition: log_f <= 0 and not NaN.  -inf (f = 0) is allowed;
  *     kernels floor log_f at -200, where exp() is already 0 in float32.
  *   - Errors: arguments are checked before anything is launched; on an

@@ -25,6 +25,10 @@ bool valid_dtype(int t) { return t == HGRN2_F32 || t == HGRN2_BF16; }
 size_t dsize(int t) { return t == HGRN2_BF16 ? 2 : 4; }
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// A launch's work-items (workgroups times their size) are counted in 32 bits
+// by the dispatch packet, so every kernel's total must stay within this.
+constexpr long long kMaxItems = 0xffffffffLL;
+
 struct Range {
   const char *name;
   const void *p;
@@ -73,6 +77,14 @@ hgrn2_status check_common(int B, int T, int H, int DK, int DV, int chunk, int dt
   if (DK != DV || !valid_d(DK))
     return fail(HGRN2_ERR_UNSUPPORTED, "need DK == DV in {16, 32, 64, 128}");
   if (!valid_chunk(chunk)) return fail(HGRN2_ERR_UNSUPPORTED, "chunk must be 16, 32 or 64");
+  {
+    // work-items of the state scans (workgroups of eight (b, h) at a time) and
+    // of the chunk kernels (one workgroup per chunk)
+    const long long BH = (long long)B * H, N = (T + (long long)chunk - 1) / chunk;
+    const long long scan = (BH + 7) / 8 * 8 * hgrn2::scan_items_per_bh(dtype, DK, chunk);
+    const long long chunks = BH * N * hgrn2::chunk_items_per_chunk(chunk);
+    if (scan > kMaxItems || chunks > kMaxItems) return fail(HGRN2_ERR_INVALID_ARG, "problem too large");
+  }
   return HGRN2_OK;
 }
 
@@ -328,6 +340,9 @@ static hgrn2_status bwd_impl(int gm, const char *fn, int B, int T, int H, int DK
   const size_t lamb = adjoint_bytes(B, T, H, DK, DV, chunk, dtype);
   const size_t partb = gm == kGate ? dlb_part_bytes(B, T, H, DK, chunk) : 0;
   const size_t need = lamb + partb + (states_in ? 0 : stb);
+  // the lower-bound sum runs H * (DK / min(DK, 64)) workgroups of 1024 work-items
+  if (gm == kGate && (long long)H * (DK / (DK < 64 ? DK : 64)) * 1024 > kMaxItems)
+    return fail(HGRN2_ERR_INVALID_ARG, "problem too large");
   if (!ws || ws_bytes < need)
     return fail(HGRN2_ERR_WORKSPACE, "workspace smaller than hgrn2_bwd_workspace_bytes()");
   if (!reads_k(gm)) k = dk = nullptr;
@@ -417,6 +432,8 @@ static hgrn2_status decode_impl(int gm, const char *fn, int B, int H, int DK, in
   if ((long long)B * H > (1LL << 30)) return fail(HGRN2_ERR_INVALID_ARG, "problem too large");
   if (!valid_dtype(dtype)) return fail(HGRN2_ERR_INVALID_ARG, "dtype must be HGRN2_F32 or HGRN2_BF16");
   if (DK != DV || !valid_d(DK)) return fail(HGRN2_ERR_UNSUPPORTED, "need DK == DV in {16, 32, 64, 128}");
+  // one workgroup per (b, h)
+  if ((long long)B * H * hgrn2::decode_items_per_bh(DK) > kMaxItems) return fail(HGRN2_ERR_INVALID_ARG, "problem too large");
   hgrn2_status st = check_ptrs({{"q", q}, {"v", v}, {gate_name(gm), log_f}, {"state", state}, {"y", y}}, {});
   if (st == HGRN2_OK) st = need_k(gm, k, "k");
   if (st == HGRN2_OK) st = need_lb(gm, lb, "lower_bound");
@@ -600,6 +617,16 @@ static hgrn2_status h1_check(int B, int T, int C, int dtype, int tied) {
   if (32LL * C * (dtype == HGRN2_F32 ? 4 : 2) >= (1LL << 32)) return fail(HGRN2_ERR_INVALID_ARG, "problem too large");
   if (tied != 0 && tied != 1) return fail(HGRN2_ERR_INVALID_ARG, "tied must be 0 or 1");
   if (C % 2 != 0) return fail(HGRN2_ERR_UNSUPPORTED, "C must be even");
+  {
+    // work-items of the three passes: summaries (B * groups * ceil(C/128)
+    // workgroups of 64 * kH1Grp), carries (B * ceil(C/256) of 256) and the
+    // segment pass (B * segments * ceil(C/512) of kH1Pairs)
+    const long long S = hgrn2::h1_segments(T), NG = hgrn2::h1_groups((int)S), P = C / 2;
+    const long long sum = (long long)B * NG * ((P + 63) / 64) * 64 * hgrn2::kH1Grp;
+    const long long carry = (long long)B * ((C + 255) / 256) * 256;
+    const long long seg = (long long)B * S * ((P + hgrn2::kH1Pairs - 1) / hgrn2::kH1Pairs) * hgrn2::kH1Pairs;
+    if (sum > kMaxItems || carry > kMaxItems || seg > kMaxItems) return fail(HGRN2_ERR_INVALID_ARG, "problem too large");
+  }
   return HGRN2_OK;
 }
 

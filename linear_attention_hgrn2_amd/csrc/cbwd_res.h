@@ -762,13 +762,11 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
   }
 }
 
-inline int res_grid(int nchunks) {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    cus = 256;
-  return nchunks < cus ? nchunks : cus;
-}
+// One persistent workgroup per compute unit: gfx950 parts have 256.  The walk
+// over chunks strides by the grid and does not depend on how many workgroups
+// are resident at once, so no device query is needed at launch.
+constexpr int kResGrid = 256;
+inline int res_grid(int nchunks) { return nchunks < kResGrid ? nchunks : kResGrid; }
 
 template <int GM>
 hipError_t launch_chunk_bwd_res(const ChunkBwdArgs &a, hipStream_t stream) {

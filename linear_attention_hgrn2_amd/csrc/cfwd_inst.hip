@@ -19,4 +19,9 @@ hipError_t dispatch_chunk_fwd(int dtype, int D, int C, int gm, const ChunkFwdArg
   return run_config<ChunkFwdOp>(dtype, D, C, gm, a, s);
 }
 
+// one workgroup of 4 C work-items per chunk (the chunk forward and the
+// non-resident chunk backward alike; the resident backward launches at most
+// one workgroup per compute unit)
+long long chunk_items_per_chunk(int C) { return 4LL * C; }
+
 }  // namespace hgrn2

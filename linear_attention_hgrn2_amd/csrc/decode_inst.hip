@@ -31,6 +31,16 @@ hipError_t dispatch_decode(int dtype, int D, int gm, const DecodeArgs &a, hipStr
   return hipErrorNotSupported;
 }
 
+long long decode_items_per_bh(int D) {
+  switch (D) {
+    case 16: return DecodeCfg<16>::NT;
+    case 32: return DecodeCfg<32>::NT;
+    case 64: return DecodeCfg<64>::NT;
+    case 128: return DecodeCfg<128>::NT;
+  }
+  return 0;
+}
+
 hipError_t dispatch_dlb_reduce(int B, int H, int N, int D, const float *part, float *dlb, hipStream_t s) {
   switch (D) {
     case 16: return launch_dlb_reduce<16>(B, H, N, part, dlb, s);

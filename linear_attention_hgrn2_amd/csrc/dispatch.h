@@ -56,4 +56,12 @@ hipError_t dispatch_dlb_reduce(int B, int H, int N, int D, const float *part, fl
 enum H1Op : int { kH1SummaryFwd, kH1SummaryRev, kH1CarryFwd, kH1CarryRev, kH1FinalFwd, kH1FinalBwd };
 hipError_t dispatch_hgrn1(int op, int dtype, int gm, const H1Args &a, hipStream_t s);
 
+// Launch geometry, for the size checks that run before anything is launched:
+// work-items per (b, h) of the state scan (its workgroups for one (b, h) are
+// padded to groups of eight (b, h)), per chunk of the chunk kernels, and per
+// (b, h) of the decode step; 0 when no kernel exists.
+long long scan_items_per_bh(int dtype, int D, int C);
+long long chunk_items_per_chunk(int C);
+long long decode_items_per_bh(int D);
+
 }  // namespace hgrn2

@@ -360,10 +360,11 @@ __global__ __launch_bounds__(kH1Pairs) void hgrn1_final_bwd_kernel(H1Args a) {
 
 inline int h1_segments(int T) { return (T + kH1Seg - 1) / kH1Seg; }
 inline int h1_groups(int S) { return (S + kH1Grp - 1) / kH1Grp; }
-inline dim3 h1_sum_grid(const H1Args &a) { return dim3((unsigned)(a.B * a.NG * ((a.C / 2 + 63) / 64))); }
+// grids in 64-bit arithmetic (the C ABI rejects sizes whose work-items pass 32 bits)
+inline dim3 h1_sum_grid(const H1Args &a) { return dim3((unsigned)((long long)a.B * a.NG * ((a.C / 2 + 63) / 64))); }
 inline dim3 h1_seg_grid(const H1Args &a) {
-  return dim3((unsigned)(a.B * a.S * ((a.C / 2 + kH1Pairs - 1) / kH1Pairs)));
+  return dim3((unsigned)((long long)a.B * a.S * ((a.C / 2 + kH1Pairs - 1) / kH1Pairs)));
 }
-inline dim3 h1_chan_grid(const H1Args &a) { return dim3((unsigned)(a.B * ((a.C + 255) / 256))); }
+inline dim3 h1_chan_grid(const H1Args &a) { return dim3((unsigned)((long long)a.B * ((a.C + 255) / 256))); }
 
 }  // namespace hgrn2

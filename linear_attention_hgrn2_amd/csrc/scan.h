@@ -273,8 +273,9 @@ template <typename T, int D, int C, bool REV, int GM = kUntied>
 hipError_t launch_scan(const ScanArgs &a, hipStream_t stream) {
   static_assert(!(REV && GM == kTied), "the adjoint scan reads q, not k: run it untied");
   using Cfg = ScanCfg<T, D, C, REV>;
-  const int groups = (a.B * a.H + 7) / 8;
-  hipLaunchKernelGGL((hgrn2_scan_kernel<T, D, C, REV, GM>), dim3(groups * 8 * Cfg::NS), dim3(Cfg::NT), 0, stream, a);
+  const long long groups = ((long long)a.B * a.H + 7) / 8;
+  hipLaunchKernelGGL((hgrn2_scan_kernel<T, D, C, REV, GM>), dim3((unsigned)(groups * 8 * Cfg::NS)), dim3(Cfg::NT), 0,
+                     stream, a);
   return hipGetLastError();
 }
 

@@ -25,4 +25,17 @@ hipError_t dispatch_scan(int dtype, int D, int C, bool reverse, int gm, const Sc
   return run_config<ScanOp>(dtype, D, C, reverse, gm, a, s);
 }
 
+template <typename T, int D, int C> struct ScanItemsOp {
+  static hipError_t run(long long *n) {
+    using Cfg = ScanCfg<T, D, C, false>;
+    *n = (long long)Cfg::NS * Cfg::NT;
+    return hipSuccess;
+  }
+};
+
+long long scan_items_per_bh(int dtype, int D, int C) {
+  long long n = 0;
+  return run_config<ScanItemsOp>(dtype, D, C, &n) == hipSuccess ? n : 0;
+}
+
 }  // namespace hgrn2

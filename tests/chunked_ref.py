@@ -171,3 +171,56 @@ def backward(q, k, v, log_f, dy, h0=None, dht=None, C=64, SB=16):
                     o[b, t0:t1, h] = val[:Lt]
             dh0[b, h] = Lam
     return (*out, dh0)
+
+
+def _bf16(x):
+    """Round to the nearest bfloat16 (ties to even), as float64."""
+    x32 = np.ascontiguousarray(x, dtype=np.float32)
+    u = x32.view(np.uint32).astype(np.uint64)
+    r = ((u + ((u >> 16) & 1) + 0x7FFF) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def forward_bf16_points(q, k, v, log_f, C=64, SB=16, round_operands=True):
+    """y of one sequence ([T, D] float64 inputs, zero initial state) by the
+    chunk forward's arithmetic with bfloat16 rounding where the bf16 kernels
+    round: the decayed score operands q e^{ell}, k e^{L - ell} (and k e^{ell}
+    times its gap factor off the adjacent blocks), the score tile, the state
+    and the inter-chunk operand, the scan's decayed k, and y.
+    round_operands=False keeps the decayed q and k operands (and the scan's
+    decayed k) in float64 and rounds the rest.  Diagonal blocks wider than
+    DIAG_LIMIT are not modelled (the workloads here have none)."""
+    T, D = q.shape
+    N = (T + C - 1) // C
+    R = _bf16 if round_operands else (lambda x: x)
+    y = np.zeros((T, D))
+    S = np.zeros((D, D))
+    NB = C // SB
+    for n in range(N):
+        t0, t1 = n * C, min(T, (n + 1) * C)
+        Lt = t1 - t0
+        qc, kc, vc, lc = (np.zeros((C, D)) for _ in range(4))
+        qc[:Lt], kc[:Lt], vc[:Lt] = q[t0:t1], k[t0:t1], v[t0:t1]
+        lc[:Lt] = np.maximum(log_f[t0:t1], FLOOR)
+        ell, L, P, G = _chunk_prefix(lc, SB)
+        assert (-L).max() <= DIAG_LIMIT
+        qo = R(qc * np.exp(ell))
+        ko = R(kc * np.exp(np.repeat(L, SB, 0) - ell))
+        A = np.zeros((C, C))
+        for i in range(NB):
+            ti = slice(i * SB, (i + 1) * SB)
+            for j in range(i + 1):
+                sj = slice(j * SB, (j + 1) * SB)
+                if j == i - 1:
+                    kt = ko[sj]                                  # gap factor exactly 1
+                else:
+                    gap = np.exp(np.minimum(-L[i], 80.0)) if j == i else np.exp(P[i] - P[j + 1])
+                    kt = R(ko[sj] * gap)
+                blk = qo[ti] @ kt.T
+                A[ti, sj] = np.tril(blk) if j == i else blk
+        qb = R(qo * np.exp(np.repeat(P, SB, 0)))
+        Y = _bf16(A) @ vc + qb @ _bf16(S)
+        xd = R(kc * np.exp(np.minimum(G - np.cumsum(lc, 0), 0.0)))
+        S = np.exp(G)[:, None] * S + xd.T @ vc
+        y[t0:t1] = _bf16(Y)[:Lt]
+    return y

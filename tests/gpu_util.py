@@ -1,5 +1,41 @@
 """Helpers shared by the GPU parity tests: move synthetic inputs to the GPU,
-run the oracle on the same values, compare slice by slice."""
+run the oracle on the same values, compare them.
+
+Comparison metrics (all three must be <= the dtype's tolerance, TOL):
+  norm  the largest normwise relative error over slices,
+        ||gpu - ref||_F / ||ref||_F;
+  row   the largest error of one row (one token's D values of a head, one
+        token's C channels, one state row), relative to that row's reference
+        norm plus the slice's root-mean-square row norm:
+        ||gpu_t - ref_t|| / (||ref_t|| + rms_t ||ref_t||);
+  elem  the largest error of one element, relative to its reference value
+        plus three times the typical magnitude around it, the larger of its
+        row's and its slice's root-mean-square value:
+        |gpu - ref| / (|ref| + 3 max(rms(ref_t), rms(ref))).
+A slice is one (b, h) sequence of a [B, T, H, D] tensor, one (b, h) matrix of
+a [B, H, D, D] state, or one (b, c) channel sequence of a [B, T, C] tensor.
+The row and element terms catch localised errors that a slice norm over
+hundreds of thousands of values would hide (one wrong token row of a 4096-token
+slice moves its norm by only about 1/64).
+
+The element scale follows the magnitude of the element's own row because
+magnitudes, and the rounding noise that comes with them, vary along a
+sequence: a decaying initial state makes the first thousand outputs of the
+long-context workload about ten times larger than the later ones.  The factor
+3 comes from the bf16 paths' arithmetic: the decayed q and k enter the score
+products as bf16 operands (relative rounding 2^-9 each), so an output that is a
+near-cancellation of terms several times its row's magnitude carries an error
+of a few percent of that magnitude.  Over the 67 million elements of a full
+training batch the largest such error is 4.2% of its row's rms (the element
+metric with factor 2 gave 2.1e-2); a float64 emulation of the kernels'
+rounding points reproduces that element's error exactly, and removing the
+operand roundings from the emulation removes it.  With 3, the threshold for an
+element whose true value is near zero is 6% of its neighbourhood's magnitude,
+1.4 times that extreme, while an element off by more than 6% of its
+neighbourhood's magnitude (or 2% of its own value) fails.  A slice whose
+reference is exactly zero is compared in absolute terms.  Any NaN or infinity
+in the GPU result fails.
+"""
 
 from __future__ import annotations
 
@@ -24,31 +60,87 @@ def to_host64(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def slice_rel(got: np.ndarray, ref: np.ndarray, token_major=True) -> float:
-    """Largest normwise relative error over (b, h) slices (inf if the GPU
-    result holds a NaN or an infinity).
+def _nz(x):
+    """Denominators: zero (an all-zero reference) becomes one (absolute error)."""
+    return np.where(x > 0, x, 1.0)
 
-    token tensors are [B,T,H,D]; state tensors [B,H,D,D]."""
+
+def errors(got: np.ndarray, ref: np.ndarray, layout: str = "token") -> dict:
+    """The three metrics above for `got` against `ref`.
+
+    layout: "token" [B, T, H, D] (slices (b, h), rows = tokens), "state"
+    [B, H, D, D] (slices (b, h), rows = state rows), "btc" [B, T, C] (slices
+    (b, c), rows = tokens of one batch element)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
     if not np.all(np.isfinite(got)):
-        return float("inf")
-    worst = 0.0
-    if token_major:
-        B, _, H, _ = ref.shape
-        for b in range(B):
-            for h in range(H):
-                r = ref[b, :, h]
-                d = np.linalg.norm(got[b, :, h] - r)
-                n = np.linalg.norm(r)
-                worst = max(worst, d / n if n > 0 else d)
+        return {"norm": float("inf"), "row": float("inf"), "elem": float("inf"), "elem_at": "non-finite"}
+    if got.size == 0:
+        return {"norm": 0.0, "row": 0.0, "elem": 0.0, "elem_at": ""}
+    d = got - ref
+    if layout == "token":       # [B, T, H, D]
+        s_ax, r_ax = (1, 3), 3
+        slice_b = lambda x: x[:, None, :, None]      # [B, H] -> broadcast over [B, T, H, D]
+        row_b = lambda x: x[:, None, :]              # [B, H] -> broadcast over rows [B, T, H]
+    elif layout == "state":     # [B, H, D, D]
+        s_ax, r_ax = (2, 3), 3
+        slice_b = lambda x: x[:, :, None, None]
+        row_b = lambda x: x[:, :, None]
+    elif layout == "btc":       # [B, T, C]: slices (b, c) along T; rows = tokens of b
+        B, T, C = ref.shape
+        n = np.sqrt((d * d).sum(axis=1))             # [B, C]
+        rn = np.sqrt((ref * ref).sum(axis=1))
+        norm = float(np.max(n / _nz(rn)))
+        rms = rn / np.sqrt(T)
+        re = np.sqrt((d * d).sum(axis=2))            # [B, T]
+        rr = np.sqrt((ref * ref).sum(axis=2))
+        rs = np.sqrt((rr * rr).mean(axis=1))         # [B]
+        row = float(np.max(re / _nz(rr + rs[:, None])))
+        scale = np.maximum(rms[:, None, :], (rr / np.sqrt(C))[:, :, None])
+        return {"norm": norm, "row": row, **_elem(d, ref, scale)}
     else:
-        B, H = ref.shape[:2]
-        for b in range(B):
-            for h in range(H):
-                r = ref[b, h]
-                d = np.linalg.norm(got[b, h] - r)
-                n = np.linalg.norm(r)
-                worst = max(worst, d / n if n > 0 else d)
-    return float(worst)
+        raise ValueError(layout)
+    n = np.sqrt((d * d).sum(axis=s_ax))
+    rn = np.sqrt((ref * ref).sum(axis=s_ax))
+    norm = float(np.max(n / _nz(rn)))
+    count = ref.shape[s_ax[0]] * ref.shape[s_ax[1]]
+    rms = rn / np.sqrt(count)
+    re = np.sqrt((d * d).sum(axis=r_ax))
+    rr = np.sqrt((ref * ref).sum(axis=r_ax))
+    nrows = ref.shape[s_ax[0]]
+    rs = rn / np.sqrt(nrows)                         # rms row norm of the slice
+    row = float(np.max(re / _nz(rr + row_b(rs))))
+    width = ref.shape[r_ax]
+    scale = np.maximum(slice_b(rms), (rr / np.sqrt(width))[..., None])
+    return {"norm": norm, "row": row, **_elem(d, ref, scale)}
+
+
+def _elem(d, ref, scale):
+    """The element metric, and where its worst element is (index, error,
+    reference, scale) for the report."""
+    scale = np.broadcast_to(scale, ref.shape)
+    ratio = np.abs(d) / _nz(np.abs(ref) + 3.0 * scale)
+    i = int(np.argmax(ratio))
+    at = np.unravel_index(i, ref.shape)
+    return {"elem": float(ratio.flat[i]),
+            "elem_at": "%s err %.2e ref %.2e scale %.2e" % (tuple(int(a) for a in at), d.flat[i], ref.flat[i],
+                                                             scale.flat[i])}
+
+
+def worst(e: dict) -> float:
+    return max(e["norm"], e["row"], e["elem"])
+
+
+def fmt(e: dict) -> str:
+    return "norm %.2e row %.2e elem %.2e [%s]" % (e["norm"], e["row"], e["elem"], e.get("elem_at", ""))
+
+
+def slice_rel(got: np.ndarray, ref: np.ndarray, token_major=True) -> float:
+    """The worst of the three metrics (normwise per slice, per row, per
+    element) for a [B, T, H, D] (token_major) or [B, H, D, D] tensor; compared
+    against TOL by the tests."""
+    return worst(errors(got, ref, "token" if token_major else "state"))
 
 
 def inputs64(d: dict):

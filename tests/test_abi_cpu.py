@@ -265,3 +265,28 @@ def test_size_limits(lib):
     assert lib.hgrn1_fwd(1, 1, 1 << 25, 0, 1, P[0], None, P[2], P[3], None, P[4], None, None, P[9], 1 << 62,
                          None) == 1
     assert b"too large" in lib.hgrn2_last_error()
+
+
+def test_launch_work_items_fit_32_bits(lib):
+    """Every launch's work-items (workgroups times their size) must fit the
+    dispatch's 32-bit count; cases that pass the older per-dimension limits."""
+    big = dict(ws=FAKE + 0x10000000, wsb=1 << 62)
+    # chunk kernels: B*H*N = 2^24 < 2^31, but 2^24 workgroups of 4 * 64 work-items = 2^32
+    assert _fwd(lib, B=1 << 10, H=1 << 7, T=128 * 64, chunk=64, **big) == 1
+    assert b"too large" in lib.hgrn2_last_error()
+    # 127/128 of it fits the size checks and stops at the next one (y overlaps q): no launch
+    assert _fwd(lib, B=1 << 10, H=1 << 7, T=127 * 64, chunk=64, **big) == 1
+    assert b"overlaps" in lib.hgrn2_last_error()
+    # state scan: B*H = 2^24 (b, h) of 4 slices x 64 work-items (D = 128, chunk 16, float32) = 2^32,
+    # while the chunk kernels (2^24 x 64) fit
+    assert _fwd(lib, B=1 << 12, H=1 << 12, T=1, DK=128, DV=128, chunk=16, **big) == 1
+    assert b"too large" in lib.hgrn2_last_error()
+    # decode: 2^25 (b, h) of 256 work-items
+    P = [FAKE + i * 0x100000 for i in range(8)]
+    assert lib.hgrn2_decode_step(1 << 12, 1 << 13, 32, 32, 0, P[0], P[1], P[2], P[3], P[4], P[5], None) == 1
+    assert b"too large" in lib.hgrn2_last_error()
+    # HGRN1 segment pass: B * 8 segments * 32 workgroups of 256 = 2^32 (B = 2^16, C = 2^14, T = 256)
+    P = [FAKE + i * 0x100000 for i in range(16)]
+    assert lib.hgrn1_fwd(1 << 16, 256, 1 << 14, 0, 1, P[0], None, P[2], P[3], None, P[4], None, None, P[9],
+                         1 << 62, None) == 1
+    assert b"too large" in lib.hgrn2_last_error()

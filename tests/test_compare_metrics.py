@@ -1,0 +1,76 @@
+"""The comparison metrics of the GPU parity tests (tests/gpu_util.py) on
+planted errors, on the CPU: a slice norm over thousands of tokens misses one
+wrong token row and one wrong element; the row and element terms do not."""
+import numpy as np
+
+from tests.gpu_util import TOL, errors, worst
+
+
+def _ref(shape, seed=0):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def test_identical_is_zero():
+    r = _ref((2, 64, 3, 16))
+    e = errors(r.copy(), r)
+    assert (e["norm"], e["row"], e["elem"]) == (0.0, 0.0, 0.0)
+
+
+def test_one_wrong_token_row_is_caught_by_the_row_term():
+    r = _ref((2, 4096, 2, 128))
+    g = r.copy()
+    g[1, 1234, 0] = 0.0                      # one token row of one (b, h) lost
+    e = errors(g, r)
+    assert e["norm"] <= TOL["bf16"]          # 1/64 of the slice norm: the norm alone passes it
+    assert e["row"] > 0.4 and worst(e) > TOL["bf16"]
+
+
+def test_one_wrong_element_is_caught_by_the_element_term():
+    r = _ref((1, 512, 1, 64))
+    g = r.copy()
+    i = np.argmax(np.abs(r))
+    g.flat[i] *= 1.05                        # 5% off on a large element
+    e = errors(g, r)
+    assert e["norm"] < TOL["bf16"] and e["row"] < TOL["bf16"]
+    assert e["elem"] > TOL["bf16"]
+
+
+def test_rounding_noise_at_bf16_scale_passes():
+    """Noise of 5e-3 of the slice rms on every element (the size of the bf16
+    paths' normwise errors) over 8 million elements stays under the bound."""
+    r = _ref((4, 4096, 4, 128))
+    g = r + 5e-3 * np.random.default_rng(1).standard_normal(r.shape)
+    assert worst(errors(g, r)) <= TOL["bf16"]
+
+
+def test_element_scale_follows_its_row():
+    """Rows ten times larger than the rest of the slice (a decaying initial
+    state) carry rounding noise ten times larger: measured against their own
+    row's magnitude, not the slice's."""
+    r = _ref((1, 4096, 1, 128))
+    r[:, :300] *= 10.0
+    noise = 4e-3 * np.random.default_rng(2).standard_normal(r.shape)
+    noise[:, :300] *= 10.0
+    assert worst(errors(r + noise, r)) <= TOL["bf16"]
+
+
+def test_state_and_channel_layouts():
+    r = _ref((2, 3, 16, 16))
+    g = r.copy()
+    g[1, 2, 5] += 0.5                        # one state row
+    e = errors(g, r, "state")
+    assert e["row"] > TOL["bf16"] and e["elem"] > TOL["bf16"]
+    r = _ref((2, 300, 8))
+    g = r.copy()
+    g[0, 17, 3] = -g[0, 17, 3]               # one element of one channel sequence
+    assert errors(g, r, "btc")["elem"] > TOL["bf16"]
+
+
+def test_nonfinite_fails_and_zero_reference_is_absolute():
+    r = _ref((1, 8, 1, 4))
+    g = r.copy()
+    g[0, 3, 0, 1] = np.nan
+    assert worst(errors(g, r)) == float("inf")
+    z = np.zeros((1, 8, 1, 4))
+    e = errors(z + 1e-9, z)
+    assert worst(e) < 1e-8

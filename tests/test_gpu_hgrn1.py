@@ -1,13 +1,15 @@
 """GPU parity of the HGRN1 elementwise recurrence (hgrn1_fwd / hgrn1_bwd over
 [B, T, C]) against the float64 oracle's HGRN1 functions (the step loop with
-one channel per head), on the same seeded inputs.  Normwise relative error per
-batch element and tensor <= 2e-2 (bf16), <= 1e-4 (fp32)."""
+one channel per head), on the same seeded inputs.  Every channel sequence,
+token row and element is compared (tests/gpu_util.py, layout "btc"; the final
+states [B, C] per batch element and per channel): <= 2e-2 (bf16), <= 1e-4
+(fp32)."""
 import numpy as np
 import pytest
 
 import oracle
 import synth
-from tests.gpu_util import TOL, to_dev, to_host64
+from tests.gpu_util import TOL, errors, fmt, to_dev, to_host64, worst
 
 pytestmark = pytest.mark.gpu
 
@@ -27,10 +29,14 @@ def _inputs(dtype, B, T, C, lam=0.3, seed=5):
     return out
 
 
-def _rel_per_b(a, b):
-    a = np.asarray(a, np.float64).reshape(a.shape[0], -1)
-    b = np.asarray(b, np.float64).reshape(b.shape[0], -1)
-    return float(max(np.linalg.norm(a[i] - b[i]) / max(np.linalg.norm(b[i]), 1e-300) for i in range(a.shape[0])))
+def _err(a, b):
+    """errors() of a [B, T, C] token tensor ("btc") or a [B, C] state (one
+    slice per batch element, one row per channel)."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    if a.ndim == 2:
+        return errors(a[:, None, :, None], b[:, None, :, None], "state")
+    return errors(a, b, "btc")
 
 
 def _run(x, tied, with_states=True):
@@ -52,14 +58,14 @@ def _check(x, tied, label=""):
     h0, dht = x["h0"].astype(np.float64), x["dht"].astype(np.float64)
     yr, htr = oracle.hgrn1_forward(f["q"], f["k"], f["v"], f["log_f"], h0, tied=tied)
     gr = oracle.hgrn1_backward(f["q"], f["k"], f["v"], f["log_f"], f["dy"], h0, dht, tied=tied)
-    errs = {"y": _rel_per_b(to_host64(y), yr), "hT": _rel_per_b(to_host64(ht), htr)}
+    errs = {"y": _err(to_host64(y), yr), "hT": _err(to_host64(ht), htr)}
     for name, a, r in zip(("dq", "dk", "dv", "dlog_f", "dh0"), (dq, dk, dv, dl, dh0), gr):
         if r is not None:
-            errs[name] = _rel_per_b(to_host64(a), r)
+            errs[name] = _err(to_host64(a), r)
     print("%s hgrn1 %s %s tied=%d: %s" % (label, dt, tuple(x["q"].shape), tied,
-                                          " ".join("%s %.3e" % e for e in errs.items())), flush=True)
+                                          "; ".join("%s %s" % (n, fmt(e)) for n, e in errs.items())), flush=True)
     for name, e in errs.items():
-        assert e <= TOL[dt], (name, e)
+        assert worst(e) <= TOL[dt], (name, e)
 
 
 @pytest.mark.parametrize("tied", [False, True])
@@ -92,9 +98,9 @@ def test_hgrn1_saved_states_equal_recomputed_and_repeat_is_bitwise():
         assert (u is None and w is None) or torch.equal(u, w)
 
 
-def test_hgrn1_full_size_sampled_channels():
+def test_hgrn1_full_size_all_channels():
     """B8 T4096 C2048 (the training workload's H16 x d128 channels), bf16, tied,
-    as the benchmark runs it; the oracle recomputes 48 sampled channels."""
+    as the benchmark runs it; the oracle recomputes every channel."""
     import torch
     import linear_attention_hgrn2_amd as m
     d = synth.generate("train_bf16", lam=0.3)
@@ -104,13 +110,14 @@ def test_hgrn1_full_size_sampled_channels():
     y, ht, st = m.hgrn1_fwd(q, None, v, lf, None, tied=True, want_states=True)
     dq, _, dv, dl, _ = m.hgrn1_bwd(q, None, v, lf, dy, None, None, st, tied=True, want_dh0=False)
     torch.cuda.synchronize()
-    ch = np.sort(np.random.default_rng(3).choice(C, size=48, replace=False))
-    f = {n: synth.to_f64(np.ascontiguousarray(x[n][:, :, ch]), "bf16") for n in ("q", "v", "log_f", "dy")}
+    f = {n: synth.to_f64(x[n], "bf16") for n in ("q", "v", "log_f", "dy")}
     yr, htr = oracle.hgrn1_forward(f["q"], None, f["v"], f["log_f"], None, tied=True)
+    errs = {"y": _err(to_host64(y), yr), "hT": _err(to_host64(ht), htr)}
+    del yr
     gr = oracle.hgrn1_backward(f["q"], None, f["v"], f["log_f"], f["dy"], None, None, tied=True)
-    errs = {"y": _rel_per_b(to_host64(y)[:, :, ch], yr), "hT": _rel_per_b(to_host64(ht)[:, ch], htr)}
     for name, a, r in zip(("dq", "dv", "dlog_f"), (dq, dv, dl), (gr[0], gr[2], gr[3])):
-        errs[name] = _rel_per_b(to_host64(a)[:, :, ch], r)
-    print("hgrn1 full size: %s" % " ".join("%s %.3e" % e for e in errs.items()), flush=True)
+        errs[name] = _err(to_host64(a), r)
+    print("hgrn1 full size, all %d channels: %s" % (B * C, "; ".join("%s %s" % (n, fmt(e)) for n, e in errs.items())),
+          flush=True)
     for name, e in errs.items():
-        assert e <= TOL["bf16"], (name, e)
+        assert worst(e) <= TOL["bf16"], (name, e)

@@ -76,9 +76,11 @@ def test_fwd_tiny_f32_workload():
     _fwd_check(d, 16, "tiny_f32")
 
 
+ALL_DC = [(D, C) for D in (16, 32, 64, 128) for C in (16, 32, 64, 128)]
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("D,C", [(16, 16), (16, 64), (32, 32), (64, 16), (64, 64), (128, 16),
-                                 (128, 32), (128, 64)])
+@pytest.mark.parametrize("D,C", ALL_DC)
 def test_fwd_shapes(dtype, D, C):
     import linear_attention_hgrn2_amd as m
     import torch
@@ -119,7 +121,7 @@ def test_fwd_ht_aliases_h0():
 # ----------------------------------------------------------------- backward
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("D,C", [(16, 16), (32, 32), (64, 16), (64, 64), (128, 16), (128, 64)])
+@pytest.mark.parametrize("D,C", ALL_DC)
 def test_bwd_shapes(dtype, D, C):
     import linear_attention_hgrn2_amd as m
     import torch
