@@ -151,6 +151,28 @@ hgrn2_status hgrn2_bwd(int B, int T, int H, int DK, int DV, int chunk, int dtype
                        float *dh0, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * hgrn2_bwd without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight training or serving loops,
+ * harnesses that forbid allocation).  Same arguments, checks, kernels and
+ * results as hgrn2_bwd (bit for bit), except ws and ws_bytes: the adjoints (and
+ * the recomputed chunk-boundary states when states_in is NULL) go to a
+ * scratch array of HGRN2_NOALLOC_SCRATCH_BYTES bytes that the library holds on
+ * every GPU it runs on until the process ends (256 MiB: the adjoints of
+ * B8 H16 T4096 at D = 128, chunk 64, bf16, with the states passed in).  A call
+ * that needs more returns HGRN2_ERR_WORKSPACE before anything is enqueued.
+ * The call itself allocates nothing.  Every call on one GPU uses that GPU's
+ * one scratch array: calls that overlap in time on one GPU (other streams,
+ * other threads) race and must be serialised by the caller; consecutive calls
+ * on one stream are safe.  Nothing in the scratch needs to start at zero.
+ */
+#define HGRN2_NOALLOC_SCRATCH_BYTES (256u << 20)
+hgrn2_status hgrn2_bwd_noalloc(int B, int T, int H, int DK, int DV, int chunk, int dtype,
+                               const void *q, const void *k, const void *v, const void *log_f,
+                               const float *h0, const void *states_in, const void *dy,
+                               const float *dht, void *dq, void *dk, void *dv, void *dlog_f,
+                               float *dh0, void *stream);
+
+/*
  * The single launches that hgrn2_fwd and hgrn2_bwd are made of, for callers
  * that schedule or time them one by one.  Same conventions and checks as the
  * composite calls; each enqueues exactly one kernel.

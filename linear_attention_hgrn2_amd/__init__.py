@@ -6,6 +6,7 @@ kernels in ``csrc/``); this package is its thin Python binding:
 
   fwd(q, k, v, log_f, h0=None, chunk=64)        chunked forward
   bwd(q, k, v, log_f, dy, h0, dht, states)      chunked backward
+  bwd_noalloc(...)                              the same without a workspace (the library's own scratch)
   fwd_chunk / bwd_adjoint / bwd_chunk           the single launches fwd and bwd are made of
   fwd_tied / bwd_tied / ... / decode_step_tied  the same with tied gates, k = 1 - exp(log_f)
   fwd_gate / bwd_gate / decode_step_gate        gate from its pre-activation z and a lower bound:
@@ -15,12 +16,13 @@ kernels in ``csrc/``); this package is its thin Python binding:
   hgrn1_fwd / hgrn1_bwd                         the HGRN1 elementwise recurrence over [B, T, C]
   hgrn2_chunk(q, k, v, log_f, h0, chunk)        autograd wrapper
 """
-from ._binding import (BF16, F32, HGRN2Chunk, HGRN2Error, LIB_PATH, adjoints_shape, bwd, bwd_adjoint,
+from ._binding import (BF16, F32, HGRN2Chunk, HGRN2Error, LIB_PATH, NOALLOC_SCRATCH_BYTES, adjoints_shape, bwd,
+                       bwd_adjoint, bwd_noalloc,
                        bwd_chunk, bwd_chunk_tied, bwd_gate, bwd_scalar, bwd_tied, decode_step, decode_step_gate,
                        decode_step_scalar, decode_step_tied, fwd_scalar, fwd, fwd_chunk, fwd_chunk_tied, fwd_gate, fwd_tied, hgrn1_bwd, hgrn1_fwd,
                        hgrn1_states_shape, hgrn2_chunk, lib, num_chunks, states_shape, supported)
 
-__all__ = ["fwd", "bwd", "fwd_chunk", "bwd_adjoint", "bwd_chunk", "adjoints_shape", "decode_step",
+__all__ = ["fwd", "bwd", "bwd_noalloc", "NOALLOC_SCRATCH_BYTES", "fwd_chunk", "bwd_adjoint", "bwd_chunk", "adjoints_shape", "decode_step",
            "fwd_tied", "bwd_tied", "fwd_chunk_tied", "bwd_chunk_tied", "decode_step_tied",
            "fwd_gate", "bwd_gate", "decode_step_gate", "fwd_scalar", "bwd_scalar", "decode_step_scalar", "hgrn1_fwd", "hgrn1_bwd", "hgrn1_states_shape", "hgrn2_chunk", "HGRN2Chunk", "HGRN2Error", "supported",
            "num_chunks", "states_shape", "lib", "LIB_PATH", "F32", "BF16"]

@@ -58,6 +58,8 @@ def _lib():
         lib.hgrn2_fwd.restype = I
         lib.hgrn2_bwd.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
         lib.hgrn2_bwd.restype = I
+        lib.hgrn2_bwd_noalloc.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
+        lib.hgrn2_bwd_noalloc.restype = I
         lib.hgrn2_fwd_chunk.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P]
         lib.hgrn2_fwd_chunk.restype = I
         lib.hgrn2_bwd_adjoint.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P]
@@ -215,6 +217,39 @@ def bwd(q, k, v, log_f, dy, h0=None, dht=None, states=None, *, chunk=64, want_dh
                           _ptr(h0), _ptr(states), _ptr(dy), _ptr(dht), _ptr(dq), _ptr(dk),
                           _ptr(dv), _ptr(dlog_f), _ptr(dh0), _ptr(ws), ws_bytes, _stream())
     _check(st, "hgrn2_bwd")
+    return dq, dk, dv, dlog_f, dh0
+
+
+# HGRN2_NOALLOC_SCRATCH_BYTES of include/hgrn2.h: the scratch hgrn2_bwd_noalloc uses
+NOALLOC_SCRATCH_BYTES = 256 << 20
+
+
+def bwd_noalloc(q, k, v, log_f, dy, h0=None, dht=None, states=None, *, chunk=64, dq=None, dk=None, dv=None,
+                dlog_f=None, dh0=None, want_dh0=True):
+    """hgrn2_bwd_noalloc: the chunked backward with the library's own scratch
+    in place of a workspace (the library allocates nothing; outputs not passed
+    are allocated here by torch).  Returns (dq, dk, dv, dlog_f, dh0 or None)."""
+    B, T, H, D = q.shape
+    dt = q.dtype
+    for n, t in (("q", q), ("k", k), ("v", v), ("log_f", log_f), ("dy", dy)):
+        _tok(n, t, B, T, H, D, dt)
+    _st("h0", h0, B, H, D)
+    _st("dht", dht, B, H, D)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    dlog_f = torch.empty_like(log_f) if dlog_f is None else dlog_f
+    for n, t in (("dq", dq), ("dk", dk), ("dv", dv), ("dlog_f", dlog_f)):
+        _tok(n, t, B, T, H, D, dt)
+    if want_dh0 and dh0 is None:
+        dh0 = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+    _st("dh0", dh0, B, H, D)
+    if states is not None:
+        _states_ok(states, B, T, H, D, chunk, dt)
+    st = _lib().hgrn2_bwd_noalloc(B, T, H, D, D, chunk, _DT[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(log_f), _ptr(h0),
+                                  _ptr(states), _ptr(dy), _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dlog_f),
+                                  _ptr(dh0), _stream())
+    _check(st, "hgrn2_bwd_noalloc")
     return dq, dk, dv, dlog_f, dh0
 
 

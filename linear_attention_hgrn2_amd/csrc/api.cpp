@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "hgrn2.h"
@@ -199,6 +200,42 @@ hgrn2_status launch_chunk_bwd(int dtype, int D, int chunk, int gm, int B, int T,
   a.lb = lb;
   a.dlb = dlb_part;
   return hip_status(hgrn2::dispatch_chunk_bwd(dtype, D, chunk, gm, &a, (hipStream_t)stream), what);
+}
+
+// ---- scratch of the allocation-free backward (hgrn2_bwd_noalloc)
+// Device memory of a fixed size in the library's own code object: every GPU
+// the library runs on holds one copy until the process ends.  In host code
+// the array's name is only a host-side handle; the device address of each
+// GPU's copy comes from hipGetSymbolAddress with that GPU current, once, and
+// only that address is ever passed to kernels.
+static __device__ __align__(256) unsigned char scratch[HGRN2_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];  // each device's address of `scratch`, set once
+
+// The current device's address of `scratch` (looked up on the first call on
+// that device), or null with the error message set.
+void *scratch_ptr(hgrn2_status &st) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    st = fail(HGRN2_ERR_HIP, std::string("hgrn2_bwd_noalloc: no current device (") +
+                                 (e != hipSuccess ? hipGetErrorString(e) : "device index out of range") + ")");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      st = fail(HGRN2_ERR_HIP, std::string("hgrn2_bwd_noalloc: scratch address: ") + hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch[dev] = p;
+  }
+  st = HGRN2_OK;
+  return g_scratch[dev];
 }
 
 }  // namespace
@@ -477,6 +514,34 @@ hgrn2_status hgrn2_bwd(int B, int T, int H, int DK, int DV, int chunk, int dtype
                        void *stream) {
   return bwd_impl(kUntied, "hgrn2_bwd", B, T, H, DK, DV, chunk, dtype, q, k, v, log_f, nullptr, h0, states_in, dy,
                   dht, dq, dk, dv, dlog_f, nullptr, dh0, ws, ws_bytes, stream);
+}
+
+hgrn2_status hgrn2_bwd_noalloc(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,
+                               const void *k, const void *v, const void *log_f, const float *h0,
+                               const void *states_in, const void *dy, const float *dht, void *dq, void *dk,
+                               void *dv, void *dlog_f, float *dh0, void *stream) {
+  // the sizes are checked before the scratch is looked up: a rejected call
+  // makes no HIP call at all
+  const size_t need = hgrn2_bwd_workspace_bytes(B, T, H, DK, DV, chunk, dtype, states_in != nullptr);
+  if (need > (size_t)HGRN2_NOALLOC_SCRATCH_BYTES) {
+    hgrn2_status st = check_common(B, T, H, DK, DV, chunk, dtype);
+    if (st != HGRN2_OK) return st;
+    return fail(HGRN2_ERR_WORKSPACE, "hgrn2_bwd_noalloc: the backward needs " + std::to_string(need) +
+                                         " bytes of scratch, more than its " +
+                                         std::to_string((size_t)HGRN2_NOALLOC_SCRATCH_BYTES) +
+                                         " (use hgrn2_bwd with a workspace)");
+  }
+  hgrn2_status st = check_common(B, T, H, DK, DV, chunk, dtype);
+  if (st != HGRN2_OK) return st;
+  st = check_ptrs({{"q", q}, {"v", v}, {"log_f", log_f}, {"dy", dy}, {"dq", dq}, {"dv", dv}, {"dlog_f", dlog_f},
+                   {"k", k}, {"dk", dk}},
+                  {{"h0", h0}, {"states_in", states_in}, {"dht", dht}, {"dh0", dh0}});
+  if (st != HGRN2_OK) return st;
+  void *ws = scratch_ptr(st);
+  if (!ws) return st;
+  return bwd_impl(kUntied, "hgrn2_bwd_noalloc", B, T, H, DK, DV, chunk, dtype, q, k, v, log_f, nullptr, h0,
+                  states_in, dy, dht, dq, dk, dv, dlog_f, nullptr, dh0, ws, (size_t)HGRN2_NOALLOC_SCRATCH_BYTES,
+                  stream);
 }
 
 hgrn2_status hgrn2_fwd_chunk(int B, int T, int H, int DK, int DV, int chunk, int dtype, const void *q,

@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
               "hgrn2_bwd_chunk_tied", "hgrn2_decode_step_tied", "hgrn2_fwd_gate", "hgrn2_bwd_gate",
               "hgrn2_decode_step_gate", "hgrn2_bwd_gate_workspace_bytes", "hgrn1_fwd", "hgrn1_bwd",
               "hgrn1_states_bytes", "hgrn1_fwd_workspace_bytes", "hgrn1_bwd_workspace_bytes",
-              "hgrn2_fwd_scalar", "hgrn2_bwd_scalar", "hgrn2_decode_step_scalar"):
+              "hgrn2_fwd_scalar", "hgrn2_bwd_scalar", "hgrn2_decode_step_scalar", "hgrn2_bwd_noalloc"):
         assert n in names
 
 
@@ -227,6 +227,24 @@ def test_hgrn1_rejections(lib):
                          P[7], None, P[9], ws, None) == 1
     assert lib.hgrn1_bwd(2, 70, 6, 0, 1, P[0], None, P[2], P[3], None, None, P[4], None, P[5], None, P[6],
                          P[4], None, P[9], ws, None) == 1
+
+
+def test_noalloc_rejections(lib):
+    """hgrn2_bwd_noalloc rejects a backward that needs more scratch than it has,
+    and bad arguments, before any HIP call (this runs without a GPU)."""
+    P = [FAKE + i * 0x100000 for i in range(12)]
+    # B8 H16 T4096 d128 bf16 chunk 64 without states: adjoints + recomputed states > 256 MiB
+    r = lib.hgrn2_bwd_noalloc(8, 4096, 16, 128, 128, 64, 1, P[0], P[1], P[2], P[3], None, None, P[4], None,
+                              P[5], P[6], P[7], P[8], None, None)
+    assert r == 3 and b"scratch" in lib.hgrn2_last_error()
+    # invalid sizes win over the scratch size
+    assert lib.hgrn2_bwd_noalloc(8, 4096, 16, 48, 48, 64, 1, P[0], P[1], P[2], P[3], None, None, P[4], None,
+                                 P[5], P[6], P[7], P[8], None, None) == 2
+    # dq NULL; dq misaligned
+    assert lib.hgrn2_bwd_noalloc(1, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], P[3], None, P[9], P[4], None,
+                                 None, P[6], P[7], P[8], None, None) == 1
+    assert lib.hgrn2_bwd_noalloc(1, 10, 1, 16, 16, 16, 0, P[0], P[1], P[2], P[3], None, P[9], P[4], None,
+                                 P[5] + 4, P[6], P[7], P[8], None, None) == 1
 
 
 def test_decode_rejections(lib):
