@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define HGRN2_ABI_VERSION 7
+#define HGRN2_ABI_VERSION 8
 
 typedef enum {
   HGRN2_OK = 0,
@@ -94,9 +94,13 @@ int hgrn2_num_chunks(int T, int chunk);
  * input dtype anyway.  Returns 0 for invalid arguments. */
 size_t hgrn2_states_bytes(int B, int T, int H, int DK, int DV, int chunk, int dtype);
 
-/* Workspace bytes hgrn2_fwd needs: 0 when the caller passes states_out,
- * hgrn2_states_bytes(...) when it passes states_out = NULL (the chunk-boundary
- * states are then written to the workspace, which the per-chunk outputs read). */
+/* Workspace bytes hgrn2_fwd needs: 0 when the caller passes states_out.  With
+ * states_out = NULL, where the forward without stored states exists (chunk
+ * 64; bf16 with D in {32, 64, 128}, float32 with D in {32, 64}): the segment
+ * summaries, 4 * B*H*((P+1)*DK*DV + P*DK) bytes for the P segments of each
+ * sequence (see hgrn2_fwd; a few MB); elsewhere hgrn2_states_bytes(...) (the
+ * chunk-boundary states are then written to the workspace, which the
+ * per-chunk outputs read). */
 size_t hgrn2_fwd_workspace_bytes(int B, int T, int H, int DK, int DV, int chunk, int dtype,
                                  int have_states);
 
@@ -108,10 +112,20 @@ size_t hgrn2_bwd_workspace_bytes(int B, int T, int H, int DK, int DV, int chunk,
 
 /*
  * Chunked forward (HGRN2 summary §3.2 p.5, chunkwise form of the recurrence).
- * Two launches on `stream`: a scan over the chunks of every (b, h) that
- * writes each chunk-boundary state, then the outputs of all chunks in
- * parallel from those states (the second is hgrn2_fwd_chunk).  With y = NULL
- * only the scan runs (one launch).
+ * With states_out (the training forward): two launches on `stream`, a scan
+ * over the chunks of every (b, h) that writes each chunk-boundary state, then
+ * the outputs of all chunks in parallel from those states (the second is
+ * hgrn2_fwd_chunk); with y = NULL only the scan runs.
+ * With states_out = NULL (inference, where that path exists: see
+ * hgrn2_fwd_workspace_bytes): no chunk-boundary state is stored.  Each
+ * sequence is cut into P segments of G chunks, P = about 256 / (B*H) (at
+ * least 1, at most the chunks), and up to three launches run: the end state
+ * and total decay of each of the first P - 1 segments from a zero state (a
+ * scan over the segment), their carry into the state entering every segment,
+ * and the segments' outputs, each segment walked chunk by chunk with its state
+ * on chip.  With P = 1 only the last launch runs and every input is read once.
+ * With y = NULL the first two run over all P segments and give ht.  Otherwise
+ * the chunk-boundary states go to ws as with states_out.
  *   q, k, log_f : [B,T,H,DK] dtype      v : [B,T,H,DV] dtype
  *   h0          : [B,H,DK,DV] float32, or NULL for a zero initial state
  *   y           : [B,T,H,DV] dtype (written), or NULL (states and ht only)

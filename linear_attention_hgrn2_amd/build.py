@@ -21,7 +21,8 @@ LIB = os.path.join(HERE, "libhgrn2.so")
 BUILD = os.path.join(HERE, "_build")
 ARCH = os.environ.get("HGRN2_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["scan_inst.hip", "cfwd_inst.hip", "cbwd_inst.hip", "decode_inst.hip", "hgrn1_inst.hip", "api.cpp"]
+SOURCES = ["scan_inst.hip", "cfwd_inst.hip", "cbwd_inst.hip", "decode_inst.hip", "hgrn1_inst.hip", "sfwd_inst.hip",
+           "api.cpp"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
@@ -34,7 +35,7 @@ FLAGS = [
 # sources whose matrix-core accumulators stay in ordinary vector registers
 # (their per-step float32 updates of the state would otherwise move it
 # between register files twice per step)
-VGPR_MFMA = {"scan_inst.hip", "cfwd_inst.hip"}
+VGPR_MFMA = {"scan_inst.hip", "cfwd_inst.hip", "sfwd_inst.hip"}
 
 
 def hipcc() -> str:

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <cstdio>
 #include <mutex>
 #include <string>
@@ -141,6 +142,41 @@ size_t adjoint_bytes(int B, int T, int H, int DK, int DV, int chunk, int dtype) 
 }
 
 
+// ---- the forward without stored chunk-boundary states (sfwd.h): each
+// sequence is cut into P segments of G chunks so that about kSegUnits
+// workgroups walk segments at once (one per compute unit); P - 1 segment
+// summaries (P when only the final state is wanted) are carried into the
+// state entering every segment.
+constexpr int kSegUnits = 256;
+
+struct SegPlan {
+  int P, G, NSEG;
+};
+
+SegPlan seg_plan(int B, int T, int H, int chunk, bool want_y) {
+  const long long BH = (long long)B * H, N = (T + (long long)chunk - 1) / chunk;
+  const long long Pt = std::min<long long>(N, std::max<long long>(1, (kSegUnits + BH - 1) / BH));
+  SegPlan sp;
+  sp.G = (int)((N + Pt - 1) / Pt);
+  sp.P = (int)((N + sp.G - 1) / sp.G);  // no empty segment
+  sp.NSEG = want_y ? sp.P - 1 : sp.P;
+  return sp;
+}
+
+bool seg_exists(int dtype, int D, int chunk, int gm) {
+  return hgrn2::dispatch_seg_fwd(dtype, D, chunk, gm, nullptr, nullptr) == hipSuccess &&
+         hgrn2::dispatch_seg_scan(dtype, D, chunk, gm, nullptr, nullptr) == hipSuccess;
+}
+
+// workspace of the forward without stored states: the states entering the
+// segments [B,H,NSEG+1,D,D] and the segments' log decay totals [B,H,NSEG,D],
+// float32, sized for NSEG = P (the larger case)
+size_t seg_ws_bytes(int B, int T, int H, int D, int chunk, bool want_y) {
+  const SegPlan sp = seg_plan(B, T, H, chunk, want_y);
+  const size_t BH = (size_t)B * H;
+  return (BH * (sp.NSEG + 1) * D * D + BH * sp.NSEG * D) * sizeof(float);
+}
+
 hgrn2_status launch_scan(int dtype, int D, int chunk, bool reverse, int gm, int B, int T, int H, const void *x,
                          const void *z, const void *log_f, const float *lb, const float *s_in, void *states,
                          float *s_out, void *stream, const char *what) {
@@ -275,7 +311,10 @@ size_t hgrn2_states_bytes(int B, int T, int H, int DK, int DV, int chunk, int dt
 
 size_t hgrn2_fwd_workspace_bytes(int B, int T, int H, int DK, int DV, int chunk, int dtype,
                                  int have_states) {
-  return have_states ? 0 : hgrn2_states_bytes(B, T, H, DK, DV, chunk, dtype);
+  if (have_states) return 0;
+  if (B <= 0 || T <= 0 || H <= 0 || DK <= 0 || DV <= 0 || chunk <= 0 || !valid_dtype(dtype)) return 0;
+  if (DK == DV && seg_exists(dtype, DK, chunk, kUntied)) return seg_ws_bytes(B, T, H, DK, chunk, false);
+  return hgrn2_states_bytes(B, T, H, DK, DV, chunk, dtype);
 }
 
 size_t hgrn2_bwd_workspace_bytes(int B, int T, int H, int DK, int DV, int chunk, int dtype,
@@ -324,6 +363,73 @@ static hgrn2_status fwd_impl(int gm, const char *fn, int B, int T, int H, int DK
     return fail(HGRN2_ERR_UNSUPPORTED, "no forward kernel for this D, chunk and dtype");
   const size_t tok = (size_t)B * T * H * DK * dsize(dtype);
   const size_t sb = (size_t)B * H * DK * DV * sizeof(float);
+  const size_t lbb = (size_t)H * DK * sizeof(float);
+  if (!states_out && seg_exists(dtype, DK, chunk, gm)) {
+    // no state is kept for a backward: walk segments, carrying the state on chip
+    const SegPlan sp = seg_plan(B, T, H, chunk, y != nullptr);
+    const size_t need = seg_ws_bytes(B, T, H, DK, chunk, false);
+    if (sp.NSEG > 0 && (!ws || ws_bytes < need))
+      return fail(HGRN2_ERR_WORKSPACE, "workspace smaller than hgrn2_fwd_workspace_bytes()");
+    const Range ins[] = {{"q", q, tok},
+                         {"k", reads_k(gm) ? k : nullptr, tok},
+                         {"v", v, tok},
+                         {gate_name(gm), log_f, gate_bytes(gm, tok, DK)},
+                         {"h0", (ht == h0) ? nullptr : h0, sb},
+                         {"lower_bound", gm == kGate ? lb : nullptr, lbb}};
+    const Range outs[] = {{"y", y, tok}, {"ht", ht, sb}, {"ws", sp.NSEG > 0 ? ws : nullptr, need}};
+    std::string msg;
+    if (!check_aliasing(ins, 6, outs, 3, msg)) return fail(HGRN2_ERR_INVALID_ARG, msg);
+    if (ht == h0 && ht && (overlap(Range{"y", y, tok}, Range{"h0", h0, sb}) ||
+                           (sp.NSEG > 0 && overlap(Range{"ws", ws, need}, Range{"h0", h0, sb}))))
+      return fail(HGRN2_ERR_INVALID_ARG, "an output overlaps h0");
+    if (!reads_k(gm)) k = nullptr;
+    if (gm != kGate) lb = nullptr;
+    const long long BH = (long long)B * H;
+    float *sin = (float *)ws;
+    float *asum = sp.NSEG > 0 ? sin + (size_t)BH * (sp.NSEG + 1) * DK * DV : nullptr;
+    if (sp.NSEG > 0) {
+      // the end state of every summarised segment from zero, and its total log decay
+      hgrn2::ScanArgs sa;
+      sa.B = B;
+      sa.T = T;
+      sa.H = H;
+      sa.N = (T + chunk - 1) / chunk;
+      sa.x = k;
+      sa.z = v;
+      sa.log_f = log_f;
+      sa.lb = lb;
+      sa.s_in = nullptr;
+      sa.states = nullptr;
+      sa.s_out = sin;
+      sa.NSEG = sp.NSEG;
+      sa.G = sp.G;
+      sa.asum = asum;
+      st = hip_status(hgrn2::dispatch_seg_scan(dtype, DK, chunk, gm, &sa, (hipStream_t)stream), fn);
+      if (st != HGRN2_OK) return st;
+      // the state entering every segment (and, with no y, the final state)
+      st = hip_status(hgrn2::dispatch_seg_carry(DK, (int)BH, sp.NSEG, h0, sin, asum, y ? nullptr : ht,
+                                                (hipStream_t)stream),
+                      fn);
+      if (st != HGRN2_OK || !y) return st;
+    }
+    hgrn2::SegFwdArgs fa;
+    fa.B = B;
+    fa.T = T;
+    fa.H = H;
+    fa.N = (T + chunk - 1) / chunk;
+    fa.P = sp.P;
+    fa.G = sp.G;
+    fa.q = q;
+    fa.k = k;
+    fa.v = v;
+    fa.log_f = log_f;
+    fa.lb = lb;
+    fa.h0 = sp.P == 1 ? h0 : nullptr;
+    fa.sin = sp.P == 1 ? nullptr : sin;
+    fa.y = y;
+    fa.ht = ht;
+    return hip_status(hgrn2::dispatch_seg_fwd(dtype, DK, chunk, gm, &fa, (hipStream_t)stream), fn);
+  }
   const size_t stb = hgrn2_states_bytes(B, T, H, DK, DV, chunk, dtype);
   void *states = states_out;
   if (!states) {
@@ -333,7 +439,6 @@ static hgrn2_status fwd_impl(int gm, const char *fn, int B, int T, int H, int DK
   }
   // ht may be exactly h0 (each workgroup reads its slice of h0 before it
   // writes the same slice of ht); any other overlap is an error.
-  const size_t lbb = (size_t)H * DK * sizeof(float);
   const Range ins[] = {{"q", q, tok},
                        {"k", reads_k(gm) ? k : nullptr, tok},
                        {"v", v, tok},

@@ -8,6 +8,7 @@
 #include "decode.h"
 #include "hgrn1.h"
 #include "scan.h"
+#include "sfwd.h"
 
 namespace hgrn2 {
 
@@ -55,6 +56,14 @@ hipError_t dispatch_dlb_reduce(int B, int H, int N, int D, const float *part, fl
 // one pass of the HGRN1 elementwise scan (gm: kUntied or kTied)
 enum H1Op : int { kH1SummaryFwd, kH1SummaryRev, kH1CarryFwd, kH1CarryRev, kH1FinalFwd, kH1FinalBwd };
 hipError_t dispatch_hgrn1(int op, int dtype, int gm, const H1Args &a, hipStream_t s);
+
+// The forward without stored chunk-boundary states (sfwd.h): the state scan
+// in segment mode (segment summaries), their carry, and the segment walk.
+// A null args pointer only asks whether the kernel exists.
+hipError_t dispatch_seg_scan(int dtype, int D, int C, int gm, const ScanArgs *a, hipStream_t s);
+hipError_t dispatch_seg_fwd(int dtype, int D, int C, int gm, const SegFwdArgs *a, hipStream_t s);
+hipError_t dispatch_seg_carry(int D, int BH, int NSEG, const float *h0, float *sin, const float *asum, float *ht,
+                              hipStream_t s);
 
 // Launch geometry, for the size checks that run before anything is launched:
 // work-items per (b, h) of the state scan (its workgroups for one (b, h) are

@@ -15,6 +15,13 @@
 // 0..N; backward: the adjoint at the end of chunk n, n = 0..N-1) so that the
 // chunk kernels can run all chunks in parallel.
 //
+// In segment mode (SEG, forward only) a workgroup walks only the G chunks of
+// one segment of its sequence, from a zero state, and writes just the
+// segment's end state (float32) and the per-channel total of its log decays:
+// the summaries from which the state entering every segment is carried
+// (hgrn2_seg_carry_kernel), so that the segments' outputs can then be
+// computed in parallel without any per-chunk state in memory.
+//
 // Rows of the state evolve independently (each row is one decay channel), so
 // one workgroup owns one (batch, head, CS-row slice) and holds those rows of
 // the state, transposed (S^T[j][c], every column j), in float32 matrix-core
@@ -34,7 +41,10 @@ struct ScanArgs {
   const float *lb;            // gate mode: lower bound of f, [H,D]
   const float *s_in;          // initial state (h0 or dht), [B,H,D,D] float32, or null
   void *states;               // forward: [B,H,N+1,D,D]; backward: [B,H,N,D,D]; input dtype
-  float *s_out;               // final state (ht or dh0), or null
+  float *s_out;               // final state (ht or dh0), or null; segment mode: [B,H,NSEG+1,D,D], entry p + 1
+                              // the end state of segment p (entry 0 is the carry's)
+  int NSEG = 0, G = 0;        // segment mode: segments summarised per (b, h), chunks per segment
+  float *asum = nullptr;      // segment mode: [B,H,NSEG,D] total log decay of each segment
 };
 
 template <typename T, int D, int C, bool REV> struct ScanCfg {
@@ -63,8 +73,9 @@ template <typename T, int D, int C, bool REV> struct ScanCfg {
   };
 };
 
-template <typename T, int D, int C, bool REV, int GM>
+template <typename T, int D, int C, bool REV, int GM, bool SEG>
 __global__ __launch_bounds__((ScanCfg<T, D, C, REV>::NT)) void hgrn2_scan_kernel(ScanArgs a) {
+  static_assert(!(SEG && REV), "segment summaries are a forward pass");
   using Cfg = ScanCfg<T, D, C, REV>;
   constexpr int NW = Cfg::NW, NT = Cfg::NT, CS = Cfg::CS, NS = Cfg::NS, NR = Cfg::NR, TPR = Cfg::TPR,
                 JB = Cfg::JB, EPV = Cfg::EPV;
@@ -73,15 +84,20 @@ __global__ __launch_bounds__((ScanCfg<T, D, C, REV>::NT)) void hgrn2_scan_kernel
   using ZT = RowTile<T, D, 32>;
   __shared__ typename Cfg::Smem sm;
 
-  // slices of one (b, h) get ids equal mod 8: they run on one XCD and share its L2
+  // slices of one (b, h) (segment mode: of one segment) get ids equal mod 8:
+  // they run on one XCD and share its L2
   const int bid = blockIdx.x;
   const int grp = bid / (8 * NS), rem = bid % (8 * NS);
   const int slice = rem / 8;
-  const int bh = grp * 8 + (rem % 8);
-  if (bh >= a.B * a.H) return;
+  const int unit = grp * 8 + (rem % 8);
+  if (unit >= a.B * a.H * (SEG ? a.NSEG : 1)) return;
+  const int bh = SEG ? unit / a.NSEG : unit;
   const int b = bh / a.H, h = bh % a.H;
   const int cs0 = slice * CS;  // first state row of this workgroup
-  const int T_ = a.T, H = a.H, N = a.N;
+  const int T_ = a.T, H = a.H;
+  // the chunks this workgroup walks: all of them, or one segment's
+  const int n0 = SEG ? (unit % a.NSEG) * a.G : 0;
+  const int N = SEG ? min(a.G, a.N - n0) : a.N;
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n16 = lane & 15, g = lane >> 4;
   const int cl = tid % CS, ri = tid / CS;  // prep layout: channel, run of TPR tokens
@@ -111,7 +127,7 @@ __global__ __launch_bounds__((ScanCfg<T, D, C, REV>::NT)) void hgrn2_scan_kernel
     const int q = w + NW * i;
     const int jb = q % JB, cb = q / JB;
     const int c = cs0 + cb * 16 + n16, j = jb * 16 + 4 * g;
-    if (q < Cfg::NTILE && a.s_in) {
+    if (q < Cfg::NTILE && a.s_in && !SEG) {
       const float4 v = *(const float4 *)(a.s_in + (size_t)bh * SS + (size_t)c * D + j);
       S[i] = f32x4_t{v.x, v.y, v.z, v.w};
     } else {
@@ -119,7 +135,7 @@ __global__ __launch_bounds__((ScanCfg<T, D, C, REV>::NT)) void hgrn2_scan_kernel
     }
   }
   // this (b, h)'s entries of the state buffer; entry `slot` at a scalar offset
-  const int nst = REV ? N : N + 1;
+  const int nst = SEG ? 0 : REV ? N : N + 1;
   const GBuf bst((const char *)a.states + (size_t)bh * nst * SS * sizeof(T), (uint32_t)(nst * SS * sizeof(T)));
   // States leave through LDS: the tiles are written there (stage), and after
   // the next barrier every thread stores two 16-byte pieces of whole rows
@@ -129,6 +145,7 @@ __global__ __launch_bounds__((ScanCfg<T, D, C, REV>::NT)) void hgrn2_scan_kernel
   constexpr int VST = CS * D / EPV;  // 16-byte vectors of the slice's state rows
   int pend = -1;                     // entry staged and not yet stored
   auto stage = [&](int slot) {
+    if constexpr (SEG) return;
 #pragma unroll
     for (int i = 0; i < Cfg::TPW; ++i) {
       const int q = w + NW * i;
@@ -143,7 +160,7 @@ __global__ __launch_bounds__((ScanCfg<T, D, C, REV>::NT)) void hgrn2_scan_kernel
     pend = slot;
   };
   auto flush = [&]() {
-    if (pend < 0) return;
+    if (SEG || pend < 0) return;
 #pragma unroll
     for (int i = 0; i < (VST + NT - 1) / NT; ++i) {
       const int idx = tid + i * NT;
@@ -176,8 +193,9 @@ __global__ __launch_bounds__((ScanCfg<T, D, C, REV>::NT)) void hgrn2_scan_kernel
   };
 
   // one chunk: consumes (px, pl, pz), then refills them with the chunk two steps on
+  float gacc = 0.f;  // segment mode: this thread's channel's total log decay over the segment
   auto step = [&](XP &px, XP &pl, ZP &pz, int it) {
-    const int n = REV ? N - 1 - it : it;
+    const int n = REV ? N - 1 - it : n0 + it;
     T *zs = sm.z[it & 1];
     // ---- chunk-local prefix of the floored log f: within the lane's run, then across runs
     float l[TPR], kx[TPR];  // kx: k of the run's tokens (forward; formed with log f)
@@ -208,6 +226,7 @@ __global__ __launch_bounds__((ScanCfg<T, D, C, REV>::NT)) void hgrn2_scan_kernel
         G += L;
       }
       if (ri == 0) sm.eG[cl] = __expf(G);
+      gacc += G;
 #pragma unroll
       for (int i = 0; i < TPR; ++i) {
         const float b_t = P + l[i];
@@ -219,7 +238,7 @@ __global__ __launch_bounds__((ScanCfg<T, D, C, REV>::NT)) void hgrn2_scan_kernel
     flush();  // the state staged in the previous step (read here, rewritten after the next barrier)
     // this register set is consumed: fetch the chunk two steps on into it (the
     // last chunk again near the end, so every step issues the same loads)
-    prefetch(px, pl, pz, REV ? max(n - 2, 0) : min(n + 2, N - 1));
+    prefetch(px, pl, pz, REV ? max(n - 2, 0) : min(n + 2, n0 + N - 1));
     __syncthreads();
     // ---- the adjoint at the end of chunk n is the value before its update
     if (REV) stage(n);
@@ -246,8 +265,8 @@ __global__ __launch_bounds__((ScanCfg<T, D, C, REV>::NT)) void hgrn2_scan_kernel
 
   T px0[TPR], pl0[TPR], px1[TPR], pl1[TPR];
   uint4 pz0[Cfg::NVZ], pz1[Cfg::NVZ];
-  prefetch(px0, pl0, pz0, REV ? N - 1 : 0);
-  prefetch(px1, pl1, pz1, REV ? max(N - 2, 0) : min(1, N - 1));
+  prefetch(px0, pl0, pz0, REV ? N - 1 : n0);
+  prefetch(px1, pl1, pz1, REV ? max(N - 2, 0) : n0 + min(1, N - 1));
   int it = 0;
   for (; it + 1 < N; it += 2) {
     step(px0, pl0, pz0, it);
@@ -257,25 +276,28 @@ __global__ __launch_bounds__((ScanCfg<T, D, C, REV>::NT)) void hgrn2_scan_kernel
   __syncthreads();
   flush();
   if (a.s_out) {
+    // the final state (segment mode: the segment's end state from zero)
+    const size_t so = (SEG ? (size_t)bh * (a.NSEG + 1) + unit % a.NSEG + 1 : (size_t)bh) * SS;
 #pragma unroll
     for (int i = 0; i < Cfg::TPW; ++i) {
       const int q = w + NW * i;
       if (q < Cfg::NTILE) {
         const int jb = q % JB, cb = q / JB;
         const int c = cs0 + cb * 16 + n16, j = jb * 16 + 4 * g;
-        *(float4 *)(a.s_out + (size_t)bh * SS + (size_t)c * D + j) = make_float4(S[i][0], S[i][1], S[i][2], S[i][3]);
+        *(float4 *)(a.s_out + so + (size_t)c * D + j) = make_float4(S[i][0], S[i][1], S[i][2], S[i][3]);
       }
     }
   }
+  if (SEG && ri == 0) a.asum[(size_t)unit * D + cs0 + cl] = gacc;
 }
 
-template <typename T, int D, int C, bool REV, int GM = kUntied>
+template <typename T, int D, int C, bool REV, int GM = kUntied, bool SEG = false>
 hipError_t launch_scan(const ScanArgs &a, hipStream_t stream) {
   static_assert(!(REV && GM == kTied), "the adjoint scan reads q, not k: run it untied");
   using Cfg = ScanCfg<T, D, C, REV>;
-  const long long groups = ((long long)a.B * a.H + 7) / 8;
-  hipLaunchKernelGGL((hgrn2_scan_kernel<T, D, C, REV, GM>), dim3((unsigned)(groups * 8 * Cfg::NS)), dim3(Cfg::NT), 0,
-                     stream, a);
+  const long long groups = ((long long)a.B * a.H * (SEG ? a.NSEG : 1) + 7) / 8;
+  hipLaunchKernelGGL((hgrn2_scan_kernel<T, D, C, REV, GM, SEG>), dim3((unsigned)(groups * 8 * Cfg::NS)), dim3(Cfg::NT),
+                     0, stream, a);
   return hipGetLastError();
 }
 

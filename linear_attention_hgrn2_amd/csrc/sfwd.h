@@ -1,0 +1,480 @@
+// Forward without stored chunk-boundary states (gfx950): the sequence of every
+// (batch, head) is cut into P segments of G chunks; each workgroup walks one
+// segment's chunks in order, carrying the d x d state in float32 matrix-core
+// accumulators, and writes y.  Nothing per chunk goes to memory.
+//
+// HGRN2 summary (paperlayer.ai) §3.2: S_t = Diag(f_t) S_{t-1} + k_t^T v_t,
+// y_t = q_t S_t; §3.2 p.5: evaluated chunk by chunk in the linear-attention
+// form.  Within chunk n, with the in-chunk inclusive prefix b of log f and
+// its total Gamma,
+//   y_t  = sum_{s <= t in chunk} (sum_c q_t[c] k_s[c] e^{b_t[c] - b_s[c]}) v_s + (q_t e^{b_t}) S
+//   S   <- Diag(e^Gamma) S + sum_t Diag(e^{Gamma - b_t}) k_t^T v_t.
+// The state entering segment p is the carry of the segment summaries (the
+// end state of every earlier segment from a zero state, written by the state
+// scan in segment mode, and the segments' total log decays), from h0:
+//   S_in(0) = h0,  S_in(p + 1) = Diag(e^{a_p}) S_in(p) + S_loc(p)
+// (hgrn2_seg_carry_kernel).  P = 1 needs no summaries: one pass reads every
+// input once, writes y once, and the final state.
+//
+// Layout: one workgroup of 2 C / 16 waves per (b, h, segment), two per SIMD
+// at chunk 64.  Wave (w, hh) forms the prefix of 16-token sub-block w (both
+// waves of a block do), writes qo = q e^{ell}, ko = k e^{L_w - ell} and
+// kh = k e^{Gamma - b_t} of the block's half hh of tokens (block-local
+// prefixes ell, totals L_j, starts P_j, as the per-chunk forward), forms one
+// or two of the 10 score tiles (with the gap factors between blocks, and the
+// diagonal summed directly when a block decays more than kDiagLimit nats),
+// which are shared through LDS, then y of block w for column half hh, and the
+// state tiles S^T[16 jb.., 16 cb..] with index wv + 8 i:
+//   S^T <- S^T Diag(e^Gamma) + v^T kh.
+// The state's copy in the input dtype in LDS feeds the next chunk's
+// inter-chunk product.
+#pragma once
+
+#include <algorithm>
+
+#include "cfwd.h"
+
+namespace hgrn2 {
+
+struct SegFwdArgs {
+  int B, T, H, N;                 // N chunks per sequence
+  int P, G;                       // segments per (b, h), chunks per segment
+  const void *q, *k, *v, *log_f;  // [B,T,H,D]; log_f holds the gate pre-activation in gate mode
+  const float *lb;                // gate mode: lower bound of f, [H,D]
+  const float *h0;                // P = 1: [B,H,D,D] float32 or null (zero), the initial state
+  const float *sin;               // P > 1: [B,H,P,D,D] float32, entry p = the state entering segment p
+  void *y;                        // [B,T,H,D]
+  float *ht;                      // [B,H,D,D] float32 final state, or null
+};
+
+template <typename T, int D, int C> struct SfwdCfg {
+  static constexpr int NB = C / 16;             // 16-token sub-blocks
+  static constexpr int NWV = 2 * NB, NT = 64 * NWV;
+  static constexpr int CPL = D > 64 ? D / 64 : 1;
+  static constexpr int LANES = D / CPL;
+  static constexpr int JB = D / 16, CB = D / 16;
+  static constexpr int KSD = D / 32;
+  static constexpr int HC = D / 2 / 16;         // column tiles of one wave's half of y
+  static constexpr int EPV = 16 / (int)sizeof(T);
+  static constexpr int NPAIR = NB * (NB + 1) / 2;
+  static constexpr int VV = C * D / EPV, NVV = (VV + NT - 1) / NT;
+  static constexpr int NTILE = JB * CB, TPW = (NTILE + NWV - 1) / NWV;  // state tiles per wave
+  static constexpr int LD = RowTile<T, D>::LD;
+  static_assert(D >= 32 && HC >= 1, "two column halves of at least one tile");
+  using Sc = PFrag4<T>;  // one lane's piece of a score tile as a 16-deep operand
+  struct Smem {
+    T qo[C * LD];  // RowTile<T, D>; after the products, each wave's y staging
+    T ko[C * LD];
+    T kh[C * LD];  // k e^{Gamma - b_t}: the state update's operand
+    T v[C * LD];
+    T S[D * LD];   // copy of the state entering the chunk, row c, column j
+    Sc sc[NPAIR][64];
+    float eL[NB][D];  // e^{L_w}, each block's decay
+    float eLd[NB][D]; // e^{-L_w}, at most e^{80}
+    float eP[NB][D];  // e^{P_w}
+    float eG[D];      // e^{Gamma}
+    int wide[NB];     // block w's diagonal is summed directly
+  };
+};
+
+// pair index p -> (i, j), i >= j, p = i (i + 1) / 2 + j
+__device__ __forceinline__ int sfwd_pair_i(int p) { return p >= 6 ? 3 : p >= 3 ? 2 : p >= 1 ? 1 : 0; }
+
+template <typename T, int D, int C, int GM>
+__global__ __launch_bounds__((SfwdCfg<T, D, C>::NT)) void hgrn2_seg_fwd_kernel(SegFwdArgs a) {
+  using Cfg = SfwdCfg<T, D, C>;
+  constexpr int NB = Cfg::NB, NWV = Cfg::NWV, NT = Cfg::NT, CPL = Cfg::CPL, JB = Cfg::JB, KSD = Cfg::KSD,
+                HC = Cfg::HC, EPV = Cfg::EPV, TPW = Cfg::TPW, NPAIR = Cfg::NPAIR;
+  static_assert(NB == 4, "the pair decoding assumes four sub-blocks");
+  using XT = RowTile<T, D>;
+  __shared__ typename Cfg::Smem sm;
+
+  const int N = a.N, T_ = a.T, H = a.H, P = a.P;
+  const int unit = blockIdx.x;
+  const int bh = unit / P, p = unit % P;
+  if (bh >= a.B * H) return;
+  const int b = bh / H, h = bh % H;
+  const int n0 = p * a.G, n1 = min(N, n0 + a.G);
+  const int tid = threadIdx.x, lane = tid & 63, n16 = lane & 15, g = lane >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int w = wv >> 1, hh = wv & 1;  // token block w; half hh of its tokens (prefix) and of y's columns
+  const bool has_ch = lane < Cfg::LANES;
+  const int c0 = (has_ch ? lane : 0) * CPL;
+  float lbv[CPL];  // gate mode: lower bounds of this lane's channels
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) lbv[e] = GM == kGate ? a.lb[h * D + c0 + e] : 0.f;
+  const uint32_t HDB = (uint32_t)H * D * sizeof(T);  // bytes from one token to the next
+  const uint32_t c0b = (uint32_t)c0 * sizeof(T);
+  auto tok = [&](int t) { return (uint32_t)t * HDB; };
+
+  // ---- the state entering the segment: S^T tiles q = wv + NWV i in float32 accumulators
+  const size_t SS = (size_t)D * D;
+  const float *s0 = P == 1 ? (a.h0 ? a.h0 + (size_t)bh * SS : nullptr) : a.sin + ((size_t)bh * P + p) * SS;
+  f32x4_t S[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int q = wv + NWV * i, jb = q % JB, cb = q / JB;
+    const int c = 16 * cb + n16, j = 16 * jb + 4 * g;
+    if (q < Cfg::NTILE && s0) {
+      const float4 x = *(const float4 *)(s0 + (size_t)c * D + j);
+      S[i] = f32x4_t{x.x, x.y, x.z, x.w};
+    } else {
+      acc_zero(S[i]);
+    }
+  }
+  // its copy as a matrix-core operand, row c, columns j..j+3
+  auto stage_state = [&]() {
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int q = wv + NWV * i, jb = q % JB, cb = q / JB;
+      if (q < Cfg::NTILE) {
+        Pack<T, 4> pk;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pk.v[r] = from_f32<T>(S[i][r]);
+        *(Pack<T, 4> *)&sm.S[XT::at(16 * cb + n16, 16 * jb + 4 * g)] = pk;
+      }
+    }
+  };
+  stage_state();
+
+  // ---- a chunk's rows in registers: the v tile (16-byte vectors), q and k of
+  // this wave's 8 tokens 16 w + 8 hh + t, and log f of all 16 tokens of block w
+  // (both waves of a block form its prefix).  Buffer windows end at the last
+  // row of the sequence: rows past it read as zero (no decay, no contribution).
+  struct Regs {
+    uint4 v[Cfg::NVV];
+    Pack<T, CPL> q[8], k[8], l[16];
+    T la;  // kScalar: log a of token 16 w + (lane & 15)
+  };
+  auto load = [&](Regs &r, int n) {
+    const int t0 = n * C, len = min(C, T_ - t0);
+    const size_t cbase = (((size_t)b * T_ + t0) * H + h) * D * sizeof(T);
+    const uint32_t rows = (uint32_t)len * HDB;
+    const GBuf bq((const char *)a.q + cbase, rows), bv((const char *)a.v + cbase, rows);
+    const GBuf bk((const char *)(reads_k(GM) ? a.k : a.q) + cbase, rows);
+    const LfRows<GM> bl = lf_rows<GM, T>(a.log_f, b, T_, H, h, D, t0, len);
+#pragma unroll
+    for (int i = 0; i < Cfg::NVV; ++i) {
+      const int idx = min(tid + i * NT, Cfg::VV - 1);
+      const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
+      r.v[i] = bv.ld16(tok(row) + (uint32_t)col * sizeof(T));
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      r.q[t] = bq.template ldpack<T, CPL>(tok(16 * w + 8 * hh + t) + c0b);
+      if constexpr (reads_k(GM)) r.k[t] = bk.template ldpack<T, CPL>(tok(16 * w + 8 * hh + t) + c0b);
+    }
+    if constexpr (GM == kScalar) {
+      r.la = bl.template ld<T, 1>(16 * w + (lane & 15), 0).v[0];
+    } else {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) r.l[t] = bl.template ld<T, CPL>(16 * w + t, c0b);
+    }
+  };
+
+  Regs rg;
+  load(rg, n0);
+  for (int n = n0; n < n1; ++n) {
+    const int t0 = n * C, len = min(C, T_ - t0);
+    // ---- P0: v tile; block w's prefix (in both of its waves); qo, ko of this wave's tokens
+#pragma unroll
+    for (int i = 0; i < Cfg::NVV; ++i) {
+      const int idx = tid + i * NT;
+      const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
+      if (idx < Cfg::VV) *(uint4 *)&sm.v[XT::at(row, col)] = rg.v[i];
+    }
+    float kof[8][CPL];  // this wave's tokens: ko in float32, k e^{L_w - ell}
+    {
+      float run[CPL], ell[8][CPL], kf[8][CPL];
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) run[e] = 0.f;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int tt = 16 * w + t;
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+          const T lx = GM == kScalar ? readlane(rg.la, t) : rg.l[t].v[e];
+          float lf, kv;
+          // k of this wave's own tokens (loaded, or formed with log f); the
+          // other half's tokens only add their log f to the prefix
+          const T kx = reads_k(GM) ? rg.k[t & 7].v[e] : lx;
+          lf_k<GM>(kx, lx, lbv[e], tt < len, lf, kv);
+          run[e] += lf;
+          if ((t >> 3) == hh) {
+            ell[t & 7][e] = run[e];
+            kf[t & 7][e] = kv;
+          }
+        }
+      }
+      bool wd = false;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) wd |= has_ch && -run[e] > kDiagLimit;
+      const bool wide = __ballot(wd) != 0;
+      if (has_ch) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int tt = 16 * w + 8 * hh + t;
+          Pack<T, CPL> oq, ok;
+#pragma unroll
+          for (int e = 0; e < CPL; ++e) {
+            oq.v[e] = from_f32<T>(to_f32(rg.q[t].v[e]) * __expf(ell[t][e]));
+            kof[t][e] = kf[t][e] * __expf(run[e] - ell[t][e]);
+            ok.v[e] = from_f32<T>(kof[t][e]);
+          }
+          stpack<T, CPL>(&sm.qo[XT::at(tt, c0)], oq);
+          stpack<T, CPL>(&sm.ko[XT::at(tt, c0)], ok);
+        }
+        // the block's decay e^{L_w} and its diagonal gap factor e^{-L_w} (at
+        // most e^{80}): every other factor of the chunk is a product of these
+        if (hh == 0) {
+#pragma unroll
+          for (int e = 0; e < CPL; ++e) {
+            sm.eL[w][c0 + e] = __expf(run[e]);
+            sm.eLd[w][c0 + e] = __expf(fminf(-run[e], 80.f));
+          }
+        }
+      }
+      if (hh == 0 && lane == 0) sm.wide[w] = wide;
+    }
+    // the registers are consumed: the next chunk's rows
+    if (n + 1 < n1) load(rg, n + 1);
+    __syncthreads();  // B1: qo, ko, v, block decays and flags of every block
+
+    // ---- P1: kh of this wave's tokens, e^{P_w}, e^{Gamma}; the score tiles
+    if (has_ch) {
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) {
+        const int c = c0 + e;
+        float eb = 1.f, ea = 1.f, eg = 1.f;  // e^{P_w}, e^{Gamma - P_{w+1}}, e^{Gamma}
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          const float x = sm.eL[i][c];
+          eb *= (i < w) ? x : 1.f;
+          ea *= (i > w) ? x : 1.f;
+          eg *= x;
+        }
+        if (hh == 0) sm.eP[w][c] = eb;
+        if (wv == 0) sm.eG[c] = eg;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) sm.kh[XT::at(16 * w + 8 * hh + t, c)] = from_f32<T>(kof[t][e] * ea);
+      }
+    }
+    // score tile tau = wv + NWV s of pair (i, j), i >= j: X[s][t] = sum_c ko_s gap_c qo_t
+    // (the transposed scores, kept as the 16-deep operand of the product with v)
+#pragma unroll
+    for (int s2 = 0; s2 < (NPAIR + NWV - 1) / NWV; ++s2) {
+      const int tau = wv + NWV * s2;
+      if (tau >= NPAIR) break;
+      const int i = sfwd_pair_i(tau), j = tau - i * (i + 1) / 2;
+      f32x4_t X;
+      acc_zero(X);
+      if (i == j && sm.wide[i]) {
+        // wide in-block decay: summed directly, every exponent <= 0 (rare;
+        // reloads the block's rows from global memory).  Lane (g, n) holds
+        // X[s = 4g + r][t = n].
+        const size_t cbase = (((size_t)b * T_ + t0) * H + h) * D * sizeof(T);
+        const uint32_t rows = (uint32_t)len * HDB;
+        const GBuf bq((const char *)a.q + cbase, rows);
+        const GBuf bk((const char *)(reads_k(GM) ? a.k : a.q) + cbase, rows);
+        const LfRows<GM> bl = lf_rows<GM, T>(a.log_f, b, T_, H, h, D, t0, len);
+        for (int t = 0; t < 16; ++t) {
+          float qt[CPL], ex[CPL];
+#pragma unroll
+          for (int e = 0; e < CPL; ++e) {
+            qt[e] = 0.f;
+            ex[e] = 0.f;
+          }
+          const Pack<T, CPL> pq = bq.template ldpack<T, CPL>(tok(16 * i + t) + c0b);
+#pragma unroll
+          for (int e = 0; e < CPL; ++e) qt[e] = has_ch ? to_f32(pq.v[e]) : 0.f;
+          for (int sd = t; sd >= 0; --sd) {
+            float part = 0.f;
+            Pack<T, CPL> pk;
+            if constexpr (reads_k(GM)) pk = bk.template ldpack<T, CPL>(tok(16 * i + sd) + c0b);
+            const Pack<T, CPL> pls = bl.template ld<T, CPL>(16 * i + sd, c0b);
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) {
+              float lf, kv;
+              lf_k<GM>(pk.v[e], lfe<GM>(pls, e), lbv[e], true, lf, kv);
+              part += qt[e] * kv * __expf(ex[e]);
+              ex[e] += lf;  // the factor of sd - 1 includes f_sd
+            }
+            const float tot = wave_sum(part);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (n16 == t && 4 * g + r == sd) X[r] = tot;
+          }
+        }
+      } else if (i == j + 1) {
+        // adjacent blocks: the gap factor is e^{P_i - P_i} = 1 exactly
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) {
+          const int c = 32 * ks + 8 * g;
+          mma(X, row8<D>(sm.ko, 16 * j + n16, c), row8<D>(sm.qo, 16 * i + n16, c));
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) {
+          const int c = 32 * ks + 8 * g;
+          float kv[8];
+          unpack8(row8<D>(sm.ko, 16 * j + n16, c), kv);
+          // gap factor: e^{P_i - P_{j+1}} (the decays of the blocks between) apart,
+          // e^{-L_i} (at most e^{80}) on the diagonal
+          Frag fa;
+#pragma unroll
+          for (int e = 0; e < 8; e += 4) {
+            float4 x;
+            if (i == j) {
+              x = ldf4(&sm.eLd[i][c + e]);
+            } else {
+              x = make_float4(1.f, 1.f, 1.f, 1.f);
+#pragma unroll
+              for (int m = 1; m < NB - 1; ++m)
+                if (m > j && m < i) {
+                  const float4 L = ldf4(&sm.eL[m][c + e]);
+                  x.x *= L.x; x.y *= L.y; x.z *= L.z; x.w *= L.w;
+                }
+            }
+            fa.v[e] = kv[e] * x.x;
+            fa.v[e + 1] = kv[e + 1] * x.y;
+            fa.v[e + 2] = kv[e + 2] * x.z;
+            fa.v[e + 3] = kv[e + 3] * x.w;
+          }
+          mma(X, to_pfrag<T>(fa), row8<D>(sm.qo, 16 * i + n16, c));
+        }
+        if (i == j) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (4 * g + r > n16) X[r] = 0.f;  // s > t
+        }
+      }
+      sm.sc[tau][lane] = acc_to_frag4<T>(X);
+    }
+    __syncthreads();  // B2: score tiles, kh, e^{P}, e^{Gamma}
+
+    // ---- P2: y of block w, column half hh: the scores' product with v, plus (qo e^{P_w}) S
+    f32x4_t Y[HC];
+#pragma unroll
+    for (int cb = 0; cb < HC; ++cb) acc_zero(Y[cb]);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (j > w) continue;  // wave-uniform
+      const PFrag4<T> fa = sm.sc[w * (w + 1) / 2 + j][lane];
+#pragma unroll
+      for (int cb = 0; cb < HC; ++cb) mma16(Y[cb], fa, tr4<D>(sm.v, 16 * j, (D / 2) * hh + 16 * cb));
+    }
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks) {
+      const int c = 32 * ks + 8 * g;
+      float qv[8];
+      unpack8(row8<D>(sm.qo, 16 * w + n16, c), qv);
+      const float4 e0 = ldf4(&sm.eP[w][c]), e1 = ldf4(&sm.eP[w][c + 4]);
+      Frag f;
+      f.v[0] = qv[0] * e0.x; f.v[1] = qv[1] * e0.y; f.v[2] = qv[2] * e0.z; f.v[3] = qv[3] * e0.w;
+      f.v[4] = qv[4] * e1.x; f.v[5] = qv[5] * e1.y; f.v[6] = qv[6] * e1.z; f.v[7] = qv[7] * e1.w;
+      const PFrag<T> qb = to_pfrag<T>(f);
+#pragma unroll
+      for (int cb = 0; cb < HC; ++cb) mma(Y[cb], qb, tr8<D>(sm.S, 32 * ks, (D / 2) * hh + 16 * cb));
+    }
+    __syncthreads();  // B3: every wave is done with qo, the scores and the state's copy
+
+    // ---- P3: y out (staged in this wave's half of block w's qo rows); the state update
+#pragma unroll
+    for (int cb = 0; cb < HC; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        sm.qo[XT::at(16 * w + 4 * g + r, (D / 2) * hh + 16 * cb + n16)] = from_f32<T>(Y[cb][r]);
+    wave_lds_sync();
+    {
+      T *gy = (T *)a.y + (((size_t)b * T_ + t0) * H + h) * D;
+      constexpr int RV = 16 * (D / 2) / EPV;  // 16-byte vectors in this wave's 16 half rows
+#pragma unroll
+      for (int i = 0; i < (RV + 63) / 64; ++i) {
+        const int idx = lane + 64 * i;
+        const int row = idx / (D / 2 / EPV), col = (D / 2) * hh + (idx % (D / 2 / EPV)) * EPV;
+        const int t = 16 * w + row;
+        if (idx < RV && t < len) {
+          const uint4 u = *(const uint4 *)&sm.qo[XT::at(t, col)];
+          __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, u), (u32x4_t *)(gy + ((size_t)t * H * D + col)));
+        }
+      }
+    }
+    // S^T <- S^T Diag(e^Gamma) + v^T kh
+    // (NWV = 8 divides JB for D = 128: every tile of this wave has jb = wv, and
+    // the compiler keeps the two v operands across the tiles)
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int q = wv + NWV * i, jb = q % JB, cb = q / JB;
+      if (q < Cfg::NTILE) {
+        const float eg = sm.eG[16 * cb + n16];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[i][r] *= eg;
+#pragma unroll
+        for (int ks = 0; ks < C / 32; ++ks) mma(S[i], tr8<D>(sm.v, 32 * ks, 16 * jb), tr8<D>(sm.kh, 32 * ks, 16 * cb));
+      }
+    }
+    stage_state();
+    __syncthreads();  // B4: the new state's copy is in place; the tiles may be rewritten
+  }
+
+  if (p == P - 1 && a.ht) {
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int q = wv + NWV * i, jb = q % JB, cb = q / JB;
+      if (q < Cfg::NTILE) {
+        const int c = 16 * cb + n16, j = 16 * jb + 4 * g;
+        *(float4 *)(a.ht + (size_t)bh * SS + (size_t)c * D + j) = make_float4(S[i][0], S[i][1], S[i][2], S[i][3]);
+      }
+    }
+  }
+}
+
+// The state entering each segment from the segments' summaries, in place in
+// sin [BH, NSEG + 1, D, D] float32, whose entry p + 1 holds the end state of
+// segment p from a zero state (the state scan in segment mode):
+//   entry 0 <- h0 (or zero);  entry p + 1 <- Diag(e^{a_p}) entry p + entry p + 1,
+// with a_p = asum [BH, NSEG, D], the segment's total log decay per channel.
+// The last value is also the final state (ht, if wanted).  One thread per
+// element of the d x d state, the segments in order; each thread reads its
+// element of h0 before it writes the same element of ht, so ht may alias h0.
+template <int D>
+__global__ __launch_bounds__(256) void hgrn2_seg_carry_kernel(int BH, int NSEG, const float *h0, float *sin,
+                                                              const float *asum, float *ht) {
+  constexpr int PER = D * D / 256 > 0 ? D * D / 256 : 1;  // workgroups' worth of elements per (b, h)
+  const size_t SS = (size_t)D * D;
+  // a grid-stride walk over (b, h, element block): the grid stays small for any B * H
+  for (long long blk = blockIdx.x; blk < (long long)BH * PER; blk += gridDim.x) {
+    const long long bh = blk / PER;
+    const int e = (int)(blk % PER) * 256 + (int)threadIdx.x;
+    if (e >= D * D) continue;
+    const int c = e / D;
+    float cur = h0 ? h0[(size_t)bh * SS + e] : 0.f;
+    float *base = sin + (size_t)bh * (NSEG + 1) * SS;
+    base[e] = cur;
+    for (int p = 0; p < NSEG; ++p) {
+      cur = __expf(asum[((size_t)bh * NSEG + p) * D + c]) * cur + base[(size_t)(p + 1) * SS + e];
+      base[(size_t)(p + 1) * SS + e] = cur;
+    }
+    if (ht) ht[(size_t)bh * SS + e] = cur;
+  }
+}
+
+template <typename T, int D, int C, int GM>
+hipError_t launch_seg_fwd(const SegFwdArgs &a, hipStream_t stream) {
+  using Cfg = SfwdCfg<T, D, C>;
+  hipLaunchKernelGGL((hgrn2_seg_fwd_kernel<T, D, C, GM>), dim3((unsigned)((long long)a.B * a.H * a.P)),
+                     dim3(Cfg::NT), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_seg_carry(int BH, int NSEG, const float *h0, float *sin, const float *asum, float *ht,
+                            hipStream_t stream) {
+  constexpr int PER = D * D / 256 > 0 ? D * D / 256 : 1;
+  const long long blocks = std::min<long long>((long long)BH * PER, 1 << 16);
+  hipLaunchKernelGGL(hgrn2_seg_carry_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, stream, BH, NSEG, h0, sin, asum,
+                     ht);
+  return hipGetLastError();
+}
+
+}  // namespace hgrn2

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.hgrn2_abi_version() == 7
+    assert lib.hgrn2_abi_version() == 8
     for s in range(5):
         assert lib.hgrn2_status_string(s).startswith(b"HGRN2_")
 
@@ -57,6 +57,11 @@ def test_sizes(lib):
     assert lib.hgrn2_bwd_workspace_bytes(1, 100, 1, 16, 16, 16, 1, 1) == 7 * 16 * 16 * 2
     assert lib.hgrn2_fwd_workspace_bytes(1, 100, 1, 16, 16, 16, 0, 1) == 0
     assert lib.hgrn2_fwd_workspace_bytes(1, 100, 1, 16, 16, 16, 0, 0) == 8 * 16 * 16 * 4
+    # the forward without stored states (chunk 64, bf16, D 128): B1 H32 T32768 has 512 chunks, cut
+    # into P = 8 segments of 64 (256 workgroups); summaries of (P + 1) states and P decay vectors
+    assert lib.hgrn2_fwd_workspace_bytes(1, 32768, 32, 128, 128, 64, 1, 0) == 32 * (9 * 128 * 128 + 8 * 128) * 4
+    # B16 H16: P = 1
+    assert lib.hgrn2_fwd_workspace_bytes(16, 4096, 16, 128, 128, 64, 1, 0) == 256 * (2 * 128 * 128 + 128) * 4
     assert lib.hgrn2_supported(128, 64, 1) == 1
     assert lib.hgrn2_supported(48, 64, 1) == 0
     assert lib.hgrn2_supported(128, 128, 1) == 0

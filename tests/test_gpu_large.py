@@ -5,7 +5,8 @@ kernels and chunk size of the training workload.  Full resets (f = 0) every
 so the float64 oracle recomputes whole windows on their own: the one that
 holds the 4 GiB byte offset of the token tensors, the last (ragged) one, and
 the first, at the highest and lowest (b, h).  Normwise relative error per
-window <= 2e-2."""
+window <= 2e-2 (every slice, row and element of the window).  The forward
+without stored states (segmented) is checked on the same windows."""
 import numpy as np
 import pytest
 
@@ -28,6 +29,9 @@ def test_token_tensors_beyond_4gib():
     dq, dk, dv, dl, _ = m.bwd(q, k, v, lf, dy, None, None, st, chunk=C, want_dh0=False)
     torch.cuda.synchronize()
     del st
+    # the forward without stored states (segments walked with the state on chip)
+    ys, _, _ = m.fwd(q, k, v, lf, None, chunk=C, want_ht=False)
+    torch.cuda.synchronize()
     # token of b = 1 at element 2^31 (byte offset 2^32 of a bf16 tensor)
     t_cross = (1 << 31) // (H * D) - T
     windows = [(1, H - 1, (t_cross // R) * R), (1, H - 1, ((T - 1) // R) * R), (0, 0, 0), (1, 3, (t_cross // R) * R)]
@@ -37,12 +41,12 @@ def test_token_tensors_beyond_4gib():
         w = {n: host(x[n], b, h, t0, t1) for n in ("q", "k", "v", "log_f", "dy")}
         yr, _ = oracle.forward(w["q"], w["k"], w["v"], w["log_f"], None)
         gr = oracle.backward(w["q"], w["k"], w["v"], w["log_f"], w["dy"], None, None)
-        errs = {"y": slice_rel(host(y, b, h, t0, t1), yr)}
+        errs = {"y": slice_rel(host(y, b, h, t0, t1), yr), "y (no states)": slice_rel(host(ys, b, h, t0, t1), yr)}
         for name, a, r in zip(("dq", "dk", "dv", "dlog_f"), (dq, dk, dv, dl), gr[:4]):
             errs[name] = slice_rel(host(a, b, h, t0, t1), r)
         print("window b=%d h=%d tokens %d..%d: %s" % (b, h, t0, t1, " ".join("%s %.3e" % e for e in errs.items())),
               flush=True)
         for name, e in errs.items():
             assert e <= TOL["bf16"], (name, e)
-    del x, q, k, v, lf, dy, y, dq, dk, dv, dl
+    del x, q, k, v, lf, dy, y, ys, dq, dk, dv, dl
     torch.cuda.empty_cache()
