@@ -28,7 +28,9 @@
  *   - dtype: HGRN2_F32 (float) or HGRN2_BF16 (bfloat16 bits).  y and all
  *     token gradients have the input dtype.  Accumulation is float32.
  *   - Supported sizes: DK == DV == D in {16, 32, 64, 128}; chunk in
- *     {16, 32, 64}; any B, H >= 1 and T >= 1 (a partial last chunk is masked).
+ *     {16, 32, 64, 128} (float32 at D = 128 only up to chunk 64: its chunk-128
+ *     tiles exceed the 160 KB of LDS); any B, H >= 1 and T >= 1 (a partial
+ *     last chunk is masked).
  *     hgrn2_supported() tells which (D, chunk, dtype) combinations have a
  *     kernel; others return HGRN2_ERR_UNSUPPORTED.  Kernels address a
  *     chunk's token rows and one sequence's chunk-boundary states with 32-bit

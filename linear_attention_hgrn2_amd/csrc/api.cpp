@@ -22,7 +22,7 @@ hgrn2_status fail(hgrn2_status s, const std::string &msg) {
 }
 
 bool valid_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
-bool valid_chunk(int c) { return c == 16 || c == 32 || c == 64; }
+bool valid_chunk(int c) { return c == 16 || c == 32 || c == 64 || c == 128; }
 bool valid_dtype(int t) { return t == HGRN2_F32 || t == HGRN2_BF16; }
 size_t dsize(int t) { return t == HGRN2_BF16 ? 2 : 4; }
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -78,7 +78,7 @@ hgrn2_status check_common(int B, int T, int H, int DK, int DV, int chunk, int dt
   }
   if (DK != DV || !valid_d(DK))
     return fail(HGRN2_ERR_UNSUPPORTED, "need DK == DV in {16, 32, 64, 128}");
-  if (!valid_chunk(chunk)) return fail(HGRN2_ERR_UNSUPPORTED, "chunk must be 16, 32 or 64");
+  if (!valid_chunk(chunk)) return fail(HGRN2_ERR_UNSUPPORTED, "chunk must be 16, 32, 64 or 128");
   {
     // work-items of the state scans (workgroups of eight (b, h) at a time) and
     // of the chunk kernels (one workgroup per chunk)

@@ -54,11 +54,25 @@ template <typename T, int D, int C> struct CbwdCfg {
   static constexpr int VS = D * D / EPV, NVS = (VS + NT - 1) / NT;
   static constexpr int LDG = D + 4;  // staging row stride (floats)
   static constexpr int LD = RowTile<T, D>::LD;
+  // the gap factors are tabulated where the table fits the LDS beside the
+  // tiles (chunk 64 and below); at chunk 128 they are formed where used
+  static constexpr size_t kTileBytes = 4 * (size_t)C * LD * sizeof(T) + (size_t)NB * D * 4 + 16;
+  static constexpr size_t kOutBytes = (2 * (size_t)NW * 16 * LDG + 2 * (size_t)NW * D + D) * 4;
+  static constexpr size_t kFixed = ((size_t)NW * 2 * D + D) * 4;
+  static constexpr bool GPT =
+      kFixed + (kTileBytes + (size_t)NW * NB * D * sizeof(T) > kOutBytes ? kTileBytes + (size_t)NW * NB * D * sizeof(T)
+                                                                         : kOutBytes) <=
+      160 * 1024;
   struct In {
     float Lb[NB][D];  // sub-block totals of log f
-    T gp[NW][NB][D];  // wave w: gap factor of its pair with block m (the same
-                      // rounded value on both sides of a pair)
-    T qo[C * LD], ko[C * LD], v[C * LD], dy[C * LD];  // RowTile<T, D>
+    T gp[GPT ? NW : 1][GPT ? NB : 1][GPT ? D : 1];  // wave w: gap factor of its pair with block m
+                                                   // (the same rounded value on both sides of a pair)
+    float Pp[GPT ? 1 : NB + 1][GPT ? 1 : D];        // without the table: prefix sums P_i of the totals
+    // RowTile<T, D> tiles, read and written 16 bytes at a time
+    alignas(16) T qo[C * LD];
+    alignas(16) T ko[C * LD];
+    alignas(16) T v[C * LD];
+    alignas(16) T dy[C * LD];
   };
   struct SL {
     T S[D * LD];  // RowTile<T, D>: the chunk's initial state (row c, column j)
@@ -197,20 +211,47 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
         Pw1 += (i <= w) ? Li : 0.f;
       }
       const float G = P[NB], Lw = sm.u.in.Lb[w][c];
+      if constexpr (Cfg::GPT) {
 #pragma unroll
-      for (int m = 0; m < NB; ++m) {
-        float x;
-        if (m < w) x = Pw - P[m + 1];
-        else if (m == w) x = fminf(-Lw, 80.f);
-        else x = P[m] - Pw1;
-        sm.u.in.gp[w][m][c] = from_f32<T>(__expf(x));
+        for (int m = 0; m < NB; ++m) {
+          float x;
+          if (m < w) x = Pw - P[m + 1];
+          else if (m == w) x = fminf(-Lw, 80.f);
+          else x = P[m] - Pw1;
+          sm.u.in.gp[w][m][c] = from_f32<T>(__expf(x));
+        }
+      } else {
+        // every wave forms the same prefix sums; wave 0 keeps them
+        if (w == 0) {
+#pragma unroll
+          for (int i = 0; i <= NB; ++i) sm.u.in.Pp[i][c] = P[i];
+        }
       }
       sm.fac[w][0][c] = __expf(Pw);
       sm.fac[w][1][c] = __expf(G - Pw1);
       if (w == 0) sm.eG[c] = __expf(G);
     }
   }
-  wave_lds_sync();
+  // the table is per wave; the prefix sums are read by every wave
+  if constexpr (Cfg::GPT) {
+    wave_lds_sync();
+  } else {
+    __syncthreads();
+  }
+
+  // the gap factor of block w's pair with block m at channel c, rounded to T:
+  // from the table, or formed again from the prefix sums with the table's
+  // arithmetic (the same sums, so the same bits on both sides of a pair)
+  auto gap = [&](int m, int c) -> float {
+    if constexpr (Cfg::GPT) {
+      return to_f32(sm.u.in.gp[w][m][c]);
+    } else {
+      const float x = m < w    ? sm.u.in.Pp[w][c] - sm.u.in.Pp[m + 1][c]
+                      : m == w ? fminf(-sm.u.in.Lb[w][c], 80.f)
+                               : sm.u.in.Pp[m][c] - sm.u.in.Pp[w + 1][c];
+      return to_f32(from_f32<T>(__expf(x)));
+    }
+  };
 
   // =============== phase 1b: products
   f32x4_t DQ[CB], DK[CB], DV[CB];
@@ -246,7 +287,7 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
       f32x4_t tmp;
       acc_zero(tmp);
       mma16(tmp, fa, tr4<D>(ko, 16 * m, 16 * cb));
-      const float gpf = to_f32(sm.u.in.gp[w][m][16 * cb + n16]);
+      const float gpf = gap(m, 16 * cb + n16);
 #pragma unroll
       for (int r = 0; r < 4; ++r) DQ[cb][r] += gpf * tmp[r];
     }
@@ -278,7 +319,7 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
         f32x4_t tmp;
         acc_zero(tmp);
         mma16(tmp, fa, tr4<D>(qo, 16 * m, 16 * cb));
-        const float gpf = to_f32(sm.u.in.gp[w][m][16 * cb + n16]);
+        const float gpf = gap(m, 16 * cb + n16);
 #pragma unroll
         for (int r = 0; r < 4; ++r) DK[cb][r] += gpf * tmp[r];
       }
@@ -295,7 +336,12 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
         float kv[8];
         unpack8(row8<D>(ko, 16 * w + n16, c), kv);
         float gv[8];
-        unpack8(ld8(&sm.u.in.gp[w][m][c]), gv);
+        if constexpr (Cfg::GPT) {
+          unpack8(ld8(&sm.u.in.gp[w][m][c]), gv);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) gv[e] = gap(m, c + e);
+        }
         Frag fb;
 #pragma unroll
         for (int i = 0; i < 8; ++i) fb.v[i] = kv[i] * gv[i];

@@ -16,13 +16,17 @@ template <typename T, int D, int C> struct ChunkBwdOp {
     }
   }
   static hipError_t run(int gm, const ChunkBwdArgs *a, hipStream_t s) {
-    static_assert(sizeof(typename CbwdCfg<T, D, C>::Smem) <= 160 * 1024, "LDS");
-    if (gm < kUntied || gm > kScalar) return hipErrorNotSupported;
-    if (!a) return hipSuccess;
-    if (gm == kTied) return go<kTied>(*a, s);
-    if (gm == kGate) return go<kGate>(*a, s);
-    if (gm == kScalar) return go<kScalar>(*a, s);
-    return go<kUntied>(*a, s);
+    // tiles too large for the 160 KB LDS (float32 at D = 128, chunk 128): no kernel
+    if constexpr (sizeof(typename CbwdCfg<T, D, C>::Smem) > 160 * 1024) {
+      return hipErrorNotSupported;
+    } else {
+      if (gm < kUntied || gm > kScalar) return hipErrorNotSupported;
+      if (!a) return hipSuccess;
+      if (gm == kTied) return go<kTied>(*a, s);
+      if (gm == kGate) return go<kGate>(*a, s);
+      if (gm == kScalar) return go<kScalar>(*a, s);
+      return go<kUntied>(*a, s);
+    }
   }
 };
 

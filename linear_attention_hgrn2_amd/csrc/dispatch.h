@@ -20,6 +20,7 @@ hipError_t run_c(int C, A... args) {
     case 16: return Op<T, D, 16>::run(args...);
     case 32: return Op<T, D, 32>::run(args...);
     case 64: return Op<T, D, 64>::run(args...);
+    case 128: return Op<T, D, 128>::run(args...);
   }
   return hipErrorNotSupported;
 }

@@ -7,17 +7,22 @@ template <typename T, int D, int C> struct ScanOp {
   // the adjoint scan never reads k: it runs in the untied form or, when log f
   // is formed from the gate pre-activation or read per head, in that mode
   static hipError_t run(bool reverse, int gm, const ScanArgs *a, hipStream_t s) {
-    if (gm < kUntied || gm > kScalar || (reverse && gm == kTied)) return hipErrorNotSupported;
-    if (!a) return hipSuccess;
-    if (reverse) {
-      if (gm == kGate) return launch_scan<T, D, C, true, kGate>(*a, s);
-      if (gm == kScalar) return launch_scan<T, D, C, true, kScalar>(*a, s);
-      return launch_scan<T, D, C, true>(*a, s);
+    // tiles too large for the 160 KB LDS (float32 at D = 128, chunk 128): no kernel
+    if constexpr (sizeof(typename ScanCfg<T, D, C, false>::Smem) > 160 * 1024) {
+      return hipErrorNotSupported;
+    } else {
+      if (gm < kUntied || gm > kScalar || (reverse && gm == kTied)) return hipErrorNotSupported;
+      if (!a) return hipSuccess;
+      if (reverse) {
+        if (gm == kGate) return launch_scan<T, D, C, true, kGate>(*a, s);
+        if (gm == kScalar) return launch_scan<T, D, C, true, kScalar>(*a, s);
+        return launch_scan<T, D, C, true>(*a, s);
+      }
+      if (gm == kTied) return launch_scan<T, D, C, false, kTied>(*a, s);
+      if (gm == kGate) return launch_scan<T, D, C, false, kGate>(*a, s);
+      if (gm == kScalar) return launch_scan<T, D, C, false, kScalar>(*a, s);
+      return launch_scan<T, D, C, false>(*a, s);
     }
-    if (gm == kTied) return launch_scan<T, D, C, false, kTied>(*a, s);
-    if (gm == kGate) return launch_scan<T, D, C, false, kGate>(*a, s);
-    if (gm == kScalar) return launch_scan<T, D, C, false, kScalar>(*a, s);
-    return launch_scan<T, D, C, false>(*a, s);
   }
 };
 
@@ -28,8 +33,12 @@ hipError_t dispatch_scan(int dtype, int D, int C, bool reverse, int gm, const Sc
 template <typename T, int D, int C> struct ScanItemsOp {
   static hipError_t run(long long *n) {
     using Cfg = ScanCfg<T, D, C, false>;
-    *n = (long long)Cfg::NS * Cfg::NT;
-    return hipSuccess;
+    if constexpr (sizeof(typename Cfg::Smem) > 160 * 1024) {
+      return hipErrorNotSupported;
+    } else {
+      *n = (long long)Cfg::NS * Cfg::NT;
+      return hipSuccess;
+    }
   }
 };
 

@@ -64,7 +64,9 @@ def test_sizes(lib):
     assert lib.hgrn2_fwd_workspace_bytes(16, 4096, 16, 128, 128, 64, 1, 0) == 256 * (2 * 128 * 128 + 128) * 4
     assert lib.hgrn2_supported(128, 64, 1) == 1
     assert lib.hgrn2_supported(48, 64, 1) == 0
-    assert lib.hgrn2_supported(128, 128, 1) == 0
+    assert lib.hgrn2_supported(128, 128, 1) == 1     # chunk 128, bf16
+    assert lib.hgrn2_supported(128, 128, 0) == 0     # float32 tiles at D 128, chunk 128 exceed the LDS
+    assert lib.hgrn2_supported(64, 128, 0) == 1
 
 
 FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation
@@ -88,6 +90,7 @@ def test_fwd_rejections(lib):
     assert _fwd(lib, DK=48, DV=48) == 2
     assert _fwd(lib, DK=16, DV=32) == 2
     assert _fwd(lib, chunk=24) == 2
+    assert _fwd(lib, chunk=256) == 2
     assert _fwd(lib, y=FAKE, st=FAKE + 0x8000) == 1    # y aliases q
     assert _fwd(lib) == 3                              # no states_out and no workspace
     assert _fwd(lib, ws=FAKE + 0x8000, wsb=100) == 3   # workspace too small

@@ -270,15 +270,15 @@ def test_state_carry_split_is_bitwise(dtype):
 
 
 def test_chunk_sizes_agree_with_each_other():
-    """Chunks of 16, 32 and 64 tokens (bfloat16, d = 128) each meet the oracle's
-    tolerance and agree with one another within it."""
+    """Chunks of 16, 32, 64 and 128 tokens (bfloat16, d = 128) each meet the
+    oracle's tolerance and agree with one another within it."""
     m = _hip()
     import torch
-    d = _case("bf16", B=2, T=4 * 64 + 5, H=2, D=128, lam=0.3, h0std=0.3, qscale=1.0)
+    d = _case("bf16", B=2, T=3 * 128 + 5, H=2, D=128, lam=0.3, h0std=0.3, qscale=1.0)
     q, k, v, lf, dy = (to_dev(d[n], "bf16") for n in ("q", "k", "v", "log_f", "dy"))
     h0 = to_dev(d["h0"], "f32")
     res = {}
-    for C in (16, 32, 64):
+    for C in (16, 32, 64, 128):
         y, ht, st = m.fwd(q, k, v, lf, h0, chunk=C, want_states=True)
         g = m.bwd(q, k, v, lf, dy, h0, None, st, chunk=C)
         res[C] = (y, ht) + tuple(g)
@@ -293,7 +293,7 @@ def test_chunk_sizes_agree_with_each_other():
             assert slice_rel(to_host64(o), r, token_major=tm) <= TOL["bf16"], (C, i)
     for i in range(len(refs)):
         tm = i not in (1, 6)
-        for C in (16, 32):
+        for C in (16, 32, 128):
             e = slice_rel(to_host64(res[C][i]), to_host64(res[64][i]), token_major=tm)
             print("chunk %d vs 64, output %d: %.3e" % (C, i, e), flush=True)
             assert e <= TOL["bf16"], (C, i, e)
