@@ -25,8 +25,13 @@
  *     row-major [B, T, H, D] (D fastest), 16-byte aligned.  States
  *     (h0, ht, dht, dh0, the decode state) are float32 [B, H, DK, DV], DV
  *     fastest, 16-byte aligned.
- *   - dtype: HGRN2_F32 (float) or HGRN2_BF16 (bfloat16 bits).  y and all
- *     token gradients have the input dtype.  Accumulation is float32.
+ *   - dtype: HGRN2_F32 (float) or HGRN2_BF16 (bfloat16 bits), the dtype of
+ *     the token inputs (q, k, v, log_f, dy) and of the stored chunk-boundary
+ *     states and adjoints.  y and all token gradients have the input dtype,
+ *     unless HGRN2_OUT_F32 is or'ed into dtype: then they are float32,
+ *     written straight from the float32 accumulators (no bfloat16 rounding
+ *     of the results).  "output dtype" below means that choice.
+ *     Accumulation is float32.
  *   - Supported sizes: DK == DV == D in {16, 32, 64, 128}; chunk in
  *     {16, 32, 64, 128} (float32 at D = 128 only up to chunk 64: its chunk-128
  *     tiles exceed the 160 KB of LDS); any B, H >= 1 and T >= 1 (a partial
@@ -60,7 +65,7 @@
 extern "C" {
 #endif
 
-#define HGRN2_ABI_VERSION 8
+#define HGRN2_ABI_VERSION 9
 
 typedef enum {
   HGRN2_OK = 0,
@@ -71,6 +76,14 @@ typedef enum {
 } hgrn2_status;
 
 typedef enum { HGRN2_F32 = 0, HGRN2_BF16 = 1 } hgrn2_dtype;
+
+/* Or'ed into the dtype argument of any call (HGRN2_BF16 | HGRN2_OUT_F32):
+ * the call's token outputs (y of the forwards and decode steps; dq, dk, dv
+ * and dlog_f / dz / dlog_a of the backwards) are float32 [.., D] tensors,
+ * 4 bytes per element, while its token inputs, dy included, keep the input
+ * dtype.  A no-op with HGRN2_F32.  Sizes of states, adjoints and workspaces
+ * do not change.  Any other bit set is HGRN2_ERR_INVALID_ARG. */
+#define HGRN2_OUT_F32 0x100
 
 /* HGRN2_ABI_VERSION of the built library. */
 int hgrn2_abi_version(void);
@@ -130,7 +143,7 @@ size_t hgrn2_bwd_workspace_bytes(int B, int T, int H, int DK, int DV, int chunk,
  * the chunk-boundary states go to ws as with states_out.
  *   q, k, log_f : [B,T,H,DK] dtype      v : [B,T,H,DV] dtype
  *   h0          : [B,H,DK,DV] float32, or NULL for a zero initial state
- *   y           : [B,T,H,DV] dtype (written), or NULL (states and ht only)
+ *   y           : [B,T,H,DV] output dtype (written), or NULL (states and ht only)
  *   ht          : [B,H,DK,DV] float32 final state, or NULL (not wanted).
  *                 ht may alias h0.
  *   states_out  : hgrn2_states_bytes() bytes of chunk-boundary states (input
@@ -155,7 +168,8 @@ hgrn2_status hgrn2_fwd(int B, int T, int H, int DK, int DV, int chunk, int dtype
  *                 needs a workspace of hgrn2_states_bytes())
  *   dy          : [B,T,H,DV] dtype
  *   dht         : [B,H,DK,DV] float32, or NULL (zero)
- *   dq, dk, dlog_f : [B,T,H,DK] dtype (written)   dv : [B,T,H,DV] dtype (written)
+ *   dq, dk, dlog_f : [B,T,H,DK] output dtype (written)
+ *   dv          : [B,T,H,DV] output dtype (written)
  *   dh0         : [B,H,DK,DV] float32 (written), or NULL (not wanted)
  *   ws, ws_bytes: workspace of at least hgrn2_bwd_workspace_bytes() bytes
  *                 (always needed: it holds the adjoints).
@@ -197,7 +211,7 @@ hgrn2_status hgrn2_bwd_noalloc(int B, int T, int H, int DK, int DV, int chunk, i
  * hgrn2_fwd(..., y = NULL, states_out = states, ...) wrote (chunkwise form,
  * HGRN2 summary §3.2 p.5): y = (in-chunk decayed scores) v + (q scaled by the
  * in-chunk cumulative decay) S_{start of chunk}.
- *   states : [B,H,N+1,DK,DV] dtype, read      y : [B,T,H,DV] dtype, written
+ *   states : [B,H,N+1,DK,DV] dtype, read      y : [B,T,H,DV] output dtype, written
  */
 hgrn2_status hgrn2_fwd_chunk(int B, int T, int H, int DK, int DV, int chunk, int dtype,
                              const void *q, const void *k, const void *v, const void *log_f,
@@ -233,8 +247,8 @@ hgrn2_status hgrn2_bwd_chunk(int B, int T, int H, int DK, int DV, int chunk, int
  * (b, h), S <- Diag(exp(log_f)) S + k^T v in place, then y = q S.
  *   q, k, log_f : [B,H,DK] dtype      v : [B,H,DV] dtype
  *   state       : [B,H,DK,DV] float32, read and overwritten
- *   y           : [B,H,DV] dtype (written)
- * Any D in {16, 32, 64, 128} with DK == DV; dtype F32 or BF16.
+ *   y           : [B,H,DV] output dtype (written)
+ * Any D in {16, 32, 64, 128} with DK == DV; dtype F32 or BF16 (| HGRN2_OUT_F32).
  */
 hgrn2_status hgrn2_decode_step(int B, int H, int DK, int DV, int dtype, const void *q,
                                const void *k, const void *v, const void *log_f,
@@ -285,7 +299,7 @@ hgrn2_status hgrn2_decode_step_tied(int B, int H, int DK, int DV, int dtype, con
  *
  * hgrn2_bwd_gate returns, with G = dlog_f - f dk the total derivative through
  * log f (the tied-gate backward's dlog_f) and s = sigmoid(z), s' = sigmoid(-z):
- *     dz            = G (1 - lb) s s' / f                    [B, T, H, DK], input dtype
+ *     dz            = G (1 - lb) s s' / f                    [B, T, H, DK], output dtype
  *     dlower_bound  = sum over b and t of G s' / f            [H, DK], float32, overwritten
  * and no dk.  dlower_bound is summed per chunk into the workspace and then over
  * chunks in a fixed order (repeat runs agree bit for bit).  Its workspace is
@@ -316,7 +330,7 @@ hgrn2_status hgrn2_decode_step_gate(int B, int H, int DK, int DV, int dtype, con
  * dimension).  These entry points take log_a [B, T, H] (input dtype; decode:
  * [B, H]) in place of log_f, the same for every row of head h's state:
  *     S_t = a_t S_{t-1} + k_t^T v_t,        y_t = q_t S_t,
- * with k an input.  The backward returns dlog_a [B, T, H] (input dtype), the
+ * with k an input.  The backward returns dlog_a [B, T, H] (output dtype), the
  * sum over the head's channels of the per-channel derivative, and dk.  The
  * log-decay bytes shrink by D.  Everything else (layouts, states, workspaces,
  * errors, gate preconditions on log_a) is as for the untied calls.
@@ -344,9 +358,10 @@ hgrn2_status hgrn2_decode_step_scalar(int B, int H, int DK, int DV, int dtype, c
  * with d_k = d_v = 1.  C = the channels of a token row (heads times head
  * width), any even C >= 2 with 32*C*E < 2^32 (E the element size: a
  * segment's rows are addressed with 32-bit byte offsets); any B, T >= 1 with
- * B*C <= 2^30 and B*T*C <= 2^40.  Token tensors [B, T, C] in dtype,
- * 16-byte aligned; h0, hT, dht, dh0 float32 [B, C] (optional, NULL = zero /
- * not written).
+ * B*C <= 2^30 and B*T*C <= 2^40.  Token tensors [B, T, C] in dtype (y and
+ * the gradients in the output dtype, as for the HGRN2 calls), 16-byte
+ * aligned; h0, hT, dht, dh0 float32 [B, C] (optional, NULL = zero / not
+ * written).
  *
  * The sequence is scanned in segments of 32 tokens, eight segments to a
  * group.  states_out (optional) receives the state entering every segment,

@@ -19,6 +19,21 @@ LIB_PATH = os.path.join(_HERE, "libhgrn2.so")
 
 F32, BF16 = 0, 1
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
+# HGRN2_OUT_F32 of include/hgrn2.h: or'ed into a dtype code, float32 token outputs
+OUT_F32 = 0x100
+
+
+def _odt(dt, out_dtype):
+    """The token outputs' dtype and the call's dtype code for inputs of dtype
+    dt: out_dtype None (or dt) keeps the input dtype; float32 with bfloat16
+    inputs writes y and the gradients as float32."""
+    if dt not in _DT:
+        raise ValueError("dtype must be float32 or bfloat16")
+    if out_dtype is None or out_dtype == dt:
+        return dt, _DT[dt]
+    if out_dtype == torch.float32:
+        return torch.float32, _DT[dt] | OUT_F32
+    raise ValueError("out_dtype must be None, the input dtype or torch.float32")
 
 
 class HGRN2Error(RuntimeError):
@@ -151,7 +166,7 @@ def states_shape(B, T, H, D, chunk):
 
 
 def fwd(q, k, v, log_f, h0=None, *, chunk=64, want_ht=True, want_states=False, want_y=True,
-        y=None, ht=None, states=None, ws=None):
+        y=None, ht=None, states=None, ws=None, out_dtype=None):
     """Chunked forward.  Returns (y or None, ht or None, states or None).
 
     Without `states` the chunk-boundary states go to a workspace (`ws`, a
@@ -159,15 +174,16 @@ def fwd(q, k, v, log_f, h0=None, *, chunk=64, want_ht=True, want_states=False, w
     if not given).  want_y=False runs the state scan alone (no y)."""
     B, T, H, D = q.shape
     dt = q.dtype
+    odt, code = _odt(dt, out_dtype)
     if dt not in _DT:
         raise ValueError("dtype must be float32 or bfloat16")
     for n, t in (("q", q), ("k", k), ("v", v), ("log_f", log_f)):
         _tok(n, t, B, T, H, D, dt)
     _st("h0", h0, B, H, D)
     if want_y and y is None:
-        y = torch.empty_like(q)
+        y = torch.empty_like(q, dtype=odt)
     if y is not None:
-        _tok("y", y, B, T, H, D, dt)
+        _tok("y", y, B, T, H, D, odt)
     if want_ht and ht is None:
         ht = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
     _st("ht", ht, B, H, D)
@@ -182,27 +198,28 @@ def fwd(q, k, v, log_f, h0=None, *, chunk=64, want_ht=True, want_states=False, w
         if ws is None:
             ws = torch.empty(need, dtype=torch.uint8, device=q.device)
         ws_bytes = ws.numel() * ws.element_size()
-    st = _lib().hgrn2_fwd(B, T, H, D, D, chunk, _DT[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(log_f),
+    st = _lib().hgrn2_fwd(B, T, H, D, D, chunk, code, _ptr(q), _ptr(k), _ptr(v), _ptr(log_f),
                           _ptr(h0), _ptr(y), _ptr(ht), _ptr(states), _ptr(ws), ws_bytes, _stream())
     _check(st, "hgrn2_fwd")
     return y, ht, states
 
 
 def bwd(q, k, v, log_f, dy, h0=None, dht=None, states=None, *, chunk=64, want_dh0=True,
-        dq=None, dk=None, dv=None, dlog_f=None, dh0=None, ws=None):
+        dq=None, dk=None, dv=None, dlog_f=None, dh0=None, ws=None, out_dtype=None):
     """Chunked backward.  Returns (dq, dk, dv, dlog_f, dh0 or None)."""
     B, T, H, D = q.shape
     dt = q.dtype
+    odt, code = _odt(dt, out_dtype)
     for n, t in (("q", q), ("k", k), ("v", v), ("log_f", log_f), ("dy", dy)):
         _tok(n, t, B, T, H, D, dt)
     _st("h0", h0, B, H, D)
     _st("dht", dht, B, H, D)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    dlog_f = torch.empty_like(log_f) if dlog_f is None else dlog_f
+    dq = torch.empty_like(q, dtype=odt) if dq is None else dq
+    dk = torch.empty_like(k, dtype=odt) if dk is None else dk
+    dv = torch.empty_like(v, dtype=odt) if dv is None else dv
+    dlog_f = torch.empty_like(log_f, dtype=odt) if dlog_f is None else dlog_f
     for n, t in (("dq", dq), ("dk", dk), ("dv", dv), ("dlog_f", dlog_f)):
-        _tok(n, t, B, T, H, D, dt)
+        _tok(n, t, B, T, H, D, odt)
     if want_dh0 and dh0 is None:
         dh0 = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
     _st("dh0", dh0, B, H, D)
@@ -213,7 +230,7 @@ def bwd(q, k, v, log_f, dy, h0=None, dht=None, states=None, *, chunk=64, want_dh
     if ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = ws.numel() * ws.element_size()
-    st = _lib().hgrn2_bwd(B, T, H, D, D, chunk, _DT[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(log_f),
+    st = _lib().hgrn2_bwd(B, T, H, D, D, chunk, code, _ptr(q), _ptr(k), _ptr(v), _ptr(log_f),
                           _ptr(h0), _ptr(states), _ptr(dy), _ptr(dht), _ptr(dq), _ptr(dk),
                           _ptr(dv), _ptr(dlog_f), _ptr(dh0), _ptr(ws), ws_bytes, _stream())
     _check(st, "hgrn2_bwd")
@@ -225,28 +242,29 @@ NOALLOC_SCRATCH_BYTES = 256 << 20
 
 
 def bwd_noalloc(q, k, v, log_f, dy, h0=None, dht=None, states=None, *, chunk=64, dq=None, dk=None, dv=None,
-                dlog_f=None, dh0=None, want_dh0=True):
+                dlog_f=None, dh0=None, want_dh0=True, out_dtype=None):
     """hgrn2_bwd_noalloc: the chunked backward with the library's own scratch
     in place of a workspace (the library allocates nothing; outputs not passed
     are allocated here by torch).  Returns (dq, dk, dv, dlog_f, dh0 or None)."""
     B, T, H, D = q.shape
     dt = q.dtype
+    odt, code = _odt(dt, out_dtype)
     for n, t in (("q", q), ("k", k), ("v", v), ("log_f", log_f), ("dy", dy)):
         _tok(n, t, B, T, H, D, dt)
     _st("h0", h0, B, H, D)
     _st("dht", dht, B, H, D)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    dlog_f = torch.empty_like(log_f) if dlog_f is None else dlog_f
+    dq = torch.empty_like(q, dtype=odt) if dq is None else dq
+    dk = torch.empty_like(k, dtype=odt) if dk is None else dk
+    dv = torch.empty_like(v, dtype=odt) if dv is None else dv
+    dlog_f = torch.empty_like(log_f, dtype=odt) if dlog_f is None else dlog_f
     for n, t in (("dq", dq), ("dk", dk), ("dv", dv), ("dlog_f", dlog_f)):
-        _tok(n, t, B, T, H, D, dt)
+        _tok(n, t, B, T, H, D, odt)
     if want_dh0 and dh0 is None:
         dh0 = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
     _st("dh0", dh0, B, H, D)
     if states is not None:
         _states_ok(states, B, T, H, D, chunk, dt)
-    st = _lib().hgrn2_bwd_noalloc(B, T, H, D, D, chunk, _DT[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(log_f), _ptr(h0),
+    st = _lib().hgrn2_bwd_noalloc(B, T, H, D, D, chunk, code, _ptr(q), _ptr(k), _ptr(v), _ptr(log_f), _ptr(h0),
                                   _ptr(states), _ptr(dy), _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dlog_f),
                                   _ptr(dh0), _stream())
     _check(st, "hgrn2_bwd_noalloc")
@@ -264,17 +282,18 @@ def adjoints_shape(B, T, H, D, chunk):
     return (B, H, num_chunks(T, chunk), D, D)
 
 
-def fwd_chunk(q, k, v, log_f, states, *, chunk=64, y=None):
+def fwd_chunk(q, k, v, log_f, states, *, chunk=64, y=None, out_dtype=None):
     """The per-chunk output launch of hgrn2_fwd alone (states from
     fwd(..., want_states=True) or fwd with y computed elsewhere).  Returns y."""
     B, T, H, D = q.shape
     dt = q.dtype
+    odt, code = _odt(dt, out_dtype)
     for n, t in (("q", q), ("k", k), ("v", v), ("log_f", log_f)):
         _tok(n, t, B, T, H, D, dt)
     _states_ok(states, B, T, H, D, chunk, dt)
-    y = torch.empty_like(q) if y is None else y
-    _tok("y", y, B, T, H, D, dt)
-    st = _lib().hgrn2_fwd_chunk(B, T, H, D, D, chunk, _DT[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(log_f),
+    y = torch.empty_like(q, dtype=odt) if y is None else y
+    _tok("y", y, B, T, H, D, odt)
+    st = _lib().hgrn2_fwd_chunk(B, T, H, D, D, chunk, code, _ptr(q), _ptr(k), _ptr(v), _ptr(log_f),
                                 _ptr(states), _ptr(y), _stream())
     _check(st, "hgrn2_fwd_chunk")
     return y
@@ -302,10 +321,11 @@ def bwd_adjoint(q, log_f, dy, dht=None, *, chunk=64, adjoints=None, dh0=None, wa
     return adjoints, dh0
 
 
-def bwd_chunk(q, k, v, log_f, dy, states, adjoints, *, chunk=64, dq=None, dk=None, dv=None, dlog_f=None):
+def bwd_chunk(q, k, v, log_f, dy, states, adjoints, *, chunk=64, dq=None, dk=None, dv=None, dlog_f=None, out_dtype=None):
     """The per-chunk gradient launch of hgrn2_bwd alone.  Returns (dq, dk, dv, dlog_f)."""
     B, T, H, D = q.shape
     dt = q.dtype
+    odt, code = _odt(dt, out_dtype)
     for n, t in (("q", q), ("k", k), ("v", v), ("log_f", log_f), ("dy", dy)):
         _tok(n, t, B, T, H, D, dt)
     _states_ok(states, B, T, H, D, chunk, dt)
@@ -313,30 +333,31 @@ def bwd_chunk(q, k, v, log_f, dy, states, adjoints, *, chunk=64, dq=None, dk=Non
             or not adjoints.is_contiguous():
         raise ValueError("adjoints: expected a contiguous %s tensor of shape %s"
                          % (dt, adjoints_shape(B, T, H, D, chunk)))
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    dlog_f = torch.empty_like(log_f) if dlog_f is None else dlog_f
+    dq = torch.empty_like(q, dtype=odt) if dq is None else dq
+    dk = torch.empty_like(k, dtype=odt) if dk is None else dk
+    dv = torch.empty_like(v, dtype=odt) if dv is None else dv
+    dlog_f = torch.empty_like(log_f, dtype=odt) if dlog_f is None else dlog_f
     for n, t in (("dq", dq), ("dk", dk), ("dv", dv), ("dlog_f", dlog_f)):
-        _tok(n, t, B, T, H, D, dt)
-    st = _lib().hgrn2_bwd_chunk(B, T, H, D, D, chunk, _DT[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(log_f),
+        _tok(n, t, B, T, H, D, odt)
+    st = _lib().hgrn2_bwd_chunk(B, T, H, D, D, chunk, code, _ptr(q), _ptr(k), _ptr(v), _ptr(log_f),
                                 _ptr(states), _ptr(adjoints), _ptr(dy), _ptr(dq), _ptr(dk), _ptr(dv),
                                 _ptr(dlog_f), _stream())
     _check(st, "hgrn2_bwd_chunk")
     return dq, dk, dv, dlog_f
 
 
-def decode_step(q, k, v, log_f, state, *, y=None):
+def decode_step(q, k, v, log_f, state, *, y=None, out_dtype=None):
     """One recurrent step; `state` [B,H,D,D] float32 is updated in place.  Returns y [B,H,D]."""
     B, H, D = q.shape
     dt = q.dtype
+    odt, code = _odt(dt, out_dtype)
     for n, t in (("q", q), ("k", k), ("v", v), ("log_f", log_f)):
         if t.shape != (B, H, D) or t.dtype != dt or not t.is_cuda or not t.is_contiguous():
             raise ValueError("%s: expected a contiguous %s CUDA tensor of shape %s" % (n, dt, (B, H, D)))
     _st("state", state, B, H, D)
     if y is None:
-        y = torch.empty_like(q)
-    st = _lib().hgrn2_decode_step(B, H, D, D, _DT[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(log_f),
+        y = torch.empty_like(q, dtype=odt)
+    st = _lib().hgrn2_decode_step(B, H, D, D, code, _ptr(q), _ptr(k), _ptr(v), _ptr(log_f),
                                   _ptr(state), _ptr(y), _stream())
     _check(st, "hgrn2_decode_step")
     return y
@@ -347,19 +368,20 @@ def decode_step(q, k, v, log_f, state, *, y=None):
 # derivative with respect to log_f and no dk.
 
 def fwd_tied(q, v, log_f, h0=None, *, chunk=64, want_ht=True, want_states=False, want_y=True,
-             y=None, ht=None, states=None, ws=None):
+             y=None, ht=None, states=None, ws=None, out_dtype=None):
     """Chunked forward with tied gates.  Returns (y or None, ht or None, states or None)."""
     B, T, H, D = q.shape
     dt = q.dtype
+    odt, code = _odt(dt, out_dtype)
     if dt not in _DT:
         raise ValueError("dtype must be float32 or bfloat16")
     for n, t in (("q", q), ("v", v), ("log_f", log_f)):
         _tok(n, t, B, T, H, D, dt)
     _st("h0", h0, B, H, D)
     if want_y and y is None:
-        y = torch.empty_like(q)
+        y = torch.empty_like(q, dtype=odt)
     if y is not None:
-        _tok("y", y, B, T, H, D, dt)
+        _tok("y", y, B, T, H, D, odt)
     if want_ht and ht is None:
         ht = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
     _st("ht", ht, B, H, D)
@@ -373,26 +395,27 @@ def fwd_tied(q, v, log_f, h0=None, *, chunk=64, want_ht=True, want_states=False,
         if ws is None:
             ws = torch.empty(need, dtype=torch.uint8, device=q.device)
         ws_bytes = ws.numel() * ws.element_size()
-    st = _lib().hgrn2_fwd_tied(B, T, H, D, D, chunk, _DT[dt], _ptr(q), _ptr(v), _ptr(log_f), _ptr(h0),
+    st = _lib().hgrn2_fwd_tied(B, T, H, D, D, chunk, code, _ptr(q), _ptr(v), _ptr(log_f), _ptr(h0),
                                _ptr(y), _ptr(ht), _ptr(states), _ptr(ws), ws_bytes, _stream())
     _check(st, "hgrn2_fwd_tied")
     return y, ht, states
 
 
 def bwd_tied(q, v, log_f, dy, h0=None, dht=None, states=None, *, chunk=64, want_dh0=True,
-             dq=None, dv=None, dlog_f=None, dh0=None, ws=None):
+             dq=None, dv=None, dlog_f=None, dh0=None, ws=None, out_dtype=None):
     """Chunked backward with tied gates.  Returns (dq, dv, dlog_f total, dh0 or None)."""
     B, T, H, D = q.shape
     dt = q.dtype
+    odt, code = _odt(dt, out_dtype)
     for n, t in (("q", q), ("v", v), ("log_f", log_f), ("dy", dy)):
         _tok(n, t, B, T, H, D, dt)
     _st("h0", h0, B, H, D)
     _st("dht", dht, B, H, D)
-    dq = torch.empty_like(q) if dq is None else dq
-    dv = torch.empty_like(v) if dv is None else dv
-    dlog_f = torch.empty_like(log_f) if dlog_f is None else dlog_f
+    dq = torch.empty_like(q, dtype=odt) if dq is None else dq
+    dv = torch.empty_like(v, dtype=odt) if dv is None else dv
+    dlog_f = torch.empty_like(log_f, dtype=odt) if dlog_f is None else dlog_f
     for n, t in (("dq", dq), ("dv", dv), ("dlog_f", dlog_f)):
-        _tok(n, t, B, T, H, D, dt)
+        _tok(n, t, B, T, H, D, odt)
     if want_dh0 and dh0 is None:
         dh0 = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
     _st("dh0", dh0, B, H, D)
@@ -402,32 +425,34 @@ def bwd_tied(q, v, log_f, dy, h0=None, dht=None, states=None, *, chunk=64, want_
     if ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = ws.numel() * ws.element_size()
-    st = _lib().hgrn2_bwd_tied(B, T, H, D, D, chunk, _DT[dt], _ptr(q), _ptr(v), _ptr(log_f), _ptr(h0),
+    st = _lib().hgrn2_bwd_tied(B, T, H, D, D, chunk, code, _ptr(q), _ptr(v), _ptr(log_f), _ptr(h0),
                                _ptr(states), _ptr(dy), _ptr(dht), _ptr(dq), _ptr(dv), _ptr(dlog_f), _ptr(dh0),
                                _ptr(ws), ws_bytes, _stream())
     _check(st, "hgrn2_bwd_tied")
     return dq, dv, dlog_f, dh0
 
 
-def fwd_chunk_tied(q, v, log_f, states, *, chunk=64, y=None):
+def fwd_chunk_tied(q, v, log_f, states, *, chunk=64, y=None, out_dtype=None):
     """The per-chunk output launch of hgrn2_fwd_tied alone.  Returns y."""
     B, T, H, D = q.shape
     dt = q.dtype
+    odt, code = _odt(dt, out_dtype)
     for n, t in (("q", q), ("v", v), ("log_f", log_f)):
         _tok(n, t, B, T, H, D, dt)
     _states_ok(states, B, T, H, D, chunk, dt)
-    y = torch.empty_like(q) if y is None else y
-    _tok("y", y, B, T, H, D, dt)
-    st = _lib().hgrn2_fwd_chunk_tied(B, T, H, D, D, chunk, _DT[dt], _ptr(q), _ptr(v), _ptr(log_f),
+    y = torch.empty_like(q, dtype=odt) if y is None else y
+    _tok("y", y, B, T, H, D, odt)
+    st = _lib().hgrn2_fwd_chunk_tied(B, T, H, D, D, chunk, code, _ptr(q), _ptr(v), _ptr(log_f),
                                      _ptr(states), _ptr(y), _stream())
     _check(st, "hgrn2_fwd_chunk_tied")
     return y
 
 
-def bwd_chunk_tied(q, v, log_f, dy, states, adjoints, *, chunk=64, dq=None, dv=None, dlog_f=None):
+def bwd_chunk_tied(q, v, log_f, dy, states, adjoints, *, chunk=64, dq=None, dv=None, dlog_f=None, out_dtype=None):
     """The per-chunk gradient launch of hgrn2_bwd_tied alone.  Returns (dq, dv, dlog_f total)."""
     B, T, H, D = q.shape
     dt = q.dtype
+    odt, code = _odt(dt, out_dtype)
     for n, t in (("q", q), ("v", v), ("log_f", log_f), ("dy", dy)):
         _tok(n, t, B, T, H, D, dt)
     _states_ok(states, B, T, H, D, chunk, dt)
@@ -435,28 +460,29 @@ def bwd_chunk_tied(q, v, log_f, dy, states, adjoints, *, chunk=64, dq=None, dv=N
             or not adjoints.is_contiguous():
         raise ValueError("adjoints: expected a contiguous %s tensor of shape %s"
                          % (dt, adjoints_shape(B, T, H, D, chunk)))
-    dq = torch.empty_like(q) if dq is None else dq
-    dv = torch.empty_like(v) if dv is None else dv
-    dlog_f = torch.empty_like(log_f) if dlog_f is None else dlog_f
+    dq = torch.empty_like(q, dtype=odt) if dq is None else dq
+    dv = torch.empty_like(v, dtype=odt) if dv is None else dv
+    dlog_f = torch.empty_like(log_f, dtype=odt) if dlog_f is None else dlog_f
     for n, t in (("dq", dq), ("dv", dv), ("dlog_f", dlog_f)):
-        _tok(n, t, B, T, H, D, dt)
-    st = _lib().hgrn2_bwd_chunk_tied(B, T, H, D, D, chunk, _DT[dt], _ptr(q), _ptr(v), _ptr(log_f), _ptr(states),
+        _tok(n, t, B, T, H, D, odt)
+    st = _lib().hgrn2_bwd_chunk_tied(B, T, H, D, D, chunk, code, _ptr(q), _ptr(v), _ptr(log_f), _ptr(states),
                                      _ptr(adjoints), _ptr(dy), _ptr(dq), _ptr(dv), _ptr(dlog_f), _stream())
     _check(st, "hgrn2_bwd_chunk_tied")
     return dq, dv, dlog_f
 
 
-def decode_step_tied(q, v, log_f, state, *, y=None):
+def decode_step_tied(q, v, log_f, state, *, y=None, out_dtype=None):
     """One recurrent step with k = 1 - exp(log_f); `state` is updated in place.  Returns y."""
     B, H, D = q.shape
     dt = q.dtype
+    odt, code = _odt(dt, out_dtype)
     for n, t in (("q", q), ("v", v), ("log_f", log_f)):
         if t.shape != (B, H, D) or t.dtype != dt or not t.is_cuda or not t.is_contiguous():
             raise ValueError("%s: expected a contiguous %s CUDA tensor of shape %s" % (n, dt, (B, H, D)))
     _st("state", state, B, H, D)
     if y is None:
-        y = torch.empty_like(q)
-    st = _lib().hgrn2_decode_step_tied(B, H, D, D, _DT[dt], _ptr(q), _ptr(v), _ptr(log_f), _ptr(state), _ptr(y),
+        y = torch.empty_like(q, dtype=odt)
+    st = _lib().hgrn2_decode_step_tied(B, H, D, D, code, _ptr(q), _ptr(v), _ptr(log_f), _ptr(state), _ptr(y),
                                        _stream())
     _check(st, "hgrn2_decode_step_tied")
     return y
@@ -469,12 +495,13 @@ def _lb(lower_bound, H, D, device):
 
 
 def fwd_gate(q, v, z, lower_bound, h0=None, *, chunk=64, want_ht=True, want_states=False, want_y=True,
-             y=None, ht=None, states=None, ws=None):
+             y=None, ht=None, states=None, ws=None, out_dtype=None):
     """Chunked forward with the gate formed from its pre-activation z and the
     lower bound [H, D] (f = lb + (1 - lb) sigmoid(z), k = 1 - f).
     Returns (y or None, ht or None, states or None)."""
     B, T, H, D = q.shape
     dt = q.dtype
+    odt, code = _odt(dt, out_dtype)
     if dt not in _DT:
         raise ValueError("dtype must be float32 or bfloat16")
     for n, t in (("q", q), ("v", v), ("z", z)):
@@ -482,9 +509,9 @@ def fwd_gate(q, v, z, lower_bound, h0=None, *, chunk=64, want_ht=True, want_stat
     _lb(lower_bound, H, D, q.device)
     _st("h0", h0, B, H, D)
     if want_y and y is None:
-        y = torch.empty_like(q)
+        y = torch.empty_like(q, dtype=odt)
     if y is not None:
-        _tok("y", y, B, T, H, D, dt)
+        _tok("y", y, B, T, H, D, odt)
     if want_ht and ht is None:
         ht = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
     _st("ht", ht, B, H, D)
@@ -498,28 +525,29 @@ def fwd_gate(q, v, z, lower_bound, h0=None, *, chunk=64, want_ht=True, want_stat
         if ws is None:
             ws = torch.empty(need, dtype=torch.uint8, device=q.device)
         ws_bytes = ws.numel() * ws.element_size()
-    st = _lib().hgrn2_fwd_gate(B, T, H, D, D, chunk, _DT[dt], _ptr(q), _ptr(v), _ptr(z), _ptr(lower_bound),
+    st = _lib().hgrn2_fwd_gate(B, T, H, D, D, chunk, code, _ptr(q), _ptr(v), _ptr(z), _ptr(lower_bound),
                                _ptr(h0), _ptr(y), _ptr(ht), _ptr(states), _ptr(ws), ws_bytes, _stream())
     _check(st, "hgrn2_fwd_gate")
     return y, ht, states
 
 
 def bwd_gate(q, v, z, lower_bound, dy, h0=None, dht=None, states=None, *, chunk=64, want_dh0=True,
-             dq=None, dv=None, dz=None, dlower_bound=None, dh0=None, ws=None):
+             dq=None, dv=None, dz=None, dlower_bound=None, dh0=None, ws=None, out_dtype=None):
     """Chunked backward with the gate formed from its pre-activation.
     Returns (dq, dv, dz, dlower_bound [H, D] float32, dh0 or None)."""
     B, T, H, D = q.shape
     dt = q.dtype
+    odt, code = _odt(dt, out_dtype)
     for n, t in (("q", q), ("v", v), ("z", z), ("dy", dy)):
         _tok(n, t, B, T, H, D, dt)
     _lb(lower_bound, H, D, q.device)
     _st("h0", h0, B, H, D)
     _st("dht", dht, B, H, D)
-    dq = torch.empty_like(q) if dq is None else dq
-    dv = torch.empty_like(v) if dv is None else dv
-    dz = torch.empty_like(z) if dz is None else dz
+    dq = torch.empty_like(q, dtype=odt) if dq is None else dq
+    dv = torch.empty_like(v, dtype=odt) if dv is None else dv
+    dz = torch.empty_like(z, dtype=odt) if dz is None else dz
     for n, t in (("dq", dq), ("dv", dv), ("dz", dz)):
-        _tok(n, t, B, T, H, D, dt)
+        _tok(n, t, B, T, H, D, odt)
     if dlower_bound is None:
         dlower_bound = torch.empty((H, D), dtype=torch.float32, device=q.device)
     _lb(dlower_bound, H, D, q.device)
@@ -532,37 +560,39 @@ def bwd_gate(q, v, z, lower_bound, dy, h0=None, dht=None, states=None, *, chunk=
     if ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = ws.numel() * ws.element_size()
-    st = _lib().hgrn2_bwd_gate(B, T, H, D, D, chunk, _DT[dt], _ptr(q), _ptr(v), _ptr(z), _ptr(lower_bound),
+    st = _lib().hgrn2_bwd_gate(B, T, H, D, D, chunk, code, _ptr(q), _ptr(v), _ptr(z), _ptr(lower_bound),
                                _ptr(h0), _ptr(states), _ptr(dy), _ptr(dht), _ptr(dq), _ptr(dv), _ptr(dz),
                                _ptr(dlower_bound), _ptr(dh0), _ptr(ws), ws_bytes, _stream())
     _check(st, "hgrn2_bwd_gate")
     return dq, dv, dz, dlower_bound, dh0
 
 
-def decode_step_gate(q, v, z, lower_bound, state, *, y=None):
+def decode_step_gate(q, v, z, lower_bound, state, *, y=None, out_dtype=None):
     """One recurrent step with the gate formed from z [B, H, D] and the lower
     bound [H, D]; `state` is updated in place.  Returns y."""
     B, H, D = q.shape
     dt = q.dtype
+    odt, code = _odt(dt, out_dtype)
     for n, t in (("q", q), ("v", v), ("z", z)):
         if t.shape != (B, H, D) or t.dtype != dt or not t.is_cuda or not t.is_contiguous():
             raise ValueError("%s: expected a contiguous %s CUDA tensor of shape %s" % (n, dt, (B, H, D)))
     _lb(lower_bound, H, D, q.device)
     _st("state", state, B, H, D)
     if y is None:
-        y = torch.empty_like(q)
-    st = _lib().hgrn2_decode_step_gate(B, H, D, D, _DT[dt], _ptr(q), _ptr(v), _ptr(z), _ptr(lower_bound),
+        y = torch.empty_like(q, dtype=odt)
+    st = _lib().hgrn2_decode_step_gate(B, H, D, D, code, _ptr(q), _ptr(v), _ptr(z), _ptr(lower_bound),
                                        _ptr(state), _ptr(y), _stream())
     _check(st, "hgrn2_decode_step_gate")
     return y
 
 
 def fwd_scalar(q, k, v, log_a, h0=None, *, chunk=64, want_ht=True, want_states=False, want_y=True,
-               y=None, ht=None, states=None, ws=None):
+               y=None, ht=None, states=None, ws=None, out_dtype=None):
     """Chunked forward with one decay per head, log_a [B, T, H].
     Returns (y or None, ht or None, states or None)."""
     B, T, H, D = q.shape
     dt = q.dtype
+    odt, code = _odt(dt, out_dtype)
     if dt not in _DT:
         raise ValueError("dtype must be float32 or bfloat16")
     for n, t in (("q", q), ("k", k), ("v", v)):
@@ -570,9 +600,9 @@ def fwd_scalar(q, k, v, log_a, h0=None, *, chunk=64, want_ht=True, want_states=F
     _tok3("log_a", log_a, B, T, H, dt)
     _st("h0", h0, B, H, D)
     if want_y and y is None:
-        y = torch.empty_like(q)
+        y = torch.empty_like(q, dtype=odt)
     if y is not None:
-        _tok("y", y, B, T, H, D, dt)
+        _tok("y", y, B, T, H, D, odt)
     if want_ht and ht is None:
         ht = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
     _st("ht", ht, B, H, D)
@@ -586,29 +616,30 @@ def fwd_scalar(q, k, v, log_a, h0=None, *, chunk=64, want_ht=True, want_states=F
         if ws is None:
             ws = torch.empty(need, dtype=torch.uint8, device=q.device)
         ws_bytes = ws.numel() * ws.element_size()
-    st = _lib().hgrn2_fwd_scalar(B, T, H, D, D, chunk, _DT[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(h0),
+    st = _lib().hgrn2_fwd_scalar(B, T, H, D, D, chunk, code, _ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(h0),
                                  _ptr(y), _ptr(ht), _ptr(states), _ptr(ws), ws_bytes, _stream())
     _check(st, "hgrn2_fwd_scalar")
     return y, ht, states
 
 
 def bwd_scalar(q, k, v, log_a, dy, h0=None, dht=None, states=None, *, chunk=64, want_dh0=True,
-               dq=None, dk=None, dv=None, dlog_a=None, dh0=None, ws=None):
+               dq=None, dk=None, dv=None, dlog_a=None, dh0=None, ws=None, out_dtype=None):
     """Chunked backward with one decay per head.  Returns (dq, dk, dv, dlog_a [B, T, H], dh0 or None)."""
     B, T, H, D = q.shape
     dt = q.dtype
+    odt, code = _odt(dt, out_dtype)
     for n, t in (("q", q), ("k", k), ("v", v), ("dy", dy)):
         _tok(n, t, B, T, H, D, dt)
     _tok3("log_a", log_a, B, T, H, dt)
     _st("h0", h0, B, H, D)
     _st("dht", dht, B, H, D)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    dlog_a = torch.empty_like(log_a) if dlog_a is None else dlog_a
+    dq = torch.empty_like(q, dtype=odt) if dq is None else dq
+    dk = torch.empty_like(k, dtype=odt) if dk is None else dk
+    dv = torch.empty_like(v, dtype=odt) if dv is None else dv
+    dlog_a = torch.empty_like(log_a, dtype=odt) if dlog_a is None else dlog_a
     for n, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-        _tok(n, t, B, T, H, D, dt)
-    _tok3("dlog_a", dlog_a, B, T, H, dt)
+        _tok(n, t, B, T, H, D, odt)
+    _tok3("dlog_a", dlog_a, B, T, H, odt)
     if want_dh0 and dh0 is None:
         dh0 = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
     _st("dh0", dh0, B, H, D)
@@ -618,17 +649,18 @@ def bwd_scalar(q, k, v, log_a, dy, h0=None, dht=None, states=None, *, chunk=64, 
     if ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = ws.numel() * ws.element_size()
-    st = _lib().hgrn2_bwd_scalar(B, T, H, D, D, chunk, _DT[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(h0),
+    st = _lib().hgrn2_bwd_scalar(B, T, H, D, D, chunk, code, _ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(h0),
                                  _ptr(states), _ptr(dy), _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dlog_a),
                                  _ptr(dh0), _ptr(ws), ws_bytes, _stream())
     _check(st, "hgrn2_bwd_scalar")
     return dq, dk, dv, dlog_a, dh0
 
 
-def decode_step_scalar(q, k, v, log_a, state, *, y=None):
+def decode_step_scalar(q, k, v, log_a, state, *, y=None, out_dtype=None):
     """One recurrent step with one decay per head, log_a [B, H]; `state` is updated in place.  Returns y."""
     B, H, D = q.shape
     dt = q.dtype
+    odt, code = _odt(dt, out_dtype)
     for n, t in (("q", q), ("k", k), ("v", v)):
         if t.shape != (B, H, D) or t.dtype != dt or not t.is_cuda or not t.is_contiguous():
             raise ValueError("%s: expected a contiguous %s CUDA tensor of shape %s" % (n, dt, (B, H, D)))
@@ -636,8 +668,8 @@ def decode_step_scalar(q, k, v, log_a, state, *, y=None):
         raise ValueError("log_a: expected a contiguous %s CUDA tensor of shape %s" % (dt, (B, H)))
     _st("state", state, B, H, D)
     if y is None:
-        y = torch.empty_like(q)
-    st = _lib().hgrn2_decode_step_scalar(B, H, D, D, _DT[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(state),
+        y = torch.empty_like(q, dtype=odt)
+    st = _lib().hgrn2_decode_step_scalar(B, H, D, D, code, _ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(state),
                                          _ptr(y), _stream())
     _check(st, "hgrn2_decode_step_scalar")
     return y
@@ -660,18 +692,19 @@ def hgrn1_states_shape(B, T, C):
 
 
 def hgrn1_fwd(q, k, v, log_f, h0=None, *, tied=False, want_ht=True, want_states=False, y=None, ht=None,
-              states=None, ws=None):
+              states=None, ws=None, out_dtype=None):
     """HGRN1 elementwise recurrence over [B, T, C] tensors (k = 1 - exp(log_f)
     when tied; k is then ignored).  Returns (y, hT or None, states or None)."""
     B, T, C = q.shape
     dt = q.dtype
+    odt, code = _odt(dt, out_dtype)
     if dt not in _DT:
         raise ValueError("dtype must be float32 or bfloat16")
     for n, t in (("q", q), ("v", v), ("log_f", log_f)) + ((("k", k),) if not tied else ()):
         _tok3(n, t, B, T, C, dt)
     _vec("h0", h0, B, C)
-    y = torch.empty_like(q) if y is None else y
-    _tok3("y", y, B, T, C, dt)
+    y = torch.empty_like(q, dtype=odt) if y is None else y
+    _tok3("y", y, B, T, C, odt)
     if want_ht and ht is None:
         ht = torch.empty((B, C), dtype=torch.float32, device=q.device)
     _vec("hT", ht, B, C)
@@ -680,29 +713,30 @@ def hgrn1_fwd(q, k, v, log_f, h0=None, *, tied=False, want_ht=True, want_states=
     need = int(_lib().hgrn1_fwd_workspace_bytes(B, T, C, int(states is not None)))
     if ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
-    st = _lib().hgrn1_fwd(B, T, C, _DT[dt], int(tied), _ptr(q), None if tied else _ptr(k), _ptr(v), _ptr(log_f),
+    st = _lib().hgrn1_fwd(B, T, C, code, int(tied), _ptr(q), None if tied else _ptr(k), _ptr(v), _ptr(log_f),
                           _ptr(h0), _ptr(y), _ptr(ht), _ptr(states), _ptr(ws), ws.numel(), _stream())
     _check(st, "hgrn1_fwd")
     return y, ht, states
 
 
 def hgrn1_bwd(q, k, v, log_f, dy, h0=None, dht=None, states=None, *, tied=False, want_dh0=True,
-              dq=None, dk=None, dv=None, dlog_f=None, dh0=None, ws=None):
+              dq=None, dk=None, dv=None, dlog_f=None, dh0=None, ws=None, out_dtype=None):
     """Backward of hgrn1_fwd.  Returns (dq, dk or None (tied), dv, dlog_f, dh0 or None);
     tied: dlog_f is the total derivative."""
     B, T, C = q.shape
     dt = q.dtype
+    odt, code = _odt(dt, out_dtype)
     for n, t in (("q", q), ("v", v), ("log_f", log_f), ("dy", dy)) + ((("k", k),) if not tied else ()):
         _tok3(n, t, B, T, C, dt)
     _vec("h0", h0, B, C)
     _vec("dht", dht, B, C)
-    dq = torch.empty_like(q) if dq is None else dq
-    dv = torch.empty_like(q) if dv is None else dv
-    dlog_f = torch.empty_like(q) if dlog_f is None else dlog_f
+    dq = torch.empty_like(q, dtype=odt) if dq is None else dq
+    dv = torch.empty_like(q, dtype=odt) if dv is None else dv
+    dlog_f = torch.empty_like(q, dtype=odt) if dlog_f is None else dlog_f
     if not tied and dk is None:
-        dk = torch.empty_like(q)
+        dk = torch.empty_like(q, dtype=odt)
     for n, t in (("dq", dq), ("dv", dv), ("dlog_f", dlog_f)) + ((("dk", dk),) if not tied else ()):
-        _tok3(n, t, B, T, C, dt)
+        _tok3(n, t, B, T, C, odt)
     if want_dh0 and dh0 is None:
         dh0 = torch.empty((B, C), dtype=torch.float32, device=q.device)
     _vec("dh0", dh0, B, C)
@@ -712,7 +746,7 @@ def hgrn1_bwd(q, k, v, log_f, dy, h0=None, dht=None, states=None, *, tied=False,
     need = int(_lib().hgrn1_bwd_workspace_bytes(B, T, C, int(states is not None)))
     if ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
-    st = _lib().hgrn1_bwd(B, T, C, _DT[dt], int(tied), _ptr(q), None if tied else _ptr(k), _ptr(v), _ptr(log_f),
+    st = _lib().hgrn1_bwd(B, T, C, code, int(tied), _ptr(q), None if tied else _ptr(k), _ptr(v), _ptr(log_f),
                           _ptr(h0), _ptr(states), _ptr(dy), _ptr(dht), _ptr(dq), None if tied else _ptr(dk),
                           _ptr(dv), _ptr(dlog_f), _ptr(dh0), _ptr(ws), ws.numel(), _stream())
     _check(st, "hgrn1_bwd")
@@ -720,14 +754,18 @@ def hgrn1_bwd(q, k, v, log_f, dy, h0=None, dht=None, states=None, *, tied=False,
 
 
 class HGRN2Chunk(torch.autograd.Function):
-    """Autograd wrapper: y, ht = HGRN2Chunk.apply(q, k, v, log_f, h0, chunk).
+    """Autograd wrapper: y, ht = HGRN2Chunk.apply(q, k, v, log_f, h0, chunk, out_dtype).
 
     k and log_f are independent inputs (a caller tying k = 1 - exp(log_f) in
-    torch gets the tied gradient from autograd through that expression)."""
+    torch gets the tied gradient from autograd through that expression).
+    out_dtype=torch.float32 with bfloat16 inputs returns y in float32; the
+    incoming dy is then taken in the input dtype (the kernels use it as a
+    bfloat16 matrix-core operand either way) and the gradients keep the
+    inputs' dtype, as autograd requires."""
 
     @staticmethod
-    def forward(ctx, q, k, v, log_f, h0, chunk):
-        y, ht, states = fwd(q, k, v, log_f, h0, chunk=chunk, want_ht=True, want_states=True)
+    def forward(ctx, q, k, v, log_f, h0, chunk, out_dtype=None):
+        y, ht, states = fwd(q, k, v, log_f, h0, chunk=chunk, want_ht=True, want_states=True, out_dtype=out_dtype)
         ctx.save_for_backward(q, k, v, log_f, h0, states)
         ctx.chunk = chunk
         return y, ht
@@ -735,13 +773,13 @@ class HGRN2Chunk(torch.autograd.Function):
     @staticmethod
     def backward(ctx, dy, dht):
         q, k, v, log_f, h0, states = ctx.saved_tensors
-        dy = dy.contiguous() if dy is not None else torch.zeros_like(q)
+        dy = dy.to(q.dtype).contiguous() if dy is not None else torch.zeros_like(q)
         dht = dht.contiguous() if dht is not None else None
         dq, dk, dv, dl, dh0 = bwd(q, k, v, log_f, dy, h0, dht, states, chunk=ctx.chunk,
                                   want_dh0=h0 is not None)
-        return dq, dk, dv, dl, dh0, None
+        return dq, dk, dv, dl, dh0, None, None
 
 
-def hgrn2_chunk(q, k, v, log_f, h0=None, chunk=64):
+def hgrn2_chunk(q, k, v, log_f, h0=None, chunk=64, out_dtype=None):
     """Differentiable chunked HGRN2 recurrence: returns (y, ht)."""
-    return HGRN2Chunk.apply(q, k, v, log_f, h0, chunk)
+    return HGRN2Chunk.apply(q, k, v, log_f, h0, chunk, out_dtype)

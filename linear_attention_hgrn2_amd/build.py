@@ -21,8 +21,8 @@ LIB = os.path.join(HERE, "libhgrn2.so")
 BUILD = os.path.join(HERE, "_build")
 ARCH = os.environ.get("HGRN2_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["scan_inst.hip", "cfwd_inst.hip", "cbwd_inst.hip", "decode_inst.hip", "hgrn1_inst.hip", "sfwd_inst.hip",
-           "api.cpp"]
+SOURCES = ["scan_inst.hip", "cfwd_inst.hip", "cbwd_inst.hip", "cbwd_f32out_inst.hip", "decode_inst.hip",
+           "hgrn1_inst.hip", "sfwd_inst.hip", "api.cpp"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,

@@ -23,8 +23,12 @@ hgrn2_status fail(hgrn2_status s, const std::string &msg) {
 
 bool valid_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool valid_chunk(int c) { return c == 16 || c == 32 || c == 64 || c == 128; }
-bool valid_dtype(int t) { return t == HGRN2_F32 || t == HGRN2_BF16; }
-size_t dsize(int t) { return t == HGRN2_BF16 ? 2 : 4; }
+// dtype arguments: the input dtype, optionally with HGRN2_OUT_F32 (float32 token outputs)
+int in_dtype(int t) { return t & ~HGRN2_OUT_F32; }
+bool out_f32(int t) { return (t & HGRN2_OUT_F32) != 0; }
+bool valid_dtype(int t) { return in_dtype(t) == HGRN2_F32 || in_dtype(t) == HGRN2_BF16; }
+size_t dsize(int t) { return in_dtype(t) == HGRN2_BF16 ? 2 : 4; }  // input element
+size_t osize(int t) { return out_f32(t) ? 4 : dsize(t); }          // output element
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 // A launch's work-items (workgroups times their size) are counted in 32 bits
@@ -67,12 +71,14 @@ hgrn2_status check_common(int B, int T, int H, int DK, int DV, int chunk, int dt
   if (DK <= 0 || DV <= 0 || chunk <= 0) return fail(HGRN2_ERR_INVALID_ARG, "DK, DV and chunk must be >= 1");
   if ((long long)B * H > (1LL << 30) || (long long)B * T * H > (1LL << 40))
     return fail(HGRN2_ERR_INVALID_ARG, "problem too large");
-  if (!valid_dtype(dtype)) return fail(HGRN2_ERR_INVALID_ARG, "dtype must be HGRN2_F32 or HGRN2_BF16");
+  if (!valid_dtype(dtype))
+    return fail(HGRN2_ERR_INVALID_ARG, "dtype must be HGRN2_F32 or HGRN2_BF16 (optionally | HGRN2_OUT_F32)");
   {
     // one workgroup per chunk; 32-bit byte offsets within a chunk's token rows
-    // and within one sequence's chunk-boundary states
-    const long long N = (T + (long long)chunk - 1) / chunk, E = dtype == HGRN2_F32 ? 4 : 2;
-    if ((long long)B * H * N >= (1LL << 31) || (long long)chunk * H * DK * E >= (1LL << 32) ||
+    // (inputs and outputs) and within one sequence's chunk-boundary states
+    const long long N = (T + (long long)chunk - 1) / chunk, E = (long long)dsize(dtype),
+                    EO = (long long)osize(dtype);
+    if ((long long)B * H * N >= (1LL << 31) || (long long)chunk * H * DK * EO >= (1LL << 32) ||
         (N + 1) * DK * DV * E >= (1LL << 32))
       return fail(HGRN2_ERR_INVALID_ARG, "problem too large");
   }
@@ -83,7 +89,7 @@ hgrn2_status check_common(int B, int T, int H, int DK, int DV, int chunk, int dt
     // work-items of the state scans (workgroups of eight (b, h) at a time) and
     // of the chunk kernels (one workgroup per chunk)
     const long long BH = (long long)B * H, N = (T + (long long)chunk - 1) / chunk;
-    const long long scan = (BH + 7) / 8 * 8 * hgrn2::scan_items_per_bh(dtype, DK, chunk);
+    const long long scan = (BH + 7) / 8 * 8 * hgrn2::scan_items_per_bh(in_dtype(dtype), DK, chunk);
     const long long chunks = BH * N * hgrn2::chunk_items_per_chunk(chunk);
     if (scan > kMaxItems || chunks > kMaxItems) return fail(HGRN2_ERR_INVALID_ARG, "problem too large");
   }
@@ -195,10 +201,11 @@ hgrn2_status launch_scan(int dtype, int D, int chunk, bool reverse, int gm, int 
   return hip_status(hgrn2::dispatch_scan(dtype, D, chunk, reverse, gm, &sa, (hipStream_t)stream), what);
 }
 
-hgrn2_status launch_chunk_fwd(int dtype, int D, int chunk, int gm, int B, int T, int H, const void *q, const void *k,
-                              const void *v, const void *log_f, const float *lb, const void *states, void *y,
-                              void *stream, const char *what) {
+hgrn2_status launch_chunk_fwd(int dtype, bool of32, int D, int chunk, int gm, int B, int T, int H, const void *q,
+                              const void *k, const void *v, const void *log_f, const float *lb, const void *states,
+                              void *y, void *stream, const char *what) {
   hgrn2::ChunkFwdArgs ca;
+  ca.out_f32 = of32;
   ca.B = B;
   ca.T = T;
   ca.H = H;
@@ -213,11 +220,12 @@ hgrn2_status launch_chunk_fwd(int dtype, int D, int chunk, int gm, int B, int T,
   return hip_status(hgrn2::dispatch_chunk_fwd(dtype, D, chunk, gm, &ca, (hipStream_t)stream), what);
 }
 
-hgrn2_status launch_chunk_bwd(int dtype, int D, int chunk, int gm, int B, int T, int H, const void *q, const void *k,
-                              const void *v, const void *log_f, const float *lb, const void *dy, const void *states,
-                              const void *lam, void *dq, void *dk, void *dv, void *dlog_f, float *dlb_part,
-                              void *stream, const char *what) {
+hgrn2_status launch_chunk_bwd(int dtype, bool of32, int D, int chunk, int gm, int B, int T, int H, const void *q,
+                              const void *k, const void *v, const void *log_f, const float *lb, const void *dy,
+                              const void *states, const void *lam, void *dq, void *dk, void *dv, void *dlog_f,
+                              float *dlb_part, void *stream, const char *what) {
   hgrn2::ChunkBwdArgs a;
+  a.out_f32 = of32;
   a.B = B;
   a.T = T;
   a.H = H;
@@ -295,6 +303,8 @@ const char *hgrn2_last_error(void) { return g_last_error.c_str(); }
 
 int hgrn2_supported(int D, int chunk, int dtype) {
   if (!valid_d(D) || !valid_chunk(chunk) || !valid_dtype(dtype)) return 0;
+  // every bfloat16 kernel also exists with float32 outputs
+  dtype = in_dtype(dtype);
   return fwd_exists(dtype, D, chunk) && bwd_exists(dtype, D, chunk) ? 1 : 0;
 }
 
@@ -313,7 +323,7 @@ size_t hgrn2_fwd_workspace_bytes(int B, int T, int H, int DK, int DV, int chunk,
                                  int have_states) {
   if (have_states) return 0;
   if (B <= 0 || T <= 0 || H <= 0 || DK <= 0 || DV <= 0 || chunk <= 0 || !valid_dtype(dtype)) return 0;
-  if (DK == DV && seg_exists(dtype, DK, chunk, kUntied)) return seg_ws_bytes(B, T, H, DK, chunk, false);
+  if (DK == DV && seg_exists(in_dtype(dtype), DK, chunk, kUntied)) return seg_ws_bytes(B, T, H, DK, chunk, false);
   return hgrn2_states_bytes(B, T, H, DK, DV, chunk, dtype);
 }
 
@@ -354,6 +364,9 @@ static hgrn2_status fwd_impl(int gm, const char *fn, int B, int T, int H, int DK
                              void *stream) {
   hgrn2_status st = check_common(B, T, H, DK, DV, chunk, dtype);
   if (st != HGRN2_OK) return st;
+  const bool of32 = out_f32(dtype);
+  const size_t toko = (size_t)B * T * H * DK * osize(dtype);  // bytes of y
+  dtype = in_dtype(dtype);
   st = check_ptrs({{"q", q}, {"v", v}, {gate_name(gm), log_f}},
                   {{"h0", h0}, {"y", y}, {"ht", ht}, {"states_out", states_out}, {"ws", ws}});
   if (st == HGRN2_OK) st = need_k(gm, k, "k");
@@ -376,10 +389,10 @@ static hgrn2_status fwd_impl(int gm, const char *fn, int B, int T, int H, int DK
                          {gate_name(gm), log_f, gate_bytes(gm, tok, DK)},
                          {"h0", (ht == h0) ? nullptr : h0, sb},
                          {"lower_bound", gm == kGate ? lb : nullptr, lbb}};
-    const Range outs[] = {{"y", y, tok}, {"ht", ht, sb}, {"ws", sp.NSEG > 0 ? ws : nullptr, need}};
+    const Range outs[] = {{"y", y, toko}, {"ht", ht, sb}, {"ws", sp.NSEG > 0 ? ws : nullptr, need}};
     std::string msg;
     if (!check_aliasing(ins, 6, outs, 3, msg)) return fail(HGRN2_ERR_INVALID_ARG, msg);
-    if (ht == h0 && ht && (overlap(Range{"y", y, tok}, Range{"h0", h0, sb}) ||
+    if (ht == h0 && ht && (overlap(Range{"y", y, toko}, Range{"h0", h0, sb}) ||
                            (sp.NSEG > 0 && overlap(Range{"ws", ws, need}, Range{"h0", h0, sb}))))
       return fail(HGRN2_ERR_INVALID_ARG, "an output overlaps h0");
     if (!reads_k(gm)) k = nullptr;
@@ -428,6 +441,7 @@ static hgrn2_status fwd_impl(int gm, const char *fn, int B, int T, int H, int DK
     fa.sin = sp.P == 1 ? nullptr : sin;
     fa.y = y;
     fa.ht = ht;
+    fa.out_f32 = of32;
     return hip_status(hgrn2::dispatch_seg_fwd(dtype, DK, chunk, gm, &fa, (hipStream_t)stream), fn);
   }
   const size_t stb = hgrn2_states_bytes(B, T, H, DK, DV, chunk, dtype);
@@ -445,10 +459,10 @@ static hgrn2_status fwd_impl(int gm, const char *fn, int B, int T, int H, int DK
                        {gate_name(gm), log_f, gate_bytes(gm, tok, DK)},
                        {"h0", (ht == h0) ? nullptr : h0, sb},
                        {"lower_bound", gm == kGate ? lb : nullptr, lbb}};
-  const Range outs[] = {{"y", y, tok}, {"ht", ht, sb}, {states_out ? "states_out" : "ws", states, stb}};
+  const Range outs[] = {{"y", y, toko}, {"ht", ht, sb}, {states_out ? "states_out" : "ws", states, stb}};
   std::string msg;
   if (!check_aliasing(ins, 6, outs, 3, msg)) return fail(HGRN2_ERR_INVALID_ARG, msg);
-  if (ht == h0 && ht && (overlap(Range{"y", y, tok}, Range{"h0", h0, sb}) ||
+  if (ht == h0 && ht && (overlap(Range{"y", y, toko}, Range{"h0", h0, sb}) ||
                          overlap(Range{"states", states, stb}, Range{"h0", h0, sb})))
     return fail(HGRN2_ERR_INVALID_ARG, "an output overlaps h0");
 
@@ -456,7 +470,7 @@ static hgrn2_status fwd_impl(int gm, const char *fn, int B, int T, int H, int DK
   if (gm != kGate) lb = nullptr;
   st = launch_scan(dtype, DK, chunk, false, gm, B, T, H, k, v, log_f, lb, h0, states, ht, stream, fn);
   if (st != HGRN2_OK || !y) return st;
-  return launch_chunk_fwd(dtype, DK, chunk, gm, B, T, H, q, k, v, log_f, lb, states, y, stream, fn);
+  return launch_chunk_fwd(dtype, of32, DK, chunk, gm, B, T, H, q, k, v, log_f, lb, states, y, stream, fn);
 }
 
 static hgrn2_status bwd_impl(int gm, const char *fn, int B, int T, int H, int DK, int DV, int chunk, int dtype,
@@ -466,6 +480,9 @@ static hgrn2_status bwd_impl(int gm, const char *fn, int B, int T, int H, int DK
                              void *stream) {
   hgrn2_status st = check_common(B, T, H, DK, DV, chunk, dtype);
   if (st != HGRN2_OK) return st;
+  const bool of32 = out_f32(dtype);
+  const size_t toko = (size_t)B * T * H * DK * osize(dtype);  // bytes of each token gradient
+  dtype = in_dtype(dtype);
   st = check_ptrs({{"q", q}, {"v", v}, {gate_name(gm), log_f}, {"dy", dy}, {"dq", dq}, {"dv", dv},
                    {dgate_name(gm), dlog_f}},
                   {{"h0", h0}, {"states_in", states_in}, {"dht", dht}, {"dh0", dh0}, {"ws", ws}});
@@ -489,12 +506,12 @@ static hgrn2_status bwd_impl(int gm, const char *fn, int B, int T, int H, int DK
     return fail(HGRN2_ERR_WORKSPACE, "workspace smaller than hgrn2_bwd_workspace_bytes()");
   if (!reads_k(gm)) k = dk = nullptr;
   if (gm != kGate) lb = dlb = nullptr;
-  const size_t lbb = (size_t)H * DK * sizeof(float), gb = gate_bytes(gm, tok, DK);
+  const size_t lbb = (size_t)H * DK * sizeof(float), gb = gate_bytes(gm, tok, DK), gbo = gate_bytes(gm, toko, DK);
   const void *states = states_in;
   const Range ins[] = {{"q", q, tok},           {"k", k, tok},          {"v", v, tok},
                        {gate_name(gm), log_f, gb}, {"h0", h0, sb},     {"dy", dy, tok},
                        {"dht", dht, sb},        {"states_in", states_in, stb}, {"lower_bound", lb, lbb}};
-  const Range outs[] = {{"dq", dq, tok},  {"dk", dk, tok},          {"dv", dv, tok}, {dgate_name(gm), dlog_f, gb},
+  const Range outs[] = {{"dq", dq, toko}, {"dk", dk, toko},         {"dv", dv, toko}, {dgate_name(gm), dlog_f, gbo},
                         {"dh0", dh0, sb}, {"dlower_bound", dlb, lbb}, {"ws", ws, need}};
   std::string msg;
   if (!check_aliasing(ins, 9, outs, 7, msg)) return fail(HGRN2_ERR_INVALID_ARG, msg);
@@ -512,8 +529,8 @@ static hgrn2_status bwd_impl(int gm, const char *fn, int B, int T, int H, int DK
   // the state adjoint at every chunk end (reverse scan), then all chunks' gradients
   st = launch_scan(dtype, DK, chunk, true, adjoint_gm(gm), B, T, H, q, dy, log_f, lb, dht, ws, dh0, stream, fn);
   if (st != HGRN2_OK) return st;
-  st = launch_chunk_bwd(dtype, DK, chunk, gm, B, T, H, q, k, v, log_f, lb, dy, states, ws, dq, dk, dv, dlog_f, part,
-                        stream, fn);
+  st = launch_chunk_bwd(dtype, of32, DK, chunk, gm, B, T, H, q, k, v, log_f, lb, dy, states, ws, dq, dk, dv, dlog_f,
+                        part, stream, fn);
   if (st != HGRN2_OK || gm != kGate) return st;
   return hip_status(hgrn2::dispatch_dlb_reduce(B, H, hgrn2_num_chunks(T, chunk), DK, part, dlb, (hipStream_t)stream),
                     fn);
@@ -524,6 +541,9 @@ static hgrn2_status fwd_chunk_impl(int gm, const char *fn, int B, int T, int H, 
                                    const void *states, void *y, void *stream) {
   hgrn2_status st = check_common(B, T, H, DK, DV, chunk, dtype);
   if (st != HGRN2_OK) return st;
+  const bool of32 = out_f32(dtype);
+  const size_t toko = (size_t)B * T * H * DK * osize(dtype);
+  dtype = in_dtype(dtype);
   st = check_ptrs({{"q", q}, {"v", v}, {"log_f", log_f}, {"states", states}, {"y", y}}, {});
   if (st == HGRN2_OK) st = need_k(gm, k, "k");
   if (st != HGRN2_OK) return st;
@@ -533,10 +553,10 @@ static hgrn2_status fwd_chunk_impl(int gm, const char *fn, int B, int T, int H, 
   const size_t tok = (size_t)B * T * H * DK * dsize(dtype);
   const size_t stb = hgrn2_states_bytes(B, T, H, DK, DV, chunk, dtype);
   const Range ins[] = {{"q", q, tok}, {"k", k, tok}, {"v", v, tok}, {"log_f", log_f, tok}, {"states", states, stb}};
-  const Range outs[] = {{"y", y, tok}};
+  const Range outs[] = {{"y", y, toko}};
   std::string msg;
   if (!check_aliasing(ins, 5, outs, 1, msg)) return fail(HGRN2_ERR_INVALID_ARG, msg);
-  return launch_chunk_fwd(dtype, DK, chunk, gm, B, T, H, q, k, v, log_f, nullptr, states, y, stream, fn);
+  return launch_chunk_fwd(dtype, of32, DK, chunk, gm, B, T, H, q, k, v, log_f, nullptr, states, y, stream, fn);
 }
 
 static hgrn2_status bwd_chunk_impl(int gm, const char *fn, int B, int T, int H, int DK, int DV, int chunk,
@@ -545,6 +565,9 @@ static hgrn2_status bwd_chunk_impl(int gm, const char *fn, int B, int T, int H, 
                                    void *dv, void *dlog_f, void *stream) {
   hgrn2_status st = check_common(B, T, H, DK, DV, chunk, dtype);
   if (st != HGRN2_OK) return st;
+  const bool of32 = out_f32(dtype);
+  const size_t toko = (size_t)B * T * H * DK * osize(dtype);
+  dtype = in_dtype(dtype);
   st = check_ptrs({{"q", q}, {"v", v}, {"log_f", log_f}, {"states", states}, {"adjoints", adjoints}, {"dy", dy},
                    {"dq", dq}, {"dv", dv}, {"dlog_f", dlog_f}},
                   {});
@@ -560,11 +583,11 @@ static hgrn2_status bwd_chunk_impl(int gm, const char *fn, int B, int T, int H, 
   const Range ins[] = {{"q", q, tok},           {"k", k, tok},   {"v", v, tok},
                        {"log_f", log_f, tok},   {"dy", dy, tok}, {"states", states, stb},
                        {"adjoints", adjoints, lamb}};
-  const Range outs[] = {{"dq", dq, tok}, {"dk", dk, tok}, {"dv", dv, tok}, {"dlog_f", dlog_f, tok}};
+  const Range outs[] = {{"dq", dq, toko}, {"dk", dk, toko}, {"dv", dv, toko}, {"dlog_f", dlog_f, toko}};
   std::string msg;
   if (!check_aliasing(ins, 7, outs, 4, msg)) return fail(HGRN2_ERR_INVALID_ARG, msg);
-  return launch_chunk_bwd(dtype, DK, chunk, gm, B, T, H, q, k, v, log_f, nullptr, dy, states, adjoints, dq, dk, dv,
-                          dlog_f, nullptr, stream, fn);
+  return launch_chunk_bwd(dtype, of32, DK, chunk, gm, B, T, H, q, k, v, log_f, nullptr, dy, states, adjoints, dq, dk,
+                          dv, dlog_f, nullptr, stream, fn);
 }
 
 static hgrn2_status decode_impl(int gm, const char *fn, int B, int H, int DK, int DV, int dtype, const void *q,
@@ -572,8 +595,12 @@ static hgrn2_status decode_impl(int gm, const char *fn, int B, int H, int DK, in
                                 void *y, void *stream) {
   if (B <= 0 || H <= 0) return fail(HGRN2_ERR_INVALID_ARG, "B and H must be >= 1");
   if ((long long)B * H > (1LL << 30)) return fail(HGRN2_ERR_INVALID_ARG, "problem too large");
-  if (!valid_dtype(dtype)) return fail(HGRN2_ERR_INVALID_ARG, "dtype must be HGRN2_F32 or HGRN2_BF16");
+  if (!valid_dtype(dtype))
+    return fail(HGRN2_ERR_INVALID_ARG, "dtype must be HGRN2_F32 or HGRN2_BF16 (optionally | HGRN2_OUT_F32)");
   if (DK != DV || !valid_d(DK)) return fail(HGRN2_ERR_UNSUPPORTED, "need DK == DV in {16, 32, 64, 128}");
+  const bool of32 = out_f32(dtype);
+  const size_t veco = (size_t)B * H * DK * osize(dtype);  // bytes of y
+  dtype = in_dtype(dtype);
   // one workgroup per (b, h)
   if ((long long)B * H * hgrn2::decode_items_per_bh(DK) > kMaxItems) return fail(HGRN2_ERR_INVALID_ARG, "problem too large");
   hgrn2_status st = check_ptrs({{"q", q}, {"v", v}, {gate_name(gm), log_f}, {"state", state}, {"y", y}}, {});
@@ -587,7 +614,7 @@ static hgrn2_status decode_impl(int gm, const char *fn, int B, int H, int DK, in
   const size_t lbb = (size_t)H * DK * sizeof(float);
   const Range ins[] = {{"q", q, vec}, {"k", k, vec}, {"v", v, vec}, {gate_name(gm), log_f, gate_bytes(gm, vec, DK)},
                        {"lower_bound", lb, lbb}};
-  const Range outs[] = {{"y", y, vec}, {"state", state, sb}};
+  const Range outs[] = {{"y", y, veco}, {"state", state, sb}};
   std::string msg;
   if (!check_aliasing(ins, 5, outs, 2, msg)) return fail(HGRN2_ERR_INVALID_ARG, msg);
   hgrn2::DecodeArgs a;
@@ -600,6 +627,7 @@ static hgrn2_status decode_impl(int gm, const char *fn, int B, int H, int DK, in
   a.lb = lb;
   a.state = state;
   a.y = y;
+  a.out_f32 = of32;
   return hip_status(hgrn2::dispatch_decode(dtype, DK, gm, a, (hipStream_t)stream), fn);
 }
 
@@ -661,6 +689,7 @@ hgrn2_status hgrn2_bwd_adjoint(int B, int T, int H, int DK, int DV, int chunk, i
                                void *stream) {
   hgrn2_status st = check_common(B, T, H, DK, DV, chunk, dtype);
   if (st != HGRN2_OK) return st;
+  dtype = in_dtype(dtype);  // no token output
   st = check_ptrs({{"q", q}, {"log_f", log_f}, {"dy", dy}, {"adjoints", adjoints}}, {{"dht", dht}, {"dh0", dh0}});
   if (st != HGRN2_OK) return st;
   if (hgrn2::dispatch_scan(dtype, DK, chunk, true, kUntied, nullptr, nullptr) != hipSuccess)
@@ -782,9 +811,10 @@ static hgrn2_status h1_check(int B, int T, int C, int dtype, int tied) {
   if (B <= 0 || T <= 0 || C <= 0) return fail(HGRN2_ERR_INVALID_ARG, "B, T and C must be >= 1");
   if ((long long)B * T * C > (1LL << 40) || (long long)B * C > (1LL << 30))
     return fail(HGRN2_ERR_INVALID_ARG, "problem too large");
-  if (!valid_dtype(dtype)) return fail(HGRN2_ERR_INVALID_ARG, "dtype must be HGRN2_F32 or HGRN2_BF16");
-  // a segment's 32 token rows are addressed with 32-bit byte offsets
-  if (32LL * C * (dtype == HGRN2_F32 ? 4 : 2) >= (1LL << 32)) return fail(HGRN2_ERR_INVALID_ARG, "problem too large");
+  if (!valid_dtype(dtype))
+    return fail(HGRN2_ERR_INVALID_ARG, "dtype must be HGRN2_F32 or HGRN2_BF16 (optionally | HGRN2_OUT_F32)");
+  // a segment's 32 token rows (inputs and outputs) are addressed with 32-bit byte offsets
+  if (32LL * C * (long long)osize(dtype) >= (1LL << 32)) return fail(HGRN2_ERR_INVALID_ARG, "problem too large");
   if (tied != 0 && tied != 1) return fail(HGRN2_ERR_INVALID_ARG, "tied must be 0 or 1");
   if (C % 2 != 0) return fail(HGRN2_ERR_UNSUPPORTED, "C must be even");
   {
@@ -856,6 +886,9 @@ hgrn2_status hgrn1_fwd(int B, int T, int C, int dtype, int tied, const void *q, 
   const char *fn = "hgrn1_fwd";
   hgrn2_status st = h1_check(B, T, C, dtype, tied);
   if (st != HGRN2_OK) return st;
+  const bool of32 = out_f32(dtype);
+  const size_t toko = (size_t)B * T * C * osize(dtype);  // bytes of y
+  dtype = in_dtype(dtype);
   st = check_ptrs({{"q", q}, {"v", v}, {"log_f", log_f}, {"y", y}},
                   {{"h0", h0}, {"hT", hT}, {"states_out", states_out}, {"ws", ws}});
   if (st == HGRN2_OK) st = need_k(tied ? kTied : kUntied, k, "k");
@@ -866,7 +899,7 @@ hgrn2_status hgrn1_fwd(int B, int T, int C, int dtype, int tied, const void *q, 
   if (!ws || ws_bytes < need) return fail(HGRN2_ERR_WORKSPACE, "workspace smaller than hgrn1_fwd_workspace_bytes()");
   if (tied) k = nullptr;
   const Range ins[] = {{"q", q, tok}, {"k", k, tok}, {"v", v, tok}, {"log_f", log_f, tok}, {"h0", h0, hb}};
-  const Range outs[] = {{"y", y, tok}, {"hT", hT, hb}, {"states_out", states_out, sb}, {"ws", ws, need}};
+  const Range outs[] = {{"y", y, toko}, {"hT", hT, hb}, {"states_out", states_out, sb}, {"ws", ws, need}};
   std::string msg;
   if (!check_aliasing(ins, 5, outs, 4, msg)) return fail(HGRN2_ERR_INVALID_ARG, msg);
   hgrn2::H1Args a = h1_args(B, T, C);
@@ -879,6 +912,7 @@ hgrn2_status hgrn1_fwd(int B, int T, int C, int dtype, int tied, const void *q, 
   a.sum = h1_sum_at(ws, B, T, C);
   a.states = states_out;
   a.y = y;
+  a.out_f32 = of32;
   const int gm = tied ? kTied : kUntied;
   if ((st = h1_launch(hgrn2::kH1SummaryFwd, dtype, gm, a, stream, fn)) != HGRN2_OK) return st;
   if ((st = h1_launch(hgrn2::kH1CarryFwd, dtype, gm, a, stream, fn)) != HGRN2_OK) return st;
@@ -892,6 +926,9 @@ hgrn2_status hgrn1_bwd(int B, int T, int C, int dtype, int tied, const void *q, 
   const char *fn = "hgrn1_bwd";
   hgrn2_status st = h1_check(B, T, C, dtype, tied);
   if (st != HGRN2_OK) return st;
+  const bool of32 = out_f32(dtype);
+  const size_t toko = (size_t)B * T * C * osize(dtype);  // bytes of each gradient
+  dtype = in_dtype(dtype);
   st = check_ptrs({{"q", q}, {"v", v}, {"log_f", log_f}, {"dy", dy}, {"dq", dq}, {"dv", dv}, {"dlog_f", dlog_f}},
                   {{"h0", h0}, {"states_in", states_in}, {"dht", dht}, {"dh0", dh0}, {"ws", ws}});
   const int gm = tied ? kTied : kUntied;
@@ -905,7 +942,7 @@ hgrn2_status hgrn1_bwd(int B, int T, int C, int dtype, int tied, const void *q, 
   if (tied) k = dk = nullptr;
   const Range ins[] = {{"q", q, tok},   {"k", k, tok},   {"v", v, tok},   {"log_f", log_f, tok},
                        {"h0", h0, hb},  {"dy", dy, tok}, {"dht", dht, hb}, {"states_in", states_in, sb}};
-  const Range outs[] = {{"dq", dq, tok}, {"dk", dk, tok}, {"dv", dv, tok}, {"dlog_f", dlog_f, tok},
+  const Range outs[] = {{"dq", dq, toko}, {"dk", dk, toko}, {"dv", dv, toko}, {"dlog_f", dlog_f, toko},
                         {"dh0", dh0, hb}, {"ws", ws, need}};
   std::string msg;
   if (!check_aliasing(ins, 8, outs, 6, msg)) return fail(HGRN2_ERR_INVALID_ARG, msg);
@@ -915,6 +952,7 @@ hgrn2_status hgrn1_bwd(int B, int T, int C, int dtype, int tied, const void *q, 
   a.v = v;
   a.log_f = log_f;
   a.dy = dy;
+  a.out_f32 = of32;
   a.states = const_cast<float *>(states_in);  // read only by the final backward
   if (!states_in) {
     // the forward summaries and group carries; the final backward combines them

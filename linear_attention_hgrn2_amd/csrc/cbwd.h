@@ -38,9 +38,11 @@ struct ChunkBwdArgs {
   const void *q, *k, *v, *log_f, *dy;  // [B,T,H,D]; log_f holds z in gate mode
   const void *states;                  // [B,H,N+1,D,D]; entry n = state before chunk n
   const void *lam;                     // [B,H,N,D,D]; entry n = adjoint at the end of chunk n
-  void *dq, *dk, *dv, *dlog_f;         // [B,T,H,D]; dlog_f receives dz in gate mode
+  void *dq, *dk, *dv, *dlog_f;         // [B,T,H,D]; dlog_f receives dz in gate mode; the input
+                                       // dtype or (out_f32) float32
   const float *lb;                     // gate mode: lower bound of f, [H,D]
   float *dlb;                          // gate mode: per-chunk sums [B,H,N,D]
+  int out_f32 = 0;                     // bfloat16 inputs: write the gradients as float32
 };
 
 template <typename T, int D, int C> struct CbwdCfg {
@@ -96,7 +98,8 @@ template <typename T, int D, int C> struct CbwdCfg {
   };
 };
 
-template <typename T, int D, int C, int GM>
+// TO: the element type of the gradients (T, or float32 for bfloat16 inputs)
+template <typename T, int D, int C, int GM, typename TO = T>
 __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void hgrn2_chunk_bwd_kernel(ChunkBwdArgs a) {
   using Cfg = CbwdCfg<T, D, C>;
   constexpr int NW = Cfg::NW, NT = Cfg::NT, NB = Cfg::NB, CPL = Cfg::CPL, CB = Cfg::CB, KSD = Cfg::KSD,
@@ -125,12 +128,16 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
   const GBuf bq((const char *)a.q + cbase, rows), bk((const char *)a.k + cbase, rows);
   const GBuf bv((const char *)a.v + cbase, rows), bl((const char *)a.log_f + cbase, rows);
   const GBuf bdy((const char *)a.dy + cbase, rows);
-  const GBuf bdq((char *)a.dq + cbase, rows), bdk((char *)a.dk + cbase, rows);
-  const GBuf bdv((char *)a.dv + cbase, rows), bdl((char *)a.dlog_f + cbase, rows);
+  // the gradients' rows, of TO elements
+  const size_t cbaseo = cbase / sizeof(T) * sizeof(TO);
+  const uint32_t HDBO = (uint32_t)H * D * sizeof(TO), rowso = (uint32_t)len * HDBO;
+  const GBuf bdq((char *)a.dq + cbaseo, rowso), bdk((char *)a.dk + cbaseo, rowso);
+  const GBuf bdv((char *)a.dv + cbaseo, rowso), bdl((char *)a.dlog_f + cbaseo, rowso);
   const GBuf bS((const char *)a.states + ((size_t)bh * (N + 1) + n) * D * D * sizeof(T), D * D * sizeof(T));
   const GBuf bL((const char *)a.lam + ((size_t)bh * N + n) * D * D * sizeof(T), D * D * sizeof(T));
-  const uint32_t c0b = (uint32_t)c0 * sizeof(T);
-  auto tok = [&](int t) { return (uint32_t)t * HDB; };  // byte offset of token t of the chunk
+  const uint32_t c0b = (uint32_t)c0 * sizeof(T), c0bo = (uint32_t)c0 * sizeof(TO);
+  auto tok = [&](int t) { return (uint32_t)t * HDB; };    // byte offset of token t of the chunk
+  auto toko = [&](int t) { return (uint32_t)t * HDBO; };  // the same in the gradients' rows
   // the chunk's log decays: per channel, or one per head broadcast (kScalar)
   const LfRows<GM> lr = lf_rows<GM, T>(a.log_f, b, T_, H, h, D, t0, len);
   // this lane's CPL elements of token t of the chunk (0 past the end)
@@ -486,19 +493,32 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
   __syncthreads();  // B4: S and Lam are dead
 
   // =============== phase 2: dv out, then the epilogues of dq, dk and dlog f
-  T *dvs = sm.u.dvs;
+  if constexpr (std::is_same<TO, T>::value) {
+    T *dvs = sm.u.dvs;
 #pragma unroll
-  for (int jb = 0; jb < CB; ++jb)
+    for (int jb = 0; jb < CB; ++jb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dvs[XT::at(16 * w + 4 * g + r, 16 * jb + n16)] = from_f32<T>(DV[jb][r]);
-  wave_lds_sync();
-  constexpr int RV = 16 * D / EPV;
+      for (int r = 0; r < 4; ++r) dvs[XT::at(16 * w + 4 * g + r, 16 * jb + n16)] = from_f32<T>(DV[jb][r]);
+    wave_lds_sync();
+    constexpr int RV = 16 * D / EPV;
 #pragma unroll
-  for (int i = 0; i < (RV + 63) / 64; ++i) {
-    const int idx = lane + 64 * i;
-    const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
-    const int t = 16 * w + row;
-    if (idx < RV) bdv.st16(tok(t) + (uint32_t)col * sizeof(T), *(const uint4 *)&dvs[XT::at(t, col)]);
+    for (int i = 0; i < (RV + 63) / 64; ++i) {
+      const int idx = lane + 64 * i;
+      const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
+      const int t = 16 * w + row;
+      if (idx < RV) bdv.st16(tok(t) + (uint32_t)col * sizeof(T), *(const uint4 *)&dvs[XT::at(t, col)]);
+    }
+  } else {
+    // float32 dv straight from the accumulators: each 16 lanes of a group
+    // write 64 contiguous bytes of one row (rows past the end are dropped)
+#pragma unroll
+    for (int jb = 0; jb < CB; ++jb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        Pack<TO, 1> o;
+        o.v[0] = DV[jb][r];
+        bdv.stpack<TO, 1>(toko(16 * w + 4 * g + r) + (uint32_t)(16 * jb + n16) * sizeof(TO), o);
+      }
   }
   __syncthreads();  // B5: the dv staging is dead
 
@@ -544,7 +564,7 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
       const Pack<T, CPL> pq = ldtok(bq, tt);
       Pack<T, CPL> pk;
       if constexpr (reads_k(GM)) pk = ldtok(bk, tt);
-      Pack<T, CPL> oq, ok;
+      Pack<TO, CPL> oq, ok;
 #pragma unroll
       for (int e = 0; e < CPL; ++e) {
         float lft, kv;
@@ -554,15 +574,15 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
         const float qor = to_f32(from_f32<T>(to_f32(pq.v[e]) * el));
         const float kor = to_f32(from_f32<T>(kv * ek));
         const float d1 = sq[t * LDG + c0 + e], d2 = sk[t * LDG + c0 + e];
-        oq.v[e] = from_f32<T>(el * d1);
-        ok.v[e] = from_f32<T>(ek * d2);
+        oq.v[e] = from_f32<TO>(el * d1);
+        ok.v[e] = from_f32<TO>(ek * d2);
         X[t][e] = qor * d1 - kor * d2;
         // k tied to f: f dk, subtracted from dlog f below (replaces the consumed dk'_t)
         if (ties_k(GM) && has_ch) sk[t * LDG + c0 + e] = __expf(lft) * (ek * d2);
       }
       if (has_ch) {
-        bdq.stpack<T, CPL>(tok(tt) + c0b, oq);
-        if constexpr (reads_k(GM)) bdk.stpack<T, CPL>(tok(tt) + c0b, ok);
+        bdq.stpack<TO, CPL>(toko(tt) + c0bo, oq);
+        if constexpr (reads_k(GM)) bdk.stpack<TO, CPL>(toko(tt) + c0bo, ok);
       }
     }
     if (has_ch) {
@@ -627,15 +647,15 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
         for (int e = 0; e < CPL; ++e) dkd[e] += dA * to_f32(pqu.v[e]) * __expf(ex[e]);
       }
-      Pack<T, CPL> oq, ok;
+      Pack<TO, CPL> oq, ok;
 #pragma unroll
       for (int e = 0; e < CPL; ++e) {
         const float el = __expf(ell[e]), ek = __expf(L[e] - ell[e]);
         const float qv = to_f32(pq.v[e]), kv = k_of<GM>(pk.v[e], lfe<GM>(plt, e), lbv[e]);
         const float qor = to_f32(from_f32<T>(qv * el)), kor = to_f32(from_f32<T>(kv * ek));
         const float d1 = sq[t * LDG + c0 + e], d2 = sk[t * LDG + c0 + e];
-        oq.v[e] = from_f32<T>(el * d1 + dqd[e]);
-        ok.v[e] = from_f32<T>(ek * d2 + dkd[e]);
+        oq.v[e] = from_f32<TO>(el * d1 + dqd[e]);
+        ok.v[e] = from_f32<TO>(ek * d2 + dkd[e]);
         const float x = (qor * d1 + qv * dqd[e]) - (kor * d2 + kv * dkd[e]);
         if (has_ch) sq[t * LDG + c0 + e] = x;  // X_t replaces the consumed dq'_t
         if (ties_k(GM) && has_ch)
@@ -643,8 +663,8 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
         tot[e] += x;
       }
       if (has_ch) {
-        bdq.stpack<T, CPL>(tok(tt) + c0b, oq);
-        if constexpr (reads_k(GM)) bdk.stpack<T, CPL>(tok(tt) + c0b, ok);
+        bdq.stpack<TO, CPL>(toko(tt) + c0bo, oq);
+        if constexpr (reads_k(GM)) bdk.stpack<TO, CPL>(toko(tt) + c0bo, ok);
       }
     }
     if (has_ch)
@@ -671,7 +691,7 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
     }
     auto emit = [&](int t, const float *cr) {
       const int tt = 16 * w + t;
-      Pack<T, CPL> o;
+      Pack<TO, CPL> o;
       Pack<T, CPL> pz;
       if constexpr (GM == kGate) pz = ldtok(bl, tt);
 #pragma unroll
@@ -682,10 +702,10 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
           if (tt < len) dlbs[e] += G * gg.dlb;
           G *= gg.dz;
         }
-        o.v[e] = from_f32<T>(G);
+        o.v[e] = from_f32<TO>(G);
         if constexpr (GM == kScalar) ssum[t] += G;
       }
-      if constexpr (GM != kScalar) bdl.stpack<T, CPL>(tok(tt) + c0b, o);
+      if constexpr (GM != kScalar) bdl.stpack<TO, CPL>(toko(tt) + c0bo, o);
     };
     if (!wide) {
 #pragma unroll
@@ -705,14 +725,14 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
   }
   if constexpr (GM == kScalar) {
     // dlog a of each token: the sum over the head's channels, across the wave
-    const GBuf bda((char *)a.dlog_f + (((size_t)b * T_ + t0) * H + h) * sizeof(T), (uint32_t)(len * H * sizeof(T)));
+    const GBuf bda((char *)a.dlog_f + (((size_t)b * T_ + t0) * H + h) * sizeof(TO), (uint32_t)(len * H * sizeof(TO)));
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       const float tot = wave_sum(ssum[t]);
       if (lane == 0) {
-        Pack<T, 1> o;
-        o.v[0] = from_f32<T>(tot);
-        bda.stpack<T, 1>((uint32_t)(16 * w + t) * H * sizeof(T), o);
+        Pack<TO, 1> o;
+        o.v[0] = from_f32<TO>(tot);
+        bda.stpack<TO, 1>((uint32_t)(16 * w + t) * H * sizeof(TO), o);
       }
     }
   }
@@ -733,10 +753,10 @@ __global__ __launch_bounds__(4 * C) __attribute__((amdgpu_waves_per_eu(2))) void
   }
 }
 
-template <typename T, int D, int C, int GM>
+template <typename T, int D, int C, int GM, typename TO = T>
 hipError_t launch_chunk_bwd(const ChunkBwdArgs &a, hipStream_t stream) {
   using Cfg = CbwdCfg<T, D, C>;
-  hipLaunchKernelGGL((hgrn2_chunk_bwd_kernel<T, D, C, GM>), dim3(a.B * a.H * a.N), dim3(Cfg::NT), 0, stream, a);
+  hipLaunchKernelGGL((hgrn2_chunk_bwd_kernel<T, D, C, GM, TO>), dim3(a.B * a.H * a.N), dim3(Cfg::NT), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -96,7 +96,8 @@ __device__ __forceinline__ PFrag<bf16_t> res_tr8(const bf16_t *m, int r0, int n0
 
 __device__ __forceinline__ int res_pair_i(int p) { return p >= 6 ? 3 : p >= 3 ? 2 : p >= 1 ? 1 : 0; }
 
-template <int GM>
+// TO: the element type of the gradients (bfloat16, or float32)
+template <int GM, typename TO = bf16_t>
 __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a) {
   using Cfg = CbwdResCfg;
   using T = bf16_t;
@@ -130,6 +131,12 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
   };
   auto win = [&](const void *base, const Chunk &k) {
     return GBuf((const char *)base + k.cbase, (uint32_t)k.len * HDB);
+  };
+  // the gradients' rows, of TO elements
+  const uint32_t HDBO = (uint32_t)H * D * sizeof(TO);
+  auto toko = [&](int t) { return (uint32_t)t * HDBO; };
+  auto wino = [&](void *base, const Chunk &k) {
+    return GBuf((char *)base + k.cbase / sizeof(T) * sizeof(TO), (uint32_t)k.len * HDBO);
   };
 
   // ---- register prefetch of a chunk's token rows, in groups: kPfTiles (v and
@@ -527,8 +534,9 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
     __syncthreads();  // B6: S, Lam, the score tiles, v and dy are dead
     if (ci + G < NC) prefetch(ci + G, kPfQL);
 
-    // ---- P4: dv out (staged through the dead v tile), dq' and dk' staging
-    {
+    // ---- P4: dv out (staged through the dead v tile, or float32 straight
+    // from the accumulators), dq' and dk' staging
+    if constexpr (std::is_same<TO, T>::value) {
       const GBuf bdv = win(a.dv, k);
       T *dvs = sm.v;
 #pragma unroll
@@ -541,6 +549,16 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
         const int idx = lane + 64 * i, t = 16 * w + (idx >> 3), col = 64 * hh + 8 * (idx & 7);
         bdv.st16<kStream>(tok(t) + (uint32_t)col * sizeof(T), *(const uint4 *)&dvs[XT::at(t, col)]);
       }
+    } else {
+      const GBuf bdv = wino(a.dv, k);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          Pack<TO, 1> o;
+          o.v[0] = DV[cb][r];
+          bdv.stpack<TO, 1, kStream>(toko(16 * w + 4 * g + r) + (uint32_t)(64 * hh + 16 * cb + n16) * sizeof(TO), o);
+        }
     }
     auto &ep = sm.u.e;
 #pragma unroll
@@ -559,7 +577,7 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
 
     // ---- P5: per token (tokens 16 w + 8 hh + t, channels c0, c0 + 1): dq = e^{ell} dq',
     // dk = e^{L - ell} dk', X = qo dq' - ko dk' with qo, ko as they entered the products
-    const GBuf bdq = win(a.dq, k), bdk = win(a.dk, k);
+    const GBuf bdq = wino(a.dq, k), bdk = wino(a.dk, k);
     float X[8][2];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -568,12 +586,12 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
       const Pack<T, 2> kr = *(const Pack<T, 2> *)&ko[XT::at(tt, c0)];
       const float2 d1 = *(const float2 *)&ep.stg[0][tt][c0], d2 = *(const float2 *)&ep.stg[1][tt][c0];
       const float dd1[2] = {d1.x, d1.y}, dd2[2] = {d2.x, d2.y};
-      Pack<T, 2> oq, ok;
+      Pack<TO, 2> oq, ok;
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const float el = __expf(l[t][e]), ek = __expf(Lw[e] - l[t][e]);
-        oq.v[e] = from_f32<T>(el * dd1[e]);
-        ok.v[e] = from_f32<T>(ek * dd2[e]);
+        oq.v[e] = from_f32<TO>(el * dd1[e]);
+        ok.v[e] = from_f32<TO>(ek * dd2[e]);
         X[t][e] = to_f32(qr.v[e]) * dd1[e] - to_f32(kr.v[e]) * dd2[e];
         // k tied to f: f dk (f from the prefix), subtracted from dlog f in P6;
         // it replaces the consumed dk'_t
@@ -581,8 +599,8 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
           ep.stg[1][tt][c0 + e] = __expf(l[t][e] - (t ? l[t - 1][e] : hoff[e])) * (ek * dd2[e]);
       }
       if (!wide) {
-        bdq.stpack<T, 2, kStream>(tok(tt) + (uint32_t)c0 * sizeof(T), oq);
-        if constexpr (reads_k(GM)) bdk.stpack<T, 2, kStream>(tok(tt) + (uint32_t)c0 * sizeof(T), ok);
+        bdq.stpack<TO, 2, kStream>(toko(tt) + (uint32_t)c0 * sizeof(TO), oq);
+        if constexpr (reads_k(GM)) bdk.stpack<TO, 2, kStream>(toko(tt) + (uint32_t)c0 * sizeof(TO), ok);
       }
     }
     if (wide) {
@@ -633,18 +651,18 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
         }
         const float2 d1 = *(const float2 *)&ep.stg[0][tt][c0], d2 = *(const float2 *)&ep.stg[1][tt][c0];
         const float dd1[2] = {d1.x, d1.y}, dd2[2] = {d2.x, d2.y};
-        Pack<T, 2> oq, ok;
+        Pack<TO, 2> oq, ok;
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const float el = __expf(l[t][e]), ek = __expf(Lw[e] - l[t][e]);
-          oq.v[e] = from_f32<T>(el * dd1[e] + dqd[e]);
-          ok.v[e] = from_f32<T>(ek * dd2[e] + dkd[e]);
+          oq.v[e] = from_f32<TO>(el * dd1[e] + dqd[e]);
+          ok.v[e] = from_f32<TO>(ek * dd2[e] + dkd[e]);
           X[t][e] += to_f32(pqt.v[e]) * dqd[e] - k_of<GM>(pkt.v[e], lfe<GM>(plt, e), lb2[e]) * dkd[e];
           if (ties_k(GM))
             ep.stg[1][tt][c0 + e] = __expf(lf_of<GM>(to_f32(lfe<GM>(plt, e)), lb2[e], tt < k.len)) * (ek * dd2[e] + dkd[e]);
         }
-        bdq.stpack<T, 2, kStream>(tok(tt) + cb2, oq);
-        if constexpr (reads_k(GM)) bdk.stpack<T, 2, kStream>(tok(tt) + cb2, ok);
+        bdq.stpack<TO, 2, kStream>(toko(tt) + (uint32_t)c0 * sizeof(TO), oq);
+        if constexpr (reads_k(GM)) bdk.stpack<TO, 2, kStream>(toko(tt) + (uint32_t)c0 * sizeof(TO), ok);
       }
     }
 #pragma unroll
@@ -660,10 +678,10 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
     // k tied to f subtracts f dk; gate mode turns that total G into dz and sums
     // G dlog f/dlb over the chunk's tokens
     {
-      const GBuf bdl = win(a.dlog_f, k);
+      const GBuf bdl = wino(a.dlog_f, k);
       // per-head decay: dlog a [B,T,H], one value per token
-      const GBuf bda((char *)a.dlog_f + (((size_t)(k.bh / H) * T_ + k.n * C) * H + k.bh % H) * sizeof(T),
-                     (uint32_t)(k.len * H * sizeof(T)));
+      const GBuf bda((char *)a.dlog_f + (((size_t)(k.bh / H) * T_ + k.n * C) * H + k.bh % H) * sizeof(TO),
+                     (uint32_t)(k.len * H * sizeof(TO)));
       float carry[2], dlbs[2] = {0.f, 0.f}, lb2[2];
       lbs(lb2);
 #pragma unroll
@@ -679,7 +697,7 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
       // one token: its total G, then (gate mode) dz and its dlb term
       auto emit = [&](int t, const GateGrad *gg) {
         const int tt = 16 * w + 8 * hh + t;
-        Pack<T, 2> o;
+        Pack<TO, 2> o;
         float gs = 0.f;
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
@@ -689,13 +707,13 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
             if (tt < k.len) dlbs[e] += G * gg[e].dlb;
             G *= gg[e].dz;
           }
-          o.v[e] = from_f32<T>(G);
+          o.v[e] = from_f32<TO>(G);
           gs += G;
         }
         if constexpr (GM == kScalar) {
           gsum[t] = gs;
         } else {
-          bdl.stpack<T, 2, kStream>(tok(tt) + (uint32_t)c0 * sizeof(T), o);
+          bdl.stpack<TO, 2, kStream>(toko(tt) + (uint32_t)c0 * sizeof(TO), o);
         }
       };
       if (GM != kGate || !wide) {
@@ -739,9 +757,9 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
         tot += __shfl_xor(tot, 2, 64);
         tot += __shfl_xor(tot, 1, 64);
         if ((lane & 7) == 0) {
-          Pack<T, 1> oa;
-          oa.v[0] = from_f32<T>(tot);
-          bda.stpack<T, 1, kStream>((uint32_t)(16 * w + 8 * hh + (lane >> 3)) * H * sizeof(T), oa);
+          Pack<TO, 1> oa;
+          oa.v[0] = from_f32<TO>(tot);
+          bda.stpack<TO, 1, kStream>((uint32_t)(16 * w + 8 * hh + (lane >> 3)) * H * sizeof(TO), oa);
         }
       }
       if constexpr (GM == kGate) {
@@ -768,10 +786,10 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
 constexpr int kResGrid = 256;
 inline int res_grid(int nchunks) { return nchunks < kResGrid ? nchunks : kResGrid; }
 
-template <int GM>
+template <int GM, typename TO = bf16_t>
 hipError_t launch_chunk_bwd_res(const ChunkBwdArgs &a, hipStream_t stream) {
   const int nc = a.B * a.H * a.N;
-  hipLaunchKernelGGL(hgrn2_chunk_bwd_res_kernel<GM>, dim3(res_grid(nc)), dim3(CbwdResCfg::NT), 0, stream, a);
+  hipLaunchKernelGGL((hgrn2_chunk_bwd_res_kernel<GM, TO>), dim3(res_grid(nc)), dim3(CbwdResCfg::NT), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -27,7 +27,8 @@ struct ChunkFwdArgs {
   const void *q, *k, *v, *log_f;  // [B,T,H,D]; log_f holds the gate pre-activation in gate mode
   const float *lb;                // gate mode: lower bound of f, [H,D]
   const void *states;             // [B,H,N+1,D,D] input dtype; entry n = state before chunk n
-  void *y;                        // [B,T,H,D]
+  void *y;                        // [B,T,H,D], the input dtype or (out_f32) float32
+  int out_f32 = 0;                // bfloat16 inputs: write y as float32
 };
 
 template <typename T, int D, int C> struct CfwdCfg {
@@ -79,7 +80,8 @@ __device__ __forceinline__ void block_prefix(const Pack<T, CPL> *pk, const Pack<
     }
 }
 
-template <typename T, int D, int C, int GM>
+// TO: the element type of y (T, or float32 for bfloat16 inputs)
+template <typename T, int D, int C, int GM, typename TO = T>
 __global__ __launch_bounds__(4 * C) void hgrn2_chunk_fwd_kernel(ChunkFwdArgs a) {
   using Cfg = CfwdCfg<T, D, C>;
   constexpr int NW = Cfg::NW, NT = Cfg::NT, NB = Cfg::NB, CPL = Cfg::CPL, CB = Cfg::CB, KSD = Cfg::KSD,
@@ -360,29 +362,42 @@ __global__ __launch_bounds__(4 * C) void hgrn2_chunk_fwd_kernel(ChunkFwdArgs a) 
       }
     }
 
-  // ---- y: stage this wave's rows in its own qo rows, store whole rows
+  if constexpr (std::is_same<TO, T>::value) {
+    // ---- y: stage this wave's rows in its own qo rows, store whole rows
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb)
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm.qo[XT::at(16 * w + 4 * g + r, 16 * cb + n16)] = from_f32<T>(Y[cb][r]);
-  wave_lds_sync();
-  constexpr int RV = 16 * D / EPV;  // 16-byte vectors in this wave's 16 rows
+      for (int r = 0; r < 4; ++r) sm.qo[XT::at(16 * w + 4 * g + r, 16 * cb + n16)] = from_f32<T>(Y[cb][r]);
+    wave_lds_sync();
+    constexpr int RV = 16 * D / EPV;  // 16-byte vectors in this wave's 16 rows
 #pragma unroll
-  for (int i = 0; i < (RV + 63) / 64; ++i) {
-    const int idx = lane + 64 * i;
-    const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
-    const int t = 16 * w + row;
-    if (idx < RV && t < len) {
-      const uint4 u = *(const uint4 *)&sm.qo[XT::at(t, col)];
-      __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, u), (u32x4_t *)(gy + (tok(t) + col)));
+    for (int i = 0; i < (RV + 63) / 64; ++i) {
+      const int idx = lane + 64 * i;
+      const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
+      const int t = 16 * w + row;
+      if (idx < RV && t < len) {
+        const uint4 u = *(const uint4 *)&sm.qo[XT::at(t, col)];
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, u), (u32x4_t *)(gy + (tok(t) + col)));
+      }
     }
+  } else {
+    // ---- float32 y straight from the accumulators (no rounding to T): each
+    // 16 lanes of a group write 64 contiguous bytes of one row
+    TO *gyo = (TO *)a.y + cbase;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * w + 4 * g + r;
+        if (t < len) __builtin_nontemporal_store(Y[cb][r], gyo + (tok(t) + 16 * cb + n16));
+      }
   }
 }
 
-template <typename T, int D, int C, int GM>
+template <typename T, int D, int C, int GM, typename TO = T>
 hipError_t launch_chunk_fwd(const ChunkFwdArgs &a, hipStream_t stream) {
   using Cfg = CfwdCfg<T, D, C>;
-  hipLaunchKernelGGL((hgrn2_chunk_fwd_kernel<T, D, C, GM>), dim3(a.B * a.H * a.N), dim3(Cfg::NT), 0, stream, a);
+  hipLaunchKernelGGL((hgrn2_chunk_fwd_kernel<T, D, C, GM, TO>), dim3(a.B * a.H * a.N), dim3(Cfg::NT), 0, stream, a);
   return hipGetLastError();
 }
 

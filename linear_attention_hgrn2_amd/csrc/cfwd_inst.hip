@@ -4,6 +4,12 @@
 namespace hgrn2 {
 
 template <typename T, int D, int C> struct ChunkFwdOp {
+  template <typename TO> static hipError_t go(int gm, const ChunkFwdArgs &a, hipStream_t s) {
+    if (gm == kTied) return launch_chunk_fwd<T, D, C, kTied, TO>(a, s);
+    if (gm == kGate) return launch_chunk_fwd<T, D, C, kGate, TO>(a, s);
+    if (gm == kScalar) return launch_chunk_fwd<T, D, C, kScalar, TO>(a, s);
+    return launch_chunk_fwd<T, D, C, kUntied, TO>(a, s);
+  }
   static hipError_t run(int gm, const ChunkFwdArgs *a, hipStream_t s) {
     // tiles too large for the 160 KB LDS (float32 at D = 128, chunk 128): no kernel
     if constexpr (sizeof(typename CfwdCfg<T, D, C>::Smem) > 160 * 1024) {
@@ -11,10 +17,11 @@ template <typename T, int D, int C> struct ChunkFwdOp {
     } else {
       if (gm < kUntied || gm > kScalar) return hipErrorNotSupported;
       if (!a) return hipSuccess;
-      if (gm == kTied) return launch_chunk_fwd<T, D, C, kTied>(*a, s);
-      if (gm == kGate) return launch_chunk_fwd<T, D, C, kGate>(*a, s);
-      if (gm == kScalar) return launch_chunk_fwd<T, D, C, kScalar>(*a, s);
-      return launch_chunk_fwd<T, D, C, kUntied>(*a, s);
+      // float32 y for bfloat16 inputs (float32 inputs write float32 anyway)
+      if constexpr (std::is_same<T, bf16_t>::value) {
+        if (a->out_f32) return go<float>(gm, *a, s);
+      }
+      return go<T>(gm, *a, s);
     }
   }
 };

@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace hgrn2 {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));

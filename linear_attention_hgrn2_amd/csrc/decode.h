@@ -21,7 +21,8 @@ struct DecodeArgs {
   const void *q, *k, *v, *log_f;  // log_f holds z in gate mode
   const float *lb;                // gate mode: lower bound of f, [H,D]
   float *state;
-  void *y;
+  void *y;          // [B,H,D], the input dtype or (out_f32) float32
+  int out_f32 = 0;  // bfloat16 inputs: write y as float32
 };
 
 template <int D> struct DecodeCfg {
@@ -32,7 +33,8 @@ template <int D> struct DecodeCfg {
   static_assert(D % RG == 0, "row split");
 };
 
-template <typename TIn, int D, int GM>
+// TO: the element type of y (TIn, or float32 for bfloat16 inputs)
+template <typename TIn, int D, int GM, typename TO = TIn>
 __global__ __launch_bounds__(256) void hgrn2_decode_kernel(DecodeArgs a) {
   using Cfg = DecodeCfg<D>;
   constexpr int CG = Cfg::CG, RG = Cfg::RG, PASSES = Cfg::PASSES;
@@ -95,17 +97,17 @@ __global__ __launch_bounds__(256) void hgrn2_decode_kernel(DecodeArgs a) {
       r.z += u.z;
       r.w += u.w;
     }
-    TIn *gy = (TIn *)a.y + (size_t)bh * D + 4 * tid;
-    gy[0] = from_f32<TIn>(r.x);
-    gy[1] = from_f32<TIn>(r.y);
-    gy[2] = from_f32<TIn>(r.z);
-    gy[3] = from_f32<TIn>(r.w);
+    TO *gy = (TO *)a.y + (size_t)bh * D + 4 * tid;
+    gy[0] = from_f32<TO>(r.x);
+    gy[1] = from_f32<TO>(r.y);
+    gy[2] = from_f32<TO>(r.z);
+    gy[3] = from_f32<TO>(r.w);
   }
 }
 
-template <typename TIn, int D, int GM>
+template <typename TIn, int D, int GM, typename TO = TIn>
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
-  hipLaunchKernelGGL((hgrn2_decode_kernel<TIn, D, GM>), dim3(a.B * a.H), dim3(DecodeCfg<D>::NT), 0,
+  hipLaunchKernelGGL((hgrn2_decode_kernel<TIn, D, GM, TO>), dim3(a.B * a.H), dim3(DecodeCfg<D>::NT), 0,
                      stream, a);
   return hipGetLastError();
 }

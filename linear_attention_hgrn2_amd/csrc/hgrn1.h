@@ -52,7 +52,8 @@ struct H1Args {
   H1Sum fsum;                          // final backward without saved states: the forward summaries
   float *states;                       // [B,S,C] state entering each segment: written by the final
                                        // forward (if not null), read by the final backward (if not null)
-  void *y, *dq, *dk, *dv, *dlog_f;     // [B,T,C]
+  void *y, *dq, *dk, *dv, *dlog_f;     // [B,T,C], the input dtype or (out_f32) float32
+  int out_f32 = 0;                     // bfloat16 inputs: write y and the gradients as float32
 };
 
 // the workgroup's (b, segment, channel-pair block) and this thread's pair
@@ -196,14 +197,16 @@ __device__ __forceinline__ float2 h1_seg_carry(const H1Sum &u, const H1Args &a, 
   return make_float2(fmaf(__expf(pa.x), gc.x, pb.x), fmaf(__expf(pa.y), gc.y, pb.y));
 }
 
-// pass 3, forward: y from the state entering the segment
-template <typename T, int GM>
+// pass 3, forward: y from the state entering the segment (TO: the element
+// type of y, T or float32 for bfloat16 inputs)
+template <typename T, int GM, typename TO = T>
 __global__ __launch_bounds__(kH1Pairs) void hgrn1_final_fwd_kernel(H1Args a) {
   const H1Place pl = h1_place(a);
   const uint32_t RB = (uint32_t)a.C * sizeof(T), cb = (uint32_t)(2 * pl.p) * sizeof(T);
+  const uint32_t RBO = (uint32_t)a.C * sizeof(TO), cbo = (uint32_t)(2 * pl.p) * sizeof(TO);
   const GBuf bq = h1_win<T>(a.q, a, pl), bk = h1_win<T>(a.k, a, pl), bv = h1_win<T>(a.v, a, pl),
              bl = h1_win<T>(a.log_f, a, pl);
-  const GBuf by((char *)a.y + pl.rowbase * sizeof(T), (uint32_t)(pl.len * a.C * sizeof(T)));
+  const GBuf by((char *)a.y + pl.rowbase * sizeof(TO), (uint32_t)(pl.len * a.C * sizeof(TO)));
   Pack<T, 2> pq[kH1Seg], pk[kH1Seg], pv[kH1Seg], pl_[kH1Seg];
 #pragma unroll
   for (int i = 0; i < kH1Seg; ++i) {
@@ -221,15 +224,15 @@ __global__ __launch_bounds__(kH1Pairs) void hgrn1_final_fwd_kernel(H1Args a) {
   }
 #pragma unroll
   for (int i = 0; i < kH1Seg; ++i) {
-    Pack<T, 2> o;
+    Pack<TO, 2> o;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const float lf = floor_logf(to_f32(pl_[i].v[e])), f = __expf(lf);
       const float kv = GM == kTied ? tied_k_ex(lf, f) : to_f32(pk[i].v[e]);
       h[e] = fmaf(f, h[e], kv * to_f32(pv[i].v[e]));
-      o.v[e] = from_f32<T>(to_f32(pq[i].v[e]) * h[e]);
+      o.v[e] = from_f32<TO>(to_f32(pq[i].v[e]) * h[e]);
     }
-    if (pl.valid) by.template stpack<T, 2, kStream>(i * RB + cb, o);
+    if (pl.valid) by.template stpack<TO, 2, kStream>(i * RBO + cbo, o);
   }
 }
 
@@ -239,16 +242,18 @@ __global__ __launch_bounds__(kH1Pairs) void hgrn1_final_fwd_kernel(H1Args a) {
 // right (h at the midpoint first), which halves the registers the recomputed
 // h and the token rows need; the first half's rows, read for the midpoint,
 // wait in LDS until its own gradients, so no row is read twice.
-template <typename T, int GM>
+template <typename T, int GM, typename TO = T>
 __global__ __launch_bounds__(kH1Pairs) void hgrn1_final_bwd_kernel(H1Args a) {
   constexpr int HS = kH1Seg / 2;
   const H1Place pl = h1_place(a);
   const uint32_t RB = (uint32_t)a.C * sizeof(T), cb = (uint32_t)(2 * pl.p) * sizeof(T);
-  const uint32_t rows = (uint32_t)(pl.len * a.C * sizeof(T));
+  // the gradients' rows (TO elements)
+  const uint32_t RBO = (uint32_t)a.C * sizeof(TO), cbo = (uint32_t)(2 * pl.p) * sizeof(TO);
+  const uint32_t rows = (uint32_t)(pl.len * a.C * sizeof(TO));
   const GBuf bq = h1_win<T>(a.q, a, pl), bk = h1_win<T>(a.k, a, pl), bv = h1_win<T>(a.v, a, pl),
              bl = h1_win<T>(a.log_f, a, pl), bdy = h1_win<T>(a.dy, a, pl);
-  const GBuf bdq((char *)a.dq + pl.rowbase * sizeof(T), rows), bdk((char *)a.dk + pl.rowbase * sizeof(T), rows),
-      bdv((char *)a.dv + pl.rowbase * sizeof(T), rows), bdl((char *)a.dlog_f + pl.rowbase * sizeof(T), rows);
+  const GBuf bdq((char *)a.dq + pl.rowbase * sizeof(TO), rows), bdk((char *)a.dk + pl.rowbase * sizeof(TO), rows),
+      bdv((char *)a.dv + pl.rowbase * sizeof(TO), rows), bdl((char *)a.dlog_f + pl.rowbase * sizeof(TO), rows);
   const size_t co = ((size_t)pl.b * a.S + pl.s) * a.C + 2 * pl.p;
   float2 hst = make_float2(0.f, 0.f), gin = make_float2(0.f, 0.f);  // state entering, gradient from the right
   if (pl.valid) {
@@ -309,7 +314,7 @@ __global__ __launch_bounds__(kH1Pairs) void hgrn1_final_bwd_kernel(H1Args a) {
     }
 #pragma unroll
     for (int i = HS - 1; i >= 0; --i) {
-      Pack<T, 2> oq, ok, ov, ol;
+      Pack<TO, 2> oq, ok, ov, ol;
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const float lf = floor_logf(to_f32(pl_[i].v[e])), f = __expf(lf);
@@ -318,19 +323,19 @@ __global__ __launch_bounds__(kH1Pairs) void hgrn1_final_bwd_kernel(H1Args a) {
         const float g = fmaf(to_f32(pq[i].v[e]), dy, e_[e]);
         const float hp = i ? hs[i - 1][e] : h0s[e];
         const float dk = g * vv;
-        oq.v[e] = from_f32<T>(dy * hs[i][e]);
-        ok.v[e] = from_f32<T>(dk);
-        ov.v[e] = from_f32<T>(g * kv);
+        oq.v[e] = from_f32<TO>(dy * hs[i][e]);
+        ok.v[e] = from_f32<TO>(dk);
+        ov.v[e] = from_f32<TO>(g * kv);
         // tied: the total derivative, dlog f - f dk
-        ol.v[e] = from_f32<T>(GM == kTied ? f * (g * hp - dk) : g * f * hp);
+        ol.v[e] = from_f32<TO>(GM == kTied ? f * (g * hp - dk) : g * f * hp);
         e_[e] = f * g;
       }
       if (pl.valid) {
-        const uint32_t off = (t0 + i) * RB + cb;
-        bdq.template stpack<T, 2, kStream>(off, oq);
-        if constexpr (GM == kUntied) bdk.template stpack<T, 2, kStream>(off, ok);
-        bdv.template stpack<T, 2, kStream>(off, ov);
-        bdl.template stpack<T, 2, kStream>(off, ol);
+        const uint32_t off = (t0 + i) * RBO + cbo;
+        bdq.template stpack<TO, 2, kStream>(off, oq);
+        if constexpr (GM == kUntied) bdk.template stpack<TO, 2, kStream>(off, ok);
+        bdv.template stpack<TO, 2, kStream>(off, ov);
+        bdl.template stpack<TO, 2, kStream>(off, ol);
       }
     }
   };

@@ -43,8 +43,9 @@ struct SegFwdArgs {
   const float *lb;                // gate mode: lower bound of f, [H,D]
   const float *h0;                // P = 1: [B,H,D,D] float32 or null (zero), the initial state
   const float *sin;               // P > 1: [B,H,P,D,D] float32, entry p = the state entering segment p
-  void *y;                        // [B,T,H,D]
+  void *y;                        // [B,T,H,D], the input dtype or (out_f32) float32
   float *ht;                      // [B,H,D,D] float32 final state, or null
+  int out_f32 = 0;                // bfloat16 inputs: write y as float32
 };
 
 template <typename T, int D, int C> struct SfwdCfg {
@@ -80,7 +81,8 @@ template <typename T, int D, int C> struct SfwdCfg {
 // pair index p -> (i, j), i >= j, p = i (i + 1) / 2 + j
 __device__ __forceinline__ int sfwd_pair_i(int p) { return p >= 6 ? 3 : p >= 3 ? 2 : p >= 1 ? 1 : 0; }
 
-template <typename T, int D, int C, int GM>
+// TO: the element type of y (T, or float32 for bfloat16 inputs)
+template <typename T, int D, int C, int GM, typename TO = T>
 __global__ __launch_bounds__((SfwdCfg<T, D, C>::NT)) void hgrn2_seg_fwd_kernel(SegFwdArgs a) {
   using Cfg = SfwdCfg<T, D, C>;
   constexpr int NB = Cfg::NB, NWV = Cfg::NWV, NT = Cfg::NT, CPL = Cfg::CPL, JB = Cfg::JB, KSD = Cfg::KSD,
@@ -378,7 +380,19 @@ __global__ __launch_bounds__((SfwdCfg<T, D, C>::NT)) void hgrn2_seg_fwd_kernel(S
     }
     __syncthreads();  // B3: every wave is done with qo, the scores and the state's copy
 
-    // ---- P3: y out (staged in this wave's half of block w's qo rows); the state update
+    // ---- P3: y out (staged in this wave's half of block w's qo rows, or
+    // float32 straight from the accumulators); the state update
+    if constexpr (!std::is_same<TO, T>::value) {
+      TO *gyo = (TO *)a.y + (((size_t)b * T_ + t0) * H + h) * D;
+#pragma unroll
+      for (int cb = 0; cb < HC; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * w + 4 * g + r;
+          if (t < len)
+            __builtin_nontemporal_store(Y[cb][r], gyo + ((size_t)t * H * D + (D / 2) * hh + 16 * cb + n16));
+        }
+    } else {
 #pragma unroll
     for (int cb = 0; cb < HC; ++cb)
 #pragma unroll
@@ -398,6 +412,7 @@ __global__ __launch_bounds__((SfwdCfg<T, D, C>::NT)) void hgrn2_seg_fwd_kernel(S
           __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, u), (u32x4_t *)(gy + ((size_t)t * H * D + col)));
         }
       }
+    }
     }
     // S^T <- S^T Diag(e^Gamma) + v^T kh
     // (NWV = 8 divides JB for D = 128: every tile of this wave has jb = wv, and
@@ -459,10 +474,10 @@ __global__ __launch_bounds__(256) void hgrn2_seg_carry_kernel(int BH, int NSEG, 
   }
 }
 
-template <typename T, int D, int C, int GM>
+template <typename T, int D, int C, int GM, typename TO = T>
 hipError_t launch_seg_fwd(const SegFwdArgs &a, hipStream_t stream) {
   using Cfg = SfwdCfg<T, D, C>;
-  hipLaunchKernelGGL((hgrn2_seg_fwd_kernel<T, D, C, GM>), dim3((unsigned)((long long)a.B * a.H * a.P)),
+  hipLaunchKernelGGL((hgrn2_seg_fwd_kernel<T, D, C, GM, TO>), dim3((unsigned)((long long)a.B * a.H * a.P)),
                      dim3(Cfg::NT), 0, stream, a);
   return hipGetLastError();
 }

@@ -11,7 +11,12 @@ namespace {
 
 template <typename T, int D, int GM> hipError_t seg_t(int op, const void *a, hipStream_t s) {
   if (op == 0) return launch_scan<T, D, 64, false, GM, true>(*(const ScanArgs *)a, s);
-  return launch_seg_fwd<T, D, 64, GM>(*(const SegFwdArgs *)a, s);
+  const SegFwdArgs &fa = *(const SegFwdArgs *)a;
+  // float32 y for bfloat16 inputs (float32 inputs write float32 anyway)
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    if (fa.out_f32) return launch_seg_fwd<T, D, 64, GM, float>(fa, s);
+  }
+  return launch_seg_fwd<T, D, 64, GM>(fa, s);
 }
 
 template <typename T, int D> hipError_t seg_g(int gm, int op, const void *a, hipStream_t s) {

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.hgrn2_abi_version() == 8
+    assert lib.hgrn2_abi_version() == 9
     for s in range(5):
         assert lib.hgrn2_status_string(s).startswith(b"HGRN2_")
 
@@ -95,6 +95,39 @@ def test_fwd_rejections(lib):
     assert _fwd(lib) == 3                              # no states_out and no workspace
     assert _fwd(lib, ws=FAKE + 0x8000, wsb=100) == 3   # workspace too small
     assert _fwd(lib, st=FAKE + 0x2000) == 1            # states_out overlaps v
+
+
+OUT_F32 = 0x100  # HGRN2_OUT_F32
+
+
+def test_out_f32_flag(lib):
+    """bfloat16 inputs with float32 token outputs: the same kernels exist, the
+    sizes of states and workspaces do not change, other bits are rejected,
+    and the aliasing checks size the outputs at 4 bytes per element."""
+    assert lib.hgrn2_supported(128, 64, 1 | OUT_F32) == 1
+    assert lib.hgrn2_supported(128, 128, 1 | OUT_F32) == 1
+    assert lib.hgrn2_supported(128, 128, 0 | OUT_F32) == 0
+    assert lib.hgrn2_states_bytes(8, 4096, 16, 128, 128, 64, 1 | OUT_F32) == 8 * 16 * 65 * 128 * 128 * 2
+    for have in (0, 1):
+        assert (lib.hgrn2_bwd_workspace_bytes(2, 300, 3, 64, 64, 64, 1 | OUT_F32, have)
+                == lib.hgrn2_bwd_workspace_bytes(2, 300, 3, 64, 64, 64, 1, have))
+        assert (lib.hgrn2_fwd_workspace_bytes(1, 32768, 32, 128, 128, 64, 1 | OUT_F32, have)
+                == lib.hgrn2_fwd_workspace_bytes(1, 32768, 32, 128, 128, 64, 1, have))
+    assert _fwd(lib, dt=1 | 0x200) == 1
+    assert _fwd(lib, dt=2) == 1
+    assert lib.hgrn2_states_bytes(8, 4096, 16, 128, 128, 64, 1 | 0x200) == 0
+    # y ends 16 bytes into q when it holds float32 (10 tokens x 16 channels x 4 bytes), and
+    # 304 bytes before q when it holds bfloat16; k (320 bytes) ends where q starts, inside y
+    y = FAKE - (10 * 16 * 4 - 16)
+    kw = dict(y=y, k=FAKE - 320, ws=FAKE + 0x8000, wsb=1 << 30)
+    assert _fwd(lib, dt=1 | OUT_F32, **kw) == 1
+    assert b"y overlaps input q" in lib.hgrn2_last_error()
+    assert _fwd(lib, dt=1, **kw) == 1
+    assert b"y overlaps input k" in lib.hgrn2_last_error()
+    # decode: y [1, 1, 16] float32 reaching into q
+    r = lib.hgrn2_decode_step(1, 1, 16, 16, 1 | OUT_F32, FAKE, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000,
+                              FAKE + 0x4000, FAKE - 48, None)
+    assert r == 1 and b"overlaps" in lib.hgrn2_last_error()
 
 
 def test_bwd_rejections(lib):
