@@ -378,6 +378,16 @@ __device__ __forceinline__ float gate_log_f(float z, float lb) {
   return __logf(arg) + (neg0 ? z : 0.f);
 }
 
+// f itself (and k = 1 - f) from the same pieces, with no logarithm: for the
+// passes that need only products of f (e^{sums of log f}).  f may underflow
+// to 0 where log f is below about -87, where e^{log f} is 0 as well.
+__device__ __forceinline__ void gate_f_k(float z, float lb, float &f, float &k) {
+  const GateParts p = gate_parts(z);
+  const bool neg0 = z < 0.f && lb == 0.f;
+  f = neg0 ? p.u * p.r : (z >= 0.f ? fmaf(lb, p.u, 1.f) : lb + p.u) * p.r;
+  k = (1.f - lb) * (z >= 0.f ? p.u * p.r : p.r);
+}
+
 // k = 1 - f = (1 - lb) sigmoid(-z), without cancellation
 __device__ __forceinline__ float gate_k(float z, float lb) {
   const GateParts p = gate_parts(z);

@@ -200,13 +200,40 @@ __global__ __launch_bounds__((ScanCfg<T, D, C, REV>::NT)) void hgrn2_scan_kernel
     // ---- chunk-local prefix of the floored log f: within the lane's run, then across runs
     float l[TPR], kx[TPR];  // kx: k of the run's tokens (forward; formed with log f)
     float run = 0.f;
+    if constexpr (GM == kGate) {
+      // f from z with no logarithm: l holds products of f within the run
+      // (forward: of the later tokens, e^{run - prefix}; backward: of the
+      // tokens so far, e^{prefix}) and only the run total is taken to the log
+      // domain, floored as the per-token floors would floor it
+      float f[TPR];
 #pragma unroll
-    for (int i = 0; i < TPR; ++i) {
-      float lf;
-      if constexpr (REV) lf = lf_of<GM>(to_f32(pl[i]), lbv, n * C + ri * TPR + i < T_);
-      else lf_k<GM>(px[i], pl[i], lbv, n * C + ri * TPR + i < T_, lf, kx[i]);
-      run += lf;
-      l[i] = run;
+      for (int i = 0; i < TPR; ++i) {
+        float kk;
+        gate_f_k(to_f32(pl[i]), lbv, f[i], kk);
+        if (n * C + ri * TPR + i >= T_) f[i] = 1.f, kk = 0.f;  // past the end: no decay, no input
+        if constexpr (!REV) kx[i] = kk;
+      }
+      float pp = 1.f;
+      if constexpr (REV) {
+#pragma unroll
+        for (int i = 0; i < TPR; ++i) l[i] = pp *= f[i];
+      } else {
+#pragma unroll
+        for (int i = TPR - 1; i >= 0; --i) {
+          l[i] = pp;
+          pp *= f[i];
+        }
+      }
+      run = fmaxf(__logf(pp), TPR * kLogFloor);
+    } else {
+#pragma unroll
+      for (int i = 0; i < TPR; ++i) {
+        float lf;
+        if constexpr (REV) lf = lf_of<GM>(to_f32(pl[i]), lbv, n * C + ri * TPR + i < T_);
+        else lf_k<GM>(px[i], pl[i], lbv, n * C + ri * TPR + i < T_, lf, kx[i]);
+        run += lf;
+        l[i] = run;
+      }
     }
     sm.Lr[ri][cl] = run;
 #pragma unroll
@@ -218,21 +245,33 @@ __global__ __launch_bounds__((ScanCfg<T, D, C, REV>::NT)) void hgrn2_scan_kernel
     __syncthreads();
     // ---- decayed x: forward x e^{Gamma - b_t}, backward x e^{b_t}
     {
-      float P = 0.f, G = 0.f;  // earlier runs' total, chunk total
+      float P = 0.f, G = 0.f, Q = 0.f;  // earlier runs' total, chunk total, later runs' total
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
         const float L = sm.Lr[r][cl];
         P += (r < ri) ? L : 0.f;
+        Q += (r > ri) ? L : 0.f;
         G += L;
       }
       if (ri == 0) sm.eG[cl] = __expf(G);
       gacc += G;
+      if constexpr (GM == kGate) {
+        // e^{b_t} (backward) or e^{Gamma - b_t} (forward) as the other runs'
+        // factor times the run's own product of f
+        const float e = __expf(REV ? P : Q);
 #pragma unroll
-      for (int i = 0; i < TPR; ++i) {
-        const float b_t = P + l[i];
-        const float ex = REV ? b_t : fminf(G - b_t, 0.f);
-        const float xv = REV ? to_f32(px[i]) : kx[i];
-        sm.x[XT::at(ri * TPR + i, cl)] = from_f32<T>(xv * __expf(ex));
+        for (int i = 0; i < TPR; ++i) {
+          const float xv = REV ? to_f32(px[i]) : kx[i];
+          sm.x[XT::at(ri * TPR + i, cl)] = from_f32<T>(xv * (e * l[i]));
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < TPR; ++i) {
+          const float b_t = P + l[i];
+          const float ex = REV ? b_t : fminf(G - b_t, 0.f);
+          const float xv = REV ? to_f32(px[i]) : kx[i];
+          sm.x[XT::at(ri * TPR + i, cl)] = from_f32<T>(xv * __expf(ex));
+        }
       }
     }
     flush();  // the state staged in the previous step (read here, rewritten after the next barrier)
