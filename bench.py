@@ -54,6 +54,11 @@ PMC_CMD = ("rocprofv3 --pmc {ctr} -d " + PROF_OUT + "/{dir} -o run --output-form
 MFMA_CMD = ("rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 MfmaUtil -d " + PROF_OUT + "/mfma -o run "
             "--output-format csv -- python3 bench.py --only train --steps 2 --warmup 1 --no-cpu")
 MFMA_SUMMARY = os.path.join(PROFILES, "hgrn2_mfma_train_bf16_B8H16T4096.txt")
+# the forward-only legs (the segmented forward), one trace and two counter runs each
+FWD_TRACE_CMD = ("rocprofv3 --kernel-trace --stats -d " + PROF_OUT + "/trace_{leg} -o run --output-format csv "
+                 "-- python3 bench.py --only {leg} --steps 20 --warmup 3 --no-cpu")
+FWD_PMC_CMD = ("rocprofv3 --pmc {ctr} -d " + PROF_OUT + "/{dir}_{leg} -o run --output-format csv "
+               "-- python3 bench.py --only {leg} --steps 2 --warmup 1 --no-cpu --calib-copy")
 
 
 def parse():
@@ -68,6 +73,9 @@ def parse():
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 1 GiB elementwise pass, read once and written once "
                         "(calibrates profiler byte counters)")
+    p.add_argument("--summarize-fwd", nargs=4, metavar=("LEG", "TRACE", "FETCH", "WRITE"),
+                   help="write the profiles/ summary of a forward-only leg from FWD_TRACE_CMD and FWD_PMC_CMD "
+                        "output")
     p.add_argument("--summarize", nargs="+", metavar="DIR",
                    help="TRACE_DIR FETCH_DIR WRITE_DIR [MFMA_DIR]: write the profiles/ summaries "
                         "from rocprofv3 csv output and exit")
@@ -174,20 +182,32 @@ GATE_SUFFIX = {"0": "", "1": "_tied", "2": "_gate", "3": "_scalar"}
 
 def kernel_label(name: str):
     """rocprofv3 kernel name -> a label of TRAIN_KERNELS, TIED_KERNELS or GATE_KERNELS,
-    "decode[_tied|_gate]", "dlb", or None.  The last template argument is the gate
-    mode (0 untied, 1 tied, 2 gate): scan <T, D, C, REV, GM>; chunk kernels
-    <T, D, C, GM> or <GM>; decode <T, D, GM>."""
+    "decode[_tied|_gate|_scalar]", "dlb", "seg_scan", "seg_fwd", "seg_carry", an
+    HGRN1 label, or None.  The gate mode (0 untied, 1 tied, 2 gate, 3 per-head
+    decay) is a template argument at a fixed place: scan <T, D, C, REV, GM, SEG>;
+    chunk forward and generic backward <T, D, C, GM, TO>; resident backward
+    <GM, TO>; segment walk <T, D, C, GM, TO>; decode <T, D, GM, TO>."""
     n = _short(name)
     a = _template_args(n)
-    sfx = GATE_SUFFIX.get(a[-1], "") if a else ""
+
+    def sfx(i):
+        return GATE_SUFFIX.get(a[i], "") if len(a) > i else ""
     if n.startswith("hgrn2_scan_kernel"):
-        return ("scan_rev" if len(a) > 3 and a[3] == "true" else "scan") + sfx
+        if len(a) > 5 and a[5] == "true":
+            return "seg_scan" + sfx(4)
+        return ("scan_rev" if len(a) > 3 and a[3] == "true" else "scan") + sfx(4)
     if n.startswith("hgrn2_chunk_fwd_kernel"):
-        return "cfwd" + sfx
+        return "cfwd" + sfx(3)
+    if n.startswith("hgrn2_chunk_bwd_res_kernel"):
+        return "cbwd" + sfx(0)
     if n.startswith("hgrn2_chunk_bwd"):
-        return "cbwd" + sfx
+        return "cbwd" + sfx(3)
+    if n.startswith("hgrn2_seg_fwd_kernel"):
+        return "seg_fwd" + sfx(3)
+    if n.startswith("hgrn2_seg_carry_kernel"):
+        return "seg_carry"
     if n.startswith("hgrn2_decode_kernel"):
-        return "decode" + sfx
+        return "decode" + sfx(2)
     if n.startswith("hgrn2_dlb_reduce_kernel"):
         return "dlb"
     if n.startswith("hgrn1_"):
@@ -667,6 +687,93 @@ def summarize(trace_dir, fetch_dir, write_dir, mfma_dir=None):
         summarize_mfma(mfma_dir, {kernel_label(r["Name"]): float(r["AverageNs"]) for r in rows}, digest)
 
 
+def seg_plan(B, T, H, chunk, want_y=True, units=256):
+    """The segment plan hgrn2_fwd uses without stored states: P segments of G
+    chunks per (b, h), NSEG of them summarised (P - 1 when y is written)."""
+    BH, N = B * H, -(-T // chunk)
+    pt = min(N, max(1, -(-units // BH)))
+    G = -(-N // pt)
+    P = -(-N // G)
+    return P, G, (P - 1 if want_y else P)
+
+
+def fwd_leg_bytes(w):
+    """Algorithmic bytes per launch of the segmented forward's kernels (bf16
+    tokens, float32 states): every tensor each launch reads or writes, once."""
+    tok = w.B * w.T * w.H * w.D * 2
+    BH, S = w.B * w.H, w.D * w.D * 4
+    P, G, NSEG = seg_plan(w.B, w.T, w.H, w.chunk)
+    N = -(-w.T // w.chunk)
+    frac = min(1.0, NSEG * G / N)                     # the summarised share of each sequence
+    h0 = BH * S if w.h0std > 0 else 0
+    return {"seg_scan": 3 * tok * frac + BH * NSEG * (S + w.D * 4),      # k, v, log f in; end states, totals out
+            "seg_carry": h0 + BH * NSEG * (S + w.D * 4) + BH * (NSEG + 1) * S,
+            "seg_fwd": 5 * tok + BH * (P if P > 1 else 0) * S + (h0 if P == 1 else 0) + BH * S}, \
+        5 * tok + h0 + BH * S, (P, G, NSEG)
+
+
+def summarize_fwd(leg, trace_dir, fetch_dir, write_dir):
+    """profiles/ summary of one forward-only leg: kernel-trace statistics, the
+    algorithmic bytes of each launch, and the HBM bytes the counters saw."""
+    import synth
+    w = synth.WORKLOADS[leg]
+    digest = kernel_source_digest()
+    alg, comp, (P, G, NSEG) = fwd_leg_bytes(w)
+    rows = _csv(os.path.join(trace_dir, "run_kernel_stats.csv"))
+
+    def per_kernel(d, ctr):
+        acc = {}
+        for r in _csv(os.path.join(d, "run_counter_collection.csv")):
+            if r["Counter_Name"] == ctr:
+                acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    copy = [k for k in fetch if "MulFunctor" in k and k in write]
+    assert copy, "the counter runs need --calib-copy"
+    f_fac = CALIB_BYTES / (fetch[copy[0]] * 1024)
+    w_fac = CALIB_BYTES / (write[copy[0]] * 1024)
+    shape = "B%d H%d T%d d%d chunk%d bf16" % (w.B, w.H, w.T, w.D, w.chunk)
+    out = ["rocprofv3 kernel trace and HBM traffic, %s: hgrn2_fwd (y and the final state, no stored "
+           "states), %s" % (leg, shape),
+           "segment plan: P = %d segments of G = %d chunks per (b, h), %d summarised" % (P, G, NSEG),
+           "trace command: " + FWD_TRACE_CMD.format(leg=leg),
+           "fetch command: " + FWD_PMC_CMD.format(ctr="FETCH_SIZE", dir="fetch", leg=leg),
+           "write command: " + FWD_PMC_CMD.format(ctr="WRITE_SIZE", dir="write", leg=leg),
+           "fetch_scale: %.4f (a 1 GiB torch.mul reads FETCH_SIZE %.0f KiB)" % (f_fac, fetch[copy[0]]),
+           "write_scale: %.4f (and writes WRITE_SIZE %.0f KiB)" % (w_fac, write[copy[0]]),
+           "source_digest: " + digest, "",
+           "%-52s %6s %10s %10s %10s %10s %10s %8s" % ("kernel", "calls", "avg_us", "min_us", "alg_MB",
+                                                     "hbm_MB", "GB/s_alg", "hbm/alg")]
+    tot_us = tot_hbm = tot_alg = 0.0
+    for r in rows:
+        label = kernel_label(r["Name"])
+        if label is None:
+            continue
+        base = label.split("_tied")[0].split("_gate")[0].split("_scalar")[0]
+        a = alg.get(base)
+        k = r["Name"]
+        hb = None
+        if k in fetch and k in write:
+            hb = fetch[k] * 1024 * f_fac + write[k] * 1024 * w_fac
+        avg = float(r["AverageNs"]) / 1e3
+        out.append("%-52s %6d %10.1f %10.1f %10.1f %10s %10.1f %8s" % (
+            _short(k)[:52], int(r["Calls"]), avg, float(r["MinNs"]) / 1e3, (a or 0) / 1e6,
+            "%.1f" % (hb / 1e6) if hb is not None else "-", (a or 0) / (avg * 1e3),
+            "%.3f" % (hb / a) if (hb is not None and a) else "-"))
+        tot_us += avg
+        tot_alg += a or 0
+        tot_hbm += hb or 0
+    out += ["",
+            "per call: %.1f us of kernels; algorithmic %.1f MB, counted %.1f MB, compulsory %.1f MB "
+            "(q, k, v, log f in, y out, h0 in, ht out); counted / compulsory = %.3f"
+            % (tot_us, tot_alg / 1e6, tot_hbm / 1e6, comp / 1e6, tot_hbm / comp)]
+    name = os.path.join(PROFILES, "hgrn2_kernels_%s_%s.txt" % (leg, shape.replace(" ", "_")))
+    with open(name, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
 def summarize_mfma(mfma_dir, avg_ns, digest):
     """Matrix-core work the counters saw per launch: executed bf16 MFMA flops
     (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512), the rate over the kernel-trace average
@@ -711,6 +818,9 @@ def main():
     args = parse()
     if args.summarize:
         summarize(*args.summarize)
+        return
+    if args.summarize_fwd:
+        summarize_fwd(*args.summarize_fwd)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
