@@ -118,7 +118,7 @@ def _same_after_rounding(name, o32, o16):
 
 
 @pytest.mark.parametrize("gm", MODES)
-@pytest.mark.parametrize("D,C", [(128, 64), (64, 64), (128, 32), (32, 128), (128, 128)])
+@pytest.mark.parametrize("D,C", [(128, 64), (64, 64), (128, 32), (32, 128), (128, 128), (16, 16)])
 def test_out_f32_fwd_bwd(gm, D, C):
     """Forward (segmented walk when no state is kept, stored-state otherwise)
     and backward, every gate mode; D 128 / chunk 64 is the resident backward."""
@@ -146,6 +146,28 @@ def test_out_f32_fwd_bwd(gm, D, C):
           flush=True)
     for n, e in errs.items():
         assert worst(e) <= TOL["bf16"], (n, fmt(e))
+
+
+def test_out_f32_flag_is_a_no_op_for_float32_inputs():
+    """float32 inputs write float32 anyway: with the flag the calls give the
+    same bits as without it (forward walk and stored-state, backward)."""
+    import torch
+    import linear_attention_hgrn2_amd as m
+    w = synth.Workload("case", B=2, H=2, T=150, D=64, chunk=0, dtype="f32", lam=0.3, qscale=1.0, h0std=0.5,
+                       train=True, seed=4)
+    d = synth.generate(w)
+    q, k, v, lf, dy = (to_dev(d[n], "f32") for n in ("q", "k", "v", "log_f", "dy"))
+    h0 = to_dev(d["h0"], "f32")
+    outs = {}
+    for od in (torch.float32, None):
+        y, ht, _ = m.fwd(q, k, v, lf, h0, chunk=64, out_dtype=od)
+        ys, _, st = m.fwd(q, k, v, lf, h0, chunk=64, want_states=True, out_dtype=od)
+        g = m.bwd(q, k, v, lf, dy, h0, None, st, chunk=64, out_dtype=od)
+        outs[od] = (y, ht, ys) + tuple(g)
+    torch.cuda.synchronize()
+    for a, b in zip(outs[torch.float32], outs[None]):
+        assert a.dtype == b.dtype == torch.float32
+        assert torch.equal(a, b)
 
 
 def test_out_f32_is_closer_to_the_oracle():
