@@ -175,8 +175,6 @@ def fwd(q, k, v, log_f, h0=None, *, chunk=64, want_ht=True, want_states=False, w
     B, T, H, D = q.shape
     dt = q.dtype
     odt, code = _odt(dt, out_dtype)
-    if dt not in _DT:
-        raise ValueError("dtype must be float32 or bfloat16")
     for n, t in (("q", q), ("k", k), ("v", v), ("log_f", log_f)):
         _tok(n, t, B, T, H, D, dt)
     _st("h0", h0, B, H, D)
@@ -357,6 +355,7 @@ def decode_step(q, k, v, log_f, state, *, y=None, out_dtype=None):
     _st("state", state, B, H, D)
     if y is None:
         y = torch.empty_like(q, dtype=odt)
+    _vec3("y", y, B, H, D, odt)
     st = _lib().hgrn2_decode_step(B, H, D, D, code, _ptr(q), _ptr(k), _ptr(v), _ptr(log_f),
                                   _ptr(state), _ptr(y), _stream())
     _check(st, "hgrn2_decode_step")
@@ -373,8 +372,6 @@ def fwd_tied(q, v, log_f, h0=None, *, chunk=64, want_ht=True, want_states=False,
     B, T, H, D = q.shape
     dt = q.dtype
     odt, code = _odt(dt, out_dtype)
-    if dt not in _DT:
-        raise ValueError("dtype must be float32 or bfloat16")
     for n, t in (("q", q), ("v", v), ("log_f", log_f)):
         _tok(n, t, B, T, H, D, dt)
     _st("h0", h0, B, H, D)
@@ -482,6 +479,7 @@ def decode_step_tied(q, v, log_f, state, *, y=None, out_dtype=None):
     _st("state", state, B, H, D)
     if y is None:
         y = torch.empty_like(q, dtype=odt)
+    _vec3("y", y, B, H, D, odt)
     st = _lib().hgrn2_decode_step_tied(B, H, D, D, code, _ptr(q), _ptr(v), _ptr(log_f), _ptr(state), _ptr(y),
                                        _stream())
     _check(st, "hgrn2_decode_step_tied")
@@ -502,8 +500,6 @@ def fwd_gate(q, v, z, lower_bound, h0=None, *, chunk=64, want_ht=True, want_stat
     B, T, H, D = q.shape
     dt = q.dtype
     odt, code = _odt(dt, out_dtype)
-    if dt not in _DT:
-        raise ValueError("dtype must be float32 or bfloat16")
     for n, t in (("q", q), ("v", v), ("z", z)):
         _tok(n, t, B, T, H, D, dt)
     _lb(lower_bound, H, D, q.device)
@@ -580,6 +576,7 @@ def decode_step_gate(q, v, z, lower_bound, state, *, y=None, out_dtype=None):
     _st("state", state, B, H, D)
     if y is None:
         y = torch.empty_like(q, dtype=odt)
+    _vec3("y", y, B, H, D, odt)
     st = _lib().hgrn2_decode_step_gate(B, H, D, D, code, _ptr(q), _ptr(v), _ptr(z), _ptr(lower_bound),
                                        _ptr(state), _ptr(y), _stream())
     _check(st, "hgrn2_decode_step_gate")
@@ -593,8 +590,6 @@ def fwd_scalar(q, k, v, log_a, h0=None, *, chunk=64, want_ht=True, want_states=F
     B, T, H, D = q.shape
     dt = q.dtype
     odt, code = _odt(dt, out_dtype)
-    if dt not in _DT:
-        raise ValueError("dtype must be float32 or bfloat16")
     for n, t in (("q", q), ("k", k), ("v", v)):
         _tok(n, t, B, T, H, D, dt)
     _tok3("log_a", log_a, B, T, H, dt)
@@ -669,10 +664,16 @@ def decode_step_scalar(q, k, v, log_a, state, *, y=None, out_dtype=None):
     _st("state", state, B, H, D)
     if y is None:
         y = torch.empty_like(q, dtype=odt)
+    _vec3("y", y, B, H, D, odt)
     st = _lib().hgrn2_decode_step_scalar(B, H, D, D, code, _ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(state),
                                          _ptr(y), _stream())
     _check(st, "hgrn2_decode_step_scalar")
     return y
+
+
+def _vec3(name, t, B, H, D, dtype):
+    if t.shape != (B, H, D) or t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+        raise ValueError("%s: expected a contiguous %s CUDA tensor of shape %s" % (name, dtype, (B, H, D)))
 
 
 def _tok3(name, t, B, T, C, dtype):
@@ -698,8 +699,6 @@ def hgrn1_fwd(q, k, v, log_f, h0=None, *, tied=False, want_ht=True, want_states=
     B, T, C = q.shape
     dt = q.dtype
     odt, code = _odt(dt, out_dtype)
-    if dt not in _DT:
-        raise ValueError("dtype must be float32 or bfloat16")
     for n, t in (("q", q), ("v", v), ("log_f", log_f)) + ((("k", k),) if not tied else ()):
         _tok3(n, t, B, T, C, dt)
     _vec("h0", h0, B, C)
@@ -710,11 +709,16 @@ def hgrn1_fwd(q, k, v, log_f, h0=None, *, tied=False, want_ht=True, want_states=
     _vec("hT", ht, B, C)
     if want_states and states is None:
         states = torch.empty(hgrn1_states_shape(B, T, C), dtype=torch.float32, device=q.device)
+    if states is not None and (tuple(states.shape) != hgrn1_states_shape(B, T, C) or states.dtype != torch.float32
+                               or not states.is_cuda or not states.is_contiguous()):
+        raise ValueError("states: expected a contiguous float32 CUDA tensor of shape %s"
+                         % (hgrn1_states_shape(B, T, C),))
     need = int(_lib().hgrn1_fwd_workspace_bytes(B, T, C, int(states is not None)))
     if ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     st = _lib().hgrn1_fwd(B, T, C, code, int(tied), _ptr(q), None if tied else _ptr(k), _ptr(v), _ptr(log_f),
-                          _ptr(h0), _ptr(y), _ptr(ht), _ptr(states), _ptr(ws), ws.numel(), _stream())
+                          _ptr(h0), _ptr(y), _ptr(ht), _ptr(states), _ptr(ws), ws.numel() * ws.element_size(),
+                          _stream())
     _check(st, "hgrn1_fwd")
     return y, ht, states
 
@@ -748,7 +752,7 @@ def hgrn1_bwd(q, k, v, log_f, dy, h0=None, dht=None, states=None, *, tied=False,
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     st = _lib().hgrn1_bwd(B, T, C, code, int(tied), _ptr(q), None if tied else _ptr(k), _ptr(v), _ptr(log_f),
                           _ptr(h0), _ptr(states), _ptr(dy), _ptr(dht), _ptr(dq), None if tied else _ptr(dk),
-                          _ptr(dv), _ptr(dlog_f), _ptr(dh0), _ptr(ws), ws.numel(), _stream())
+                          _ptr(dv), _ptr(dlog_f), _ptr(dh0), _ptr(ws), ws.numel() * ws.element_size(), _stream())
     _check(st, "hgrn1_bwd")
     return dq, (None if tied else dk), dv, dlog_f, dh0
 

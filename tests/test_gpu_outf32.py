@@ -212,6 +212,12 @@ def test_out_f32_decode(gm, D):
             y = m.decode_step_scalar(x["q"], x["k"], x["v"], x["log_a"], s, out_dtype=od)
         outs[od] = (y, s)
     torch.cuda.synchronize()
+    # an output of the wrong dtype or shape is refused before anything runs
+    with pytest.raises(ValueError):
+        m.decode_step(x["q"], x["k"], x["v"], x["log_f"], s0.clone(), out_dtype=torch.float32,
+                      y=torch.empty_like(x["q"]))
+    with pytest.raises(ValueError):
+        m.decode_step(x["q"], x["k"], x["v"], x["log_f"], s0.clone(), y=torch.empty_like(x["q"])[:, :1])
     (y32, s32), (y16, s16) = outs[torch.float32], outs[None]
     assert torch.equal(s32, s16)
     _same_after_rounding("y", y32, y16)
