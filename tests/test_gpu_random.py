@@ -1,0 +1,130 @@
+"""Randomised GPU parity: cases drawn from a fixed master seed, each a random
+gate mode (untied, tied, gate from z, one decay per head), dtype, head size,
+chunk size, ragged length (shorter than one chunk up to several chunks),
+batch and head counts, decay regime, with or without an initial state and a
+final-state gradient, with saved or recomputed boundary states, through the
+segmented or the stored-state forward, and (bfloat16) with bfloat16 or
+float32 outputs.  Every output is compared with the float64 oracle by the
+metrics of tests/gpu_util.py against the dtype's tolerance.
+
+HGRN2_RANDOM_CASES sets the number of cases (default 24); the cases are the
+same on every run."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import TOL, errors, fmt, to_dev, to_host64, worst
+
+pytestmark = pytest.mark.gpu
+
+MASTER_SEED = 20241
+N_CASES = int(os.environ.get("HGRN2_RANDOM_CASES", "24"))
+
+
+def _draw(i):
+    r = np.random.default_rng(MASTER_SEED + 7919 * i)
+    c = dict(gm=str(r.choice(["untied", "tied", "gate", "scalar"])), dtype=str(r.choice(["bf16", "f32"])),
+             D=int(r.choice([16, 32, 64, 128])), C=int(r.choice([16, 32, 64, 128])),
+             B=int(r.integers(1, 4)), H=int(r.integers(1, 4)), lam=float(r.choice([0.0, 0.3, 0.6, 0.9, 0.97])),
+             h0=bool(r.integers(0, 2)), dht=bool(r.integers(0, 2)), saved=bool(r.integers(0, 2)),
+             out32=bool(r.integers(0, 2)), seed=int(r.integers(1, 1 << 30)))
+    c["T"] = int(r.integers(1, 4 * c["C"] + 38))
+    return c
+
+
+def _label(c):
+    return "%s %s D%d C%d B%d H%d T%d lam%.2f%s%s%s%s" % (
+        c["gm"], c["dtype"], c["D"], c["C"], c["B"], c["H"], c["T"], c["lam"], " h0" if c["h0"] else "",
+        " dht" if c["dht"] else "", " saved" if c["saved"] else " recomputed",
+        " out-f32" if c["out32"] and c["dtype"] == "bf16" else "")
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_case(i):
+    import torch
+    import linear_attention_hgrn2_amd as m
+    c = _draw(i)
+    dt, D, C, gm = c["dtype"], c["D"], c["C"], c["gm"]
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    if not m.supported(D, C, tdt):
+        pytest.skip("no kernel for D %d, chunk %d, %s" % (D, C, dt))
+    print("case %d: %s" % (i, _label(c)), flush=True)
+    w = synth.Workload("random", B=c["B"], H=c["H"], T=c["T"], D=D, chunk=0, dtype=dt, lam=c["lam"], qscale=1.0,
+                       h0std=0.5 if c["h0"] else 0.0, train=True, seed=c["seed"])
+    d = synth.generate(w)
+    lb = synth.lower_bounds(c["H"], D, c["lam"], 0.2, seed=c["seed"] + 1)
+    la = np.ascontiguousarray(d["log_f"][..., 0])
+    rr = np.random.default_rng(c["seed"] + 2)
+    dht = (rr.standard_normal((c["B"], c["H"], D, D)) * 0.5).astype(np.float32) if c["dht"] else None
+    x = {n: to_dev(d[n], dt) for n in ("q", "k", "v", "log_f", "z", "dy")}
+    x["la"] = to_dev(la, dt)
+    lbd, h0, dhtd = to_dev(lb, "f32"), to_dev(d["h0"], "f32"), to_dev(dht, "f32")
+    od = torch.float32 if (c["out32"] and dt == "bf16") else None
+    kw = dict(chunk=C, out_dtype=od)
+
+    def fwd(want_states):
+        if gm == "untied":
+            return m.fwd(x["q"], x["k"], x["v"], x["log_f"], h0, want_states=want_states, **kw)
+        if gm == "tied":
+            return m.fwd_tied(x["q"], x["v"], x["log_f"], h0, want_states=want_states, **kw)
+        if gm == "gate":
+            return m.fwd_gate(x["q"], x["v"], x["z"], lbd, h0, want_states=want_states, **kw)
+        return m.fwd_scalar(x["q"], x["k"], x["v"], x["la"], h0, want_states=want_states, **kw)
+
+    y, ht, _ = fwd(False)             # no states kept: the segmented forward where it exists
+    _, _, st = fwd(True)
+    st = st if c["saved"] else None
+    if gm == "untied":
+        g = m.bwd(x["q"], x["k"], x["v"], x["log_f"], x["dy"], h0, dhtd, st, **kw)
+        got = dict(dq=g[0], dk=g[1], dv=g[2], dlog_f=g[3], dh0=g[4])
+    elif gm == "tied":
+        g = m.bwd_tied(x["q"], x["v"], x["log_f"], x["dy"], h0, dhtd, st, **kw)
+        got = dict(dq=g[0], dv=g[1], dlog_f=g[2], dh0=g[3])
+    elif gm == "gate":
+        g = m.bwd_gate(x["q"], x["v"], x["z"], lbd, x["dy"], h0, dhtd, st, **kw)
+        got = dict(dq=g[0], dv=g[1], dz=g[2], dlb=g[3], dh0=g[4])
+    else:
+        g = m.bwd_scalar(x["q"], x["k"], x["v"], x["la"], x["dy"], h0, dhtd, st, **kw)
+        got = dict(dq=g[0], dk=g[1], dv=g[2], dlog_a=g[3], dh0=g[4])
+    torch.cuda.synchronize()
+
+    f = {n: synth.to_f64(d[n], dt) for n in ("q", "k", "v", "log_f", "z", "dy")}
+    f["la"] = synth.to_f64(la, dt)
+    h064 = None if d["h0"] is None else d["h0"].astype(np.float64)
+    dht64 = None if dht is None else dht.astype(np.float64)
+    lb64 = lb.astype(np.float64)
+    if gm == "untied":
+        yr, htr = oracle.forward(f["q"], f["k"], f["v"], f["log_f"], h064)
+        gr = oracle.backward(f["q"], f["k"], f["v"], f["log_f"], f["dy"], h064, dht64)
+        ref = dict(dq=gr[0], dk=gr[1], dv=gr[2], dlog_f=gr[3], dh0=gr[4])
+    elif gm == "tied":
+        yr, htr = oracle.forward_tied(f["q"], f["v"], f["log_f"], h064)
+        gr = oracle.backward_tied(f["q"], f["v"], f["log_f"], f["dy"], h064, dht64)
+        ref = dict(dq=gr[0], dv=gr[1], dlog_f=gr[2], dh0=gr[3])
+    elif gm == "gate":
+        yr, htr = oracle.forward_gate(f["q"], f["v"], f["z"], lb64, h064)
+        gr = oracle.backward_gate(f["q"], f["v"], f["z"], lb64, f["dy"], h064, dht64)
+        ref = dict(dq=gr[0], dv=gr[1], dz=gr[2], dlb=gr[3], dh0=gr[4])
+    else:
+        yr, htr = oracle.forward_scalar(f["q"], f["k"], f["v"], f["la"], h064)
+        gr = oracle.backward_scalar(f["q"], f["k"], f["v"], f["la"], f["dy"], h064, dht64)
+        ref = dict(dq=gr[0], dk=gr[1], dv=gr[2], dlog_a=gr[3], dh0=gr[4])
+
+    def err(name, a, r):
+        a, r = to_host64(a), np.asarray(r, np.float64)
+        if name in ("ht", "dh0"):
+            return errors(a, r, "state")
+        if name == "dlb":
+            return errors(a[None, :, :, None], r[None, :, :, None], "state")
+        if name == "dlog_a":
+            return errors(a[..., None], r[..., None], "token")
+        return errors(a, r, "token")
+
+    errs = {"y": err("y", y, yr), "ht": err("ht", ht, htr)}
+    errs.update({n: err(n, got[n], ref[n]) for n in ref})
+    print("  " + "; ".join("%s %s" % (n, fmt(e)) for n, e in errs.items()), flush=True)
+    for n, e in errs.items():
+        assert worst(e) <= TOL[dt], (i, _label(c), n, fmt(e))
