@@ -332,16 +332,22 @@ def bench_hgrn1(torch, m, args, sets):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    timer = KernelTimer(torch)
+    # the step time with nothing between the launches, then the per-call times
+    # from a second pass with events around each call
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record()
     for i in range(args.steps):
-        step(i, timer)
+        step(i)
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
+    timer = KernelTimer(torch)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, timer)
+    torch.cuda.synchronize()
     kms = {label: timer.mean_ms(label) for label in labels}
     log("timed (hgrn1): %.3f ms/step (%s)" % (ms, ", ".join("%s %.3f ms" % kv for kv in kms.items())))
     alg = hgrn1_algorithmic_bytes(B, T, C)
@@ -432,8 +438,24 @@ def bench_train(torch, m, args, sets, mode="untied"):
         step(i)
     torch.cuda.synchronize()
     log("warmup done (%s)" % mode)
-    # timed region: exactly `steps` steps, bracketed by synchronisation; the
-    # events around each launch are recorded on the stream the kernels run on
+    # timed region: exactly `steps` steps, bracketed by synchronisation, with
+    # one event at each step boundary and nothing between a step's launches
+    # (the per-step times give the median and the minimum)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(args.steps):
+        step(i)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+    step_stats = {"mean": ms, "median": per[len(per) // 2] if len(per) % 2 else 0.5 * (per[len(per) // 2 - 1] +
+                                                                                    per[len(per) // 2]),
+                  "min": per[0], "n": args.steps}
+    # the same steps again with events around each launch (on the stream the
+    # kernels run on), for the per-kernel times; the events themselves sit
+    # between the launches, so this pass's step time is reported beside
     timer = KernelTimer(torch)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
@@ -443,10 +465,11 @@ def bench_train(torch, m, args, sets, mode="untied"):
         step(i, timer)
     t1.record()
     torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
+    ms_inst = t0.elapsed_time(t1) / args.steps
     kms = {label: timer.mean_ms(label) for label, _ in kernels}
     kstats = {label: timer.stats(label) for label, _ in kernels}
-    log("timed (%s): %.3f ms/step (%s)" % (mode, ms, ", ".join("%s %.3f ms" % kv for kv in kms.items())))
+    log("timed (%s): %.3f ms/step; with events around each launch %.3f ms/step (%s)"
+        % (mode, ms, ms_inst, ", ".join("%s %.3f ms" % kv for kv in kms.items())))
     out = None
     if mode == "untied":
         # after the timed region: one more step on the first input set, whose
@@ -455,7 +478,7 @@ def bench_train(torch, m, args, sets, mode="untied"):
         torch.cuda.synchronize()
         out = {"y": y.clone(), "dq": grads[0].clone(), "dk": grads[1].clone(), "dv": grads[2].clone(),
                "dlog_f": grads[3].clone()}
-    return dict(w=w, ms=ms, kernel_ms=kms, kernel_stats=kstats, step_stats=timer.stats("step"),
+    return dict(w=w, ms=ms, kernel_ms=kms, kernel_stats=kstats, step_stats=step_stats, ms_instrumented=ms_inst,
                 host=sets[0]["host"], out=out)
 
 
@@ -849,6 +872,7 @@ def main():
         out["value"] = tokens / (res["ms"] * 1e-3)
         out["ms_per_step"] = res["ms"]
         out["ms_per_step_stats"] = res["step_stats"]
+        out["ms_per_step_with_kernel_events"] = res["ms_instrumented"]
         out["config"] = {"workload": "train_bf16: B8 H16 T4096 d128 chunk64 fwd(states)+bwd",
                          "global_batch": w.B, "seq_len": w.T, "heads": w.H, "head_dim": w.D,
                          "chunk": w.chunk, "parallelism": "none (1 GPU)"}
@@ -894,6 +918,7 @@ def main():
         out["tied"] = {"workload": "train_bf16 with tied gates (k = 1 - f): fwd(states)+bwd, total dlog_f",
                        "value": tokens / (tres["ms"] * 1e-3), "unit": "tokens/s", "ms_per_step": tres["ms"],
                        "ms_per_step_stats": tres["step_stats"],
+                       "ms_per_step_with_kernel_events": tres["ms_instrumented"],
                        "kernels": {label: {"kernel": kn, "ms": tk[label], "ms_stats": tres["kernel_stats"][label],
                                            "bytes": abi[label], "design_bytes": alg[label],
                                            "GBps": abi[label] / tk[label] / 1e6,
@@ -904,12 +929,14 @@ def main():
                                    "[H, D] (f = lb + (1 - lb) sigmoid(z), k = 1 - f): fwd(states)+bwd, dz and dlb",
                        "value": tokens / (gres["ms"] * 1e-3), "unit": "tokens/s", "ms_per_step": gres["ms"],
                        "ms_per_step_stats": gres["step_stats"],
+                       "ms_per_step_with_kernel_events": gres["ms_instrumented"],
                        "calls_ms": {label: gk[label] for label, _ in GATE_CALLS}}
         sk_ = sres["kernel_ms"]
         out["scalar"] = {"workload": "train_bf16 with one decay per head (log_a [B,T,H] = the first channel's "
                                      "log f): fwd(states)+bwd, dlog_a",
                          "value": tokens / (sres["ms"] * 1e-3), "unit": "tokens/s", "ms_per_step": sres["ms"],
                          "ms_per_step_stats": sres["step_stats"],
+                         "ms_per_step_with_kernel_events": sres["ms_instrumented"],
                          "calls_ms": {label: sk_[label] for label, _ in SCALAR_CALLS}}
         out["hgrn1"] = h1res
     if args.only in ("decode", "all"):
