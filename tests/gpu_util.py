@@ -16,7 +16,10 @@ A slice is one (b, h) sequence of a [B, T, H, D] tensor, one (b, h) matrix of
 a [B, H, D, D] state, or one (b, c) channel sequence of a [B, T, C] tensor.
 The row and element terms catch localised errors that a slice norm over
 hundreds of thousands of values would hide (one wrong token row of a 4096-token
-slice moves its norm by only about 1/64).
+slice moves its norm by only about 1/64).  Where a row holds a single value
+(the per-head dlog_a [B, T, H], a per-channel [H, D] or [B, C] quantity read
+as rows of one), the row term would be the element term with a factor 1, so
+the element term stands for it: it already checks every row.
 
 The element scale follows the magnitude of the element's own row because
 magnitudes, and the rounding noise that comes with them, vary along a
@@ -110,10 +113,11 @@ def errors(got: np.ndarray, ref: np.ndarray, layout: str = "token") -> dict:
     rr = np.sqrt((ref * ref).sum(axis=r_ax))
     nrows = ref.shape[s_ax[0]]
     rs = rn / np.sqrt(nrows)                         # rms row norm of the slice
-    row = float(np.max(re / _nz(rr + row_b(rs))))
     width = ref.shape[r_ax]
     scale = np.maximum(slice_b(rms), (rr / np.sqrt(width))[..., None])
-    return {"norm": norm, "row": row, **_elem(d, ref, scale)}
+    el = _elem(d, ref, scale)
+    row = el["elem"] if width == 1 else float(np.max(re / _nz(rr + row_b(rs))))
+    return {"norm": norm, "row": row, **el}
 
 
 def _elem(d, ref, scale):

@@ -74,3 +74,25 @@ def test_nonfinite_fails_and_zero_reference_is_absolute():
     z = np.zeros((1, 8, 1, 4))
     e = errors(z + 1e-9, z)
     assert worst(e) < 1e-8
+
+
+def test_one_value_rows_use_the_element_term():
+    """Rows of a single value (the per-head dlog_a [B, T, H], read as rows of
+    one): the row term is the element term.  A near-cancelling value off by
+    2.4% of its slice's rms (what bfloat16 operand rounding leaves on a sum
+    whose terms are hundreds of times the result) passes; a value off by 20%
+    of the slice rms fails; so does a lost token."""
+    r = _ref((3, 200, 3, 1)) * 20.0
+    rms = np.sqrt(np.mean(r[2, :, 0, 0] ** 2))
+    g = r.copy()
+    g[2, 1, 0, 0] = -0.88
+    r2 = r.copy()
+    r2[2, 1, 0, 0] = -0.88 + 0.024 * rms
+    e = errors(g, r2)
+    assert e["row"] == e["elem"] and worst(e) <= TOL["bf16"]
+    g = r.copy()
+    g[1, 5, 2, 0] += 0.2 * rms
+    assert worst(errors(g, r)) > TOL["bf16"]
+    g = r.copy()
+    g[0, 17, 1, 0] = 0.0
+    assert worst(errors(g, r)) > TOL["bf16"] or abs(r[0, 17, 1, 0]) < 0.06 * rms
