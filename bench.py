@@ -710,13 +710,21 @@ def summarize(trace_dir, fetch_dir, write_dir, mfma_dir=None):
         summarize_mfma(mfma_dir, {kernel_label(r["Name"]): float(r["AverageNs"]) for r in rows}, digest)
 
 
-def seg_plan(B, T, H, chunk, want_y=True, units=256):
+def seg_plan(B, T, H, chunk, want_y=True, units=512):
     """The segment plan hgrn2_fwd uses without stored states: P segments of G
-    chunks per (b, h), NSEG of them summarised (P - 1 when y is written)."""
+    chunks per (b, h), NSEG of them summarised (P - 1 when y is written), for
+    about `units` walking workgroups (512 for bf16 at d 128: two per compute
+    unit, unless that leaves segments of fewer than 8 chunks; then 256)."""
     BH, N = B * H, -(-T // chunk)
-    pt = min(N, max(1, -(-units // BH)))
-    G = -(-N // pt)
-    P = -(-N // G)
+
+    def plan(u):
+        pt = min(N, max(1, -(-u // BH)))
+        G = -(-N // pt)
+        return -(-N // G), G
+
+    P, G = plan(units)
+    if units > 256 and P > 1 and G < 8:
+        P, G = plan(256)
     return P, G, (P - 1 if want_y else P)
 
 

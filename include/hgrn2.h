@@ -133,8 +133,10 @@ size_t hgrn2_bwd_workspace_bytes(int B, int T, int H, int DK, int DV, int chunk,
  * hgrn2_fwd_chunk); with y = NULL only the scan runs.
  * With states_out = NULL (inference, where that path exists: see
  * hgrn2_fwd_workspace_bytes): no chunk-boundary state is stored.  Each
- * sequence is cut into P segments of G chunks, P = about 256 / (B*H) (at
- * least 1, at most the chunks), and up to three launches run: the end state
+ * sequence is cut into P segments of G chunks, P = about U / (B*H) (at
+ * least 1, at most the chunks; U = 512 for bf16 at D 128, whose segment walk
+ * runs two workgroups per compute unit, else 256), and up to three launches
+ * run: the end state
  * and total decay of each of the first P - 1 segments from a zero state (a
  * scan over the segment), their carry into the state entering every segment,
  * and the segments' outputs, each segment walked chunk by chunk with its state

@@ -149,23 +149,33 @@ size_t adjoint_bytes(int B, int T, int H, int DK, int DV, int chunk, int dtype) 
 
 
 // ---- the forward without stored chunk-boundary states (sfwd.h): each
-// sequence is cut into P segments of G chunks so that about kSegUnits
-// workgroups walk segments at once (one per compute unit); P - 1 segment
-// summaries (P when only the final state is wanted) are carried into the
-// state entering every segment.
-constexpr int kSegUnits = 256;
+// sequence is cut into P segments of G chunks so that about seg_units()
+// workgroups walk segments at once; P - 1 segment summaries (P when only the
+// final state is wanted) are carried into the state entering every segment.
+// The walk fits two workgroups per compute unit where it keeps its state in
+// the accumulators (bfloat16, d = 128, chunk 64), one elsewhere; gfx950 parts
+// have 256 compute units.  The second workgroup per unit pays for the extra
+// summaries only when each segment walks at least kSegMinG chunks.
+int seg_units(int dtype, int D, int chunk) { return (dtype == 1 && D == 128 && chunk == 64) ? 512 : 256; }
+constexpr long long kSegMinG = 8;
 
 struct SegPlan {
   int P, G, NSEG;
 };
 
-SegPlan seg_plan(int B, int T, int H, int chunk, bool want_y) {
+SegPlan seg_plan(int dtype, int D, int B, int T, int H, int chunk, bool want_y) {
   const long long BH = (long long)B * H, N = (T + (long long)chunk - 1) / chunk;
-  const long long Pt = std::min<long long>(N, std::max<long long>(1, (kSegUnits + BH - 1) / BH));
-  SegPlan sp;
-  sp.G = (int)((N + Pt - 1) / Pt);
-  sp.P = (int)((N + sp.G - 1) / sp.G);  // no empty segment
-  sp.NSEG = want_y ? sp.P - 1 : sp.P;
+  auto plan = [&](long long units) {
+    const long long Pt = std::min<long long>(N, std::max<long long>(1, (units + BH - 1) / BH));
+    SegPlan sp;
+    sp.G = (int)((N + Pt - 1) / Pt);
+    sp.P = (int)((N + sp.G - 1) / sp.G);  // no empty segment
+    sp.NSEG = want_y ? sp.P - 1 : sp.P;
+    return sp;
+  };
+  const long long units = seg_units(dtype, D, chunk);
+  SegPlan sp = plan(units);
+  if (units > 256 && sp.P > 1 && sp.G < kSegMinG) sp = plan(256);
   return sp;
 }
 
@@ -177,8 +187,8 @@ bool seg_exists(int dtype, int D, int chunk, int gm) {
 // workspace of the forward without stored states: the states entering the
 // segments [B,H,NSEG+1,D,D] and the segments' log decay totals [B,H,NSEG,D],
 // float32, sized for NSEG = P (the larger case)
-size_t seg_ws_bytes(int B, int T, int H, int D, int chunk, bool want_y) {
-  const SegPlan sp = seg_plan(B, T, H, chunk, want_y);
+size_t seg_ws_bytes(int dtype, int B, int T, int H, int D, int chunk, bool want_y) {
+  const SegPlan sp = seg_plan(dtype, D, B, T, H, chunk, want_y);
   const size_t BH = (size_t)B * H;
   return (BH * (sp.NSEG + 1) * D * D + BH * sp.NSEG * D) * sizeof(float);
 }
@@ -323,7 +333,8 @@ size_t hgrn2_fwd_workspace_bytes(int B, int T, int H, int DK, int DV, int chunk,
                                  int have_states) {
   if (have_states) return 0;
   if (B <= 0 || T <= 0 || H <= 0 || DK <= 0 || DV <= 0 || chunk <= 0 || !valid_dtype(dtype)) return 0;
-  if (DK == DV && seg_exists(in_dtype(dtype), DK, chunk, kUntied)) return seg_ws_bytes(B, T, H, DK, chunk, false);
+  if (DK == DV && seg_exists(in_dtype(dtype), DK, chunk, kUntied))
+    return seg_ws_bytes(in_dtype(dtype), B, T, H, DK, chunk, false);
   return hgrn2_states_bytes(B, T, H, DK, DV, chunk, dtype);
 }
 
@@ -379,8 +390,8 @@ static hgrn2_status fwd_impl(int gm, const char *fn, int B, int T, int H, int DK
   const size_t lbb = (size_t)H * DK * sizeof(float);
   if (!states_out && seg_exists(dtype, DK, chunk, gm)) {
     // no state is kept for a backward: walk segments, carrying the state on chip
-    const SegPlan sp = seg_plan(B, T, H, chunk, y != nullptr);
-    const size_t need = seg_ws_bytes(B, T, H, DK, chunk, false);
+    const SegPlan sp = seg_plan(dtype, DK, B, T, H, chunk, y != nullptr);
+    const size_t need = seg_ws_bytes(dtype, B, T, H, DK, chunk, false);
     if (sp.NSEG > 0 && (!ws || ws_bytes < need))
       return fail(HGRN2_ERR_WORKSPACE, "workspace smaller than hgrn2_fwd_workspace_bytes()");
     const Range ins[] = {{"q", q, tok},

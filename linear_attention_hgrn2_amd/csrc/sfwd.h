@@ -28,6 +28,17 @@
 //   S^T <- S^T Diag(e^Gamma) + v^T kh.
 // The state's copy in the input dtype in LDS feeds the next chunk's
 // inter-chunk product.
+//
+// bfloat16 at d = 128, chunk 64 (ACC): the state stays in the accumulators
+// as S itself, wave wv holding columns 16 wv .. 16 wv + 15 for every row.  An
+// accumulator tile is then already a 16-deep operand along the rows of S, so
+// the inter-chunk product reads it from registers (rows scaled by e^{P_w})
+// and no copy of S goes through LDS.  Each wave then writes y's column tile wv
+// for all four token blocks, staged in the (dead) ko tile for full-row stores.
+// Without the copy and the e^{-L} table the tiles fit in 80 KB, so two
+// workgroups share a compute unit and hide each other's barriers and latency
+// (at 128 registers per lane: lane-dependent values are derived anew in the
+// walk so that the compiler does not keep their addresses live).
 #pragma once
 
 #include <algorithm>
@@ -62,19 +73,26 @@ template <typename T, int D, int C> struct SfwdCfg {
   static constexpr int NTILE = JB * CB, TPW = (NTILE + NWV - 1) / NWV;  // state tiles per wave
   static constexpr int LD = RowTile<T, D>::LD;
   static_assert(D >= 32 && HC >= 1, "two column halves of at least one tile");
+  // the state in the accumulators as S (two workgroups per compute unit)
+  static constexpr bool ACC = std::is_same<T, bf16_t>::value && D == 128 && C == 64;
+  // v and kh are read only by transposing reads (8 rows of 32 bytes per
+  // instruction), which a 32-byte row padding keeps free of bank conflicts;
+  // ACC has the LDS for it
+  static constexpr int PV = ACC ? 32 : 16;
+  static constexpr int LDV = RowTile<T, D, PV>::LD;
   using Sc = PFrag4<T>;  // one lane's piece of a score tile as a 16-deep operand
   struct Smem {
     T qo[C * LD];  // RowTile<T, D>; after the products, each wave's y staging
-    T ko[C * LD];
-    T kh[C * LD];  // k e^{Gamma - b_t}: the state update's operand
-    T v[C * LD];
-    T S[D * LD];   // copy of the state entering the chunk, row c, column j
-    Sc sc[NPAIR][64];
-    float eL[NB][D];  // e^{L_w}, each block's decay
-    float eLd[NB][D]; // e^{-L_w}, at most e^{80}
-    float eP[NB][D];  // e^{P_w}
-    float eG[D];      // e^{Gamma}
-    int wide[NB];     // block w's diagonal is summed directly
+    T ko[C * LD];  // ACC: after the scores, y's staging
+    T kh[C * LDV];  // k e^{Gamma - b_t}: the state update's operand
+    T v[C * LDV];
+    alignas(16) T S[ACC ? 8 : D * LD];  // copy of the state entering the chunk, row c, column j (not with ACC)
+    alignas(16) Sc sc[NPAIR][64];
+    alignas(16) float eL[NB][D];        // e^{L_w}, each block's decay
+    alignas(16) float eLd[ACC ? 1 : NB][ACC ? 4 : D];  // e^{-L_w}, at most e^{80} (ACC: 1 / e^{L_w})
+    alignas(16) float eP[NB][D];        // e^{P_w}
+    alignas(16) float eG[D];            // e^{Gamma}
+    int wide[NB];                       // block w's diagonal is summed directly
   };
 };
 
@@ -83,12 +101,17 @@ __device__ __forceinline__ int sfwd_pair_i(int p) { return p >= 6 ? 3 : p >= 3 ?
 
 // TO: the element type of y (T, or float32 for bfloat16 inputs)
 template <typename T, int D, int C, int GM, typename TO = T>
-__global__ __launch_bounds__((SfwdCfg<T, D, C>::NT)) void hgrn2_seg_fwd_kernel(SegFwdArgs a) {
+__global__ __launch_bounds__((SfwdCfg<T, D, C>::NT))
+__attribute__((amdgpu_waves_per_eu(SfwdCfg<T, D, C>::ACC ? 4 : 1))) void hgrn2_seg_fwd_kernel(SegFwdArgs a) {
   using Cfg = SfwdCfg<T, D, C>;
   constexpr int NB = Cfg::NB, NWV = Cfg::NWV, NT = Cfg::NT, CPL = Cfg::CPL, JB = Cfg::JB, KSD = Cfg::KSD,
                 HC = Cfg::HC, EPV = Cfg::EPV, TPW = Cfg::TPW, NPAIR = Cfg::NPAIR;
+  constexpr bool ACC = Cfg::ACC;
+  static_assert(!ACC || (TPW == 8 && NWV == 8 && NB == 4), "ACC: eight 16-row tiles of one column tile per wave");
   static_assert(NB == 4, "the pair decoding assumes four sub-blocks");
   using XT = RowTile<T, D>;
+  constexpr int PV = Cfg::PV;
+  using VT = RowTile<T, D, PV>;  // v and kh
   __shared__ typename Cfg::Smem sm;
 
   const int N = a.N, T_ = a.T, H = a.H, P = a.P;
@@ -112,12 +135,19 @@ __global__ __launch_bounds__((SfwdCfg<T, D, C>::NT)) void hgrn2_seg_fwd_kernel(S
   // ---- the state entering the segment: S^T tiles q = wv + NWV i in float32 accumulators
   const size_t SS = (size_t)D * D;
   const float *s0 = P == 1 ? (a.h0 ? a.h0 + (size_t)bh * SS : nullptr) : a.sin + ((size_t)bh * P + p) * SS;
+  // (ACC: S tiles i = rows 16 i + 4 g + r, column 16 wv + n)
   f32x4_t S[TPW];
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
     const int q = wv + NWV * i, jb = q % JB, cb = q / JB;
     const int c = 16 * cb + n16, j = 16 * jb + 4 * g;
-    if (q < Cfg::NTILE && s0) {
+    if constexpr (ACC) {
+      acc_zero(S[i]);
+      if (s0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[i][r] = s0[(size_t)(16 * i + 4 * g + r) * D + 16 * wv + n16];
+      }
+    } else if (q < Cfg::NTILE && s0) {
       const float4 x = *(const float4 *)(s0 + (size_t)c * D + j);
       S[i] = f32x4_t{x.x, x.y, x.z, x.w};
     } else {
@@ -126,14 +156,16 @@ __global__ __launch_bounds__((SfwdCfg<T, D, C>::NT)) void hgrn2_seg_fwd_kernel(S
   }
   // its copy as a matrix-core operand, row c, columns j..j+3
   auto stage_state = [&]() {
+    if constexpr (!ACC) {
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int q = wv + NWV * i, jb = q % JB, cb = q / JB;
-      if (q < Cfg::NTILE) {
-        Pack<T, 4> pk;
+      for (int i = 0; i < TPW; ++i) {
+        const int q = wv + NWV * i, jb = q % JB, cb = q / JB;
+        if (q < Cfg::NTILE) {
+          Pack<T, 4> pk;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pk.v[r] = from_f32<T>(S[i][r]);
-        *(Pack<T, 4> *)&sm.S[XT::at(16 * cb + n16, 16 * jb + 4 * g)] = pk;
+          for (int r = 0; r < 4; ++r) pk.v[r] = from_f32<T>(S[i][r]);
+          *(Pack<T, 4> *)&sm.S[XT::at(16 * cb + n16, 16 * jb + 4 * g)] = pk;
+        }
       }
     }
   };
@@ -149,6 +181,11 @@ __global__ __launch_bounds__((SfwdCfg<T, D, C>::NT)) void hgrn2_seg_fwd_kernel(S
     T la;  // kScalar: log a of token 16 w + (lane & 15)
   };
   auto load = [&](Regs &r, int n) {
+    // lane-dependent values derived anew, so that the addresses built from
+    // them are not hoisted out of the walk and kept live in registers
+    const int tid = opaque((int)threadIdx.x), lane = tid & 63;
+    const int c0 = (has_ch ? lane : 0) * CPL;
+    const uint32_t c0b = (uint32_t)c0 * sizeof(T);
     const int t0 = n * C, len = min(C, T_ - t0);
     const size_t cbase = (((size_t)b * T_ + t0) * H + h) * D * sizeof(T);
     const uint32_t rows = (uint32_t)len * HDB;
@@ -178,12 +215,16 @@ __global__ __launch_bounds__((SfwdCfg<T, D, C>::NT)) void hgrn2_seg_fwd_kernel(S
   load(rg, n0);
   for (int n = n0; n < n1; ++n) {
     const int t0 = n * C, len = min(C, T_ - t0);
+    // (as in load: lane-dependent values derived anew each chunk)
+    const int tid = opaque((int)threadIdx.x), lane = tid & 63, n16 = lane & 15, g = lane >> 4;
+    const int c0 = (has_ch ? lane : 0) * CPL;
+    const uint32_t c0b = (uint32_t)c0 * sizeof(T);
     // ---- P0: v tile; block w's prefix (in both of its waves); qo, ko of this wave's tokens
 #pragma unroll
     for (int i = 0; i < Cfg::NVV; ++i) {
       const int idx = tid + i * NT;
       const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
-      if (idx < Cfg::VV) *(uint4 *)&sm.v[XT::at(row, col)] = rg.v[i];
+      if (idx < Cfg::VV) *(uint4 *)&sm.v[VT::at(row, col)] = rg.v[i];
     }
     float kof[8][CPL];  // this wave's tokens: ko in float32, k e^{L_w - ell}
     {
@@ -191,20 +232,25 @@ __global__ __launch_bounds__((SfwdCfg<T, D, C>::NT)) void hgrn2_seg_fwd_kernel(S
 #pragma unroll
       for (int e = 0; e < CPL; ++e) run[e] = 0.f;
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const int tt = 16 * w + t;
+      for (int half = 0; half < 2; ++half) {
+        const bool own = half == hh;  // wave-uniform
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) {
-          const T lx = GM == kScalar ? readlane(rg.la, t) : rg.l[t].v[e];
-          float lf, kv;
-          // k of this wave's own tokens (loaded, or formed with log f); the
-          // other half's tokens only add their log f to the prefix
-          const T kx = reads_k(GM) ? rg.k[t & 7].v[e] : lx;
-          lf_k<GM>(kx, lx, lbv[e], tt < len, lf, kv);
-          run[e] += lf;
-          if ((t >> 3) == hh) {
-            ell[t & 7][e] = run[e];
-            kf[t & 7][e] = kv;
+        for (int t8 = 0; t8 < 8; ++t8) {
+          const int t = 8 * half + t8, tt = 16 * w + t;
+#pragma unroll
+          for (int e = 0; e < CPL; ++e) {
+            const T lx = GM == kScalar ? readlane(rg.la, t) : rg.l[t].v[e];
+            float lf;
+            if (own) {
+              // k of this wave's own tokens (loaded, or formed with log f)
+              const T kx = reads_k(GM) ? rg.k[t8].v[e] : lx;
+              lf_k<GM>(kx, lx, lbv[e], tt < len, lf, kf[t8][e]);
+            } else {
+              // the other half's tokens only add their log f to the prefix
+              lf = lf_of<GM>(to_f32(lx), lbv[e], tt < len);
+            }
+            run[e] += lf;
+            if (own) ell[t8][e] = run[e];
           }
         }
       }
@@ -232,7 +278,7 @@ __global__ __launch_bounds__((SfwdCfg<T, D, C>::NT)) void hgrn2_seg_fwd_kernel(S
 #pragma unroll
           for (int e = 0; e < CPL; ++e) {
             sm.eL[w][c0 + e] = __expf(run[e]);
-            sm.eLd[w][c0 + e] = __expf(fminf(-run[e], 80.f));
+            if constexpr (!ACC) sm.eLd[w][c0 + e] = __expf(fminf(-run[e], 80.f));
           }
         }
       }
@@ -244,21 +290,28 @@ __global__ __launch_bounds__((SfwdCfg<T, D, C>::NT)) void hgrn2_seg_fwd_kernel(S
 
     // ---- P1: kh of this wave's tokens, e^{P_w}, e^{Gamma}; the score tiles
     if (has_ch) {
+      float ea[CPL];  // e^{Gamma - P_{w+1}}
 #pragma unroll
       for (int e = 0; e < CPL; ++e) {
         const int c = c0 + e;
-        float eb = 1.f, ea = 1.f, eg = 1.f;  // e^{P_w}, e^{Gamma - P_{w+1}}, e^{Gamma}
+        float eb = 1.f, eg = 1.f;  // e^{P_w}, e^{Gamma}
+        ea[e] = 1.f;
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
           const float x = sm.eL[i][c];
           eb *= (i < w) ? x : 1.f;
-          ea *= (i > w) ? x : 1.f;
+          ea[e] *= (i > w) ? x : 1.f;
           eg *= x;
         }
         if (hh == 0) sm.eP[w][c] = eb;
         if (wv == 0) sm.eG[c] = eg;
+      }
 #pragma unroll
-        for (int t = 0; t < 8; ++t) sm.kh[XT::at(16 * w + 8 * hh + t, c)] = from_f32<T>(kof[t][e] * ea);
+      for (int t = 0; t < 8; ++t) {
+        Pack<T, CPL> o;
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) o.v[e] = from_f32<T>(kof[t][e] * ea[e]);
+        stpack<T, CPL>(&sm.kh[VT::at(16 * w + 8 * hh + t, c0)], o);
       }
     }
     // score tile tau = wv + NWV s of pair (i, j), i >= j: X[s][t] = sum_c ko_s gap_c qo_t
@@ -327,7 +380,14 @@ __global__ __launch_bounds__((SfwdCfg<T, D, C>::NT)) void hgrn2_seg_fwd_kernel(S
           for (int e = 0; e < 8; e += 4) {
             float4 x;
             if (i == j) {
-              x = ldf4(&sm.eLd[i][c + e]);
+              if constexpr (ACC) {
+                // e^{-L_i}: not wide, so e^{L_i} >= e^{-64}
+                x = ldf4(&sm.eL[i][c + e]);
+                x = make_float4(__builtin_amdgcn_rcpf(x.x), __builtin_amdgcn_rcpf(x.y), __builtin_amdgcn_rcpf(x.z),
+                                __builtin_amdgcn_rcpf(x.w));
+              } else {
+                x = ldf4(&sm.eLd[i][c + e]);
+              }
             } else {
               x = make_float4(1.f, 1.f, 1.f, 1.f);
 #pragma unroll
@@ -354,91 +414,180 @@ __global__ __launch_bounds__((SfwdCfg<T, D, C>::NT)) void hgrn2_seg_fwd_kernel(S
     }
     __syncthreads();  // B2: score tiles, kh, e^{P}, e^{Gamma}
 
-    // ---- P2: y of block w, column half hh: the scores' product with v, plus (qo e^{P_w}) S
-    f32x4_t Y[HC];
+    if constexpr (ACC) {
+      // ---- P2: y of all four token blocks for column tile wv: the scores'
+      // product with v, plus (qo e^{P_w}) S from the accumulators
+      f32x4_t Y[NB];
 #pragma unroll
-    for (int cb = 0; cb < HC; ++cb) acc_zero(Y[cb]);
+      for (int w2 = 0; w2 < NB; ++w2) acc_zero(Y[w2]);
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      if (j > w) continue;  // wave-uniform
-      const PFrag4<T> fa = sm.sc[w * (w + 1) / 2 + j][lane];
+      for (int j = 0; j < NB; ++j) {
+        const PFrag4<T> fv = tr4<D, PV>(sm.v, 16 * j, 16 * wv);
 #pragma unroll
-      for (int cb = 0; cb < HC; ++cb) mma16(Y[cb], fa, tr4<D>(sm.v, 16 * j, (D / 2) * hh + 16 * cb));
-    }
+        for (int w2 = j; w2 < NB; ++w2) mma16(Y[w2], sm.sc[w2 * (w2 + 1) / 2 + j][lane], fv);
+      }
+      // k slots of pair p: 0-3 <-> rows 32 p + 4 g + r (tile 2 p), 4-7 <-> rows
+      // 32 p + 16 + 4 g + r (tile 2 p + 1), the same in both operands
 #pragma unroll
-    for (int ks = 0; ks < KSD; ++ks) {
-      const int c = 32 * ks + 8 * g;
-      float qv[8];
-      unpack8(row8<D>(sm.qo, 16 * w + n16, c), qv);
-      const float4 e0 = ldf4(&sm.eP[w][c]), e1 = ldf4(&sm.eP[w][c + 4]);
-      Frag f;
-      f.v[0] = qv[0] * e0.x; f.v[1] = qv[1] * e0.y; f.v[2] = qv[2] * e0.z; f.v[3] = qv[3] * e0.w;
-      f.v[4] = qv[4] * e1.x; f.v[5] = qv[5] * e1.y; f.v[6] = qv[6] * e1.z; f.v[7] = qv[7] * e1.w;
-      const PFrag<T> qb = to_pfrag<T>(f);
+      for (int w2 = 0; w2 < NB; ++w2) {
 #pragma unroll
-      for (int cb = 0; cb < HC; ++cb) mma(Y[cb], qb, tr8<D>(sm.S, 32 * ks, (D / 2) * hh + 16 * cb));
-    }
-    __syncthreads();  // B3: every wave is done with qo, the scores and the state's copy
+        for (int pp = 0; pp < TPW / 2; ++pp) {
+          Frag f;
+          if (w2 == 0) {  // e^{P_0} = 1
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              f.v[r] = S[2 * pp][r];
+              f.v[4 + r] = S[2 * pp + 1][r];
+            }
+          } else {
+            const float4 e0 = ldf4(&sm.eP[w2][32 * pp + 4 * g]), e1 = ldf4(&sm.eP[w2][32 * pp + 16 + 4 * g]);
+            f.v[0] = S[2 * pp][0] * e0.x; f.v[1] = S[2 * pp][1] * e0.y;
+            f.v[2] = S[2 * pp][2] * e0.z; f.v[3] = S[2 * pp][3] * e0.w;
+            f.v[4] = S[2 * pp + 1][0] * e1.x; f.v[5] = S[2 * pp + 1][1] * e1.y;
+            f.v[6] = S[2 * pp + 1][2] * e1.z; f.v[7] = S[2 * pp + 1][3] * e1.w;
+          }
+          const PFrag<T> qa = ld4x2(&sm.qo[XT::at(16 * w2 + n16, 32 * pp + 4 * g)],
+                                    &sm.qo[XT::at(16 * w2 + n16, 32 * pp + 16 + 4 * g)]);
+          mma(Y[w2], qa, to_pfrag<T>(f));
+        }
+      }
+      // y out: float32 straight from the accumulators, else staged in the
+      // dead ko tile (rows 16 w2 + 4 g + r, column 16 wv + n)
+      if constexpr (!std::is_same<TO, T>::value) {
+        TO *gyo = (TO *)a.y + (((size_t)b * T_ + t0) * H + h) * D;
+#pragma unroll
+        for (int w2 = 0; w2 < NB; ++w2)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = 16 * w2 + 4 * g + r;
+            if (t < len) __builtin_nontemporal_store(Y[w2][r], gyo + ((size_t)t * H * D + 16 * wv + n16));
+          }
+      } else {
+#pragma unroll
+        for (int w2 = 0; w2 < NB; ++w2)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sm.ko[XT::at(16 * w2 + 4 * g + r, 16 * wv + n16)] = from_f32<T>(Y[w2][r]);
+      }
+      __syncthreads();  // B3: y staged
 
-    // ---- P3: y out (staged in this wave's half of block w's qo rows, or
-    // float32 straight from the accumulators); the state update
-    if constexpr (!std::is_same<TO, T>::value) {
-      TO *gyo = (TO *)a.y + (((size_t)b * T_ + t0) * H + h) * D;
+      // ---- P3: y's full rows out; the state update S <- Diag(e^Gamma) S + kh^T v
+      if constexpr (std::is_same<TO, T>::value) {
+        T *gy = (T *)a.y + (((size_t)b * T_ + t0) * H + h) * D;
+#pragma unroll
+        for (int i = 0; i < Cfg::NVV; ++i) {
+          const int idx = tid + i * NT;
+          const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
+          if (idx < Cfg::VV && row < len) {
+            const uint4 u = *(const uint4 *)&sm.ko[XT::at(row, col)];
+            __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, u), (u32x4_t *)(gy + ((size_t)row * H * D + col)));
+          }
+        }
+      }
+      const PFrag<T> fv0 = tr8<D, PV>(sm.v, 0, 16 * wv), fv1 = tr8<D, PV>(sm.v, 32, 16 * wv);
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        const float4 eg = ldf4(&sm.eG[16 * i + 4 * g]);
+        S[i][0] *= eg.x;
+        S[i][1] *= eg.y;
+        S[i][2] *= eg.z;
+        S[i][3] *= eg.w;
+        mma(S[i], tr8<D, PV>(sm.kh, 0, 16 * i), fv0);
+        mma(S[i], tr8<D, PV>(sm.kh, 32, 16 * i), fv1);
+      }
+    } else {
+      // ---- P2: y of block w, column half hh: the scores' product with v, plus (qo e^{P_w}) S
+      f32x4_t Y[HC];
+#pragma unroll
+      for (int cb = 0; cb < HC; ++cb) acc_zero(Y[cb]);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        if (j > w) continue;  // wave-uniform
+        const PFrag4<T> fa = sm.sc[w * (w + 1) / 2 + j][lane];
+#pragma unroll
+        for (int cb = 0; cb < HC; ++cb) mma16(Y[cb], fa, tr4<D, PV>(sm.v, 16 * j, (D / 2) * hh + 16 * cb));
+      }
+#pragma unroll
+      for (int ks = 0; ks < KSD; ++ks) {
+        const int c = 32 * ks + 8 * g;
+        float qv[8];
+        unpack8(row8<D>(sm.qo, 16 * w + n16, c), qv);
+        const float4 e0 = ldf4(&sm.eP[w][c]), e1 = ldf4(&sm.eP[w][c + 4]);
+        Frag f;
+        f.v[0] = qv[0] * e0.x; f.v[1] = qv[1] * e0.y; f.v[2] = qv[2] * e0.z; f.v[3] = qv[3] * e0.w;
+        f.v[4] = qv[4] * e1.x; f.v[5] = qv[5] * e1.y; f.v[6] = qv[6] * e1.z; f.v[7] = qv[7] * e1.w;
+        const PFrag<T> qb = to_pfrag<T>(f);
+#pragma unroll
+        for (int cb = 0; cb < HC; ++cb) mma(Y[cb], qb, tr8<D>(sm.S, 32 * ks, (D / 2) * hh + 16 * cb));
+      }
+      __syncthreads();  // B3: every wave is done with qo, the scores and the state's copy
+
+      // ---- P3: y out (staged in this wave's half of block w's qo rows, or
+      // float32 straight from the accumulators); the state update
+      if constexpr (!std::is_same<TO, T>::value) {
+        TO *gyo = (TO *)a.y + (((size_t)b * T_ + t0) * H + h) * D;
+#pragma unroll
+        for (int cb = 0; cb < HC; ++cb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = 16 * w + 4 * g + r;
+            if (t < len)
+              __builtin_nontemporal_store(Y[cb][r], gyo + ((size_t)t * H * D + (D / 2) * hh + 16 * cb + n16));
+          }
+      } else {
 #pragma unroll
       for (int cb = 0; cb < HC; ++cb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = 16 * w + 4 * g + r;
-          if (t < len)
-            __builtin_nontemporal_store(Y[cb][r], gyo + ((size_t)t * H * D + (D / 2) * hh + 16 * cb + n16));
-        }
-    } else {
+        for (int r = 0; r < 4; ++r)
+          sm.qo[XT::at(16 * w + 4 * g + r, (D / 2) * hh + 16 * cb + n16)] = from_f32<T>(Y[cb][r]);
+      wave_lds_sync();
+      {
+        T *gy = (T *)a.y + (((size_t)b * T_ + t0) * H + h) * D;
+        constexpr int RV = 16 * (D / 2) / EPV;  // 16-byte vectors in this wave's 16 half rows
 #pragma unroll
-    for (int cb = 0; cb < HC; ++cb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        sm.qo[XT::at(16 * w + 4 * g + r, (D / 2) * hh + 16 * cb + n16)] = from_f32<T>(Y[cb][r]);
-    wave_lds_sync();
-    {
-      T *gy = (T *)a.y + (((size_t)b * T_ + t0) * H + h) * D;
-      constexpr int RV = 16 * (D / 2) / EPV;  // 16-byte vectors in this wave's 16 half rows
-#pragma unroll
-      for (int i = 0; i < (RV + 63) / 64; ++i) {
-        const int idx = lane + 64 * i;
-        const int row = idx / (D / 2 / EPV), col = (D / 2) * hh + (idx % (D / 2 / EPV)) * EPV;
-        const int t = 16 * w + row;
-        if (idx < RV && t < len) {
-          const uint4 u = *(const uint4 *)&sm.qo[XT::at(t, col)];
-          __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, u), (u32x4_t *)(gy + ((size_t)t * H * D + col)));
+        for (int i = 0; i < (RV + 63) / 64; ++i) {
+          const int idx = lane + 64 * i;
+          const int row = idx / (D / 2 / EPV), col = (D / 2) * hh + (idx % (D / 2 / EPV)) * EPV;
+          const int t = 16 * w + row;
+          if (idx < RV && t < len) {
+            const uint4 u = *(const uint4 *)&sm.qo[XT::at(t, col)];
+            __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, u), (u32x4_t *)(gy + ((size_t)t * H * D + col)));
+          }
         }
       }
-    }
-    }
-    // S^T <- S^T Diag(e^Gamma) + v^T kh
-    // (NWV = 8 divides JB for D = 128: every tile of this wave has jb = wv, and
-    // the compiler keeps the two v operands across the tiles)
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int q = wv + NWV * i, jb = q % JB, cb = q / JB;
-      if (q < Cfg::NTILE) {
-        const float eg = sm.eG[16 * cb + n16];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) S[i][r] *= eg;
-#pragma unroll
-        for (int ks = 0; ks < C / 32; ++ks) mma(S[i], tr8<D>(sm.v, 32 * ks, 16 * jb), tr8<D>(sm.kh, 32 * ks, 16 * cb));
       }
+      // S^T <- S^T Diag(e^Gamma) + v^T kh
+      // (NWV = 8 divides JB for D = 128: every tile of this wave has jb = wv, and
+      // the compiler keeps the two v operands across the tiles)
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        const int q = wv + NWV * i, jb = q % JB, cb = q / JB;
+        if (q < Cfg::NTILE) {
+          const float eg = sm.eG[16 * cb + n16];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) S[i][r] *= eg;
+#pragma unroll
+          for (int ks = 0; ks < C / 32; ++ks) mma(S[i], tr8<D, PV>(sm.v, 32 * ks, 16 * jb), tr8<D, PV>(sm.kh, 32 * ks, 16 * cb));
+        }
+      }
+      stage_state();
     }
-    stage_state();
-    __syncthreads();  // B4: the new state's copy is in place; the tiles may be rewritten
+    __syncthreads();  // B4: the tiles may be rewritten (and the state's copy is in place)
   }
 
   if (p == P - 1 && a.ht) {
+    if constexpr (ACC) {
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int q = wv + NWV * i, jb = q % JB, cb = q / JB;
-      if (q < Cfg::NTILE) {
-        const int c = 16 * cb + n16, j = 16 * jb + 4 * g;
-        *(float4 *)(a.ht + (size_t)bh * SS + (size_t)c * D + j) = make_float4(S[i][0], S[i][1], S[i][2], S[i][3]);
+      for (int i = 0; i < TPW; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) a.ht[(size_t)bh * SS + (size_t)(16 * i + 4 * g + r) * D + 16 * wv + n16] = S[i][r];
+    } else {
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        const int q = wv + NWV * i, jb = q % JB, cb = q / JB;
+        if (q < Cfg::NTILE) {
+          const int c = 16 * cb + n16, j = 16 * jb + 4 * g;
+          *(float4 *)(a.ht + (size_t)bh * SS + (size_t)c * D + j) = make_float4(S[i][0], S[i][1], S[i][2], S[i][3]);
+        }
       }
     }
   }
@@ -466,9 +615,24 @@ __global__ __launch_bounds__(256) void hgrn2_seg_carry_kernel(int BH, int NSEG, 
     float cur = h0 ? h0[(size_t)bh * SS + e] : 0.f;
     float *base = sin + (size_t)bh * (NSEG + 1) * SS;
     base[e] = cur;
-    for (int p = 0; p < NSEG; ++p) {
-      cur = __expf(asum[((size_t)bh * NSEG + p) * D + c]) * cur + base[(size_t)(p + 1) * SS + e];
-      base[(size_t)(p + 1) * SS + e] = cur;
+    // eight segments at a time: their loads are issued together, so that the
+    // walk waits for one memory round trip per eight segments, not per segment
+    for (int p0 = 0; p0 < NSEG; p0 += 8) {
+      float loc[8], dec[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (p0 + i < NSEG) {
+          loc[i] = base[(size_t)(p0 + i + 1) * SS + e];
+          dec[i] = asum[((size_t)bh * NSEG + p0 + i) * D + c];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (p0 + i < NSEG) {
+          cur = __expf(dec[i]) * cur + loc[i];
+          base[(size_t)(p0 + i + 1) * SS + e] = cur;
+        }
+      }
     }
     if (ht) ht[(size_t)bh * SS + e] = cur;
   }

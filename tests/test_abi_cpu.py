@@ -57,11 +57,16 @@ def test_sizes(lib):
     assert lib.hgrn2_bwd_workspace_bytes(1, 100, 1, 16, 16, 16, 1, 1) == 7 * 16 * 16 * 2
     assert lib.hgrn2_fwd_workspace_bytes(1, 100, 1, 16, 16, 16, 0, 1) == 0
     assert lib.hgrn2_fwd_workspace_bytes(1, 100, 1, 16, 16, 16, 0, 0) == 8 * 16 * 16 * 4
-    # the forward without stored states (chunk 64, bf16, D 128): B1 H32 T32768 has 512 chunks, cut
-    # into P = 8 segments of 64 (256 workgroups); summaries of (P + 1) states and P decay vectors
-    assert lib.hgrn2_fwd_workspace_bytes(1, 32768, 32, 128, 128, 64, 1, 0) == 32 * (9 * 128 * 128 + 8 * 128) * 4
-    # B16 H16: P = 1
-    assert lib.hgrn2_fwd_workspace_bytes(16, 4096, 16, 128, 128, 64, 1, 0) == 256 * (2 * 128 * 128 + 128) * 4
+    # the forward without stored states (chunk 64, bf16, D 128, two walking workgroups per compute
+    # unit): B1 H32 T32768 has 512 chunks, cut into P = 16 segments of 32 (512 workgroups);
+    # summaries of (P + 1) states and P decay vectors
+    assert lib.hgrn2_fwd_workspace_bytes(1, 32768, 32, 128, 128, 64, 1, 0) == 32 * (17 * 128 * 128 + 16 * 128) * 4
+    # B4 H8 T2048: 512 workgroups would walk segments of 2 chunks, so 256 walk P = 8 segments of 4
+    assert lib.hgrn2_fwd_workspace_bytes(4, 2048, 8, 128, 128, 64, 1, 0) == 32 * (9 * 128 * 128 + 8 * 128) * 4
+    # B16 H16: P = 2
+    assert lib.hgrn2_fwd_workspace_bytes(16, 4096, 16, 128, 128, 64, 1, 0) == 256 * (3 * 128 * 128 + 2 * 128) * 4
+    # float32 at D 64 walks one workgroup per compute unit: P = 8 segments for 256 workgroups
+    assert lib.hgrn2_fwd_workspace_bytes(1, 32768, 32, 64, 64, 64, 0, 0) == 32 * (9 * 64 * 64 + 8 * 64) * 4
     assert lib.hgrn2_supported(128, 64, 1) == 1
     assert lib.hgrn2_supported(48, 64, 1) == 0
     assert lib.hgrn2_supported(128, 128, 1) == 1     # chunk 128, bf16
