@@ -161,6 +161,7 @@ constexpr long long kSegMinG = 8;
 
 struct SegPlan {
   int P, G, NSEG;
+  bool pair;  // planned for two walking workgroups per compute unit
 };
 
 SegPlan seg_plan(int dtype, int D, int B, int T, int H, int chunk, bool want_y) {
@@ -171,6 +172,7 @@ SegPlan seg_plan(int dtype, int D, int B, int T, int H, int chunk, bool want_y) 
     sp.G = (int)((N + Pt - 1) / Pt);
     sp.P = (int)((N + sp.G - 1) / sp.G);  // no empty segment
     sp.NSEG = want_y ? sp.P - 1 : sp.P;
+    sp.pair = units > 256 && BH * sp.P > 256;
     return sp;
   };
   const long long units = seg_units(dtype, D, chunk);
@@ -453,6 +455,7 @@ static hgrn2_status fwd_impl(int gm, const char *fn, int B, int T, int H, int DK
     fa.y = y;
     fa.ht = ht;
     fa.out_f32 = of32;
+    fa.pair = sp.pair ? 1 : 0;
     return hip_status(hgrn2::dispatch_seg_fwd(dtype, DK, chunk, gm, &fa, (hipStream_t)stream), fn);
   }
   const size_t stb = hgrn2_states_bytes(B, T, H, DK, DV, chunk, dtype);

@@ -29,7 +29,8 @@
 // The state's copy in the input dtype in LDS feeds the next chunk's
 // inter-chunk product.
 //
-// bfloat16 at d = 128, chunk 64 (ACC): the state stays in the accumulators
+// bfloat16 at d = 128, chunk 64, when two workgroups per compute unit walk
+// at once (PAIR, giving ACC): the state stays in the accumulators
 // as S itself, wave wv holding columns 16 wv .. 16 wv + 15 for every row.  An
 // accumulator tile is then already a 16-deep operand along the rows of S, so
 // the inter-chunk product reads it from registers (rows scaled by e^{P_w})
@@ -57,9 +58,10 @@ struct SegFwdArgs {
   void *y;                        // [B,T,H,D], the input dtype or (out_f32) float32
   float *ht;                      // [B,H,D,D] float32 final state, or null
   int out_f32 = 0;                // bfloat16 inputs: write y as float32
+  int pair = 0;                   // two workgroups per compute unit walk at once (the ACC layout, where it exists)
 };
 
-template <typename T, int D, int C> struct SfwdCfg {
+template <typename T, int D, int C, bool PAIR = false> struct SfwdCfg {
   static constexpr int NB = C / 16;             // 16-token sub-blocks
   static constexpr int NWV = 2 * NB, NT = 64 * NWV;
   static constexpr int CPL = D > 64 ? D / 64 : 1;
@@ -73,8 +75,8 @@ template <typename T, int D, int C> struct SfwdCfg {
   static constexpr int NTILE = JB * CB, TPW = (NTILE + NWV - 1) / NWV;  // state tiles per wave
   static constexpr int LD = RowTile<T, D>::LD;
   static_assert(D >= 32 && HC >= 1, "two column halves of at least one tile");
-  // the state in the accumulators as S (two workgroups per compute unit)
-  static constexpr bool ACC = std::is_same<T, bf16_t>::value && D == 128 && C == 64;
+  // the state in the accumulators as S, for two workgroups per compute unit
+  static constexpr bool ACC = PAIR && std::is_same<T, bf16_t>::value && D == 128 && C == 64;
   // v and kh are read only by transposing reads (8 rows of 32 bytes per
   // instruction), which a 32-byte row padding keeps free of bank conflicts;
   // ACC has the LDS for it
@@ -100,10 +102,12 @@ template <typename T, int D, int C> struct SfwdCfg {
 __device__ __forceinline__ int sfwd_pair_i(int p) { return p >= 6 ? 3 : p >= 3 ? 2 : p >= 1 ? 1 : 0; }
 
 // TO: the element type of y (T, or float32 for bfloat16 inputs)
-template <typename T, int D, int C, int GM, typename TO = T>
-__global__ __launch_bounds__((SfwdCfg<T, D, C>::NT))
-__attribute__((amdgpu_waves_per_eu(SfwdCfg<T, D, C>::ACC ? 4 : 1))) void hgrn2_seg_fwd_kernel(SegFwdArgs a) {
-  using Cfg = SfwdCfg<T, D, C>;
+// PAIR: the ACC layout (bfloat16, d = 128, chunk 64), two workgroups per
+// compute unit; otherwise one workgroup per compute unit, state copy in LDS
+template <typename T, int D, int C, int GM, typename TO = T, bool PAIR = false>
+__global__ __launch_bounds__((SfwdCfg<T, D, C, PAIR>::NT))
+__attribute__((amdgpu_waves_per_eu(SfwdCfg<T, D, C, PAIR>::ACC ? 4 : 1))) void hgrn2_seg_fwd_kernel(SegFwdArgs a) {
+  using Cfg = SfwdCfg<T, D, C, PAIR>;
   constexpr int NB = Cfg::NB, NWV = Cfg::NWV, NT = Cfg::NT, CPL = Cfg::CPL, JB = Cfg::JB, KSD = Cfg::KSD,
                 HC = Cfg::HC, EPV = Cfg::EPV, TPW = Cfg::TPW, NPAIR = Cfg::NPAIR;
   constexpr bool ACC = Cfg::ACC;
@@ -181,9 +185,10 @@ __attribute__((amdgpu_waves_per_eu(SfwdCfg<T, D, C>::ACC ? 4 : 1))) void hgrn2_s
     T la;  // kScalar: log a of token 16 w + (lane & 15)
   };
   auto load = [&](Regs &r, int n) {
-    // lane-dependent values derived anew, so that the addresses built from
-    // them are not hoisted out of the walk and kept live in registers
-    const int tid = opaque((int)threadIdx.x), lane = tid & 63;
+    // ACC (128 registers per lane): lane-dependent values derived anew, so
+    // that the addresses built from them are not hoisted out of the walk and
+    // kept live in registers
+    const int tid = ACC ? opaque((int)threadIdx.x) : (int)threadIdx.x, lane = tid & 63;
     const int c0 = (has_ch ? lane : 0) * CPL;
     const uint32_t c0b = (uint32_t)c0 * sizeof(T);
     const int t0 = n * C, len = min(C, T_ - t0);
@@ -216,7 +221,7 @@ __attribute__((amdgpu_waves_per_eu(SfwdCfg<T, D, C>::ACC ? 4 : 1))) void hgrn2_s
   for (int n = n0; n < n1; ++n) {
     const int t0 = n * C, len = min(C, T_ - t0);
     // (as in load: lane-dependent values derived anew each chunk)
-    const int tid = opaque((int)threadIdx.x), lane = tid & 63, n16 = lane & 15, g = lane >> 4;
+    const int tid = ACC ? opaque((int)threadIdx.x) : (int)threadIdx.x, lane = tid & 63, n16 = lane & 15, g = lane >> 4;
     const int c0 = (has_ch ? lane : 0) * CPL;
     const uint32_t c0b = (uint32_t)c0 * sizeof(T);
     // ---- P0: v tile; block w's prefix (in both of its waves); qo, ko of this wave's tokens
@@ -231,26 +236,48 @@ __attribute__((amdgpu_waves_per_eu(SfwdCfg<T, D, C>::ACC ? 4 : 1))) void hgrn2_s
       float run[CPL], ell[8][CPL], kf[8][CPL];
 #pragma unroll
       for (int e = 0; e < CPL; ++e) run[e] = 0.f;
+      if constexpr (ACC) {
+        // (k formed only for this wave's own tokens: fewer live registers)
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const bool own = half == hh;  // wave-uniform
+        for (int half = 0; half < 2; ++half) {
+          const bool own = half == hh;  // wave-uniform
 #pragma unroll
-        for (int t8 = 0; t8 < 8; ++t8) {
-          const int t = 8 * half + t8, tt = 16 * w + t;
+          for (int t8 = 0; t8 < 8; ++t8) {
+            const int t = 8 * half + t8, tt = 16 * w + t;
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) {
+              const T lx = GM == kScalar ? readlane(rg.la, t) : rg.l[t].v[e];
+              float lf;
+              if (own) {
+                // k of this wave's own tokens (loaded, or formed with log f)
+                const T kx = reads_k(GM) ? rg.k[t8].v[e] : lx;
+                lf_k<GM>(kx, lx, lbv[e], tt < len, lf, kf[t8][e]);
+              } else {
+                // the other half's tokens only add their log f to the prefix
+                lf = lf_of<GM>(to_f32(lx), lbv[e], tt < len);
+              }
+              run[e] += lf;
+              if (own) ell[t8][e] = run[e];
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const int tt = 16 * w + t;
 #pragma unroll
           for (int e = 0; e < CPL; ++e) {
             const T lx = GM == kScalar ? readlane(rg.la, t) : rg.l[t].v[e];
-            float lf;
-            if (own) {
-              // k of this wave's own tokens (loaded, or formed with log f)
-              const T kx = reads_k(GM) ? rg.k[t8].v[e] : lx;
-              lf_k<GM>(kx, lx, lbv[e], tt < len, lf, kf[t8][e]);
-            } else {
-              // the other half's tokens only add their log f to the prefix
-              lf = lf_of<GM>(to_f32(lx), lbv[e], tt < len);
-            }
+            float lf, kv;
+            // k of this wave's own tokens (loaded, or formed with log f); the
+            // other half's tokens only add their log f to the prefix
+            const T kx = reads_k(GM) ? rg.k[t & 7].v[e] : lx;
+            lf_k<GM>(kx, lx, lbv[e], tt < len, lf, kv);
             run[e] += lf;
-            if (own) ell[t8][e] = run[e];
+            if ((t >> 3) == hh) {
+              ell[t & 7][e] = run[e];
+              kf[t & 7][e] = kv;
+            }
           }
         }
       }
@@ -640,9 +667,15 @@ __global__ __launch_bounds__(256) void hgrn2_seg_carry_kernel(int BH, int NSEG, 
 
 template <typename T, int D, int C, int GM, typename TO = T>
 hipError_t launch_seg_fwd(const SegFwdArgs &a, hipStream_t stream) {
-  using Cfg = SfwdCfg<T, D, C>;
-  hipLaunchKernelGGL((hgrn2_seg_fwd_kernel<T, D, C, GM, TO>), dim3((unsigned)((long long)a.B * a.H * a.P)),
-                     dim3(Cfg::NT), 0, stream, a);
+  const dim3 grid((unsigned)((long long)a.B * a.H * a.P));
+  if constexpr (SfwdCfg<T, D, C, true>::ACC) {
+    if (a.pair) {
+      hipLaunchKernelGGL((hgrn2_seg_fwd_kernel<T, D, C, GM, TO, true>), grid, dim3(SfwdCfg<T, D, C, true>::NT), 0,
+                         stream, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((hgrn2_seg_fwd_kernel<T, D, C, GM, TO>), grid, dim3(SfwdCfg<T, D, C>::NT), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -6,7 +6,11 @@ keeps only the state).  Against the oracle (every slice, row and element):
 one segment per sequence (B*H >= 256), many segments with a ragged last one,
 the final state alone (y = NULL), ht aliasing h0 across segments, every gate
 mode, float32, decays wide enough for the directly summed diagonal, and
-agreement with the forward that stores its states."""
+agreement with the forward that stores its states.  bfloat16 at d = 128 walks
+two workgroups per compute unit (the state kept in the accumulators) where the
+plan fills both; the paired-walk tests cover that layout in every gate mode."""
+import functools
+
 import numpy as np
 import pytest
 
@@ -23,12 +27,22 @@ def _case(dtype, B, T, H, D, lam=0.3, seed=41, h0std=0.3):
     return synth.generate(w)
 
 
-def _plan(B, H, T):
-    """The segments the library cuts (mirrors the ABI's rule, for the report)."""
-    N = -(-T // 64)
-    Pt = min(N, max(1, -(-256 // (B * H))))
-    G = -(-N // Pt)
-    return -(-N // G), G
+def _plan(B, H, T, dtype="bf16", D=128):
+    """The segments the library cuts and whether two workgroups per compute
+    unit walk them (mirrors the ABI's rule, for the report)."""
+    N, BH = -(-T // 64), B * H
+
+    def plan(u):
+        Pt = min(N, max(1, -(-u // BH)))
+        G = -(-N // Pt)
+        return -(-N // G), G
+
+    units = 512 if (dtype == "bf16" and D == 128) else 256
+    P, G = plan(units)
+    if units > 256 and P > 1 and G < 8:
+        units = 256
+        P, G = plan(units)
+    return P, G, units > 256 and BH * P > 256
 
 
 def _check(d, label=""):
@@ -42,9 +56,9 @@ def _check(d, label=""):
     x = inputs64(d)
     yr, htr = oracle.forward(x["q"], x["k"], x["v"], x["log_f"], x["h0"])
     ey, eh = errors(to_host64(y), yr), errors(to_host64(ht), htr, "state")
-    P, G = _plan(d["B"], d["H"], d["T"])
-    print("%s seg fwd %s B%d H%d T%d D%d (P=%d G=%d): y %s | ht %s" % (label, dt, d["B"], d["H"], d["T"], d["D"],
-                                                                     P, G, fmt(ey), fmt(eh)), flush=True)
+    P, G, pair = _plan(d["B"], d["H"], d["T"], dt, d["D"])
+    print("%s seg fwd %s B%d H%d T%d D%d (P=%d G=%d%s): y %s | ht %s" % (
+        label, dt, d["B"], d["H"], d["T"], d["D"], P, G, ", paired" if pair else "", fmt(ey), fmt(eh)), flush=True)
     assert worst(ey) <= TOL[dt] and worst(eh) <= TOL[dt]
     return y, ht
 
@@ -163,3 +177,74 @@ def test_gate_modes(dtype):
         eh = errors(to_host64(out[mode][1]), ref[mode][1], "state")
         print("seg %s %s: y %s | ht %s" % (mode, dtype, fmt(ey), fmt(eh)), flush=True)
         assert worst(ey) <= TOL[dtype] and worst(eh) <= TOL[dtype], mode
+
+
+# B5 H13 T4049: 65 sequences of 64 chunks (the last one 17 tokens), cut into
+# 8 segments of 8 chunks: 520 workgroups, two per compute unit
+PAIRED = dict(B=5, T=63 * 64 + 17, H=13, D=128)
+
+
+@functools.lru_cache(maxsize=1)
+def _paired_inputs():
+    return _case("bf16", lam=0.5, seed=51, **PAIRED)
+
+
+def test_paired_walk_plan():
+    assert _plan(PAIRED["B"], PAIRED["H"], PAIRED["T"]) == (8, 8, True)
+    assert _plan(4, 8, 2048) == (8, 4, False)       # segments of 2 chunks would be too short
+    assert _plan(1, 32, 32768) == (16, 32, True)
+
+
+@pytest.mark.parametrize("mode", ["untied", "tied", "gate", "scalar"])
+def test_paired_walk(mode):
+    """The two-per-compute-unit walk in every gate mode, with an initial state
+    and the final state, against the oracle."""
+    import torch
+    import linear_attention_hgrn2_amd as m
+    d = _paired_inputs()
+    q, k, v, lf, z = (to_dev(d[n], "bf16") for n in ("q", "k", "v", "log_f", "z"))
+    h0 = to_dev(d["h0"], "f32")
+    x = {n: synth.to_f64(d[n], "bf16") for n in ("q", "k", "v", "log_f", "z")}
+    h064 = d["h0"].astype(np.float64)
+    if mode == "untied":
+        y, ht, _ = m.fwd(q, k, v, lf, h0, chunk=64)
+        yr, htr = oracle.forward(x["q"], x["k"], x["v"], x["log_f"], h064)
+    elif mode == "tied":
+        y, ht, _ = m.fwd_tied(q, v, lf, h0, chunk=64)
+        yr, htr = oracle.forward_tied(x["q"], x["v"], x["log_f"], h064)
+    elif mode == "gate":
+        lbn = synth.lower_bounds(d["H"], 128, 0.5, 0.25, seed=5)
+        y, ht, _ = m.fwd_gate(q, v, z, to_dev(lbn, "f32"), h0, chunk=64)
+        yr, htr = oracle.forward_gate(x["q"], x["v"], x["z"], lbn.astype(np.float64), h064)
+    else:
+        la = np.ascontiguousarray(d["log_f"][..., 0])
+        y, ht, _ = m.fwd_scalar(q, k, v, to_dev(la, "bf16"), h0, chunk=64)
+        yr, htr = oracle.forward_scalar(x["q"], x["k"], x["v"], synth.to_f64(la, "bf16"), h064)
+    torch.cuda.synchronize()
+    ey, eh = errors(to_host64(y), yr), errors(to_host64(ht), htr, "state")
+    print("paired walk %s: y %s | ht %s" % (mode, fmt(ey), fmt(eh)), flush=True)
+    assert worst(ey) <= TOL["bf16"] and worst(eh) <= TOL["bf16"]
+
+
+def test_paired_walk_f32_out_and_wide_decays():
+    """float32 y from the accumulators, full resets, the -200 floor and
+    in-block decays past kDiagLimit, in the paired walk."""
+    import torch
+    import linear_attention_hgrn2_amd as m
+    d = _case("bf16", lam=0.0, seed=52, **PAIRED)
+    lf = synth.to_f64(d["log_f"], "bf16")
+    lf[0, 3, 0, :] = -np.inf
+    lf[1, 20, 1, 2] = -200.0
+    lf[2, 400:404, 5, 1] = -30.0
+    lf[4, 2000:2010, 12, :] = -9.0
+    d["log_f"] = synth.f32_to_bf16_bits(lf.astype(np.float32))
+    q, k, v, lfd = (to_dev(d[n], "bf16") for n in ("q", "k", "v", "log_f"))
+    h0 = to_dev(d["h0"], "f32")
+    y, ht, _ = m.fwd(q, k, v, lfd, h0, chunk=64, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert y.dtype == torch.float32
+    x = inputs64(d)
+    yr, htr = oracle.forward(x["q"], x["k"], x["v"], x["log_f"], x["h0"])
+    ey, eh = errors(to_host64(y), yr), errors(to_host64(ht), htr, "state")
+    print("paired walk, float32 y, wide decays: y %s | ht %s" % (fmt(ey), fmt(eh)), flush=True)
+    assert worst(ey) <= TOL["bf16"] and worst(eh) <= TOL["bf16"]
