@@ -196,6 +196,21 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
       sm.lbc[0][cc + 1] = plb[1];
     }
   }
+  // gate mode: a chunk's token sums of G dlog f/dlb, per wave in the dq'
+  // staging rows 0..7 (written at the chunk's end), summed over the waves in
+  // a fixed order by the first D threads once a barrier has passed: after the
+  // next chunk's B0 (beside that chunk's prefix work, before its B1, after
+  // which the copies into S may land there), and after the walk for the last
+  auto dlb_out = [&](int cprev) {
+    const int t = (int)threadIdx.x;
+    if (t < D) {
+      const Chunk kp = chunk_of(cprev);
+      float acc = 0.f;
+#pragma unroll
+      for (int o = 0; o < NWV; ++o) acc += sm.u.e.stg[0][o][t];
+      a.dlb[((size_t)kp.bh * N + kp.n) * D + t] = acc;
+    }
+  };
   int par = 0;  // parity of this workgroup's chunk count: the lbc slot of the current chunk
   for (; ci < NC; ci += G, par ^= 1) {
     const Chunk k = chunk_of(ci);
@@ -213,6 +228,9 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
     };
     float lb2[2];
     lbs(lb2);
+    if constexpr (GM == kGate) {
+      if (ci != (int)blockIdx.x) dlb_out(ci - G);
+    }
 
     // ---- P0a: v, dy tiles; half-block totals of log f
 #pragma unroll
@@ -763,19 +781,17 @@ __global__ __launch_bounds__(512) void hgrn2_chunk_bwd_res_kernel(ChunkBwdArgs a
         }
       }
       if constexpr (GM == kGate) {
-        // per-wave sums into the consumed dq' staging, then a fixed-order sum
-        // over the eight waves per channel (read before the next chunk's B1,
-        // after which the copies into S may land there)
+        // per-wave sums into the consumed dq' staging (dlb_out sums them)
         ep.stg[0][wv][c0] = dlbs[0];
         ep.stg[0][wv][c0 + 1] = dlbs[1];
-        __syncthreads();  // B9
-        if (tid < D) {
-          float acc = 0.f;
-#pragma unroll
-          for (int o = 0; o < NWV; ++o) acc += ep.stg[0][o][tid];
-          a.dlb[((size_t)k.bh * N + k.n) * D + tid] = acc;
-        }
       }
+    }
+  }
+  if constexpr (GM == kGate) {
+    // the last chunk's lower-bound sums
+    if ((int)blockIdx.x < NC) {
+      __syncthreads();
+      dlb_out(ci - G);
     }
   }
 }
