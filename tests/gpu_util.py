@@ -14,6 +14,25 @@ Comparison metrics (all three must be <= the dtype's tolerance, TOL):
         |gpu - ref| / (|ref| + 3 max(rms(ref_t), rms(ref))).
 A slice is one (b, h) sequence of a [B, T, H, D] tensor, one (b, h) matrix of
 a [B, H, D, D] state, or one (b, c) channel sequence of a [B, T, C] tensor.
+A slice of fewer than MIN_NORM_ROWS rows (sequences shorter than one 16-token
+sub-block) is held to the row term in place of the norm term: its norm is
+then the relative error of one or a few rows, with nothing to average over.
+With one token a row of y is one score times v, and that score a dot product
+of q e^{ell} (a bf16 operand) with k: where its terms cancel thirty-fold, the
+operand rounding alone leaves about 3% in every element of the row (a float64
+model of the kernels' rounding points reproduces the GPU's error to three
+digits, and drops it tenfold without the operand rounding).  The row term
+measures that row against its norm plus the slice's rms row norm, as it does
+every row of every slice.  Where the comparison also has the magnitude of the
+terms each output sums (`terms`: the oracle on the absolute values of the
+inputs, |q|, |k|, |v|, |h0|, |dy|, |dht| with f unchanged, which for these
+sums of products with positive weights is the sum of the terms' magnitudes),
+a short slice's row and element denominators also get TERMS_FRAC of it: a
+path rounds a term at most about five times at its unit roundoff (bf16:
+decayed operands, score tile, state, output), so the fraction is five unit
+roundoffs over the tolerance, 5 * 2^-9 / 2e-2 (about 1/2) for bf16 and
+5 * 2^-24 / 1e-4 for float32.  An output that cancels its terms almost completely is then held
+to the rounding its arithmetic allows, not to its own tiny magnitude.
 The row and element terms catch localised errors that a slice norm over
 hundreds of thousands of values would hide (one wrong token row of a 4096-token
 slice moves its norm by only about 1/64).  Where a row holds a single value
@@ -48,6 +67,8 @@ import torch
 import synth
 
 TOL = {"bf16": 2e-2, "f32": 1e-4}
+MIN_NORM_ROWS = 16
+TERMS_FRAC = {"bf16": 5 * 2.0 ** -9 / TOL["bf16"], "f32": 5 * 2.0 ** -24 / TOL["f32"]}
 
 
 def to_dev(a: np.ndarray | None, dtype: str):
@@ -68,12 +89,15 @@ def _nz(x):
     return np.where(x > 0, x, 1.0)
 
 
-def errors(got: np.ndarray, ref: np.ndarray, layout: str = "token") -> dict:
+def errors(got: np.ndarray, ref: np.ndarray, layout: str = "token", terms: np.ndarray | None = None,
+           dtype: str = "bf16") -> dict:
     """The three metrics above for `got` against `ref`.
 
     layout: "token" [B, T, H, D] (slices (b, h), rows = tokens), "state"
     [B, H, D, D] (slices (b, h), rows = state rows), "btc" [B, T, C] (slices
-    (b, c), rows = tokens of one batch element)."""
+    (b, c), rows = tokens of one batch element).  terms: the magnitude of the
+    terms each reference value sums, same shape (used for short slices of the
+    input dtype `dtype`)."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (got.shape, ref.shape)
@@ -101,7 +125,7 @@ def errors(got: np.ndarray, ref: np.ndarray, layout: str = "token") -> dict:
         rs = np.sqrt((rr * rr).mean(axis=1))         # [B]
         row = float(np.max(re / _nz(rr + rs[:, None])))
         scale = np.maximum(rms[:, None, :], (rr / np.sqrt(C))[:, :, None])
-        return {"norm": norm, "row": row, **_elem(d, ref, scale)}
+        return {"norm": row if T < MIN_NORM_ROWS else norm, "row": row, **_elem(d, ref, scale)}
     else:
         raise ValueError(layout)
     n = np.sqrt((d * d).sum(axis=s_ax))
@@ -115,16 +139,20 @@ def errors(got: np.ndarray, ref: np.ndarray, layout: str = "token") -> dict:
     rs = rn / np.sqrt(nrows)                         # rms row norm of the slice
     width = ref.shape[r_ax]
     scale = np.maximum(slice_b(rms), (rr / np.sqrt(width))[..., None])
-    el = _elem(d, ref, scale)
-    row = el["elem"] if width == 1 else float(np.max(re / _nz(rr + row_b(rs))))
-    return {"norm": norm, "row": row, **el}
+    short = nrows < MIN_NORM_ROWS
+    ta = np.zeros_like(ref) if (terms is None or not short) else TERMS_FRAC[dtype] * np.abs(np.asarray(terms, np.float64))
+    el = _elem(d, ref, scale, ta)
+    ra = np.sqrt((ta * ta).sum(axis=r_ax))
+    row = el["elem"] if width == 1 else float(np.max(re / _nz(rr + row_b(rs) + ra)))
+    return {"norm": row if short else norm, "row": row, **el}
 
 
-def _elem(d, ref, scale):
+def _elem(d, ref, scale, extra=0.0):
     """The element metric, and where its worst element is (index, error,
-    reference, scale) for the report."""
+    reference, scale) for the report.  extra: a further per-element term of
+    the denominator (a short slice's share of its terms' magnitude)."""
     scale = np.broadcast_to(scale, ref.shape)
-    ratio = np.abs(d) / _nz(np.abs(ref) + 3.0 * scale)
+    ratio = np.abs(d) / _nz(np.abs(ref) + 3.0 * scale + extra)
     i = int(np.argmax(ratio))
     at = np.unravel_index(i, ref.shape)
     return {"elem": float(ratio.flat[i]),

@@ -96,3 +96,53 @@ def test_one_value_rows_use_the_element_term():
     g = r.copy()
     g[0, 17, 1, 0] = 0.0
     assert worst(errors(g, r)) > TOL["bf16"] or abs(r[0, 17, 1, 0]) < 0.06 * rms
+
+
+def test_short_slices_use_the_row_term():
+    """Sequences shorter than one 16-token sub-block: the norm term is the row
+    term.  A one-token row off by 2.8% in every element (what bf16 operand
+    rounding leaves on a score whose terms cancel thirty-fold) passes; 10% off
+    fails; at 16 tokens the slice norm applies again."""
+    r = _ref((2, 1, 2, 64))
+    g = r.copy()
+    g[0, 0, 1] *= 1.028
+    e = errors(g, r)
+    assert e["norm"] == e["row"] and worst(e) <= TOL["bf16"]
+    g = r.copy()
+    g[1, 0, 0] *= 1.10
+    assert worst(errors(g, r)) > TOL["bf16"]
+    r = _ref((1, 16, 1, 64))
+    g = r * 1.028
+    e = errors(g, r)
+    assert e["norm"] > TOL["bf16"] and e["norm"] != e["row"]
+
+
+def test_short_slices_measure_against_their_terms():
+    """A one-token slice whose score q.k cancels its terms 200-fold: the
+    bf16 kernels' rounding (the float64 model of their rounding points) is
+    several percent of y itself, so the plain metric fails it; measured
+    against the magnitude of y's terms (the oracle on absolute values) it
+    passes, while one channel of q with its sign flipped still fails."""
+    import oracle
+    from tests import chunked_ref as cr
+    rng = np.random.default_rng(7)
+    B, T, H, D = 1, 1, 2, 64
+    q = cr._bf16(rng.standard_normal((B, T, H, D)))
+    k = cr._bf16(rng.standard_normal((B, T, H, D)))
+    for h in range(H):                              # q.k about 1/200 of sum |q k|
+        qk = q[0, 0, h] * k[0, 0, h]
+        c = int(np.argmax(np.abs(q[0, 0, h])))
+        want = 0.005 * np.abs(qk).sum()
+        k[0, 0, h, c] = cr._bf16(np.array([k[0, 0, h, c] + (want - qk.sum()) / q[0, 0, h, c]]))[0]
+    v = cr._bf16(rng.standard_normal((B, T, H, D)))
+    lf = np.full((B, T, H, D), np.log(0.9))
+    ref, _ = oracle.forward(q, k, v, lf, None)
+    got = np.stack([cr.forward_bf16_points(q[0, :, h], k[0, :, h], v[0, :, h], lf[0, :, h], C=16)
+                    for h in range(H)], axis=1)[None]
+    terms, _ = oracle.forward(np.abs(q), np.abs(k), np.abs(v), lf, None)
+    assert worst(errors(got, ref)) > TOL["bf16"]
+    assert worst(errors(got, ref, "token", terms)) <= TOL["bf16"]
+    q2 = q.copy()
+    q2[..., 5] = -q2[..., 5]
+    bad, _ = oracle.forward(q2, k, v, lf, None)
+    assert worst(errors(bad, ref, "token", terms)) > TOL["bf16"]
