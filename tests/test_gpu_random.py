@@ -11,7 +11,10 @@ values, the magnitude of the terms each output sums (the arithmetic's rounding
 scale for outputs that cancel their terms).
 
 HGRN2_RANDOM_CASES sets the number of cases (default 24); the cases are the
-same on every run."""
+same on every run.  A second stream of medium cases (HGRN2_RANDOM_MEDIUM,
+default 6) draws up to 4 x 16 sequences of up to 2048 tokens (at most 32768
+token-heads), so that the persistent backward walks several chunks per
+workgroup and the scans many chunks per sequence."""
 import os
 
 import numpy as np
@@ -25,6 +28,7 @@ pytestmark = pytest.mark.gpu
 
 MASTER_SEED = 20241
 N_CASES = int(os.environ.get("HGRN2_RANDOM_CASES", "24"))
+N_MEDIUM = int(os.environ.get("HGRN2_RANDOM_MEDIUM", "6"))
 
 
 def _draw(i):
@@ -35,6 +39,17 @@ def _draw(i):
              h0=bool(r.integers(0, 2)), dht=bool(r.integers(0, 2)), saved=bool(r.integers(0, 2)),
              out32=bool(r.integers(0, 2)), seed=int(r.integers(1, 1 << 30)))
     c["T"] = int(r.integers(1, 4 * c["C"] + 38))
+    return c
+
+
+def _draw_medium(i):
+    r = np.random.default_rng(MASTER_SEED + 1 + 6101 * i)
+    c = dict(gm=str(r.choice(["untied", "tied", "gate", "scalar"])), dtype=str(r.choice(["bf16", "f32"])),
+             D=int(r.choice([64, 128])), C=int(r.choice([16, 32, 64, 128])),
+             B=int(r.integers(1, 5)), H=int(r.integers(1, 17)), lam=float(r.choice([0.0, 0.3, 0.6, 0.9, 0.97])),
+             h0=bool(r.integers(0, 2)), dht=bool(r.integers(0, 2)), saved=bool(r.integers(0, 2)),
+             out32=bool(r.integers(0, 2)), seed=int(r.integers(1, 1 << 30)))
+    c["T"] = int(r.integers(64, min(2048, 32768 // (c["B"] * c["H"])) + 1))
     return c
 
 
@@ -82,9 +97,17 @@ def _terms(c, f, h064, dht64, lb64):
 
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_case(i):
+    _run(i, _draw(i))
+
+
+@pytest.mark.parametrize("i", range(N_MEDIUM))
+def test_random_medium_case(i):
+    _run(i, _draw_medium(i))
+
+
+def _run(i, c):
     import torch
     import linear_attention_hgrn2_amd as m
-    c = _draw(i)
     dt, D, C, gm = c["dtype"], c["D"], c["C"], c["gm"]
     tdt = torch.float32 if dt == "f32" else torch.bfloat16
     if not m.supported(D, C, tdt):
