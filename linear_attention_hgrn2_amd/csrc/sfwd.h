@@ -101,6 +101,36 @@ template <typename T, int D, int C, bool PAIR = false> struct SfwdCfg {
 // pair index p -> (i, j), i >= j, p = i (i + 1) / 2 + j
 __device__ __forceinline__ int sfwd_pair_i(int p) { return p >= 6 ? 3 : p >= 3 ? 2 : p >= 1 ? 1 : 0; }
 
+// The v tile of the ACC layout (64 rows of 128 bfloat16): unpadded, each
+// row's 16-byte chunks permuted by XOR with 2 (row & 7), a layout that an
+// asynchronous copy straight into LDS can write (a wave's copy fills 1 KB
+// contiguously, four whole rows).  The transposing reads take 32 bytes (two
+// chunks that the permutation keeps together) from each of 4 or 8
+// consecutive rows, which then fall on distinct banks.
+__device__ __forceinline__ int sfwd_vsw(int r, int col) { return r * 128 + ((((col >> 3) ^ (2 * (r & 7)))) << 3) + (col & 7); }
+__device__ __forceinline__ v4s_t sfwd_vtr(const bf16_t *t, int r, int n0, int lane) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s_t *)(t + sfwd_vsw(r, n0 + 4 * (lane & 3))));
+}
+// as tr4 and tr8 (rows r0 + 4 g + j, and r0 + 8 g + i; column n0 + n) on that layout
+__device__ __forceinline__ PFrag4<bf16_t> sfwd_vtr4(const bf16_t *t, int r0, int n0, int lane) {
+  PFrag4<bf16_t> f;
+  f.x = sfwd_vtr(t, r0 + 4 * (lane >> 4) + ((lane & 15) >> 2), n0, lane);
+  return f;
+}
+__device__ __forceinline__ PFrag<bf16_t> sfwd_vtr8(const bf16_t *t, int r0, int n0, int lane) {
+  const int rr = r0 + 8 * (lane >> 4) + ((lane & 15) >> 2);
+  union {
+    v4s_t h[2];
+    bf16x8_t v;
+  } u;
+  u.h[0] = sfwd_vtr(t, rr, n0, lane);
+  u.h[1] = sfwd_vtr(t, rr + 4, n0, lane);
+  PFrag<bf16_t> f;
+  f.x = u.v;
+  return f;
+}
+
 // TO: the element type of y (T, or float32 for bfloat16 inputs)
 // PAIR: the ACC layout (bfloat16, d = 128, chunk 64), two workgroups per
 // compute unit; otherwise one workgroup per compute unit, state copy in LDS
@@ -184,7 +214,12 @@ __attribute__((amdgpu_waves_per_eu(SfwdCfg<T, D, C, PAIR>::ACC ? 4 : 1))) void h
     Pack<T, CPL> q[8], k[8], l[16];
     T la;  // kScalar: log a of token 16 w + (lane & 15)
   };
-  auto load = [&](Regs &r, int n) {
+  // parts of a chunk's rows: the v tile, and q, k and log f
+  constexpr int kLdV = 1, kLdQKL = 2, kLdAll = 3;
+  // vector-memory loads of a kLdQKL load: q and k of 8 tokens (k unless
+  // formed from the gate), log f of 16 tokens (one log a with one decay per head)
+  constexpr int kQKL = 8 + (reads_k(GM) ? 8 : 0) + (GM == kScalar ? 1 : 16);
+  auto load = [&](Regs &r, int n, int parts) {
     // ACC (128 registers per lane): lane-dependent values derived anew, so
     // that the addresses built from them are not hoisted out of the walk and
     // kept live in registers
@@ -197,12 +232,15 @@ __attribute__((amdgpu_waves_per_eu(SfwdCfg<T, D, C, PAIR>::ACC ? 4 : 1))) void h
     const GBuf bq((const char *)a.q + cbase, rows), bv((const char *)a.v + cbase, rows);
     const GBuf bk((const char *)(reads_k(GM) ? a.k : a.q) + cbase, rows);
     const LfRows<GM> bl = lf_rows<GM, T>(a.log_f, b, T_, H, h, D, t0, len);
+    if (parts & kLdV) {
 #pragma unroll
-    for (int i = 0; i < Cfg::NVV; ++i) {
-      const int idx = min(tid + i * NT, Cfg::VV - 1);
-      const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
-      r.v[i] = bv.ld16(tok(row) + (uint32_t)col * sizeof(T));
+      for (int i = 0; i < Cfg::NVV; ++i) {
+        const int idx = min(tid + i * NT, Cfg::VV - 1);
+        const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
+        r.v[i] = bv.ld16(tok(row) + (uint32_t)col * sizeof(T));
+      }
     }
+    if (!(parts & kLdQKL)) return;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       r.q[t] = bq.template ldpack<T, CPL>(tok(16 * w + 8 * hh + t) + c0b);
@@ -217,7 +255,7 @@ __attribute__((amdgpu_waves_per_eu(SfwdCfg<T, D, C, PAIR>::ACC ? 4 : 1))) void h
   };
 
   Regs rg;
-  load(rg, n0);
+  load(rg, n0, ACC ? kLdQKL : kLdAll);
   for (int n = n0; n < n1; ++n) {
     const int t0 = n * C, len = min(C, T_ - t0);
     // (as in load: lane-dependent values derived anew each chunk)
@@ -225,11 +263,27 @@ __attribute__((amdgpu_waves_per_eu(SfwdCfg<T, D, C, PAIR>::ACC ? 4 : 1))) void h
     const int c0 = (has_ch ? lane : 0) * CPL;
     const uint32_t c0b = (uint32_t)c0 * sizeof(T);
     // ---- P0: v tile; block w's prefix (in both of its waves); qo, ko of this wave's tokens
+    if constexpr (ACC) {
+      // the v tile by asynchronous copies straight into LDS (the tiles are
+      // free since B4), waited for before B2: wave wv copies rows 8 wv .. + 7,
+      // four rows of 256 bytes per instruction; lane i lands in chunk i % 16
+      // of row 4 j + i / 16 and fetches the logical chunk the swizzle puts
+      // there.
+      const size_t cbase = (((size_t)b * T_ + t0) * H + h) * D * sizeof(T);
+      const GBuf bvc((const char *)a.v + cbase, (uint32_t)len * HDB);
 #pragma unroll
-    for (int i = 0; i < Cfg::NVV; ++i) {
-      const int idx = tid + i * NT;
-      const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
-      if (idx < Cfg::VV) *(uint4 *)&sm.v[VT::at(row, col)] = rg.v[i];
+      for (int j = 0; j < 2; ++j) {
+        const int r = 8 * wv + 4 * j + (lane >> 4);
+        const int q = (lane & 15) ^ (2 * (r & 7));
+        lds_dma16(bvc, tok(r) + (uint32_t)q * 16, sm.v + (8 * wv + 4 * j) * D);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < Cfg::NVV; ++i) {
+        const int idx = tid + i * NT;
+        const int row = idx / (D / EPV), col = (idx % (D / EPV)) * EPV;
+        if (idx < Cfg::VV) *(uint4 *)&sm.v[VT::at(row, col)] = rg.v[i];
+      }
     }
     float kof[8][CPL];  // this wave's tokens: ko in float32, k e^{L_w - ell}
     {
@@ -312,7 +366,10 @@ __attribute__((amdgpu_waves_per_eu(SfwdCfg<T, D, C, PAIR>::ACC ? 4 : 1))) void h
       if (hh == 0 && lane == 0) sm.wide[w] = wide;
     }
     // the registers are consumed: the next chunk's rows
-    if (n + 1 < n1) load(rg, n + 1);
+    // (ACC: q, k and log f; its v tile is copied into LDS when that chunk
+    // starts.  Held in registers from here, the v vectors were spilled, and
+    // the spill's store waited for the load it spilled.)
+    if (n + 1 < n1) load(rg, n + 1, ACC ? kLdQKL : kLdAll);
     __syncthreads();  // B1: qo, ko, v, block decays and flags of every block
 
     // ---- P1: kh of this wave's tokens, e^{P_w}, e^{Gamma}; the score tiles
@@ -439,7 +496,26 @@ __attribute__((amdgpu_waves_per_eu(SfwdCfg<T, D, C, PAIR>::ACC ? 4 : 1))) void h
       }
       sm.sc[tau][lane] = acc_to_frag4<T>(X);
     }
-    __syncthreads();  // B2: score tiles, kh, e^{P}, e^{Gamma}
+    if constexpr (ACC) {
+      // this wave's copies of the v tile have landed: vector-memory operations
+      // complete in issue order, and kQKL loads were issued after the copies
+      // when a next chunk was prefetched
+      if (n + 1 < n1) {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kQKL) : "memory");
+      } else {
+        vm_drain();
+      }
+      // a ragged last chunk: this wave's rows past the sequence's end are
+      // zero whatever the copy left there
+      if (len < C) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int idx = lane + 64 * i, r = 8 * wv + (idx >> 4);
+          if (r >= len) *(uint4 *)&sm.v[r * D + 8 * (idx & 15)] = uint4{0u, 0u, 0u, 0u};
+        }
+      }
+    }
+    __syncthreads();  // B2: score tiles, kh, e^{P}, e^{Gamma}, v
 
     if constexpr (ACC) {
       // ---- P2: y of all four token blocks for column tile wv: the scores'
@@ -449,7 +525,7 @@ __attribute__((amdgpu_waves_per_eu(SfwdCfg<T, D, C, PAIR>::ACC ? 4 : 1))) void h
       for (int w2 = 0; w2 < NB; ++w2) acc_zero(Y[w2]);
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const PFrag4<T> fv = tr4<D, PV>(sm.v, 16 * j, 16 * wv);
+        const PFrag4<T> fv = sfwd_vtr4(sm.v, 16 * j, 16 * wv, lane);
 #pragma unroll
         for (int w2 = j; w2 < NB; ++w2) mma16(Y[w2], sm.sc[w2 * (w2 + 1) / 2 + j][lane], fv);
       }
@@ -510,7 +586,7 @@ __attribute__((amdgpu_waves_per_eu(SfwdCfg<T, D, C, PAIR>::ACC ? 4 : 1))) void h
           }
         }
       }
-      const PFrag<T> fv0 = tr8<D, PV>(sm.v, 0, 16 * wv), fv1 = tr8<D, PV>(sm.v, 32, 16 * wv);
+      const PFrag<T> fv0 = sfwd_vtr8(sm.v, 0, 16 * wv, lane), fv1 = sfwd_vtr8(sm.v, 32, 16 * wv, lane);
 #pragma unroll
       for (int i = 0; i < TPW; ++i) {
         const float4 eg = ldf4(&sm.eG[16 * i + 4 * g]);
