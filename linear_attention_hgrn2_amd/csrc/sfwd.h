@@ -254,6 +254,27 @@ __attribute__((amdgpu_waves_per_eu(SfwdCfg<T, D, C, PAIR>::ACC ? 4 : 1))) void h
     }
   };
 
+  // ACC: every prefetched register passes through an empty asm statement, so
+  // that the compiler's wait for those loads (issued a chunk earlier, long
+  // landed) falls here, ahead of the v tile's copies: the compiler does not
+  // count the copies, and a wait of its own after them would wait for them too
+  auto settle = [&](const Regs &r) {
+    if constexpr (ACC) {
+      static_assert(sizeof(Pack<T, CPL>) == 4, "two bfloat16 channels per lane");
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        asm volatile("" ::"v"(__builtin_bit_cast(uint32_t, r.q[t])));
+        if constexpr (reads_k(GM)) asm volatile("" ::"v"(__builtin_bit_cast(uint32_t, r.k[t])));
+      }
+      if constexpr (GM == kScalar) {
+        asm volatile("" ::"v"((uint32_t)__builtin_bit_cast(uint16_t, r.la)));
+      } else {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) asm volatile("" ::"v"(__builtin_bit_cast(uint32_t, r.l[t])));
+      }
+    }
+  };
+
   Regs rg;
   load(rg, n0, ACC ? kLdQKL : kLdAll);
   for (int n = n0; n < n1; ++n) {
@@ -264,6 +285,7 @@ __attribute__((amdgpu_waves_per_eu(SfwdCfg<T, D, C, PAIR>::ACC ? 4 : 1))) void h
     const uint32_t c0b = (uint32_t)c0 * sizeof(T);
     // ---- P0: v tile; block w's prefix (in both of its waves); qo, ko of this wave's tokens
     if constexpr (ACC) {
+      settle(rg);
       // the v tile by asynchronous copies straight into LDS (the tiles are
       // free since B4), waited for before B2: wave wv copies rows 8 wv .. + 7,
       // four rows of 256 bytes per instruction; lane i lands in chunk i % 16
