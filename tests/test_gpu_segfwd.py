@@ -248,3 +248,11 @@ def test_paired_walk_f32_out_and_wide_decays():
     ey, eh = errors(to_host64(y), yr), errors(to_host64(ht), htr, "state")
     print("paired walk, float32 y, wide decays: y %s | ht %s" % (fmt(ey), fmt(eh)), flush=True)
     assert worst(ey) <= TOL["bf16"] and worst(eh) <= TOL["bf16"]
+
+
+def test_paired_walk_uneven_segments():
+    """The paired walk where the segments do not divide the sequence: B2 H20
+    T6369 is 40 sequences of 100 chunks (the last one 33 tokens), cut into 13
+    segments of 8 chunks, the last of them 4 chunks long; no initial state."""
+    assert _plan(2, 20, 99 * 64 + 33) == (13, 8, True)
+    _check(_case("bf16", B=2, T=99 * 64 + 33, H=20, D=128, lam=0.6, seed=53, h0std=0.0), "uneven")
