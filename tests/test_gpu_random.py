@@ -14,7 +14,13 @@ HGRN2_RANDOM_CASES sets the number of cases (default 24); the cases are the
 same on every run.  A second stream of medium cases (HGRN2_RANDOM_MEDIUM,
 default 6) draws up to 4 x 16 sequences of up to 2048 tokens (at most 32768
 token-heads), so that the persistent backward walks several chunks per
-workgroup and the scans many chunks per sequence."""
+workgroup and the scans many chunks per sequence.  A third stream
+(HGRN2_RANDOM_PAIRED, default 6) draws bfloat16 d = 128 chunk-64 cases of 33
+to 96 sequences long enough that the forward without stored states walks two
+workgroups per compute unit (segments of at least 8 chunks), with ragged
+lengths, so that the paired walk's copies of the v tile into LDS, its
+uneven last segments and its ragged last chunks meet random inputs in every
+gate mode."""
 import os
 
 import numpy as np
@@ -29,6 +35,7 @@ pytestmark = pytest.mark.gpu
 MASTER_SEED = 20241
 N_CASES = int(os.environ.get("HGRN2_RANDOM_CASES", "24"))
 N_MEDIUM = int(os.environ.get("HGRN2_RANDOM_MEDIUM", "6"))
+N_PAIRED = int(os.environ.get("HGRN2_RANDOM_PAIRED", "6"))
 
 
 def _draw(i):
@@ -50,6 +57,19 @@ def _draw_medium(i):
              h0=bool(r.integers(0, 2)), dht=bool(r.integers(0, 2)), saved=bool(r.integers(0, 2)),
              out32=bool(r.integers(0, 2)), seed=int(r.integers(1, 1 << 30)))
     c["T"] = int(r.integers(64, min(2048, 32768 // (c["B"] * c["H"])) + 1))
+    return c
+
+
+def _draw_paired(i):
+    r = np.random.default_rng(MASTER_SEED + 2 + 4513 * i)
+    B = int(r.integers(1, 4))
+    H = int(r.integers(-(-33 // B), 96 // B + 1))
+    c = dict(gm=str(r.choice(["untied", "tied", "gate", "scalar"])), dtype="bf16", D=128, C=64, B=B, H=H,
+             lam=float(r.choice([0.0, 0.3, 0.6, 0.9, 0.97])), h0=bool(r.integers(0, 2)), dht=bool(r.integers(0, 2)),
+             saved=bool(r.integers(0, 2)), out32=bool(r.integers(0, 2)), seed=int(r.integers(1, 1 << 30)))
+    pt = -(-512 // (B * H))                     # segments per sequence the plan aims at
+    n = int(r.integers(8 * pt, 10 * pt + 1))    # chunks: segments of at least 8
+    c["T"] = (n - 1) * 64 + int(r.integers(1, 65))
     return c
 
 
@@ -103,6 +123,14 @@ def test_random_case(i):
 @pytest.mark.parametrize("i", range(N_MEDIUM))
 def test_random_medium_case(i):
     _run(i, _draw_medium(i))
+
+
+@pytest.mark.parametrize("i", range(N_PAIRED))
+def test_random_paired_walk_case(i):
+    from tests.test_gpu_segfwd import _plan
+    c = _draw_paired(i)
+    assert _plan(c["B"], c["H"], c["T"])[2], "the case must take the paired walk"
+    _run(i, c)
 
 
 def _run(i, c):
