@@ -36,7 +36,9 @@
 // the inter-chunk product reads it from registers (rows scaled by e^{P_w})
 // and no copy of S goes through LDS.  Each wave then writes y's column tile wv
 // for all four token blocks, staged in the (dead) ko tile for full-row stores.
-// Without the copy and the e^{-L} table the tiles fit in 80 KB, so two
+// The v tile arrives by asynchronous copies straight into LDS when its chunk
+// starts (held in registers from the chunk before, it was spilled at this
+// register budget).  Without the copy and the e^{-L} table the tiles fit in 80 KB, so two
 // workgroups share a compute unit and hide each other's barriers and latency
 // (at 128 registers per lane: lane-dependent values are derived anew in the
 // walk so that the compiler does not keep their addresses live).
@@ -77,9 +79,10 @@ template <typename T, int D, int C, bool PAIR = false> struct SfwdCfg {
   static_assert(D >= 32 && HC >= 1, "two column halves of at least one tile");
   // the state in the accumulators as S, for two workgroups per compute unit
   static constexpr bool ACC = PAIR && std::is_same<T, bf16_t>::value && D == 128 && C == 64;
-  // v and kh are read only by transposing reads (8 rows of 32 bytes per
-  // instruction), which a 32-byte row padding keeps free of bank conflicts;
-  // ACC has the LDS for it
+  // kh (and, without ACC, v) is read only by transposing reads (8 rows of 32
+  // bytes per instruction), which a 32-byte row padding keeps free of bank
+  // conflicts; ACC has the LDS for it.  With ACC the v tile is unpadded and
+  // permuted instead (sfwd_vsw), as its asynchronous copy into LDS needs.
   static constexpr int PV = ACC ? 32 : 16;
   static constexpr int LDV = RowTile<T, D, PV>::LD;
   using Sc = PFrag4<T>;  // one lane's piece of a score tile as a 16-deep operand
@@ -87,7 +90,7 @@ template <typename T, int D, int C, bool PAIR = false> struct SfwdCfg {
     T qo[C * LD];  // RowTile<T, D>; after the products, each wave's y staging
     T ko[C * LD];  // ACC: after the scores, y's staging
     T kh[C * LDV];  // k e^{Gamma - b_t}: the state update's operand
-    T v[C * LDV];
+    T v[C * LDV];   // ACC: the first C * D elements, in the sfwd_vsw layout
     alignas(16) T S[ACC ? 8 : D * LD];  // copy of the state entering the chunk, row c, column j (not with ACC)
     alignas(16) Sc sc[NPAIR][64];
     alignas(16) float eL[NB][D];        // e^{L_w}, each block's decay
