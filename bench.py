@@ -87,10 +87,13 @@ def parse():
 
 
 def kernel_source_digest() -> str:
-    """Digest of the kernel sources; a traffic figure taken on other sources is void."""
+    """Digest of the kernel sources and of their build options (build.py); a
+    traffic figure taken on other sources or options is void."""
     import hashlib
     csrc = os.path.join(ROOT, "linear_attention_hgrn2_amd", "csrc")
     h = hashlib.sha256()
+    with open(os.path.join(ROOT, "linear_attention_hgrn2_amd", "build.py"), "rb") as f:
+        h.update(f.read())
     for n in sorted(os.listdir(csrc)):
         if n.endswith((".h", ".hip", ".cpp")):
             h.update(n.encode())

@@ -1,21 +1,22 @@
 // The per-chunk gradients of one (T, D, C), gradients written as TO: the
-// resident kernel for bfloat16 at D = 128, chunk 64, else the generic one.
-// Instantiated by cbwd_inst.hip (TO = T) and cbwd_f32out_inst.hip (bfloat16
-// inputs, float32 gradients).
+// resident kernel for bfloat16 at D = 128, chunk 64 (instantiated apart, in
+// cbwd_res_inst.hip), else the generic one, instantiated by cbwd_inst.hip
+// (TO = T) and cbwd_f32out_inst.hip (bfloat16 inputs, float32 gradients).
 #pragma once
 
 #include <type_traits>
 
-#include "cbwd_res.h"
 #include "dispatch.h"
 
 namespace hgrn2 {
 
+// the resident kernel (cbwd_res_inst.hip): gradients in bfloat16 or float32
+hipError_t chunk_bwd_res(int gm, bool out_f32, const ChunkBwdArgs &a, hipStream_t s);
+
 template <typename T, int D, int C, typename TO> struct ChunkBwdLaunch {
   template <int GM> static hipError_t go(const ChunkBwdArgs &a, hipStream_t s) {
     if constexpr (std::is_same<T, bf16_t>::value && D == 128 && C == 64) {
-      static_assert(sizeof(CbwdResCfg::Smem) <= 160 * 1024, "LDS");
-      return launch_chunk_bwd_res<GM, TO>(a, s);
+      return chunk_bwd_res(GM, std::is_same<TO, float>::value, a, s);
     } else {
       return launch_chunk_bwd<T, D, C, GM, TO>(a, s);
     }
